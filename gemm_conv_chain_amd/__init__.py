@@ -1,0 +1,259 @@
+"""gemm_conv_chain_amd -- Python binding of libfusedchain (MI355X / gfx950).
+
+Argument marshalling only: every computation runs in the HIP kernels of
+``libfusedchain.so`` behind the C ABI in ``include/fusedchain.h``.  PyTorch is
+used for device memory and the current stream; there is no CPU or PyTorch
+fallback -- if the library is missing, every call raises.
+
+The functions mirror the C entry points:
+
+* ``chain_gemm2(A, W0, b0, W1, b1, act)``      D1 = act(A W0 + b0) W1 + b1
+* ``chain_conv_pool(x, w, b, act, pool)``      maxpool2x2(act(conv3x3(x) + b))
+* ``chain_conv2(x, w0, b0, w1, b1, act)``      conv1x1(act(conv3x3(x) + b0)) + b1
+* ``gemm_bias_act``, ``conv_bias_act``, ``maxpool2x2``   single operators
+* ``pad_channels`` / ``pad_weight_channels``   zero padding of channel counts
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+__all__ = ["lib", "FusedChainError", "chain_gemm2", "chain_conv_pool", "chain_conv2", "gemm_bias_act",
+           "conv_bias_act", "maxpool2x2", "pad_channels", "pad_weight_channels", "abi_version", "ACT", "VARIANT",
+           "LIB_PATH", "HEADER_PATH", "exported_names"]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libfusedchain.so")
+HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "fusedchain.h")
+
+ACT = {"none": 0, "relu": 1, "gelu_tanh": 2}
+POOL = {"none": 0, "max2x2": 1}
+VARIANT = {"auto": 0, "rf": 1, "lds": 2}
+
+
+class FusedChainError(RuntimeError):
+    def __init__(self, fn, status, detail):
+        self.status = status
+        super().__init__("%s failed: %s (%s)" % (fn, _lib_status_str(status), detail))
+
+
+class ConvShape(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in ("n", "h", "w", "c", "k", "r", "s", "stride", "pad")]
+
+
+_lib = None
+_vp = ctypes.c_void_p
+_i32 = ctypes.c_int32
+_i64 = ctypes.c_int64
+
+
+def lib():
+    """Load libfusedchain.so (built by ``gemm_conv_chain_amd.build``)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise FusedChainError("load", -1, "libfusedchain.so not built: run python -m gemm_conv_chain_amd.build")
+        L = ctypes.CDLL(LIB_PATH)
+        L.fc_abi_version.restype = _i32
+        L.fc_status_str.restype = ctypes.c_char_p
+        L.fc_status_str.argtypes = [ctypes.c_int]
+        L.fc_last_error.restype = ctypes.c_char_p
+        L.chain_gemm2.argtypes = [_vp, _vp, _vp, ctypes.c_int, _vp, _vp, _vp, _i64, _i32, _i32, _i32, _vp]
+        L.chain_gemm2_variant.argtypes = [_vp, _vp, _vp, ctypes.c_int, _vp, _vp, _vp, _i64, _i32, _i32, _i32,
+                                          ctypes.c_int, _vp]
+        L.chain_conv_pool.argtypes = [_vp, _vp, _vp, ctypes.c_int, ctypes.c_int, _vp, ctypes.POINTER(ConvShape),
+                                      _vp, _vp]
+        L.chain_conv2.argtypes = [_vp, _vp, _vp, ctypes.c_int, _vp, _vp, _i32, _vp, ctypes.POINTER(ConvShape), _vp]
+        L.gemm_bias_act.argtypes = [_vp, _vp, _vp, ctypes.c_int, _vp, _i64, _i32, _i32, _vp]
+        L.conv_bias_act.argtypes = [_vp, _vp, _vp, ctypes.c_int, _vp, ctypes.POINTER(ConvShape), _vp]
+        L.maxpool2x2.argtypes = [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _vp]
+        L.pad_channels.argtypes = [_vp, _vp, _i64, _i32, _i32, _i32, _vp]
+        for name in ("chain_gemm2", "chain_gemm2_variant", "chain_conv_pool", "chain_conv2", "gemm_bias_act",
+                     "conv_bias_act", "maxpool2x2", "pad_channels"):
+            getattr(L, name).restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _lib_status_str(s):
+    try:
+        return lib().fc_status_str(int(s)).decode()
+    except Exception:
+        return str(s)
+
+
+def abi_version() -> int:
+    return int(lib().fc_abi_version())
+
+
+def exported_names():
+    """Function names declared in include/fusedchain.h."""
+    with open(HEADER_PATH) as f:
+        text = f.read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*([a-z_0-9]+)\s*\(", text, re.M)))
+
+
+def _check(fn, status):
+    if status != 0:
+        raise FusedChainError(fn, status, lib().fc_last_error().decode())
+
+
+# ------------------------------------------------------------ tensor helpers
+def _torch():
+    import torch
+    return torch
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _need(t, name, ndim=None):
+    torch = _torch()
+    if t is None:
+        return
+    if t.dtype != torch.float16:
+        raise TypeError("%s must be float16, got %s" % (name, t.dtype))
+    if not t.is_cuda:
+        raise TypeError("%s must be a device tensor" % name)
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError("%s must have %d dims, got %s" % (name, ndim, tuple(t.shape)))
+
+
+def _stream(t):
+    torch = _torch()
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _act(a):
+    return ACT[a] if isinstance(a, str) else int(a)
+
+
+# ------------------------------------------------------------ entry points
+def chain_gemm2(A, W0, b0, W1, b1, act="relu", out=None, variant="auto"):
+    """D1 [M, N1] = act(A [M,K0] @ W0 [K0,N0] + b0) @ W1 [N0,N1] + b1 (fp16)."""
+    for t, n, d in ((A, "A", 2), (W0, "W0", 2), (W1, "W1", 2), (b0, "b0", 1), (b1, "b1", 1)):
+        _need(t, n, d)
+    M, K0 = A.shape
+    N0, N1 = W0.shape[1], W1.shape[1]
+    if W0.shape[0] != K0 or W1.shape[0] != N0:
+        raise ValueError("shape mismatch A%s W0%s W1%s" % (tuple(A.shape), tuple(W0.shape), tuple(W1.shape)))
+    if out is None:
+        out = _torch().empty((M, N1), dtype=A.dtype, device=A.device)
+    _need(out, "out", 2)
+    v = VARIANT[variant] if isinstance(variant, str) else int(variant)
+    _check("chain_gemm2", lib().chain_gemm2_variant(_ptr(A), _ptr(W0), _ptr(b0), _act(act), _ptr(W1), _ptr(b1),
+                                                    _ptr(out), M, K0, N0, N1, v, _stream(A)))
+    return out
+
+
+def gemm_bias_act(A, W, b, act="none", out=None):
+    """C [M, N] = act(A [M,K] @ W [K,N] + b) (fp16)."""
+    for t, n, d in ((A, "A", 2), (W, "W", 2), (b, "b", 1)):
+        _need(t, n, d)
+    M, K = A.shape
+    N = W.shape[1]
+    if out is None:
+        out = _torch().empty((M, N), dtype=A.dtype, device=A.device)
+    _need(out, "out", 2)
+    _check("gemm_bias_act", lib().gemm_bias_act(_ptr(A), _ptr(W), _ptr(b), _act(act), _ptr(out), M, K, N,
+                                                _stream(A)))
+    return out
+
+
+def _conv_shape(x, w, stride=1, pad=1):
+    n, h, wd, c = x.shape
+    r, s, c2, k = w.shape
+    if c2 != c:
+        raise ValueError("x has %d channels, w expects %d" % (c, c2))
+    return ConvShape(n, h, wd, c, k, r, s, stride, pad)
+
+
+def chain_conv_pool(x, w, b, act="relu", pool="max2x2", out=None, argmax=None):
+    """y = maxpool2x2(act(conv3x3(x, w) + b)) (or act(conv+b) with pool='none').
+    ``argmax``: None, True (allocate) or a uint8 tensor; returns y or (y, argmax)."""
+    torch = _torch()
+    for t, n, d in ((x, "x", 4), (w, "w", 4), (b, "b", 1)):
+        _need(t, n, d)
+    sh = _conv_shape(x, w)
+    P, Q = sh.h, sh.w   # 3x3, stride 1, pad 1
+    p = POOL[pool] if isinstance(pool, str) else int(pool)
+    oshape = (sh.n, P // 2, Q // 2, sh.k) if p else (sh.n, P, Q, sh.k)
+    if out is None:
+        out = torch.empty(oshape, dtype=x.dtype, device=x.device)
+    _need(out, "out", 4)
+    am = None
+    if argmax is True:
+        am = torch.empty(oshape, dtype=torch.uint8, device=x.device)
+    elif argmax is not None and argmax is not False:
+        am = argmax
+    _check("chain_conv_pool", lib().chain_conv_pool(_ptr(x), _ptr(w), _ptr(b), _act(act), p, _ptr(out),
+                                                    ctypes.byref(sh), _ptr(am), _stream(x)))
+    return (out, am) if am is not None else out
+
+
+def conv_bias_act(x, w, b, act="relu", out=None):
+    """y NHWC = act(conv3x3(x, w) + b)."""
+    for t, n, d in ((x, "x", 4), (w, "w", 4), (b, "b", 1)):
+        _need(t, n, d)
+    sh = _conv_shape(x, w)
+    if out is None:
+        out = _torch().empty((sh.n, sh.h, sh.w, sh.k), dtype=x.dtype, device=x.device)
+    _need(out, "out", 4)
+    _check("conv_bias_act", lib().conv_bias_act(_ptr(x), _ptr(w), _ptr(b), _act(act), _ptr(out), ctypes.byref(sh),
+                                                _stream(x)))
+    return out
+
+
+def chain_conv2(x, w0, b0, w1, b1, act="relu", out=None):
+    """y = conv1x1(act(conv3x3(x, w0) + b0), w1) + b1; w1 is [k0, k1] or [1,1,k0,k1]."""
+    for t, n, d in ((x, "x", 4), (w0, "w0", 4), (b0, "b0", 1), (b1, "b1", 1)):
+        _need(t, n, d)
+    _need(w1, "w1")
+    sh = _conv_shape(x, w0)
+    k1 = w1.shape[-1]
+    if w1.numel() != sh.k * k1:
+        raise ValueError("w1 must hold k0 x k1 = %d x %d values" % (sh.k, k1))
+    if out is None:
+        out = _torch().empty((sh.n, sh.h, sh.w, k1), dtype=x.dtype, device=x.device)
+    _need(out, "out", 4)
+    _check("chain_conv2", lib().chain_conv2(_ptr(x), _ptr(w0), _ptr(b0), _act(act), _ptr(w1), _ptr(b1), k1,
+                                            _ptr(out), ctypes.byref(sh), _stream(x)))
+    return out
+
+
+def maxpool2x2(x, out=None, argmax=None):
+    """y [n, h/2, w/2, c] = 2x2/2 max pool of NHWC x (+ optional argmax)."""
+    torch = _torch()
+    _need(x, "x", 4)
+    n, h, w, c = x.shape
+    oshape = (n, h // 2, w // 2, c)
+    if out is None:
+        out = torch.empty(oshape, dtype=x.dtype, device=x.device)
+    _need(out, "out", 4)
+    am = torch.empty(oshape, dtype=torch.uint8, device=x.device) if argmax is True else (
+        argmax if argmax is not None and argmax is not False else None)
+    _check("maxpool2x2", lib().maxpool2x2(_ptr(x), _ptr(out), _ptr(am), n, h, w, c, _stream(x)))
+    return (out, am) if am is not None else out
+
+
+def pad_channels(x, c_out):
+    """Zero-pad the channels (last dim) of NHWC x to c_out."""
+    _need(x, "x")
+    c_in = x.shape[-1]
+    out = _torch().empty(tuple(x.shape[:-1]) + (c_out,), dtype=x.dtype, device=x.device)
+    _check("pad_channels", lib().pad_channels(_ptr(x), _ptr(out), x.numel() // max(c_in, 1), c_in, c_out, 1,
+                                              _stream(x)))
+    return out
+
+
+def pad_weight_channels(w, c_out):
+    """Zero-pad the input channels of HWIO w [r,s,c,k] to c_out."""
+    _need(w, "w", 4)
+    r, s, c_in, k = w.shape
+    out = _torch().empty((r, s, c_out, k), dtype=w.dtype, device=w.device)
+    _check("pad_channels", lib().pad_channels(_ptr(w), _ptr(out), r * s, c_in, c_out, k, _stream(w)))
+    return out

@@ -1,0 +1,214 @@
+// api.hip -- the C ABI of libfusedchain (declared in include/fusedchain.h):
+// host-side argument validation, variant choice and launch on the caller's
+// stream.  Validation happens before any HIP call.
+#include <stdarg.h>
+#include <stdio.h>
+
+#include "../../include/fusedchain.h"
+#include "fc_launch.h"
+
+namespace fc {
+hipError_t run_conv_bias_act3x3(const half_t* x, const half_t* w, const half_t* b, int act, half_t* y, int NB,
+                                int H, int W, int C, int K, hipStream_t st);
+hipError_t run_conv_pool3x3(const half_t* x, const half_t* w, const half_t* b, int act, half_t* y,
+                            uint8_t* argmax, int NB, int H, int W, int C, int K, hipStream_t st);
+hipError_t run_chain_conv2_3x3(const half_t* x, const half_t* w0, const half_t* b0, int act, const half_t* w1,
+                               const half_t* b1, half_t* y, int NB, int H, int W, int C, int K0, int K1,
+                               hipStream_t st);
+hipError_t run_maxpool2x2(const half_t* v, half_t* y, uint8_t* am, int NB, int P, int Q, int K, hipStream_t st);
+hipError_t run_pad_mid(const half_t* src, half_t* dst, long outer, int c_in, int c_out, int inner, hipStream_t st);
+bool convw_fits(int C, int K);
+}  // namespace fc
+
+using fc::half_t;
+
+namespace {
+
+thread_local char g_err[256];
+
+fc_status fail(fc_status s, const char* fmt, ...)
+{
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return s;
+}
+
+fc_status ok()
+{
+    g_err[0] = 0;
+    return FC_OK;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+fc_status hip_status(hipError_t e, const char* what)
+{
+    if (e != hipSuccess) return fail(FC_E_HIP, "%s: %s", what, hipGetErrorString(e));
+    return ok();
+}
+
+const half_t* H(const fc_half* p) { return reinterpret_cast<const half_t*>(p); }
+half_t* Hm(fc_half* p) { return reinterpret_cast<half_t*>(p); }
+
+fc_status check_act(fc_act act)
+{
+    if ((int)act < 0 || (int)act > 2) return fail(FC_E_ARG, "act %d out of range", (int)act);
+    return FC_OK;
+}
+
+// Shapes the conv kernels implement: 3x3, stride 1, pad 1, c % 32, k % 8.
+fc_status check_conv(const fc_conv_shape* s, int kmax)
+{
+    if (!s) return fail(FC_E_NULL, "shape is NULL");
+    if (s->n < 0 || s->h < 0 || s->w < 0 || s->c <= 0 || s->k <= 0 || s->r <= 0 || s->s <= 0 || s->stride <= 0 ||
+        s->pad < 0)
+        return fail(FC_E_SHAPE, "bad conv shape");
+    if (s->c % 8 || s->k % 8) return fail(FC_E_SHAPE, "c=%d and k=%d must be multiples of 8", s->c, s->k);
+    if (s->r != 3 || s->s != 3 || s->stride != 1 || s->pad != 1)
+        return fail(FC_E_UNSUPPORTED, "only 3x3 stride-1 pad-1 convolutions are implemented");
+    if (s->c % 32) return fail(FC_E_UNSUPPORTED, "c=%d: pad channels to a multiple of 32", s->c);
+    if (s->k > kmax) return fail(FC_E_UNSUPPORTED, "k=%d exceeds the %d output channels one block keeps", s->k, kmax);
+    return FC_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t fc_abi_version(void) { return FC_ABI_VERSION; }
+
+const char* fc_status_str(fc_status s)
+{
+    switch (s) {
+    case FC_OK: return "FC_OK";
+    case FC_E_NULL: return "FC_E_NULL";
+    case FC_E_SHAPE: return "FC_E_SHAPE";
+    case FC_E_ALIGN: return "FC_E_ALIGN";
+    case FC_E_UNSUPPORTED: return "FC_E_UNSUPPORTED";
+    case FC_E_HIP: return "FC_E_HIP";
+    case FC_E_ARG: return "FC_E_ARG";
+    }
+    return "FC_E_UNKNOWN";
+}
+
+const char* fc_last_error(void) { return g_err; }
+
+fc_status chain_gemm2_variant(const fc_half* A, const fc_half* W0, const fc_half* b0, fc_act act,
+                              const fc_half* W1, const fc_half* b1, fc_half* D1, int64_t M, int32_t K0, int32_t N0,
+                              int32_t N1, fc_variant variant, void* stream)
+{
+    if (M < 0 || K0 <= 0 || N0 <= 0 || N1 <= 0) return fail(FC_E_SHAPE, "M>=0 and K0, N0, N1 > 0 required");
+    if (!W0 || !W1 || (M > 0 && (!A || !D1))) return fail(FC_E_NULL, "A, W0, W1 and D1 are required");
+    if (K0 % 8 || N0 % 8 || N1 % 8) return fail(FC_E_SHAPE, "K0, N0, N1 must be multiples of 8");
+    if (!aligned16(A) || !aligned16(W0) || !aligned16(W1) || !aligned16(D1) || !aligned16(b0) || !aligned16(b1))
+        return fail(FC_E_ALIGN, "tensor pointers must be 16-byte aligned");
+    fc_status s = check_act(act);
+    if (s != FC_OK) return s;
+    if ((int)variant < 0 || (int)variant > 2) return fail(FC_E_ARG, "variant %d out of range", (int)variant);
+    if (N0 > 256) return fail(FC_E_UNSUPPORTED, "N0=%d exceeds the residence limit of 256", N0);
+    const bool rf_ok = N0 <= 128 && fc::rf_fits(K0, N0, N1);
+    int v = variant;
+    if (v == FC_VARIANT_AUTO) v = rf_ok ? fc::VARIANT_RF : fc::VARIANT_LDS;
+    if (v == FC_VARIANT_RF && !rf_ok)
+        return fail(FC_E_UNSUPPORTED, "register-resident variant needs N0<=128 and W0,W1 within LDS");
+    return hip_status(fc::run_chain_gemm2(H(A), H(W0), H(b0), act, H(W1), H(b1), Hm(D1), M, K0, N0, N1, v,
+                                          (hipStream_t)stream),
+                      "chain_gemm2");
+}
+
+fc_status chain_gemm2(const fc_half* A, const fc_half* W0, const fc_half* b0, fc_act act, const fc_half* W1,
+                      const fc_half* b1, fc_half* D1, int64_t M, int32_t K0, int32_t N0, int32_t N1, void* stream)
+{
+    return chain_gemm2_variant(A, W0, b0, act, W1, b1, D1, M, K0, N0, N1, FC_VARIANT_AUTO, stream);
+}
+
+fc_status gemm_bias_act(const fc_half* A, const fc_half* W, const fc_half* b, fc_act act, fc_half* C, int64_t M,
+                        int32_t K, int32_t N, void* stream)
+{
+    if (M < 0 || K <= 0 || N <= 0) return fail(FC_E_SHAPE, "M>=0 and K, N > 0 required");
+    if (!W || (M > 0 && (!A || !C))) return fail(FC_E_NULL, "A, W and C are required");
+    if (K % 8 || N % 8) return fail(FC_E_SHAPE, "K and N must be multiples of 8");
+    if (!aligned16(A) || !aligned16(W) || !aligned16(C) || !aligned16(b))
+        return fail(FC_E_ALIGN, "tensor pointers must be 16-byte aligned");
+    fc_status s = check_act(act);
+    if (s != FC_OK) return s;
+    return hip_status(fc::run_gemm_bias_act(H(A), H(W), H(b), act, Hm(C), M, K, N, (hipStream_t)stream),
+                      "gemm_bias_act");
+}
+
+fc_status chain_conv_pool(const fc_half* x, const fc_half* w, const fc_half* b, fc_act act, fc_pool pool,
+                          fc_half* y, const fc_conv_shape* shape, uint8_t* argmax, void* stream)
+{
+    fc_status s = check_act(act);
+    if (s != FC_OK) return s;
+    if ((int)pool < 0 || (int)pool > 1) return fail(FC_E_ARG, "pool %d out of range", (int)pool);
+    if (pool == FC_POOL_NONE && argmax) return fail(FC_E_ARG, "argmax needs a pool");
+    s = check_conv(shape, 128);
+    if (s != FC_OK) return s;
+    const long npix = (long)shape->n * shape->h * shape->w;
+    const long nout = pool == FC_POOL_NONE ? npix : (long)shape->n * (shape->h / 2) * (shape->w / 2);
+    if (!w || (npix > 0 && !x) || (nout > 0 && !y)) return fail(FC_E_NULL, "x, w and y are required");
+    if (!aligned16(x) || !aligned16(w) || !aligned16(y) || !aligned16(b))
+        return fail(FC_E_ALIGN, "tensor pointers must be 16-byte aligned");
+    if (nout == 0) return ok();
+    if (!fc::convw_fits(shape->c, shape->k)) return fail(FC_E_UNSUPPORTED, "weights exceed LDS");
+    hipStream_t st = (hipStream_t)stream;
+    if (pool == FC_POOL_NONE)
+        return hip_status(fc::run_conv_bias_act3x3(H(x), H(w), H(b), act, Hm(y), shape->n, shape->h, shape->w,
+                                                    shape->c, shape->k, st),
+                          "conv_bias_act");
+    return hip_status(fc::run_conv_pool3x3(H(x), H(w), H(b), act, Hm(y), argmax, shape->n, shape->h, shape->w,
+                                           shape->c, shape->k, st),
+                      "chain_conv_pool");
+}
+
+fc_status conv_bias_act(const fc_half* x, const fc_half* w, const fc_half* b, fc_act act, fc_half* y,
+                        const fc_conv_shape* shape, void* stream)
+{
+    return chain_conv_pool(x, w, b, act, FC_POOL_NONE, y, shape, nullptr, stream);
+}
+
+fc_status chain_conv2(const fc_half* x, const fc_half* w0, const fc_half* b0, fc_act act, const fc_half* w1,
+                      const fc_half* b1, int32_t k1, fc_half* y, const fc_conv_shape* shape0, void* stream)
+{
+    fc_status s = check_act(act);
+    if (s != FC_OK) return s;
+    if (k1 <= 0 || k1 % 8) return fail(FC_E_SHAPE, "k1=%d must be a positive multiple of 8", k1);
+    s = check_conv(shape0, 128);
+    if (s != FC_OK) return s;
+    const long npix = (long)shape0->n * shape0->h * shape0->w;
+    if (!w0 || !w1 || (npix > 0 && (!x || !y))) return fail(FC_E_NULL, "x, w0, w1 and y are required");
+    if (!aligned16(x) || !aligned16(w0) || !aligned16(w1) || !aligned16(y) || !aligned16(b0) || !aligned16(b1))
+        return fail(FC_E_ALIGN, "tensor pointers must be 16-byte aligned");
+    if (npix == 0) return ok();
+    if (!fc::rf_fits(9 * shape0->c, shape0->k, k1))
+        return fail(FC_E_UNSUPPORTED, "w0 and w1 do not fit in LDS together");
+    return hip_status(fc::run_chain_conv2_3x3(H(x), H(w0), H(b0), act, H(w1), H(b1), Hm(y), shape0->n, shape0->h,
+                                              shape0->w, shape0->c, shape0->k, k1, (hipStream_t)stream),
+                      "chain_conv2");
+}
+
+fc_status maxpool2x2(const fc_half* x, fc_half* y, uint8_t* argmax, int32_t n, int32_t h, int32_t w, int32_t c,
+                     void* stream)
+{
+    if (n < 0 || h < 0 || w < 0 || c <= 0 || c % 8) return fail(FC_E_SHAPE, "bad pool shape");
+    const long nout = (long)n * (h / 2) * (w / 2);
+    if (nout > 0 && (!x || !y)) return fail(FC_E_NULL, "x and y are required");
+    if (nout == 0) return ok();
+    if (!aligned16(x) || !aligned16(y) || ((uintptr_t)argmax & 7u))
+        return fail(FC_E_ALIGN, "x, y 16-byte and argmax 8-byte aligned");
+    return hip_status(fc::run_maxpool2x2(H(x), Hm(y), argmax, n, h, w, c, (hipStream_t)stream), "maxpool2x2");
+}
+
+fc_status pad_channels(const fc_half* src, fc_half* dst, int64_t outer, int32_t c_in, int32_t c_out, int32_t inner,
+                       void* stream)
+{
+    if (!src || !dst) return fail(FC_E_NULL, "src and dst are required");
+    if (outer < 0 || c_in < 0 || c_out < c_in || inner <= 0) return fail(FC_E_SHAPE, "bad padding shape");
+    return hip_status(fc::run_pad_mid(H(src), Hm(dst), outer, c_in, c_out, inner, (hipStream_t)stream),
+                      "pad_channels");
+}
+
+}  // extern "C"

@@ -1,0 +1,24 @@
+// fc_launch.h -- host-side launch functions behind the C ABI (internal).
+#pragma once
+#include <hip/hip_runtime.h>
+
+namespace fc {
+
+typedef _Float16 half_t;
+
+enum { VARIANT_AUTO = 0, VARIANT_RF = 1, VARIANT_LDS = 2 };
+
+// LDS a block may use (gfx950: 160 KiB per CU; one block of the persistent
+// kernels per CU).
+constexpr size_t RF_LDS_LIMIT = 160 * 1024;
+
+int device_cu_count();
+bool rf_fits(int K0, int N0, int N1);
+
+hipError_t run_chain_gemm2(const half_t* A, const half_t* W0, const half_t* b0, int act, const half_t* W1,
+                           const half_t* b1, half_t* D1, long M, int K0, int N0, int N1, int variant,
+                           hipStream_t st);
+hipError_t run_gemm_bias_act(const half_t* A, const half_t* W, const half_t* b, int act, half_t* C, long M,
+                             int K, int N, hipStream_t st);
+
+}  // namespace fc

@@ -1,0 +1,166 @@
+/*
+ * fusedchain.h -- C ABI of libfusedchain: fused operator chains that keep the
+ * intermediate on-chip, for AMD Instinct MI355X (gfx950).
+ *
+ * Sources of the operations (the pages this library follows):
+ *   - BOLT reading notes ("BOLT: Bridging the Gap between Auto-tuners and
+ *     Hardware-native Performance"), section "Persistent kernel (GEMM/Conv)
+ *     fusion": several GEMMs/convs fused into one kernel under the
+ *     threadblock-residence rule (a block computing a tile of the first GEMM
+ *     owns all of that GEMM's N, so the second GEMM reads its input from
+ *     on-chip storage); register-file-resident and shared-memory-resident
+ *     variants; section "Prerequisite: Epilogue fusion" (element-wise op, type
+ *     conversion, broadcast vector, partial reduction); section "Templated code
+ *     generation" (NHWC layout; tensors padded to 8 fp16 elements = 128 bits).
+ *   - Welder reading notes ("Welder: Scheduling Deep Learning Memory Access via
+ *     Tile-graph"), sections "Operator-tile and Tile-graph" and "Tile-graph
+ *     Scheduling" (Figure 5): Conv -> ReLU -> MaxPool connected through an
+ *     on-chip reuse tile; the conv output is never written to global memory.
+ *   - Interview page ("Alibaba AI Infra (2)"), question on GEMM/Conv operator
+ *     optimisation: implicit GEMM convolution; 1x1 conv = GEMM.
+ *
+ * Common conventions
+ *   - fc_half is an IEEE-754 binary16 bit pattern.  Every tensor pointer is a
+ *     DEVICE pointer owned by the caller; the library allocates nothing and keeps
+ *     no per-call state, so calls may be issued from several host threads.
+ *   - All matrices are row-major.  Conv tensors are NHWC; conv weights are HWIO
+ *     (w[r][s][c][k]), i.e. a row-major [(R*S*C) x K] matrix.
+ *   - Every call validates its arguments on the host BEFORE any HIP call and
+ *     returns a status; nothing is launched when validation fails.  On success
+ *     the work is enqueued on `stream` (a hipStream_t; NULL = the default
+ *     stream) and the call returns without synchronising.  Launch failures
+ *     return FC_E_HIP; faults inside a kernel surface at the caller's next
+ *     synchronisation.
+ *   - Tensor pointers must be 16-byte aligned; the lengths of the contiguous
+ *     (innermost) dimensions -- K0, N0, N1, K, N, C, channel counts -- must be
+ *     multiples of 8 (8 fp16 = 128 bits, the widest vector access).  Row counts
+ *     (M, batch, spatial sizes) are arbitrary; tails are masked.
+ *   - Bias pointers may be NULL (zero bias).  Data pointers of tensors with no
+ *     elements (M == 0, an empty batch, a pooled output of zero size) may be
+ *     NULL; such calls launch nothing.  Outputs must not alias inputs and are
+ *     fully overwritten.
+ *   - Accumulation is fp32; each intermediate is rounded once to fp16 (round to
+ *     nearest even) after bias and activation; outputs are fp16.
+ */
+#ifndef FUSEDCHAIN_H
+#define FUSEDCHAIN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FC_ABI_VERSION 1
+
+typedef uint16_t fc_half;
+
+typedef enum {
+    FC_OK = 0,
+    FC_E_NULL = 1,        /* a required pointer is NULL */
+    FC_E_SHAPE = 2,       /* a size is negative, zero where it must not be, or not a multiple of 8 */
+    FC_E_ALIGN = 3,       /* a pointer is not 16-byte aligned */
+    FC_E_UNSUPPORTED = 4, /* valid, but outside what the kernels implement (e.g. residence limit) */
+    FC_E_HIP = 5,         /* a HIP runtime call failed while launching */
+    FC_E_ARG = 6          /* an enum argument is out of range */
+} fc_status;
+
+typedef enum { FC_ACT_NONE = 0, FC_ACT_RELU = 1, FC_ACT_GELU_TANH = 2 } fc_act;
+typedef enum { FC_POOL_NONE = 0, FC_POOL_MAX_2X2_S2 = 1 } fc_pool;
+typedef enum { FC_VARIANT_AUTO = 0, FC_VARIANT_RF = 1, FC_VARIANT_LDS = 2 } fc_variant;
+
+/* x NHWC [n,h,w,c]; w HWIO [r,s,c,k]; output spatial size
+ * P = (h + 2*pad - r)/stride + 1, Q = (w + 2*pad - s)/stride + 1. */
+typedef struct {
+    int32_t n, h, w, c, k, r, s, stride, pad;
+} fc_conv_shape;
+
+/* Version of this ABI (FC_ABI_VERSION). */
+int32_t fc_abi_version(void);
+
+/* Static, human-readable name of a status code. */
+const char *fc_status_str(fc_status s);
+
+/* Detail message of the last failed call on the calling host thread ("" if
+ * none).  The pointer stays valid until the thread's next call. */
+const char *fc_last_error(void);
+
+/*
+ * chain_gemm2 -- D1 = act(A*W0 + b0) * W1 + b1 in one kernel
+ * (BOLT notes, "Persistent kernel (GEMM/Conv) fusion").
+ *   A  [M  x K0]   W0 [K0 x N0]   b0 [N0]
+ *   W1 [N0 x N1]   b1 [N1]        D1 [M  x N1]
+ *   act: FC_ACT_NONE / FC_ACT_RELU / FC_ACT_GELU_TANH (tanh form).
+ * The intermediate H = fp16(act(A*W0 + b0)) [M x N0] never reaches global
+ * memory.  Residence: one block owns all N0 columns, so N0 <= 256
+ * (FC_E_UNSUPPORTED above).  M == 0 is a no-op.
+ * Variant (chain_gemm2_variant): FC_VARIANT_RF keeps H in VGPRs (N0 <= 128 and
+ * W0, W1 fit in LDS together); FC_VARIANT_LDS stages H through LDS
+ * (N0 <= 256); FC_VARIANT_AUTO (chain_gemm2) picks RF when it applies.
+ */
+fc_status chain_gemm2(const fc_half *A, const fc_half *W0, const fc_half *b0, fc_act act,
+                      const fc_half *W1, const fc_half *b1, fc_half *D1,
+                      int64_t M, int32_t K0, int32_t N0, int32_t N1, void *stream);
+fc_status chain_gemm2_variant(const fc_half *A, const fc_half *W0, const fc_half *b0, fc_act act,
+                              const fc_half *W1, const fc_half *b1, fc_half *D1,
+                              int64_t M, int32_t K0, int32_t N0, int32_t N1,
+                              fc_variant variant, void *stream);
+
+/*
+ * chain_conv_pool -- y = maxpool2x2(act(conv(x, w) + b)) with the conv output
+ * kept in registers (Welder notes, Conv+ReLU+MaxPool tile graph, Figure 5).
+ *   x NHWC [n,h,w,c], w HWIO [3,3,c,k], b [k];
+ *   pool == FC_POOL_MAX_2X2_S2: y [n, P/2, Q/2, k] (floor), argmax (nullable,
+ *   uint8 [n, P/2, Q/2, k]) = 2*dy + dx of the first maximum in the order
+ *   (0,0),(0,1),(1,0),(1,1), decided on the fp16-rounded values;
+ *   pool == FC_POOL_NONE: y [n, P, Q, k] = act(conv + b) (argmax must be NULL).
+ * Implemented shapes: r = s = 3, stride 1, pad 1, c % 32 == 0 (pad channels
+ * with pad_channels first), k % 8 == 0 and k <= 128 (all output channels in
+ * one block), and the weights, held in LDS for the whole kernel, within
+ * 160 KiB: roundup(k,32) * (roundup(9c,64) + 8) * 2 bytes (c = 64: k <= 128;
+ * c = 128: k <= 64).  Others: FC_E_UNSUPPORTED.
+ */
+fc_status chain_conv_pool(const fc_half *x, const fc_half *w, const fc_half *b, fc_act act, fc_pool pool,
+                          fc_half *y, const fc_conv_shape *shape, uint8_t *argmax, void *stream);
+
+/*
+ * chain_conv2 -- y = conv1x1(act(conv(x, w0) + b0), w1) + b1, the first conv's
+ * output kept in VGPRs (BOLT persistent conv fusion; a 1x1 conv is a GEMM,
+ * interview page, conv item 5).
+ *   x NHWC [n,h,w,c], w0 HWIO [3,3,c,k0] (k0 = shape0->k), b0 [k0],
+ *   w1 [k0 x k1] (= HWIO [1,1,k0,k1]), b1 [k1], y NHWC [n,P,Q,k1].
+ * Implemented: r = s = 3, stride 1, pad 1, c % 32 == 0, k0 % 8 == 0 and
+ * k0 <= 128, k1 % 8 == 0, and both weights fit in LDS together.
+ */
+fc_status chain_conv2(const fc_half *x, const fc_half *w0, const fc_half *b0, fc_act act,
+                      const fc_half *w1, const fc_half *b1, int32_t k1, fc_half *y,
+                      const fc_conv_shape *shape0, void *stream);
+
+/* ---- unfused single-operator kernels (the two-kernel baselines) ---- */
+
+/* C [M x N] = act(A [M x K] * W [K x N] + b [N]), fp16 out (GEMM + epilogue). */
+fc_status gemm_bias_act(const fc_half *A, const fc_half *W, const fc_half *b, fc_act act, fc_half *C,
+                        int64_t M, int32_t K, int32_t N, void *stream);
+
+/* y NHWC [n,P,Q,k] = act(conv(x, w) + b); same shape limits as chain_conv_pool. */
+fc_status conv_bias_act(const fc_half *x, const fc_half *w, const fc_half *b, fc_act act, fc_half *y,
+                        const fc_conv_shape *shape, void *stream);
+
+/* y [n, h/2, w/2, c] = 2x2 stride-2 max pool of x NHWC [n,h,w,c] (floor);
+ * argmax nullable (8-byte aligned), encoded as in chain_conv_pool. */
+fc_status maxpool2x2(const fc_half *x, fc_half *y, uint8_t *argmax, int32_t n, int32_t h, int32_t w, int32_t c,
+                     void *stream);
+
+/* ---- input preparation (BOLT notes, "Templated code generation": tensors
+ *      whose channel count is not a multiple of 8 are zero-padded) ----
+ * dst[o][j][i] = j < c_in ? src[o][j][i] : 0 for a tensor viewed as
+ * [outer, c, inner]: NHWC activations use inner = 1 (outer = n*h*w); HWIO
+ * weights use outer = r*s, inner = k.  c_out >= c_in.  No alignment needed. */
+fc_status pad_channels(const fc_half *src, fc_half *dst, int64_t outer, int32_t c_in, int32_t c_out,
+                       int32_t inner, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FUSEDCHAIN_H */

@@ -1,0 +1,114 @@
+"""Host-only checks of the C ABI: the library loads, exports every function the
+header declares, and rejects bad arguments synchronously (validation runs
+before any HIP call, so these need no GPU and launch nothing)."""
+import ctypes
+
+import pytest
+
+import gemm_conv_chain_amd as fc
+
+pytestmark = pytest.mark.cpu
+
+OK, E_NULL, E_SHAPE, E_ALIGN, E_UNSUP, E_HIP, E_ARG = range(7)
+P = ctypes.c_void_p(0x10000)       # fake, 16-byte aligned device pointers:
+P2 = ctypes.c_void_p(0x20000)      # validation never dereferences them
+BAD = ctypes.c_void_p(0x10002)     # misaligned
+NUL = None
+
+
+@pytest.fixture(scope="module")
+def L():
+    return fc.lib()
+
+
+def test_exports_every_declared_symbol(L):
+    names = fc.exported_names()
+    for n in ("chain_gemm2", "chain_gemm2_variant", "chain_conv_pool", "chain_conv2", "gemm_bias_act",
+              "conv_bias_act", "maxpool2x2", "pad_channels", "fc_abi_version", "fc_status_str", "fc_last_error"):
+        assert n in names
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_version_and_status_strings(L):
+    assert fc.abi_version() == 1
+    for code, name in enumerate(["FC_OK", "FC_E_NULL", "FC_E_SHAPE", "FC_E_ALIGN", "FC_E_UNSUPPORTED", "FC_E_HIP",
+                                 "FC_E_ARG"]):
+        assert L.fc_status_str(code).decode() == name
+
+
+def g2(L, A=P, W0=P, b0=NUL, act=1, W1=P, b1=NUL, D1=P2, M=512, K0=64, N0=64, N1=64, variant=0):
+    return L.chain_gemm2_variant(A, W0, b0, act, W1, b1, D1, M, K0, N0, N1, variant, None)
+
+
+def test_chain_gemm2_validation(L):
+    assert g2(L, A=NUL) == E_NULL
+    assert g2(L, D1=NUL) == E_NULL
+    assert g2(L, M=-1) == E_SHAPE
+    assert g2(L, K0=0) == E_SHAPE
+    assert g2(L, K0=60) == E_SHAPE          # not a multiple of 8 (128-bit vectors)
+    assert g2(L, N1=20) == E_SHAPE
+    assert g2(L, A=BAD) == E_ALIGN
+    assert g2(L, b0=BAD) == E_ALIGN
+    assert g2(L, act=7) == E_ARG
+    assert g2(L, variant=5) == E_ARG
+    assert g2(L, N0=264) == E_UNSUP          # residence: one block owns all N0 <= 256
+    assert g2(L, N0=256, variant=1) == E_UNSUP   # register-resident needs N0 <= 128
+    assert b"N0" in L.fc_last_error()
+
+
+def test_gemm_bias_act_validation(L):
+    assert L.gemm_bias_act(NUL, P, NUL, 0, P2, 8, 8, 8, None) == E_NULL
+    assert L.gemm_bias_act(P, P, NUL, 0, P2, 8, 12, 8, None) == E_SHAPE
+    assert L.gemm_bias_act(P, P, BAD, 0, P2, 8, 8, 8, None) == E_ALIGN
+    assert L.gemm_bias_act(P, P, NUL, 3, P2, 8, 8, 8, None) == E_ARG
+
+
+def shape(n=1, h=8, w=8, c=64, k=128, r=3, s=3, stride=1, pad=1):
+    return fc.ConvShape(n, h, w, c, k, r, s, stride, pad)
+
+
+def test_conv_validation(L):
+    sh = shape()
+    assert L.chain_conv_pool(P, P, NUL, 1, 1, P2, None, NUL, None) == E_NULL
+    assert L.chain_conv_pool(NUL, P, NUL, 1, 1, P2, ctypes.byref(sh), NUL, None) == E_NULL
+    assert L.chain_conv_pool(P, P, NUL, 1, 1, P2, ctypes.byref(shape(c=60)), NUL, None) == E_SHAPE
+    assert L.chain_conv_pool(P, P, NUL, 1, 1, P2, ctypes.byref(shape(c=40)), NUL, None) == E_UNSUP
+    assert L.chain_conv_pool(P, P, NUL, 1, 1, P2, ctypes.byref(shape(k=136)), NUL, None) == E_UNSUP
+    assert L.chain_conv_pool(P, P, NUL, 1, 1, P2, ctypes.byref(shape(r=5, s=5)), NUL, None) == E_UNSUP
+    assert L.chain_conv_pool(P, P, NUL, 1, 1, P2, ctypes.byref(shape(stride=2)), NUL, None) == E_UNSUP
+    assert L.chain_conv_pool(P, P, NUL, 1, 2, P2, ctypes.byref(sh), NUL, None) == E_ARG
+    assert L.chain_conv_pool(P, P, NUL, 1, 0, P2, ctypes.byref(sh), P, None) == E_ARG  # argmax needs a pool
+    assert L.chain_conv_pool(BAD, P, NUL, 1, 1, P2, ctypes.byref(sh), NUL, None) == E_ALIGN
+    assert L.conv_bias_act(P, P, NUL, 1, P2, ctypes.byref(shape(h=-1)), None) == E_SHAPE
+    assert L.chain_conv2(P, P, NUL, 1, P, NUL, 20, P2, ctypes.byref(shape(k=64)), None) == E_SHAPE
+    assert L.chain_conv2(P, P, NUL, 1, P, NUL, 256, P2, ctypes.byref(shape(k=256)), None) == E_UNSUP
+    assert L.chain_conv2(P, P, NUL, 1, NUL, NUL, 256, P2, ctypes.byref(shape(k=64)), None) == E_NULL
+    # weights-resident kernels: the HWIO weights must fit in LDS
+    assert L.chain_conv_pool(P, P, NUL, 1, 1, P2, ctypes.byref(shape(c=96, k=96)), NUL, None) == E_UNSUP
+    assert L.chain_conv2(P, P, NUL, 1, P, NUL, 64, P2, ctypes.byref(shape(c=64, k=128)), None) == E_UNSUP
+
+
+def test_empty_tensors_may_be_null(L):
+    # nothing to compute: NULL data pointers of empty tensors are accepted
+    assert g2(L, A=NUL, D1=NUL, M=0) == OK
+    assert L.chain_conv_pool(P, P, NUL, 1, 1, NUL, ctypes.byref(shape(h=1)), NUL, None) == OK
+    assert L.chain_conv_pool(NUL, P, NUL, 1, 1, NUL, ctypes.byref(shape(h=1)), NUL, None) == E_NULL
+    assert L.chain_conv2(NUL, P, NUL, 1, P, NUL, 64, NUL, ctypes.byref(shape(n=0, k=64)), None) == OK
+    assert L.maxpool2x2(NUL, NUL, NUL, 2, 1, 9, 8, None) == OK
+    assert g2(L, W0=NUL, M=0) == E_NULL
+
+
+def test_pool_and_pad_validation(L):
+    assert L.maxpool2x2(NUL, P2, NUL, 1, 4, 4, 8, None) == E_NULL
+    assert L.maxpool2x2(P, P2, NUL, 1, 4, 4, 12, None) == E_SHAPE
+    assert L.maxpool2x2(P, P2, ctypes.c_void_p(0x30004), 1, 4, 4, 8, None) == E_ALIGN
+    assert L.pad_channels(P, P2, 10, 60, 56, 1, None) == E_SHAPE
+    assert L.pad_channels(NUL, P2, 10, 60, 64, 1, None) == E_NULL
+
+
+def test_binding_refuses_host_tensors():
+    torch = pytest.importorskip("torch")
+    A = torch.zeros(4, 8, dtype=torch.float16)
+    with pytest.raises(TypeError):
+        fc.chain_gemm2(A, A.T.contiguous(), None, A, None)

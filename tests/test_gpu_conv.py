@@ -1,0 +1,157 @@
+"""GPU parity of the conv chains, the single conv, the max pool and the channel
+padding against the fp64 oracle (same seeded inputs)."""
+import numpy as np
+import pytest
+
+import oracle
+from gemm_conv_chain_amd import inputs
+from parity import assert_close, pool_tie_mask, to_np
+
+pytestmark = pytest.mark.gpu
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module")
+def fc():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import gemm_conv_chain_amd as m
+    m.lib()
+    return m
+
+
+def dev(a):
+    return None if a is None else torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def check_pool(y, am, x_np, w_np, b_np, what):
+    """y, am from the GPU; oracle on the (unpadded) inputs."""
+    yo, amo, v, c64 = oracle.chain_conv_pool(x_np, w_np, b_np, oracle.ACT_RELU, want_conv64=True)
+    assert_close(y, yo.astype(np.float64), what)
+    if am is not None:
+        ties = pool_tie_mask(c64, c64.shape[1], c64.shape[2])
+        free = ~ties
+        assert np.array_equal(am[free], amo[free]), "%s: argmax differs on %d tie-free windows" % (
+            what, int(np.sum(am[free] != amo[free])))
+        assert np.all(am < 4)
+        # on tie windows the GPU's choice must still be a maximal position (to
+        # within the same 2-ulp band)
+        n, PO, QO, K = am.shape
+        win = c64[:, :2 * PO, :2 * QO].reshape(n, PO, 2, QO, 2, K).transpose(0, 1, 3, 5, 2, 4).reshape(n, PO, QO, K, 4)
+        picked = np.take_along_axis(win, am[..., None].astype(np.int64), -1)[..., 0]
+        top = win.max(-1)
+        assert np.all(top - picked <= 2 * np.maximum(np.abs(top), 2.0 ** -14) * 2.0 ** -10 + 1e-30)
+        return int(np.sum(free)), int(np.sum(ties))
+    return 0, 0
+
+
+@pytest.mark.parametrize("n,h,w,c,k", [(2, 8, 10, 64, 128), (1, 5, 7, 32, 64), (2, 9, 6, 64, 72), (1, 4, 6, 96, 64),
+                                       (1, 12, 12, 64, 8), (3, 3, 17, 32, 32)])
+def test_conv_pool_small(fc, n, h, w, c, k):
+    d = inputs.conv_pool_inputs(n, h, w, c, k, seed=h * w)
+    print("case conv_pool", n, h, w, c, k, flush=True)
+    y, am = fc.chain_conv_pool(dev(d["x"]), dev(d["w"]), dev(d["b"]), act="relu", pool="max2x2", argmax=True)
+    torch.cuda.synchronize()
+    free, ties = check_pool(to_np(y), to_np(am), d["x"], d["w"], d["b"], "conv_pool small")
+    assert free > 0
+
+
+def test_conv_pool_padded_channels(fc):
+    # 60 real channels zero-padded to 64 on the GPU; the oracle uses the 60
+    d = inputs.conv_pool_inputs(2, 12, 14, 60, 128, seed=5)
+    x = fc.pad_channels(dev(d["x"]), 64)
+    w = fc.pad_weight_channels(dev(d["w"]), 64)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_np(x)[..., :60].view(np.uint16), d["x"].view(np.uint16))
+    assert not np.any(to_np(x)[..., 60:].astype(np.float64))
+    assert np.array_equal(to_np(w)[:, :, :60].view(np.uint16), d["w"].view(np.uint16))
+    assert not np.any(to_np(w)[:, :, 60:].astype(np.float64))
+    y, am = fc.chain_conv_pool(x, w, dev(d["b"]), argmax=True)
+    torch.cuda.synchronize()
+    check_pool(to_np(y), to_np(am), d["x"], d["w"], d["b"], "conv_pool padded")
+
+
+def test_conv_pool_degenerate(fc):
+    # conv output of height 1: the pooled output is empty (floor)
+    d = inputs.conv_pool_inputs(1, 1, 8, 32, 32, seed=1)
+    y = fc.chain_conv_pool(dev(d["x"]), dev(d["w"]), dev(d["b"]))
+    torch.cuda.synchronize()
+    assert y.shape == (1, 0, 4, 32)
+
+
+@pytest.mark.parametrize("n,h,w,c,k,act", [(2, 7, 9, 64, 64, "relu"), (1, 6, 6, 32, 128, "gelu_tanh"),
+                                           (1, 5, 11, 64, 24, "none")])
+def test_conv_bias_act(fc, n, h, w, c, k, act):
+    d = inputs.conv_pool_inputs(n, h, w, c, k, seed=n * h)
+    a = {"none": 0, "relu": 1, "gelu_tanh": 2}[act]
+    print("case conv_bias_act", n, h, w, c, k, act, flush=True)
+    y = to_np(fc.conv_bias_act(dev(d["x"]), dev(d["w"]), dev(d["b"]), act=act))
+    assert_close(y, oracle.conv_bias_act(d["x"], d["w"], d["b"], a), "conv_bias_act")
+
+
+@pytest.mark.parametrize("n,h,w,c,k0,k1", [(2, 7, 9, 64, 64, 256), (1, 5, 6, 32, 32, 40), (1, 8, 8, 32, 128, 64),
+                                           (3, 4, 13, 96, 40, 8)])
+def test_conv2_small(fc, n, h, w, c, k0, k1):
+    d = inputs.conv2_inputs(n, h, w, c, k0, k1, seed=h + w)
+    print("case conv2", n, h, w, c, k0, k1, flush=True)
+    y = to_np(fc.chain_conv2(dev(d["x"]), dev(d["w0"]), dev(d["b0"]), dev(d["w1"]), dev(d["b1"]), act="relu"))
+    ref, _ = oracle.chain_conv2(d["x"], d["w0"], d["b0"], oracle.ACT_RELU, d["w1"], d["b1"])
+    assert_close(y, ref, "conv2 small")
+
+
+def test_conv2_fused_equals_unfused(fc):
+    d = inputs.conv2_inputs(2, 14, 14, 64, 64, 256, seed=2)
+    x, w0, b0, w1, b1 = (dev(d[k]) for k in ("x", "w0", "b0", "w1", "b1"))
+    fused = to_np(fc.chain_conv2(x, w0, b0, w1, b1))
+    H = fc.conv_bias_act(x, w0, b0, act="relu")
+    un = to_np(fc.gemm_bias_act(H.reshape(-1, 64), w1, b1, act="none")).reshape(fused.shape)
+    assert_close(fused, un.astype(np.float64), "conv2 fused vs unfused")
+
+
+def test_conv_pool_fused_equals_unfused(fc):
+    d = inputs.conv_pool_inputs(2, 16, 16, 64, 128, seed=3)
+    x, w, b = dev(d["x"]), dev(d["w"]), dev(d["b"])
+    yf, af = fc.chain_conv_pool(x, w, b, argmax=True)
+    v = fc.conv_bias_act(x, w, b, act="relu")
+    yu, au = fc.maxpool2x2(v, argmax=True)
+    torch.cuda.synchronize()
+    # same accumulation order in both paths: bit-identical
+    assert np.array_equal(to_np(yf).view(np.uint16), to_np(yu).view(np.uint16))
+    assert np.array_equal(to_np(af), to_np(au))
+
+
+def test_maxpool2x2(fc):
+    rng = np.random.default_rng(0)
+    v = rng.standard_normal((2, 7, 9, 24)).astype(np.float16)
+    v[0, 0, 0, :] = 0.0
+    v[0, 1, 1, :] = 0.0
+    v[0, 0, 1, :] = 0.0
+    v[0, 1, 0, :] = 0.0          # an all-equal window: argmax must be 0
+    y, am = fc.maxpool2x2(dev(v), argmax=True)
+    yo, amo = oracle.maxpool2x2(v)
+    assert np.array_equal(to_np(y).view(np.uint16), yo.view(np.uint16))
+    assert np.array_equal(to_np(am), amo)
+
+
+@pytest.mark.slow
+def test_conv_pool_full_size_sampled(fc):
+    spec, d = inputs.workload("conv3x3_relu_maxpool")
+    print("case full conv3x3_relu_maxpool", flush=True)
+    x = fc.pad_channels(dev(d["x"]), 64)
+    w = fc.pad_weight_channels(dev(d["w"]), 64)
+    y, am = fc.chain_conv_pool(x, w, dev(d["b"]), argmax=True)
+    torch.cuda.synchronize()
+    y, am = to_np(y), to_np(am)
+    assert np.all(np.isfinite(y.astype(np.float64)))
+    for img in (0, 31):
+        check_pool(y[img:img + 1], am[img:img + 1], d["x"][img:img + 1], d["w"], d["b"], "full img %d" % img)
+
+
+@pytest.mark.slow
+def test_conv2_full_size_sampled(fc):
+    spec, d = inputs.workload("conv3x3_conv1x1")
+    print("case full conv3x3_conv1x1", flush=True)
+    y = to_np(fc.chain_conv2(*(dev(d[k]) for k in ("x", "w0", "b0", "w1", "b1"))))
+    for img in (0, 17, 31):
+        ref, _ = oracle.chain_conv2(d["x"][img:img + 1], d["w0"], d["b0"], oracle.ACT_RELU, d["w1"], d["b1"])
+        assert_close(y[img:img + 1], ref, "full conv2 img %d" % img)

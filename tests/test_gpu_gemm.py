@@ -1,0 +1,151 @@
+"""GPU parity of the GEMM chain and the single GEMM against the fp64 oracle.
+
+Every case runs the HIP kernels through the C ABI (via the binding) and
+compares with the oracle on the same seeded inputs, to
+max|err| <= 1e-2 max|ref| + 1e-3."""
+import numpy as np
+import pytest
+
+import oracle
+from gemm_conv_chain_amd import inputs
+from parity import assert_close, to_np
+
+pytestmark = pytest.mark.gpu
+torch = pytest.importorskip("torch")
+ACTS = {"none": oracle.ACT_NONE, "relu": oracle.ACT_RELU, "gelu_tanh": oracle.ACT_GELU_TANH}
+
+
+@pytest.fixture(scope="module")
+def fc():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import gemm_conv_chain_amd as m
+    m.lib()
+    return m
+
+
+def dev(a):
+    return None if a is None else torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def run_chain(fc, d, act, variant):
+    A, W0, b0, W1, b1 = (dev(d[k]) for k in ("A", "W0", "b0", "W1", "b1"))
+    out = fc.chain_gemm2(A, W0, b0, W1, b1, act=act, variant=variant)
+    torch.cuda.synchronize()
+    return to_np(out)
+
+
+def oracle_chain(d, act, rows=None):
+    A = d["A"] if rows is None else d["A"][rows]
+    ref, _ = oracle.chain_gemm2(A, d["W0"], d["b0"], ACTS[act], d["W1"], d["b1"])
+    return ref
+
+
+@pytest.mark.parametrize("variant", ["rf", "lds", "auto"])
+def test_tiny_full(fc, variant):
+    spec, d = inputs.workload("b2b_gemm_tiny")
+    print("case b2b_gemm_tiny", variant, flush=True)
+    assert_close(run_chain(fc, d, "relu", variant), oracle_chain(d, "relu"), "tiny " + variant)
+
+
+@pytest.mark.parametrize("variant", ["rf", "lds"])
+def test_rf_shape_ragged(fc, variant):
+    # the register-resident workload's widths at a size the oracle does at once,
+    # with a ragged last tile (M % 32 != 0, M % 128 != 0)
+    d = inputs.gemm2_inputs(1000, 256, 64, 128, "uniform", seed=3)
+    print("case rf-shape M=1000", variant, flush=True)
+    assert_close(run_chain(fc, d, "relu", variant), oracle_chain(d, "relu"), "rf-shape " + variant)
+
+
+def test_lds_shape_ragged(fc):
+    d = inputs.gemm2_inputs(300, 576, 256, 256, "normal", seed=4)
+    print("case lds-shape M=300", flush=True)
+    assert_close(run_chain(fc, d, "gelu_tanh", "lds"), oracle_chain(d, "gelu_tanh"), "lds-shape")
+
+
+@pytest.mark.parametrize("M,K0,N0,N1,act,variant", [
+    (1, 8, 8, 8, "relu", "rf"), (1, 8, 8, 8, "relu", "lds"),
+    (33, 40, 24, 72, "gelu_tanh", "rf"), (33, 40, 24, 72, "gelu_tanh", "lds"),
+    (130, 72, 96, 264, "none", "rf"), (130, 72, 96, 264, "none", "lds"),
+    (257, 200, 128, 40, "relu", "rf"), (200, 136, 136, 520, "relu", "lds"),
+    (64, 32, 200, 16, "gelu_tanh", "lds"), (97, 1000, 64, 64, "relu", "auto"),
+])
+def test_edge_shapes(fc, M, K0, N0, N1, act, variant):
+    d = inputs.gemm2_inputs(M, K0, N0, N1, "normal", seed=M + K0)
+    print("case", M, K0, N0, N1, act, variant, flush=True)
+    assert_close(run_chain(fc, d, act, variant), oracle_chain(d, act), "edge")
+
+
+@pytest.mark.parametrize("variant", ["rf", "lds"])
+def test_sensitivity_unscaled(fc, variant):
+    # unscaled inputs and zero biases: the outputs are not bias-dominated, so a
+    # partial-K or dropped-tile mistake cannot hide inside the tolerance
+    d = inputs.gemm2_inputs(256, 256, 64, 128, "uniform", seed=7, scaled=False)
+    d["b0"] = np.zeros_like(d["b0"])
+    d["b1"] = np.zeros_like(d["b1"])
+    d["W1"] = (d["W1"].astype(np.float64) / 16).astype(np.float16)
+    print("case sensitivity", variant, flush=True)
+    assert_close(run_chain(fc, d, "relu", variant), oracle_chain(d, "relu"), "sensitivity")
+
+
+def test_null_biases(fc):
+    d = inputs.gemm2_inputs(96, 64, 64, 64, "uniform", seed=9)
+    A, W0, W1 = dev(d["A"]), dev(d["W0"]), dev(d["W1"])
+    for v in ("rf", "lds"):
+        out = to_np(fc.chain_gemm2(A, W0, None, W1, None, act="relu", variant=v))
+        ref, _ = oracle.chain_gemm2(d["A"], d["W0"], None, oracle.ACT_RELU, d["W1"], None)
+        assert_close(out, ref, "null bias " + v)
+
+
+def test_m_zero_is_noop(fc):
+    W0 = torch.zeros(64, 64, dtype=torch.float16, device="cuda")
+    A = torch.zeros(0, 64, dtype=torch.float16, device="cuda")
+    out = fc.chain_gemm2(A, W0, None, W0, None)
+    torch.cuda.synchronize()
+    assert out.shape == (0, 64)
+
+
+def test_deterministic(fc):
+    d = inputs.gemm2_inputs(512, 256, 64, 128, "uniform", seed=11)
+    for v in ("rf", "lds"):
+        a = run_chain(fc, d, "relu", v)
+        b = run_chain(fc, d, "relu", v)
+        assert np.array_equal(a.view(np.uint16), b.view(np.uint16))
+
+
+@pytest.mark.parametrize("M,K,N,act", [(1000, 256, 64, "relu"), (300, 64, 128, "none"), (129, 576, 256, "gelu_tanh"),
+                                       (70, 40, 520, "relu"), (5, 8, 8, "none")])
+def test_gemm_bias_act(fc, M, K, N, act):
+    rng = np.random.default_rng(M)
+    A = (rng.standard_normal((M, K)) / np.sqrt(K)).astype(np.float16)
+    W = rng.standard_normal((K, N)).astype(np.float16)
+    b = rng.standard_normal(N).astype(np.float16)
+    print("case gemm_bias_act", M, K, N, act, flush=True)
+    out = to_np(fc.gemm_bias_act(dev(A), dev(W), dev(b), act=act))
+    assert_close(out, oracle.gemm_bias_act(A, W, b, ACTS[act]), "gemm_bias_act")
+
+
+def test_fused_equals_unfused(fc):
+    d = inputs.gemm2_inputs(2048, 256, 64, 128, "uniform", seed=5)
+    A, W0, b0, W1, b1 = (dev(d[k]) for k in ("A", "W0", "b0", "W1", "b1"))
+    H = fc.gemm_bias_act(A, W0, b0, act="relu")
+    un = to_np(fc.gemm_bias_act(H, W1, b1, act="none"))
+    for v in ("rf", "lds"):
+        fu = to_np(fc.chain_gemm2(A, W0, b0, W1, b1, act="relu", variant=v))
+        assert_close(fu, un.astype(np.float64), "fused vs unfused " + v)
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("name,variant", [("b2b_gemm_rf", "auto"), ("b2b_gemm_rf", "lds"),
+                                          ("b2b_gemm_lds", "auto")])
+def test_full_size_sampled(fc, name, variant):
+    """Full workload size in the bench's launch configuration; the oracle
+    checks 320 sampled rows (first and last tiles plus random rows)."""
+    spec, d = inputs.workload(name)
+    print("case full", name, variant, flush=True)
+    out = run_chain(fc, d, spec["act"], variant)
+    M = spec["M"]
+    rng = np.random.default_rng(0)
+    rows = np.unique(np.concatenate([np.arange(32), np.arange(M - 32, M), rng.integers(0, M, 256)]))
+    assert_close(out[rows], oracle_chain(d, spec["act"], rows), "full " + name)
+    assert np.all(np.isfinite(out))
