@@ -1,0 +1,326 @@
+#!/usr/bin/env python3
+"""Benchmark of one fused-chain workload on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step is one pass of the fused chain over one batch of synthetic input (one
+kernel launch: GEMM0 + epilogue + on-chip hand-off + GEMM1 + epilogue, or
+conv + bias + ReLU + pool).  Inputs are resident in HBM before the timed
+region; the step rotates over enough copies of the activations and outputs
+(> 2x the 256 MiB Infinity Cache) that every step reads its inputs from HBM.
+Timing: HIP events on the stream the kernels run on (torch's current stream).
+
+Prints ONE JSON line: throughput in TFLOP/s (algorithmic FLOPs), the roofline
+position of the fused kernel, the unfused two-kernel baseline, and the CPU
+oracle timed on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import glob
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_F16_TFLOPS = 256 * 4096 * 2.4e9 / 1e12   # 2516.6: 256 CUs x 4096 fp16 FLOP/clk x 2.4 GHz (dense)
+PEAK_HBM_GBS = 8000.0                          # HBM3E, 8 TB/s
+RIDGE = PEAK_F16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
+METRIC = "fused-chain TFLOP/s & % of fp16 MFMA peak; HBM bytes vs unfused"
+COLD_BYTES = 640 << 20
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_src_hash():
+    h = hashlib.sha256()
+    for p in sorted(glob.glob(os.path.join(ROOT, "gemm_conv_chain_amd", "csrc", "*"))):
+        with open(p, "rb") as f:
+            h.update(os.path.basename(p).encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+class Problem:
+    """Device buffers, step functions and the byte/FLOP model of one workload."""
+
+    def __init__(self, name, cold=True):
+        import numpy as np
+        import torch
+
+        import gemm_conv_chain_amd as fc
+        from gemm_conv_chain_amd import inputs
+
+        self.fc, self.torch, self.np = fc, torch, np
+        self.name = name
+        self.spec, d = inputs.workload(name)
+        self.host = d
+        dev = torch.device("cuda:0")
+        t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+        s = self.spec
+        if s["kind"] == "gemm2":
+            M, K0, N0, N1 = s["M"], s["K0"], s["N0"], s["N1"]
+            self.act = s["act"]
+            self.flops = 2 * M * (K0 * N0 + N0 * N1)
+            self.flops_exec = self.flops
+            wbytes = 2 * (K0 * N0 + N0 + N0 * N1 + N1)
+            self.bytes_fused = 2 * (M * K0 + M * N1) + wbytes
+            self.bytes_interm = 2 * M * N0
+            self.W = [t(d["W0"]), t(d["b0"]), t(d["W1"]), t(d["b1"])]
+            per_set = 2 * (M * K0 + M * N1)
+            self.nsets = max(1, math.ceil(COLD_BYTES / per_set)) if cold else 1
+            A = t(d["A"])
+            self.X = [A] + [A.clone() for _ in range(self.nsets - 1)]
+            self.Y = [torch.empty((M, N1), dtype=torch.float16, device=dev) for _ in range(self.nsets)]
+            self.H = torch.empty((M, N0), dtype=torch.float16, device=dev)
+            self.config = {"workload": name, "M": M, "K0": K0, "N0": N0, "N1": N1, "act": self.act,
+                           "variant": "rf" if name != "b2b_gemm_lds" else "lds",
+                           "dist": s["dist"] + "(-1,1)/sqrt(K)" if s["dist"] == "uniform" else "normal(0,1)/sqrt(K)"}
+            self.kernel = "k_chain_rf" if self.config["variant"] == "rf" else "k_gemm_lds"
+        elif s["kind"] == "conv2":
+            n, h, w, c, k0, k1 = s["n"], s["h"], s["w"], s["c"], s["k0"], s["k1"]
+            npix = n * h * w
+            self.flops = 2 * npix * (9 * c * k0 + k0 * k1)
+            self.flops_exec = self.flops
+            wbytes = 2 * (9 * c * k0 + k0 + k0 * k1 + k1)
+            self.bytes_fused = 2 * (npix * c + npix * k1) + wbytes
+            self.bytes_interm = 2 * npix * k0
+            self.W = [t(d["w0"]), t(d["b0"]), t(d["w1"]), t(d["b1"])]
+            per_set = 2 * (npix * c + npix * k1)
+            self.nsets = max(1, math.ceil(COLD_BYTES / per_set)) if cold else 1
+            x = t(d["x"])
+            self.X = [x] + [x.clone() for _ in range(self.nsets - 1)]
+            self.Y = [torch.empty((n, h, w, k1), dtype=torch.float16, device=dev) for _ in range(self.nsets)]
+            self.H = torch.empty((n, h, w, k0), dtype=torch.float16, device=dev)
+            self.config = {"workload": name, "x": [n, h, w, c], "conv0": "3x3 s1 p1 %d->%d +b ReLU" % (c, k0),
+                           "conv1": "1x1 %d->%d +b" % (k0, k1)}
+            self.kernel = "k_chain_rf"
+        else:
+            n, h, w, c, cp, k = s["n"], s["h"], s["w"], s["c"], s["cpad"], s["k"]
+            npix = n * h * w
+            self.flops = 2 * npix * k * 9 * c               # algorithmic: the 60 real channels
+            self.flops_exec = 2 * npix * k * 9 * cp         # executed: padded to 64
+            npool = n * (h // 2) * (w // 2)
+            self.bytes_fused = 2 * (npix * cp + 9 * cp * k + k + npool * k)
+            self.bytes_interm = 2 * npix * k
+            xp = fc.pad_channels(t(d["x"]), cp)             # input preparation, outside the timed chain
+            wp = fc.pad_weight_channels(t(d["w"]), cp)
+            self.W = [wp, t(d["b"])]
+            per_set = 2 * (npix * cp + npool * k)
+            self.nsets = max(1, math.ceil(COLD_BYTES / per_set)) if cold else 1
+            self.X = [xp] + [xp.clone() for _ in range(self.nsets - 1)]
+            self.Y = [torch.empty((n, h // 2, w // 2, k), dtype=torch.float16, device=dev) for _ in range(self.nsets)]
+            self.H = torch.empty((n, h, w, k), dtype=torch.float16, device=dev)
+            self.config = {"workload": name, "x": [n, h, w, c], "channels_padded_to": cp,
+                           "conv": "3x3 s1 p1 %d->%d +b ReLU" % (c, k), "pool": "max 2x2 s2"}
+            self.kernel = "k_conv_w"
+        torch.cuda.synchronize()
+
+    def step(self, i):
+        fc, j, s = self.fc, i % self.nsets, self.spec
+        if s["kind"] == "gemm2":
+            W0, b0, W1, b1 = self.W
+            fc.chain_gemm2(self.X[j], W0, b0, W1, b1, act=self.act, out=self.Y[j])
+        elif s["kind"] == "conv2":
+            w0, b0, w1, b1 = self.W
+            fc.chain_conv2(self.X[j], w0, b0, w1, b1, act="relu", out=self.Y[j])
+        else:
+            w, b = self.W
+            fc.chain_conv_pool(self.X[j], w, b, act="relu", pool="max2x2", out=self.Y[j])
+
+    def step_unfused(self, i):
+        """The two-kernel baseline: the intermediate goes to HBM and back."""
+        fc, j, s = self.fc, i % self.nsets, self.spec
+        if s["kind"] == "gemm2":
+            W0, b0, W1, b1 = self.W
+            fc.gemm_bias_act(self.X[j], W0, b0, act=self.act, out=self.H)
+            fc.gemm_bias_act(self.H, W1, b1, act="none", out=self.Y[j])
+        elif s["kind"] == "conv2":
+            w0, b0, w1, b1 = self.W
+            fc.conv_bias_act(self.X[j], w0, b0, act="relu", out=self.H)
+            k0 = self.H.shape[-1]
+            fc.gemm_bias_act(self.H.view(-1, k0), w1, b1, act="none", out=self.Y[j].view(-1, self.Y[j].shape[-1]))
+        else:
+            w, b = self.W
+            fc.conv_bias_act(self.X[j], w, b, act="relu", out=self.H)
+            fc.maxpool2x2(self.H, out=self.Y[j])
+
+
+def time_steps(torch, fn, steps, warmup):
+    """(ms per step over the timed region, mean per-launch ms, wall ms per step)."""
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    w0 = time.perf_counter()
+    t0.record()
+    for i in range(steps):
+        ev[i][0].record()
+        fn(warmup + i)
+        ev[i][1].record()
+    t1.record()
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - w0) * 1e3 / steps
+    per = [a.elapsed_time(b) for a, b in ev]
+    return t0.elapsed_time(t1) / steps, sum(per) / len(per), wall
+
+
+def cpu_baseline(prob, seconds):
+    """The oracle, as it stands, on a bounded sample of the same workload."""
+    import numpy as np
+
+    import oracle
+    s, d = prob.spec, prob.host
+    cores = oracle.num_threads()
+    actk = {"relu": oracle.ACT_RELU, "gelu_tanh": oracle.ACT_GELU_TANH, "none": oracle.ACT_NONE}
+    if s["kind"] == "gemm2":
+        M = s["M"]
+        per_row = prob.flops / M
+
+        def run(rows):
+            t = time.perf_counter()
+            oracle.chain_gemm2(d["A"][:rows], d["W0"], d["b0"], actk[s["act"]], d["W1"], d["b1"])
+            return time.perf_counter() - t
+
+        probe = min(M, 2048)
+        tp = run(probe)
+        rows = int(min(M, max(probe, probe * seconds / max(tp, 1e-6))))
+        t = run(rows) if rows != probe else tp
+        return {"value": per_row * rows / t / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+                "sample": "first %d of %d rows (fp64, unfused, same seeded inputs)" % (rows, M),
+                "seconds": round(t, 3)}
+    n = s["n"]
+    per_img = prob.flops / n
+
+    def run(imgs):
+        t = time.perf_counter()
+        if s["kind"] == "conv2":
+            oracle.chain_conv2(d["x"][:imgs], d["w0"], d["b0"], oracle.ACT_RELU, d["w1"], d["b1"])
+        else:
+            oracle.chain_conv_pool(d["x"][:imgs], d["w"], d["b"], oracle.ACT_RELU)
+        return time.perf_counter() - t
+
+    tp = run(1)
+    imgs = int(min(n, max(1, seconds / max(tp, 1e-6))))
+    t = run(imgs) if imgs != 1 else tp
+    return {"value": per_img * imgs / t / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": "first %d of %d images (fp64, unfused, same seeded inputs)" % (imgs, n),
+            "seconds": round(t, 3)}
+
+
+def measured_traffic(name, kernel_hash):
+    """HBM bytes per launch from the committed rocprofv3 PMC summary, if it
+    was taken on the current kernel sources; else None."""
+    p = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(p):
+        return None
+    with open(p) as f:
+        db = json.load(f)
+    e = db.get("workloads", {}).get(name)
+    if not e or e.get("src_hash") != kernel_hash:
+        return None
+    return e
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="b2b_gemm_rf",
+                    choices=["b2b_gemm_tiny", "b2b_gemm_rf", "b2b_gemm_lds", "conv3x3_conv1x1",
+                             "conv3x3_relu_maxpool"])
+    ap.add_argument("--warm", action="store_true", help="reuse one buffer set (cache-warm timing)")
+    ap.add_argument("--no-unfused", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="also run one 256 MiB device copy (known bytes, for PMC counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print("bench.py: this build measures one GPU only (the fused chain needs no collectives; "
+              "--gpus %d is not supported)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    import gemm_conv_chain_amd as fc
+    fc.lib()
+
+    prob = Problem(args.workload, cold=not args.warm)
+    log("workload %s: %d buffer set(s), %.1f MB fused algorithmic bytes, %.3f GFLOP"
+        % (args.workload, prob.nsets, prob.bytes_fused / 1e6, prob.flops / 1e9))
+
+    ms_step, ms_kernel, ms_wall = time_steps(torch, prob.step, args.steps, args.warmup)
+    log("fused:   %.4f ms/step (events), kernel %.4f ms, wall %.4f ms" % (ms_step, ms_kernel, ms_wall))
+
+    unfused = None
+    if not args.no_unfused:
+        u_step, u_kernel, _ = time_steps(torch, prob.step_unfused, max(5, args.steps // 2), 2)
+        ub = prob.bytes_fused + 2 * prob.bytes_interm
+        unfused = {"ms_per_step": round(u_step, 5), "algorithmic_bytes": ub,
+                   "fused_over_unfused_bytes": round(prob.bytes_fused / ub, 4),
+                   "speedup_fused": round(u_step / ms_step, 3)}
+        log("unfused: %.4f ms/step -> fused speedup %.2fx" % (u_step, u_step / ms_step))
+
+    if args.calib_copy:
+        src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        src.fill_(1)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+
+    tflops = prob.flops / (ms_step * 1e-3) / 1e12
+    ai = prob.flops / prob.bytes_fused
+    ksec = ms_kernel * 1e-3
+    h = kernel_src_hash()
+    tr = measured_traffic(args.workload, h)
+    traffic = None
+    if tr is not None:
+        traffic = int(tr["fetch_kib"] * tr["fetch_scale"] * 1024 + tr["write_kib"] * tr["write_scale"] * 1024)
+        if unfused is not None and "unfused_bytes" in tr:
+            unfused["measured_bytes"] = tr["unfused_bytes"]
+            unfused["measured_fused_over_unfused"] = round(traffic / tr["unfused_bytes"], 4)
+    if ai < RIDGE:
+        achieved = prob.bytes_fused / ksec / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic}
+    else:
+        achieved = prob.flops / ksec / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": round(PEAK_F16_TFLOPS, 1),
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK_F16_TFLOPS, 4), "traffic": traffic}
+    roof.update({"kernel": prob.kernel, "kernel_ms": round(ms_kernel, 5), "flop_per_byte": round(ai, 1),
+                 "algorithmic_bytes": prob.bytes_fused, "algorithmic_flops": prob.flops,
+                 "executed_flops": prob.flops_exec})
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(prob, args.cpu_seconds)
+        log("oracle:  %.5f TFLOP/s on %d threads (%s)" % (cpu["value"], cpu["cores"], cpu["sample"]))
+
+    out = {
+        "metric": METRIC, "value": round(tflops, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f16", "accumulate": "f32", "data": "synthetic",
+        "config": dict(prob.config, cache="cold (rotating %d buffer sets)" % prob.nsets if prob.nsets > 1 else "warm"),
+        "pct_fp16_mfma_peak": round(100 * tflops / PEAK_F16_TFLOPS, 2),
+        "roofline": roof, "unfused": unfused, "cpu_baseline": cpu, "kernel_src": h,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
