@@ -16,9 +16,10 @@
 //   * The GEMM0 accumulator gives lane (m, h) the values of its row m at
 //     n0 = 32t + 8(r/4) + 4h + (r%4).  Packed to fp16 after bias+act, 8 of them
 //     form the operand-B register of GEMM1 for k-step s = 2t + r/8 -- no data
-//     leaves the lane.  GEMM1's operand A (W1^T) is staged in LDS with the
-//     matching permutation of its k index (PERM16 in the transposed staging).
-//   * W0^T, W1^T and the biases live in LDS for the whole kernel; the grid is
+//     leaves the lane.  GEMM1's operand A (W1^T) fragments are read with the
+//     matching permutation of the k rows.
+//   * W0, W1 (natural row-major layout, read as transposed fragments with
+//     ds_read_b64_tr_b16) and the biases live in LDS for the whole kernel; the grid is
 //     persistent (about one block per CU), each block owning a contiguous range
 //     of 32-row tiles that its waves take in turn.
 //   * X is loaded in 64-wide k chunks: lane half h reads 64 contiguous bytes
@@ -49,85 +50,151 @@ struct RfArgs {
     long tiles_per_block;
 };
 
-// LDS bytes used by the RF kernel for a given padded problem.
+// Per-wave output staging tile: 32 rows x 64 columns (+8 halves of padding).
+constexpr int RF_OLD = 64 + 8;
+constexpr size_t RF_OSTAGE_BYTES = (size_t)RF_WAVES * 32 * RF_OLD * 2;
+
+// LDS bytes used by the RF kernel for a given padded problem: W0 and W1 in
+// their natural layout (rows = k), the biases, the per-wave output tiles.
 inline size_t rf_lds_bytes(int N0P, int K0p, int N1p)
 {
-    return (size_t)N0P * (K0p + 8) * 2 + (size_t)N1p * (N0P + 8) * 2 + (size_t)(N0P + N1p) * 4;
+    return (size_t)K0p * wtile_ld(N0P) * 2 + (size_t)N0P * wtile_ld(N1p) * 2 + (size_t)(N0P + N1p) * 4 +
+           RF_OSTAGE_BYTES;
 }
 
-template <int NT0, class Loader>
-__global__ __launch_bounds__(RF_THREADS) void k_chain_rf(Loader ld, RfArgs a)
+// KCH: compile-time number of 64-wide k chunks (0 = runtime loop); with a
+// known count the chunk loop unrolls fully and every load is waited for
+// exactly where its data is used.
+// One block per CU (its LDS holds both weight matrices), 8 waves: 2 waves per
+// SIMD.  Saying so lets the scheduler spend registers on loads in flight
+// instead of shrinking them for an occupancy the LDS use rules out.
+template <int NT0, int KCH, class Loader>
+__global__ __launch_bounds__(RF_THREADS) __attribute__((amdgpu_waves_per_eu(1, 2)))
+void k_chain_rf(Loader ld, RfArgs a)
 {
     constexpr int N0P = 32 * NT0;
     extern __shared__ __align__(16) char smem[];
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int lr = lane & 31, hh = lane >> 5;
-    const int ldw0 = a.K0p + 8, ldw1 = N0P + 8;
-    half_t* W0t = reinterpret_cast<half_t*>(smem);
-    half_t* W1t = W0t + N0P * ldw0;
-    float* b0s = reinterpret_cast<float*>(W1t + a.N1p * ldw1);
-    float* b1s = b0s + N0P;
+    typedef FC_LDS float lds_float;
+    typedef FC_LDS half4 lds_half4;
+    WTile W0n, W1n;   // natural layouts: W0n [K0p][N0P], W1n [N0P][N1p]
+    W0n.p = (lds_half*)smem;
+    W0n.ld = wtile_ld(N0P);
+    W0n.swz = wtile_swz(N0P);
+    W1n.p = W0n.p + a.K0p * W0n.ld;
+    W1n.ld = wtile_ld(a.N1p);
+    W1n.swz = wtile_swz(a.N1p);
+    lds_float* b0s = (lds_float*)(W1n.p + N0P * W1n.ld);
+    lds_float* b1s = b0s + N0P;
+    lds_half* Ost = (lds_half*)(b1s + a.N1p) + wave * 32 * RF_OLD;
 
     const long t_begin = (long)blockIdx.x * a.tiles_per_block;
     const long t_end = min(t_begin + a.tiles_per_block, a.ntiles);
-    const int nch = a.K0p >> 6;
+    const int nch = KCH ? KCH : a.K0p >> 6;
 
-    // Start the row stream before staging the weights so HBM is busy at once.
+    // Row chunks are held in a ring of R register sets.  With a compile-time
+    // chunk count (KCH > 0) the chunk loop is fully unrolled and chunk c lives
+    // in set c % R, so the ring rotates by name: PD = R - 1 chunks are always
+    // in flight ahead of the one being multiplied (for K0 = 256 that is the
+    // whole tile).  Loaded-HBM latency is far longer than the MFMA work of one
+    // chunk, so the depth, not the MFMA rate, sets the speed here.  KCH == 0
+    // (runtime chunk count) falls back to a two-set ring.
+    constexpr int R = KCH >= 4 ? 4 : (KCH > 0 ? KCH : 2);
+    constexpr int PD = R - 1;
     long tile = t_begin + wave;
-    half8 cur[4];
+    half8 xr[R][4];
     typename Loader::Row row;
-    if (tile < t_end) {
-        row = ld.row(tile * 32 + lr);
-        ld.load(row, 0, hh, cur);
-    }
-
-    stage_transposed<false>(a.W0, a.K0, a.N0, a.N0, 0, a.K0p, N0P, W0t, ldw0, tid, RF_THREADS);
-    stage_transposed<true>(a.W1, a.N0, a.N1, a.N1, 0, N0P, a.N1p, W1t, ldw1, tid, RF_THREADS);
-    for (int i = tid; i < N0P + a.N1p; i += RF_THREADS) {
-        float v = 0.0f;
-        if (i < N0P) {
-            if (a.b0 && i < a.N0) v = (float)a.b0[i];
-            b0s[i] = v;
-        } else {
-            const int j = i - N0P;
-            if (a.b1 && j < a.N1) v = (float)a.b1[j];
-            b1s[j] = v;
+    // Loads complete in issue order as far as a wave's wait counter is
+    // concerned, so a wave that already streams its rows cannot stage weights
+    // without waiting for those rows.  The first half of the waves therefore
+    // stages W0^T, W1^T and the biases while the second half starts its row
+    // stream at once; the stagers start theirs after the barrier (each SIMD
+    // hosts one wave of each half).
+    constexpr int NSTAGE = RF_THREADS / 2;
+    const bool stager = tid < NSTAGE;
+    auto start_rows = [&]() {
+        if (tile < t_end) {
+            row = ld.row(tile * 32 + lr);
+#pragma unroll
+            for (int p = 0; p < PD; ++p)
+                if (p < nch) ld.load(row, p, hh, xr[p]);
+        }
+    };
+    if (!stager) start_rows();
+    if (stager) {
+        stage_natural<8>(a.W0, a.K0, a.N0, a.N0, a.K0p, N0P, W0n, tid, NSTAGE);
+        stage_natural<8>(a.W1, a.N0, a.N1, a.N1, N0P, a.N1p, W1n, tid, NSTAGE);
+        for (int i = tid; i < N0P + a.N1p; i += NSTAGE) {
+            float v = 0.0f;
+            if (i < N0P) {
+                if (a.b0 && i < a.N0) v = (float)a.b0[i];
+                b0s[i] = v;
+            } else {
+                const int j = i - N0P;
+                if (a.b1 && j < a.N1) v = (float)a.b1[j];
+                b1s[j] = v;
+            }
         }
     }
     __syncthreads();
+    if (stager) start_rows();
+
+    // Per-lane parts of the fragment addresses (row bases 32hh / 4hh folded in).
+    const lds_half* w0lane[NT0];
+#pragma unroll
+    for (int t = 0; t < NT0; ++t) w0lane[t] = W0n.p + frag_lane_off(W0n, 32 * t, lane) + 32 * hh * W0n.ld;
+    const lds_half* w1lane[2];
+#pragma unroll
+    for (int t1 = 0; t1 < 2; ++t1) w1lane[t1] = W1n.p + frag_lane_off(W1n, 32 * t1, lane) + 4 * hh * W1n.ld;
 
     for (; tile < t_end; tile += RF_WAVES) {
-        const long m = tile * 32 + lr;
         floatx16 acc0[NT0];
 #pragma unroll
         for (int t = 0; t < NT0; ++t) acc0[t] = zero16();
 
-        for (int c = 0; c < nch; ++c) {
-            half8 nxt[4];
-            const bool more = c + 1 < nch;
-            if (more) ld.load(row, c + 1, hh, nxt);
-            const half_t* wbase = W0t + lr * ldw0 + 64 * c + 32 * hh;
+        // W0^T fragment for k = 64c + 32hh + 8q + j (the rows this lane's
+        // 16-byte loads of X cover) and n0 = 32t + lane%32.
+        auto mma_chunk = [&](int c, const half8 (&cur)[4]) {
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
 #pragma unroll
                 for (int t = 0; t < NT0; ++t) {
-                    const half8 w = *reinterpret_cast<const half8*>(wbase + 32 * t * ldw0 + 8 * q);
+                    const half8 w = frag_tr_at(w0lane[t] + (64 * c + 8 * q) * W0n.ld, 4 * W0n.ld);
                     acc0[t] = mfma32x32x16(w, cur[q], acc0[t]);
                 }
             }
-            if (more) {
+        };
+        if constexpr (KCH > 0) {
 #pragma unroll
-                for (int q = 0; q < 4; ++q) cur[q] = nxt[q];
+            for (int c = 0; c < KCH; ++c) {
+                if (c + PD < KCH) ld.load(row, c + PD, hh, xr[(c + PD) % R]);
+                __builtin_amdgcn_sched_barrier(0);   // keep the prefetch issued here
+                mma_chunk(c, xr[c % R]);
+            }
+        } else {
+            for (int c = 0; c < nch; c += 2) {
+                if (c + 1 < nch) ld.load(row, c + 1, hh, xr[1]);
+                __builtin_amdgcn_sched_barrier(0);
+                mma_chunk(c, xr[0]);
+                if (c + 1 < nch) {
+                    if (c + 2 < nch) ld.load(row, c + 2, hh, xr[0]);
+                    __builtin_amdgcn_sched_barrier(0);
+                    mma_chunk(c + 1, xr[1]);
+                }
             }
         }
 
-        // Put the next tile's first chunk in flight before the epilogues.
+        // Put the next tile's first chunks in flight (every set is free once
+        // the last chunk's MFMAs are issued) before the epilogues.
         const long ntile = tile + RF_WAVES;
         typename Loader::Row nrow = row;
         if (ntile < t_end) {
             nrow = ld.row(ntile * 32 + lr);
-            ld.load(nrow, 0, hh, cur);
+#pragma unroll
+            for (int p = 0; p < PD; ++p)
+                if (p < nch) ld.load(nrow, p, hh, xr[p]);
         }
 
         // Epilogue 0 in registers: bias (broadcast along rows), activation,
@@ -148,31 +215,32 @@ __global__ __launch_bounds__(RF_THREADS) void k_chain_rf(Loader ld, RfArgs a)
             floatx16 acc1[2];
             acc1[0] = zero16();
             acc1[1] = zero16();
-            const half_t* w1base = W1t + (n1c + lr) * ldw1 + 8 * hh;
+            // hf[s] element j holds n0 = 16s + 8(j/4) + 4hh + j%4, so the W1^T
+            // fragment reads rows 16s + 4hh + [0,4) and 16s + 8 + 4hh + [0,4).
 #pragma unroll
             for (int s = 0; s < 2 * NT0; ++s) {
 #pragma unroll
                 for (int t1 = 0; t1 < 2; ++t1) {
-                    const half8 w = *reinterpret_cast<const half8*>(w1base + 32 * t1 * ldw1 + 16 * s);
+                    const half8 w = frag_tr_at(w1lane[t1] + n1c + 16 * s * W1n.ld, 8 * W1n.ld);
                     acc1[t1] = mfma32x32x16(w, hf[s], acc1[t1]);
                 }
             }
-            if (m < a.M) {
-                half_t* orow = a.out + m * (long)a.N1;
+            // + b1, fp16 into this wave's LDS tile, then whole-line stores:
+            // each store instruction writes 8 rows x 128 contiguous bytes.
 #pragma unroll
-                for (int t1 = 0; t1 < 2; ++t1) {
+            for (int t1 = 0; t1 < 2; ++t1) {
 #pragma unroll
-                    for (int g = 0; g < 4; ++g) {
-                        const int n1 = n1c + 32 * t1 + 8 * g + 4 * hh;
-                        if (n1 < a.N1) {
-                            half4 o;
+                for (int g = 0; g < 4; ++g) {
+                    const int nl = 32 * t1 + 8 * g + 4 * hh;
+                    half4 o;
 #pragma unroll
-                            for (int e = 0; e < 4; ++e) o[e] = (half_t)(acc1[t1][4 * g + e] + b1s[n1 + e]);
-                            *reinterpret_cast<half4*>(orow + n1) = o;
-                        }
-                    }
+                    for (int e = 0; e < 4; ++e) o[e] = (half_t)(acc1[t1][4 * g + e] + b1s[n1c + nl + e]);
+                    *reinterpret_cast<lds_half4*>(Ost + lr * RF_OLD + nl) = o;
                 }
             }
+            wave_lds_sync();
+            store_tile(Ost, RF_OLD, 32, 64, a.out, a.N1, tile * 32, a.M, n1c, a.N1, lane, 64);
+            wave_lds_sync();
         }
         row = nrow;
     }
@@ -198,17 +266,19 @@ struct DenseRows {
     {
         const int k0 = 64 * c + 32 * hh;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) out[q] = ld16_if(r.p + k0 + 8 * q, r.ok && (k0 + 8 * q) < K);
+        for (int q = 0; q < 4; ++q) {
+            out[q] = ld16_if(r.p + k0 + 8 * q, r.ok && (k0 + 8 * q) < K);
+        }
     }
 };
 
 // ----------------------------------------------------------------- launch
 
-template <int NT0, class Loader>
-static hipError_t launch_rf_t(const Loader& ld, RfArgs a, hipStream_t st)
+template <int NT0, int KCH, class Loader>
+static hipError_t launch_rf_k(const Loader& ld, RfArgs a, hipStream_t st)
 {
     const size_t lds = rf_lds_bytes(32 * NT0, a.K0p, a.N1p);
-    hipError_t e = hipFuncSetAttribute((const void*)k_chain_rf<NT0, Loader>,
+    hipError_t e = hipFuncSetAttribute((const void*)k_chain_rf<NT0, KCH, Loader>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     const long per_block_min = RF_WAVES;  // at least one tile per wave
@@ -217,8 +287,20 @@ static hipError_t launch_rf_t(const Loader& ld, RfArgs a, hipStream_t st)
     if (grid < 1) grid = 1;
     a.tiles_per_block = (a.ntiles + grid - 1) / grid;
     grid = (a.ntiles + a.tiles_per_block - 1) / a.tiles_per_block;
-    hipLaunchKernelGGL((k_chain_rf<NT0, Loader>), dim3((unsigned)grid), dim3(RF_THREADS), lds, st, ld, a);
+    hipLaunchKernelGGL((k_chain_rf<NT0, KCH, Loader>), dim3((unsigned)grid), dim3(RF_THREADS), lds, st, ld, a);
     return hipGetLastError();
+}
+
+// Compile-time chunk counts for the k lengths in use (64, 256, 576).
+template <int NT0, class Loader>
+static hipError_t launch_rf_t(const Loader& ld, const RfArgs& a, hipStream_t st)
+{
+    switch (a.K0p >> 6) {
+    case 1: return launch_rf_k<NT0, 1>(ld, a, st);
+    case 4: return launch_rf_k<NT0, 4>(ld, a, st);
+    case 9: return launch_rf_k<NT0, 9>(ld, a, st);
+    }
+    return launch_rf_k<NT0, 0>(ld, a, st);
 }
 
 template <class Loader>
@@ -232,6 +314,5 @@ inline hipError_t launch_rf(const Loader& ld, const RfArgs& a, int nt0, hipStrea
     }
     return hipErrorInvalidValue;
 }
-
 
 }  // namespace fc

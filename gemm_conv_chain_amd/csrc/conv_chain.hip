@@ -80,7 +80,7 @@ struct ConvWArgs {
 
 inline size_t convw_lds_bytes(int KP, int Kp)
 {
-    return (size_t)KP * (Kp + 8) * 2 + (size_t)KP * 4 + 16;
+    return (size_t)Kp * wtile_ld(KP) * 2 + (size_t)KP * 4 + 16;
 }
 
 // One wave = 64 GEMM rows (two 32-row MFMA tiles) x all K output channels.
@@ -90,23 +90,30 @@ inline size_t convw_lds_bytes(int KP, int Kp)
 // rows 4g'..4g'+3 of a 32x32 tile into one lane's registers 4g..4g+3, i.e. a
 // whole window, so the pool is three max operations in registers.
 // Non-transposed MFMA: operand A = pixel rows (16-byte loads from x), operand
-// B = W^T rows from LDS.
-template <int NTK, int EPI>
-__global__ __launch_bounds__(CW_THREADS) void k_conv_w(ConvWArgs a)
+// B = W fragments read from the natural (HWIO = [(r,s,c)][k]) LDS copy of the
+// weights with the transposing LDS load.
+// KCH: compile-time number of 64-wide k chunks (0 = runtime loop), see the
+// register-resident chain kernel.
+template <int NTK, int EPI, int KCH>
+__global__ __launch_bounds__(CW_THREADS) __attribute__((amdgpu_waves_per_eu(1, 2)))
+void k_conv_w(ConvWArgs a)
 {
     constexpr int KP = 32 * NTK;
     extern __shared__ __align__(16) char smem[];
-    const int ldw = a.Kp + 8;
-    half_t* Wt = reinterpret_cast<half_t*>(smem);
-    float* bs = reinterpret_cast<float*>(Wt + KP * ldw);
-    int* next_tile = reinterpret_cast<int*>(bs + KP);
+    typedef FC_LDS float lds_float;
+    WTile Wn;   // natural layout [Kp][KP] (rows = (r, s, c))
+    Wn.p = (lds_half*)smem;
+    Wn.ld = wtile_ld(KP);
+    Wn.swz = wtile_swz(KP);
+    lds_float* bs = (lds_float*)(Wn.p + a.Kp * Wn.ld);
+    FC_LDS int* next_tile = (FC_LDS int*)(bs + KP);
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int lr = lane & 31, hh = lane >> 5;
     const long t_begin = (long)blockIdx.x * a.tiles_per_block;
     const long t_end = min(t_begin + a.tiles_per_block, a.ntiles);
-    const int nch = a.Kp >> 6;
+    const int nch = KCH ? KCH : a.Kp >> 6;
     const int PO = a.H >> 1, QO = a.W >> 1;
     const long nrows = EPI == EPI_POOL ? (long)a.NB * PO * QO * 4 : (long)a.NB * a.H * a.W;
 
@@ -137,21 +144,29 @@ __global__ __launch_bounds__(CW_THREADS) void k_conv_w(ConvWArgs a)
         return r;
     };
 
+    // Chunks alternate between two register sets by name (chunk c in set
+    // c % 2, loop unrolled by two): no loaded register is ever copied.
     long tile = t_begin + wave;
     Conv3x3Rows::Row rows[2];
-    half8 cur[2][4];
+    half8 xa[2][4], xb[2][4];
     if (tile < t_end) {
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
             rows[u] = make_row(tile * 64 + 32 * u + lr);
-            ld.load(rows[u], 0, hh, cur[u]);
+            ld.load(rows[u], 0, hh, xa[u]);
         }
     }
 
-    stage_transposed<false>(a.w, a.Kr, a.K, a.K, 0, a.Kp, KP, Wt, ldw, tid, CW_THREADS);
+    stage_natural<8>(a.w, a.Kr, a.K, a.K, a.Kp, KP, Wn, tid, CW_THREADS);
     for (int i = tid; i < KP; i += CW_THREADS) bs[i] = (a.b && i < a.K) ? (float)a.b[i] : 0.0f;
     if (tid == 0) *next_tile = (int)(t_begin + CW_WAVES);
     __syncthreads();
+
+    // Per-lane parts of the W fragment addresses: column k_out = 32t + lane%32,
+    // rows 64c + 32hh + 8q + [0,8) (the k this lane's pixel loads cover).
+    const lds_half* wlane[NTK];
+#pragma unroll
+    for (int t = 0; t < NTK; ++t) wlane[t] = Wn.p + frag_lane_off(Wn, 32 * t, lane) + 32 * hh * Wn.ld;
 
     while (tile < t_end) {
         floatx16 acc[2][NTK];
@@ -160,35 +175,31 @@ __global__ __launch_bounds__(CW_THREADS) void k_conv_w(ConvWArgs a)
 #pragma unroll
             for (int t = 0; t < NTK; ++t) acc[u][t] = zero16();
 
-        for (int c = 0; c < nch; ++c) {
-            const bool more = c + 1 < nch;
-            half8 nxt[2][4];
-            if (more) {
+        auto step = [&](int c, const half8 (&cur)[2][4], half8 (&nxt)[2][4]) {
+            if (c + 1 < nch) {
                 ld.load(rows[0], c + 1, hh, nxt[0]);
                 ld.load(rows[1], c + 1, hh, nxt[1]);
             }
-            const half_t* wb = Wt + lr * ldw + 64 * c + 32 * hh;
+            __builtin_amdgcn_sched_barrier(0);   // keep the prefetch issued here
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
 #pragma unroll
                 for (int t = 0; t < NTK; ++t) {
-                    const half8 wv = *reinterpret_cast<const half8*>(wb + 32 * t * ldw + 8 * q);
+                    const half8 wv = frag_tr_at(wlane[t] + (64 * c + 8 * q) * Wn.ld, 4 * Wn.ld);
                     acc[0][t] = mfma32x32x16(cur[0][q], wv, acc[0][t]);
                     acc[1][t] = mfma32x32x16(cur[1][q], wv, acc[1][t]);
                 }
             }
-            if (more) {
+        };
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    cur[0][q] = nxt[0][q];
-                    cur[1][q] = nxt[1][q];
-                }
-            }
+        for (int c = 0; c < nch; c += 2) {
+            step(c, xa, xb);
+            if (c + 1 < nch) step(c + 1, xb, xa);
         }
 
         // Claim the next tile and put its first chunk in flight.
         int nt = 0;
-        if (lane == 0) nt = atomicAdd(next_tile, 1);
+        if (lane == 0) nt = __hip_atomic_fetch_add(next_tile, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
         nt = __shfl(nt, 0);
         const long ntile = nt;
         Conv3x3Rows::Row nrows_[2] = {rows[0], rows[1]};
@@ -196,7 +207,7 @@ __global__ __launch_bounds__(CW_THREADS) void k_conv_w(ConvWArgs a)
 #pragma unroll
             for (int u = 0; u < 2; ++u) {
                 nrows_[u] = make_row(ntile * 64 + 32 * u + lr);
-                ld.load(nrows_[u], 0, hh, cur[u]);
+                ld.load(nrows_[u], 0, hh, xa[u]);
             }
         }
 
@@ -244,11 +255,11 @@ __global__ __launch_bounds__(CW_THREADS) void k_conv_w(ConvWArgs a)
     }
 }
 
-template <int NTK, int EPI>
-static hipError_t launch_convw_t(ConvWArgs a, hipStream_t st)
+template <int NTK, int EPI, int KCH>
+static hipError_t launch_convw_k(ConvWArgs a, hipStream_t st)
 {
     const size_t lds = convw_lds_bytes(32 * NTK, a.Kp);
-    hipError_t e = hipFuncSetAttribute((const void*)k_conv_w<NTK, EPI>,
+    hipError_t e = hipFuncSetAttribute((const void*)k_conv_w<NTK, EPI, KCH>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     long grid = device_cu_count();
@@ -256,8 +267,15 @@ static hipError_t launch_convw_t(ConvWArgs a, hipStream_t st)
     if (grid < 1) grid = 1;
     a.tiles_per_block = (a.ntiles + grid - 1) / grid;
     grid = (a.ntiles + a.tiles_per_block - 1) / a.tiles_per_block;
-    hipLaunchKernelGGL((k_conv_w<NTK, EPI>), dim3((unsigned)grid), dim3(CW_THREADS), lds, st, a);
+    hipLaunchKernelGGL((k_conv_w<NTK, EPI, KCH>), dim3((unsigned)grid), dim3(CW_THREADS), lds, st, a);
     return hipGetLastError();
+}
+
+template <int NTK, int EPI>
+static hipError_t launch_convw_t(ConvWArgs a, hipStream_t st)
+{
+    if ((a.Kp >> 6) == 9) return launch_convw_k<NTK, EPI, 9>(a, st);   // C = 64
+    return launch_convw_k<NTK, EPI, 0>(a, st);
 }
 
 template <int EPI>

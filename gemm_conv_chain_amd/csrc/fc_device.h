@@ -22,6 +22,12 @@ typedef _Float16 half4 __attribute__((ext_vector_type(4)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 
+// Pointers into LDS carry address space 3 explicitly, so every access compiles
+// to a ds_* instruction (a generic pointer would be a flat access or need a
+// null-checked cast at each use).
+#define FC_LDS __attribute__((address_space(3)))
+typedef FC_LDS half_t lds_half;
+
 enum { ACT_NONE = 0, ACT_RELU = 1, ACT_GELU_TANH = 2 };
 
 __device__ __forceinline__ floatx16 mfma32x32x16(half8 a, half8 b, floatx16 c)
@@ -51,9 +57,25 @@ __device__ __forceinline__ half8 ld16(const half_t* p)
     return *reinterpret_cast<const half8*>(p);
 }
 
+// 64 bytes of zeros in device (global) memory: masked-off lanes load from
+// here.  Never written; non-const so that it lives in the global address space
+// like the tensors (a pointer select between address spaces would turn the
+// loads into flat loads, which also occupy the LDS wait counter).
+static __device__ __align__(64) unsigned int fc_zero_line[16];
+
+__device__ __forceinline__ const half_t* zero_ptr()
+{
+    return reinterpret_cast<const half_t*>(fc_zero_line);
+}
+
+// Branch-free masked 16-byte load: lanes with !ok read the zero line instead
+// of p.  The choice is made on the address, before the load, so nothing
+// consumes the loaded value early: the load stays in flight until the MFMA
+// that needs it (a select on the VALUE would force a wait right after the
+// load and expose its full latency).
 __device__ __forceinline__ half8 ld16_if(const half_t* p, bool ok)
 {
-    return ok ? ld16(p) : zero8();
+    return ld16(ok ? p : zero_ptr());
 }
 
 // Element-wise activation in fp32 (the epilogue's element-wise operator).
@@ -101,12 +123,12 @@ __device__ __forceinline__ void tblock_load(const half_t* __restrict__ G, int ro
     for (int i = 0; i < 4; ++i) {
         const int r = r0 + br * 4 + i;
         const bool ok = r < rows && c0 < cols;
-        b.v[i] = ok ? *reinterpret_cast<const u32x4*>(G + (long)r * ldg + c0) : u32x4{0u, 0u, 0u, 0u};
+        b.v[i] = *reinterpret_cast<const u32x4*>(ok ? G + (long)r * ldg + c0 : zero_ptr());
     }
 }
 
 template <bool PERM16>
-__device__ __forceinline__ void tblock_store(half_t* T, int ldt, int ncp, int blk, const TBlock& b)
+__device__ __forceinline__ void tblock_store(lds_half* T, int ldt, int ncp, int blk, const TBlock& b)
 {
     const int nbc = ncp >> 3;
     const int br = blk / nbc, bc = blk - br * nbc;
@@ -125,14 +147,14 @@ __device__ __forceinline__ void tblock_store(half_t* T, int ldt, int ncp, int bl
         lo.y = __builtin_amdgcn_perm(b.v[3][d], b.v[2][d], 0x05040100u);
         hi.x = __builtin_amdgcn_perm(b.v[1][d], b.v[0][d], 0x07060302u);
         hi.y = __builtin_amdgcn_perm(b.v[3][d], b.v[2][d], 0x07060302u);
-        *reinterpret_cast<u32x2*>(T + (c0 + 2 * d) * ldt + slot) = lo;
-        *reinterpret_cast<u32x2*>(T + (c0 + 2 * d + 1) * ldt + slot) = hi;
+        *reinterpret_cast<FC_LDS u32x2*>(T + (c0 + 2 * d) * ldt + slot) = lo;
+        *reinterpret_cast<FC_LDS u32x2*>(T + (c0 + 2 * d + 1) * ldt + slot) = hi;
     }
 }
 
 template <bool PERM16>
 __device__ __forceinline__ void stage_transposed(const half_t* __restrict__ G, int rows, int cols, long ldg,
-                                                 int r0, int nr, int ncp, half_t* T, int ldt,
+                                                 int r0, int nr, int ncp, lds_half* T, int ldt,
                                                  int tid, int nthreads)
 {
     const int nblk = (nr >> 2) * (ncp >> 3);
@@ -141,6 +163,133 @@ __device__ __forceinline__ void stage_transposed(const half_t* __restrict__ G, i
         tblock_load(G, rows, cols, ldg, r0, ncp, blk, b);
         tblock_store<PERM16>(T, ldt, ncp, blk, b);
     }
+}
+
+// ---------------------------------------------------------------------------
+// MFMA operand fragment read from a row-major LDS tile with the gfx950
+// transposing LDS load (ds_read_b64_tr_b16).  The tile T holds k along its rows
+// (T[k][n], row stride ldt halves), as weights arrive from HBM.  The fragment
+// is that of a 32x32x16 operand whose lane l stands for index nb + (l % 32)
+// (a row of operand A or a column of operand B) and k-group h = l / 32:
+//     element j (0..7) = T[k0 + 8h + j][nb + l % 32].
+// Measured behaviour of the instruction: inside each group of 16 lanes, lane i
+// receives element (i % 4) of the 8-byte chunks addressed by lanes
+// 4e + i/4, e = 0..3.  So lane j of a group addresses row k0 + 8h + j/4 (+4 for
+// the second read), columns nb + 16*(group & 1) + 4*(j % 4) .. +3.
+// Conflict-free when the row stride is 32 bytes modulo 128 (the four rows a
+// group reads then fill all 32 banks).
+typedef __fp16 fp16x4_t __attribute__((__vector_size__(4 * sizeof(__fp16))));
+typedef FC_LDS fp16x4_t lds_fp16x4_t;
+
+__device__ __forceinline__ half8 frag_tr(const lds_half* T, int ldt, int k0, int nb, int lane)
+{
+    const int g = lane >> 4, i = lane & 15;
+    const lds_half* p = T + (k0 + 8 * (g >> 1) + (i >> 2)) * ldt + nb + 16 * (g & 1) + 4 * (i & 3);
+    const fp16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4f16((lds_fp16x4_t*)(p));
+    const fp16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4f16((lds_fp16x4_t*)(p + 4 * ldt));
+    half8 r;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        r[e] = (half_t)lo[e];
+        r[e + 4] = (half_t)hi[e];
+    }
+    return r;
+}
+
+// A natural (row-major, rows = k) weight tile in LDS, optionally XOR-swizzled.
+struct WTile {
+    lds_half* p;
+    int ld;      // row stride in halves
+    bool swz;    // XOR the 16-half segment index with (row & 3)
+    __device__ __forceinline__ int off(int r, int c) const
+    {
+        return r * ld + (swz ? (c ^ ((r & 3) << 4)) : c);
+    }
+};
+
+// Row stride / swizzle for a natural [rows x N] fp16 tile (N % 32 == 0): N a
+// multiple of 64 uses the XOR swizzle and no padding; otherwise 16 halves of
+// padding (row stride 96 bytes mod 128).  Either way the four rows one
+// 16-lane group reads fall into four different 32-byte bank groups.
+__host__ __device__ constexpr int wtile_ld(int N) { return (N % 64 == 0) ? N : N + 16; }
+__host__ __device__ constexpr bool wtile_swz(int N) { return N % 64 == 0; }
+
+// Lane part of a transposing fragment read from a WTile: the offset (in
+// halves) of this lane's 8-byte chunk for rows starting at 0 and the column
+// block nb (nb % 64 == 0 or 32: the XOR only touches the two low segment
+// bits, so for nb % 64 == 0 it commutes with adding nb).  Add row * ld for
+// the row base; the second read of a fragment is 4 rows further down.
+__device__ __forceinline__ int frag_lane_off(const WTile& T, int nb, int lane)
+{
+    const int g = lane >> 4, i = lane & 15;
+    return T.off(i >> 2, nb + 16 * (g & 1) + 4 * (i & 3));
+}
+
+__device__ __forceinline__ half8 frag_tr_at(const lds_half* p, int hi_off)
+{
+    const fp16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4f16((lds_fp16x4_t*)(p));
+    const fp16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4f16((lds_fp16x4_t*)(p + hi_off));
+    half8 r;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        r[e] = (half_t)lo[e];
+        r[e + 4] = (half_t)hi[e];
+    }
+    return r;
+}
+
+// Copy rows [0, nr) x columns [0, ncp) of the row-major G (leading dimension
+// ldg; zero outside rows x cols) into the natural tile T, 16-byte vectors,
+// NB vectors per thread per batch (all loads of a batch are issued before its
+// stores).
+template <int NB>
+__device__ __forceinline__ void stage_natural(const half_t* __restrict__ G, int rows, int cols, long ldg, int nr,
+                                              int ncp, const WTile& T, int tid, int nthreads)
+{
+    typedef FC_LDS u32x4 lds_u32x4;
+    const int vpr = ncp >> 3;
+    const int nv = nr * vpr;
+    for (int v0 = 0; v0 < nv; v0 += NB * nthreads) {
+        u32x4 x[NB];
+#pragma unroll
+        for (int i = 0; i < NB; ++i) {
+            const int v = v0 + tid + i * nthreads;
+            const int r = v / vpr, c = (v - r * vpr) * 8;
+            const bool ok = v < nv && r < rows && c < cols;
+            x[i] = *reinterpret_cast<const u32x4*>(ok ? G + (long)r * ldg + c : zero_ptr());
+        }
+#pragma unroll
+        for (int i = 0; i < NB; ++i) {
+            const int v = v0 + tid + i * nthreads;
+            const int r = v / vpr, c = (v - r * vpr) * 8;
+            if (v < nv) *reinterpret_cast<lds_u32x4*>(T.p + T.off(r, c)) = x[i];
+        }
+    }
+}
+
+// Line-coalesced store of an fp16 tile held in LDS: T [rows x cols] (row
+// stride ldt halves, cols % 8 == 0) -> out[(row0 + r) * ldo + col0 + c] for
+// row0 + r < nrows and col0 + c < ncols.  Consecutive threads write consecutive
+// 16-byte pieces of a row, so every store instruction covers whole 128-byte
+// lines (partial-line stores are written back to HBM several times over).
+__device__ __forceinline__ void store_tile(const lds_half* T, int ldt, int rows, int cols, half_t* out, long ldo,
+                                           long row0, long nrows, int col0, int ncols, int tid, int nthreads)
+{
+    typedef FC_LDS const u32x4 lds_u32x4;
+    const int vpr = cols >> 3;
+    for (int v = tid; v < rows * vpr; v += nthreads) {
+        const int r = v / vpr, c = (v - r * vpr) * 8;
+        if (row0 + r < nrows && col0 + c < ncols)
+            *reinterpret_cast<u32x4*>(out + (row0 + r) * ldo + col0 + c) = *reinterpret_cast<lds_u32x4*>(T + r * ldt + c);
+    }
+}
+
+// Orders this wave's LDS accesses around a hand-off through LDS between its
+// own lanes (LDS instructions of one wave execute in order; this also keeps
+// the compiler from moving accesses across it).
+__device__ __forceinline__ void wave_lds_sync()
+{
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 }
 
 }  // namespace fc

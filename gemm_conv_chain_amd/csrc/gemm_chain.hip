@@ -18,8 +18,7 @@ namespace fc {
 
 constexpr int LDS_THREADS = 256;   // 4 waves: 2 (rows) x 2 (columns)
 constexpr int LDS_MT = 128;        // rows per block
-constexpr int LDS_KC = 32;         // k per staged chunk (two MFMA k-steps)
-constexpr int LDS_LDW = LDS_KC + 8;  // padded LDS row of a staged weight chunk
+constexpr int LDS_KC = 64;         // k per staged weight chunk (four MFMA k-steps)
 constexpr int LDS_N1C = 256;       // GEMM1 columns per pass (2 waves x 4 tiles x 32)
 
 struct LdsArgs {
@@ -34,28 +33,89 @@ struct LdsArgs {
     int act;
 };
 
+// Weight chunks are staged in their natural row-major layout (rows = k) with
+// a row stride of (columns + 16) halves: 32 bytes modulo 128, which keeps the
+// transposing fragment reads conflict-free.
+__host__ __device__ constexpr int lds_wcols(int N0P, bool chain)
+{
+    return chain ? (N0P > LDS_N1C ? N0P : LDS_N1C) : N0P;
+}
+
 inline size_t lds_lds_bytes(int N0P, bool chain)
 {
-    const int wrows = chain ? (N0P > LDS_N1C ? N0P : LDS_N1C) : N0P;
-    size_t b = (size_t)2 * wrows * LDS_LDW * 2;
+    size_t b = (size_t)2 * LDS_KC * (lds_wcols(N0P, chain) + 16) * 2;
     if (chain) b += (size_t)LDS_MT * (N0P + 8) * 2;
+    b += (size_t)(N0P + (chain ? LDS_N1C : 0)) * 4;   // biases (fp32)
     return b;
 }
 
-// One block: LDS_MT rows.  Waves (wm, wn): rows 64*wm.., GEMM0 columns
-// [wn*NT0W*32, +NT0W*32) and, in the chain, GEMM1 columns [wn*128, +128) of
-// each 256-column pass.  Single-GEMM mode: blockIdx.y selects a block of
-// 64*NT0W output columns.
-template <int NT0W, bool CHAIN>
-__global__ __launch_bounds__(LDS_THREADS) void k_gemm_lds(LdsArgs a)
+// Copy a [LDS_KC x ncp] chunk of the row-major matrix G (rows r0.., leading
+// dimension ldg) through registers into LDS (16-byte vectors, zero outside
+// rows x cols).
+template <int NV>
+struct WChunk {
+    u32x4 v[NV];
+};
+
+template <int NV>
+__device__ __forceinline__ void wchunk_load(const half_t* __restrict__ G, int rows, int cols, long ldg, int r0,
+                                            int ncp, int tid, WChunk<NV>& w)
+{
+    const int vpr = ncp >> 3;   // 16-byte vectors per row
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+        const int v = tid + i * LDS_THREADS;
+        const int r = v / vpr, c = (v - r * vpr) * 8;
+        const bool ok = (r0 + r) < rows && c < cols && r < LDS_KC;
+        w.v[i] = *reinterpret_cast<const u32x4*>(ok ? G + (long)(r0 + r) * ldg + c : zero_ptr());
+    }
+}
+
+template <int NV>
+__device__ __forceinline__ void wchunk_store(lds_half* T, int ldt, int ncp, int tid, const WChunk<NV>& w)
+{
+    typedef FC_LDS u32x4 lds_u32x4;
+    const int vpr = ncp >> 3;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+        const int v = tid + i * LDS_THREADS;
+        const int r = v / vpr, c = (v - r * vpr) * 8;
+        if (r < LDS_KC) *reinterpret_cast<lds_u32x4*>(T + r * ldt + c) = w.v[i];
+    }
+}
+
+// One block: LDS_MT rows.  Waves (wm, wn): rows 64*wm + [0, 64) (two 32-row
+// MFMA tiles), GEMM0 columns wn*NT0W*32 + [0, NT0W*32) and, in the chain,
+// GEMM1 columns wn*128 + [0, 128) of each 256-column pass.  Single-GEMM mode:
+// blockIdx.y selects a block of 64*NT0W output columns.
+//   A rows stream from HBM straight into MFMA operand-B registers (two
+//   chunks ahead); weight chunks are copied into LDS in their natural layout
+//   (double-buffered, one chunk ahead) and read as operand-A fragments with the
+//   transposing LDS load, one k-step ahead of the MFMAs that use them.
+// KCH: number of 64-wide k chunks of GEMM0 when known at compile time (the
+// chunk loop is then fully unrolled, which lets the compiler track exactly
+// which loads each MFMA waits for; across a runtime loop's back edge it
+// waits for loads that are still two chunks ahead); 0 = runtime loop.
+template <int NT0W, bool CHAIN, int KCH>
+__global__ __launch_bounds__(LDS_THREADS) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void k_gemm_lds(LdsArgs a)
 {
     constexpr int N0P = 64 * NT0W;
-    constexpr int WROWS = CHAIN ? (N0P > LDS_N1C ? N0P : LDS_N1C) : N0P;
-    extern __shared__ __align__(16) char smem[];
-    half_t* Wbuf0 = reinterpret_cast<half_t*>(smem);
-    half_t* Wbuf1 = Wbuf0 + WROWS * LDS_LDW;
-    half_t* Hs = Wbuf1 + WROWS * LDS_LDW;   // CHAIN only: [LDS_MT][N0P + 8]
+    constexpr int WC = lds_wcols(N0P, CHAIN);
+    constexpr int LDW = WC + 16;
+    constexpr int WBUF = LDS_KC * LDW;   // halves per weight buffer
     constexpr int LDH = N0P + 8;
+    constexpr int NV0 = (LDS_KC * N0P / 8 + LDS_THREADS - 1) / LDS_THREADS;   // W0 vectors per thread
+    constexpr int NV1 = LDS_KC * LDS_N1C / 8 / LDS_THREADS;                    // W1 vectors per thread
+    static_assert(LDS_MT * (N0P + 8) <= 2 * WBUF, "output tile exceeds the weight buffers");
+    static_assert(!CHAIN || LDS_MT * (LDS_N1C + 8) <= 2 * WBUF, "output tile exceeds the weight buffers");
+    extern __shared__ __align__(16) char smem[];
+    typedef FC_LDS float lds_float;
+    typedef FC_LDS const floatx4 lds_float4;
+    lds_half* const Wb = (lds_half*)smem;       // two weight buffers, then H
+    lds_half* const Hs = Wb + 2 * WBUF;          // CHAIN only: [LDS_MT][LDH]
+    lds_float* const b0s = (lds_float*)(Hs + (CHAIN ? LDS_MT * LDH : 0));   // [N0P]
+    lds_float* const b1s = b0s + N0P;            // CHAIN only: [LDS_N1C] of the current pass
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
@@ -66,7 +126,6 @@ __global__ __launch_bounds__(LDS_THREADS) void k_gemm_lds(LdsArgs a)
     const int ncols0 = a.N0 - n_base;        // columns of W0 this block reads
     const half_t* W0b = a.W0 + n_base;
 
-    // Rows of A this lane feeds as operand B (two 32-row tiles).
     long mrow[2];
     bool mok[2];
 #pragma unroll
@@ -74,28 +133,32 @@ __global__ __launch_bounds__(LDS_THREADS) void k_gemm_lds(LdsArgs a)
         mrow[u] = m_blk + 64 * wm + 32 * u + lr;
         mok[u] = mrow[u] < a.M;
     }
-    auto load_a = [&](int c, half8 (&af)[2][2]) {
+    const half_t* arow[2] = {a.A + (mok[0] ? mrow[0] : 0) * (long)a.K0, a.A + (mok[1] ? mrow[1] : 0) * (long)a.K0};
+    // A chunk c for this lane: k = 64c + 16s + 8hh + [0,8), s = 0..3, both row tiles
+    auto load_a = [&](int c, half8 (&af)[2][4]) {
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
 #pragma unroll
-            for (int s = 0; s < 2; ++s) {
-                const int k = LDS_KC * c + 16 * hh + 8 * s;
-                af[u][s] = ld16_if(a.A + (mok[u] ? mrow[u] : 0) * (long)a.K0 + k, mok[u] && k < a.K0);
+            for (int s = 0; s < 4; ++s) {
+                const int k = LDS_KC * c + 16 * s + 8 * hh;
+                af[u][s] = ld16_if(arow[u] + k, mok[u] && k < a.K0);
             }
         }
     };
 
-    const int nch0 = (a.K0 + LDS_KC - 1) / LDS_KC;
-    const int nblk0 = (LDS_KC / 4) * (N0P / 8);   // <= LDS_THREADS
-    TBlock wreg;
-    half8 af[2][2];
+    const int nch0 = KCH ? KCH : (a.K0 + LDS_KC - 1) / LDS_KC;
+    // A chunks rotate through three register sets by name (chunk c lives in
+    // set c % 3); the loop below is unrolled by three so no registers are
+    // copied -- a copy would force a wait on the loads still in flight.
+    half8 af0[2][4], af1[2][4], af2[2][4];
+    WChunk<NV0> w0r;
 
-    // Prologue: chunk 0 of A in registers, chunk 0 of W0^T in LDS.
-    load_a(0, af);
-    if (tid < nblk0) {
-        tblock_load(W0b, a.K0, ncols0, a.N0, 0, N0P, tid, wreg);
-        tblock_store<false>(Wbuf0, LDS_LDW, N0P, tid, wreg);
-    }
+    // Prologue: W0 chunk 0 into LDS, A chunks 0 and 1 in flight.
+    load_a(0, af0);
+    if (1 < nch0) load_a(1, af1);
+    wchunk_load<NV0>(W0b, a.K0, ncols0, a.N0, 0, N0P, tid, w0r);
+    for (int i = tid; i < N0P; i += LDS_THREADS) b0s[i] = (a.b0 && i < ncols0) ? (float)a.b0[n_base + i] : 0.0f;
+    wchunk_store<NV0>(Wb, LDW, N0P, tid, w0r);
     __syncthreads();
 
     floatx16 acc[NT0W][2];
@@ -104,92 +167,99 @@ __global__ __launch_bounds__(LDS_THREADS) void k_gemm_lds(LdsArgs a)
         acc[t][0] = zero16();
         acc[t][1] = zero16();
     }
+    const int nb0 = wn * NT0W * 32;
 
     // ---------------- GEMM0 (transposed: C0^T = W0^T A^T) ----------------
-    for (int c = 0; c < nch0; ++c) {
+    auto step0 = [&](int c, const half8 (&cur)[2][4], half8 (&ld2)[2][4]) {
         const bool more = c + 1 < nch0;
-        half8 an[2][2];
-        if (more) {
-            load_a(c + 1, an);
-            if (tid < nblk0) tblock_load(W0b, a.K0, ncols0, a.N0, LDS_KC * (c + 1), N0P, tid, wreg);
-        }
-        const half_t* wb = ((c & 1) ? Wbuf1 : Wbuf0) + (wn * NT0W * 32 + lr) * LDS_LDW + 16 * hh;
+        if (more) wchunk_load<NV0>(W0b, a.K0, ncols0, a.N0, LDS_KC * (c + 1), N0P, tid, w0r);
+        if (c + 2 < nch0) load_a(c + 2, ld2);
+        __builtin_amdgcn_sched_barrier(0);   // keep the prefetches issued here
+        const lds_half* wb = Wb + (c & 1) * WBUF;
+        half8 wf[2][NT0W];
 #pragma unroll
-        for (int s = 0; s < 2; ++s) {
+        for (int t = 0; t < NT0W; ++t) wf[0][t] = frag_tr(wb, LDW, 0, nb0 + 32 * t, lane);
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            if (s < 3) {
+#pragma unroll
+                for (int t = 0; t < NT0W; ++t) wf[(s + 1) & 1][t] = frag_tr(wb, LDW, 16 * (s + 1), nb0 + 32 * t, lane);
+            }
 #pragma unroll
             for (int t = 0; t < NT0W; ++t) {
-                const half8 w = *reinterpret_cast<const half8*>(wb + 32 * t * LDS_LDW + 8 * s);
-                acc[t][0] = mfma32x32x16(w, af[0][s], acc[t][0]);
-                acc[t][1] = mfma32x32x16(w, af[1][s], acc[t][1]);
+                acc[t][0] = mfma32x32x16(wf[s & 1][t], cur[0][s], acc[t][0]);
+                acc[t][1] = mfma32x32x16(wf[s & 1][t], cur[1][s], acc[t][1]);
             }
         }
-        if (more) {
-            if (tid < nblk0) tblock_store<false>((c & 1) ? Wbuf0 : Wbuf1, LDS_LDW, N0P, tid, wreg);
-#pragma unroll
-            for (int u = 0; u < 2; ++u) {
-                af[u][0] = an[u][0];
-                af[u][1] = an[u][1];
-            }
-        }
+        if (more) wchunk_store<NV0>(Wb + ((c + 1) & 1) * WBUF, LDW, N0P, tid, w0r);
         __syncthreads();
+    };
+#pragma unroll
+    for (int c = 0; c < nch0; c += 3) {
+        step0(c, af0, af2);
+        if (c + 1 < nch0) step0(c + 1, af1, af0);
+        if (c + 2 < nch0) step0(c + 2, af2, af1);
     }
 
+    typedef FC_LDS half4 lds_half4;
+    typedef FC_LDS const half8 lds_half8;
     if (!CHAIN) {
-        // Epilogue: bias + act + fp16, 8-byte stores of 4 consecutive columns.
+        // Epilogue: bias + act + fp16 into an LDS tile (the weight buffers are
+        // free after the last barrier), then line-coalesced row stores.
+        constexpr int LDO0 = N0P + 8;
+        lds_half* Ot = Wb;
 #pragma unroll
         for (int t = 0; t < NT0W; ++t) {
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
-                const int nl = wn * NT0W * 32 + 32 * t + 8 * g + 4 * hh;
-                const int n = n_base + nl;
-                if (n >= a.N0) continue;
-                float bb[4];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) bb[e] = a.b0 ? (float)a.b0[n + e] : 0.0f;
+                const int nl = nb0 + 32 * t + 8 * g + 4 * hh;
+                const floatx4 bb = *reinterpret_cast<lds_float4*>(b0s + nl);
 #pragma unroll
                 for (int u = 0; u < 2; ++u) {
-                    if (!mok[u]) continue;
                     half4 o;
 #pragma unroll
                     for (int e = 0; e < 4; ++e) o[e] = (half_t)act_apply(a.act, acc[t][u][4 * g + e] + bb[e]);
-                    *reinterpret_cast<half4*>(a.out + mrow[u] * (long)a.N0 + n) = o;
+                    *reinterpret_cast<lds_half4*>(Ot + (64 * wm + 32 * u + lr) * LDO0 + nl) = o;
                 }
             }
         }
+        __syncthreads();
+        store_tile(Ot, LDO0, LDS_MT, N0P, a.out, a.N0, m_blk, a.M, n_base, a.N0, tid, LDS_THREADS);
         return;
     }
+
+    // Fetch W1 chunk 0 while the epilogue runs.
+    WChunk<NV1> w1r;
+    wchunk_load<NV1>(a.W1, a.N0, a.N1, a.N1, 0, LDS_N1C, tid, w1r);
 
     // ------- accumulator-fragment -> LDS iterator: H = fp16(act(C0 + b0)) -------
 #pragma unroll
     for (int t = 0; t < NT0W; ++t) {
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-            const int n0 = wn * NT0W * 32 + 32 * t + 8 * g + 4 * hh;
-            float bb[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) bb[e] = (a.b0 && n0 + e < a.N0) ? (float)a.b0[n0 + e] : 0.0f;
+            const int n0 = nb0 + 32 * t + 8 * g + 4 * hh;
+            const floatx4 bb = *reinterpret_cast<lds_float4*>(b0s + n0);
 #pragma unroll
             for (int u = 0; u < 2; ++u) {
                 half4 o;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) o[e] = (half_t)act_apply(a.act, acc[t][u][4 * g + e] + bb[e]);
-                *reinterpret_cast<half4*>(Hs + (64 * wm + 32 * u + lr) * LDH + n0) = o;
+                *reinterpret_cast<lds_half4*>(Hs + (64 * wm + 32 * u + lr) * LDH + n0) = o;
             }
         }
     }
-    // (the barrier at the end of the last GEMM0 iteration already released
-    //  both weight buffers; the one below publishes H)
+    // (the barrier closing the last GEMM0 iteration released both weight
+    //  buffers; the barrier below publishes H and W1 chunk 0)
 
     // ---------------- GEMM1 (transposed: D^T = W1^T H^T) ----------------
     const int nch1 = N0P / LDS_KC;
-    const int nblk1 = (LDS_KC / 4) * (LDS_N1C / 8);   // == LDS_THREADS
+    int buf = 0;
     for (int n1c = 0; n1c < a.N1; n1c += LDS_N1C) {
         const half_t* W1b = a.W1 + n1c;
         const int ncols1 = a.N1 - n1c;
-        if (tid < nblk1) {
-            tblock_load(W1b, a.N0, ncols1, a.N1, 0, LDS_N1C, tid, wreg);
-            tblock_store<false>(Wbuf0, LDS_LDW, LDS_N1C, tid, wreg);
-        }
+        if (n1c > 0) wchunk_load<NV1>(W1b, a.N0, ncols1, a.N1, 0, LDS_N1C, tid, w1r);
+        for (int i = tid; i < LDS_N1C; i += LDS_THREADS) b1s[i] = (a.b1 && i < ncols1) ? (float)a.b1[n1c + i] : 0.0f;
+        wchunk_store<NV1>(Wb + buf * WBUF, LDW, LDS_N1C, tid, w1r);
         __syncthreads();
         floatx16 acc1[4][2];
 #pragma unroll
@@ -199,43 +269,56 @@ __global__ __launch_bounds__(LDS_THREADS) void k_gemm_lds(LdsArgs a)
         }
         for (int c = 0; c < nch1; ++c) {
             const bool more = c + 1 < nch1;
-            if (more && tid < nblk1) tblock_load(W1b, a.N0, ncols1, a.N1, LDS_KC * (c + 1), LDS_N1C, tid, wreg);
-            const half_t* wb = ((c & 1) ? Wbuf1 : Wbuf0) + (wn * 128 + lr) * LDS_LDW + 16 * hh;
-            const half_t* hb = Hs + (64 * wm + lr) * LDH + LDS_KC * c + 16 * hh;
+            if (more) wchunk_load<NV1>(W1b, a.N0, ncols1, a.N1, LDS_KC * (c + 1), LDS_N1C, tid, w1r);
+            __builtin_amdgcn_sched_barrier(0);
+            const lds_half* wb = Wb + buf * WBUF;
+            const lds_half* hb = Hs + (64 * wm + lr) * LDH + LDS_KC * c + 8 * hh;
+            half8 wf[2][4], hf[2][2];
 #pragma unroll
-            for (int s = 0; s < 2; ++s) {
-                const half8 h0 = *reinterpret_cast<const half8*>(hb + 8 * s);
-                const half8 h1 = *reinterpret_cast<const half8*>(hb + 32 * LDH + 8 * s);
+            for (int t = 0; t < 4; ++t) wf[0][t] = frag_tr(wb, LDW, 0, wn * 128 + 32 * t, lane);
+            hf[0][0] = *reinterpret_cast<lds_half8*>(hb);
+            hf[0][1] = *reinterpret_cast<lds_half8*>(hb + 32 * LDH);
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                if (s < 3) {
+#pragma unroll
+                    for (int t = 0; t < 4; ++t)
+                        wf[(s + 1) & 1][t] = frag_tr(wb, LDW, 16 * (s + 1), wn * 128 + 32 * t, lane);
+                    hf[(s + 1) & 1][0] = *reinterpret_cast<lds_half8*>(hb + 16 * (s + 1));
+                    hf[(s + 1) & 1][1] = *reinterpret_cast<lds_half8*>(hb + 32 * LDH + 16 * (s + 1));
+                }
 #pragma unroll
                 for (int t = 0; t < 4; ++t) {
-                    const half8 w = *reinterpret_cast<const half8*>(wb + 32 * t * LDS_LDW + 8 * s);
-                    acc1[t][0] = mfma32x32x16(w, h0, acc1[t][0]);
-                    acc1[t][1] = mfma32x32x16(w, h1, acc1[t][1]);
+                    acc1[t][0] = mfma32x32x16(wf[s & 1][t], hf[s & 1][0], acc1[t][0]);
+                    acc1[t][1] = mfma32x32x16(wf[s & 1][t], hf[s & 1][1], acc1[t][1]);
                 }
             }
-            if (more && tid < nblk1) tblock_store<false>((c & 1) ? Wbuf0 : Wbuf1, LDS_LDW, LDS_N1C, tid, wreg);
+            if (more) wchunk_store<NV1>(Wb + (buf ^ 1) * WBUF, LDW, LDS_N1C, tid, w1r);
+            buf ^= 1;
             __syncthreads();
         }
-        // Epilogue 1: + b1, fp16, 8-byte stores.
+        // Epilogue 1: + b1, fp16 into an LDS tile over the (now free) weight
+        // buffers, then line-coalesced row stores.
+        constexpr int LDO1 = LDS_N1C + 8;
+        lds_half* Ot = Wb;
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
-                const int n1 = n1c + wn * 128 + 32 * t + 8 * g + 4 * hh;
-                if (n1 >= a.N1) continue;
-                float bb[4];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) bb[e] = a.b1 ? (float)a.b1[n1 + e] : 0.0f;
+                const int nl = wn * 128 + 32 * t + 8 * g + 4 * hh;
+                const floatx4 bb = *reinterpret_cast<lds_float4*>(b1s + nl);
 #pragma unroll
                 for (int u = 0; u < 2; ++u) {
-                    if (!mok[u]) continue;
                     half4 o;
 #pragma unroll
                     for (int e = 0; e < 4; ++e) o[e] = (half_t)(acc1[t][u][4 * g + e] + bb[e]);
-                    *reinterpret_cast<half4*>(a.out + mrow[u] * (long)a.N1 + n1) = o;
+                    *reinterpret_cast<lds_half4*>(Ot + (64 * wm + 32 * u + lr) * LDO1 + nl) = o;
                 }
             }
         }
+        __syncthreads();
+        store_tile(Ot, LDO1, LDS_MT, LDS_N1C, a.out, a.N1, m_blk, a.M, n1c, a.N1, tid, LDS_THREADS);
+        __syncthreads();
     }
 }
 
@@ -255,17 +338,30 @@ int device_cu_count()
     return g_num_cu;
 }
 
-template <int NT0W, bool CHAIN>
-static hipError_t launch_lds_t(const LdsArgs& a, hipStream_t st)
+template <int NT0W, bool CHAIN, int KCH>
+static hipError_t launch_lds_k(const LdsArgs& a, hipStream_t st)
 {
     const size_t lds = lds_lds_bytes(64 * NT0W, CHAIN);
-    hipError_t e = hipFuncSetAttribute((const void*)k_gemm_lds<NT0W, CHAIN>,
+    hipError_t e = hipFuncSetAttribute((const void*)k_gemm_lds<NT0W, CHAIN, KCH>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     const unsigned gx = (unsigned)((a.M + LDS_MT - 1) / LDS_MT);
     const unsigned gy = CHAIN ? 1u : (unsigned)((a.N0 + 64 * NT0W - 1) / (64 * NT0W));
-    hipLaunchKernelGGL((k_gemm_lds<NT0W, CHAIN>), dim3(gx, gy), dim3(LDS_THREADS), lds, st, a);
+    hipLaunchKernelGGL((k_gemm_lds<NT0W, CHAIN, KCH>), dim3(gx, gy), dim3(LDS_THREADS), lds, st, a);
     return hipGetLastError();
+}
+
+// Compile-time chunk counts for the k lengths in use (64, 256, 576); others
+// run the loop with a runtime trip count.
+template <int NT0W, bool CHAIN>
+static hipError_t launch_lds_t(const LdsArgs& a, hipStream_t st)
+{
+    switch ((a.K0 + LDS_KC - 1) / LDS_KC) {
+    case 1: return launch_lds_k<NT0W, CHAIN, 1>(a, st);
+    case 4: return launch_lds_k<NT0W, CHAIN, 4>(a, st);
+    case 9: return launch_lds_k<NT0W, CHAIN, 9>(a, st);
+    }
+    return launch_lds_k<NT0W, CHAIN, 0>(a, st);
 }
 
 // ---------------------------------------------------------------- entry points
