@@ -34,6 +34,7 @@ namespace fc {
 
 constexpr int RF_THREADS = 512;
 constexpr int RF_WAVES = RF_THREADS / 64;
+constexpr int RF_WB = 16;   // weight vectors (16 bytes) per thread staged ahead of the row stream
 
 struct RfArgs {
     const half_t* W0;   // [K0 x N0] row-major
@@ -106,40 +107,50 @@ void k_chain_rf(Loader ld, RfArgs a)
     long tile = t_begin + wave;
     half8 xr[R][4];
     typename Loader::Row row;
-    // Loads complete in issue order as far as a wave's wait counter is
-    // concerned, so a wave that already streams its rows cannot stage weights
-    // without waiting for those rows.  The first half of the waves therefore
-    // stages W0^T, W1^T and the biases while the second half starts its row
-    // stream at once; the stagers start theirs after the barrier (each SIMD
-    // hosts one wave of each half).
-    constexpr int NSTAGE = RF_THREADS / 2;
-    const bool stager = tid < NSTAGE;
-    auto start_rows = [&]() {
-        if (tile < t_end) {
-            row = ld.row(tile * 32 + lr);
+    // Prologue.  Every wave first issues its share of the weight (and bias)
+    // loads, then the row loads of its first tile, and only then writes the
+    // weights to LDS: the wait before those LDS writes covers the weight loads
+    // alone (a wave's wait counter retires loads in issue order), and the
+    // weight requests, which hit L2, are not queued behind the row stream.
+    // Weights beyond one batch of RF_WB vectors per thread are staged after
+    // the barrier-free first batch (their loads then wait behind the rows).
+    WStage2<RF_WB> ws;
+    ws.G0 = a.W0; ws.rows0 = a.K0; ws.cols0 = a.N0; ws.ldg0 = a.N0; ws.nr0 = a.K0p; ws.ncp0 = N0P; ws.T0 = W0n;
+    ws.G1 = a.W1; ws.rows1 = a.N0; ws.cols1 = a.N1; ws.ldg1 = a.N1; ws.nr1 = N0P; ws.ncp1 = a.N1p; ws.T1 = W1n;
+    ws.init();
+    ws.load(tid, RF_THREADS);
+    // this thread's bias value (raw fp16; converted only after the row loads
+    // are issued, so nothing waits on it early)
+    const half_t* bp = zero_ptr();
+    if (tid < N0P) {
+        if (a.b0 && tid < a.N0) bp = a.b0 + tid;
+    } else if (tid < N0P + a.N1p && a.b1 && tid - N0P < a.N1) {
+        bp = a.b1 + (tid - N0P);
+    }
+    const half_t bias = *bp;
+    if (tile < t_end) {
+        row = ld.row(tile * 32 + lr);
 #pragma unroll
-            for (int p = 0; p < PD; ++p)
-                if (p < nch) ld.load(row, p, hh, xr[p]);
+        for (int p = 0; p < PD; ++p)
+            if (p < nch) ld.load(row, p, hh, xr[p]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    ws.store(tid, RF_THREADS);
+    if (tid < N0P + a.N1p) b0s[tid] = (float)bias;   // b1s follows b0s
+    for (int i = tid + RF_THREADS; i < N0P + a.N1p; i += RF_THREADS) {
+        float v = 0.0f;
+        if (i < N0P) {
+            if (a.b0 && i < a.N0) v = (float)a.b0[i];
+        } else if (a.b1 && i - N0P < a.N1) {
+            v = (float)a.b1[i - N0P];
         }
-    };
-    if (!stager) start_rows();
-    if (stager) {
-        stage_natural<8>(a.W0, a.K0, a.N0, a.N0, a.K0p, N0P, W0n, tid, NSTAGE);
-        stage_natural<8>(a.W1, a.N0, a.N1, a.N1, N0P, a.N1p, W1n, tid, NSTAGE);
-        for (int i = tid; i < N0P + a.N1p; i += NSTAGE) {
-            float v = 0.0f;
-            if (i < N0P) {
-                if (a.b0 && i < a.N0) v = (float)a.b0[i];
-                b0s[i] = v;
-            } else {
-                const int j = i - N0P;
-                if (a.b1 && j < a.N1) v = (float)a.b1[j];
-                b1s[j] = v;
-            }
-        }
+        b0s[i] = v;
+    }
+    for (int v0 = RF_WB * RF_THREADS; v0 < ws.nvt; v0 += RF_WB * RF_THREADS) {
+        ws.load(tid + v0, RF_THREADS);
+        ws.store(tid + v0, RF_THREADS);
     }
     __syncthreads();
-    if (stager) start_rows();
 
     // Per-lane parts of the fragment addresses (row bases 32hh / 4hh folded in).
     const lds_half* w0lane[NT0];

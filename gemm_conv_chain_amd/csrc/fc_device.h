@@ -267,6 +267,76 @@ __device__ __forceinline__ void stage_natural(const half_t* __restrict__ G, int 
     }
 }
 
+// Two-phase staging of up to two natural weight tiles into LDS: load()
+// issues this thread's share of the global loads into registers, store()
+// writes them to LDS.  Between the two a kernel may issue its own streaming
+// loads: the wait before store() then covers only the staging loads (a wave's
+// wait counter retires loads in issue order).  Vector v (16 bytes) of matrix m
+// is row v / vpr, column 8 (v % vpr); thread tid handles v = tid + i*nthreads,
+// whose (row, column) advance by a fixed step -- no division per vector.
+template <int NV>
+struct WStage2 {
+    u32x4 x[NV];
+    // matrix 0 and matrix 1 (kept as separate fields: a runtime-indexed
+    // array would be placed in scratch memory)
+    const half_t* G0;
+    const half_t* G1;
+    int rows0, cols0, nr0, ncp0, rows1, cols1, nr1, ncp1;
+    long ldg0, ldg1;
+    WTile T0, T1;
+    int nv0, nvt;    // vectors of matrix 0; of both
+
+    __device__ __forceinline__ void init()
+    {
+        nv0 = nr0 * (ncp0 >> 3);
+        nvt = nv0 + nr1 * (ncp1 >> 3);
+    }
+    template <bool STORE>
+    __device__ __forceinline__ void walk(int v0, int nthreads)
+    {
+        typedef FC_LDS u32x4 lds_u32x4;
+        const int step = nthreads * 8;
+        // position in matrix 0 (one division per call)
+        const int vpr0 = ncp0 >> 3, vpr1 = ncp1 >> 3;
+        int m = v0 >= nv0;
+        int vv = m ? v0 - nv0 : v0;
+        int r = vv / (m ? vpr1 : vpr0);
+        int c = (vv - r * (m ? vpr1 : vpr0)) * 8;
+        const int dr0 = step / ncp0, dc0 = step - dr0 * ncp0;
+        const int dr1 = step / ncp1, dc1 = step - dr1 * ncp1;
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+            const int v = v0 + i * nthreads;
+            if (v - (int)(threadIdx.x & 63) >= nvt) break;   // the whole wave is past the end
+            if (!m && v >= nv0) {   // crossed into matrix 1 (once)
+                m = 1;
+                vv = v - nv0;
+                r = vv / vpr1;
+                c = (vv - r * vpr1) * 8;
+            }
+            const int ncp = m ? ncp1 : ncp0;
+            if (STORE) {
+                if (v < nvt) {
+                    lds_half* dst = m ? T1.p + T1.off(r, c) : T0.p + T0.off(r, c);
+                    *reinterpret_cast<lds_u32x4*>(dst) = x[i];
+                }
+            } else {
+                const bool ok = v < nvt && r < (m ? rows1 : rows0) && c < (m ? cols1 : cols0);
+                const half_t* src = m ? G1 + (long)r * ldg1 + c : G0 + (long)r * ldg0 + c;
+                x[i] = *reinterpret_cast<const u32x4*>(ok ? src : zero_ptr());
+            }
+            c += m ? dc1 : dc0;
+            r += m ? dr1 : dr0;
+            if (c >= ncp) {
+                c -= ncp;
+                ++r;
+            }
+        }
+    }
+    __device__ __forceinline__ void load(int v0, int nthreads) { walk<false>(v0, nthreads); }
+    __device__ __forceinline__ void store(int v0, int nthreads) { walk<true>(v0, nthreads); }
+};
+
 // Line-coalesced store of an fp16 tile held in LDS: T [rows x cols] (row
 // stride ldt halves, cols % 8 == 0) -> out[(row0 + r) * ldo + col0 + c] for
 // row0 + r < nrows and col0 + c < ncols.  Consecutive threads write consecutive

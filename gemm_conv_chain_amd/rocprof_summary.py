@@ -1,0 +1,96 @@
+"""Summaries of rocprofv3 output for this library's kernels.
+
+    python -m gemm_conv_chain_amd.rocprof_summary trace  DIR        # --kernel-trace --stats -f csv
+    python -m gemm_conv_chain_amd.rocprof_summary pmc    DIR WORKLOAD [--json profiles/traffic.json]
+
+``trace``: the kernel_stats.csv rows (calls, average/min/max duration).
+``pmc``: FETCH_SIZE / WRITE_SIZE per dispatch (KiB, mean over the dispatches of
+each kernel) from two ``--pmc`` runs (DIR/fetch, DIR/write) of
+``bench.py --calib-copy``.  Each counter is scaled by what it reads for the
+256 MiB device-to-device copy that ``--calib-copy`` issues last (known bytes):
+scale = 262144 KiB / counter value of that dispatch.  With --json the scaled
+HBM bytes of the fused kernel (and the sum over the unfused kernels) are
+recorded for bench.py, keyed by the hash of the kernel sources they were taken
+on (bench.py reports them only while that hash still matches).
+"""
+from __future__ import annotations
+
+import csv
+import glob
+import json
+import os
+import sys
+
+
+def _rows(path_glob):
+    out = []
+    for f in sorted(glob.glob(path_glob, recursive=True)):
+        with open(f) as fh:
+            out.extend(csv.DictReader(fh))
+    return out
+
+
+def trace(d):
+    rows = _rows(os.path.join(d, "**", "*kernel_stats.csv"))
+    print("| kernel | calls | avg (us) | min (us) | max (us) | % of time |")
+    print("|---|---|---|---|---|---|")
+    for r in rows:
+        print("| `%s` | %s | %.3f | %.3f | %.3f | %.1f |" % (
+            r["Name"][:90], r["Calls"], float(r["AverageNs"]) / 1e3, float(r["MinNs"]) / 1e3,
+            float(r["MaxNs"]) / 1e3, float(r["Percentage"])))
+
+
+def _pmc(d, counter):
+    rows = [r for r in _rows(os.path.join(d, "**", "*counter_collection.csv")) if r["Counter_Name"] == counter]
+    copies = [r for r in rows if "copyBuffer" in r["Kernel_Name"]]
+    if not copies:
+        raise SystemExit("no calibration copy dispatch in %s" % d)
+    calib = max(copies, key=lambda r: int(r["Dispatch_Id"]))
+    scale = 262144.0 / float(calib["Counter_Value"])
+    per = {}
+    for r in rows:
+        if "fc::" in r["Kernel_Name"]:
+            per.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+    return scale, float(calib["Counter_Value"]), {k: sum(v) / len(v) for k, v in per.items()}
+
+
+def pmc(d, workload, json_path=None):
+    fs, fcal, fetch = _pmc(os.path.join(d, "fetch"), "FETCH_SIZE")
+    ws, wcal, write = _pmc(os.path.join(d, "write"), "WRITE_SIZE")
+    print("calibration (256 MiB copy): FETCH_SIZE %.0f KiB -> scale %.4f; WRITE_SIZE %.0f KiB -> scale %.4f"
+          % (fcal, fs, wcal, ws))
+    print()
+    print("| kernel | FETCH_SIZE (KiB) | WRITE_SIZE (KiB) | scaled HBM bytes (MB) |")
+    print("|---|---|---|---|")
+    tot = {}
+    for k in sorted(fetch):
+        b = fetch[k] * fs * 1024 + write.get(k, 0.0) * ws * 1024
+        tot[k] = b
+        print("| `%s` | %.1f | %.1f | %.2f |" % (k[:90], fetch[k], write.get(k, 0.0), b / 1e6))
+    if json_path:
+        sys.path.insert(0, os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+        import bench
+        fused = {"b2b_gemm_tiny": "k_chain_rf", "b2b_gemm_rf": "k_chain_rf", "b2b_gemm_lds": "k_gemm_lds<4, true",
+                 "conv3x3_conv1x1": "k_chain_rf", "conv3x3_relu_maxpool": "k_conv_w<4, 1"}[workload]
+        fk = [k for k in fetch if fused in k]
+        if len(fk) != 1:
+            raise SystemExit("cannot identify the fused kernel among %s" % list(fetch))
+        fk = fk[0]
+        unf = sum(v for k, v in tot.items() if k != fk)
+        db = {"workloads": {}}
+        if os.path.exists(json_path):
+            with open(json_path) as f:
+                db = json.load(f)
+        db.setdefault("workloads", {})[workload] = {
+            "kernel": fk, "src_hash": bench.kernel_src_hash(), "fetch_kib": fetch[fk], "write_kib": write.get(fk, 0.0),
+            "fetch_scale": fs, "write_scale": ws, "unfused_bytes": int(unf)}
+        with open(json_path, "w") as f:
+            json.dump(db, f, indent=1, sort_keys=True)
+
+
+if __name__ == "__main__":
+    if sys.argv[1] == "trace":
+        trace(sys.argv[2])
+    else:
+        jp = sys.argv[sys.argv.index("--json") + 1] if "--json" in sys.argv else None
+        pmc(sys.argv[2], sys.argv[3], jp)
