@@ -70,6 +70,8 @@ fc_status check_conv(const fc_conv_shape* s, int kmax)
         return fail(FC_E_UNSUPPORTED, "only 3x3 stride-1 pad-1 convolutions are implemented");
     if (s->c % 32) return fail(FC_E_UNSUPPORTED, "c=%d: pad channels to a multiple of 32", s->c);
     if (s->k > kmax) return fail(FC_E_UNSUPPORTED, "k=%d exceeds the %d output channels one block keeps", s->k, kmax);
+    if ((long)s->n * s->h * s->w > 0x7fffffffL)
+        return fail(FC_E_UNSUPPORTED, "n*h*w exceeds 2^31 - 1 pixels (pixel indices are 32-bit)");
     return FC_OK;
 }
 

@@ -132,7 +132,7 @@ void k_chain_rf(Loader ld, RfArgs a)
         row = ld.row(tile * 32 + lr);
 #pragma unroll
         for (int p = 0; p < PD; ++p)
-            if (p < nch) ld.load(row, p, hh, xr[p]);
+            if (p < nch) ld.template load<KCH>(row, p, hh, xr[p]);
     }
     __builtin_amdgcn_sched_barrier(0);
     ws.store(tid, RF_THREADS);
@@ -152,10 +152,10 @@ void k_chain_rf(Loader ld, RfArgs a)
     }
     __syncthreads();
 
-    // Per-lane parts of the fragment addresses (row bases 32hh / 4hh folded in).
+    // Per-lane parts of the fragment addresses (row bases 8hh / 4hh folded in).
     const lds_half* w0lane[NT0];
 #pragma unroll
-    for (int t = 0; t < NT0; ++t) w0lane[t] = W0n.p + frag_lane_off(W0n, 32 * t, lane) + 32 * hh * W0n.ld;
+    for (int t = 0; t < NT0; ++t) w0lane[t] = W0n.p + frag_lane_off(W0n, 32 * t, lane) + 8 * hh * W0n.ld;
     const lds_half* w1lane[2];
 #pragma unroll
     for (int t1 = 0; t1 < 2; ++t1) w1lane[t1] = W1n.p + frag_lane_off(W1n, 32 * t1, lane) + 4 * hh * W1n.ld;
@@ -165,14 +165,14 @@ void k_chain_rf(Loader ld, RfArgs a)
 #pragma unroll
         for (int t = 0; t < NT0; ++t) acc0[t] = zero16();
 
-        // W0^T fragment for k = 64c + 32hh + 8q + j (the rows this lane's
+        // W0^T fragment for k = 64c + 16q + 8hh + j (the rows this lane's
         // 16-byte loads of X cover) and n0 = 32t + lane%32.
         auto mma_chunk = [&](int c, const half8 (&cur)[4]) {
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
 #pragma unroll
                 for (int t = 0; t < NT0; ++t) {
-                    const half8 w = frag_tr_at(w0lane[t] + (64 * c + 8 * q) * W0n.ld, 4 * W0n.ld);
+                    const half8 w = frag_tr_at(w0lane[t] + (64 * c + 16 * q) * W0n.ld, 4 * W0n.ld);
                     acc0[t] = mfma32x32x16(w, cur[q], acc0[t]);
                 }
             }
@@ -180,17 +180,17 @@ void k_chain_rf(Loader ld, RfArgs a)
         if constexpr (KCH > 0) {
 #pragma unroll
             for (int c = 0; c < KCH; ++c) {
-                if (c + PD < KCH) ld.load(row, c + PD, hh, xr[(c + PD) % R]);
+                if (c + PD < KCH) ld.template load<KCH>(row, c + PD, hh, xr[(c + PD) % R]);
                 __builtin_amdgcn_sched_barrier(0);   // keep the prefetch issued here
                 mma_chunk(c, xr[c % R]);
             }
         } else {
             for (int c = 0; c < nch; c += 2) {
-                if (c + 1 < nch) ld.load(row, c + 1, hh, xr[1]);
+                if (c + 1 < nch) ld.template load<KCH>(row, c + 1, hh, xr[1]);
                 __builtin_amdgcn_sched_barrier(0);
                 mma_chunk(c, xr[0]);
                 if (c + 1 < nch) {
-                    if (c + 2 < nch) ld.load(row, c + 2, hh, xr[0]);
+                    if (c + 2 < nch) ld.template load<KCH>(row, c + 2, hh, xr[0]);
                     __builtin_amdgcn_sched_barrier(0);
                     mma_chunk(c + 1, xr[1]);
                 }
@@ -205,21 +205,22 @@ void k_chain_rf(Loader ld, RfArgs a)
             nrow = ld.row(ntile * 32 + lr);
 #pragma unroll
             for (int p = 0; p < PD; ++p)
-                if (p < nch) ld.load(nrow, p, hh, xr[p]);
+                if (p < nch) ld.template load<KCH>(nrow, p, hh, xr[p]);
         }
 
         // Epilogue 0 in registers: bias (broadcast along rows), activation,
         // one rounding to fp16.  hf[s] is GEMM1's operand B for k-step s.
         half8 hf[2 * NT0];
+        act_dispatch(a.act, [&](auto act) {
 #pragma unroll
-        for (int t = 0; t < NT0; ++t) {
+            for (int t = 0; t < NT0; ++t) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int n0 = 32 * t + 8 * (r >> 2) + 4 * hh + (r & 3);
-                const float v = act_apply(a.act, acc0[t][r] + b0s[n0]);
-                hf[2 * t + (r >> 3)][r & 7] = (half_t)v;
+                for (int r = 0; r < 16; ++r) {
+                    const int n0 = 32 * t + 8 * (r >> 2) + 4 * hh + (r & 3);
+                    hf[2 * t + (r >> 3)][r & 7] = (half_t)act.f(acc0[t][r] + b0s[n0]);
+                }
             }
-        }
+        });
 
         // GEMM1 over N1 in chunks of 64 columns (two 32x32 tiles).
         for (int n1c = 0; n1c < a.N1p; n1c += 64) {
@@ -273,12 +274,15 @@ struct DenseRows {
         r.p = A + (r.ok ? m : 0) * (long)K;
         return r;
     }
+    template <int KCH>
     __device__ __forceinline__ void load(const Row& r, int c, int hh, half8 out[4]) const
     {
-        const int k0 = 64 * c + 32 * hh;
+        // k = 64c + 16q + 8hh + [0, 8): the MFMA's own k order, so the two
+        // lanes holding a row's k-step read 32 contiguous bytes
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-            out[q] = ld16_if(r.p + k0 + 8 * q, r.ok && (k0 + 8 * q) < K);
+            const int k = 64 * c + 16 * q + 8 * hh;
+            out[q] = ld16_if(r.p + k, r.ok && k < K);
         }
     }
 };

@@ -26,43 +26,117 @@ namespace fc {
 // 3x3, stride 1, pad 1 NHWC conv pixels as GEMM rows (P = H, Q = W).  A lane
 // half h reads, for chunk c, the 32 consecutive k = 64c + 32h + [0, 32): a
 // single (r, s) position and 32 consecutive channels (C % 32 == 0).
+// Unsigned division by a runtime constant d >= 1 without a divide sequence:
+// magic = floor(2^32 / d) (2^32 - 1 for d = 1) gives q0 = mulhi(x, magic) in
+// {x/d - 1, x/d}, and one comparison fixes it (exact for every 32-bit x).
+struct FastDiv {
+    unsigned d, magic;
+    static FastDiv make(unsigned dd)
+    {
+        FastDiv f;
+        f.d = dd;
+        f.magic = dd > 1 ? (unsigned)(0x100000000ull / dd) : 0xffffffffu;
+        return f;
+    }
+    __device__ __forceinline__ unsigned div(unsigned x) const
+    {
+        unsigned q = __umulhi(x, magic);
+        if (x - q * d >= d) ++q;
+        return q;
+    }
+};
+
 struct Conv3x3Rows {
     const half_t* x;
     int H, W, C;
-    long M;   // N*H*W
+    long M;   // N*H*W (< 2^31)
+    FastDiv fhw, fw, fc16;   // by H*W, by W, by C/16
+    // A GEMM row = one output pixel: its centre in x and a 9-bit mask whose
+    // bit 3r+s says that tap (r, s) lies inside the image (0 for a row past M).
     struct Row {
-        int n, p, q;
-        bool ok;
+        const half_t* pix;
+        unsigned mask;
     };
-    __device__ __forceinline__ Row row(long m) const
+    void set_divisors()
+    {
+        fhw = FastDiv::make((unsigned)H * (unsigned)W);
+        fw = FastDiv::make((unsigned)W);
+        fc16 = FastDiv::make((unsigned)C / 16);
+    }
+    __device__ __forceinline__ Row make(int n, int p, int q, bool ok) const
     {
         Row r;
-        r.ok = m < M;
-        const long mm = r.ok ? m : 0;
-        const long hw = (long)H * W;
-        r.n = (int)(mm / hw);
-        const int rem = (int)(mm - (long)r.n * hw);
-        r.p = rem / W;
-        r.q = rem - r.p * W;
+        r.pix = x + (((long)n * H + p) * W + q) * C;
+        // rows r with 0 <= p + r - 1 < H, columns s likewise
+        const unsigned rm = 2u | (p > 0 ? 1u : 0u) | (p < H - 1 ? 4u : 0u);
+        const unsigned sm = 2u | (q > 0 ? 1u : 0u) | (q < W - 1 ? 4u : 0u);
+        const unsigned m = ((rm & 1u) ? sm : 0u) | ((rm & 2u) ? sm << 3 : 0u) | ((rm & 4u) ? sm << 6 : 0u);
+        r.mask = ok ? m : 0u;
         return r;
     }
+    __device__ __forceinline__ Row row(long m) const
+    {
+        const bool ok = m < M;
+        const unsigned mm = ok ? (unsigned)m : 0u;
+        const unsigned n = fhw.div(mm);
+        const unsigned rem = mm - n * fhw.d;
+        const unsigned p = fw.div(rem);
+        return make((int)n, (int)p, (int)(rem - p * fw.d), ok);
+    }
+    // Chunk c, lane half hh, vector q: k = 64c + 16q + 8hh + [0, 8), the
+    // MFMA's own k order, so that the two lanes holding one pixel's k-step
+    // read 32 contiguous bytes (one cache access per pixel and load
+    // instruction).  k lies in tap rs = k / C at channel k % C; a 16-aligned
+    // run of k never crosses a tap (C % 32 == 0).  KCH = 9 chunks (9C rounded
+    // up to 64) means C = 64, known at compile time: then rs = c and the
+    // channel is 16q + 8hh.
+    template <int KCH>
     __device__ __forceinline__ void load(const Row& r, int c, int hh, half8 out[4]) const
     {
-        const int k0 = 64 * c + 32 * hh;
-        const int rs = k0 / C;
-        const int coff = k0 - rs * C;
-        const int ih = r.p + rs / 3 - 1, iw = r.q + rs % 3 - 1;
-        const bool ok = r.ok && rs < 9 && ih >= 0 && ih < H && iw >= 0 && iw < W;
-        const half_t* p = x + (((long)r.n * H + (ok ? ih : 0)) * W + (ok ? iw : 0)) * C + coff;
+        // An opaque copy of W keeps the compiler from hoisting every chunk's
+        // tap offset out of the tile loop (nine values held across the whole
+        // loop would spill); recomputing one is a couple of scalar operations.
+        int w = W;
+        asm volatile("" : "+s"(w));
 #pragma unroll
-        for (int q = 0; q < 4; ++q) out[q] = ld16_if(p + 8 * q, ok);
+        for (int q = 0; q < 4; ++q) {
+            unsigned rs;
+            int coff, cc;
+            if (KCH == 9) {
+                rs = (unsigned)c;
+                coff = 16 * q + 8 * hh;
+                cc = 64;
+            } else {
+                const unsigned kq = 4u * c + q;          // k / 16
+                rs = fc16.div(kq);
+                coff = (int)(kq - rs * fc16.d) * 16 + 8 * hh;
+                cc = C;
+            }
+            const int rr = (int)((rs * 11u) >> 5);       // rs / 3 for rs < 32
+            const int ss = (int)rs - 3 * rr;
+            const bool ok = (r.mask >> rs) & 1u;
+            const int delta = ((rr - 1) * w + (ss - 1)) * cc + coff;   // |delta| < (W + 2) C < 2^31
+            out[q] = ld16_if(r.pix + (ok ? delta : 0), ok);
+        }
     }
 };
 
 // ------------------------------------------- weights-resident conv kernel
-constexpr int CW_THREADS = 512;
-constexpr int CW_WAVES = CW_THREADS / 64;
 enum { EPI_STORE = 0, EPI_POOL = 1 };
+
+// With the chunk count known at compile time: CONVW_WPS waves per SIMD
+// (4 * CONVW_WPS per block, 512 / CONVW_WPS registers each) and a register
+// ring CONVW_RING pixel chunks deep.  Otherwise two waves per SIMD and a
+// two-deep ring.
+#ifndef CONVW_WPS
+#define CONVW_WPS 2
+#endif
+#ifndef CONVW_RING
+#define CONVW_RING 2
+#endif
+__host__ __device__ constexpr int convw_wps(int KCH) { return KCH > 0 ? CONVW_WPS : 2; }
+__host__ __device__ constexpr int convw_threads(int KCH) { return 256 * convw_wps(KCH); }
+__host__ __device__ constexpr int convw_ring(int KCH) { return KCH > 0 ? CONVW_RING : 2; }
 
 struct ConvWArgs {
     const half_t* x;   // [NB, H, W, C]
@@ -76,6 +150,9 @@ struct ConvWArgs {
     int act;
     long ntiles;       // 64-row tiles
     long tiles_per_block;
+    // row decoding: STORE: pixel = (n, p, q) with fa = P*Q, fb = Q;
+    // POOL: window = (n, i, j) with fa = (P/2)*(Q/2), fb = Q/2; fc16 = C/16
+    FastDiv fa, fb, fc16;
 };
 
 inline size_t convw_lds_bytes(int KP, int Kp)
@@ -95,10 +172,12 @@ inline size_t convw_lds_bytes(int KP, int Kp)
 // KCH: compile-time number of 64-wide k chunks (0 = runtime loop), see the
 // register-resident chain kernel.
 template <int NTK, int EPI, int KCH>
-__global__ __launch_bounds__(CW_THREADS) __attribute__((amdgpu_waves_per_eu(1, 2)))
+__global__ __launch_bounds__(convw_threads(KCH)) __attribute__((amdgpu_waves_per_eu(1, convw_wps(KCH))))
 void k_conv_w(ConvWArgs a)
 {
     constexpr int KP = 32 * NTK;
+    constexpr int NTHR = convw_threads(KCH);
+    constexpr int NWAVES = NTHR / 64;
     extern __shared__ __align__(16) char smem[];
     typedef FC_LDS float lds_float;
     WTile Wn;   // natural layout [Kp][KP] (rows = (r, s, c))
@@ -111,147 +190,267 @@ void k_conv_w(ConvWArgs a)
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int lr = lane & 31, hh = lane >> 5;
-    const long t_begin = (long)blockIdx.x * a.tiles_per_block;
+    const long t_begin = (long)xcd_block(blockIdx.x, gridDim.x) * a.tiles_per_block;
     const long t_end = min(t_begin + a.tiles_per_block, a.ntiles);
     const int nch = KCH ? KCH : a.Kp >> 6;
-    const int PO = a.H >> 1, QO = a.W >> 1;
-    const long nrows = EPI == EPI_POOL ? (long)a.NB * PO * QO * 4 : (long)a.NB * a.H * a.W;
+    const long nrows = EPI == EPI_POOL ? (long)a.NB * (a.H >> 1) * (a.W >> 1) * 4 : (long)a.NB * a.H * a.W;
 
     Conv3x3Rows ld;
     ld.x = a.x; ld.H = a.H; ld.W = a.W; ld.C = a.C; ld.M = (long)a.NB * a.H * a.W;
+    ld.fc16 = a.fc16;
 
     // GEMM row -> conv output pixel
     auto make_row = [&](long gr) -> Conv3x3Rows::Row {
-        Conv3x3Rows::Row r;
-        r.ok = gr < nrows;
-        const long g = r.ok ? gr : 0;
+        const bool ok = gr < nrows;
+        const unsigned g = ok ? (unsigned)gr : 0u;
+        unsigned n, p, q;
         if (EPI == EPI_POOL) {
-            const long win = g >> 2;
-            const int e = (int)(g & 3);
-            const long pq = (long)PO * QO;
-            r.n = (int)(win / pq);
-            const int rem = (int)(win - (long)r.n * pq);
-            const int i = rem / QO, j = rem - (rem / QO) * QO;
-            r.p = 2 * i + (e >> 1);
-            r.q = 2 * j + (e & 1);
+            const unsigned win = g >> 2, e = g & 3u;
+            n = a.fa.div(win);
+            const unsigned rem = win - n * a.fa.d;
+            const unsigned i = a.fb.div(rem);
+            p = 2 * i + (e >> 1);
+            q = 2 * (rem - i * a.fb.d) + (e & 1u);
         } else {
-            const long hw = (long)a.H * a.W;
-            r.n = (int)(g / hw);
-            const int rem = (int)(g - (long)r.n * hw);
-            r.p = rem / a.W;
-            r.q = rem - r.p * a.W;
+            n = a.fa.div(g);
+            const unsigned rem = g - n * a.fa.d;
+            p = a.fb.div(rem);
+            q = rem - p * a.fb.d;
         }
-        return r;
+        return ld.make((int)n, (int)p, (int)q, ok);
+    };
+    auto claim = [&]() -> long {
+        int nt = 0;
+        if (lane == 0) nt = __hip_atomic_fetch_add(next_tile, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        return __builtin_amdgcn_readfirstlane(nt);
     };
 
-    // Chunks alternate between two register sets by name (chunk c in set
-    // c % 2, loop unrolled by two): no loaded register is ever copied.
+    // Ring depth: chunk g of a wave's chunk sequence lives in register set
+    // g % R, named at compile time (the chunk loops are fully unrolled, and a
+    // copy of a loaded register would force a wait on the loads in flight).
+    constexpr int R = convw_ring(KCH);
+    constexpr int PD = R - 1;   // chunks in flight ahead of the one in use
+    static_assert(KCH == 0 || (2 * KCH) % R == 0, "two tiles of chunks must fill whole ring turns");
+    half8 ring[R][2][4];
+
     long tile = t_begin + wave;
     Conv3x3Rows::Row rows[2];
-    half8 xa[2][4], xb[2][4];
     if (tile < t_end) {
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
             rows[u] = make_row(tile * 64 + 32 * u + lr);
-            ld.load(rows[u], 0, hh, xa[u]);
+#pragma unroll
+            for (int p = 0; p < PD; ++p)
+                if (p < nch) ld.template load<KCH>(rows[u], p, hh, ring[p][u]);
         }
     }
 
-    stage_natural<8>(a.w, a.Kr, a.K, a.K, a.Kp, KP, Wn, tid, CW_THREADS);
-    for (int i = tid; i < KP; i += CW_THREADS) bs[i] = (a.b && i < a.K) ? (float)a.b[i] : 0.0f;
-    if (tid == 0) *next_tile = (int)(t_begin + CW_WAVES);
+    stage_natural<8>(a.w, a.Kr, a.K, a.K, a.Kp, KP, Wn, tid, NTHR);
+    for (int i = tid; i < KP; i += NTHR) bs[i] = (a.b && i < a.K) ? (float)a.b[i] : 0.0f;
+    if (tid == 0) *next_tile = (int)(t_begin + NWAVES);
     __syncthreads();
 
     // Per-lane parts of the W fragment addresses: column k_out = 32t + lane%32,
-    // rows 64c + 32hh + 8q + [0,8) (the k this lane's pixel loads cover).
+    // rows 64c + 16q + 8hh + [0,8) (the k this lane's pixel loads cover).
     const lds_half* wlane[NTK];
 #pragma unroll
-    for (int t = 0; t < NTK; ++t) wlane[t] = Wn.p + frag_lane_off(Wn, 32 * t, lane) + 32 * hh * Wn.ld;
+    for (int t = 0; t < NTK; ++t) wlane[t] = Wn.p + frag_lane_off(Wn, 32 * t, lane) + 8 * hh * Wn.ld;
 
-    while (tile < t_end) {
-        floatx16 acc[2][NTK];
+    auto mma_chunk = [&](int c, const half8 (&cur)[2][4], floatx16 (&acc)[2][NTK]) {
 #pragma unroll
-        for (int u = 0; u < 2; ++u)
+        for (int q = 0; q < 4; ++q) {
 #pragma unroll
-            for (int t = 0; t < NTK; ++t) acc[u][t] = zero16();
-
-        auto step = [&](int c, const half8 (&cur)[2][4], half8 (&nxt)[2][4]) {
-            if (c + 1 < nch) {
-                ld.load(rows[0], c + 1, hh, nxt[0]);
-                ld.load(rows[1], c + 1, hh, nxt[1]);
+            for (int t = 0; t < NTK; ++t) {
+                const half8 wv = frag_tr_at(wlane[t] + (64 * c + 16 * q) * Wn.ld, 4 * Wn.ld);
+                acc[0][t] = mfma32x32x16(cur[0][q], wv, acc[0][t]);
+                acc[1][t] = mfma32x32x16(cur[1][q], wv, acc[1][t]);
             }
-            __builtin_amdgcn_sched_barrier(0);   // keep the prefetch issued here
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
+        }
+    };
+
+    // Epilogue.  Lane holds output channel k = 32t + lr; register r of
+    // tile (u, t) is GEMM row tile*64 + 32u + 8(r/4) + 4hh + (r%4).
+    // Addresses are 32-bit offsets from the tile's first output row: a
+    // per-lane part plus a part that is uniform across the wave.  The opaque
+    // copy of K keeps the compiler from hoisting every store's offset out of
+    // the tile loop (dozens of values held across the loop would spill).
+    // Rows past the end are masked per store (no early exits).
+    auto epilogue = [&](long tl, const floatx16 (&acc)[2][NTK]) {
+        const long row0 = tl * 64;
+        int K = a.K;
+        asm volatile("" : "+s"(K));
+        act_dispatch(a.act, [&](auto act) {
+            if (EPI == EPI_POOL) {
+                // window w of the tile = GEMM rows 4w..4w+3 (w = 8u + 2g + hh);
+                // windows are enumerated like y's pixels
+                const long win0 = row0 >> 2;
+                half_t* yb = a.y + win0 * K;
+                uint8_t* ab = a.argmax ? a.argmax + win0 * K : nullptr;
+                const int nw = (int)min(16L, (nrows >> 2) - win0);
+                const int olane = hh * K + lr;
 #pragma unroll
                 for (int t = 0; t < NTK; ++t) {
-                    const half8 wv = frag_tr_at(wlane[t] + (64 * c + 8 * q) * Wn.ld, 4 * Wn.ld);
-                    acc[0][t] = mfma32x32x16(cur[0][q], wv, acc[0][t]);
-                    acc[1][t] = mfma32x32x16(cur[1][q], wv, acc[1][t]);
+                    const float bk = bs[32 * t + lr];
+                    const bool kok = 32 * t + lr < K;
+#pragma unroll
+                    for (int u = 0; u < 2; ++u) {
+#pragma unroll
+                        for (int g = 0; g < 4; ++g) {
+                            // round each value to fp16 first: the pooled value
+                            // and its argmax are decided on the fp16 intermediate
+                            half_t best = (half_t)act.f(acc[u][t][4 * g] + bk);
+                            int bi = 0;
+#pragma unroll
+                            for (int e = 1; e < 4; ++e) {
+                                const half_t v = (half_t)act.f(acc[u][t][4 * g + e] + bk);
+                                const bool gt = v > best;
+                                best = gt ? v : best;
+                                bi = gt ? e : bi;
+                            }
+                            const int w0 = 8 * u + 2 * g;
+                            if (kok && hh < nw - w0) {
+                                const int o = olane + w0 * K + 32 * t;
+                                yb[o] = best;
+                                if (ab) ab[o] = (uint8_t)bi;
+                            }
+                        }
+                        // bound the scheduling window
+                        __builtin_amdgcn_sched_barrier(0);
+                    }
                 }
-            }
-        };
+            } else {
+                half_t* yb = a.y + row0 * K;
+                const int nr = (int)min(64L, nrows - row0);
+                const int olane = 4 * hh * K + lr;
 #pragma unroll
-        for (int c = 0; c < nch; c += 2) {
-            step(c, xa, xb);
-            if (c + 1 < nch) step(c + 1, xb, xa);
-        }
-
-        // Claim the next tile and put its first chunk in flight.
-        int nt = 0;
-        if (lane == 0) nt = __hip_atomic_fetch_add(next_tile, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-        nt = __shfl(nt, 0);
-        const long ntile = nt;
-        Conv3x3Rows::Row nrows_[2] = {rows[0], rows[1]};
-        if (ntile < t_end) {
+                for (int t = 0; t < NTK; ++t) {
+                    const float bk = bs[32 * t + lr];
+                    const bool kok = 32 * t + lr < K;
 #pragma unroll
-            for (int u = 0; u < 2; ++u) {
-                nrows_[u] = make_row(ntile * 64 + 32 * u + lr);
-                ld.load(nrows_[u], 0, hh, xa[u]);
-            }
-        }
-
-        // Epilogue.  Lane holds output channel k = 32t + lr; register r of
-        // tile (u, t) is GEMM row tile*64 + 32u + 8(r/4) + 4hh + (r%4).
+                    for (int u = 0; u < 2; ++u) {
 #pragma unroll
-        for (int t = 0; t < NTK; ++t) {
-            const int k = 32 * t + lr;
-            const float bk = bs[k];
-            const bool kok = k < a.K;
-#pragma unroll
-            for (int u = 0; u < 2; ++u) {
-#pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    const long gr0 = tile * 64 + 32 * u + 8 * g + 4 * hh;
-                    if (EPI == EPI_POOL) {
-                        const long win = gr0 >> 2;
-                        if (!kok || gr0 >= nrows) continue;
-                        // round each value to fp16 first: the pooled value and
-                        // its argmax are decided on the fp16 intermediate
-                        float best = (float)(half_t)act_apply(a.act, acc[u][t][4 * g] + bk);
-                        int bi = 0;
-#pragma unroll
-                        for (int e = 1; e < 4; ++e) {
-                            const float v = (float)(half_t)act_apply(a.act, acc[u][t][4 * g + e] + bk);
-                            if (v > best) { best = v; bi = e; }
+                        for (int r = 0; r < 16; ++r) {
+                            const int r0 = 32 * u + 8 * (r >> 2) + (r & 3);   // row minus 4hh
+                            if (kok && 4 * hh < nr - r0)
+                                yb[olane + r0 * K + 32 * t] = (half_t)act.f(acc[u][t][r] + bk);
                         }
-                        const long o = win * a.K + k;   // windows are enumerated like y's pixels
-                        a.y[o] = (half_t)best;
-                        if (a.argmax) a.argmax[o] = (uint8_t)bi;
-                    } else {
-                        if (!kok) continue;
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            const long gr = gr0 + e;
-                            if (gr < nrows) a.y[gr * a.K + k] = (half_t)act_apply(a.act, acc[u][t][4 * g + e] + bk);
-                        }
+                        __builtin_amdgcn_sched_barrier(0);
                     }
                 }
             }
+        });
+    };
+
+    if constexpr (KCH > 0) {
+        // One tile = KCH chunks; its chunk c sits in set (SB + c) % R, where
+        // SB = (tiles done * KCH) % R takes the two values 0 and KCH % R.
+        // While the tile's last PD chunks are multiplied, the next tile's
+        // first PD chunks are loaded.
+        // W fragments are software-pipelined one k-step (16 k) ahead: step
+        // s = 4c + q uses set s % 2 while set (s + 1) % 2 is read from LDS,
+        // and the first step's fragments (the same for every tile) are read
+        // during the previous tile's last step.  The scheduling groups
+        // interleave each step's eight MFMAs with the next step's eight LDS
+        // reads, so the LDS latency hides under the matrix core.
+        half8 wf[2][NTK];
+#pragma unroll
+        for (int t = 0; t < NTK; ++t) wf[0][t] = frag_tr_at(wlane[t], 4 * Wn.ld);
+        auto body = [&](auto sb) {
+            constexpr int SB = decltype(sb)::value;
+            // The next tile's loads are issued even when there is no next
+            // tile (its rows then lie past the end, read the zero line and
+            // are never used): a load under a branch would make the wait
+            // counts after it assume the fewest loads in flight, i.e. wait
+            // for the prefetches too.
+            const long ntile = claim();
+            Conv3x3Rows::Row nrows_[2];
+#pragma unroll
+            for (int u = 0; u < 2; ++u) nrows_[u] = make_row(min(ntile, t_end) * 64 + 32 * u + lr);
+            floatx16 acc[2][NTK];
+#pragma unroll
+            for (int u = 0; u < 2; ++u)
+#pragma unroll
+                for (int t = 0; t < NTK; ++t) acc[u][t] = zero16();
+#pragma unroll
+            for (int c = 0; c < KCH; ++c) {
+                const int cl = c + PD;
+                if (cl < KCH) {
+                    ld.template load<KCH>(rows[0], cl, hh, ring[(SB + cl) % R][0]);
+                    ld.template load<KCH>(rows[1], cl, hh, ring[(SB + cl) % R][1]);
+                } else {
+                    ld.template load<KCH>(nrows_[0], cl - KCH, hh, ring[(SB + cl) % R][0]);
+                    ld.template load<KCH>(nrows_[1], cl - KCH, hh, ring[(SB + cl) % R][1]);
+                }
+                __builtin_amdgcn_sched_barrier(0);   // keep the prefetch issued here
+                const half8 (&cur)[2][4] = ring[(SB + c) % R];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int s = 4 * c + q;
+                    const int sn = (s + 1) % (4 * KCH);   // next step (wraps to the next tile)
+                    const int cn = sn >> 2, qn = sn & 3;
+#pragma unroll
+                    for (int t = 0; t < NTK; ++t)
+                        wf[(s + 1) & 1][t] = frag_tr_at(wlane[t] + (64 * cn + 16 * qn) * Wn.ld, 4 * Wn.ld);
+#pragma unroll
+                    for (int t = 0; t < NTK; ++t) {
+                        acc[0][t] = mfma32x32x16(cur[0][q], wf[s & 1][t], acc[0][t]);
+                        acc[1][t] = mfma32x32x16(cur[1][q], wf[s & 1][t], acc[1][t]);
+                    }
+#pragma unroll
+                    for (int i = 0; i < 2 * NTK; ++i) {
+                        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+                        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read
+                    }
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            epilogue(tile, acc);
+            tile = ntile;
+            rows[0] = nrows_[0];
+            rows[1] = nrows_[1];
+        };
+        while (tile < t_end) {
+            body(IntC<0>{});
+            if constexpr (KCH % R != 0) {
+                if (tile >= t_end) break;
+                body(IntC<KCH % R>{});
+            }
         }
-        tile = ntile;
-        rows[0] = nrows_[0];
-        rows[1] = nrows_[1];
+    } else {
+        // Runtime chunk count: two sets, the loop unrolled by two.
+        while (tile < t_end) {
+            floatx16 acc[2][NTK];
+#pragma unroll
+            for (int u = 0; u < 2; ++u)
+#pragma unroll
+                for (int t = 0; t < NTK; ++t) acc[u][t] = zero16();
+            auto step = [&](int c, const half8 (&cur)[2][4], half8 (&nxt)[2][4]) {
+                if (c + 1 < nch) {
+                    ld.template load<KCH>(rows[0], c + 1, hh, nxt[0]);
+                    ld.template load<KCH>(rows[1], c + 1, hh, nxt[1]);
+                }
+                __builtin_amdgcn_sched_barrier(0);   // keep the prefetch issued here
+                mma_chunk(c, cur, acc);
+            };
+            for (int c = 0; c < nch; c += 2) {
+                step(c, ring[0], ring[1]);
+                if (c + 1 < nch) step(c + 1, ring[1], ring[0]);
+            }
+            // Claim the next tile and put its first chunk in flight.
+            const long ntile = claim();
+            Conv3x3Rows::Row nrows_[2] = {rows[0], rows[1]};
+            if (ntile < t_end) {
+#pragma unroll
+                for (int u = 0; u < 2; ++u) {
+                    nrows_[u] = make_row(ntile * 64 + 32 * u + lr);
+                    ld.template load<KCH>(nrows_[u], 0, hh, ring[0][u]);
+                }
+            }
+            epilogue(tile, acc);
+            tile = ntile;
+            rows[0] = nrows_[0];
+            rows[1] = nrows_[1];
+        }
     }
 }
 
@@ -262,12 +461,13 @@ static hipError_t launch_convw_k(ConvWArgs a, hipStream_t st)
     hipError_t e = hipFuncSetAttribute((const void*)k_conv_w<NTK, EPI, KCH>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
+    constexpr int nwaves = convw_threads(KCH) / 64;
     long grid = device_cu_count();
-    if (grid * CW_WAVES > a.ntiles) grid = (a.ntiles + CW_WAVES - 1) / CW_WAVES;
+    if (grid * nwaves > a.ntiles) grid = (a.ntiles + nwaves - 1) / nwaves;
     if (grid < 1) grid = 1;
     a.tiles_per_block = (a.ntiles + grid - 1) / grid;
     grid = (a.ntiles + a.tiles_per_block - 1) / a.tiles_per_block;
-    hipLaunchKernelGGL((k_conv_w<NTK, EPI, KCH>), dim3((unsigned)grid), dim3(CW_THREADS), lds, st, a);
+    hipLaunchKernelGGL((k_conv_w<NTK, EPI, KCH>), dim3((unsigned)grid), dim3(convw_threads(KCH)), lds, st, a);
     return hipGetLastError();
 }
 
@@ -306,6 +506,9 @@ hipError_t run_conv_bias_act3x3(const half_t* x, const half_t* w, const half_t* 
     const long rows = (long)NB * H * W;
     if (rows == 0) return hipSuccess;
     a.ntiles = (rows + 63) / 64;
+    a.fa = FastDiv::make((unsigned)H * (unsigned)W);
+    a.fb = FastDiv::make((unsigned)W);
+    a.fc16 = FastDiv::make((unsigned)C / 16);
     return launch_convw<EPI_STORE>(a, st);
 }
 
@@ -319,6 +522,9 @@ hipError_t run_conv_pool3x3(const half_t* x, const half_t* w, const half_t* b, i
     const long rows = (long)NB * (H / 2) * (W / 2) * 4;
     if (rows == 0) return hipSuccess;
     a.ntiles = (rows + 63) / 64;
+    a.fa = FastDiv::make((unsigned)(H / 2) * (unsigned)(W / 2));
+    a.fb = FastDiv::make((unsigned)(W / 2));
+    a.fc16 = FastDiv::make((unsigned)C / 16);
     return launch_convw<EPI_POOL>(a, st);
 }
 
@@ -338,6 +544,7 @@ hipError_t run_chain_conv2_3x3(const half_t* x, const half_t* w0, const half_t* 
     a.tiles_per_block = 0;
     Conv3x3Rows ld;
     ld.x = x; ld.H = H; ld.W = W; ld.C = C; ld.M = M;
+    ld.set_divisors();
     return launch_rf(ld, a, (K0 + 31) / 32, st);
 }
 

@@ -78,22 +78,52 @@ __device__ __forceinline__ half8 ld16_if(const half_t* p, bool ok)
     return ld16(ok ? p : zero_ptr());
 }
 
-// Element-wise activation in fp32 (the epilogue's element-wise operator).
-// GELU, tanh form: 0.5 x (1 + tanh(u)) with u = sqrt(2/pi) (x + 0.044715 x^3).
-// Since 0.5 (1 + tanh(u)) = 1 / (1 + e^{-2u}), this evaluates
-// x / (1 + 2^{-2u log2 e}) with the hardware base-2 exponential and
-// reciprocal: no cancellation near 0, and the exponential saturating to 0 or
-// infinity gives x or 0 at the extremes.
-__device__ __forceinline__ float act_apply(int act, float x)
-{
-    if (act == ACT_RELU) return x > 0.0f ? x : 0.0f;
-    if (act == ACT_GELU_TANH) {
-        const float k2 = 2.0f * 0.7978845608028654f * 1.4426950408889634f;  // 2 sqrt(2/pi) log2(e)
-        float u = x + 0.044715f * x * x * x;
-        float e = __builtin_amdgcn_exp2f(-k2 * u);
-        return x * __builtin_amdgcn_rcpf(1.0f + e);
+// Element-wise activation in fp32 (the epilogue's element-wise operator),
+// fixed at compile time so that an epilogue is straight-line code the
+// scheduler can interleave.  GELU, tanh form: 0.5 x (1 + tanh(u)) with
+// u = sqrt(2/pi) (x + 0.044715 x^3).  Since 0.5 (1 + tanh(u)) = 1/(1 + e^{-2u}),
+// this evaluates x / (1 + 2^q) with q = -2 log2(e) sqrt(2/pi) x (1 + 0.044715 x^2)
+// by the hardware base-2 exponential and reciprocal: no cancellation near 0,
+// and the exponential saturating to 0 or infinity gives x or 0 at the extremes.
+template <int ACT> struct Act;
+template <> struct Act<ACT_NONE> {
+    __device__ static __forceinline__ float f(float x) { return x; }
+};
+template <> struct Act<ACT_RELU> {
+    __device__ static __forceinline__ float f(float x) { return x > 0.0f ? x : 0.0f; }
+};
+template <> struct Act<ACT_GELU_TANH> {
+    __device__ static __forceinline__ float f(float x)
+    {
+        const float c1 = -2.0f * 0.7978845608028654f * 1.4426950408889634f;   // -2 sqrt(2/pi) log2(e)
+        const float c3 = c1 * 0.044715f;
+        const float q = x * __builtin_fmaf(x * x, c3, c1);
+        return x * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(q));
     }
-    return x;
+};
+
+template <int V> struct IntC {
+    static constexpr int value = V;
+};
+
+// Workgroups are dispatched round-robin over the 8 XCDs (block b runs on XCD
+// b % 8), and each XCD has its own L2.  This renumbering gives every XCD a
+// contiguous range of block indices, so neighbouring tiles (which share halo
+// rows or weights) meet in the same L2.  A bijection of [0, n) when 8 | n;
+// the identity otherwise.
+__device__ __forceinline__ unsigned xcd_block(unsigned b, unsigned n)
+{
+    return (n & 7u) ? b : (b & 7u) * (n >> 3) + (b >> 3);
+}
+
+// Calls f(Act<act>{}) with the activation as a compile-time type: the branch
+// on the (wave-uniform) activation is taken once per epilogue, not per element.
+template <class F>
+__device__ __forceinline__ void act_dispatch(int act, F&& f)
+{
+    if (act == ACT_GELU_TANH) f(Act<ACT_GELU_TANH>{});
+    else if (act == ACT_RELU) f(Act<ACT_RELU>{});
+    else f(Act<ACT_NONE>{});
 }
 
 // Transposed staging of a row-major fp16 matrix G [rows x cols] (leading

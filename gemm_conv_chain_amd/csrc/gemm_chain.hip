@@ -208,21 +208,23 @@ void k_gemm_lds(LdsArgs a)
         // free after the last barrier), then line-coalesced row stores.
         constexpr int LDO0 = N0P + 8;
         lds_half* Ot = Wb;
+        act_dispatch(a.act, [&](auto act) {
 #pragma unroll
-        for (int t = 0; t < NT0W; ++t) {
+            for (int t = 0; t < NT0W; ++t) {
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int nl = nb0 + 32 * t + 8 * g + 4 * hh;
-                const floatx4 bb = *reinterpret_cast<lds_float4*>(b0s + nl);
+                for (int g = 0; g < 4; ++g) {
+                    const int nl = nb0 + 32 * t + 8 * g + 4 * hh;
+                    const floatx4 bb = *reinterpret_cast<lds_float4*>(b0s + nl);
 #pragma unroll
-                for (int u = 0; u < 2; ++u) {
-                    half4 o;
+                    for (int u = 0; u < 2; ++u) {
+                        half4 o;
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) o[e] = (half_t)act_apply(a.act, acc[t][u][4 * g + e] + bb[e]);
-                    *reinterpret_cast<lds_half4*>(Ot + (64 * wm + 32 * u + lr) * LDO0 + nl) = o;
+                        for (int e = 0; e < 4; ++e) o[e] = (half_t)act.f(acc[t][u][4 * g + e] + bb[e]);
+                        *reinterpret_cast<lds_half4*>(Ot + (64 * wm + 32 * u + lr) * LDO0 + nl) = o;
+                    }
                 }
             }
-        }
+        });
         __syncthreads();
         store_tile(Ot, LDO0, LDS_MT, N0P, a.out, a.N0, m_blk, a.M, n_base, a.N0, tid, LDS_THREADS);
         return;
@@ -233,21 +235,23 @@ void k_gemm_lds(LdsArgs a)
     wchunk_load<NV1>(a.W1, a.N0, a.N1, a.N1, 0, LDS_N1C, tid, w1r);
 
     // ------- accumulator-fragment -> LDS iterator: H = fp16(act(C0 + b0)) -------
+    act_dispatch(a.act, [&](auto act) {
 #pragma unroll
-    for (int t = 0; t < NT0W; ++t) {
+        for (int t = 0; t < NT0W; ++t) {
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-            const int n0 = nb0 + 32 * t + 8 * g + 4 * hh;
-            const floatx4 bb = *reinterpret_cast<lds_float4*>(b0s + n0);
+            for (int g = 0; g < 4; ++g) {
+                const int n0 = nb0 + 32 * t + 8 * g + 4 * hh;
+                const floatx4 bb = *reinterpret_cast<lds_float4*>(b0s + n0);
 #pragma unroll
-            for (int u = 0; u < 2; ++u) {
-                half4 o;
+                for (int u = 0; u < 2; ++u) {
+                    half4 o;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) o[e] = (half_t)act_apply(a.act, acc[t][u][4 * g + e] + bb[e]);
-                *reinterpret_cast<lds_half4*>(Hs + (64 * wm + 32 * u + lr) * LDH + n0) = o;
+                    for (int e = 0; e < 4; ++e) o[e] = (half_t)act.f(acc[t][u][4 * g + e] + bb[e]);
+                    *reinterpret_cast<lds_half4*>(Hs + (64 * wm + 32 * u + lr) * LDH + n0) = o;
+                }
             }
         }
-    }
+    });
     // (the barrier closing the last GEMM0 iteration released both weight
     //  buffers; the barrier below publishes H and W1 chunk 0)
 

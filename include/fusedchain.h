@@ -116,9 +116,9 @@ fc_status chain_gemm2_variant(const fc_half *A, const fc_half *W0, const fc_half
  *   pool == FC_POOL_NONE: y [n, P, Q, k] = act(conv + b) (argmax must be NULL).
  * Implemented shapes: r = s = 3, stride 1, pad 1, c % 32 == 0 (pad channels
  * with pad_channels first), k % 8 == 0 and k <= 128 (all output channels in
- * one block), and the weights, held in LDS for the whole kernel, within
- * 160 KiB: roundup(k,32) * (roundup(9c,64) + 8) * 2 bytes (c = 64: k <= 128;
- * c = 128: k <= 64).  Others: FC_E_UNSUPPORTED.
+ * one block), n*h*w < 2^31, and the weights, held in LDS for the whole
+ * kernel, within 160 KiB: roundup(k,32) * (roundup(9c,64) + 8) * 2 bytes
+ * (c = 64: k <= 128; c = 128: k <= 64).  Others: FC_E_UNSUPPORTED.
  */
 fc_status chain_conv_pool(const fc_half *x, const fc_half *w, const fc_half *b, fc_act act, fc_pool pool,
                           fc_half *y, const fc_conv_shape *shape, uint8_t *argmax, void *stream);
@@ -130,7 +130,7 @@ fc_status chain_conv_pool(const fc_half *x, const fc_half *w, const fc_half *b, 
  *   x NHWC [n,h,w,c], w0 HWIO [3,3,c,k0] (k0 = shape0->k), b0 [k0],
  *   w1 [k0 x k1] (= HWIO [1,1,k0,k1]), b1 [k1], y NHWC [n,P,Q,k1].
  * Implemented: r = s = 3, stride 1, pad 1, c % 32 == 0, k0 % 8 == 0 and
- * k0 <= 128, k1 % 8 == 0, and both weights fit in LDS together.
+ * k0 <= 128, k1 % 8 == 0, n*h*w < 2^31, and both weights fit in LDS together.
  */
 fc_status chain_conv2(const fc_half *x, const fc_half *w0, const fc_half *b0, fc_act act,
                       const fc_half *w1, const fc_half *b1, int32_t k1, fc_half *y,

@@ -87,6 +87,12 @@ def test_conv_validation(L):
     # weights-resident kernels: the HWIO weights must fit in LDS
     assert L.chain_conv_pool(P, P, NUL, 1, 1, P2, ctypes.byref(shape(c=96, k=96)), NUL, None) == E_UNSUP
     assert L.chain_conv2(P, P, NUL, 1, P, NUL, 64, P2, ctypes.byref(shape(c=64, k=128)), None) == E_UNSUP
+    # pixel indices are decoded in 32 bits: n*h*w must stay below 2^31
+    big = shape(n=32768, h=256, w=256)
+    assert L.chain_conv_pool(P, P, NUL, 1, 1, P2, ctypes.byref(big), NUL, None) == E_UNSUP
+    assert L.chain_conv2(P, P, NUL, 1, P, NUL, 64, P2, ctypes.byref(shape(n=32768, h=256, w=256, k=64)),
+                         None) == E_UNSUP
+    assert b"2^31" in L.fc_last_error()
 
 
 def test_empty_tensors_may_be_null(L):
