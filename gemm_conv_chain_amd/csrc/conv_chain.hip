@@ -134,6 +134,12 @@ enum { EPI_STORE = 0, EPI_POOL = 1 };
 #ifndef CONVW_RING
 #define CONVW_RING 2
 #endif
+#ifndef CONVW_WPIPE   // W fragments read one k-step ahead (1) or just in time (0)
+#define CONVW_WPIPE 0
+#endif
+#ifndef CONVW_DESYNC  // start offset of the second wave on each SIMD, in units of ~8K clocks
+#define CONVW_DESYNC 0
+#endif
 __host__ __device__ constexpr int convw_wps(int KCH) { return KCH > 0 ? CONVW_WPS : 2; }
 __host__ __device__ constexpr int convw_threads(int KCH) { return 256 * convw_wps(KCH); }
 __host__ __device__ constexpr int convw_ring(int KCH) { return KCH > 0 ? CONVW_RING : 2; }
@@ -155,9 +161,12 @@ struct ConvWArgs {
     FastDiv fa, fb, fc16;
 };
 
+// LDS: weights [Kp][KP] (natural, swizzled or padded), biases, the tile
+// counter, then a 1 KiB output staging area per wave.
+constexpr int CW_OSTAGE = 1024;
 inline size_t convw_lds_bytes(int KP, int Kp)
 {
-    return (size_t)Kp * wtile_ld(KP) * 2 + (size_t)KP * 4 + 16;
+    return (size_t)Kp * wtile_ld(KP) * 2 + (size_t)KP * 4 + 16 + (size_t)8 * CW_OSTAGE;
 }
 
 // One wave = 64 GEMM rows (two 32-row MFMA tiles) x all K output channels.
@@ -186,6 +195,7 @@ void k_conv_w(ConvWArgs a)
     Wn.swz = wtile_swz(KP);
     lds_float* bs = (lds_float*)(Wn.p + a.Kp * Wn.ld);
     FC_LDS int* next_tile = (FC_LDS int*)(bs + KP);
+    static_assert(convw_threads(KCH) <= 512, "eight staging areas");
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
@@ -230,18 +240,95 @@ void k_conv_w(ConvWArgs a)
     // copy of a loaded register would force a wait on the loads in flight).
     constexpr int R = convw_ring(KCH);
     constexpr int PD = R - 1;   // chunks in flight ahead of the one in use
+    static_assert(KCH == 0 || KCH == 9, "the compile-time path is the C = 64 one");
     static_assert(KCH == 0 || (2 * KCH) % R == 0, "two tiles of chunks must fill whole ring turns");
     half8 ring[R][2][4];
 
+    // ---- quad-coalesced rows (compile-time path, C = 64) ----
+    // Lane 4i + m loads, for tile row 4i + j (j = 0..3), the 16-byte segment
+    // m of each 64-byte half h of the pixel's 128 bytes in chunk c (tap c):
+    // ring[.][h][j]; every quad of lanes reads 64 contiguous bytes.  The
+    // in-quad transpose and the half swap turn these into the MFMA operands
+    // of row tiles u = 0, 1 (tile rows 32u + lane%32), the same layout the
+    // runtime-chunk path loads directly.  POOL: tile row 4i + j is element
+    // j = 2dy + dx of the tile's window i; STORE: pixel tile*64 + 4i + j.
+    const int qi = lane >> 2, qm = lane & 3;
+    // A lane's four tile rows: the pixel of row j is base + off(j) with
+    // off(j) = (dy W + dx) C (POOL, the window's 2x2 pixels) or j C (STORE,
+    // consecutive pixels are C apart); bits 6j..6j+5 hold the tap masks of
+    // row j: rows r (bits 6j + r) and columns s (bits 6j + 3 + s) of the 3x3
+    // window that lie inside the image (all 0 for a row past the end).
+    struct QRows {
+        const half_t* base;
+        unsigned bits;
+    };
+    auto tap_bits = [&](int p, int q, bool ok) -> unsigned {
+        const unsigned rm = 2u | (p > 0 ? 1u : 0u) | (p < a.H - 1 ? 4u : 0u);
+        const unsigned sm = 2u | (q > 0 ? 1u : 0u) | (q < a.W - 1 ? 4u : 0u);
+        return ok ? rm | (sm << 3) : 0u;
+    };
+    auto make_qrows = [&](long tl) -> QRows {
+        QRows r;
+        r.bits = 0;
+        if (EPI == EPI_POOL) {
+            const long wi = tl * 16 + qi;
+            const bool ok = wi < (nrows >> 2);
+            const unsigned g = ok ? (unsigned)wi : 0u;
+            const unsigned n = a.fa.div(g);
+            const unsigned rem = g - n * a.fa.d;
+            const unsigned i = a.fb.div(rem);
+            const unsigned j = rem - i * a.fb.d;
+            r.base = a.x + (((long)n * a.H + 2 * i) * a.W + 2 * j) * 64;
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj)
+                r.bits |= tap_bits((int)(2 * i) + (jj >> 1), (int)(2 * j) + (jj & 1), ok) << (6 * jj);
+        } else {
+            const long g0 = tl * 64 + 4 * qi;
+            r.base = a.x + min(g0, nrows - 1) * 64;
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+                const long gr = g0 + jj;
+                const bool ok = gr < nrows;
+                const unsigned g = ok ? (unsigned)gr : 0u;
+                const unsigned n = a.fa.div(g);
+                const unsigned rem = g - n * a.fa.d;
+                const unsigned p = a.fb.div(rem);
+                r.bits |= tap_bits((int)p, (int)(rem - p * a.fb.d), ok) << (6 * jj);
+            }
+        }
+        return r;
+    };
+    auto load_q = [&](const QRows& r, int c, half8 (&A)[2][4]) {
+        // An opaque copy of W keeps every chunk's tap offset from being
+        // hoisted out of the tile loop (held across the loop, they spill).
+        int w = a.W;
+        asm volatile("" : "+s"(w));
+        const int rr = c / 3, ss = c % 3;
+        const int delta = ((rr - 1) * w + (ss - 1)) * 64 + 8 * qm;
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+            const bool ok = (r.bits >> (6 * jj + rr)) & (r.bits >> (6 * jj + 3 + ss)) & 1u;
+            const int off = EPI == EPI_POOL ? ((jj >> 1) * w + (jj & 1)) * 64 : jj * 64;
+            const half_t* p = r.base + (delta + off);
+#pragma unroll
+            for (int h = 0; h < 2; ++h) A[h][jj] = ld16_if(p + 32 * h, ok);
+        }
+    };
+
     long tile = t_begin + wave;
     Conv3x3Rows::Row rows[2];
+    QRows qrows;
     if (tile < t_end) {
+        if constexpr (KCH > 0) {
+            qrows = make_qrows(tile);
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            rows[u] = make_row(tile * 64 + 32 * u + lr);
+            for (int p = 0; p < PD; ++p) load_q(qrows, p, ring[p]);
+        } else {
 #pragma unroll
-            for (int p = 0; p < PD; ++p)
-                if (p < nch) ld.template load<KCH>(rows[u], p, hh, ring[p][u]);
+            for (int u = 0; u < 2; ++u) {
+                rows[u] = make_row(tile * 64 + 32 * u + lr);
+                ld.template load<KCH>(rows[u], 0, hh, ring[0][u]);
+            }
         }
     }
 
@@ -251,47 +338,45 @@ void k_conv_w(ConvWArgs a)
     __syncthreads();
 
     // Per-lane parts of the W fragment addresses: column k_out = 32t + lane%32,
-    // rows 64c + 16q + 8hh + [0,8) (the k this lane's pixel loads cover).
+    // rows 64c + 16q + 8hh + [0,8) (the k the lane's operand holds at step q).
     const lds_half* wlane[NTK];
 #pragma unroll
     for (int t = 0; t < NTK; ++t) wlane[t] = Wn.p + frag_lane_off(Wn, 32 * t, lane) + 8 * hh * Wn.ld;
 
-    auto mma_chunk = [&](int c, const half8 (&cur)[2][4], floatx16 (&acc)[2][NTK]) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-#pragma unroll
-            for (int t = 0; t < NTK; ++t) {
-                const half8 wv = frag_tr_at(wlane[t] + (64 * c + 16 * q) * Wn.ld, 4 * Wn.ld);
-                acc[0][t] = mfma32x32x16(cur[0][q], wv, acc[0][t]);
-                acc[1][t] = mfma32x32x16(cur[1][q], wv, acc[1][t]);
-            }
-        }
-    };
-
-    // Epilogue.  Lane holds output channel k = 32t + lr; register r of
-    // tile (u, t) is GEMM row tile*64 + 32u + 8(r/4) + 4hh + (r%4).
-    // Addresses are 32-bit offsets from the tile's first output row: a
-    // per-lane part plus a part that is uniform across the wave.  The opaque
-    // copy of K keeps the compiler from hoisting every store's offset out of
-    // the tile loop (dozens of values held across the loop would spill).
-    // Rows past the end are masked per store (no early exits).
+    // Epilogue.  Lane holds output channel k = 32t + lr; register r = 4g + e
+    // of tile (u, t) is tile row 32u + 8g + 4hh + e, so registers 4g..4g+3
+    // hold the four elements of pool window 8u + 2g + hh.  Results go through
+    // this wave's 1 KiB LDS staging area as [16 rows][32 channels] fp16 and
+    // leave as 16-byte stores, four lanes per 64 contiguous bytes (2-byte
+    // stores from every lane would cost the address unit a clock per lane).
+    lds_half* const ost = (lds_half*)((FC_LDS char*)(next_tile + 4) + wave * CW_OSTAGE);
+    typedef FC_LDS half8 lds_half8;
     auto epilogue = [&](long tl, const floatx16 (&acc)[2][NTK]) {
         const long row0 = tl * 64;
         int K = a.K;
-        asm volatile("" : "+s"(K));
+        asm volatile("" : "+s"(K));   // keeps per-store offsets from being hoisted out of the tile loop
+        const int rr = lane >> 2, grp = lane & 3;   // read-back: staged row, 8-channel group
+        // per-lane bases; every (u, g, e, t) adds a constant (LDS instruction offsets)
+        lds_half* const ow = ost + hh * 32 + lr;
+        const lds_float* const bsl = bs + lr;
+        const lds_half8* const orb = reinterpret_cast<const lds_half8*>(ost + rr * 32 + 8 * grp);
         act_dispatch(a.act, [&](auto act) {
             if (EPI == EPI_POOL) {
-                // window w of the tile = GEMM rows 4w..4w+3 (w = 8u + 2g + hh);
                 // windows are enumerated like y's pixels
                 const long win0 = row0 >> 2;
                 half_t* yb = a.y + win0 * K;
                 uint8_t* ab = a.argmax ? a.argmax + win0 * K : nullptr;
                 const int nw = (int)min(16L, (nrows >> 2) - win0);
+                // comparisons keep the per-lane value on one side and the
+                // wave-uniform remainder on the other, so no per-(t, u, g)
+                // lane value is precomputed and held
                 const int olane = hh * K + lr;
+                int nwl = nw - hh;   // window 8u + 2g + hh is valid iff 8u + 2g < nwl
+                asm volatile("" : "+v"(nwl));   // (opaque: compared against constants, not folded back)
 #pragma unroll
                 for (int t = 0; t < NTK; ++t) {
-                    const float bk = bs[32 * t + lr];
-                    const bool kok = 32 * t + lr < K;
+                    const float bk = bsl[32 * t];
+                    const bool kok = lr < K - 32 * t;
 #pragma unroll
                     for (int u = 0; u < 2; ++u) {
 #pragma unroll
@@ -308,33 +393,42 @@ void k_conv_w(ConvWArgs a)
                                 bi = gt ? e : bi;
                             }
                             const int w0 = 8 * u + 2 * g;
-                            if (kok && hh < nw - w0) {
-                                const int o = olane + w0 * K + 32 * t;
-                                yb[o] = best;
-                                if (ab) ab[o] = (uint8_t)bi;
-                            }
+                            ow[w0 * 32] = best;
+                            if (ab && kok && w0 < nwl) ab[olane + w0 * K + 32 * t] = (uint8_t)bi;
                         }
-                        // bound the scheduling window
-                        __builtin_amdgcn_sched_barrier(0);
+                        __builtin_amdgcn_sched_barrier(0);   // bound the scheduling window
                     }
+                    wave_lds_sync();
+                    const half8 v = *orb;
+                    if (rr < nw && 8 * grp < K - 32 * t)
+                        *reinterpret_cast<half8*>(yb + rr * K + 32 * t + 8 * grp) = v;
+                    wave_lds_sync();   // the next t overwrites the staging area
                 }
             } else {
                 half_t* yb = a.y + row0 * K;
                 const int nr = (int)min(64L, nrows - row0);
-                const int olane = 4 * hh * K + lr;
 #pragma unroll
                 for (int t = 0; t < NTK; ++t) {
-                    const float bk = bs[32 * t + lr];
-                    const bool kok = 32 * t + lr < K;
+                    const float bk = bsl[32 * t];
 #pragma unroll
                     for (int u = 0; u < 2; ++u) {
 #pragma unroll
-                        for (int r = 0; r < 16; ++r) {
-                            const int r0 = 32 * u + 8 * (r >> 2) + (r & 3);   // row minus 4hh
-                            if (kok && 4 * hh < nr - r0)
-                                yb[olane + r0 * K + 32 * t] = (half_t)act.f(acc[u][t][r] + bk);
+                        for (int eh = 0; eh < 2; ++eh) {
+                            // staged row (e % 2) * 8 + 2g + hh for e = 2eh, 2eh + 1
+#pragma unroll
+                            for (int g = 0; g < 4; ++g)
+#pragma unroll
+                                for (int e = 2 * eh; e < 2 * eh + 2; ++e)
+                                    ow[((e & 1) * 8 + 2 * g) * 32] = (half_t)act.f(acc[u][t][4 * g + e] + bk);
+                            wave_lds_sync();
+                            // staged row rr -> tile row
+                            const int e = 2 * eh + (rr >> 3), g = (rr & 7) >> 1, h1 = rr & 1;
+                            const int row = 32 * u + 8 * g + 4 * h1 + e;
+                            const half8 v = *orb;
+                            if (row < nr && 8 * grp < K - 32 * t)
+                                *reinterpret_cast<half8*>(yb + row * K + 32 * t + 8 * grp) = v;
+                            wave_lds_sync();
                         }
-                        __builtin_amdgcn_sched_barrier(0);
                     }
                 }
             }
@@ -353,8 +447,10 @@ void k_conv_w(ConvWArgs a)
         // interleave each step's eight MFMAs with the next step's eight LDS
         // reads, so the LDS latency hides under the matrix core.
         half8 wf[2][NTK];
+        if (CONVW_WPIPE) {
 #pragma unroll
-        for (int t = 0; t < NTK; ++t) wf[0][t] = frag_tr_at(wlane[t], 4 * Wn.ld);
+            for (int t = 0; t < NTK; ++t) wf[0][t] = frag_tr_at(wlane[t], 4 * Wn.ld);
+        }
         auto body = [&](auto sb) {
             constexpr int SB = decltype(sb)::value;
             // The next tile's loads are issued even when there is no next
@@ -363,9 +459,7 @@ void k_conv_w(ConvWArgs a)
             // counts after it assume the fewest loads in flight, i.e. wait
             // for the prefetches too.
             const long ntile = claim();
-            Conv3x3Rows::Row nrows_[2];
-#pragma unroll
-            for (int u = 0; u < 2; ++u) nrows_[u] = make_row(min(ntile, t_end) * 64 + 32 * u + lr);
+            const QRows nq = make_qrows(min(ntile, t_end));
             floatx16 acc[2][NTK];
 #pragma unroll
             for (int u = 0; u < 2; ++u)
@@ -374,41 +468,58 @@ void k_conv_w(ConvWArgs a)
 #pragma unroll
             for (int c = 0; c < KCH; ++c) {
                 const int cl = c + PD;
-                if (cl < KCH) {
-                    ld.template load<KCH>(rows[0], cl, hh, ring[(SB + cl) % R][0]);
-                    ld.template load<KCH>(rows[1], cl, hh, ring[(SB + cl) % R][1]);
-                } else {
-                    ld.template load<KCH>(nrows_[0], cl - KCH, hh, ring[(SB + cl) % R][0]);
-                    ld.template load<KCH>(nrows_[1], cl - KCH, hh, ring[(SB + cl) % R][1]);
-                }
+                if (cl < KCH) load_q(qrows, cl, ring[(SB + cl) % R]);
+                else load_q(nq, cl - KCH, ring[(SB + cl) % R]);
                 __builtin_amdgcn_sched_barrier(0);   // keep the prefetch issued here
-                const half8 (&cur)[2][4] = ring[(SB + c) % R];
+                half8 (&cur)[2][4] = ring[(SB + c) % R];
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const int s = 4 * c + q;
-                    const int sn = (s + 1) % (4 * KCH);   // next step (wraps to the next tile)
-                    const int cn = sn >> 2, qn = sn & 3;
+                for (int h = 0; h < 2; ++h) {
+                    quad_transpose4(cur[h], lane);
 #pragma unroll
-                    for (int t = 0; t < NTK; ++t)
-                        wf[(s + 1) & 1][t] = frag_tr_at(wlane[t] + (64 * cn + 16 * qn) * Wn.ld, 4 * Wn.ld);
+                    for (int sp = 0; sp < 2; ++sp) {
+                        const int q = 2 * h + sp;
+                        half8 x0 = cur[h][2 * sp], x1 = cur[h][2 * sp + 1];
+                        swap_halves(x0, x1);   // x0: row tile 0, x1: row tile 1; k-halves 2q, 2q + 1
+                        const int st = 4 * c + q;
+                        if (CONVW_WPIPE) {
+                            const int sn = (st + 1) % (4 * KCH);   // next step (wraps to the next tile)
+                            const int cn = sn >> 2, qn = sn & 3;
 #pragma unroll
-                    for (int t = 0; t < NTK; ++t) {
-                        acc[0][t] = mfma32x32x16(cur[0][q], wf[s & 1][t], acc[0][t]);
-                        acc[1][t] = mfma32x32x16(cur[1][q], wf[s & 1][t], acc[1][t]);
-                    }
+                            for (int t = 0; t < NTK; ++t)
+                                wf[(st + 1) & 1][t] = frag_tr_at(wlane[t] + (64 * cn + 16 * qn) * Wn.ld, 4 * Wn.ld);
 #pragma unroll
-                    for (int i = 0; i < 2 * NTK; ++i) {
-                        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
-                        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read
+                            for (int t = 0; t < NTK; ++t) {
+                                acc[0][t] = mfma32x32x16(x0, wf[st & 1][t], acc[0][t]);
+                                acc[1][t] = mfma32x32x16(x1, wf[st & 1][t], acc[1][t]);
+                            }
+#pragma unroll
+                            for (int i = 0; i < 2 * NTK; ++i) {
+                                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+                                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read
+                            }
+                        } else {
+#pragma unroll
+                            for (int t = 0; t < NTK; ++t) {
+                                const half8 wv = frag_tr_at(wlane[t] + (64 * c + 16 * q) * Wn.ld, 4 * Wn.ld);
+                                acc[0][t] = mfma32x32x16(x0, wv, acc[0][t]);
+                                acc[1][t] = mfma32x32x16(x1, wv, acc[1][t]);
+                            }
+                        }
                     }
                 }
                 __builtin_amdgcn_sched_barrier(0);
             }
             epilogue(tile, acc);
             tile = ntile;
-            rows[0] = nrows_[0];
-            rows[1] = nrows_[1];
+            qrows = nq;
         };
+        // The two waves sharing a SIMD (w, w + 4) start half a tile apart, so
+        // that one's epilogue and transposes (vector ALU) overlap the other's
+        // MFMAs instead of both waves switching phase together.
+        if (CONVW_DESYNC > 0 && wave >= 4) {
+#pragma unroll
+            for (int i = 0; i < CONVW_DESYNC; ++i) __builtin_amdgcn_s_sleep(127);
+        }
         while (tile < t_end) {
             body(IntC<0>{});
             if constexpr (KCH % R != 0) {
@@ -417,7 +528,19 @@ void k_conv_w(ConvWArgs a)
             }
         }
     } else {
-        // Runtime chunk count: two sets, the loop unrolled by two.
+        // Runtime chunk count: two sets, the loop unrolled by two; rows of
+        // MFMA row tile u are tile rows 32u + lane%32 (operand layout loads).
+        auto mma_chunk = [&](int c, const half8 (&cur)[2][4], floatx16 (&acc)[2][NTK]) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+#pragma unroll
+                for (int t = 0; t < NTK; ++t) {
+                    const half8 wv = frag_tr_at(wlane[t] + (64 * c + 16 * q) * Wn.ld, 4 * Wn.ld);
+                    acc[0][t] = mfma32x32x16(cur[0][q], wv, acc[0][t]);
+                    acc[1][t] = mfma32x32x16(cur[1][q], wv, acc[1][t]);
+                }
+            }
+        };
         while (tile < t_end) {
             floatx16 acc[2][NTK];
 #pragma unroll

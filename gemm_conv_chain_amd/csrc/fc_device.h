@@ -20,6 +20,7 @@ typedef _Float16 half_t;
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef _Float16 half4 __attribute__((ext_vector_type(4)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 
 // Pointers into LDS carry address space 3 explicitly, so every access compiles
@@ -116,6 +117,63 @@ __device__ __forceinline__ unsigned xcd_block(unsigned b, unsigned n)
     return (n & 7u) ? b : (b & 7u) * (n >> 3) + (b >> 3);
 }
 
+// ---- quad-coalesced MFMA operand loads -------------------------------------
+// The texture addresser takes a 16-byte-per-lane load at four lanes per clock
+// when each group of four consecutive lanes reads one 64-byte segment, and at
+// one lane per clock otherwise.  MFMA operand layouts put a different row in
+// every lane of a quad, so rows are loaded quad-wise (lane 4i + m reads
+// segment m of row group i) and moved into operand layout in registers: a 4x4
+// transpose inside every quad (two DPP exchange stages), then a swap of lane
+// halves between two registers.
+
+__device__ __forceinline__ unsigned dpp_quad_xor2(unsigned v)
+{
+    return (unsigned)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, true);   // quad_perm [2,3,0,1]
+}
+__device__ __forceinline__ unsigned dpp_quad_xor1(unsigned v)
+{
+    return (unsigned)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, true);   // quad_perm [1,0,3,2]
+}
+
+// In every quad (lanes 4i..4i+3): a[r] at quad lane j  ->  a[j] at quad lane r.
+__device__ __forceinline__ void quad_transpose4(half8 (&a)[4], int lane)
+{
+    const bool b1 = (lane >> 1) & 1, b0 = lane & 1;
+    u32x4 x[4], y[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) x[r] = __builtin_bit_cast(u32x4, a[r]);
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+            const unsigned o = dpp_quad_xor2(x[r ^ 2][d]);
+            y[r][d] = (b1 == (bool)((r >> 1) & 1)) ? x[r][d] : o;
+        }
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+            const unsigned o = dpp_quad_xor1(y[r ^ 1][d]);
+            x[r][d] = (b0 == (bool)(r & 1)) ? y[r][d] : o;
+        }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) a[r] = __builtin_bit_cast(half8, x[r]);
+}
+
+// lo = [lo lanes 0-31 | hi lanes 0-31], hi = [lo lanes 32-63 | hi lanes 32-63].
+__device__ __forceinline__ void swap_halves(half8& lo, half8& hi)
+{
+    u32x4 x = __builtin_bit_cast(u32x4, lo), y = __builtin_bit_cast(u32x4, hi);
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+        const auto p = __builtin_amdgcn_permlane32_swap(x[d], y[d], false, false);
+        x[d] = p[0];
+        y[d] = p[1];
+    }
+    lo = __builtin_bit_cast(half8, x);
+    hi = __builtin_bit_cast(half8, y);
+}
+
 // Calls f(Act<act>{}) with the activation as a compile-time type: the branch
 // on the (wave-uniform) activation is taken once per epilogue, not per element.
 template <class F>
@@ -136,7 +194,6 @@ __device__ __forceinline__ void act_dispatch(int act, F&& f)
 // each group of 16 slots, the quad swap 0-3,4-7,8-11,12-15 -> 0-3,8-11,4-7,12-15:
 // the order in which a 32x32 accumulator hands rows to a lane (the
 // register-resident hand-off of the chain kernels).
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
 struct TBlock {

@@ -126,22 +126,39 @@ void k_gemm_lds(LdsArgs a)
     const int ncols0 = a.N0 - n_base;        // columns of W0 this block reads
     const half_t* W0b = a.W0 + n_base;
 
-    long mrow[2];
-    bool mok[2];
+    // A rows, quad-coalesced: lane 4i + m reads rows 4i + j (j = 0..3) of the
+    // wave's 64, 16-byte segment m of each 64-byte half h of a 64-wide k
+    // chunk, so every quad of lanes reads 64 contiguous bytes (the address
+    // unit then takes four lanes per clock instead of one).  The in-quad
+    // transpose and the half swap turn raw[h][j] into the MFMA operands
+    // op[u][s] (rows 32u + lane%32, k = 64c + 16s + 8(lane/32) + [0,8)).
+    const int qi = lane >> 2, qm = lane & 3;
+    const half_t* arow[4];
+    bool aok[4];
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-        mrow[u] = m_blk + 64 * wm + 32 * u + lr;
-        mok[u] = mrow[u] < a.M;
+    for (int j = 0; j < 4; ++j) {
+        const long r = m_blk + 64 * wm + 4 * qi + j;
+        aok[j] = r < a.M;
+        arow[j] = a.A + (aok[j] ? r : 0) * (long)a.K0 + 8 * qm;
     }
-    const half_t* arow[2] = {a.A + (mok[0] ? mrow[0] : 0) * (long)a.K0, a.A + (mok[1] ? mrow[1] : 0) * (long)a.K0};
-    // A chunk c for this lane: k = 64c + 16s + 8hh + [0,8), s = 0..3, both row tiles
     auto load_a = [&](int c, half8 (&af)[2][4]) {
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
+        for (int h = 0; h < 2; ++h) {
+            const int k = LDS_KC * c + 32 * h + 8 * qm;
 #pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                const int k = LDS_KC * c + 16 * s + 8 * hh;
-                af[u][s] = ld16_if(arow[u] + k, mok[u] && k < a.K0);
+            for (int j = 0; j < 4; ++j) af[h][j] = ld16_if(arow[j] + LDS_KC * c + 32 * h, aok[j] && k < a.K0);
+        }
+    };
+    auto to_operand = [&](half8 (&raw)[2][4], half8 (&op)[2][4]) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            quad_transpose4(raw[h], lane);
+#pragma unroll
+            for (int sp = 0; sp < 2; ++sp) {
+                half8 x0 = raw[h][2 * sp], x1 = raw[h][2 * sp + 1];
+                swap_halves(x0, x1);
+                op[0][2 * h + sp] = x0;
+                op[1][2 * h + sp] = x1;
             }
         }
     };
@@ -170,11 +187,13 @@ void k_gemm_lds(LdsArgs a)
     const int nb0 = wn * NT0W * 32;
 
     // ---------------- GEMM0 (transposed: C0^T = W0^T A^T) ----------------
-    auto step0 = [&](int c, const half8 (&cur)[2][4], half8 (&ld2)[2][4]) {
+    auto step0 = [&](int c, half8 (&raw)[2][4], half8 (&ld2)[2][4]) {
         const bool more = c + 1 < nch0;
         if (more) wchunk_load<NV0>(W0b, a.K0, ncols0, a.N0, LDS_KC * (c + 1), N0P, tid, w0r);
         if (c + 2 < nch0) load_a(c + 2, ld2);
         __builtin_amdgcn_sched_barrier(0);   // keep the prefetches issued here
+        half8 cur[2][4];
+        to_operand(raw, cur);
         const lds_half* wb = Wb + (c & 1) * WBUF;
         half8 wf[2][NT0W];
 #pragma unroll
