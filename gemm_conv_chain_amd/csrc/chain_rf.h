@@ -32,9 +32,6 @@
 
 namespace fc {
 
-#ifndef RF_STAGGER   // s_sleep units (64 clocks) the second half of the waves waits before its row loads
-#define RF_STAGGER 0
-#endif
 constexpr int RF_THREADS = 512;
 constexpr int RF_WAVES = RF_THREADS / 64;
 constexpr int RF_WB = 16;   // weight vectors (16 bytes) per thread staged ahead of the row stream
@@ -131,7 +128,6 @@ void k_chain_rf(Loader ld, RfArgs a)
         bp = a.b1 + (tid - N0P);
     }
     const half_t bias = *bp;
-    if (RF_STAGGER > 0 && wave >= RF_WAVES / 2) __builtin_amdgcn_s_sleep(RF_STAGGER);
     if (tile < t_end) {
         row = ld.row(tile * 32 + lr);
 #pragma unroll

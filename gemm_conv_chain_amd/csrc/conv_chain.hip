@@ -137,9 +137,6 @@ enum { EPI_STORE = 0, EPI_POOL = 1 };
 #ifndef CONVW_WPIPE   // W fragments read one k-step ahead (1) or just in time (0)
 #define CONVW_WPIPE 0
 #endif
-#ifndef CONVW_DESYNC  // start offset of the second wave on each SIMD, in units of ~8K clocks
-#define CONVW_DESYNC 0
-#endif
 __host__ __device__ constexpr int convw_wps(int KCH) { return KCH > 0 ? CONVW_WPS : 2; }
 __host__ __device__ constexpr int convw_threads(int KCH) { return 256 * convw_wps(KCH); }
 __host__ __device__ constexpr int convw_ring(int KCH) { return KCH > 0 ? CONVW_RING : 2; }
@@ -513,13 +510,6 @@ void k_conv_w(ConvWArgs a)
             tile = ntile;
             qrows = nq;
         };
-        // The two waves sharing a SIMD (w, w + 4) start half a tile apart, so
-        // that one's epilogue and transposes (vector ALU) overlap the other's
-        // MFMAs instead of both waves switching phase together.
-        if (CONVW_DESYNC > 0 && wave >= 4) {
-#pragma unroll
-            for (int i = 0; i < CONVW_DESYNC; ++i) __builtin_amdgcn_s_sleep(127);
-        }
         while (tile < t_end) {
             body(IntC<0>{});
             if constexpr (KCH % R != 0) {
