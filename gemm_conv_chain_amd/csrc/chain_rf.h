@@ -293,8 +293,8 @@ template <int NT0, int KCH, class Loader>
 static hipError_t launch_rf_k(const Loader& ld, RfArgs a, hipStream_t st)
 {
     const size_t lds = rf_lds_bytes(32 * NT0, a.K0p, a.N1p);
-    hipError_t e = hipFuncSetAttribute((const void*)k_chain_rf<NT0, KCH, Loader>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    static std::atomic<unsigned long long> lds_set{0};
+    hipError_t e = allow_full_lds((const void*)k_chain_rf<NT0, KCH, Loader>, &lds_set);
     if (e != hipSuccess) return e;
     const long per_block_min = RF_WAVES;  // at least one tile per wave
     long grid = device_cu_count();

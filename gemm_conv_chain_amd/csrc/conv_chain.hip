@@ -571,8 +571,8 @@ template <int NTK, int EPI, int KCH>
 static hipError_t launch_convw_k(ConvWArgs a, hipStream_t st)
 {
     const size_t lds = convw_lds_bytes(32 * NTK, a.Kp);
-    hipError_t e = hipFuncSetAttribute((const void*)k_conv_w<NTK, EPI, KCH>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    static std::atomic<unsigned long long> lds_set{0};
+    hipError_t e = allow_full_lds((const void*)k_conv_w<NTK, EPI, KCH>, &lds_set);
     if (e != hipSuccess) return e;
     constexpr int nwaves = convw_threads(KCH) / 64;
     long grid = device_cu_count();

@@ -1,6 +1,7 @@
 // fc_launch.h -- host-side launch functions behind the C ABI (internal).
 #pragma once
 #include <hip/hip_runtime.h>
+#include <atomic>
 
 namespace fc {
 
@@ -11,6 +12,21 @@ enum { VARIANT_AUTO = 0, VARIANT_RF = 1, VARIANT_LDS = 2 };
 // LDS a block may use (gfx950: 160 KiB per CU; one block of the persistent
 // kernels per CU).
 constexpr size_t RF_LDS_LIMIT = 160 * 1024;
+
+// Lets kernel f use the whole LDS on the current device.  The attribute is
+// set once per device (bit d of *done); launches then need no extra call,
+// which also keeps them capturable in a HIP graph.
+inline hipError_t allow_full_lds(const void* f, std::atomic<unsigned long long>* done)
+{
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    const unsigned long long bit = dev < 64 ? 1ull << dev : 0ull;
+    if (bit && (done->load(std::memory_order_relaxed) & bit)) return hipSuccess;
+    e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)RF_LDS_LIMIT);
+    if (e == hipSuccess && bit) done->fetch_or(bit, std::memory_order_relaxed);
+    return e;
+}
 
 int device_cu_count();
 bool rf_fits(int K0, int N0, int N1);

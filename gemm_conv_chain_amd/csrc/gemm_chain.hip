@@ -347,26 +347,28 @@ void k_gemm_lds(LdsArgs a)
 
 // ----------------------------------------------------------------- launchers
 
-static int g_num_cu = 0;
-
+// Compute units of the current device (cached per device; 256 if unknown).
 int device_cu_count()
 {
-    if (g_num_cu == 0) {
-        int dev = 0;
-        hipDeviceProp_t p;
-        if (hipGetDevice(&dev) == hipSuccess && hipGetDeviceProperties(&p, dev) == hipSuccess)
-            g_num_cu = p.multiProcessorCount;
-        if (g_num_cu <= 0) g_num_cu = 256;
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 256;
+    if (dev >= 0 && dev < 64) {
+        const int c = cache[dev].load(std::memory_order_relaxed);
+        if (c > 0) return c;
     }
-    return g_num_cu;
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    if (dev >= 0 && dev < 64) cache[dev].store(n, std::memory_order_relaxed);
+    return n;
 }
 
 template <int NT0W, bool CHAIN, int KCH>
 static hipError_t launch_lds_k(const LdsArgs& a, hipStream_t st)
 {
     const size_t lds = lds_lds_bytes(64 * NT0W, CHAIN);
-    hipError_t e = hipFuncSetAttribute((const void*)k_gemm_lds<NT0W, CHAIN, KCH>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    static std::atomic<unsigned long long> lds_set{0};
+    hipError_t e = allow_full_lds((const void*)k_gemm_lds<NT0W, CHAIN, KCH>, &lds_set);
     if (e != hipSuccess) return e;
     const unsigned gx = (unsigned)((a.M + LDS_MT - 1) / LDS_MT);
     const unsigned gy = CHAIN ? 1u : (unsigned)((a.N0 + 64 * NT0W - 1) / (64 * NT0W));
