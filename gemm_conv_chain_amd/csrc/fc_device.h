@@ -372,11 +372,13 @@ struct WStage2 {
     long ldg0, ldg1;
     WTile T0, T1;
     int nv0, nvt;    // vectors of matrix 0; of both
+    bool dense;      // both matrices fill their tiles exactly and are contiguous in memory
 
     __device__ __forceinline__ void init()
     {
         nv0 = nr0 * (ncp0 >> 3);
         nvt = nv0 + nr1 * (ncp1 >> 3);
+        dense = rows0 == nr0 && cols0 == ncp0 && ldg0 == cols0 && rows1 == nr1 && cols1 == ncp1 && ldg1 == cols1;
     }
     template <bool STORE>
     __device__ __forceinline__ void walk(int v0, int nthreads)
@@ -420,7 +422,22 @@ struct WStage2 {
             }
         }
     }
-    __device__ __forceinline__ void load(int v0, int nthreads) { walk<false>(v0, nthreads); }
+    // Loads: vector v of a dense pair is simply the 8 halves at G0 + 8v (or
+    // G1 + 8(v - nv0)), a few operations per vector instead of the walk.
+    __device__ __forceinline__ void load(int v0, int nthreads)
+    {
+        if (!dense) {
+            walk<false>(v0, nthreads);
+            return;
+        }
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+            const int v = v0 + i * nthreads;
+            if (v - (int)(threadIdx.x & 63) >= nvt) break;   // the whole wave is past the end
+            const half_t* src = v < nv0 ? G0 + 8L * v : G1 + 8L * (v - nv0);
+            x[i] = *reinterpret_cast<const u32x4*>(v < nvt ? src : zero_ptr());
+        }
+    }
     __device__ __forceinline__ void store(int v0, int nthreads) { walk<true>(v0, nthreads); }
 };
 
