@@ -24,9 +24,12 @@ def dev(a):
     return None if a is None else torch.from_numpy(np.ascontiguousarray(a)).cuda()
 
 
-def check_pool(y, am, x_np, w_np, b_np, what):
+ACTS = {"none": oracle.ACT_NONE, "relu": oracle.ACT_RELU, "gelu_tanh": oracle.ACT_GELU_TANH}
+
+
+def check_pool(y, am, x_np, w_np, b_np, what, act="relu"):
     """y, am from the GPU; oracle on the (unpadded) inputs."""
-    yo, amo, v, c64 = oracle.chain_conv_pool(x_np, w_np, b_np, oracle.ACT_RELU, want_conv64=True)
+    yo, amo, v, c64 = oracle.chain_conv_pool(x_np, w_np, b_np, ACTS[act], want_conv64=True)
     assert_close(y, yo.astype(np.float64), what)
     if am is not None:
         ties = pool_tie_mask(c64, c64.shape[1], c64.shape[2])
@@ -54,6 +57,46 @@ def test_conv_pool_small(fc, n, h, w, c, k):
     torch.cuda.synchronize()
     free, ties = check_pool(to_np(y), to_np(am), d["x"], d["w"], d["b"], "conv_pool small")
     assert free > 0
+
+
+@pytest.mark.parametrize("act", ["none", "gelu_tanh"])
+@pytest.mark.parametrize("c", [64, 32])
+def test_conv_pool_activations(fc, act, c):
+    # the pool decides on the fp16 activation output; argmax ties are
+    # checked as in check_pool (for "none" the post-activation values can be
+    # negative, so ties at zero are rare)
+    d = inputs.conv_pool_inputs(2, 10, 14, c, 96, seed=17)
+    print("case conv_pool act", act, "c", c, flush=True)
+    y, am = fc.chain_conv_pool(dev(d["x"]), dev(d["w"]), dev(d["b"]), act=act, pool="max2x2", argmax=True)
+    torch.cuda.synchronize()
+    free, _ = check_pool(to_np(y), to_np(am), d["x"], d["w"], d["b"], "conv_pool " + act, act=act)
+    assert free > 0
+
+
+def test_conv_pool_many_tiles_ragged(fc):
+    # several tiles per block and per wave, and a partial last tile (765
+    # windows = 47 full 16-window tiles + 13), C = 64 (compile-time chunk path)
+    d = inputs.conv_pool_inputs(3, 30, 34, 64, 128, seed=23)
+    print("case conv_pool 3x30x34x64->128", flush=True)
+    y, am = fc.chain_conv_pool(dev(d["x"]), dev(d["w"]), dev(d["b"]), argmax=True)
+    torch.cuda.synchronize()
+    check_pool(to_np(y), to_np(am), d["x"], d["w"], d["b"], "conv_pool many tiles")
+
+
+def test_conv_bias_act_many_tiles_ragged(fc):
+    # the unfused conv: 2*33*35 = 2310 pixels = 36 full 64-row tiles + 6 rows
+    d = inputs.conv_pool_inputs(2, 33, 35, 64, 128, seed=29)
+    print("case conv_bias_act 2x33x35x64->128", flush=True)
+    y = to_np(fc.conv_bias_act(dev(d["x"]), dev(d["w"]), dev(d["b"]), act="relu"))
+    assert_close(y, oracle.conv_bias_act(d["x"], d["w"], d["b"], oracle.ACT_RELU), "conv_bias_act many tiles")
+
+
+def test_conv2_gelu(fc):
+    d = inputs.conv2_inputs(2, 9, 11, 64, 64, 128, seed=31)
+    print("case conv2 gelu", flush=True)
+    y = to_np(fc.chain_conv2(dev(d["x"]), dev(d["w0"]), dev(d["b0"]), dev(d["w1"]), dev(d["b1"]), act="gelu_tanh"))
+    ref, _ = oracle.chain_conv2(d["x"], d["w0"], d["b0"], oracle.ACT_GELU_TANH, d["w1"], d["b1"])
+    assert_close(y, ref, "conv2 gelu")
 
 
 def test_conv_pool_padded_channels(fc):
