@@ -98,10 +98,12 @@ void k_chain_rf(Loader ld, RfArgs a)
     // Row chunks are held in a ring of R register sets.  With a compile-time
     // chunk count (KCH > 0) the chunk loop is fully unrolled and chunk c lives
     // in set c % R, so the ring rotates by name: PD = R - 1 chunks are always
-    // in flight ahead of the one being multiplied (for K0 = 256 that is the
-    // whole tile).  Loaded-HBM latency is far longer than the MFMA work of one
-    // chunk, so the depth, not the MFMA rate, sets the speed here.  KCH == 0
-    // (runtime chunk count) falls back to a two-set ring.
+    // in flight ahead of the one being multiplied.  Loaded-HBM latency is far
+    // longer than the MFMA work of one chunk, so the depth, not the MFMA rate,
+    // sets the speed here.  (Requesting all four chunks of a K0 = 256 tile in
+    // the prologue is slower: the extra requests delay the weight loads every
+    // wave waits for.)  KCH == 0 (runtime chunk count) falls back to a two-set
+    // ring.
     constexpr int R = KCH >= 4 ? 4 : (KCH > 0 ? KCH : 2);
     constexpr int PD = R - 1;
     long tile = t_begin + wave;

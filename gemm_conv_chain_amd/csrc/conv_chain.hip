@@ -398,7 +398,7 @@ void k_conv_w(ConvWArgs a)
                     wave_lds_sync();
                     const half8 v = *orb;
                     if (rr < nw && 8 * grp < K - 32 * t)
-                        *reinterpret_cast<half8*>(yb + rr * K + 32 * t + 8 * grp) = v;
+                        st_out(reinterpret_cast<half8*>(yb + rr * K + 32 * t + 8 * grp), v);
                     wave_lds_sync();   // the next t overwrites the staging area
                 }
             } else {
@@ -423,7 +423,7 @@ void k_conv_w(ConvWArgs a)
                             const int row = 32 * u + 8 * g + 4 * h1 + e;
                             const half8 v = *orb;
                             if (row < nr && 8 * grp < K - 32 * t)
-                                *reinterpret_cast<half8*>(yb + row * K + 32 * t + 8 * grp) = v;
+                                st_out(reinterpret_cast<half8*>(yb + row * K + 32 * t + 8 * grp), v);
                             wave_lds_sync();
                         }
                     }

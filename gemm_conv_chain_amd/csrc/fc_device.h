@@ -79,6 +79,19 @@ __device__ __forceinline__ half8 ld16_if(const half_t* p, bool ok)
     return ld16(ok ? p : zero_ptr());
 }
 
+// Final outputs are stored with the non-temporal hint (global_store ... nt):
+// they are not read again by the kernel, and without the hint they pile up as
+// dirty L2 lines that are written back only when the kernel ends, after the
+// last input has arrived.  Measured on the 64K-row b2b GEMM (reads 33 MB,
+// writes 17 MB): 16.6 -> 13.6 us.  (Non-temporal LOADS are slower there: the
+// operand layout reads each 128-byte line in four 32-byte pieces, and with
+// the hint the line is not kept in L2 between them.)
+template <class V>
+__device__ __forceinline__ void st_out(V* p, const V& v)
+{
+    __builtin_nontemporal_store(v, p);
+}
+
 // Element-wise activation in fp32 (the epilogue's element-wise operator),
 // fixed at compile time so that an epilogue is straight-line code the
 // scheduler can interleave.  GELU, tanh form: 0.5 x (1 + tanh(u)) with
@@ -454,7 +467,7 @@ __device__ __forceinline__ void store_tile(const lds_half* T, int ldt, int rows,
     for (int v = tid; v < rows * vpr; v += nthreads) {
         const int r = v / vpr, c = (v - r * vpr) * 8;
         if (row0 + r < nrows && col0 + c < ncols)
-            *reinterpret_cast<u32x4*>(out + (row0 + r) * ldo + col0 + c) = *reinterpret_cast<lds_u32x4*>(T + r * ldt + c);
+            st_out(reinterpret_cast<u32x4*>(out + (row0 + r) * ldo + col0 + c), (u32x4)*reinterpret_cast<lds_u32x4*>(T + r * ldt + c));
     }
 }
 
