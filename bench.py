@@ -51,7 +51,7 @@ def kernel_src_hash():
 class Problem:
     """Device buffers, step functions and the byte/FLOP model of one workload."""
 
-    def __init__(self, name, cold=True):
+    def __init__(self, name, cold=True, variant=None):
         import numpy as np
         import torch
 
@@ -60,6 +60,7 @@ class Problem:
 
         self.fc, self.torch, self.np = fc, torch, np
         self.name = name
+        self.traffic_key = name   # entry of the measured-traffic table
         self.spec, d = inputs.workload(name)
         self.host = d
         dev = torch.device("cuda:0")
@@ -80,10 +81,15 @@ class Problem:
             self.X = [A] + [A.clone() for _ in range(self.nsets - 1)]
             self.Y = [torch.empty((M, N1), dtype=torch.float16, device=dev) for _ in range(self.nsets)]
             self.H = torch.empty((M, N0), dtype=torch.float16, device=dev)
+            default = "rf" if name != "b2b_gemm_lds" else "lds"
+            if variant is None:
+                variant = default
+            if variant != default:
+                self.traffic_key = name + "@" + variant
             self.config = {"workload": name, "M": M, "K0": K0, "N0": N0, "N1": N1, "act": self.act,
-                           "variant": "rf" if name != "b2b_gemm_lds" else "lds",
+                           "variant": variant,
                            "dist": s["dist"] + "(-1,1)/sqrt(K)" if s["dist"] == "uniform" else "normal(0,1)/sqrt(K)"}
-            self.kernel = "k_chain_rf" if self.config["variant"] == "rf" else "k_gemm_lds"
+            self.kernel = {"rf": "k_chain_rf", "lds": "k_gemm_lds", "stream": "k_chain_stream"}[variant]
         elif s["kind"] == "conv2":
             n, h, w, c, k0, k1 = s["n"], s["h"], s["w"], s["c"], s["k0"], s["k1"]
             npix = n * h * w
@@ -127,7 +133,7 @@ class Problem:
         fc, j, s = self.fc, i % self.nsets, self.spec
         if s["kind"] == "gemm2":
             W0, b0, W1, b1 = self.W
-            fc.chain_gemm2(self.X[j], W0, b0, W1, b1, act=self.act, out=self.Y[j])
+            fc.chain_gemm2(self.X[j], W0, b0, W1, b1, act=self.act, out=self.Y[j], variant=self.config["variant"])
         elif s["kind"] == "conv2":
             w0, b0, w1, b1 = self.W
             fc.chain_conv2(self.X[j], w0, b0, w1, b1, act="relu", out=self.Y[j])
@@ -267,6 +273,8 @@ def main():
     ap.add_argument("--workload", default="b2b_gemm_rf",
                     choices=["b2b_gemm_tiny", "b2b_gemm_rf", "b2b_gemm_lds", "conv3x3_conv1x1",
                              "conv3x3_relu_maxpool"])
+    ap.add_argument("--variant", choices=["rf", "lds", "stream"], default=None,
+                    help="GEMM-chain kernel variant (default: rf, or lds for b2b_gemm_lds)")
     ap.add_argument("--warm", action="store_true", help="reuse one buffer set (cache-warm timing)")
     ap.add_argument("--no-unfused", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -287,7 +295,7 @@ def main():
     import gemm_conv_chain_amd as fc
     fc.lib()
 
-    prob = Problem(args.workload, cold=not args.warm)
+    prob = Problem(args.workload, cold=not args.warm, variant=args.variant)
     log("workload %s: %d buffer set(s), %.1f MB fused algorithmic bytes, %.3f GFLOP"
         % (args.workload, prob.nsets, prob.bytes_fused / 1e6, prob.flops / 1e9))
 
@@ -315,7 +323,7 @@ def main():
     ai = prob.flops / prob.bytes_fused
     ksec = ms_kernel * 1e-3
     h = kernel_src_hash()
-    tr = measured_traffic(args.workload, h)
+    tr = measured_traffic(prob.traffic_key, h)
     traffic = None
     if tr is not None:
         traffic = int(tr["fetch_kib"] * tr["fetch_scale"] * 1024 + tr["write_kib"] * tr["write_scale"] * 1024)

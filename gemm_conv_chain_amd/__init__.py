@@ -29,7 +29,7 @@ HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "fusedchain.h")
 
 ACT = {"none": 0, "relu": 1, "gelu_tanh": 2}
 POOL = {"none": 0, "max2x2": 1}
-VARIANT = {"auto": 0, "rf": 1, "lds": 2}
+VARIANT = {"auto": 0, "rf": 1, "lds": 2, "stream": 3}
 
 
 class FusedChainError(RuntimeError):

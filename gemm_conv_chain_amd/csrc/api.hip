@@ -108,13 +108,16 @@ fc_status chain_gemm2_variant(const fc_half* A, const fc_half* W0, const fc_half
         return fail(FC_E_ALIGN, "tensor pointers must be 16-byte aligned");
     fc_status s = check_act(act);
     if (s != FC_OK) return s;
-    if ((int)variant < 0 || (int)variant > 2) return fail(FC_E_ARG, "variant %d out of range", (int)variant);
+    if ((int)variant < 0 || (int)variant > 3) return fail(FC_E_ARG, "variant %d out of range", (int)variant);
     if (N0 > 256) return fail(FC_E_UNSUPPORTED, "N0=%d exceeds the residence limit of 256", N0);
     const bool rf_ok = N0 <= 128 && fc::rf_fits(K0, N0, N1);
+    const bool stream_ok = fc::stream_fits(N0, N1);
     int v = variant;
-    if (v == FC_VARIANT_AUTO) v = rf_ok ? fc::VARIANT_RF : fc::VARIANT_LDS;
+    if (v == FC_VARIANT_AUTO) v = rf_ok ? fc::VARIANT_RF : (stream_ok ? fc::VARIANT_STREAM : fc::VARIANT_LDS);
     if (v == FC_VARIANT_RF && !rf_ok)
         return fail(FC_E_UNSUPPORTED, "register-resident variant needs N0<=128 and W0,W1 within LDS");
+    if (v == FC_VARIANT_STREAM && !stream_ok)
+        return fail(FC_E_UNSUPPORTED, "streamed variant needs N1<=16128 (biases beside the weight buffers)");
     return hip_status(fc::run_chain_gemm2(H(A), H(W0), H(b0), act, H(W1), H(b1), Hm(D1), M, K0, N0, N1, v,
                                           (hipStream_t)stream),
                       "chain_gemm2");

@@ -7,7 +7,7 @@ namespace fc {
 
 typedef _Float16 half_t;
 
-enum { VARIANT_AUTO = 0, VARIANT_RF = 1, VARIANT_LDS = 2 };
+enum { VARIANT_AUTO = 0, VARIANT_RF = 1, VARIANT_LDS = 2, VARIANT_STREAM = 3 };
 
 // LDS a block may use (gfx950: 160 KiB per CU; one block of the persistent
 // kernels per CU).
@@ -30,6 +30,7 @@ inline hipError_t allow_full_lds(const void* f, std::atomic<unsigned long long>*
 
 int device_cu_count();
 bool rf_fits(int K0, int N0, int N1);
+bool stream_fits(int N0, int N1);
 
 hipError_t run_chain_gemm2(const half_t* A, const half_t* W0, const half_t* b0, int act, const half_t* W1,
                            const half_t* b1, half_t* D1, long M, int K0, int N0, int N1, int variant,

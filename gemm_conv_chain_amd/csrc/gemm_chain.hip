@@ -12,6 +12,7 @@
 // to shared memory (here: LDS) by an accumulator-fragment iterator, and every
 // wave of GEMM1 streams operand fragments of the whole row back from it.
 #include "chain_rf.h"
+#include "chain_stream.h"
 #include "fc_launch.h"
 
 namespace fc {
@@ -409,6 +410,14 @@ hipError_t run_chain_gemm2(const half_t* A, const half_t* W0, const half_t* b0, 
         ld.A = A; ld.M = M; ld.K = K0;
         return launch_rf(ld, a, (N0 + 31) / 32, st);
     }
+    if (variant == VARIANT_STREAM) {
+        StreamArgs a;
+        a.A = A; a.W0 = W0; a.b0 = b0; a.W1 = W1; a.b1 = b1; a.out = D1;
+        a.M = M; a.K0 = K0; a.N0 = N0; a.N1 = N1;
+        a.N1p = (N1 + CS_N1C - 1) / CS_N1C * CS_N1C;
+        a.ntiles = (M + CS_MT - 1) / CS_MT;
+        return launch_stream(a, act, st);
+    }
     LdsArgs a;
     a.A = A; a.W0 = W0; a.b0 = b0; a.W1 = W1; a.b1 = b1; a.out = D1;
     a.M = M; a.K0 = K0; a.N0 = N0; a.N1 = N1; a.act = act;
@@ -431,6 +440,11 @@ hipError_t run_gemm_bias_act(const half_t* A, const half_t* W, const half_t* b, 
     if (N <= 64) return launch_lds_t<1, false>(a, st);
     if (N <= 128) return launch_lds_t<2, false>(a, st);
     return launch_lds_t<4, false>(a, st);
+}
+
+bool stream_fits(int N0, int N1)
+{
+    return stream_fits_lds(N0, N1);
 }
 
 bool rf_fits(int K0, int N0, int N1)

@@ -67,7 +67,7 @@ typedef enum {
 
 typedef enum { FC_ACT_NONE = 0, FC_ACT_RELU = 1, FC_ACT_GELU_TANH = 2 } fc_act;
 typedef enum { FC_POOL_NONE = 0, FC_POOL_MAX_2X2_S2 = 1 } fc_pool;
-typedef enum { FC_VARIANT_AUTO = 0, FC_VARIANT_RF = 1, FC_VARIANT_LDS = 2 } fc_variant;
+typedef enum { FC_VARIANT_AUTO = 0, FC_VARIANT_RF = 1, FC_VARIANT_LDS = 2, FC_VARIANT_STREAM = 3 } fc_variant;
 
 /* x NHWC [n,h,w,c]; w HWIO [r,s,c,k]; output spatial size
  * P = (h + 2*pad - r)/stride + 1, Q = (w + 2*pad - s)/stride + 1. */
@@ -94,9 +94,14 @@ const char *fc_last_error(void);
  * The intermediate H = fp16(act(A*W0 + b0)) [M x N0] never reaches global
  * memory.  Residence: one block owns all N0 columns, so N0 <= 256
  * (FC_E_UNSUPPORTED above).  M == 0 is a no-op.
- * Variant (chain_gemm2_variant): FC_VARIANT_RF keeps H in VGPRs (N0 <= 128 and
- * W0, W1 fit in LDS together); FC_VARIANT_LDS stages H through LDS
- * (N0 <= 256); FC_VARIANT_AUTO (chain_gemm2) picks RF when it applies.
+ * Variant (chain_gemm2_variant): FC_VARIANT_RF keeps H in VGPRs with W0, W1
+ * resident in LDS (N0 <= 128 and W0, W1 fit in LDS together);
+ * FC_VARIANT_LDS stages the GEMM0 accumulator tile through LDS into GEMM1
+ * (shared-memory-resident fusion, same notes; N0 <= 256); FC_VARIANT_STREAM
+ * keeps H in VGPRs and streams W0, W1 through LDS (N0 <= 256, and N1 <= 16128
+ * so the biases fit beside the weight buffers).  FC_VARIANT_AUTO (chain_gemm2)
+ * picks RF when it applies, else STREAM, else LDS.  All variants compute the
+ * same values up to fp32 summation order.
  */
 fc_status chain_gemm2(const fc_half *A, const fc_half *W0, const fc_half *b0, fc_act act,
                       const fc_half *W1, const fc_half *b1, fc_half *D1,

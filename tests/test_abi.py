@@ -52,6 +52,8 @@ def test_chain_gemm2_validation(L):
     assert g2(L, b0=BAD) == E_ALIGN
     assert g2(L, act=7) == E_ARG
     assert g2(L, variant=5) == E_ARG
+    assert g2(L, variant=4) == E_ARG
+    assert g2(L, N0=256, N1=16136, variant=3) == E_UNSUP   # streamed: biases must fit beside the weight buffers
     assert g2(L, N0=264) == E_UNSUP          # residence: one block owns all N0 <= 256
     assert g2(L, N0=256, variant=1) == E_UNSUP   # register-resident needs N0 <= 128
     assert b"N0" in L.fc_last_error()

@@ -41,14 +41,14 @@ def oracle_chain(d, act, rows=None):
     return ref
 
 
-@pytest.mark.parametrize("variant", ["rf", "lds", "auto"])
+@pytest.mark.parametrize("variant", ["rf", "lds", "stream", "auto"])
 def test_tiny_full(fc, variant):
     spec, d = inputs.workload("b2b_gemm_tiny")
     print("case b2b_gemm_tiny", variant, flush=True)
     assert_close(run_chain(fc, d, "relu", variant), oracle_chain(d, "relu"), "tiny " + variant)
 
 
-@pytest.mark.parametrize("variant", ["rf", "lds"])
+@pytest.mark.parametrize("variant", ["rf", "lds", "stream"])
 def test_rf_shape_ragged(fc, variant):
     # the register-resident workload's widths at a size the oracle does at once,
     # with a ragged last tile (M % 32 != 0, M % 128 != 0)
@@ -69,6 +69,9 @@ def test_lds_shape_ragged(fc):
     (130, 72, 96, 264, "none", "rf"), (130, 72, 96, 264, "none", "lds"),
     (257, 200, 128, 40, "relu", "rf"), (200, 136, 136, 520, "relu", "lds"),
     (64, 32, 200, 16, "gelu_tanh", "lds"), (97, 1000, 64, 64, "relu", "auto"),
+    (1, 8, 8, 8, "relu", "stream"), (33, 40, 24, 72, "gelu_tanh", "stream"),
+    (130, 72, 96, 264, "none", "stream"), (200, 136, 136, 520, "relu", "stream"),
+    (64, 32, 200, 16, "gelu_tanh", "stream"), (300, 576, 256, 256, "gelu_tanh", "stream"),
 ])
 def test_edge_shapes(fc, M, K0, N0, N1, act, variant):
     d = inputs.gemm2_inputs(M, K0, N0, N1, "normal", seed=M + K0)
@@ -76,7 +79,7 @@ def test_edge_shapes(fc, M, K0, N0, N1, act, variant):
     assert_close(run_chain(fc, d, act, variant), oracle_chain(d, act), "edge")
 
 
-@pytest.mark.parametrize("variant", ["rf", "lds"])
+@pytest.mark.parametrize("variant", ["rf", "lds", "stream"])
 def test_sensitivity_unscaled(fc, variant):
     # unscaled inputs and zero biases: the outputs are not bias-dominated, so a
     # partial-K or dropped-tile mistake cannot hide inside the tolerance
@@ -91,7 +94,7 @@ def test_sensitivity_unscaled(fc, variant):
 def test_null_biases(fc):
     d = inputs.gemm2_inputs(96, 64, 64, 64, "uniform", seed=9)
     A, W0, W1 = dev(d["A"]), dev(d["W0"]), dev(d["W1"])
-    for v in ("rf", "lds"):
+    for v in ("rf", "lds", "stream"):
         out = to_np(fc.chain_gemm2(A, W0, None, W1, None, act="relu", variant=v))
         ref, _ = oracle.chain_gemm2(d["A"], d["W0"], None, oracle.ACT_RELU, d["W1"], None)
         assert_close(out, ref, "null bias " + v)
@@ -107,7 +110,7 @@ def test_m_zero_is_noop(fc):
 
 def test_deterministic(fc):
     d = inputs.gemm2_inputs(512, 256, 64, 128, "uniform", seed=11)
-    for v in ("rf", "lds"):
+    for v in ("rf", "lds", "stream"):
         a = run_chain(fc, d, "relu", v)
         b = run_chain(fc, d, "relu", v)
         assert np.array_equal(a.view(np.uint16), b.view(np.uint16))
@@ -130,14 +133,34 @@ def test_fused_equals_unfused(fc):
     A, W0, b0, W1, b1 = (dev(d[k]) for k in ("A", "W0", "b0", "W1", "b1"))
     H = fc.gemm_bias_act(A, W0, b0, act="relu")
     un = to_np(fc.gemm_bias_act(H, W1, b1, act="none"))
-    for v in ("rf", "lds"):
+    for v in ("rf", "lds", "stream"):
         fu = to_np(fc.chain_gemm2(A, W0, b0, W1, b1, act="relu", variant=v))
         assert_close(fu, un.astype(np.float64), "fused vs unfused " + v)
 
 
+@pytest.mark.parametrize("M,K0,N0,N1,act,variant", [
+    (131149, 200, 96, 136, "gelu_tanh", "stream"),   # runtime k-chunk count, padded N0, ragged second pass
+    (70000, 576, 256, 256, "relu", "stream"),        # the LDS workload's widths, some blocks take two tiles
+    (70000, 64, 64, 256, "none", "stream"),          # one W1 chunk per pass, two passes
+    (131149, 64, 64, 64, "relu", "stream"),          # a single GEMM1 step per tile
+    (70000, 576, 256, 256, "relu", "lds"),
+])
+def test_many_tiles(fc, M, K0, N0, N1, act, variant):
+    # Many more tiles than resident blocks: the streamed variant's blocks loop
+    # over 256-row tiles and request each tile's first row chunks during the
+    # previous tile's GEMM1.  First and last tiles plus random rows checked.
+    d = inputs.gemm2_inputs(M, K0, N0, N1, "uniform", seed=21)
+    print("case many tiles", M, K0, N0, N1, act, variant, flush=True)
+    out = run_chain(fc, d, act, variant)
+    rng = np.random.default_rng(1)
+    rows = np.unique(np.concatenate([np.arange(256), np.arange(M - 300, M), rng.integers(0, M, 2000)]))
+    assert_close(out[rows], oracle_chain(d, act, rows), "many tiles")
+    assert np.all(np.isfinite(out))
+
+
 @pytest.mark.slow
 @pytest.mark.parametrize("name,variant", [("b2b_gemm_rf", "auto"), ("b2b_gemm_rf", "lds"),
-                                          ("b2b_gemm_lds", "auto")])
+                                          ("b2b_gemm_lds", "lds"), ("b2b_gemm_lds", "stream")])
 def test_full_size_sampled(fc, name, variant):
     """Full workload size in the bench's launch configuration; the oracle
     checks 320 sampled rows (first and last tiles plus random rows)."""
