@@ -32,10 +32,7 @@
 
 namespace fc {
 
-#ifndef RF_TPB
-#define RF_TPB 512
-#endif
-constexpr int RF_THREADS = RF_TPB;
+constexpr int RF_THREADS = 512;
 constexpr int RF_WAVES = RF_THREADS / 64;
 constexpr int RF_WB = 16;   // weight vectors (16 bytes) per thread staged ahead of the row stream
 
@@ -302,7 +299,7 @@ static hipError_t launch_rf_k(const Loader& ld, RfArgs a, hipStream_t st)
     hipError_t e = allow_full_lds((const void*)k_chain_rf<NT0, KCH, Loader>, &lds_set);
     if (e != hipSuccess) return e;
     const long per_block_min = RF_WAVES;  // at least one tile per wave
-    long grid = device_cu_count() * (512 / RF_THREADS);
+    long grid = device_cu_count();
     if (grid * per_block_min > a.ntiles) grid = (a.ntiles + per_block_min - 1) / per_block_min;
     if (grid < 1) grid = 1;
     a.tiles_per_block = (a.ntiles + grid - 1) / grid;
