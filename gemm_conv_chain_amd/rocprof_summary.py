@@ -6,7 +6,8 @@
 ``trace``: the kernel_stats.csv rows (calls, average/min/max duration).
 ``pmc``: FETCH_SIZE / WRITE_SIZE per dispatch (KiB, mean over the dispatches of
 each kernel) from two ``--pmc`` runs (DIR/fetch, DIR/write) of
-``bench.py --calib-copy``.  Each counter is scaled by what it reads for the
+``bench.py --calib-copy``; WORKLOAD is the bench workload, or WORKLOAD@VARIANT
+for a run with ``--variant`` other than the workload's own.  Each counter is scaled by what it reads for the
 256 MiB device-to-device copy that ``--calib-copy`` issues last (known bytes):
 scale = 262144 KiB / counter value of that dispatch.  With --json the scaled
 HBM bytes of the fused kernel (and the sum over the unfused kernels) are
@@ -71,6 +72,7 @@ def pmc(d, workload, json_path=None):
         sys.path.insert(0, os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
         import bench
         fused = {"b2b_gemm_tiny": "k_chain_rf", "b2b_gemm_rf": "k_chain_rf", "b2b_gemm_lds": "k_gemm_lds<4, true",
+                 "b2b_gemm_lds@stream": "k_chain_stream",
                  "conv3x3_conv1x1": "k_chain_rf", "conv3x3_relu_maxpool": "k_conv_w<4, 1"}[workload]
         fk = [k for k in fetch if fused in k]
         if len(fk) != 1:
