@@ -229,9 +229,14 @@ def cpu_baseline(prob, seconds):
         tp = run(probe)
         rows = int(min(M, max(probe, probe * seconds / max(tp, 1e-6))))
         t = run(rows) if rows != probe else tp
-        return {"value": per_row * rows / t / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
-                "sample": "first %d of %d rows (fp64, unfused, same seeded inputs)" % (rows, M),
-                "seconds": round(t, 3)}
+        passes = 1
+        if rows == M:   # the whole workload is quick: repeat it for a stable time (up to ~2 s)
+            while t < min(seconds, 2.0) and passes < 100:
+                t += run(M)
+                passes += 1
+        sample = "first %d of %d rows" % (rows, M) if rows < M else "all %d rows x %d passes" % (M, passes)
+        return {"value": per_row * rows * passes / t / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+                "sample": sample + " (fp64, unfused, same seeded inputs)", "seconds": round(t, 3)}
     n = s["n"]
     per_img = prob.flops / n
 
