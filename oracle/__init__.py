@@ -46,7 +46,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
 
-ACT_NONE, ACT_RELU, ACT_GELU_TANH = 0, 1, 2
+ACT_NONE, ACT_RELU, ACT_GELU_TANH, ACT_HARDSWISH = 0, 1, 2, 3
 
 _lock = threading.Lock()
 _lib = None

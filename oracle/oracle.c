@@ -34,6 +34,10 @@
  * GELU: the tanh form 0.5*s*(1 + tanh(sqrt(2/pi)*(s + 0.044715*s^3))) from
  * Hendrycks & Gimpel, "Gaussian Error Linear Units" (the pages never define
  * GELU; the workload names its tanh form).
+ * Hardswish: s * min(max(s + 3, 0), 6) / 6, as defined in Howard et al.,
+ * "Searching for MobileNetV3" (BOLT notes, "Enabling deeper operator
+ * fusion", name Conv2D + BiasAdd + Hardswish as the fused epilogue but do not
+ * define it).
  */
 #include <math.h>
 #include <stdint.h>
@@ -46,6 +50,7 @@
 #define ORC_ACT_NONE 0
 #define ORC_ACT_RELU 1
 #define ORC_ACT_GELU_TANH 2
+#define ORC_ACT_HARDSWISH 3
 
 /* ------------------------------------------------------------------ */
 /* fp16 codec (IEEE 754 binary16)                                      */
@@ -112,6 +117,11 @@ double orc_act(int act, double s)
     if (act == ORC_ACT_GELU_TANH) {
         double c = sqrt(2.0 / M_PI);
         return 0.5 * s * (1.0 + tanh(c * (s + 0.044715 * s * s * s)));
+    }
+    if (act == ORC_ACT_HARDSWISH) {
+        double r6 = s + 3.0;
+        r6 = r6 < 0.0 ? 0.0 : (r6 > 6.0 ? 6.0 : r6);
+        return s * r6 / 6.0;
     }
     return s;
 }

@@ -89,6 +89,23 @@ def test_gelu_odd_identity(orc):
     assert np.max(np.abs(g - x)) < 1e-14
 
 
+def test_hardswish_values(orc):
+    # x * relu6(x + 3) / 6 at hand-worked points: 0 for x <= -3, x for x >= 3
+    s = np.array([-4.0, -3.0, -1.0, 0.0, 1.0, 2.0, 3.0, 4.0, -1.5])
+    exp = np.array([0.0, 0.0, -1.0 / 3.0, 0.0, 2.0 / 3.0, 5.0 / 3.0, 3.0, 4.0, -0.375])
+    assert np.allclose(orc.act(orc.ACT_HARDSWISH, s), exp, rtol=1e-15, atol=0)
+
+
+def test_hardswish_identities(orc):
+    # the same function through ReLU differences, and the odd identity
+    # hs(x) - hs(-x) = x, which holds for every real x
+    x = RNG.uniform(-8, 8, 10000)
+    relu = lambda v: np.maximum(v, 0.0)
+    hs = orc.act(orc.ACT_HARDSWISH, x)
+    assert np.max(np.abs(hs - x * (relu(x + 3) - relu(x - 3)) / 6)) < 1e-14
+    assert np.max(np.abs(hs - orc.act(orc.ACT_HARDSWISH, -x) - x)) < 1e-14
+
+
 # ------------------------------------------------------------------ GEMM
 def test_gemm_golden(orc):
     g = read_fields("matmul_2x2.txt")
