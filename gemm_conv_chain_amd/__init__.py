@@ -27,7 +27,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libfusedchain.so")
 HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "fusedchain.h")
 
-ACT = {"none": 0, "relu": 1, "gelu_tanh": 2}
+ACT = {"none": 0, "relu": 1, "gelu_tanh": 2, "hardswish": 3}
 POOL = {"none": 0, "max2x2": 1}
 VARIANT = {"auto": 0, "rf": 1, "lds": 2, "stream": 3}
 

@@ -54,7 +54,7 @@ half_t* Hm(fc_half* p) { return reinterpret_cast<half_t*>(p); }
 
 fc_status check_act(fc_act act)
 {
-    if ((int)act < 0 || (int)act > 2) return fail(FC_E_ARG, "act %d out of range", (int)act);
+    if ((int)act < 0 || (int)act > 3) return fail(FC_E_ARG, "act %d out of range", (int)act);
     return FC_OK;
 }
 

@@ -200,15 +200,16 @@ void k_chain_rf(Loader ld, RfArgs a)
         }
 
         // Put the next tile's first chunks in flight (every set is free once
-        // the last chunk's MFMAs are issued) before the epilogues.
+        // the last chunk's MFMAs are issued) before the epilogues.  The loads
+        // are issued even when there is no next tile (its rows are then row M,
+        // past the end, and read the zero line): loads under a branch leave
+        // the ring registers to be merged after it, and that copy waits for
+        // every load in flight -- the prefetch's full latency before GEMM1.
         const long ntile = tile + RF_WAVES;
-        typename Loader::Row nrow = row;
-        if (ntile < t_end) {
-            nrow = ld.row(ntile * 32 + lr);
+        const typename Loader::Row nrow = ld.row(ntile < t_end ? ntile * 32 + lr : a.M);
 #pragma unroll
-            for (int p = 0; p < PD; ++p)
-                if (p < nch) ld.template load<KCH>(nrow, p, hh, xr[p]);
-        }
+        for (int p = 0; p < PD; ++p)
+            if (p < nch) ld.template load<KCH>(nrow, p, hh, xr[p]);
 
         // Epilogue 0 in registers: bias (broadcast along rows), activation,
         // one rounding to fp16.  hf[s] is GEMM1's operand B for k-step s.

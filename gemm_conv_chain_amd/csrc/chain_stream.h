@@ -489,6 +489,7 @@ template <int NT0>
 static hipError_t launch_stream_n(const StreamArgs& a, int act, hipStream_t st)
 {
     if (act == ACT_GELU_TANH) return launch_stream_a<NT0, ACT_GELU_TANH>(a, st);
+    if (act == ACT_HARDSWISH) return launch_stream_a<NT0, ACT_HARDSWISH>(a, st);
     if (act == ACT_RELU) return launch_stream_a<NT0, ACT_RELU>(a, st);
     return launch_stream_a<NT0, ACT_NONE>(a, st);
 }

@@ -29,7 +29,7 @@ typedef float floatx4 __attribute__((ext_vector_type(4)));
 #define FC_LDS __attribute__((address_space(3)))
 typedef FC_LDS half_t lds_half;
 
-enum { ACT_NONE = 0, ACT_RELU = 1, ACT_GELU_TANH = 2 };
+enum { ACT_NONE = 0, ACT_RELU = 1, ACT_GELU_TANH = 2, ACT_HARDSWISH = 3 };
 
 __device__ __forceinline__ floatx16 mfma32x32x16(half8 a, half8 b, floatx16 c)
 {
@@ -116,6 +116,16 @@ template <> struct Act<ACT_GELU_TANH> {
     }
 };
 
+// Hardswish x * min(max(x + 3, 0), 6) / 6 (the fused Conv2D + BiasAdd +
+// Hardswish epilogue of the BOLT notes, "Enabling deeper operator fusion").
+template <> struct Act<ACT_HARDSWISH> {
+    __device__ static __forceinline__ float f(float x)
+    {
+        const float r6 = __builtin_fminf(__builtin_fmaxf(x + 3.0f, 0.0f), 6.0f);
+        return x * r6 * (1.0f / 6.0f);
+    }
+};
+
 template <int V> struct IntC {
     static constexpr int value = V;
 };
@@ -194,6 +204,7 @@ __device__ __forceinline__ void act_dispatch(int act, F&& f)
 {
     if (act == ACT_GELU_TANH) f(Act<ACT_GELU_TANH>{});
     else if (act == ACT_RELU) f(Act<ACT_RELU>{});
+    else if (act == ACT_HARDSWISH) f(Act<ACT_HARDSWISH>{});
     else f(Act<ACT_NONE>{});
 }
 

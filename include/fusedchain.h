@@ -65,7 +65,10 @@ typedef enum {
     FC_E_ARG = 6          /* an enum argument is out of range */
 } fc_status;
 
-typedef enum { FC_ACT_NONE = 0, FC_ACT_RELU = 1, FC_ACT_GELU_TANH = 2 } fc_act;
+/* Element-wise epilogue activations.  GELU is its tanh form; Hardswish is
+ * x * min(max(x + 3, 0), 6) / 6 (BOLT notes, "Enabling deeper operator
+ * fusion": Conv2D + BiasAdd + Hardswish in one kernel). */
+typedef enum { FC_ACT_NONE = 0, FC_ACT_RELU = 1, FC_ACT_GELU_TANH = 2, FC_ACT_HARDSWISH = 3 } fc_act;
 typedef enum { FC_POOL_NONE = 0, FC_POOL_MAX_2X2_S2 = 1 } fc_pool;
 typedef enum { FC_VARIANT_AUTO = 0, FC_VARIANT_RF = 1, FC_VARIANT_LDS = 2, FC_VARIANT_STREAM = 3 } fc_variant;
 
@@ -90,7 +93,7 @@ const char *fc_last_error(void);
  * (BOLT notes, "Persistent kernel (GEMM/Conv) fusion").
  *   A  [M  x K0]   W0 [K0 x N0]   b0 [N0]
  *   W1 [N0 x N1]   b1 [N1]        D1 [M  x N1]
- *   act: FC_ACT_NONE / FC_ACT_RELU / FC_ACT_GELU_TANH (tanh form).
+ *   act: FC_ACT_NONE / FC_ACT_RELU / FC_ACT_GELU_TANH (tanh form) / FC_ACT_HARDSWISH.
  * The intermediate H = fp16(act(A*W0 + b0)) [M x N0] never reaches global
  * memory.  Residence: one block owns all N0 columns, so N0 <= 256
  * (FC_E_UNSUPPORTED above).  M == 0 is a no-op.

@@ -51,6 +51,7 @@ def test_chain_gemm2_validation(L):
     assert g2(L, A=BAD) == E_ALIGN
     assert g2(L, b0=BAD) == E_ALIGN
     assert g2(L, act=7) == E_ARG
+    assert g2(L, act=4) == E_ARG
     assert g2(L, variant=5) == E_ARG
     assert g2(L, variant=4) == E_ARG
     assert g2(L, N0=256, N1=16136, variant=3) == E_UNSUP   # streamed: biases must fit beside the weight buffers
@@ -63,7 +64,7 @@ def test_gemm_bias_act_validation(L):
     assert L.gemm_bias_act(NUL, P, NUL, 0, P2, 8, 8, 8, None) == E_NULL
     assert L.gemm_bias_act(P, P, NUL, 0, P2, 8, 12, 8, None) == E_SHAPE
     assert L.gemm_bias_act(P, P, BAD, 0, P2, 8, 8, 8, None) == E_ALIGN
-    assert L.gemm_bias_act(P, P, NUL, 3, P2, 8, 8, 8, None) == E_ARG
+    assert L.gemm_bias_act(P, P, NUL, 4, P2, 8, 8, 8, None) == E_ARG
 
 
 def shape(n=1, h=8, w=8, c=64, k=128, r=3, s=3, stride=1, pad=1):

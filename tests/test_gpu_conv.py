@@ -24,7 +24,8 @@ def dev(a):
     return None if a is None else torch.from_numpy(np.ascontiguousarray(a)).cuda()
 
 
-ACTS = {"none": oracle.ACT_NONE, "relu": oracle.ACT_RELU, "gelu_tanh": oracle.ACT_GELU_TANH}
+ACTS = {"none": oracle.ACT_NONE, "relu": oracle.ACT_RELU, "gelu_tanh": oracle.ACT_GELU_TANH,
+        "hardswish": oracle.ACT_HARDSWISH}
 
 
 def check_pool(y, am, x_np, w_np, b_np, what, act="relu"):
@@ -59,7 +60,7 @@ def test_conv_pool_small(fc, n, h, w, c, k):
     assert free > 0
 
 
-@pytest.mark.parametrize("act", ["none", "gelu_tanh"])
+@pytest.mark.parametrize("act", ["none", "gelu_tanh", "hardswish"])
 @pytest.mark.parametrize("c", [64, 32])
 def test_conv_pool_activations(fc, act, c):
     # the pool decides on the fp16 activation output; argmax ties are
@@ -91,12 +92,13 @@ def test_conv_bias_act_many_tiles_ragged(fc):
     assert_close(y, oracle.conv_bias_act(d["x"], d["w"], d["b"], oracle.ACT_RELU), "conv_bias_act many tiles")
 
 
-def test_conv2_gelu(fc):
+@pytest.mark.parametrize("act", ["gelu_tanh", "hardswish"])
+def test_conv2_act(fc, act):
     d = inputs.conv2_inputs(2, 9, 11, 64, 64, 128, seed=31)
-    print("case conv2 gelu", flush=True)
-    y = to_np(fc.chain_conv2(dev(d["x"]), dev(d["w0"]), dev(d["b0"]), dev(d["w1"]), dev(d["b1"]), act="gelu_tanh"))
-    ref, _ = oracle.chain_conv2(d["x"], d["w0"], d["b0"], oracle.ACT_GELU_TANH, d["w1"], d["b1"])
-    assert_close(y, ref, "conv2 gelu")
+    print("case conv2", act, flush=True)
+    y = to_np(fc.chain_conv2(dev(d["x"]), dev(d["w0"]), dev(d["b0"]), dev(d["w1"]), dev(d["b1"]), act=act))
+    ref, _ = oracle.chain_conv2(d["x"], d["w0"], d["b0"], ACTS[act], d["w1"], d["b1"])
+    assert_close(y, ref, "conv2 " + act)
 
 
 def test_conv_pool_padded_channels(fc):
@@ -123,10 +125,10 @@ def test_conv_pool_degenerate(fc):
 
 
 @pytest.mark.parametrize("n,h,w,c,k,act", [(2, 7, 9, 64, 64, "relu"), (1, 6, 6, 32, 128, "gelu_tanh"),
-                                           (1, 5, 11, 64, 24, "none")])
+                                           (1, 5, 11, 64, 24, "none"), (2, 6, 10, 64, 128, "hardswish")])
 def test_conv_bias_act(fc, n, h, w, c, k, act):
     d = inputs.conv_pool_inputs(n, h, w, c, k, seed=n * h)
-    a = {"none": 0, "relu": 1, "gelu_tanh": 2}[act]
+    a = ACTS[act]
     print("case conv_bias_act", n, h, w, c, k, act, flush=True)
     y = to_np(fc.conv_bias_act(dev(d["x"]), dev(d["w"]), dev(d["b"]), act=act))
     assert_close(y, oracle.conv_bias_act(d["x"], d["w"], d["b"], a), "conv_bias_act")

@@ -12,7 +12,8 @@ from parity import assert_close, to_np
 
 pytestmark = pytest.mark.gpu
 torch = pytest.importorskip("torch")
-ACTS = {"none": oracle.ACT_NONE, "relu": oracle.ACT_RELU, "gelu_tanh": oracle.ACT_GELU_TANH}
+ACTS = {"none": oracle.ACT_NONE, "relu": oracle.ACT_RELU, "gelu_tanh": oracle.ACT_GELU_TANH,
+        "hardswish": oracle.ACT_HARDSWISH}
 
 
 @pytest.fixture(scope="module")
@@ -72,6 +73,8 @@ def test_lds_shape_ragged(fc):
     (1, 8, 8, 8, "relu", "stream"), (33, 40, 24, 72, "gelu_tanh", "stream"),
     (130, 72, 96, 264, "none", "stream"), (200, 136, 136, 520, "relu", "stream"),
     (64, 32, 200, 16, "gelu_tanh", "stream"), (300, 576, 256, 256, "gelu_tanh", "stream"),
+    (130, 72, 96, 264, "hardswish", "rf"), (130, 72, 96, 264, "hardswish", "lds"),
+    (300, 576, 256, 256, "hardswish", "stream"),
 ])
 def test_edge_shapes(fc, M, K0, N0, N1, act, variant):
     d = inputs.gemm2_inputs(M, K0, N0, N1, "normal", seed=M + K0)
@@ -117,7 +120,7 @@ def test_deterministic(fc):
 
 
 @pytest.mark.parametrize("M,K,N,act", [(1000, 256, 64, "relu"), (300, 64, 128, "none"), (129, 576, 256, "gelu_tanh"),
-                                       (70, 40, 520, "relu"), (5, 8, 8, "none")])
+                                       (70, 40, 520, "relu"), (5, 8, 8, "none"), (300, 128, 192, "hardswish")])
 def test_gemm_bias_act(fc, M, K, N, act):
     rng = np.random.default_rng(M)
     A = (rng.standard_normal((M, K)) / np.sqrt(K)).astype(np.float16)
