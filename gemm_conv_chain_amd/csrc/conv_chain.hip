@@ -47,6 +47,7 @@ struct FastDiv {
 };
 
 struct Conv3x3Rows {
+    static constexpr bool kRaw = false;   // loads land in operand layout
     const half_t* x;
     int H, W, C;
     long M;   // N*H*W (< 2^31)

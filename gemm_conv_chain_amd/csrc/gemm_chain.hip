@@ -406,6 +406,11 @@ hipError_t run_chain_gemm2(const half_t* A, const half_t* W0, const half_t* b0, 
         a.act = act;
         a.ntiles = (M + 31) / 32;
         a.tiles_per_block = 0;
+        if (K0 == 64 || K0 == 256 || K0 == 576) {   // compile-time chunk counts: quad-coalesced rows
+            DenseRowsQ ld;
+            ld.A = A; ld.M = M; ld.K = K0;
+            return launch_rf(ld, a, (N0 + 31) / 32, st);
+        }
         DenseRows ld;
         ld.A = A; ld.M = M; ld.K = K0;
         return launch_rf(ld, a, (N0 + 31) / 32, st);
