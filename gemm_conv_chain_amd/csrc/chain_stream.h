@@ -114,9 +114,10 @@ __device__ __forceinline__ void dma16(i32x4 rsrc, unsigned voff, const lds_half*
 }
 
 // 16-byte load into registers (the kernel waits for it with vm_wait).
+// Non-temporal: each row line is read once, by one instruction (quad layout).
 __device__ __forceinline__ void bload16(half8& dst, i32x4 rsrc, unsigned voff)
 {
-    asm volatile("buffer_load_dwordx4 %0, %1, %2, 0 offen" : "=v"(dst) : "v"(voff), "s"(rsrc));
+    asm volatile("buffer_load_dwordx4 %0, %1, %2, 0 offen nt" : "=v"(dst) : "v"(voff), "s"(rsrc));
 }
 
 // 16-byte non-temporal store.
