@@ -90,6 +90,24 @@ class Problem:
                            "variant": variant,
                            "dist": s["dist"] + "(-1,1)/sqrt(K)" if s["dist"] == "uniform" else "normal(0,1)/sqrt(K)"}
             self.kernel = {"rf": "k_chain_rf", "lds": "k_gemm_lds", "stream": "k_chain_stream"}[variant]
+        elif s["kind"] == "gemmN":
+            M, wd = s["M"], s["widths"]
+            self.acts = s["acts"]
+            self.flops = 2 * M * sum(wd[i] * wd[i + 1] for i in range(len(wd) - 1))
+            self.flops_exec = self.flops
+            wbytes = 2 * sum(wd[i] * wd[i + 1] + wd[i + 1] for i in range(len(wd) - 1))
+            self.bytes_fused = 2 * (M * wd[0] + M * wd[-1]) + wbytes
+            self.bytes_interm = 2 * M * sum(wd[1:-1])
+            self.W = [t(x) for x in d["Ws"]] + [t(x) for x in d["bs"]]
+            per_set = 2 * (M * wd[0] + M * wd[-1])
+            self.nsets = max(1, math.ceil(COLD_BYTES / per_set)) if cold else 1
+            A = t(d["A"])
+            self.X = [A] + [A.clone() for _ in range(self.nsets - 1)]
+            self.Y = [torch.empty((M, wd[-1]), dtype=torch.float16, device=dev) for _ in range(self.nsets)]
+            self.Hs = [torch.empty((M, x), dtype=torch.float16, device=dev) for x in wd[1:-1]]
+            self.config = {"workload": name, "M": M, "widths": wd, "acts": self.acts, "variant": "rf",
+                           "dist": "uniform(-1,1)/sqrt(K)"}
+            self.kernel = "k_chain_rf"
         elif s["kind"] == "conv2":
             n, h, w, c, k0, k1 = s["n"], s["h"], s["w"], s["c"], s["k0"], s["k1"]
             npix = n * h * w
@@ -134,6 +152,9 @@ class Problem:
         if s["kind"] == "gemm2":
             W0, b0, W1, b1 = self.W
             fc.chain_gemm2(self.X[j], W0, b0, W1, b1, act=self.act, out=self.Y[j], variant=self.config["variant"])
+        elif s["kind"] == "gemmN":
+            n = len(self.acts)
+            fc.chain_gemmN(self.X[j], self.W[:n], self.W[n:], self.acts, out=self.Y[j])
         elif s["kind"] == "conv2":
             w0, b0, w1, b1 = self.W
             fc.chain_conv2(self.X[j], w0, b0, w1, b1, act="relu", out=self.Y[j])
@@ -148,6 +169,13 @@ class Problem:
             W0, b0, W1, b1 = self.W
             fc.gemm_bias_act(self.X[j], W0, b0, act=self.act, out=self.H)
             fc.gemm_bias_act(self.H, W1, b1, act="none", out=self.Y[j])
+        elif s["kind"] == "gemmN":
+            n = len(self.acts)
+            src = self.X[j]
+            for k in range(n):
+                dst = self.Hs[k] if k < n - 1 else self.Y[j]
+                fc.gemm_bias_act(src, self.W[k], self.W[n + k], act=self.acts[k], out=dst)
+                src = dst
         elif s["kind"] == "conv2":
             w0, b0, w1, b1 = self.W
             fc.conv_bias_act(self.X[j], w0, b0, act="relu", out=self.H)
@@ -215,14 +243,18 @@ def cpu_baseline(prob, seconds):
     import oracle
     s, d = prob.spec, prob.host
     cores = oracle.num_threads()
-    actk = {"relu": oracle.ACT_RELU, "gelu_tanh": oracle.ACT_GELU_TANH, "none": oracle.ACT_NONE}
-    if s["kind"] == "gemm2":
+    actk = {"relu": oracle.ACT_RELU, "gelu_tanh": oracle.ACT_GELU_TANH, "none": oracle.ACT_NONE,
+            "hardswish": oracle.ACT_HARDSWISH}
+    if s["kind"] in ("gemm2", "gemmN"):
         M = s["M"]
         per_row = prob.flops / M
 
         def run(rows):
             t = time.perf_counter()
-            oracle.chain_gemm2(d["A"][:rows], d["W0"], d["b0"], actk[s["act"]], d["W1"], d["b1"])
+            if s["kind"] == "gemm2":
+                oracle.chain_gemm2(d["A"][:rows], d["W0"], d["b0"], actk[s["act"]], d["W1"], d["b1"])
+            else:
+                oracle.chain_gemmN(d["A"][:rows], d["Ws"], d["bs"], [actk[a] for a in s["acts"]])
             return time.perf_counter() - t
 
         probe = min(M, 2048)
@@ -276,7 +308,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="b2b_gemm_rf",
-                    choices=["b2b_gemm_tiny", "b2b_gemm_rf", "b2b_gemm_lds", "conv3x3_conv1x1",
+                    choices=["b2b_gemm_tiny", "b2b_gemm_rf", "b2b_gemm_lds", "gemm3_rf", "conv3x3_conv1x1",
                              "conv3x3_relu_maxpool"])
     ap.add_argument("--variant", choices=["rf", "lds", "stream"], default=None,
                     help="GEMM-chain kernel variant (default: rf, or lds for b2b_gemm_lds)")

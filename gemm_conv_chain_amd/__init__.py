@@ -19,7 +19,7 @@ import ctypes
 import os
 import re
 
-__all__ = ["lib", "FusedChainError", "chain_gemm2", "chain_conv_pool", "chain_conv2", "gemm_bias_act",
+__all__ = ["lib", "FusedChainError", "chain_gemm2", "chain_gemmN", "chain_conv_pool", "chain_conv2", "gemm_bias_act",
            "conv_bias_act", "maxpool2x2", "pad_channels", "pad_weight_channels", "abi_version", "ACT", "VARIANT",
            "LIB_PATH", "HEADER_PATH", "exported_names"]
 
@@ -62,6 +62,8 @@ def lib():
         L.chain_gemm2.argtypes = [_vp, _vp, _vp, ctypes.c_int, _vp, _vp, _vp, _i64, _i32, _i32, _i32, _vp]
         L.chain_gemm2_variant.argtypes = [_vp, _vp, _vp, ctypes.c_int, _vp, _vp, _vp, _i64, _i32, _i32, _i32,
                                           ctypes.c_int, _vp]
+        L.chain_gemmN.argtypes = [_vp, _i32, ctypes.POINTER(_vp), ctypes.POINTER(_vp), ctypes.POINTER(ctypes.c_int),
+                                  ctypes.POINTER(_i32), _vp, _i64, _vp]
         L.chain_conv_pool.argtypes = [_vp, _vp, _vp, ctypes.c_int, ctypes.c_int, _vp, ctypes.POINTER(ConvShape),
                                       _vp, _vp]
         L.chain_conv2.argtypes = [_vp, _vp, _vp, ctypes.c_int, _vp, _vp, _i32, _vp, ctypes.POINTER(ConvShape), _vp]
@@ -69,7 +71,7 @@ def lib():
         L.conv_bias_act.argtypes = [_vp, _vp, _vp, ctypes.c_int, _vp, ctypes.POINTER(ConvShape), _vp]
         L.maxpool2x2.argtypes = [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _vp]
         L.pad_channels.argtypes = [_vp, _vp, _i64, _i32, _i32, _i32, _vp]
-        for name in ("chain_gemm2", "chain_gemm2_variant", "chain_conv_pool", "chain_conv2", "gemm_bias_act",
+        for name in ("chain_gemm2", "chain_gemm2_variant", "chain_gemmN", "chain_conv_pool", "chain_conv2", "gemm_bias_act",
                      "conv_bias_act", "maxpool2x2", "pad_channels"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
@@ -91,7 +93,7 @@ def exported_names():
     """Function names declared in include/fusedchain.h."""
     with open(HEADER_PATH) as f:
         text = f.read()
-    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*([a-z_0-9]+)\s*\(", text, re.M)))
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*([A-Za-z_0-9]+)\s*\(", text, re.M)))
 
 
 def _check(fn, status):
@@ -147,6 +149,32 @@ def chain_gemm2(A, W0, b0, W1, b1, act="relu", out=None, variant="auto"):
     v = VARIANT[variant] if isinstance(variant, str) else int(variant)
     _check("chain_gemm2", lib().chain_gemm2_variant(_ptr(A), _ptr(W0), _ptr(b0), _act(act), _ptr(W1), _ptr(b1),
                                                     _ptr(out), M, K0, N0, N1, v, _stream(A)))
+    return out
+
+
+def chain_gemmN(A, Ws, bs, acts, out=None):
+    """D = act[n-1](... act[0](A @ Ws[0] + bs[0]) ... @ Ws[n-1] + bs[n-1]) (fp16; n = 3 or 4),
+    every intermediate rounded once to fp16 and kept on chip."""
+    n = len(Ws)
+    if len(bs) != n or len(acts) != n:
+        raise ValueError("Ws, bs and acts must have the same length")
+    _need(A, "A", 2)
+    for i in range(n):
+        _need(Ws[i], "W%d" % i, 2)
+        _need(bs[i], "b%d" % i, 1)
+    M = A.shape[0]
+    widths = [A.shape[1]] + [W.shape[1] for W in Ws]
+    for i, W in enumerate(Ws):
+        if W.shape[0] != widths[i]:
+            raise ValueError("W%d has %d rows, the previous width is %d" % (i, W.shape[0], widths[i]))
+    if out is None:
+        out = _torch().empty((M, widths[-1]), dtype=A.dtype, device=A.device)
+    _need(out, "out", 2)
+    Wp = (_vp * n)(*[W.data_ptr() for W in Ws])
+    bp = (_vp * n)(*[None if b is None else b.data_ptr() for b in bs])
+    ap = (ctypes.c_int * n)(*[_act(a) for a in acts])
+    wp = (_i32 * (n + 1))(*widths)
+    _check("chain_gemmN", lib().chain_gemmN(_ptr(A), n, Wp, bp, ap, wp, _ptr(out), M, _stream(A)))
     return out
 
 

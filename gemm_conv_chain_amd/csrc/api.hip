@@ -129,6 +129,46 @@ fc_status chain_gemm2(const fc_half* A, const fc_half* W0, const fc_half* b0, fc
     return chain_gemm2_variant(A, W0, b0, act, W1, b1, D1, M, K0, N0, N1, FC_VARIANT_AUTO, stream);
 }
 
+fc_status chain_gemmN(const fc_half* A, int32_t nstages, const fc_half* const* W, const fc_half* const* b,
+                      const fc_act* act, const int32_t* widths, fc_half* D, int64_t M, void* stream)
+{
+    if (!W || !act || !widths) return fail(FC_E_NULL, "W, act and widths are required");
+    if (nstages < 3 || nstages > 4)
+        return fail(FC_E_UNSUPPORTED, "nstages=%d: chain_gemmN runs 3 or 4 GEMMs (chain_gemm2 runs 2)", (int)nstages);
+    if (M < 0) return fail(FC_E_SHAPE, "M>=0 required");
+    for (int i = 0; i <= nstages; ++i) {
+        if (widths[i] <= 0 || widths[i] % 8)
+            return fail(FC_E_SHAPE, "widths[%d]=%d must be a positive multiple of 8", i, (int)widths[i]);
+    }
+    if (M > 0 && (!A || !D)) return fail(FC_E_NULL, "A and D are required");
+    if (!aligned16(A) || !aligned16(D)) return fail(FC_E_ALIGN, "tensor pointers must be 16-byte aligned");
+    const fc_half* Ws[4];
+    const fc_half* bs[4];
+    int acts[4];
+    for (int i = 0; i < nstages; ++i) {
+        if (!W[i]) return fail(FC_E_NULL, "W[%d] is required", i);
+        const fc_half* bi = b ? b[i] : nullptr;
+        if (!aligned16(W[i]) || !aligned16(bi)) return fail(FC_E_ALIGN, "W[%d] and b[%d] must be 16-byte aligned", i, i);
+        fc_status s = check_act(act[i]);
+        if (s != FC_OK) return s;
+        Ws[i] = W[i];
+        bs[i] = bi;
+        acts[i] = (int)act[i];
+    }
+    int w[5];
+    for (int i = 0; i <= nstages; ++i) w[i] = widths[i];
+    if (!fc::gemmn_fits(nstages, w))
+        return fail(FC_E_UNSUPPORTED, "register residence: every intermediate width <= 128 and all weights within LDS");
+    const fc::half_t* Wh[4];
+    const fc::half_t* bh[4];
+    for (int i = 0; i < nstages; ++i) {
+        Wh[i] = H(Ws[i]);
+        bh[i] = H(bs[i]);
+    }
+    return hip_status(fc::run_chain_gemmN(H(A), nstages, Wh, bh, acts, w, Hm(D), M, (hipStream_t)stream),
+                      "chain_gemmN");
+}
+
 fc_status gemm_bias_act(const fc_half* A, const fc_half* W, const fc_half* b, fc_act act, fc_half* C, int64_t M,
                         int32_t K, int32_t N, void* stream)
 {

@@ -49,6 +49,16 @@ struct RfArgs {
     int act;
     long ntiles;        // ceil(M / 32)
     long tiles_per_block;
+    // N-stage chains only (kernel template NMID > 0): NMID middle GEMMs run
+    // between the first and the last, each on the previous one's fp16 output
+    // kept in the lane.  Middle i maps width Nin_i (N0, then Nm[0]) to Nm[i].
+    const half_t* Wm[2];   // [Nin_i x Nm[i]] row-major
+    const half_t* bm[2];   // [Nm[i]] or null
+    int Nm[2];             // <= 128
+    int Nmp[2];            // Nm rounded up to 64
+    int actm[2];
+    int act1;              // activation after the last GEMM
+    int Nin1, Nin1p;       // input width of the last GEMM, and its padded row count in LDS
 };
 
 // Per-wave output staging tile: 32 rows x 64 columns (+8 halves of padding).
@@ -63,33 +73,61 @@ inline size_t rf_lds_bytes(int N0P, int K0p, int N1p)
            RF_OSTAGE_BYTES;
 }
 
+// ... and with nmid middle GEMMs (padded widths Nmp[0..nmid-1]): their weight
+// tiles sit between W0 and the last GEMM's, their biases after b1.
+inline size_t rf_lds_bytes_n(int N0P, int K0p, int N1p, int nmid, const int* Nmp)
+{
+    size_t b = (size_t)K0p * wtile_ld(N0P) * 2;
+    int nin = N0P;
+    for (int i = 0; i < nmid; ++i) {
+        b += (size_t)nin * wtile_ld(Nmp[i]) * 2 + (size_t)Nmp[i] * 4;
+        nin = Nmp[i];
+    }
+    return b + (size_t)nin * wtile_ld(N1p) * 2 + (size_t)(N0P + N1p) * 4 + RF_OSTAGE_BYTES;
+}
+
 // KCH: compile-time number of 64-wide k chunks (0 = runtime loop); with a
 // known count the chunk loop unrolls fully and every load is waited for
 // exactly where its data is used.
 // One block per CU (its LDS holds both weight matrices), 8 waves: 2 waves per
 // SIMD.  Saying so lets the scheduler spend registers on loads in flight
 // instead of shrinking them for an occupancy the LDS use rules out.
-template <int NT0, int KCH, class Loader>
+// NMID: middle GEMMs of an N-stage chain (0 for two GEMMs).
+template <int NT0, int KCH, class Loader, int NMID = 0>
 __global__ __launch_bounds__(RF_THREADS) __attribute__((amdgpu_waves_per_eu(1, 2)))
 void k_chain_rf(Loader ld, RfArgs a)
 {
     constexpr int N0P = 32 * NT0;
+    constexpr int HF = NMID ? 8 : 2 * NT0;   // k-steps of the hand-off registers (8 = 128 columns)
     extern __shared__ __align__(16) char smem[];
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int lr = lane & 31, hh = lane >> 5;
     typedef FC_LDS float lds_float;
     typedef FC_LDS half4 lds_half4;
-    WTile W0n, W1n;   // natural layouts: W0n [K0p][N0P], W1n [N0P][N1p]
+    // natural layouts: W0n [K0p][N0P], Wmn[i] [Nin_i][Nmp[i]], W1n [Nin1p][N1p]
+    const int nin1p = NMID ? a.Nin1p : N0P;
+    WTile W0n, W1n, Wmn[NMID > 0 ? NMID : 1];
     W0n.p = (lds_half*)smem;
     W0n.ld = wtile_ld(N0P);
     W0n.swz = wtile_swz(N0P);
-    W1n.p = W0n.p + a.K0p * W0n.ld;
+    lds_half* wnext = W0n.p + a.K0p * W0n.ld;
+    if constexpr (NMID > 0) {
+#pragma unroll
+        for (int i = 0; i < NMID; ++i) {
+            Wmn[i].p = wnext;
+            Wmn[i].ld = wtile_ld(a.Nmp[i]);
+            Wmn[i].swz = wtile_swz(a.Nmp[i]);
+            wnext += (i == 0 ? N0P : a.Nmp[i - 1]) * Wmn[i].ld;
+        }
+    }
+    W1n.p = wnext;
     W1n.ld = wtile_ld(a.N1p);
     W1n.swz = wtile_swz(a.N1p);
-    lds_float* b0s = (lds_float*)(W1n.p + N0P * W1n.ld);
+    lds_float* b0s = (lds_float*)(W1n.p + nin1p * W1n.ld);
     lds_float* b1s = b0s + N0P;
-    lds_half* Ost = (lds_half*)(b1s + a.N1p) + wave * 32 * RF_OLD;
+    lds_float* bms = b1s + a.N1p;   // middle biases (NMID > 0), Nmp[0] then Nmp[1]
+    lds_half* Ost = (lds_half*)(bms + (NMID > 0 ? a.Nmp[0] : 0) + (NMID > 1 ? a.Nmp[1] : 0)) + wave * 32 * RF_OLD;
 
     const long t_begin = (long)blockIdx.x * a.tiles_per_block;
     const long t_end = min(t_begin + a.tiles_per_block, a.ntiles);
@@ -118,7 +156,8 @@ void k_chain_rf(Loader ld, RfArgs a)
     // the barrier-free first batch (their loads then wait behind the rows).
     WStage2<RF_WB> ws;
     ws.G0 = a.W0; ws.rows0 = a.K0; ws.cols0 = a.N0; ws.ldg0 = a.N0; ws.nr0 = a.K0p; ws.ncp0 = N0P; ws.T0 = W0n;
-    ws.G1 = a.W1; ws.rows1 = a.N0; ws.cols1 = a.N1; ws.ldg1 = a.N1; ws.nr1 = N0P; ws.ncp1 = a.N1p; ws.T1 = W1n;
+    ws.G1 = a.W1; ws.rows1 = NMID ? a.Nin1 : a.N0; ws.cols1 = a.N1; ws.ldg1 = a.N1; ws.nr1 = nin1p; ws.ncp1 = a.N1p;
+    ws.T1 = W1n;
     ws.init();
     ws.load(tid, RF_THREADS);
     // this thread's bias value (raw fp16; converted only after the row loads
@@ -151,6 +190,15 @@ void k_chain_rf(Loader ld, RfArgs a)
     for (int v0 = RF_WB * RF_THREADS; v0 < ws.nvt; v0 += RF_WB * RF_THREADS) {
         ws.load(tid + v0, RF_THREADS);
         ws.store(tid + v0, RF_THREADS);
+    }
+    if constexpr (NMID > 0) {
+#pragma unroll
+        for (int i = 0; i < NMID; ++i) {
+            const int nin = i == 0 ? a.N0 : a.Nm[i - 1], ninp = i == 0 ? N0P : a.Nmp[i - 1];
+            stage_natural<4>(a.Wm[i], nin, a.Nm[i], a.Nm[i], ninp, a.Nmp[i], Wmn[i], tid, RF_THREADS);
+            lds_float* bd = bms + (i == 0 ? 0 : a.Nmp[0]);
+            for (int j = tid; j < a.Nmp[i]; j += RF_THREADS) bd[j] = (a.bm[i] && j < a.Nm[i]) ? (float)a.bm[i][j] : 0.0f;
+        }
     }
     __syncthreads();
 
@@ -212,19 +260,20 @@ void k_chain_rf(Loader ld, RfArgs a)
 
         // Put the next tile's first chunks in flight (every set is free once
         // the last chunk's MFMAs are issued) before the epilogues.  The loads
-        // are issued even when there is no next tile (its rows are then row M,
-        // past the end, and read the zero line): loads under a branch leave
-        // the ring registers to be merged after it, and that copy waits for
-        // every load in flight -- the prefetch's full latency before GEMM1.
+        // are issued even when there is no next tile (its rows are then those
+        // of tile ntiles, past the end, and read the zero line): loads under a
+        // branch leave the ring registers to be merged after it, and that copy
+        // waits for every load in flight -- the prefetch's full latency before
+        // GEMM1.
         const long ntile = tile + RF_WAVES;
-        const typename Loader::Row nrow = ld.row(ntile < t_end ? ntile * 32 + lr : a.M);
+        const typename Loader::Row nrow = ld.row((ntile < t_end ? ntile : a.ntiles) * 32 + lr);
 #pragma unroll
         for (int p = 0; p < PD; ++p)
             if (p < nch) ld.template load<KCH>(nrow, p, hh, xr[p]);
 
         // Epilogue 0 in registers: bias (broadcast along rows), activation,
         // one rounding to fp16.  hf[s] is GEMM1's operand B for k-step s.
-        half8 hf[2 * NT0];
+        half8 hf[HF];
         act_dispatch(a.act, [&](auto act) {
 #pragma unroll
             for (int t = 0; t < NT0; ++t) {
@@ -236,6 +285,57 @@ void k_chain_rf(Loader ld, RfArgs a)
             }
         });
 
+        // Middle GEMMs of an N-stage chain: the same hand-off again.  Each
+        // takes the previous fp16 output (ks k-steps of 16) as operand B and
+        // produces Nmp columns in passes of 64; bias + activation + fp16 put
+        // pass p's tile t into hn[2 (2p + t) + r / 8] -- again no data leaves
+        // the lane.
+        int ks = 2 * NT0;   // k-steps of hf
+        if constexpr (NMID > 0) {
+#pragma unroll
+            for (int i = 0; i < NMID; ++i) {
+                int lm = lane;
+                asm volatile("" : "+v"(lm));
+                const lds_half* wml[2];
+#pragma unroll
+                for (int t1 = 0; t1 < 2; ++t1)
+                    wml[t1] = Wmn[i].p + frag_lane_off(Wmn[i], 32 * t1, lm) + 4 * (lm >> 5) * Wmn[i].ld;
+                const lds_float* bmi = bms + (i == 0 ? 0 : a.Nmp[0]);
+                half8 hn[8];
+#pragma unroll
+                for (int p = 0; p < 2; ++p) {
+                    if (64 * p < a.Nmp[i]) {
+                        floatx16 am[2];
+                        am[0] = zero16();
+                        am[1] = zero16();
+#pragma unroll
+                        for (int s2 = 0; s2 < 8; ++s2) {
+                            if (s2 < ks) {
+#pragma unroll
+                                for (int t1 = 0; t1 < 2; ++t1) {
+                                    const half8 w = frag_tr_at(wml[t1] + 64 * p + 16 * s2 * Wmn[i].ld, 8 * Wmn[i].ld);
+                                    am[t1] = mfma32x32x16(w, hf[s2], am[t1]);
+                                }
+                            }
+                        }
+                        act_dispatch(a.actm[i], [&](auto act) {
+#pragma unroll
+                            for (int t1 = 0; t1 < 2; ++t1) {
+#pragma unroll
+                                for (int r = 0; r < 16; ++r) {
+                                    const int n = 64 * p + 32 * t1 + 8 * (r >> 2) + 4 * hh + (r & 3);
+                                    hn[2 * (2 * p + t1) + (r >> 3)][r & 7] = (half_t)act.f(am[t1][r] + bmi[n]);
+                                }
+                            }
+                        });
+                    }
+                }
+                ks = a.Nmp[i] >> 4;
+#pragma unroll
+                for (int s2 = 0; s2 < 8; ++s2) hf[s2] = hn[s2];
+            }
+        }
+
         // GEMM1 over N1 in chunks of 64 columns (two 32x32 tiles).
         for (int n1c = 0; n1c < a.N1p; n1c += 64) {
             floatx16 acc1[2];
@@ -244,26 +344,34 @@ void k_chain_rf(Loader ld, RfArgs a)
             // hf[s] element j holds n0 = 16s + 8(j/4) + 4hh + j%4, so the W1^T
             // fragment reads rows 16s + 4hh + [0,4) and 16s + 8 + 4hh + [0,4).
 #pragma unroll
-            for (int s = 0; s < 2 * NT0; ++s) {
+            for (int s = 0; s < HF; ++s) {
+                if (NMID == 0 || s < ks) {
 #pragma unroll
-                for (int t1 = 0; t1 < 2; ++t1) {
-                    const half8 w = frag_tr_at(w1lane[t1] + n1c + 16 * s * W1n.ld, 8 * W1n.ld);
-                    acc1[t1] = mfma32x32x16(w, hf[s], acc1[t1]);
+                    for (int t1 = 0; t1 < 2; ++t1) {
+                        const half8 w = frag_tr_at(w1lane[t1] + n1c + 16 * s * W1n.ld, 8 * W1n.ld);
+                        acc1[t1] = mfma32x32x16(w, hf[s], acc1[t1]);
+                    }
                 }
             }
             // + b1, fp16 into this wave's LDS tile, then whole-line stores:
             // each store instruction writes 8 rows x 128 contiguous bytes.
+            auto out_tile = [&](auto act) {
 #pragma unroll
-            for (int t1 = 0; t1 < 2; ++t1) {
+                for (int t1 = 0; t1 < 2; ++t1) {
 #pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    const int nl = 32 * t1 + 8 * g + 4 * hh;
-                    half4 o;
+                    for (int g = 0; g < 4; ++g) {
+                        const int nl = 32 * t1 + 8 * g + 4 * hh;
+                        half4 o;
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) o[e] = (half_t)(acc1[t1][4 * g + e] + b1s[n1c + nl + e]);
-                    *reinterpret_cast<lds_half4*>(Ost + lr * RF_OLD + nl) = o;
+                        for (int e = 0; e < 4; ++e)
+                            o[e] = (half_t)act.f(acc1[t1][4 * g + e] + b1s[n1c + nl + e]);
+                        *reinterpret_cast<lds_half4*>(Ost + lr * RF_OLD + nl) = o;
+                    }
                 }
-            }
+            };
+            // (the two-GEMM chain has no activation after GEMM1)
+            if constexpr (NMID > 0) act_dispatch(a.act1, out_tile);
+            else out_tile(Act<ACT_NONE>{});
             wave_lds_sync();
             store_tile(Ost, RF_OLD, 32, 64, a.out, a.N1, tile * 32, a.M, n1c, a.N1, lane, 64);
             wave_lds_sync();
@@ -319,15 +427,17 @@ struct DenseRowsQ {
         const half_t* p;   // tile row 4 (qi & 7), this lane's piece
         unsigned ok;       // bit j: tile row 4 (qi & 7) + j exists
     };
+    // m = tile * 32 + lane % 32 (the lane's operand row); the rows this lane
+    // loads are other rows of the same tile, each checked against M.
     __device__ __forceinline__ Row row(long m) const
     {
         const int lane = threadIdx.x & 63, qi = lane >> 2;
-        const long r0 = m - (lane & 31) + 4 * (qi & 7);   // m = tile * 32 + lane % 32, or M past the end
+        const long r0 = m - (lane & 31) + 4 * (qi & 7);
         Row r;
         r.ok = 0;
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-            if (m < M && r0 + j < M) r.ok |= 1u << j;
+            if (r0 + j < M) r.ok |= 1u << j;
         r.p = A + ((r.ok & 1u) ? r0 : 0) * (long)K + 32 * (qi >> 3) + 8 * (lane & 3);
         return r;
     }
@@ -358,12 +468,12 @@ struct DenseRowsQ {
 
 // ----------------------------------------------------------------- launch
 
-template <int NT0, int KCH, class Loader>
+template <int NT0, int KCH, class Loader, int NMID = 0>
 static hipError_t launch_rf_k(const Loader& ld, RfArgs a, hipStream_t st)
 {
-    const size_t lds = rf_lds_bytes(32 * NT0, a.K0p, a.N1p);
+    const size_t lds = NMID ? rf_lds_bytes_n(32 * NT0, a.K0p, a.N1p, NMID, a.Nmp) : rf_lds_bytes(32 * NT0, a.K0p, a.N1p);
     static std::atomic<unsigned long long> lds_set{0};
-    hipError_t e = allow_full_lds((const void*)k_chain_rf<NT0, KCH, Loader>, &lds_set);
+    hipError_t e = allow_full_lds((const void*)k_chain_rf<NT0, KCH, Loader, NMID>, &lds_set);
     if (e != hipSuccess) return e;
     const long per_block_min = RF_WAVES;  // at least one tile per wave
     long grid = device_cu_count();
@@ -371,30 +481,30 @@ static hipError_t launch_rf_k(const Loader& ld, RfArgs a, hipStream_t st)
     if (grid < 1) grid = 1;
     a.tiles_per_block = (a.ntiles + grid - 1) / grid;
     grid = (a.ntiles + a.tiles_per_block - 1) / a.tiles_per_block;
-    hipLaunchKernelGGL((k_chain_rf<NT0, KCH, Loader>), dim3((unsigned)grid), dim3(RF_THREADS), lds, st, ld, a);
+    hipLaunchKernelGGL((k_chain_rf<NT0, KCH, Loader, NMID>), dim3((unsigned)grid), dim3(RF_THREADS), lds, st, ld, a);
     return hipGetLastError();
 }
 
 // Compile-time chunk counts for the k lengths in use (64, 256, 576).
-template <int NT0, class Loader>
+template <int NT0, class Loader, int NMID = 0>
 static hipError_t launch_rf_t(const Loader& ld, const RfArgs& a, hipStream_t st)
 {
     switch (a.K0p >> 6) {
-    case 1: return launch_rf_k<NT0, 1>(ld, a, st);
-    case 4: return launch_rf_k<NT0, 4>(ld, a, st);
-    case 9: return launch_rf_k<NT0, 9>(ld, a, st);
+    case 1: return launch_rf_k<NT0, 1, Loader, NMID>(ld, a, st);
+    case 4: return launch_rf_k<NT0, 4, Loader, NMID>(ld, a, st);
+    case 9: return launch_rf_k<NT0, 9, Loader, NMID>(ld, a, st);
     }
-    return launch_rf_k<NT0, 0>(ld, a, st);
+    return launch_rf_k<NT0, 0, Loader, NMID>(ld, a, st);
 }
 
-template <class Loader>
+template <class Loader, int NMID = 0>
 inline hipError_t launch_rf(const Loader& ld, const RfArgs& a, int nt0, hipStream_t st)
 {
     switch (nt0) {
-    case 1: return launch_rf_t<1>(ld, a, st);
-    case 2: return launch_rf_t<2>(ld, a, st);
-    case 3: return launch_rf_t<3>(ld, a, st);
-    case 4: return launch_rf_t<4>(ld, a, st);
+    case 1: return launch_rf_t<1, Loader, NMID>(ld, a, st);
+    case 2: return launch_rf_t<2, Loader, NMID>(ld, a, st);
+    case 3: return launch_rf_t<3, Loader, NMID>(ld, a, st);
+    case 4: return launch_rf_t<4, Loader, NMID>(ld, a, st);
     }
     return hipErrorInvalidValue;
 }

@@ -648,7 +648,7 @@ hipError_t run_chain_conv2_3x3(const half_t* x, const half_t* w0, const half_t* 
 {
     const long M = (long)NB * H * W;
     if (M == 0) return hipSuccess;
-    RfArgs a;
+    RfArgs a{};
     a.W0 = w0; a.b0 = b0; a.W1 = w1; a.b1 = b1; a.out = y;
     a.M = M; a.K0 = 9 * C; a.N0 = K0; a.N1 = K1;
     a.K0p = (9 * C + 63) / 64 * 64;

@@ -31,6 +31,9 @@ inline hipError_t allow_full_lds(const void* f, std::atomic<unsigned long long>*
 int device_cu_count();
 bool rf_fits(int K0, int N0, int N1);
 bool stream_fits(int N0, int N1);
+bool gemmn_fits(int nst, const int* widths);
+hipError_t run_chain_gemmN(const half_t* A, int nst, const half_t* const* W, const half_t* const* b, const int* act,
+                           const int* widths, half_t* D, long M, hipStream_t st);
 
 hipError_t run_chain_gemm2(const half_t* A, const half_t* W0, const half_t* b0, int act, const half_t* W1,
                            const half_t* b1, half_t* D1, long M, int K0, int N0, int N1, int variant,

@@ -398,7 +398,7 @@ hipError_t run_chain_gemm2(const half_t* A, const half_t* W0, const half_t* b0, 
 {
     if (M == 0) return hipSuccess;
     if (variant == VARIANT_RF) {
-        RfArgs a;
+        RfArgs a{};
         a.W0 = W0; a.b0 = b0; a.W1 = W1; a.b1 = b1; a.out = D1;
         a.M = M; a.K0 = K0; a.N0 = N0; a.N1 = N1;
         a.K0p = (K0 + 63) / 64 * 64;
@@ -445,6 +445,61 @@ hipError_t run_gemm_bias_act(const half_t* A, const half_t* W, const half_t* b, 
     if (N <= 64) return launch_lds_t<1, false>(a, st);
     if (N <= 128) return launch_lds_t<2, false>(a, st);
     return launch_lds_t<4, false>(a, st);
+}
+
+// N-stage register-resident chain: widths[0] = K0, widths[i + 1] = output
+// width of GEMM i (i < nst); every width but K0 and the last <= 128.
+static void gemmn_args(int nst, const half_t* const* W, const half_t* const* b, const int* act, const int* widths,
+                       half_t* D, long M, RfArgs& a)
+{
+    const int nmid = nst - 2;
+    a.W0 = W[0]; a.b0 = b[0]; a.act = act[0];
+    a.W1 = W[nst - 1]; a.b1 = b[nst - 1]; a.act1 = act[nst - 1];
+    a.out = D;
+    a.M = M; a.K0 = widths[0]; a.N0 = widths[1]; a.N1 = widths[nst];
+    a.K0p = (a.K0 + 63) / 64 * 64;
+    a.N1p = (a.N1 + 63) / 64 * 64;
+    for (int i = 0; i < 2; ++i) {
+        const bool on = i < nmid;
+        a.Wm[i] = on ? W[1 + i] : nullptr;
+        a.bm[i] = on ? b[1 + i] : nullptr;
+        a.Nm[i] = on ? widths[2 + i] : 0;
+        a.Nmp[i] = on ? (widths[2 + i] + 63) / 64 * 64 : 0;
+        a.actm[i] = on ? act[1 + i] : 0;
+    }
+    a.Nin1 = widths[nst - 1];
+    a.Nin1p = nmid ? a.Nmp[nmid - 1] : (a.N0 + 31) / 32 * 32;
+    a.ntiles = (M + 31) / 32;
+    a.tiles_per_block = 0;
+}
+
+bool gemmn_fits(int nst, const int* widths)
+{
+    if (nst < 3 || nst > 4) return false;
+    for (int i = 1; i < nst; ++i)
+        if (widths[i] > 128) return false;
+    const half_t* W[4] = {nullptr, nullptr, nullptr, nullptr};
+    const int act[4] = {0, 0, 0, 0};
+    RfArgs a{};
+    gemmn_args(nst, W, W, act, widths, nullptr, 0, a);
+    return rf_lds_bytes_n((a.N0 + 31) / 32 * 32, a.K0p, a.N1p, nst - 2, a.Nmp) <= RF_LDS_LIMIT;
+}
+
+hipError_t run_chain_gemmN(const half_t* A, int nst, const half_t* const* W, const half_t* const* b, const int* act,
+                           const int* widths, half_t* D, long M, hipStream_t st)
+{
+    if (M == 0) return hipSuccess;
+    RfArgs a{};
+    gemmn_args(nst, W, b, act, widths, D, M, a);
+    const int nt0 = (a.N0 + 31) / 32;
+    if (a.K0 == 64 || a.K0 == 256 || a.K0 == 576) {
+        DenseRowsQ ld;
+        ld.A = A; ld.M = M; ld.K = a.K0;
+        return nst == 3 ? launch_rf<DenseRowsQ, 1>(ld, a, nt0, st) : launch_rf<DenseRowsQ, 2>(ld, a, nt0, st);
+    }
+    DenseRows ld;
+    ld.A = A; ld.M = M; ld.K = a.K0;
+    return nst == 3 ? launch_rf<DenseRows, 1>(ld, a, nt0, st) : launch_rf<DenseRows, 2>(ld, a, nt0, st);
 }
 
 bool stream_fits(int N0, int N1)

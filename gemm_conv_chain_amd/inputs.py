@@ -53,6 +53,20 @@ def gemm2_inputs(M, K0, N0, N1, dist="uniform", seed=0, scaled=True):
     return dict(A=A, W0=W0, b0=b0, W1=W1, b1=b1)
 
 
+def gemmN_inputs(M, widths, dist="uniform", seed=0, scaled=True):
+    """A[M,widths[0]], Ws[i] [widths[i], widths[i+1]], bs[i] [widths[i+1]] (fp16);
+    A, W0, b0 scaled by 1/sqrt(widths[0]), W_i and b_i by 1/sqrt(widths[i])."""
+    rng = np.random.default_rng(seed)
+    s0 = 1.0 / math.sqrt(widths[0]) if scaled else 1.0
+    A = _draw(rng, dist, (M, widths[0]), s0)
+    Ws, bs = [], []
+    for i in range(len(widths) - 1):
+        si = 1.0 / math.sqrt(widths[i]) if scaled else 1.0
+        Ws.append(_draw(rng, dist, (widths[i], widths[i + 1]), si))
+        bs.append(_draw(rng, dist, (widths[i + 1],), si))
+    return dict(A=A, Ws=Ws, bs=bs)
+
+
 def conv2_inputs(n, h, w, c, k0, k1, r=3, s=3, seed=0):
     """x[n,h,w,c] ~ N(0,1); w0 HWIO [r,s,c,k0], b0 ~ N(0,1)/sqrt(r*s*c);
     w1 [c1=k0, k1], b1 ~ N(0,1)/sqrt(k0)."""
@@ -84,7 +98,7 @@ def pad_last_dim_np(a, axis, to):
     return np.pad(a, pad)
 
 
-# The five workloads: sizes, distributions and activation of each.
+# The workloads: sizes, distributions and activations of each.
 WORKLOADS = {
     "b2b_gemm_tiny": dict(kind="gemm2", M=512, K0=64, N0=64, N1=64, dist="uniform", act="relu",
                           desc="B2B GEMM A[512x64] W0[64x64] W1[64x64], ReLU"),
@@ -92,6 +106,9 @@ WORKLOADS = {
                         desc="RF-resident B2B GEMM A[65536x256] W0[256x64] W1[64x128], ReLU"),
     "b2b_gemm_lds": dict(kind="gemm2", M=65536, K0=576, N0=256, N1=256, dist="normal", act="gelu_tanh",
                          desc="LDS-resident B2B GEMM A[65536x576] W0[576x256] W1[256x256], GELU(tanh)"),
+    "gemm3_rf": dict(kind="gemmN", M=65536, widths=[256, 64, 64, 128], dist="uniform",
+                     acts=["relu", "relu", "none"],
+                     desc="three-GEMM register-resident chain A[65536x256] -> 64 (ReLU) -> 64 (ReLU) -> 128"),
     "conv3x3_conv1x1": dict(kind="conv2", n=32, h=56, w=56, c=64, k0=64, k1=256, act="relu",
                             desc="NHWC x[32,56,56,64] conv3x3 64->64 +b+ReLU -> conv1x1 64->256 +b"),
     "conv3x3_relu_maxpool": dict(kind="conv_pool", n=32, h=112, w=112, c=60, cpad=64, k=128, act="relu",
@@ -105,6 +122,8 @@ def workload(name, seed=0, **override):
     spec.update(override)
     if spec["kind"] == "gemm2":
         return spec, gemm2_inputs(spec["M"], spec["K0"], spec["N0"], spec["N1"], spec["dist"], seed)
+    if spec["kind"] == "gemmN":
+        return spec, gemmN_inputs(spec["M"], spec["widths"], spec["dist"], seed)
     if spec["kind"] == "conv2":
         return spec, conv2_inputs(spec["n"], spec["h"], spec["w"], spec["c"], spec["k0"], spec["k1"], seed=seed)
     if spec["kind"] == "conv_pool":

@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define FC_ABI_VERSION 1
+#define FC_ABI_VERSION 2
 
 typedef uint16_t fc_half;
 
@@ -113,6 +113,23 @@ fc_status chain_gemm2_variant(const fc_half *A, const fc_half *W0, const fc_half
                               const fc_half *W1, const fc_half *b1, fc_half *D1,
                               int64_t M, int32_t K0, int32_t N0, int32_t N1,
                               fc_variant variant, void *stream);
+
+/*
+ * chain_gemmN -- an N-stage chain of GEMMs in one kernel, every intermediate
+ * kept in registers (BOLT notes, "Persistent kernel (GEMM/Conv) fusion":
+ * persistent fusion of more than two GEMMs, MLP-style):
+ *   X_0 = A [M x widths[0]];  X_{i+1} = act[i](X_i * W[i] + b[i]),
+ *   W[i] [widths[i] x widths[i+1]] row-major, b[i] [widths[i+1]] (b or b[i]
+ *   may be NULL), every X_i with 0 < i < nstages rounded once to fp16,
+ *   D = X_nstages [M x widths[nstages]] (fp16, rounded once).
+ * nstages is 3 or 4 (two GEMMs: chain_gemm2, whose last GEMM has no
+ * activation -- pass FC_ACT_NONE as the last act to match it).  Residence:
+ * widths[1..nstages-1] <= 128 and all weights within LDS, else
+ * FC_E_UNSUPPORTED.  The arrays are host arrays read during the call; W[i],
+ * b[i], A and D are device pointers owned by the caller.  M == 0 is a no-op.
+ */
+fc_status chain_gemmN(const fc_half *A, int32_t nstages, const fc_half *const *W, const fc_half *const *b,
+                      const fc_act *act, const int32_t *widths, fc_half *D, int64_t M, void *stream);
 
 /*
  * chain_conv_pool -- y = maxpool2x2(act(conv(x, w) + b)) with the conv output

@@ -201,6 +201,21 @@ def chain_gemm2(A, W0, b0, act_kind: int, W1, b1):
     return ref, H.view(np.float16)
 
 
+def chain_gemmN(A, Ws, bs, acts):
+    """fp64 [M, widths[n]] of the N-stage chain X_{i+1} = act_i(X_i W_i + b_i)
+    (BOLT notes, "Persistent kernel (GEMM/Conv) fusion", applied to more than
+    two GEMMs): each intermediate is rounded once to fp16, as the fused GPU
+    chain keeps it; the last result is returned unrounded.  Built from the
+    single-operator gemm_bias_act and the fp16 codec (nothing else)."""
+    X = np.asarray(A, dtype=np.float16)
+    n = len(Ws)
+    for i in range(n):
+        Y = gemm_bias_act(X, Ws[i], bs[i], acts[i])
+        if i == n - 1:
+            return Y
+        X = f64_to_f16(Y)
+
+
 def chain_conv2(x, w0, b0, act_kind: int, w1, b1, stride: int = 1, pad: int = 1):
     """(ref fp64 [n,P,Q,K1], H fp16 [n,P,Q,K0]); w1 is [K0,K1] or [1,1,K0,K1]."""
     n, H_, Wd, C = x.shape

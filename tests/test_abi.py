@@ -23,7 +23,7 @@ def L():
 
 def test_exports_every_declared_symbol(L):
     names = fc.exported_names()
-    for n in ("chain_gemm2", "chain_gemm2_variant", "chain_conv_pool", "chain_conv2", "gemm_bias_act",
+    for n in ("chain_gemm2", "chain_gemm2_variant", "chain_gemmN", "chain_conv_pool", "chain_conv2", "gemm_bias_act",
               "conv_bias_act", "maxpool2x2", "pad_channels", "fc_abi_version", "fc_status_str", "fc_last_error"):
         assert n in names
     for n in names:
@@ -31,7 +31,7 @@ def test_exports_every_declared_symbol(L):
 
 
 def test_version_and_status_strings(L):
-    assert fc.abi_version() == 1
+    assert fc.abi_version() == 2
     for code, name in enumerate(["FC_OK", "FC_E_NULL", "FC_E_SHAPE", "FC_E_ALIGN", "FC_E_UNSUPPORTED", "FC_E_HIP",
                                  "FC_E_ARG"]):
         assert L.fc_status_str(code).decode() == name
@@ -58,6 +58,28 @@ def test_chain_gemm2_validation(L):
     assert g2(L, N0=264) == E_UNSUP          # residence: one block owns all N0 <= 256
     assert g2(L, N0=256, variant=1) == E_UNSUP   # register-resident needs N0 <= 128
     assert b"N0" in L.fc_last_error()
+
+
+def gn(L, n=3, widths=(64, 64, 64, 64, 64), W=None, b=None, acts=None, A=P, D=P2, M=512):
+    Wp = (ctypes.c_void_p * 4)(*([P.value] * 4 if W is None else W))
+    bp = None if b is None else (ctypes.c_void_p * 4)(*b)
+    ap = (ctypes.c_int * 4)(*(acts or [1, 1, 1, 0]))
+    wp = (ctypes.c_int32 * 5)(*widths)
+    return L.chain_gemmN(A, n, Wp, bp, ap, wp, D, M, None)
+
+
+def test_chain_gemmN_validation(L):
+    assert gn(L, n=2) == E_UNSUP                    # two GEMMs: chain_gemm2
+    assert gn(L, n=5) == E_UNSUP
+    assert gn(L, widths=(64, 60, 64, 64, 64)) == E_SHAPE
+    assert gn(L, widths=(64, 64, 0, 64, 64)) == E_SHAPE
+    assert gn(L, A=NUL) == E_NULL
+    assert gn(L, W=[P.value, None, P.value, P.value]) == E_NULL
+    assert gn(L, W=[P.value, BAD.value, P.value, P.value]) == E_ALIGN
+    assert gn(L, acts=[1, 9, 1, 0]) == E_ARG
+    assert gn(L, widths=(64, 136, 64, 64, 64)) == E_UNSUP   # an intermediate wider than 128
+    assert b"128" in L.fc_last_error()
+    assert gn(L, M=0) == OK                          # nothing to launch
 
 
 def test_gemm_bias_act_validation(L):

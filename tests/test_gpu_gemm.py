@@ -94,6 +94,20 @@ def test_sensitivity_unscaled(fc, variant):
     assert_close(run_chain(fc, d, "relu", variant), oracle_chain(d, "relu"), "sensitivity")
 
 
+@pytest.mark.parametrize("M,K0", [(130, 64), (130, 256), (161, 576), (63, 256), (33, 64)])
+def test_rf_ragged_unscaled(fc, M, K0):
+    # the last 32-row tile holds 1..31 valid rows; the register-resident dense
+    # loader reads each row through a lane other than the one whose operand it
+    # becomes, so a validity test on the wrong row zeroes valid rows here --
+    # unscaled data with zero biases keeps such a loss above the tolerance
+    d = inputs.gemm2_inputs(M, K0, 64, 128, "uniform", seed=M * 7 + K0, scaled=False)
+    d["b0"] = np.zeros_like(d["b0"])
+    d["b1"] = np.zeros_like(d["b1"])
+    d["W1"] = (d["W1"].astype(np.float64) / 16).astype(np.float16)
+    print("case ragged-unscaled", M, K0, flush=True)
+    assert_close(run_chain(fc, d, "relu", "rf"), oracle_chain(d, "relu"), "ragged")
+
+
 def test_null_biases(fc):
     d = inputs.gemm2_inputs(96, 64, 64, 64, "uniform", seed=9)
     A, W0, W1 = dev(d["A"]), dev(d["W0"]), dev(d["W1"])
@@ -175,3 +189,52 @@ def test_full_size_sampled(fc, name, variant):
     rows = np.unique(np.concatenate([np.arange(32), np.arange(M - 32, M), rng.integers(0, M, 256)]))
     assert_close(out[rows], oracle_chain(d, spec["act"], rows), "full " + name)
     assert np.all(np.isfinite(out))
+
+
+# ------------------------------------------------------------ N-stage chains
+def run_chainN(fc, d, acts):
+    A = dev(d["A"])
+    Ws = [dev(w) for w in d["Ws"]]
+    bs = [dev(b) for b in d["bs"]]
+    out = fc.chain_gemmN(A, Ws, bs, acts)
+    torch.cuda.synchronize()
+    return to_np(out)
+
+
+@pytest.mark.parametrize("M,widths,acts", [
+    (1000, [256, 64, 64, 128], ["relu", "relu", "none"]),                     # the bench's three-GEMM workload shape
+    (333, [72, 96, 40, 136], ["gelu_tanh", "hardswish", "none"]),             # runtime chunk count, padded widths
+    (130, [64, 128, 32, 64, 200], ["relu", "gelu_tanh", "relu", "none"]),     # four GEMMs
+    (97, [576, 32, 128, 64], ["relu", "none", "hardswish"]),                  # activation after the last GEMM
+    (130, [256, 64, 64, 128], ["relu", "relu", "none"]),                      # two valid rows in the last tile
+    (1, [8, 8, 8, 8], ["relu", "relu", "none"]),
+])
+def test_chain_gemmN(fc, M, widths, acts):
+    d = inputs.gemmN_inputs(M, widths, "uniform", seed=M)
+    print("case chain_gemmN", M, widths, acts, flush=True)
+    ref = oracle.chain_gemmN(d["A"], d["Ws"], d["bs"], [ACTS[a] for a in acts])
+    assert_close(run_chainN(fc, d, acts), ref, "chain_gemmN")
+
+
+def test_chain_gemmN_many_tiles_and_unfused(fc):
+    # more tiles than waves (persistent loop), sampled against the oracle, and
+    # the whole output against the composition of single-GEMM kernels
+    M, widths, acts = 70001, [256, 64, 64, 128], ["relu", "relu", "none"]
+    d = inputs.gemmN_inputs(M, widths, "uniform", seed=7)
+    print("case chain_gemmN many tiles", M, widths, flush=True)
+    out = run_chainN(fc, d, acts)
+    rng = np.random.default_rng(2)
+    rows = np.unique(np.concatenate([np.arange(64), np.arange(M - 64, M), rng.integers(0, M, 1000)]))
+    sub = dict(A=d["A"][rows], Ws=d["Ws"], bs=d["bs"])
+    assert_close(out[rows], oracle.chain_gemmN(sub["A"], sub["Ws"], sub["bs"], [ACTS[a] for a in acts]),
+                 "chain_gemmN many tiles")
+    x = dev(d["A"])
+    for i in range(3):
+        x = fc.gemm_bias_act(x, dev(d["Ws"][i]), dev(d["bs"][i]), act=acts[i])
+    assert_close(out, to_np(x).astype(np.float64), "chain_gemmN vs unfused")
+
+
+def test_chain_gemmN_rejects_wide_intermediate(fc):
+    d = inputs.gemmN_inputs(8, [64, 136, 64, 64], "uniform", seed=1)
+    with pytest.raises(fc.FusedChainError):
+        run_chainN(fc, d, ["relu", "relu", "none"])

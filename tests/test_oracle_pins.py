@@ -14,6 +14,7 @@ import numpy as np
 import pytest
 
 from golden_io import read_fields, read_rounding_cases
+from gemm_conv_chain_amd import inputs
 
 pytestmark = pytest.mark.cpu
 
@@ -339,3 +340,38 @@ def test_threads_do_not_change_results(orc):
     finally:
         orc.set_threads(n0)
     assert np.array_equal(a, b)
+
+
+# ------------------------------------------------------------------ N-stage GEMM chains
+def test_chain_gemmN_two_stages_is_chain_gemm2(orc):
+    # the Python composition of single operators equals the C two-GEMM chain
+    d = inputs.gemm2_inputs(37, 24, 40, 16, "uniform", seed=9)
+    ref2, _ = orc.chain_gemm2(d["A"], d["W0"], d["b0"], orc.ACT_GELU_TANH, d["W1"], d["b1"])
+    refn = orc.chain_gemmN(d["A"], [d["W0"], d["W1"]], [d["b0"], d["b1"]], [orc.ACT_GELU_TANH, orc.ACT_NONE])
+    assert np.array_equal(ref2, refn)
+
+
+def test_chain_gemmN_identity_stage(orc):
+    # an identity middle GEMM (zero bias, no activation) reproduces its fp16
+    # input exactly, so the three-stage chain equals the two-stage one
+    d = inputs.gemm2_inputs(29, 16, 32, 24, "uniform", seed=10)
+    eye = np.eye(32, dtype=np.float16)
+    zero = np.zeros(32, dtype=np.float16)
+    ref2, _ = orc.chain_gemm2(d["A"], d["W0"], d["b0"], orc.ACT_RELU, d["W1"], d["b1"])
+    ref3 = orc.chain_gemmN(d["A"], [d["W0"], eye, d["W1"]], [d["b0"], zero, d["b1"]],
+                           [orc.ACT_RELU, orc.ACT_NONE, orc.ACT_NONE])
+    assert np.array_equal(ref2, ref3)
+
+
+def test_chain_gemmN_intermediates_rounded(orc):
+    # stage by stage by hand: each intermediate is the fp16 rounding of the
+    # previous stage's fp64 result (checked against numpy's float16 cast)
+    d = inputs.gemmN_inputs(11, [16, 24, 8, 32], "uniform", seed=12)
+    X = d["A"].astype(np.float64)
+    acts = [orc.ACT_RELU, orc.ACT_HARDSWISH, orc.ACT_NONE]
+    for i in range(3):
+        Y = X @ d["Ws"][i].astype(np.float64) + d["bs"][i].astype(np.float64)
+        Y = orc.act(acts[i], Y)
+        X = Y.astype(np.float16).astype(np.float64) if i < 2 else Y
+    ref = orc.chain_gemmN(d["A"], d["Ws"], d["bs"], acts)
+    assert np.max(np.abs(ref - X)) <= 1e-12 * max(1.0, np.max(np.abs(X)))
