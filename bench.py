@@ -375,6 +375,9 @@ def main():
         achieved = prob.flops / ksec / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": round(PEAK_F16_TFLOPS, 1),
                 "unit": "TFLOP/s", "frac": round(achieved / PEAK_F16_TFLOPS, 4), "traffic": traffic}
+    if tr is not None and "mfma_busy_frac" in tr:
+        # rocprofv3 counters of the same kernel (profiled dispatches, which run a little slower)
+        roof["mfma_busy_frac_pmc"] = tr["mfma_busy_frac"]
     roof.update({"kernel": prob.kernel, "kernel_ms": round(ms_kernel, 5), "timing": method,
                  "flop_per_byte": round(ai, 1),
                  "algorithmic_bytes": prob.bytes_fused, "algorithmic_flops": prob.flops,

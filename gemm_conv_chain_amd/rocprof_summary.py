@@ -2,8 +2,16 @@
 
     python -m gemm_conv_chain_amd.rocprof_summary trace  DIR        # --kernel-trace --stats -f csv
     python -m gemm_conv_chain_amd.rocprof_summary pmc    DIR WORKLOAD [--json profiles/traffic.json]
+    python -m gemm_conv_chain_amd.rocprof_summary mfma   DIR [WORKLOAD --json profiles/traffic.json]
+        (DIR from --pmc SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_VALU_MFMA_MOPS_F16 GRBM_GUI_ACTIVE; run after pmc)
 
 ``trace``: the kernel_stats.csv rows (calls, average/min/max duration).
+``mfma``: matrix-core activity per dispatch of this library's kernels.  On
+MI355X one fp16 MFMA "MOP" is 512 FLOP (SQ_INSTS_VALU_MFMA_MOPS_F16 x 512 is
+the executed FLOP count) and SQ_VALU_MFMA_BUSY_CYCLES is the sum over all
+SIMDs of their busy clocks (it equals executed FLOP / 1024, the fp16 rate of
+one SIMD per clock); GRBM_GUI_ACTIVE is summed over the 8 XCDs, so the
+busy fraction of the 1024 SIMDs is BUSY / (GRBM_GUI_ACTIVE / 8 * 1024).
 ``pmc``: FETCH_SIZE / WRITE_SIZE per dispatch (KiB, mean over the dispatches of
 each kernel) from two ``--pmc`` runs (DIR/fetch, DIR/write) of
 ``bench.py --calib-copy``; WORKLOAD is the bench workload, or WORKLOAD@VARIANT
@@ -41,6 +49,12 @@ def trace(d):
             float(r["MaxNs"]) / 1e3, float(r["Percentage"])))
 
 
+def _ours(name):
+    """This library's kernels: templates appear demangled (fc::...), plain
+    functions keep their mangled name (_ZN2fc...)."""
+    return "fc::" in name or name.startswith("_ZN2fc")
+
+
 def _pmc(d, counter):
     rows = [r for r in _rows(os.path.join(d, "**", "*counter_collection.csv")) if r["Counter_Name"] == counter]
     copies = [r for r in rows if "copyBuffer" in r["Kernel_Name"]]
@@ -50,9 +64,33 @@ def _pmc(d, counter):
     scale = 262144.0 / float(calib["Counter_Value"])
     per = {}
     for r in rows:
-        if "fc::" in r["Kernel_Name"]:
+        if _ours(r["Kernel_Name"]) and "k_pad_mid" not in r["Kernel_Name"]:   # padding is input preparation
             per.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
     return scale, float(calib["Counter_Value"]), {k: sum(v) / len(v) for k, v in per.items()}
+
+
+def mfma(d, workload=None, json_path=None):
+    rows = _rows(os.path.join(d, "**", "*counter_collection.csv"))
+    per = {}
+    for r in rows:
+        if "fc::" in r["Kernel_Name"]:
+            per.setdefault(r["Kernel_Name"], {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    print("| kernel | executed GFLOP (MOPS x 512) | MFMA busy (SIMD-clk) | GRBM_GUI_ACTIVE / 8 (clk) | MFMA busy fraction |")
+    print("|---|---|---|---|---|")
+    for k in sorted(per):
+        v = {c: sum(x) / len(x) for c, x in per[k].items()}
+        mops, busy, act = (v.get(c, 0.0) for c in ("SQ_INSTS_VALU_MFMA_MOPS_F16", "SQ_VALU_MFMA_BUSY_CYCLES",
+                                                  "GRBM_GUI_ACTIVE"))
+        frac = busy / (act / 8 * 1024) if act else 0.0
+        print("| `%s` | %.3f | %.0f | %.0f | %.3f |" % (k[:90], mops * 512 / 1e9, busy, act / 8, frac))
+        if json_path and workload:
+            with open(json_path) as f:
+                db = json.load(f)
+            e = db.get("workloads", {}).get(workload)
+            if e and e.get("kernel") == k:
+                e.update({"mfma_busy_frac": round(frac, 4), "mfma_executed_flops": int(mops * 512)})
+                with open(json_path, "w") as f:
+                    json.dump(db, f, indent=1, sort_keys=True)
 
 
 def pmc(d, workload, json_path=None):
@@ -93,6 +131,9 @@ def pmc(d, workload, json_path=None):
 if __name__ == "__main__":
     if sys.argv[1] == "trace":
         trace(sys.argv[2])
+    elif sys.argv[1] == "mfma":
+        jp = sys.argv[sys.argv.index("--json") + 1] if "--json" in sys.argv else None
+        mfma(sys.argv[2], sys.argv[3] if len(sys.argv) > 3 and sys.argv[3] != "--json" else None, jp)
     else:
         jp = sys.argv[sys.argv.index("--json") + 1] if "--json" in sys.argv else None
         pmc(sys.argv[2], sys.argv[3], jp)
