@@ -315,6 +315,9 @@ def main():
     ap.add_argument("--warm", action="store_true", help="reuse one buffer set (cache-warm timing)")
     ap.add_argument("--no-unfused", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--tune", action="store_true",
+                    help="GEMM-chain workloads: profile the residence variants on the GPU first "
+                         "(chain_gemm2_tune) and time the fastest")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run one 256 MiB device copy (known bytes, for PMC counter calibration)")
@@ -335,6 +338,17 @@ def main():
     prob = Problem(args.workload, cold=not args.warm, variant=args.variant)
     log("workload %s: %d buffer set(s), %.1f MB fused algorithmic bytes, %.3f GFLOP"
         % (args.workload, prob.nsets, prob.bytes_fused / 1e6, prob.flops / 1e9))
+    if args.tune:
+        if prob.spec["kind"] != "gemm2":
+            print("bench.py: --tune applies to the two-GEMM chain workloads", file=sys.stderr)
+            sys.exit(2)
+        W0, b0, W1, b1 = prob.W
+        best, times, _ = fc.tune_chain_gemm2(prob.X[0], W0, b0, W1, b1, act=prob.act, out=prob.Y[0], reps=10)
+        log("tuned: %s (%s)" % (best, ", ".join("%s %.2f us" % kv for kv in sorted(times.items()))))
+        prob.config.update(variant=best, tuned_us={k: round(v, 2) for k, v in times.items()})
+        prob.kernel = {"rf": "k_chain_rf", "lds": "k_gemm_lds", "stream": "k_chain_stream"}[best]
+        prob.traffic_key = args.workload if best == ("lds" if args.workload == "b2b_gemm_lds" else "rf") \
+            else args.workload + "@" + best
 
     ms_step, ms_kernel, ms_wall, method = time_steps(torch, prob.step, args.steps, args.warmup)
     log("fused:   %.4f ms/step (%s, events), kernel %.4f ms, wall %.4f ms" % (ms_step, method, ms_kernel, ms_wall))

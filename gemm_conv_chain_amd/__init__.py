@@ -19,7 +19,7 @@ import ctypes
 import os
 import re
 
-__all__ = ["lib", "FusedChainError", "chain_gemm2", "chain_gemmN", "chain_conv_pool", "chain_conv2", "gemm_bias_act",
+__all__ = ["lib", "FusedChainError", "chain_gemm2", "tune_chain_gemm2", "auto_variant", "tune_clear", "chain_gemmN", "chain_conv_pool", "chain_conv2", "gemm_bias_act",
            "conv_bias_act", "maxpool2x2", "pad_channels", "pad_weight_channels", "abi_version", "ACT", "VARIANT",
            "LIB_PATH", "HEADER_PATH", "exported_names"]
 
@@ -71,7 +71,12 @@ def lib():
         L.conv_bias_act.argtypes = [_vp, _vp, _vp, ctypes.c_int, _vp, ctypes.POINTER(ConvShape), _vp]
         L.maxpool2x2.argtypes = [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _vp]
         L.pad_channels.argtypes = [_vp, _vp, _i64, _i32, _i32, _i32, _vp]
-        for name in ("chain_gemm2", "chain_gemm2_variant", "chain_gemmN", "chain_conv_pool", "chain_conv2", "gemm_bias_act",
+        L.chain_gemm2_tune.argtypes = [_vp, _vp, _vp, ctypes.c_int, _vp, _vp, _vp, _i64, _i32, _i32, _i32, _i32,
+                                       ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_float), _vp]
+        L.chain_gemm2_auto_variant.argtypes = [_i64, _i32, _i32, _i32, ctypes.c_int, ctypes.POINTER(ctypes.c_int)]
+        L.fc_tune_clear.restype = None
+        L.fc_tune_clear.argtypes = []
+        for name in ("chain_gemm2_tune", "chain_gemm2_auto_variant", "chain_gemm2", "chain_gemm2_variant", "chain_gemmN", "chain_conv_pool", "chain_conv2", "gemm_bias_act",
                      "conv_bias_act", "maxpool2x2", "pad_channels"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
@@ -150,6 +155,44 @@ def chain_gemm2(A, W0, b0, W1, b1, act="relu", out=None, variant="auto"):
     _check("chain_gemm2", lib().chain_gemm2_variant(_ptr(A), _ptr(W0), _ptr(b0), _act(act), _ptr(W1), _ptr(b1),
                                                     _ptr(out), M, K0, N0, N1, v, _stream(A)))
     return out
+
+
+_VARIANT_NAME = {v: k for k, v in VARIANT.items()}
+
+
+def tune_chain_gemm2(A, W0, b0, W1, b1, act="relu", out=None, reps=20):
+    """Time every applicable variant of chain_gemm2 on these tensors (blocking),
+    cache the fastest for this shape (later variant='auto' calls use it).
+    Returns (best variant name, {variant name: us per launch}, out)."""
+    for t, n, d in ((A, "A", 2), (W0, "W0", 2), (W1, "W1", 2), (b0, "b0", 1), (b1, "b1", 1)):
+        _need(t, n, d)
+    M, K0 = A.shape
+    N0, N1 = W0.shape[1], W1.shape[1]
+    if W0.shape[0] != K0 or W1.shape[0] != N0:
+        raise ValueError("shape mismatch A%s W0%s W1%s" % (tuple(A.shape), tuple(W0.shape), tuple(W1.shape)))
+    if out is None:
+        out = _torch().empty((M, N1), dtype=A.dtype, device=A.device)
+    _need(out, "out", 2)
+    best = ctypes.c_int(-1)
+    us = (ctypes.c_float * 4)()
+    _check("chain_gemm2_tune", lib().chain_gemm2_tune(_ptr(A), _ptr(W0), _ptr(b0), _act(act), _ptr(W1), _ptr(b1),
+                                                      _ptr(out), M, K0, N0, N1, int(reps), ctypes.byref(best), us,
+                                                      _stream(A)))
+    times = {_VARIANT_NAME[v]: float(us[v]) for v in (1, 2, 3) if us[v] >= 0}
+    return _VARIANT_NAME[best.value], times, out
+
+
+def auto_variant(M, K0, N0, N1, act="relu"):
+    """Name of the variant chain_gemm2(variant='auto') runs for this shape."""
+    v = ctypes.c_int(-1)
+    _check("chain_gemm2_auto_variant", lib().chain_gemm2_auto_variant(int(M), int(K0), int(N0), int(N1), _act(act),
+                                                                      ctypes.byref(v)))
+    return _VARIANT_NAME[v.value]
+
+
+def tune_clear():
+    """Forget every tuned variant choice."""
+    lib().fc_tune_clear()
 
 
 def chain_gemmN(A, Ws, bs, acts, out=None):

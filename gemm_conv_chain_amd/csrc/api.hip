@@ -4,6 +4,10 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <map>
+#include <mutex>
+#include <tuple>
+
 #include "../../include/fusedchain.h"
 #include "fc_launch.h"
 
@@ -75,6 +79,58 @@ fc_status check_conv(const fc_conv_shape* s, int kmax)
     return FC_OK;
 }
 
+
+// Shape rules of chain_gemm2 (no pointers): residence, multiples of 8, the
+// activation, and which variants apply.
+fc_status check_g2_shape(int64_t M, int32_t K0, int32_t N0, int32_t N1, fc_act act, bool* rf_ok, bool* stream_ok)
+{
+    if (M < 0 || K0 <= 0 || N0 <= 0 || N1 <= 0) return fail(FC_E_SHAPE, "M>=0 and K0, N0, N1 > 0 required");
+    if (K0 % 8 || N0 % 8 || N1 % 8) return fail(FC_E_SHAPE, "K0, N0, N1 must be multiples of 8");
+    fc_status s = check_act(act);
+    if (s != FC_OK) return s;
+    if (N0 > 256) return fail(FC_E_UNSUPPORTED, "N0=%d exceeds the residence limit of 256", N0);
+    *rf_ok = N0 <= 128 && fc::rf_fits(K0, N0, N1);
+    *stream_ok = fc::stream_fits(N0, N1);
+    return FC_OK;
+}
+
+fc_status check_g2_ptrs(const fc_half* A, const fc_half* W0, const fc_half* b0, const fc_half* W1, const fc_half* b1,
+                        const fc_half* D1, int64_t M)
+{
+    if (!W0 || !W1 || (M > 0 && (!A || !D1))) return fail(FC_E_NULL, "A, W0, W1 and D1 are required");
+    if (!aligned16(A) || !aligned16(W0) || !aligned16(W1) || !aligned16(D1) || !aligned16(b0) || !aligned16(b1))
+        return fail(FC_E_ALIGN, "tensor pointers must be 16-byte aligned");
+    return FC_OK;
+}
+
+// Tuned variant choices (chain_gemm2_tune), per device and shape.
+typedef std::tuple<int, int64_t, int32_t, int32_t, int32_t, int> TuneKey;   // device, M, K0, N0, N1, act
+std::mutex g_tune_mu;
+std::map<TuneKey, int> g_tune;
+
+int rule_variant(bool rf_ok, bool stream_ok)
+{
+    return rf_ok ? fc::VARIANT_RF : (stream_ok ? fc::VARIANT_STREAM : fc::VARIANT_LDS);
+}
+
+// The variant FC_VARIANT_AUTO runs: the tuned one for this device and shape if
+// any, else the static rule.  The device is only queried when something has
+// been tuned.
+int auto_variant(int64_t M, int32_t K0, int32_t N0, int32_t N1, int act, bool rf_ok, bool stream_ok)
+{
+    {
+        std::lock_guard<std::mutex> g(g_tune_mu);
+        if (!g_tune.empty()) {
+            int dev = 0;
+            if (hipGetDevice(&dev) == hipSuccess) {
+                auto it = g_tune.find(TuneKey(dev, M, K0, N0, N1, act));
+                if (it != g_tune.end()) return it->second;
+            }
+        }
+    }
+    return rule_variant(rf_ok, stream_ok);
+}
+
 }  // namespace
 
 extern "C" {
@@ -101,26 +157,92 @@ fc_status chain_gemm2_variant(const fc_half* A, const fc_half* W0, const fc_half
                               const fc_half* W1, const fc_half* b1, fc_half* D1, int64_t M, int32_t K0, int32_t N0,
                               int32_t N1, fc_variant variant, void* stream)
 {
+    bool rf_ok = false, stream_ok = false;
     if (M < 0 || K0 <= 0 || N0 <= 0 || N1 <= 0) return fail(FC_E_SHAPE, "M>=0 and K0, N0, N1 > 0 required");
-    if (!W0 || !W1 || (M > 0 && (!A || !D1))) return fail(FC_E_NULL, "A, W0, W1 and D1 are required");
-    if (K0 % 8 || N0 % 8 || N1 % 8) return fail(FC_E_SHAPE, "K0, N0, N1 must be multiples of 8");
-    if (!aligned16(A) || !aligned16(W0) || !aligned16(W1) || !aligned16(D1) || !aligned16(b0) || !aligned16(b1))
-        return fail(FC_E_ALIGN, "tensor pointers must be 16-byte aligned");
-    fc_status s = check_act(act);
+    fc_status s = check_g2_ptrs(A, W0, b0, W1, b1, D1, M);
+    if (s != FC_OK) return s;
+    s = check_g2_shape(M, K0, N0, N1, act, &rf_ok, &stream_ok);
     if (s != FC_OK) return s;
     if ((int)variant < 0 || (int)variant > 3) return fail(FC_E_ARG, "variant %d out of range", (int)variant);
-    if (N0 > 256) return fail(FC_E_UNSUPPORTED, "N0=%d exceeds the residence limit of 256", N0);
-    const bool rf_ok = N0 <= 128 && fc::rf_fits(K0, N0, N1);
-    const bool stream_ok = fc::stream_fits(N0, N1);
     int v = variant;
-    if (v == FC_VARIANT_AUTO) v = rf_ok ? fc::VARIANT_RF : (stream_ok ? fc::VARIANT_STREAM : fc::VARIANT_LDS);
     if (v == FC_VARIANT_RF && !rf_ok)
         return fail(FC_E_UNSUPPORTED, "register-resident variant needs N0<=128 and W0,W1 within LDS");
     if (v == FC_VARIANT_STREAM && !stream_ok)
         return fail(FC_E_UNSUPPORTED, "streamed variant needs N1<=16128 (biases beside the weight buffers)");
+    if (M == 0) return ok();
+    if (v == FC_VARIANT_AUTO) v = auto_variant(M, K0, N0, N1, (int)act, rf_ok, stream_ok);
     return hip_status(fc::run_chain_gemm2(H(A), H(W0), H(b0), act, H(W1), H(b1), Hm(D1), M, K0, N0, N1, v,
                                           (hipStream_t)stream),
                       "chain_gemm2");
+}
+
+fc_status chain_gemm2_tune(const fc_half* A, const fc_half* W0, const fc_half* b0, fc_act act, const fc_half* W1,
+                           const fc_half* b1, fc_half* D1, int64_t M, int32_t K0, int32_t N0, int32_t N1,
+                           int32_t reps, fc_variant* best, float* us, void* stream)
+{
+    bool rf_ok = false, stream_ok = false;
+    if (M < 0 || K0 <= 0 || N0 <= 0 || N1 <= 0) return fail(FC_E_SHAPE, "M>=0 and K0, N0, N1 > 0 required");
+    fc_status s = check_g2_ptrs(A, W0, b0, W1, b1, D1, M);
+    if (s != FC_OK) return s;
+    s = check_g2_shape(M, K0, N0, N1, act, &rf_ok, &stream_ok);
+    if (s != FC_OK) return s;
+    if (M == 0) return fail(FC_E_SHAPE, "M == 0: nothing to time");
+    if (reps < 1 || reps > 1000) return fail(FC_E_SHAPE, "reps=%d outside 1..1000", (int)reps);
+    hipStream_t st = (hipStream_t)stream;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_status(e, "chain_gemm2_tune: hipGetDevice");
+    hipEvent_t t0 = nullptr, t1 = nullptr;
+    e = hipEventCreate(&t0);
+    if (e == hipSuccess) e = hipEventCreate(&t1);
+    float tv[4] = {-1.0f, -1.0f, -1.0f, -1.0f};
+    int vbest = -1;
+    const int cand[3] = {fc::VARIANT_RF, fc::VARIANT_STREAM, fc::VARIANT_LDS};
+    for (int i = 0; i < 3 && e == hipSuccess; ++i) {
+        const int v = cand[i];
+        if ((v == fc::VARIANT_RF && !rf_ok) || (v == fc::VARIANT_STREAM && !stream_ok)) continue;
+        auto launch = [&]() {
+            return fc::run_chain_gemm2(H(A), H(W0), H(b0), act, H(W1), H(b1), Hm(D1), M, K0, N0, N1, v, st);
+        };
+        e = launch();   // untimed: first-use set-up (LDS limits, code upload)
+        if (e == hipSuccess) e = hipEventRecord(t0, st);
+        for (int r = 0; r < reps && e == hipSuccess; ++r) e = launch();
+        if (e == hipSuccess) e = hipEventRecord(t1, st);
+        if (e == hipSuccess) e = hipEventSynchronize(t1);
+        float ms = 0.0f;
+        if (e == hipSuccess) e = hipEventElapsedTime(&ms, t0, t1);
+        if (e != hipSuccess) break;
+        tv[v] = 1000.0f * ms / (float)reps;
+        if (vbest < 0 || tv[v] < tv[vbest]) vbest = v;
+    }
+    if (t0) (void)hipEventDestroy(t0);
+    if (t1) (void)hipEventDestroy(t1);
+    if (e != hipSuccess) return hip_status(e, "chain_gemm2_tune");
+    tv[FC_VARIANT_AUTO] = tv[vbest];
+    {
+        std::lock_guard<std::mutex> g(g_tune_mu);
+        g_tune[TuneKey(dev, M, K0, N0, N1, (int)act)] = vbest;
+    }
+    if (best) *best = (fc_variant)vbest;
+    if (us)
+        for (int i = 0; i < 4; ++i) us[i] = tv[i];
+    return ok();
+}
+
+fc_status chain_gemm2_auto_variant(int64_t M, int32_t K0, int32_t N0, int32_t N1, fc_act act, fc_variant* out)
+{
+    bool rf_ok = false, stream_ok = false;
+    if (!out) return fail(FC_E_NULL, "out is required");
+    fc_status s = check_g2_shape(M, K0, N0, N1, act, &rf_ok, &stream_ok);
+    if (s != FC_OK) return s;
+    *out = (fc_variant)auto_variant(M, K0, N0, N1, (int)act, rf_ok, stream_ok);
+    return ok();
+}
+
+void fc_tune_clear(void)
+{
+    std::lock_guard<std::mutex> g(g_tune_mu);
+    g_tune.clear();
 }
 
 fc_status chain_gemm2(const fc_half* A, const fc_half* W0, const fc_half* b0, fc_act act, const fc_half* W1,

@@ -365,42 +365,83 @@ void k_conv_w(ConvWArgs a)
                 half_t* yb = a.y + win0 * K;
                 uint8_t* ab = a.argmax ? a.argmax + win0 * K : nullptr;
                 const int nw = (int)min(16L, (nrows >> 2) - win0);
-                // comparisons keep the per-lane value on one side and the
-                // wave-uniform remainder on the other, so no per-(t, u, g)
-                // lane value is precomputed and held
-                const int olane = hh * K + lr;
-                int nwl = nw - hh;   // window 8u + 2g + hh is valid iff 8u + 2g < nwl
-                asm volatile("" : "+v"(nwl));   // (opaque: compared against constants, not folded back)
+                // pv[t][u][g]: pooled value of window 8u + 2g + hh, channel 32t + lr
+                half_t pv[NTK][2][4];
+                if (decltype(act)::monotone && !ab) {
+                    // Bias addition (fp32 rounding), a non-decreasing activation and
+                    // the fp16 rounding are all monotone, so the max of the four
+                    // rounded values is the rounded value of the largest
+                    // accumulator: pool first, then one bias/act/convert per window.
 #pragma unroll
-                for (int t = 0; t < NTK; ++t) {
-                    const float bk = bsl[32 * t];
-                    const bool kok = lr < K - 32 * t;
+                    for (int t = 0; t < NTK; ++t) {
+                        const float bk = bsl[32 * t];
 #pragma unroll
-                    for (int u = 0; u < 2; ++u) {
+                        for (int u = 0; u < 2; ++u)
 #pragma unroll
-                        for (int g = 0; g < 4; ++g) {
-                            // round each value to fp16 first: the pooled value
-                            // and its argmax are decided on the fp16 intermediate
-                            half_t best = (half_t)act.f(acc[u][t][4 * g] + bk);
-                            int bi = 0;
-#pragma unroll
-                            for (int e = 1; e < 4; ++e) {
-                                const half_t v = (half_t)act.f(acc[u][t][4 * g + e] + bk);
-                                const bool gt = v > best;
-                                best = gt ? v : best;
-                                bi = gt ? e : bi;
+                            for (int g = 0; g < 4; ++g) {
+                                const float m = __builtin_fmaxf(
+                                    __builtin_fmaxf(acc[u][t][4 * g], acc[u][t][4 * g + 1]),
+                                    __builtin_fmaxf(acc[u][t][4 * g + 2], acc[u][t][4 * g + 3]));
+                                pv[t][u][g] = (half_t)act.f(m + bk);
                             }
-                            const int w0 = 8 * u + 2 * g;
-                            ow[w0 * 32] = best;
-                            if (ab && kok && w0 < nwl) ab[olane + w0 * K + 32 * t] = (uint8_t)bi;
-                        }
-                        __builtin_amdgcn_sched_barrier(0);   // bound the scheduling window
                     }
+                } else {
+                    // The pooled value and its argmax are decided on the rounded
+                    // fp16 intermediate (first maximum in window order).
+                    // Comparisons keep the per-lane value on one side and the
+                    // wave-uniform remainder on the other, so no per-(t, u, g)
+                    // lane value is precomputed and held.
+                    const int olane = hh * K + lr;
+                    int nwl = nw - hh;   // window 8u + 2g + hh is valid iff 8u + 2g < nwl
+                    asm volatile("" : "+v"(nwl));   // (opaque: compared against constants, not folded back)
+#pragma unroll
+                    for (int t = 0; t < NTK; ++t) {
+                        const float bk = bsl[32 * t];
+                        const bool kok = lr < K - 32 * t;
+#pragma unroll
+                        for (int u = 0; u < 2; ++u) {
+#pragma unroll
+                            for (int g = 0; g < 4; ++g) {
+                                half_t best = (half_t)act.f(acc[u][t][4 * g] + bk);
+                                int bi = 0;
+#pragma unroll
+                                for (int e = 1; e < 4; ++e) {
+                                    const half_t v = (half_t)act.f(acc[u][t][4 * g + e] + bk);
+                                    const bool gt = v > best;
+                                    best = gt ? v : best;
+                                    bi = gt ? e : bi;
+                                }
+                                pv[t][u][g] = best;
+                                const int w0 = 8 * u + 2 * g;
+                                if (ab && kok && w0 < nwl) ab[olane + w0 * K + 32 * t] = (uint8_t)bi;
+                            }
+                            __builtin_amdgcn_sched_barrier(0);   // bound the scheduling window
+                        }
+                    }
+                }
+                // Whole output rows: four passes of four windows, each staged as
+                // [4 windows][KP channels] fp16 (1 KiB for KP = 128) and stored
+                // by KP/8 lanes per window row, 16 bytes each, so every store
+                // instruction writes whole 256-byte rows of y.  Pass p holds
+                // windows 4p..4p+3 = 8u + 2g + hh with u = p/2, g = 2(p%2) + gg.
+                static_assert(4 * KP * 2 <= CW_OSTAGE, "four staged rows fit the staging area");
+                constexpr int LPR = KP / 8;   // lanes per staged row
+                const int sr = lane / LPR, sg = lane % LPR;
+                const lds_half8* const srd = reinterpret_cast<const lds_half8*>(ost + sr * KP + 8 * sg);
+#pragma unroll
+                for (int p = 0; p < 4; ++p) {
+#pragma unroll
+                    for (int gg = 0; gg < 2; ++gg)
+#pragma unroll
+                        for (int t = 0; t < NTK; ++t)
+                            ost[(2 * gg + hh) * KP + 32 * t + lr] = pv[t][p >> 1][2 * (p & 1) + gg];
                     wave_lds_sync();
-                    const half8 v = *orb;
-                    if (rr < nw && 8 * grp < K - 32 * t)
-                        st_out(reinterpret_cast<half8*>(yb + rr * K + 32 * t + 8 * grp), v);
-                    wave_lds_sync();   // the next t overwrites the staging area
+                    if (sr < 4) {
+                        const half8 v = *srd;
+                        const int w = 4 * p + sr;
+                        if (w < nw && 8 * sg < K) st_out(reinterpret_cast<half8*>(yb + w * K + 8 * sg), v);
+                    }
+                    wave_lds_sync();   // the next pass overwrites the staging area
                 }
             } else {
                 half_t* yb = a.y + row0 * K;

@@ -100,13 +100,18 @@ __device__ __forceinline__ void st_out(V* p, const V& v)
 // by the hardware base-2 exponential and reciprocal: no cancellation near 0,
 // and the exponential saturating to 0 or infinity gives x or 0 at the extremes.
 template <int ACT> struct Act;
+// `monotone`: f is non-decreasing, so max_i f(v_i) = f(max_i v_i) (used by
+// the max-pool epilogue; GELU and Hardswish dip below zero and are not).
 template <> struct Act<ACT_NONE> {
+    static constexpr bool monotone = true;
     __device__ static __forceinline__ float f(float x) { return x; }
 };
 template <> struct Act<ACT_RELU> {
+    static constexpr bool monotone = true;
     __device__ static __forceinline__ float f(float x) { return x > 0.0f ? x : 0.0f; }
 };
 template <> struct Act<ACT_GELU_TANH> {
+    static constexpr bool monotone = false;
     __device__ static __forceinline__ float f(float x)
     {
         const float c1 = -2.0f * 0.7978845608028654f * 1.4426950408889634f;   // -2 sqrt(2/pi) log2(e)
@@ -119,6 +124,7 @@ template <> struct Act<ACT_GELU_TANH> {
 // Hardswish x * min(max(x + 3, 0), 6) / 6 (the fused Conv2D + BiasAdd +
 // Hardswish epilogue of the BOLT notes, "Enabling deeper operator fusion").
 template <> struct Act<ACT_HARDSWISH> {
+    static constexpr bool monotone = false;
     __device__ static __forceinline__ float f(float x)
     {
         const float r6 = __builtin_fminf(__builtin_fmaxf(x + 3.0f, 0.0f), 6.0f);

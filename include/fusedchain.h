@@ -115,6 +115,41 @@ fc_status chain_gemm2_variant(const fc_half *A, const fc_half *W0, const fc_half
                               fc_variant variant, void *stream);
 
 /*
+ * chain_gemm2_tune -- hardware profiling of the fused-chain variants for one
+ * shape (BOLT notes, "Light-weight performance profiler": candidate kernel
+ * configurations are measured on the GPU and the fastest is kept; Welder
+ * notes, "Tile-graph Scheduling": a few efficient tile configurations are
+ * profiled on the hardware and the best one chosen).  The candidates are the
+ * residence forms of chain_gemm2_variant that apply to (K0, N0, N1).
+ * Arguments as for chain_gemm2, plus:
+ *   reps     timed launches per candidate, 1..1000 (one untimed launch first);
+ *   best     out (host, may be NULL): the fastest variant;
+ *   us       out (host, may be NULL): float[4], mean microseconds per launch
+ *            indexed by fc_variant (us[FC_VARIANT_AUTO] = the best time;
+ *            -1 for a variant that does not apply).
+ * The result is cached per (device, M, K0, N0, N1, act): later chain_gemm2 /
+ * FC_VARIANT_AUTO calls of that shape run the chosen variant (the cache is
+ * process-wide, guarded by a lock).  D1 is overwritten with the chain's
+ * result (every candidate computes it).  BLOCKING: the call records HIP
+ * events on `stream` and waits for them, so it must not be issued during
+ * stream capture.  Validation errors as chain_gemm2; FC_E_SHAPE if reps is
+ * out of range; FC_E_SHAPE if M == 0 (nothing to time).
+ */
+fc_status chain_gemm2_tune(const fc_half *A, const fc_half *W0, const fc_half *b0, fc_act act,
+                           const fc_half *W1, const fc_half *b1, fc_half *D1,
+                           int64_t M, int32_t K0, int32_t N0, int32_t N1,
+                           int32_t reps, fc_variant *best, float *us, void *stream);
+
+/* The variant FC_VARIANT_AUTO runs for this shape on the current device:
+ * the tuned choice if chain_gemm2_tune cached one, else the static rule (RF
+ * when it applies, else STREAM, else LDS).  Host only, launches nothing.
+ * Returns FC_E_SHAPE / FC_E_ARG / FC_E_UNSUPPORTED as chain_gemm2 would. */
+fc_status chain_gemm2_auto_variant(int64_t M, int32_t K0, int32_t N0, int32_t N1, fc_act act, fc_variant *out);
+
+/* Forget every tuned choice (all devices). */
+void fc_tune_clear(void);
+
+/*
  * chain_gemmN -- an N-stage chain of GEMMs in one kernel, every intermediate
  * kept in registers (BOLT notes, "Persistent kernel (GEMM/Conv) fusion":
  * persistent fusion of more than two GEMMs, MLP-style):

@@ -24,7 +24,8 @@ def L():
 def test_exports_every_declared_symbol(L):
     names = fc.exported_names()
     for n in ("chain_gemm2", "chain_gemm2_variant", "chain_gemmN", "chain_conv_pool", "chain_conv2", "gemm_bias_act",
-              "conv_bias_act", "maxpool2x2", "pad_channels", "fc_abi_version", "fc_status_str", "fc_last_error"):
+              "conv_bias_act", "maxpool2x2", "pad_channels", "fc_abi_version", "fc_status_str", "fc_last_error",
+              "chain_gemm2_tune", "chain_gemm2_auto_variant", "fc_tune_clear"):
         assert n in names
     for n in names:
         assert hasattr(L, n), n
@@ -143,3 +144,33 @@ def test_binding_refuses_host_tensors():
     A = torch.zeros(4, 8, dtype=torch.float16)
     with pytest.raises(TypeError):
         fc.chain_gemm2(A, A.T.contiguous(), None, A, None)
+
+
+def test_tune_validation(L):
+    import ctypes as C
+    best, us = C.c_int(-1), (C.c_float * 4)()
+
+    def tune(A=P, W0=P, D1=P2, M=512, K0=64, N0=64, N1=64, act=1, reps=5):
+        return L.chain_gemm2_tune(A, W0, NUL, act, P, NUL, D1, M, K0, N0, N1, reps, C.byref(best), us, None)
+    assert tune(A=NUL) == E_NULL
+    assert tune(D1=BAD) == E_ALIGN
+    assert tune(K0=60) == E_SHAPE
+    assert tune(M=0) == E_SHAPE            # nothing to time
+    assert tune(reps=0) == E_SHAPE
+    assert tune(reps=1001) == E_SHAPE
+    assert tune(act=9) == E_ARG
+    assert tune(N0=264) == E_UNSUP
+    assert best.value == -1                # nothing written on failure
+
+
+def test_auto_variant_rule(L):
+    # without tuning, 'auto' follows the static rule: register-resident when
+    # W0 and W1 fit in LDS with N0 <= 128, else streamed weights, else LDS
+    fc.tune_clear()
+    assert fc.auto_variant(65536, 256, 64, 128, "relu") == "rf"
+    assert fc.auto_variant(65536, 576, 256, 256, "gelu_tanh") == "stream"
+    assert fc.auto_variant(4096, 64, 256, 16136, "relu") == "lds"
+    v = ctypes.c_int(-1)
+    assert L.chain_gemm2_auto_variant(-1, 64, 64, 64, 1, ctypes.byref(v)) == E_SHAPE
+    assert L.chain_gemm2_auto_variant(64, 64, 64, 64, 1, None) == E_NULL
+    assert L.chain_gemm2_auto_variant(64, 64, 264, 64, 1, ctypes.byref(v)) == E_UNSUP

@@ -49,14 +49,25 @@ def check_pool(y, am, x_np, w_np, b_np, what, act="relu"):
     return 0, 0
 
 
+def pool_both(fc, x, w, b, act="relu"):
+    """The fused conv+pool with and without argmax: without argmax and with a
+    non-decreasing activation the kernel pools the fp32 accumulators before
+    bias/activation/rounding, which must give bit-identical y."""
+    y, am = fc.chain_conv_pool(x, w, b, act=act, pool="max2x2", argmax=True)
+    y2 = fc.chain_conv_pool(x, w, b, act=act, pool="max2x2")
+    torch.cuda.synchronize()
+    y, am, y2 = to_np(y), to_np(am), to_np(y2)
+    assert np.array_equal(y.view(np.uint16), y2.view(np.uint16)), "y with and without argmax differ"
+    return y, am
+
+
 @pytest.mark.parametrize("n,h,w,c,k", [(2, 8, 10, 64, 128), (1, 5, 7, 32, 64), (2, 9, 6, 64, 72), (1, 4, 6, 96, 64),
                                        (1, 12, 12, 64, 8), (3, 3, 17, 32, 32)])
 def test_conv_pool_small(fc, n, h, w, c, k):
     d = inputs.conv_pool_inputs(n, h, w, c, k, seed=h * w)
     print("case conv_pool", n, h, w, c, k, flush=True)
-    y, am = fc.chain_conv_pool(dev(d["x"]), dev(d["w"]), dev(d["b"]), act="relu", pool="max2x2", argmax=True)
-    torch.cuda.synchronize()
-    free, ties = check_pool(to_np(y), to_np(am), d["x"], d["w"], d["b"], "conv_pool small")
+    y, am = pool_both(fc, dev(d["x"]), dev(d["w"]), dev(d["b"]))
+    free, ties = check_pool(y, am, d["x"], d["w"], d["b"], "conv_pool small")
     assert free > 0
 
 
@@ -68,9 +79,8 @@ def test_conv_pool_activations(fc, act, c):
     # negative, so ties at zero are rare)
     d = inputs.conv_pool_inputs(2, 10, 14, c, 96, seed=17)
     print("case conv_pool act", act, "c", c, flush=True)
-    y, am = fc.chain_conv_pool(dev(d["x"]), dev(d["w"]), dev(d["b"]), act=act, pool="max2x2", argmax=True)
-    torch.cuda.synchronize()
-    free, _ = check_pool(to_np(y), to_np(am), d["x"], d["w"], d["b"], "conv_pool " + act, act=act)
+    y, am = pool_both(fc, dev(d["x"]), dev(d["w"]), dev(d["b"]), act=act)
+    free, _ = check_pool(y, am, d["x"], d["w"], d["b"], "conv_pool " + act, act=act)
     assert free > 0
 
 
@@ -79,9 +89,8 @@ def test_conv_pool_many_tiles_ragged(fc):
     # windows = 47 full 16-window tiles + 13), C = 64 (compile-time chunk path)
     d = inputs.conv_pool_inputs(3, 30, 34, 64, 128, seed=23)
     print("case conv_pool 3x30x34x64->128", flush=True)
-    y, am = fc.chain_conv_pool(dev(d["x"]), dev(d["w"]), dev(d["b"]), argmax=True)
-    torch.cuda.synchronize()
-    check_pool(to_np(y), to_np(am), d["x"], d["w"], d["b"], "conv_pool many tiles")
+    y, am = pool_both(fc, dev(d["x"]), dev(d["w"]), dev(d["b"]))
+    check_pool(y, am, d["x"], d["w"], d["b"], "conv_pool many tiles")
 
 
 def test_conv_bias_act_many_tiles_ragged(fc):
@@ -184,9 +193,7 @@ def test_conv_pool_full_size_sampled(fc):
     print("case full conv3x3_relu_maxpool", flush=True)
     x = fc.pad_channels(dev(d["x"]), 64)
     w = fc.pad_weight_channels(dev(d["w"]), 64)
-    y, am = fc.chain_conv_pool(x, w, dev(d["b"]), argmax=True)
-    torch.cuda.synchronize()
-    y, am = to_np(y), to_np(am)
+    y, am = pool_both(fc, x, w, dev(d["b"]))   # without argmax: the launch the bench times
     assert np.all(np.isfinite(y.astype(np.float64)))
     for img in (0, 31):
         check_pool(y[img:img + 1], am[img:img + 1], d["x"][img:img + 1], d["w"], d["b"], "full img %d" % img)

@@ -238,3 +238,27 @@ def test_chain_gemmN_rejects_wide_intermediate(fc):
     d = inputs.gemmN_inputs(8, [64, 136, 64, 64], "uniform", seed=1)
     with pytest.raises(fc.FusedChainError):
         run_chainN(fc, d, ["relu", "relu", "none"])
+
+
+@pytest.mark.parametrize("shape,act", [((1000, 256, 64, 128), "relu"), ((2000, 576, 256, 256), "gelu_tanh")])
+def test_tune_chain_gemm2(fc, shape, act):
+    # hardware profiling of the residence variants: every applicable one is
+    # timed, the fastest is cached for the shape and then used by 'auto'
+    M, K0, N0, N1 = shape
+    d = inputs.gemm2_inputs(M, K0, N0, N1, "uniform", seed=11)
+    A, W0, b0, W1, b1 = (dev(d[k]) for k in ("A", "W0", "b0", "W1", "b1"))
+    print("case tune", shape, act, flush=True)
+    fc.tune_clear()
+    rule = fc.auto_variant(M, K0, N0, N1, act)
+    best, times, out = fc.tune_chain_gemm2(A, W0, b0, W1, b1, act=act, reps=5)
+    torch.cuda.synchronize()
+    ref = oracle_chain(d, act)
+    assert_close(to_np(out), ref, "tuned output")
+    expect = {"rf", "lds", "stream"} if N0 <= 128 else {"lds", "stream"}
+    assert set(times) == expect and all(t > 0 for t in times.values())
+    assert best == min(times, key=times.get)
+    assert fc.auto_variant(M, K0, N0, N1, act) == best
+    assert fc.auto_variant(M + 8, K0, N0, N1, act) == rule        # another shape keeps the static rule
+    assert_close(run_chain(fc, d, act, "auto"), ref, "auto after tuning")
+    fc.tune_clear()
+    assert fc.auto_variant(M, K0, N0, N1, act) == rule
