@@ -126,6 +126,26 @@ class Problem:
             self.config = {"workload": name, "x": [n, h, w, c], "conv0": "3x3 s1 p1 %d->%d +b ReLU" % (c, k0),
                            "conv1": "1x1 %d->%d +b" % (k0, k1)}
             self.kernel = "k_chain_rf"
+        elif s["kind"] == "convN":
+            n, h, w, c, ks = s["n"], s["h"], s["w"], s["c"], s["ks"]
+            self.acts = s["acts"]
+            npix = n * h * w
+            chans = [9 * c] + ks
+            self.flops = 2 * npix * sum(chans[i] * chans[i + 1] for i in range(len(ks)))
+            self.flops_exec = self.flops
+            wbytes = 2 * sum(chans[i] * chans[i + 1] + chans[i + 1] for i in range(len(ks)))
+            self.bytes_fused = 2 * (npix * c + npix * ks[-1]) + wbytes
+            self.bytes_interm = 2 * npix * sum(ks[:-1])
+            self.W = [t(x) for x in d["ws"]] + [t(x) for x in d["bs"]]
+            per_set = 2 * (npix * c + npix * ks[-1])
+            self.nsets = max(1, math.ceil(COLD_BYTES / per_set)) if cold else 1
+            x = t(d["x"])
+            self.X = [x] + [x.clone() for _ in range(self.nsets - 1)]
+            self.Y = [torch.empty((n, h, w, ks[-1]), dtype=torch.float16, device=dev) for _ in range(self.nsets)]
+            self.Hs = [torch.empty((n, h, w, k), dtype=torch.float16, device=dev) for k in ks[:-1]]
+            self.config = {"workload": name, "x": [n, h, w, c], "conv0": "3x3 s1 p1 %d->%d +b %s" % (c, ks[0], self.acts[0]),
+                           "conv1x1": ["%d->%d +b %s" % (ks[i - 1], ks[i], self.acts[i]) for i in range(1, len(ks))]}
+            self.kernel = "k_chain_rf"
         else:
             n, h, w, c, cp, k = s["n"], s["h"], s["w"], s["c"], s["cpad"], s["k"]
             npix = n * h * w
@@ -158,6 +178,9 @@ class Problem:
         elif s["kind"] == "conv2":
             w0, b0, w1, b1 = self.W
             fc.chain_conv2(self.X[j], w0, b0, w1, b1, act="relu", out=self.Y[j])
+        elif s["kind"] == "convN":
+            n = len(self.acts)
+            fc.chain_convN(self.X[j], self.W[:n], self.W[n:], self.acts, out=self.Y[j])
         else:
             w, b = self.W
             fc.chain_conv_pool(self.X[j], w, b, act="relu", pool="max2x2", out=self.Y[j])
@@ -181,6 +204,14 @@ class Problem:
             fc.conv_bias_act(self.X[j], w0, b0, act="relu", out=self.H)
             k0 = self.H.shape[-1]
             fc.gemm_bias_act(self.H.view(-1, k0), w1, b1, act="none", out=self.Y[j].view(-1, self.Y[j].shape[-1]))
+        elif s["kind"] == "convN":
+            n = len(self.acts)
+            fc.conv_bias_act(self.X[j], self.W[0], self.W[n], act=self.acts[0], out=self.Hs[0])
+            for k in range(1, n):
+                src = self.Hs[k - 1]
+                dst = self.Hs[k] if k < n - 1 else self.Y[j]
+                fc.gemm_bias_act(src.view(-1, src.shape[-1]), self.W[k], self.W[n + k], act=self.acts[k],
+                                 out=dst.view(-1, dst.shape[-1]))
         else:
             w, b = self.W
             fc.conv_bias_act(self.X[j], w, b, act="relu", out=self.H)
@@ -276,6 +307,8 @@ def cpu_baseline(prob, seconds):
         t = time.perf_counter()
         if s["kind"] == "conv2":
             oracle.chain_conv2(d["x"][:imgs], d["w0"], d["b0"], oracle.ACT_RELU, d["w1"], d["b1"])
+        elif s["kind"] == "convN":
+            oracle.chain_convN(d["x"][:imgs], d["ws"], d["bs"], [actk[a] for a in s["acts"]])
         else:
             oracle.chain_conv_pool(d["x"][:imgs], d["w"], d["b"], oracle.ACT_RELU)
         return time.perf_counter() - t
@@ -308,7 +341,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="b2b_gemm_rf",
-                    choices=["b2b_gemm_tiny", "b2b_gemm_rf", "b2b_gemm_lds", "gemm3_rf", "conv3x3_conv1x1",
+                    choices=["b2b_gemm_tiny", "b2b_gemm_rf", "b2b_gemm_lds", "gemm3_rf", "conv3x3_conv1x1", "conv3x3_conv1x1x2",
                              "conv3x3_relu_maxpool"])
     ap.add_argument("--variant", choices=["rf", "lds", "stream"], default=None,
                     help="GEMM-chain kernel variant (default: rf, or lds for b2b_gemm_lds)")

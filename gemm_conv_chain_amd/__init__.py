@@ -19,8 +19,8 @@ import ctypes
 import os
 import re
 
-__all__ = ["lib", "FusedChainError", "chain_gemm2", "tune_chain_gemm2", "auto_variant", "tune_clear", "chain_gemmN", "chain_conv_pool", "chain_conv2", "gemm_bias_act",
-           "conv_bias_act", "maxpool2x2", "pad_channels", "pad_weight_channels", "abi_version", "ACT", "VARIANT",
+__all__ = ["lib", "FusedChainError", "chain_gemm2", "tune_chain_gemm2", "auto_variant", "tune_clear", "chain_gemmN", "chain_conv_pool", "chain_conv2", "chain_convN",
+           "gemm_bias_act", "conv_bias_act", "maxpool2x2", "pad_channels", "pad_weight_channels", "abi_version", "ACT", "VARIANT",
            "LIB_PATH", "HEADER_PATH", "exported_names"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -74,9 +74,11 @@ def lib():
         L.chain_gemm2_tune.argtypes = [_vp, _vp, _vp, ctypes.c_int, _vp, _vp, _vp, _i64, _i32, _i32, _i32, _i32,
                                        ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_float), _vp]
         L.chain_gemm2_auto_variant.argtypes = [_i64, _i32, _i32, _i32, ctypes.c_int, ctypes.POINTER(ctypes.c_int)]
+        L.chain_convN.argtypes = [_vp, ctypes.POINTER(ConvShape), _i32, ctypes.POINTER(_vp), ctypes.POINTER(_vp),
+                                  ctypes.POINTER(ctypes.c_int), ctypes.POINTER(_i32), _vp, _vp]
         L.fc_tune_clear.restype = None
         L.fc_tune_clear.argtypes = []
-        for name in ("chain_gemm2_tune", "chain_gemm2_auto_variant", "chain_gemm2", "chain_gemm2_variant", "chain_gemmN", "chain_conv_pool", "chain_conv2", "gemm_bias_act",
+        for name in ("chain_convN", "chain_gemm2_tune", "chain_gemm2_auto_variant", "chain_gemm2", "chain_gemm2_variant", "chain_gemmN", "chain_conv_pool", "chain_conv2", "gemm_bias_act",
                      "conv_bias_act", "maxpool2x2", "pad_channels"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
@@ -293,6 +295,34 @@ def chain_conv2(x, w0, b0, w1, b1, act="relu", out=None):
     _need(out, "out", 4)
     _check("chain_conv2", lib().chain_conv2(_ptr(x), _ptr(w0), _ptr(b0), _act(act), _ptr(w1), _ptr(b1), k1,
                                             _ptr(out), ctypes.byref(sh), _stream(x)))
+    return out
+
+
+def chain_convN(x, ws, bs, acts, out=None):
+    """y = stage_{n-1}(... stage_0(x)): stage 0 = act[0](conv3x3(x, ws[0]) + bs[0]),
+    stage i > 0 = act[i](1x1 conv with ws[i] [k_{i-1}, k_i] (or [1,1,k_{i-1},k_i]) + bs[i]);
+    n = 3 or 4, every intermediate rounded once to fp16 and kept on chip."""
+    n = len(ws)
+    if len(bs) != n or len(acts) != n:
+        raise ValueError("ws, bs and acts must have the same length")
+    _need(x, "x", 4)
+    _need(ws[0], "w0", 4)
+    for i in range(n):
+        _need(ws[i], "w%d" % i)
+        _need(bs[i], "b%d" % i, 1)
+    sh = _conv_shape(x, ws[0])
+    ks = [sh.k] + [int(w.shape[-1]) for w in ws[1:]]
+    for i in range(1, n):
+        if ws[i].numel() != ks[i - 1] * ks[i]:
+            raise ValueError("w%d must hold %d x %d values" % (i, ks[i - 1], ks[i]))
+    if out is None:
+        out = _torch().empty((sh.n, sh.h, sh.w, ks[-1]), dtype=x.dtype, device=x.device)
+    _need(out, "out", 4)
+    wp = (_vp * n)(*[w.data_ptr() for w in ws])
+    bp = (_vp * n)(*[None if b is None else b.data_ptr() for b in bs])
+    ap = (ctypes.c_int * n)(*[_act(a) for a in acts])
+    kp = (_i32 * n)(*ks)
+    _check("chain_convN", lib().chain_convN(_ptr(x), ctypes.byref(sh), n, wp, bp, ap, kp, _ptr(out), _stream(x)))
     return out
 
 

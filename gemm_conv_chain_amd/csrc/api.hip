@@ -19,6 +19,10 @@ hipError_t run_conv_pool3x3(const half_t* x, const half_t* w, const half_t* b, i
 hipError_t run_chain_conv2_3x3(const half_t* x, const half_t* w0, const half_t* b0, int act, const half_t* w1,
                                const half_t* b1, half_t* y, int NB, int H, int W, int C, int K0, int K1,
                                hipStream_t st);
+hipError_t run_chain_convN_3x3(const half_t* x, int nst, const half_t* const* w, const half_t* const* b,
+                               const int* act, const int* widths, half_t* y, int NB, int H, int W, int C,
+                               hipStream_t st);
+bool gemmn_fits(int nst, const int* widths);
 hipError_t run_maxpool2x2(const half_t* v, half_t* y, uint8_t* am, int NB, int P, int Q, int K, hipStream_t st);
 hipError_t run_pad_mid(const half_t* src, half_t* dst, long outer, int c_in, int c_out, int inner, hipStream_t st);
 bool convw_fits(int C, int K);
@@ -355,6 +359,44 @@ fc_status chain_conv2(const fc_half* x, const fc_half* w0, const fc_half* b0, fc
     return hip_status(fc::run_chain_conv2_3x3(H(x), H(w0), H(b0), act, H(w1), H(b1), Hm(y), shape0->n, shape0->h,
                                               shape0->w, shape0->c, shape0->k, k1, (hipStream_t)stream),
                       "chain_conv2");
+}
+
+fc_status chain_convN(const fc_half* x, const fc_conv_shape* shape0, int32_t nstages, const fc_half* const* w,
+                      const fc_half* const* b, const fc_act* act, const int32_t* k, fc_half* y, void* stream)
+{
+    if (!w || !act || !k) return fail(FC_E_NULL, "w, act and k are required");
+    if (nstages < 3 || nstages > 4)
+        return fail(FC_E_UNSUPPORTED, "nstages=%d: chain_convN runs 3 or 4 stages (chain_conv2 runs 2)", (int)nstages);
+    fc_status s = check_conv(shape0, 128);
+    if (s != FC_OK) return s;
+    if (k[0] != shape0->k) return fail(FC_E_SHAPE, "k[0]=%d must equal shape0->k=%d", (int)k[0], (int)shape0->k);
+    for (int i = 1; i < nstages; ++i)
+        if (k[i] <= 0 || k[i] % 8) return fail(FC_E_SHAPE, "k[%d]=%d must be a positive multiple of 8", i, (int)k[i]);
+    const long npix = (long)shape0->n * shape0->h * shape0->w;
+    if (npix > 0 && (!x || !y)) return fail(FC_E_NULL, "x and y are required");
+    if (!aligned16(x) || !aligned16(y)) return fail(FC_E_ALIGN, "tensor pointers must be 16-byte aligned");
+    const fc::half_t* wh[4];
+    const fc::half_t* bh[4];
+    int acts[4];
+    for (int i = 0; i < nstages; ++i) {
+        if (!w[i]) return fail(FC_E_NULL, "w[%d] is required", i);
+        const fc_half* bi = b ? b[i] : nullptr;
+        if (!aligned16(w[i]) || !aligned16(bi)) return fail(FC_E_ALIGN, "w[%d] and b[%d] must be 16-byte aligned", i, i);
+        s = check_act(act[i]);
+        if (s != FC_OK) return s;
+        wh[i] = H(w[i]);
+        bh[i] = H(bi);
+        acts[i] = (int)act[i];
+    }
+    int widths[5];
+    widths[0] = 9 * shape0->c;
+    for (int i = 0; i < nstages; ++i) widths[i + 1] = k[i];
+    if (!fc::gemmn_fits(nstages, widths))
+        return fail(FC_E_UNSUPPORTED, "register residence: every intermediate width <= 128 and all weights within LDS");
+    if (npix == 0) return ok();
+    return hip_status(fc::run_chain_convN_3x3(H(x), nstages, wh, bh, acts, widths, Hm(y), shape0->n, shape0->h,
+                                              shape0->w, shape0->c, (hipStream_t)stream),
+                      "chain_convN");
 }
 
 fc_status maxpool2x2(const fc_half* x, fc_half* y, uint8_t* argmax, int32_t n, int32_t h, int32_t w, int32_t c,

@@ -61,6 +61,11 @@ struct RfArgs {
     int Nin1, Nin1p;       // input width of the last GEMM, and its padded row count in LDS
 };
 
+// Fills the N-stage fields of RfArgs (host): widths[0] = K0 of the first
+// GEMM, widths[i + 1] = output width of GEMM i (i < nst).
+void gemmn_args(int nst, const half_t* const* W, const half_t* const* b, const int* act, const int* widths,
+                half_t* D, long M, RfArgs& a);
+
 // Per-wave output staging tile: 32 rows x 64 columns (+8 halves of padding).
 constexpr int RF_OLD = 64 + 8;
 constexpr size_t RF_OSTAGE_BYTES = (size_t)RF_WAVES * 32 * RF_OLD * 2;

@@ -703,6 +703,37 @@ hipError_t run_chain_conv2_3x3(const half_t* x, const half_t* w0, const half_t* 
     return launch_rf(ld, a, (K0 + 31) / 32, st);
 }
 
+// conv3x3 -> 1x1 (-> 1x1): the N-stage register-resident chain with the
+// implicit-GEMM loader; widths[0] = 9C (the first GEMM's k), widths[i + 1] =
+// output channels of stage i.  Compile-time chunk count only for C = 64.
+template <int NMID>
+static hipError_t launch_convN(const Conv3x3Rows& ld, const RfArgs& a, int nt0, hipStream_t st)
+{
+    const bool k9 = (a.K0p >> 6) == 9;
+    switch (nt0) {
+    case 1: return k9 ? launch_rf_k<1, 9, Conv3x3Rows, NMID>(ld, a, st) : launch_rf_k<1, 0, Conv3x3Rows, NMID>(ld, a, st);
+    case 2: return k9 ? launch_rf_k<2, 9, Conv3x3Rows, NMID>(ld, a, st) : launch_rf_k<2, 0, Conv3x3Rows, NMID>(ld, a, st);
+    case 3: return k9 ? launch_rf_k<3, 9, Conv3x3Rows, NMID>(ld, a, st) : launch_rf_k<3, 0, Conv3x3Rows, NMID>(ld, a, st);
+    case 4: return k9 ? launch_rf_k<4, 9, Conv3x3Rows, NMID>(ld, a, st) : launch_rf_k<4, 0, Conv3x3Rows, NMID>(ld, a, st);
+    }
+    return hipErrorInvalidValue;
+}
+
+hipError_t run_chain_convN_3x3(const half_t* x, int nst, const half_t* const* w, const half_t* const* b,
+                               const int* act, const int* widths, half_t* y, int NB, int H, int W, int C,
+                               hipStream_t st)
+{
+    const long M = (long)NB * H * W;
+    if (M == 0) return hipSuccess;
+    RfArgs a{};
+    gemmn_args(nst, w, b, act, widths, y, M, a);
+    Conv3x3Rows ld;
+    ld.x = x; ld.H = H; ld.W = W; ld.C = C; ld.M = M;
+    ld.set_divisors();
+    const int nt0 = (a.N0 + 31) / 32;
+    return nst == 3 ? launch_convN<1>(ld, a, nt0, st) : launch_convN<2>(ld, a, nt0, st);
+}
+
 // ------------------------------------------------------------ max pool 2x2/2
 // One thread: one output pixel x 8 channels (16-byte loads of the 4 inputs).
 __global__ __launch_bounds__(256) void k_maxpool2x2(const half_t* __restrict__ v, half_t* __restrict__ y,

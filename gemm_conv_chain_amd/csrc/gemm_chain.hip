@@ -449,7 +449,7 @@ hipError_t run_gemm_bias_act(const half_t* A, const half_t* W, const half_t* b, 
 
 // N-stage register-resident chain: widths[0] = K0, widths[i + 1] = output
 // width of GEMM i (i < nst); every width but K0 and the last <= 128.
-static void gemmn_args(int nst, const half_t* const* W, const half_t* const* b, const int* act, const int* widths,
+void gemmn_args(int nst, const half_t* const* W, const half_t* const* b, const int* act, const int* widths,
                        half_t* D, long M, RfArgs& a)
 {
     const int nmid = nst - 2;

@@ -81,6 +81,21 @@ def conv2_inputs(n, h, w, c, k0, k1, r=3, s=3, seed=0):
     return dict(x=x, w0=w0, b0=b0, w1=w1, b1=b1)
 
 
+def convN_inputs(n, h, w, c, ks, seed=0):
+    """x[n,h,w,c] ~ N(0,1); ws[0] HWIO [3,3,c,ks[0]] and bs[0] ~ N(0,1)/sqrt(9c);
+    ws[i] [ks[i-1], ks[i]] and bs[i] ~ N(0,1)/sqrt(ks[i-1]) (1x1 stages)."""
+    rng = np.random.default_rng(seed)
+    x = _draw(rng, "normal", (n, h, w, c), 1.0)
+    f0 = 1.0 / math.sqrt(9 * c)
+    ws = [_draw(rng, "normal", (3, 3, c, ks[0]), f0)]
+    bs = [_draw(rng, "normal", (ks[0],), f0)]
+    for i in range(1, len(ks)):
+        fi = 1.0 / math.sqrt(ks[i - 1])
+        ws.append(_draw(rng, "normal", (ks[i - 1], ks[i]), fi))
+        bs.append(_draw(rng, "normal", (ks[i],), fi))
+    return dict(x=x, ws=ws, bs=bs)
+
+
 def conv_pool_inputs(n, h, w, c, k, r=3, s=3, seed=0):
     """x[n,h,w,c] ~ U(-1,1); w HWIO [r,s,c,k] and b[k] ~ N(0,1)/sqrt(r*s*c)."""
     rng = np.random.default_rng(seed)
@@ -111,6 +126,9 @@ WORKLOADS = {
                      desc="three-GEMM register-resident chain A[65536x256] -> 64 (ReLU) -> 64 (ReLU) -> 128"),
     "conv3x3_conv1x1": dict(kind="conv2", n=32, h=56, w=56, c=64, k0=64, k1=256, act="relu",
                             desc="NHWC x[32,56,56,64] conv3x3 64->64 +b+ReLU -> conv1x1 64->256 +b"),
+    "conv3x3_conv1x1x2": dict(kind="convN", n=32, h=56, w=56, c=64, ks=[64, 64, 256], acts=["relu", "relu", "none"],
+                              desc="NHWC x[32,56,56,64] conv3x3 64->64 +b+ReLU -> conv1x1 64->64 +b+ReLU "
+                                   "-> conv1x1 64->256 +b"),
     "conv3x3_relu_maxpool": dict(kind="conv_pool", n=32, h=112, w=112, c=60, cpad=64, k=128, act="relu",
                                  desc="NHWC x[32,112,112,60->64] conv3x3 60->128 +b+ReLU -> maxpool2x2"),
 }
@@ -126,6 +144,8 @@ def workload(name, seed=0, **override):
         return spec, gemmN_inputs(spec["M"], spec["widths"], spec["dist"], seed)
     if spec["kind"] == "conv2":
         return spec, conv2_inputs(spec["n"], spec["h"], spec["w"], spec["c"], spec["k0"], spec["k1"], seed=seed)
+    if spec["kind"] == "convN":
+        return spec, convN_inputs(spec["n"], spec["h"], spec["w"], spec["c"], spec["ks"], seed=seed)
     if spec["kind"] == "conv_pool":
         return spec, conv_pool_inputs(spec["n"], spec["h"], spec["w"], spec["c"], spec["k"], seed=seed)
     raise ValueError(spec["kind"])

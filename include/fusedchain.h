@@ -196,6 +196,28 @@ fc_status chain_conv2(const fc_half *x, const fc_half *w0, const fc_half *b0, fc
                       const fc_half *w1, const fc_half *b1, int32_t k1, fc_half *y,
                       const fc_conv_shape *shape0, void *stream);
 
+/*
+ * chain_convN -- a 3x3 convolution followed by 1x1 convolutions in one
+ * kernel, every intermediate kept in registers (BOLT notes, "Persistent
+ * kernel (GEMM/Conv) fusion": several convolutions fused under the
+ * threadblock-residence rule; interview page, Conv item 5: a 1x1 conv is a
+ * GEMM over the pixels):
+ *   X_1     = act[0](conv3x3(x, w[0]) + b[0])      shape0: x [n,h,w,c], w[0] HWIO [3,3,c,k[0]]
+ *   X_{i+1} = act[i](X_i * w[i] + b[i])            1x1: w[i] [k[i-1] x k[i]] (= HWIO [1,1,k[i-1],k[i]])
+ *   y       = X_nstages                            [n, h, w, k[nstages-1]]
+ * for i = 1 .. nstages-1; each X_i with i < nstages rounded once to fp16.
+ * k (host array, nstages entries): output channels of every stage, k[0] ==
+ * shape0->k.  nstages is 3 or 4 (two stages: chain_conv2).  shape0 follows
+ * chain_conv_pool's rules (3x3, stride 1, pad 1, c % 32 == 0, k[0] <= 128);
+ * k[1 .. nstages-2] <= 128 and all weights must fit in LDS together, else
+ * FC_E_UNSUPPORTED.  b or b[i] may be NULL.  w, b, act and k are host
+ * arrays read during the call; the tensors are device pointers owned by the
+ * caller.  An empty batch is a no-op.
+ */
+fc_status chain_convN(const fc_half *x, const fc_conv_shape *shape0, int32_t nstages,
+                      const fc_half *const *w, const fc_half *const *b, const fc_act *act,
+                      const int32_t *k, fc_half *y, void *stream);
+
 /* ---- unfused single-operator kernels (the two-kernel baselines) ---- */
 
 /* C [M x N] = act(A [M x K] * W [K x N] + b [N]), fp16 out (GEMM + epilogue). */

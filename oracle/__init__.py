@@ -236,6 +236,25 @@ def chain_conv2(x, w0, b0, act_kind: int, w1, b1, stride: int = 1, pad: int = 1)
     return ref, Hb.view(np.float16)
 
 
+def chain_convN(x, ws, bs, acts, stride: int = 1, pad: int = 1):
+    """fp64 [n,P,Q,K_last] of a conv3x3 followed by 1x1 convs, each stage
+    act_i(stage_i(X_i) + b_i) with every intermediate rounded once to fp16
+    (BOLT notes, "Persistent kernel (GEMM/Conv) fusion": several convs fused
+    under the residence rule; interview page, Conv item 5: a 1x1 conv is a
+    GEMM over the pixels).  ws[0] is HWIO [R,S,C,K0]; ws[i > 0] is [K_{i-1},
+    K_i] or [1,1,K_{i-1},K_i].  Built from conv_bias_act, gemm_bias_act and
+    the fp16 codec; the last stage is returned unrounded."""
+    Y = conv_bias_act(x, ws[0], bs[0], acts[0], stride, pad)
+    n, P, Q, K = Y.shape
+    for i in range(1, len(ws)):
+        X = f64_to_f16(Y).reshape(n * P * Q, K)
+        w = np.asarray(ws[i]).reshape(K, -1)
+        Y = gemm_bias_act(X, w, bs[i], acts[i])
+        K = w.shape[1]
+        Y = Y.reshape(n, P, Q, K)
+    return Y
+
+
 def chain_conv_pool(x, w, b, act_kind: int = ACT_RELU, stride: int = 1, pad: int = 1, want_conv64=False):
     """(y fp16, argmax uint8, v fp16 conv output, conv64 fp64 or None)."""
     n, H_, Wd, C = x.shape

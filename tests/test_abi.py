@@ -25,7 +25,7 @@ def test_exports_every_declared_symbol(L):
     names = fc.exported_names()
     for n in ("chain_gemm2", "chain_gemm2_variant", "chain_gemmN", "chain_conv_pool", "chain_conv2", "gemm_bias_act",
               "conv_bias_act", "maxpool2x2", "pad_channels", "fc_abi_version", "fc_status_str", "fc_last_error",
-              "chain_gemm2_tune", "chain_gemm2_auto_variant", "fc_tune_clear"):
+              "chain_gemm2_tune", "chain_gemm2_auto_variant", "fc_tune_clear", "chain_convN"):
         assert n in names
     for n in names:
         assert hasattr(L, n), n
@@ -174,3 +174,25 @@ def test_auto_variant_rule(L):
     assert L.chain_gemm2_auto_variant(-1, 64, 64, 64, 1, ctypes.byref(v)) == E_SHAPE
     assert L.chain_gemm2_auto_variant(64, 64, 64, 64, 1, None) == E_NULL
     assert L.chain_gemm2_auto_variant(64, 64, 264, 64, 1, ctypes.byref(v)) == E_UNSUP
+
+
+def test_chain_convN_validation(L):
+    import ctypes as C
+    sh = fc.ConvShape(1, 8, 8, 64, 64, 3, 3, 1, 1)
+
+    def cn(n=3, k=(64, 64, 128), w=(P, P, P, P), acts=(1, 1, 0, 0), x=P, y=P2, shape=sh):
+        kp = (C.c_int32 * 4)(*(list(k) + [0] * (4 - len(k))))
+        wp = (C.c_void_p * 4)(*w)
+        ap = (C.c_int * 4)(*acts)
+        return L.chain_convN(x, C.byref(shape) if shape is not None else None, n, wp, None, ap, kp, y, None)
+    assert cn(n=2) == E_UNSUP                 # two stages: chain_conv2
+    assert cn(n=5) == E_UNSUP
+    assert cn(shape=None) == E_NULL
+    assert cn(k=(72, 64, 128)) == E_SHAPE     # k[0] must equal shape0.k
+    assert cn(k=(64, 60, 128)) == E_SHAPE     # not a multiple of 8
+    assert cn(w=(P, NUL, P, P)) == E_NULL
+    assert cn(x=NUL) == E_NULL
+    assert cn(y=BAD) == E_ALIGN
+    assert cn(acts=(1, 9, 0, 0)) == E_ARG
+    assert cn(k=(64, 136, 128)) == E_UNSUP    # intermediate wider than 128: not register-resident
+    assert cn(shape=fc.ConvShape(1, 8, 8, 48, 64, 3, 3, 1, 1)) == E_UNSUP   # c % 32

@@ -207,3 +207,41 @@ def test_conv2_full_size_sampled(fc):
     for img in (0, 17, 31):
         ref, _ = oracle.chain_conv2(d["x"][img:img + 1], d["w0"], d["b0"], oracle.ACT_RELU, d["w1"], d["b1"])
         assert_close(y[img:img + 1], ref, "full conv2 img %d" % img)
+
+
+@pytest.mark.parametrize("n,h,w,c,ks,acts", [
+    (2, 9, 11, 64, [64, 64, 128], ["relu", "relu", "none"]),            # compile-time chunks, ragged last tile
+    (1, 7, 13, 32, [96, 40, 64], ["relu", "gelu_tanh", "none"]),        # runtime chunks, odd widths
+    (2, 6, 10, 64, [32, 128, 64, 56], ["relu", "hardswish", "relu", "none"]),   # four stages
+    (1, 1, 3, 64, [64, 64, 64], ["none", "relu", "none"]),              # three pixels: one partial tile
+])
+def test_chain_convN(fc, n, h, w, c, ks, acts):
+    d = inputs.convN_inputs(n, h, w, c, ks, seed=n * h + w)
+    print("case convN", n, h, w, c, ks, acts, flush=True)
+    y = to_np(fc.chain_convN(dev(d["x"]), [dev(x) for x in d["ws"]], [dev(b) for b in d["bs"]], acts))
+    ref = oracle.chain_convN(d["x"], d["ws"], d["bs"], [ACTS[a] for a in acts])
+    assert_close(y, ref, "convN %s" % (ks,))
+
+
+def test_chain_convN_unscaled_zero_bias(fc):
+    # sensitivity: unit-variance weights, zero biases (a dropped k chunk or a
+    # wrong stage would not hide under the bias), many tiles
+    d = inputs.convN_inputs(2, 20, 22, 64, [64, 48, 96], seed=41)
+    ws = [(x.astype(np.float32) * 4).astype(np.float16) for x in d["ws"]]
+    bs = [np.zeros_like(b) for b in d["bs"]]
+    acts = ["relu", "relu", "none"]
+    print("case convN unscaled", flush=True)
+    y = to_np(fc.chain_convN(dev(d["x"]), [dev(x) for x in ws], [dev(b) for b in bs], acts))
+    ref = oracle.chain_convN(d["x"], ws, bs, [ACTS[a] for a in acts])
+    assert_close(y, ref, "convN unscaled")
+
+
+@pytest.mark.slow
+def test_convN_full_size_sampled(fc):
+    spec, d = inputs.workload("conv3x3_conv1x1x2")
+    print("case full conv3x3_conv1x1x2", flush=True)
+    y = to_np(fc.chain_convN(dev(d["x"]), [dev(x) for x in d["ws"]], [dev(b) for b in d["bs"]], spec["acts"]))
+    assert np.all(np.isfinite(y.astype(np.float64)))
+    for img in (0, 31):
+        ref = oracle.chain_convN(d["x"][img:img + 1], d["ws"], d["bs"], [ACTS[a] for a in spec["acts"]])
+        assert_close(y[img:img + 1], ref, "full convN img %d" % img)

@@ -375,3 +375,36 @@ def test_chain_gemmN_intermediates_rounded(orc):
         X = Y.astype(np.float16).astype(np.float64) if i < 2 else Y
     ref = orc.chain_gemmN(d["A"], d["Ws"], d["bs"], acts)
     assert np.max(np.abs(ref - X)) <= 1e-12 * max(1.0, np.max(np.abs(X)))
+
+
+def test_chain_convN_two_stages_is_chain_conv2(orc):
+    # the Python composition of single operators equals the C two-stage conv chain
+    d = inputs.conv2_inputs(2, 5, 7, 8, 16, 24, seed=13)
+    ref2, _ = orc.chain_conv2(d["x"], d["w0"], d["b0"], orc.ACT_RELU, d["w1"], d["b1"])
+    refn = orc.chain_convN(d["x"], [d["w0"], d["w1"]], [d["b0"], d["b1"]], [orc.ACT_RELU, orc.ACT_NONE])
+    assert np.array_equal(ref2, refn)
+
+
+def test_chain_convN_identity_stage(orc):
+    # an identity 1x1 stage (zero bias, no activation) reproduces its fp16 input
+    d = inputs.convN_inputs(1, 6, 5, 8, [16, 16, 24], seed=14)
+    eye = np.eye(16, dtype=np.float16)
+    zero = np.zeros(16, dtype=np.float16)
+    acts = [orc.ACT_RELU, orc.ACT_NONE, orc.ACT_NONE]
+    ref3 = orc.chain_convN(d["x"], [d["ws"][0], eye, d["ws"][2].reshape(16, 24)], [d["bs"][0], zero, d["bs"][2]],
+                           acts)
+    ref2, _ = orc.chain_conv2(d["x"], d["ws"][0], d["bs"][0], orc.ACT_RELU, d["ws"][2].reshape(16, 24), d["bs"][2])
+    assert np.array_equal(ref2, ref3)
+
+
+def test_chain_convN_stages_by_hand(orc):
+    # each 1x1 stage is a per-pixel matrix product of the fp16-rounded previous
+    # stage (numpy fp64 matmul and numpy's float16 cast)
+    d = inputs.convN_inputs(1, 4, 6, 8, [16, 8, 24], seed=15)
+    acts = [orc.ACT_RELU, orc.ACT_HARDSWISH, orc.ACT_NONE]
+    X = orc.conv_bias_act(d["x"], d["ws"][0], d["bs"][0], acts[0])
+    for i in (1, 2):
+        Xh = X.astype(np.float16).astype(np.float64)
+        X = orc.act(acts[i], Xh @ d["ws"][i].astype(np.float64) + d["bs"][i].astype(np.float64))
+    ref = orc.chain_convN(d["x"], d["ws"], d["bs"], acts)
+    assert np.max(np.abs(ref - X)) <= 1e-12 * max(1.0, np.max(np.abs(X)))
