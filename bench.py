@@ -60,6 +60,7 @@ class Problem:
 
         self.fc, self.torch, self.np = fc, torch, np
         self.name = name
+        self.bn = False
         self.traffic_key = name   # entry of the measured-traffic table
         self.spec, d = inputs.workload(name)
         self.host = d
@@ -152,18 +153,20 @@ class Problem:
             self.flops = 2 * npix * k * 9 * c               # algorithmic: the 60 real channels
             self.flops_exec = 2 * npix * k * 9 * cp         # executed: padded to 64
             npool = n * (h // 2) * (w // 2)
-            self.bytes_fused = 2 * (npix * cp + 9 * cp * k + k + npool * k)
+            self.bn = bool(s.get("bn"))
+            self.bytes_fused = 2 * (npix * cp + 9 * cp * k + k + npool * k) + (2 * k if self.bn else 0)
             self.bytes_interm = 2 * npix * k
             xp = fc.pad_channels(t(d["x"]), cp)             # input preparation, outside the timed chain
             wp = fc.pad_weight_channels(t(d["w"]), cp)
-            self.W = [wp, t(d["b"])]
+            self.W = [wp, t(d["scale"]), t(d["shift"])] if self.bn else [wp, t(d["b"])]
             per_set = 2 * (npix * cp + npool * k)
             self.nsets = max(1, math.ceil(COLD_BYTES / per_set)) if cold else 1
             self.X = [xp] + [xp.clone() for _ in range(self.nsets - 1)]
             self.Y = [torch.empty((n, h // 2, w // 2, k), dtype=torch.float16, device=dev) for _ in range(self.nsets)]
             self.H = torch.empty((n, h, w, k), dtype=torch.float16, device=dev)
             self.config = {"workload": name, "x": [n, h, w, c], "channels_padded_to": cp,
-                           "conv": "3x3 s1 p1 %d->%d +b ReLU" % (c, k), "pool": "max 2x2 s2"}
+                           "conv": "3x3 s1 p1 %d->%d %s ReLU" % (c, k, "x scale + shift" if self.bn else "+b"),
+                           "pool": "max 2x2 s2"}
             self.kernel = "k_conv_w"
         torch.cuda.synchronize()
 
@@ -181,6 +184,9 @@ class Problem:
         elif s["kind"] == "convN":
             n = len(self.acts)
             fc.chain_convN(self.X[j], self.W[:n], self.W[n:], self.acts, out=self.Y[j])
+        elif self.bn:
+            w, sc, sh = self.W
+            fc.chain_conv_bn_pool(self.X[j], w, sc, sh, act="relu", pool="max2x2", out=self.Y[j])
         else:
             w, b = self.W
             fc.chain_conv_pool(self.X[j], w, b, act="relu", pool="max2x2", out=self.Y[j])
@@ -212,6 +218,10 @@ class Problem:
                 dst = self.Hs[k] if k < n - 1 else self.Y[j]
                 fc.gemm_bias_act(src.view(-1, src.shape[-1]), self.W[k], self.W[n + k], act=self.acts[k],
                                  out=dst.view(-1, dst.shape[-1]))
+        elif self.bn:
+            w, sc, sh = self.W
+            fc.chain_conv_bn_pool(self.X[j], w, sc, sh, act="relu", pool="none", out=self.H)
+            fc.maxpool2x2(self.H, out=self.Y[j])
         else:
             w, b = self.W
             fc.conv_bias_act(self.X[j], w, b, act="relu", out=self.H)
@@ -309,6 +319,8 @@ def cpu_baseline(prob, seconds):
             oracle.chain_conv2(d["x"][:imgs], d["w0"], d["b0"], oracle.ACT_RELU, d["w1"], d["b1"])
         elif s["kind"] == "convN":
             oracle.chain_convN(d["x"][:imgs], d["ws"], d["bs"], [actk[a] for a in s["acts"]])
+        elif s.get("bn"):
+            oracle.chain_conv_bn_pool(d["x"][:imgs], d["w"], d["scale"], d["shift"], oracle.ACT_RELU)
         else:
             oracle.chain_conv_pool(d["x"][:imgs], d["w"], d["b"], oracle.ACT_RELU)
         return time.perf_counter() - t
@@ -342,7 +354,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="b2b_gemm_rf",
                     choices=["b2b_gemm_tiny", "b2b_gemm_rf", "b2b_gemm_lds", "gemm3_rf", "conv3x3_conv1x1", "conv3x3_conv1x1x2",
-                             "conv3x3_relu_maxpool"])
+                             "conv3x3_relu_maxpool", "conv3x3_bn_relu_maxpool"])
     ap.add_argument("--variant", choices=["rf", "lds", "stream"], default=None,
                     help="GEMM-chain kernel variant (default: rf, or lds for b2b_gemm_lds)")
     ap.add_argument("--warm", action="store_true", help="reuse one buffer set (cache-warm timing)")

@@ -19,7 +19,7 @@ import ctypes
 import os
 import re
 
-__all__ = ["lib", "FusedChainError", "chain_gemm2", "tune_chain_gemm2", "auto_variant", "tune_clear", "chain_gemmN", "chain_conv_pool", "chain_conv2", "chain_convN",
+__all__ = ["lib", "FusedChainError", "chain_gemm2", "tune_chain_gemm2", "auto_variant", "tune_clear", "chain_gemmN", "chain_conv_pool", "chain_conv_bn_pool", "chain_conv2", "chain_convN",
            "gemm_bias_act", "conv_bias_act", "maxpool2x2", "pad_channels", "pad_weight_channels", "abi_version", "ACT", "VARIANT",
            "LIB_PATH", "HEADER_PATH", "exported_names"]
 
@@ -76,9 +76,11 @@ def lib():
         L.chain_gemm2_auto_variant.argtypes = [_i64, _i32, _i32, _i32, ctypes.c_int, ctypes.POINTER(ctypes.c_int)]
         L.chain_convN.argtypes = [_vp, ctypes.POINTER(ConvShape), _i32, ctypes.POINTER(_vp), ctypes.POINTER(_vp),
                                   ctypes.POINTER(ctypes.c_int), ctypes.POINTER(_i32), _vp, _vp]
+        L.chain_conv_bn_pool.argtypes = [_vp, _vp, _vp, _vp, ctypes.c_int, ctypes.c_int, _vp,
+                                         ctypes.POINTER(ConvShape), _vp, _vp]
         L.fc_tune_clear.restype = None
         L.fc_tune_clear.argtypes = []
-        for name in ("chain_convN", "chain_gemm2_tune", "chain_gemm2_auto_variant", "chain_gemm2", "chain_gemm2_variant", "chain_gemmN", "chain_conv_pool", "chain_conv2", "gemm_bias_act",
+        for name in ("chain_conv_bn_pool", "chain_convN", "chain_gemm2_tune", "chain_gemm2_auto_variant", "chain_gemm2", "chain_gemm2_variant", "chain_gemmN", "chain_conv_pool", "chain_conv2", "gemm_bias_act",
                      "conv_bias_act", "maxpool2x2", "pad_channels"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
@@ -248,6 +250,19 @@ def _conv_shape(x, w, stride=1, pad=1):
 def chain_conv_pool(x, w, b, act="relu", pool="max2x2", out=None, argmax=None):
     """y = maxpool2x2(act(conv3x3(x, w) + b)) (or act(conv+b) with pool='none').
     ``argmax``: None, True (allocate) or a uint8 tensor; returns y or (y, argmax)."""
+    return _conv_pool("chain_conv_pool", x, w, None, b, act, pool, out, argmax)
+
+
+def chain_conv_bn_pool(x, w, scale, shift, act="relu", pool="max2x2", out=None, argmax=None):
+    """y = maxpool2x2(act(conv3x3(x, w) * scale + shift)) per output channel (batch
+    norm at inference as a scale and a shift); pool='none' stores act(...)."""
+    _need(scale, "scale", 1)
+    if scale is None:
+        raise ValueError("scale is required")
+    return _conv_pool("chain_conv_bn_pool", x, w, scale, shift, act, pool, out, argmax)
+
+
+def _conv_pool(fn, x, w, scale, b, act, pool, out, argmax):
     torch = _torch()
     for t, n, d in ((x, "x", 4), (w, "w", 4), (b, "b", 1)):
         _need(t, n, d)
@@ -263,8 +278,14 @@ def chain_conv_pool(x, w, b, act="relu", pool="max2x2", out=None, argmax=None):
         am = torch.empty(oshape, dtype=torch.uint8, device=x.device)
     elif argmax is not None and argmax is not False:
         am = argmax
-    _check("chain_conv_pool", lib().chain_conv_pool(_ptr(x), _ptr(w), _ptr(b), _act(act), p, _ptr(out),
-                                                    ctypes.byref(sh), _ptr(am), _stream(x)))
+    L = lib()
+    if scale is None:
+        st = L.chain_conv_pool(_ptr(x), _ptr(w), _ptr(b), _act(act), p, _ptr(out), ctypes.byref(sh), _ptr(am),
+                               _stream(x))
+    else:
+        st = L.chain_conv_bn_pool(_ptr(x), _ptr(w), _ptr(scale), _ptr(b), _act(act), p, _ptr(out), ctypes.byref(sh),
+                                  _ptr(am), _stream(x))
+    _check(fn, st)
     return (out, am) if am is not None else out
 
 

@@ -12,10 +12,10 @@
 #include "fc_launch.h"
 
 namespace fc {
-hipError_t run_conv_bias_act3x3(const half_t* x, const half_t* w, const half_t* b, int act, half_t* y, int NB,
-                                int H, int W, int C, int K, hipStream_t st);
-hipError_t run_conv_pool3x3(const half_t* x, const half_t* w, const half_t* b, int act, half_t* y,
-                            uint8_t* argmax, int NB, int H, int W, int C, int K, hipStream_t st);
+hipError_t run_conv_bias_act3x3(const half_t* x, const half_t* w, const half_t* scale, const half_t* b, int act,
+                                half_t* y, int NB, int H, int W, int C, int K, hipStream_t st);
+hipError_t run_conv_pool3x3(const half_t* x, const half_t* w, const half_t* scale, const half_t* b, int act,
+                            half_t* y, uint8_t* argmax, int NB, int H, int W, int C, int K, hipStream_t st);
 hipError_t run_chain_conv2_3x3(const half_t* x, const half_t* w0, const half_t* b0, int act, const half_t* w1,
                                const half_t* b1, half_t* y, int NB, int H, int W, int C, int K0, int K1,
                                hipStream_t st);
@@ -309,8 +309,10 @@ fc_status gemm_bias_act(const fc_half* A, const fc_half* W, const fc_half* b, fc
                       "gemm_bias_act");
 }
 
-fc_status chain_conv_pool(const fc_half* x, const fc_half* w, const fc_half* b, fc_act act, fc_pool pool,
-                          fc_half* y, const fc_conv_shape* shape, uint8_t* argmax, void* stream)
+// conv3x3 -> (x scale) + b -> act -> optional 2x2 max pool (scale may be NULL).
+static fc_status conv_pool_impl(const char* name, const fc_half* x, const fc_half* w, const fc_half* scale,
+                                const fc_half* b, fc_act act, fc_pool pool, fc_half* y, const fc_conv_shape* shape,
+                                uint8_t* argmax, void* stream)
 {
     fc_status s = check_act(act);
     if (s != FC_OK) return s;
@@ -321,18 +323,33 @@ fc_status chain_conv_pool(const fc_half* x, const fc_half* w, const fc_half* b, 
     const long npix = (long)shape->n * shape->h * shape->w;
     const long nout = pool == FC_POOL_NONE ? npix : (long)shape->n * (shape->h / 2) * (shape->w / 2);
     if (!w || (npix > 0 && !x) || (nout > 0 && !y)) return fail(FC_E_NULL, "x, w and y are required");
-    if (!aligned16(x) || !aligned16(w) || !aligned16(y) || !aligned16(b))
+    if (!aligned16(x) || !aligned16(w) || !aligned16(y) || !aligned16(b) || !aligned16(scale))
         return fail(FC_E_ALIGN, "tensor pointers must be 16-byte aligned");
     if (nout == 0) return ok();
     if (!fc::convw_fits(shape->c, shape->k)) return fail(FC_E_UNSUPPORTED, "weights exceed LDS");
     hipStream_t st = (hipStream_t)stream;
     if (pool == FC_POOL_NONE)
-        return hip_status(fc::run_conv_bias_act3x3(H(x), H(w), H(b), act, Hm(y), shape->n, shape->h, shape->w,
-                                                    shape->c, shape->k, st),
-                          "conv_bias_act");
-    return hip_status(fc::run_conv_pool3x3(H(x), H(w), H(b), act, Hm(y), argmax, shape->n, shape->h, shape->w,
-                                           shape->c, shape->k, st),
-                      "chain_conv_pool");
+        return hip_status(fc::run_conv_bias_act3x3(H(x), H(w), H(scale), H(b), act, Hm(y), shape->n, shape->h,
+                                                    shape->w, shape->c, shape->k, st),
+                          name);
+    return hip_status(fc::run_conv_pool3x3(H(x), H(w), H(scale), H(b), act, Hm(y), argmax, shape->n, shape->h,
+                                           shape->w, shape->c, shape->k, st),
+                      name);
+}
+
+fc_status chain_conv_pool(const fc_half* x, const fc_half* w, const fc_half* b, fc_act act, fc_pool pool,
+                          fc_half* y, const fc_conv_shape* shape, uint8_t* argmax, void* stream)
+{
+    return conv_pool_impl(pool == FC_POOL_NONE ? "conv_bias_act" : "chain_conv_pool", x, w, nullptr, b, act, pool, y,
+                          shape, argmax, stream);
+}
+
+fc_status chain_conv_bn_pool(const fc_half* x, const fc_half* w, const fc_half* scale, const fc_half* shift,
+                             fc_act act, fc_pool pool, fc_half* y, const fc_conv_shape* shape, uint8_t* argmax,
+                             void* stream)
+{
+    if (!scale) return fail(FC_E_NULL, "scale is required (use chain_conv_pool for a plain bias)");
+    return conv_pool_impl("chain_conv_bn_pool", x, w, scale, shift, act, pool, y, shape, argmax, stream);
 }
 
 fc_status conv_bias_act(const fc_half* x, const fc_half* w, const fc_half* b, fc_act act, fc_half* y,

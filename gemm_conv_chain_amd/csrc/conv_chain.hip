@@ -146,6 +146,7 @@ struct ConvWArgs {
     const half_t* x;   // [NB, H, W, C]
     const half_t* w;   // HWIO [3, 3, C, K]
     const half_t* b;   // [K] or null
+    const half_t* s;   // [K] per-channel scale applied before b (batch-norm at inference), or null = 1
     half_t* y;         // STORE: [NB, H, W, K];  POOL: [NB, H/2, W/2, K]
     uint8_t* argmax;   // POOL only, nullable: [NB, H/2, W/2, K]
     int NB, H, W, C, K;
@@ -159,12 +160,12 @@ struct ConvWArgs {
     FastDiv fa, fb, fc16;
 };
 
-// LDS: weights [Kp][KP] (natural, swizzled or padded), biases, the tile
-// counter, then a 1 KiB output staging area per wave.
+// LDS: weights [Kp][KP] (natural, swizzled or padded), biases, scales, the
+// tile counter, then a 1 KiB output staging area per wave.
 constexpr int CW_OSTAGE = 1024;
 inline size_t convw_lds_bytes(int KP, int Kp)
 {
-    return (size_t)Kp * wtile_ld(KP) * 2 + (size_t)KP * 4 + 16 + (size_t)8 * CW_OSTAGE;
+    return (size_t)Kp * wtile_ld(KP) * 2 + (size_t)KP * 8 + 16 + (size_t)8 * CW_OSTAGE;
 }
 
 // One wave = 64 GEMM rows (two 32-row MFMA tiles) x all K output channels.
@@ -192,7 +193,8 @@ void k_conv_w(ConvWArgs a)
     Wn.ld = wtile_ld(KP);
     Wn.swz = wtile_swz(KP);
     lds_float* bs = (lds_float*)(Wn.p + a.Kp * Wn.ld);
-    FC_LDS int* next_tile = (FC_LDS int*)(bs + KP);
+    lds_float* ss = bs + KP;
+    FC_LDS int* next_tile = (FC_LDS int*)(ss + KP);
     static_assert(convw_threads(KCH) <= 512, "eight staging areas");
 
     const int tid = threadIdx.x;
@@ -331,7 +333,10 @@ void k_conv_w(ConvWArgs a)
     }
 
     stage_natural<8>(a.w, a.Kr, a.K, a.K, a.Kp, KP, Wn, tid, NTHR);
-    for (int i = tid; i < KP; i += NTHR) bs[i] = (a.b && i < a.K) ? (float)a.b[i] : 0.0f;
+    for (int i = tid; i < KP; i += NTHR) {
+        bs[i] = (a.b && i < a.K) ? (float)a.b[i] : 0.0f;
+        ss[i] = (a.s && i < a.K) ? (float)a.s[i] : 1.0f;
+    }
     if (tid == 0) *next_tile = (int)(t_begin + NWAVES);
     __syncthreads();
 
@@ -357,6 +362,7 @@ void k_conv_w(ConvWArgs a)
         // per-lane bases; every (u, g, e, t) adds a constant (LDS instruction offsets)
         lds_half* const ow = ost + hh * 32 + lr;
         const lds_float* const bsl = bs + lr;
+        const lds_float* const ssl = ss + lr;
         const lds_half8* const orb = reinterpret_cast<const lds_half8*>(ost + rr * 32 + 8 * grp);
         act_dispatch(a.act, [&](auto act) {
             if (EPI == EPI_POOL) {
@@ -368,21 +374,29 @@ void k_conv_w(ConvWArgs a)
                 // pv[t][u][g]: pooled value of window 8u + 2g + hh, channel 32t + lr
                 half_t pv[NTK][2][4];
                 if (decltype(act)::monotone && !ab) {
-                    // Bias addition (fp32 rounding), a non-decreasing activation and
-                    // the fp16 rounding are all monotone, so the max of the four
-                    // rounded values is the rounded value of the largest
-                    // accumulator: pool first, then one bias/act/convert per window.
+                    // v = fp16(act(fma(acc, s, b))): the fused multiply-add (one
+                    // rounding), a non-decreasing activation and the fp16 rounding
+                    // are monotone in acc -- non-decreasing for s >= 0,
+                    // non-increasing for s < 0 -- so the max of the four rounded
+                    // values is v of the largest (s >= 0) or smallest (s < 0)
+                    // accumulator: pool first, then one scale/bias/act/convert per
+                    // window.  (With no scale s = 1 and fma(acc, 1, b) = acc + b.)
 #pragma unroll
                     for (int t = 0; t < NTK; ++t) {
                         const float bk = bsl[32 * t];
+                        const float sk = ssl[32 * t];
+                        const bool up = sk >= 0.0f;
 #pragma unroll
                         for (int u = 0; u < 2; ++u)
 #pragma unroll
                             for (int g = 0; g < 4; ++g) {
-                                const float m = __builtin_fmaxf(
+                                const float hi = __builtin_fmaxf(
                                     __builtin_fmaxf(acc[u][t][4 * g], acc[u][t][4 * g + 1]),
                                     __builtin_fmaxf(acc[u][t][4 * g + 2], acc[u][t][4 * g + 3]));
-                                pv[t][u][g] = (half_t)act.f(m + bk);
+                                const float lo = __builtin_fminf(
+                                    __builtin_fminf(acc[u][t][4 * g], acc[u][t][4 * g + 1]),
+                                    __builtin_fminf(acc[u][t][4 * g + 2], acc[u][t][4 * g + 3]));
+                                pv[t][u][g] = (half_t)act.f(__builtin_fmaf(up ? hi : lo, sk, bk));
                             }
                     }
                 } else {
@@ -397,16 +411,17 @@ void k_conv_w(ConvWArgs a)
 #pragma unroll
                     for (int t = 0; t < NTK; ++t) {
                         const float bk = bsl[32 * t];
+                        const float sk = ssl[32 * t];
                         const bool kok = lr < K - 32 * t;
 #pragma unroll
                         for (int u = 0; u < 2; ++u) {
 #pragma unroll
                             for (int g = 0; g < 4; ++g) {
-                                half_t best = (half_t)act.f(acc[u][t][4 * g] + bk);
+                                half_t best = (half_t)act.f(__builtin_fmaf(acc[u][t][4 * g], sk, bk));
                                 int bi = 0;
 #pragma unroll
                                 for (int e = 1; e < 4; ++e) {
-                                    const half_t v = (half_t)act.f(acc[u][t][4 * g + e] + bk);
+                                    const half_t v = (half_t)act.f(__builtin_fmaf(acc[u][t][4 * g + e], sk, bk));
                                     const bool gt = v > best;
                                     best = gt ? v : best;
                                     bi = gt ? e : bi;
@@ -449,6 +464,7 @@ void k_conv_w(ConvWArgs a)
 #pragma unroll
                 for (int t = 0; t < NTK; ++t) {
                     const float bk = bsl[32 * t];
+                    const float sk = ssl[32 * t];
 #pragma unroll
                     for (int u = 0; u < 2; ++u) {
 #pragma unroll
@@ -458,7 +474,8 @@ void k_conv_w(ConvWArgs a)
                             for (int g = 0; g < 4; ++g)
 #pragma unroll
                                 for (int e = 2 * eh; e < 2 * eh + 2; ++e)
-                                    ow[((e & 1) * 8 + 2 * g) * 32] = (half_t)act.f(acc[u][t][4 * g + e] + bk);
+                                    ow[((e & 1) * 8 + 2 * g) * 32] =
+                                        (half_t)act.f(__builtin_fmaf(acc[u][t][4 * g + e], sk, bk));
                             wave_lds_sync();
                             // staged row rr -> tile row
                             const int e = 2 * eh + (rr >> 3), g = (rr & 7) >> 1, h1 = rr & 1;
@@ -651,11 +668,11 @@ bool convw_fits(int C, int K)
     return K <= 128 && convw_lds_bytes((K + 31) / 32 * 32, Kp) <= RF_LDS_LIMIT;
 }
 
-hipError_t run_conv_bias_act3x3(const half_t* x, const half_t* w, const half_t* b, int act, half_t* y, int NB,
-                                int H, int W, int C, int K, hipStream_t st)
+hipError_t run_conv_bias_act3x3(const half_t* x, const half_t* w, const half_t* scale, const half_t* b, int act,
+                                half_t* y, int NB, int H, int W, int C, int K, hipStream_t st)
 {
     ConvWArgs a;
-    a.x = x; a.w = w; a.b = b; a.y = y; a.argmax = nullptr;
+    a.x = x; a.w = w; a.s = scale; a.b = b; a.y = y; a.argmax = nullptr;
     a.NB = NB; a.H = H; a.W = W; a.C = C; a.K = K;
     a.Kr = 9 * C; a.Kp = (9 * C + 63) / 64 * 64; a.act = act;
     const long rows = (long)NB * H * W;
@@ -667,11 +684,11 @@ hipError_t run_conv_bias_act3x3(const half_t* x, const half_t* w, const half_t* 
     return launch_convw<EPI_STORE>(a, st);
 }
 
-hipError_t run_conv_pool3x3(const half_t* x, const half_t* w, const half_t* b, int act, half_t* y,
-                            uint8_t* argmax, int NB, int H, int W, int C, int K, hipStream_t st)
+hipError_t run_conv_pool3x3(const half_t* x, const half_t* w, const half_t* scale, const half_t* b, int act,
+                            half_t* y, uint8_t* argmax, int NB, int H, int W, int C, int K, hipStream_t st)
 {
     ConvWArgs a;
-    a.x = x; a.w = w; a.b = b; a.y = y; a.argmax = argmax;
+    a.x = x; a.w = w; a.s = scale; a.b = b; a.y = y; a.argmax = argmax;
     a.NB = NB; a.H = H; a.W = W; a.C = C; a.K = K;
     a.Kr = 9 * C; a.Kp = (9 * C + 63) / 64 * 64; a.act = act;
     const long rows = (long)NB * (H / 2) * (W / 2) * 4;

@@ -106,6 +106,19 @@ def conv_pool_inputs(n, h, w, c, k, r=3, s=3, seed=0):
     return dict(x=x, w=wt, b=b)
 
 
+def conv_bn_pool_inputs(n, h, w, c, k, seed=0):
+    """conv_pool_inputs plus a batch-norm scale and shift per output channel:
+    scale ~ U(0.5, 1.5) with every fourth channel negated (so both signs
+    occur), shift ~ N(0,1)/sqrt(9c) (like the bias)."""
+    d = conv_pool_inputs(n, h, w, c, k, seed=seed)
+    rng = np.random.default_rng(seed + 1000003)
+    sc = rng.uniform(0.5, 1.5, k)
+    sc[::4] *= -1.0
+    d["scale"] = sc.astype(np.float16)
+    d["shift"] = d.pop("b")
+    return d
+
+
 def pad_last_dim_np(a, axis, to):
     """Zero-pad ``axis`` of an fp16 array up to ``to`` entries (a bit copy)."""
     pad = [(0, 0)] * a.ndim
@@ -129,6 +142,9 @@ WORKLOADS = {
     "conv3x3_conv1x1x2": dict(kind="convN", n=32, h=56, w=56, c=64, ks=[64, 64, 256], acts=["relu", "relu", "none"],
                               desc="NHWC x[32,56,56,64] conv3x3 64->64 +b+ReLU -> conv1x1 64->64 +b+ReLU "
                                    "-> conv1x1 64->256 +b"),
+    "conv3x3_bn_relu_maxpool": dict(kind="conv_pool", bn=True, n=32, h=112, w=112, c=60, cpad=64, k=128, act="relu",
+                                    desc="NHWC x[32,112,112,60->64] conv3x3 60->128 x scale + shift (batch norm) "
+                                         "+ReLU -> maxpool2x2"),
     "conv3x3_relu_maxpool": dict(kind="conv_pool", n=32, h=112, w=112, c=60, cpad=64, k=128, act="relu",
                                  desc="NHWC x[32,112,112,60->64] conv3x3 60->128 +b+ReLU -> maxpool2x2"),
 }
@@ -146,6 +162,8 @@ def workload(name, seed=0, **override):
         return spec, conv2_inputs(spec["n"], spec["h"], spec["w"], spec["c"], spec["k0"], spec["k1"], seed=seed)
     if spec["kind"] == "convN":
         return spec, convN_inputs(spec["n"], spec["h"], spec["w"], spec["c"], spec["ks"], seed=seed)
+    if spec["kind"] == "conv_pool" and spec.get("bn"):
+        return spec, conv_bn_pool_inputs(spec["n"], spec["h"], spec["w"], spec["c"], spec["k"], seed=seed)
     if spec["kind"] == "conv_pool":
         return spec, conv_pool_inputs(spec["n"], spec["h"], spec["w"], spec["c"], spec["k"], seed=seed)
     raise ValueError(spec["kind"])

@@ -184,6 +184,22 @@ fc_status chain_conv_pool(const fc_half *x, const fc_half *w, const fc_half *b, 
                           fc_half *y, const fc_conv_shape *shape, uint8_t *argmax, void *stream);
 
 /*
+ * chain_conv_bn_pool -- chain_conv_pool with a per-channel scale before the
+ * shift: the inference form of batch normalisation, which the interview
+ * page's inference simplification replaces by a scale and a bias
+ * (scale = gamma / sqrt(var + eps), shift = beta - mean * scale, computed by
+ * the caller), fused into the conv epilogue (BOLT notes, "Prerequisite:
+ * Epilogue fusion": broadcast vectors in the epilogue):
+ *   v[n,p,q,k] = act(conv3x3(x, w)[n,p,q,k] * scale[k] + shift[k])   (one fp32 fma)
+ *   y = maxpool2x2(fp16(v)) (FC_POOL_MAX_2X2_S2), or fp16(v) (FC_POOL_NONE).
+ * scale [k] is required (any sign); shift may be NULL.  Everything else --
+ * shapes, argmax, alignment, errors -- as chain_conv_pool.
+ */
+fc_status chain_conv_bn_pool(const fc_half *x, const fc_half *w, const fc_half *scale, const fc_half *shift,
+                             fc_act act, fc_pool pool, fc_half *y, const fc_conv_shape *shape,
+                             uint8_t *argmax, void *stream);
+
+/*
  * chain_conv2 -- y = conv1x1(act(conv(x, w0) + b0), w1) + b1, the first conv's
  * output kept in VGPRs (BOLT persistent conv fusion; a 1x1 conv is a GEMM,
  * interview page, conv item 5).

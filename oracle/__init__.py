@@ -255,6 +255,29 @@ def chain_convN(x, ws, bs, acts, stride: int = 1, pad: int = 1):
     return Y
 
 
+def conv_bn_act(x, w, scale, shift, act_kind: int, stride: int = 1, pad: int = 1) -> np.ndarray:
+    """fp64 act(conv(x, w) * scale[k] + shift[k]): batch normalisation at
+    inference written as a per-channel scale and shift (interview page, the
+    inference simplification that replaces BN by a scale and a bias), applied
+    to the bias-free convolution.  Built from conv_bias_act (zero bias, no
+    activation) and act()."""
+    K = w.shape[-1]
+    s = conv_bias_act(x, w, np.zeros(K, dtype=np.float16), ACT_NONE, stride, pad)
+    t = s * np.asarray(scale, dtype=np.float16).astype(np.float64) + np.asarray(shift, dtype=np.float16).astype(np.float64)
+    return act(act_kind, t)
+
+
+def chain_conv_bn_pool(x, w, scale, shift, act_kind: int = ACT_RELU, want_conv64=False):
+    """(y fp16, argmax uint8, v fp16, conv64 fp64 or None) of
+    maxpool2x2(fp16(conv_bn_act(...))) -- the Welder Conv+ReLU+MaxPool chain
+    with a batch-norm epilogue; built from conv_bn_act, the fp16 codec and
+    maxpool2x2."""
+    c64 = conv_bn_act(x, w, scale, shift, act_kind)
+    v = f64_to_f16(c64)
+    y, am = maxpool2x2(v)
+    return y, am, v, (c64 if want_conv64 else None)
+
+
 def chain_conv_pool(x, w, b, act_kind: int = ACT_RELU, stride: int = 1, pad: int = 1, want_conv64=False):
     """(y fp16, argmax uint8, v fp16 conv output, conv64 fp64 or None)."""
     n, H_, Wd, C = x.shape

@@ -25,7 +25,7 @@ def test_exports_every_declared_symbol(L):
     names = fc.exported_names()
     for n in ("chain_gemm2", "chain_gemm2_variant", "chain_gemmN", "chain_conv_pool", "chain_conv2", "gemm_bias_act",
               "conv_bias_act", "maxpool2x2", "pad_channels", "fc_abi_version", "fc_status_str", "fc_last_error",
-              "chain_gemm2_tune", "chain_gemm2_auto_variant", "fc_tune_clear", "chain_convN"):
+              "chain_gemm2_tune", "chain_gemm2_auto_variant", "fc_tune_clear", "chain_convN", "chain_conv_bn_pool"):
         assert n in names
     for n in names:
         assert hasattr(L, n), n
@@ -196,3 +196,19 @@ def test_chain_convN_validation(L):
     assert cn(acts=(1, 9, 0, 0)) == E_ARG
     assert cn(k=(64, 136, 128)) == E_UNSUP    # intermediate wider than 128: not register-resident
     assert cn(shape=fc.ConvShape(1, 8, 8, 48, 64, 3, 3, 1, 1)) == E_UNSUP   # c % 32
+
+
+def test_chain_conv_bn_pool_validation(L):
+    import ctypes as C
+    sh = fc.ConvShape(1, 8, 8, 64, 64, 3, 3, 1, 1)
+
+    def bn(x=P, w=P, scale=P, shift=NUL, act=1, pool=1, y=P2, am=NUL, shape=sh):
+        return L.chain_conv_bn_pool(x, w, scale, shift, act, pool, y, C.byref(shape), am, None)
+    assert bn(scale=NUL) == E_NULL            # the scale is what this entry adds
+    assert bn(scale=BAD) == E_ALIGN
+    assert bn(shift=BAD) == E_ALIGN
+    assert bn(w=NUL) == E_NULL
+    assert bn(act=5) == E_ARG
+    assert bn(pool=2) == E_ARG
+    assert bn(pool=0, am=P) == E_ARG           # argmax needs a pool
+    assert bn(shape=fc.ConvShape(1, 8, 8, 64, 136, 3, 3, 1, 1)) == E_UNSUP

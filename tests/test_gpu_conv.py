@@ -245,3 +245,72 @@ def test_convN_full_size_sampled(fc):
     for img in (0, 31):
         ref = oracle.chain_convN(d["x"][img:img + 1], d["ws"], d["bs"], [ACTS[a] for a in spec["acts"]])
         assert_close(y[img:img + 1], ref, "full convN img %d" % img)
+
+
+def check_bn_pool(y, am, d, act, what):
+    yo, amo, _, c64 = oracle.chain_conv_bn_pool(d["x"], d["w"], d["scale"], d["shift"], ACTS[act], want_conv64=True)
+    assert_close(y, yo.astype(np.float64), what)
+    ties = pool_tie_mask(c64, c64.shape[1], c64.shape[2])
+    free = ~ties
+    assert np.array_equal(am[free], amo[free]), "%s: argmax differs on %d tie-free windows" % (
+        what, int(np.sum(am[free] != amo[free])))
+    return int(np.sum(free))
+
+
+@pytest.mark.parametrize("n,h,w,c,k,act", [(2, 8, 10, 64, 128, "relu"), (1, 9, 7, 32, 64, "relu"),
+                                           (2, 6, 14, 64, 96, "none"), (1, 10, 6, 64, 128, "gelu_tanh")])
+def test_conv_bn_pool(fc, n, h, w, c, k, act):
+    # batch-norm epilogue with both signs of scale; without argmax (ReLU/none)
+    # the kernel pools max or min of the accumulators by the sign of the scale
+    d = inputs.conv_bn_pool_inputs(n, h, w, c, k, seed=n + h * w)
+    x, wt, sc, sh = dev(d["x"]), dev(d["w"]), dev(d["scale"]), dev(d["shift"])
+    print("case conv_bn_pool", n, h, w, c, k, act, flush=True)
+    y, am = fc.chain_conv_bn_pool(x, wt, sc, sh, act=act, argmax=True)
+    y2 = fc.chain_conv_bn_pool(x, wt, sc, sh, act=act)
+    torch.cuda.synchronize()
+    y, am, y2 = to_np(y), to_np(am), to_np(y2)
+    assert np.array_equal(y.view(np.uint16), y2.view(np.uint16)), "y with and without argmax differ"
+    assert check_bn_pool(y, am, d, act, "conv_bn_pool") > 0
+
+
+def test_conv_bn_no_pool(fc):
+    # pool = none: conv + batch norm + act stored (many tiles, ragged)
+    d = inputs.conv_bn_pool_inputs(2, 17, 23, 64, 128, seed=5)
+    print("case conv_bn no pool", flush=True)
+    y = to_np(fc.chain_conv_bn_pool(dev(d["x"]), dev(d["w"]), dev(d["scale"]), dev(d["shift"]), act="relu",
+                                    pool="none"))
+    ref = oracle.conv_bn_act(d["x"], d["w"], d["scale"], d["shift"], oracle.ACT_RELU)
+    assert_close(y, ref, "conv_bn no pool")
+
+
+def test_conv_bn_unit_scale_equals_bias_path(fc):
+    # scale 1: fma(acc, 1, b) = acc + b, so y and argmax equal chain_conv_pool's bit for bit
+    d = inputs.conv_pool_inputs(2, 12, 16, 64, 128, seed=8)
+    x, w, b = dev(d["x"]), dev(d["w"]), dev(d["b"])
+    one = torch.ones(128, dtype=torch.float16, device="cuda")
+    print("case conv_bn unit scale", flush=True)
+    for argmax in (True, None):
+        r1 = fc.chain_conv_bn_pool(x, w, one, b, argmax=argmax)
+        r0 = fc.chain_conv_pool(x, w, b, argmax=argmax)
+        torch.cuda.synchronize()
+        r1 = r1 if isinstance(r1, tuple) else (r1,)
+        r0 = r0 if isinstance(r0, tuple) else (r0,)
+        for p, q in zip(r1, r0):
+            assert np.array_equal(to_np(p).view(np.uint8), to_np(q).view(np.uint8))
+
+
+@pytest.mark.slow
+def test_conv_bn_pool_full_size_sampled(fc):
+    spec, d = inputs.workload("conv3x3_bn_relu_maxpool")
+    print("case full conv3x3_bn_relu_maxpool", flush=True)
+    x = fc.pad_channels(dev(d["x"]), 64)
+    w = fc.pad_weight_channels(dev(d["w"]), 64)
+    sc, sh = dev(d["scale"]), dev(d["shift"])
+    y = to_np(fc.chain_conv_bn_pool(x, w, sc, sh))   # the launch the bench times
+    y2, am = fc.chain_conv_bn_pool(x, w, sc, sh, argmax=True)
+    torch.cuda.synchronize()
+    assert np.array_equal(y.view(np.uint16), to_np(y2).view(np.uint16))
+    am = to_np(am)
+    for img in (0, 31):
+        di = dict(d, x=d["x"][img:img + 1])
+        check_bn_pool(y[img:img + 1], am[img:img + 1], di, "relu", "full bn img %d" % img)

@@ -408,3 +408,45 @@ def test_chain_convN_stages_by_hand(orc):
         X = orc.act(acts[i], Xh @ d["ws"][i].astype(np.float64) + d["bs"][i].astype(np.float64))
     ref = orc.chain_convN(d["x"], d["ws"], d["bs"], acts)
     assert np.max(np.abs(ref - X)) <= 1e-12 * max(1.0, np.max(np.abs(X)))
+
+
+# ------------------------------------------------------- batch-norm epilogue
+def test_conv_bn_pool_golden(orc):
+    # conv -> scale -1, shift 5 -> ReLU -> pool, worked by hand
+    g = read_fields("conv_bn_relu_pool_sobel.txt")
+    x = f16(g["x"])[None, :, :, None]
+    w = f16(g["w"])[:, :, None, None]
+    y, am, v, c64 = orc.chain_conv_bn_pool(x, w, f16(g["scale"][0]), f16(g["shift"][0]), orc.ACT_RELU,
+                                           want_conv64=True)
+    assert np.array_equal(c64[0, :, :, 0], g["v"])
+    assert np.array_equal(v[0, :, :, 0].astype(np.float64), g["v"])
+    assert y.shape == (1, 1, 1, 1) and float(y[0, 0, 0, 0]) == g["y"][0, 0]
+    assert int(am[0, 0, 0, 0]) == int(g["argmax"][0, 0])
+
+
+def test_conv_bn_is_weight_folding(orc):
+    # with power-of-two scales, multiplying the weights of output channel k by
+    # scale[k] is exact, so BN folded into the weights (a plain conv + bias)
+    # gives the epilogue form to fp64 rounding
+    x = f16(RNG.standard_normal((2, 5, 6, 8)))
+    w = f16(RNG.standard_normal((3, 3, 8, 12)) / 8)
+    scale = f16([0.5, -1, 2, -0.25, 1, -2, 0.125, 4, -0.5, 1, -1, 0.25])
+    shift = f16(RNG.standard_normal(12) / 4)
+    wf = f16(w.astype(np.float64) * scale.astype(np.float64))
+    for act in (orc.ACT_NONE, orc.ACT_RELU, orc.ACT_HARDSWISH):
+        bn = orc.conv_bn_act(x, w, scale, shift, act)
+        folded = orc.conv_bias_act(x, wf, shift, act)
+        assert np.max(np.abs(bn - folded)) <= 1e-12 * max(1.0, np.max(np.abs(folded)))
+    # the shift is added after the scale (it is not scaled itself)
+    bn0 = orc.conv_bn_act(x, w, scale, np.zeros(12, dtype=np.float16), orc.ACT_NONE)
+    bn1 = orc.conv_bn_act(x, w, scale, shift, orc.ACT_NONE)
+    assert np.max(np.abs(bn0 + shift.astype(np.float64) - bn1)) <= 1e-12 * max(1.0, np.max(np.abs(bn1)))
+
+
+def test_conv_bn_unit_scale_is_conv_bias(orc):
+    # scale 1 reduces the batch-norm chain to the plain Conv+ReLU+MaxPool chain
+    d = inputs.conv_pool_inputs(1, 6, 8, 8, 16, seed=31)
+    y1, a1, v1, _ = orc.chain_conv_bn_pool(d["x"], d["w"], np.ones(16, dtype=np.float16), d["b"], orc.ACT_RELU)
+    y0, a0, v0, _ = orc.chain_conv_pool(d["x"], d["w"], d["b"], orc.ACT_RELU)
+    assert np.array_equal(v1.view(np.uint16), v0.view(np.uint16))
+    assert np.array_equal(y1.view(np.uint16), y0.view(np.uint16)) and np.array_equal(a1, a0)
