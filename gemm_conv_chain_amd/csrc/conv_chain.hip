@@ -198,7 +198,10 @@ void k_conv_w(ConvWArgs a)
     static_assert(convw_threads(KCH) <= 512, "eight staging areas");
 
     const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
+    // wave index in a scalar register (it is wave-uniform; derived per lane it
+    // would hold a vector register, and the staging-area address built from it
+    // across the whole kernel)
+    const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lr = lane & 31, hh = lane >> 5;
     const long t_begin = (long)xcd_block(blockIdx.x, gridDim.x) * a.tiles_per_block;
     const long t_end = min(t_begin + a.tiles_per_block, a.ntiles);
@@ -270,6 +273,7 @@ void k_conv_w(ConvWArgs a)
     auto make_qrows = [&](long tl) -> QRows {
         QRows r;
         r.bits = 0;
+        const int qi = lane_id_here() >> 2;   // recomputed per tile, not held across the main loop
         if (EPI == EPI_POOL) {
             const long wi = tl * 16 + qi;
             const bool ok = wi < (nrows >> 2);
@@ -358,7 +362,14 @@ void k_conv_w(ConvWArgs a)
         const long row0 = tl * 64;
         int K = a.K;
         asm volatile("" : "+s"(K));   // keeps per-store offsets from being hoisted out of the tile loop
-        const int rr = lane >> 2, grp = lane & 3;   // read-back: staged row, 8-channel group
+        // Every per-lane value of the epilogue derives from a lane id computed
+        // here: derived from `lane`, the compiler hoists them out of the tile
+        // loop, holds them across the main loop (where all registers are
+        // taken) and spills them, and each tile's reload then waits for every
+        // prefetch in flight.
+        const int ln = lane_id_here();
+        const int lr = ln & 31, hh = ln >> 5;
+        const int rr = ln >> 2, grp = ln & 3;   // read-back: staged row, 8-channel group
         // per-lane bases; every (u, g, e, t) adds a constant (LDS instruction offsets)
         lds_half* const ow = ost + hh * 32 + lr;
         const lds_float* const bsl = bs + lr;
@@ -371,69 +382,9 @@ void k_conv_w(ConvWArgs a)
                 half_t* yb = a.y + win0 * K;
                 uint8_t* ab = a.argmax ? a.argmax + win0 * K : nullptr;
                 const int nw = (int)min(16L, (nrows >> 2) - win0);
-                // pv[t][u][g]: pooled value of window 8u + 2g + hh, channel 32t + lr
-                half_t pv[NTK][2][4];
-                if (decltype(act)::monotone && !ab) {
-                    // v = fp16(act(fma(acc, s, b))): the fused multiply-add (one
-                    // rounding), a non-decreasing activation and the fp16 rounding
-                    // are monotone in acc -- non-decreasing for s >= 0,
-                    // non-increasing for s < 0 -- so the max of the four rounded
-                    // values is v of the largest (s >= 0) or smallest (s < 0)
-                    // accumulator: pool first, then one scale/bias/act/convert per
-                    // window.  (With no scale s = 1 and fma(acc, 1, b) = acc + b.)
-#pragma unroll
-                    for (int t = 0; t < NTK; ++t) {
-                        const float bk = bsl[32 * t];
-                        const float sk = ssl[32 * t];
-                        const bool up = sk >= 0.0f;
-#pragma unroll
-                        for (int u = 0; u < 2; ++u)
-#pragma unroll
-                            for (int g = 0; g < 4; ++g) {
-                                const float hi = __builtin_fmaxf(
-                                    __builtin_fmaxf(acc[u][t][4 * g], acc[u][t][4 * g + 1]),
-                                    __builtin_fmaxf(acc[u][t][4 * g + 2], acc[u][t][4 * g + 3]));
-                                const float lo = __builtin_fminf(
-                                    __builtin_fminf(acc[u][t][4 * g], acc[u][t][4 * g + 1]),
-                                    __builtin_fminf(acc[u][t][4 * g + 2], acc[u][t][4 * g + 3]));
-                                pv[t][u][g] = (half_t)act.f(__builtin_fmaf(up ? hi : lo, sk, bk));
-                            }
-                    }
-                } else {
-                    // The pooled value and its argmax are decided on the rounded
-                    // fp16 intermediate (first maximum in window order).
-                    // Comparisons keep the per-lane value on one side and the
-                    // wave-uniform remainder on the other, so no per-(t, u, g)
-                    // lane value is precomputed and held.
-                    const int olane = hh * K + lr;
-                    int nwl = nw - hh;   // window 8u + 2g + hh is valid iff 8u + 2g < nwl
-                    asm volatile("" : "+v"(nwl));   // (opaque: compared against constants, not folded back)
-#pragma unroll
-                    for (int t = 0; t < NTK; ++t) {
-                        const float bk = bsl[32 * t];
-                        const float sk = ssl[32 * t];
-                        const bool kok = lr < K - 32 * t;
-#pragma unroll
-                        for (int u = 0; u < 2; ++u) {
-#pragma unroll
-                            for (int g = 0; g < 4; ++g) {
-                                half_t best = (half_t)act.f(__builtin_fmaf(acc[u][t][4 * g], sk, bk));
-                                int bi = 0;
-#pragma unroll
-                                for (int e = 1; e < 4; ++e) {
-                                    const half_t v = (half_t)act.f(__builtin_fmaf(acc[u][t][4 * g + e], sk, bk));
-                                    const bool gt = v > best;
-                                    best = gt ? v : best;
-                                    bi = gt ? e : bi;
-                                }
-                                pv[t][u][g] = best;
-                                const int w0 = 8 * u + 2 * g;
-                                if (ab && kok && w0 < nwl) ab[olane + w0 * K + 32 * t] = (uint8_t)bi;
-                            }
-                            __builtin_amdgcn_sched_barrier(0);   // bound the scheduling window
-                        }
-                    }
-                }
+                // Pooled values go to the staging area as they are computed,
+                // pass by pass, so each accumulator register dies once its
+                // window is staged (no array of pooled values is held).
                 // Whole output rows: four passes of four windows, each staged as
                 // [4 windows][KP channels] fp16 (1 KiB for KP = 128) and stored
                 // by KP/8 lanes per window row, 16 bytes each, so every store
@@ -441,15 +392,58 @@ void k_conv_w(ConvWArgs a)
                 // windows 4p..4p+3 = 8u + 2g + hh with u = p/2, g = 2(p%2) + gg.
                 static_assert(4 * KP * 2 <= CW_OSTAGE, "four staged rows fit the staging area");
                 constexpr int LPR = KP / 8;   // lanes per staged row
-                const int sr = lane / LPR, sg = lane % LPR;
+                const int sr = ln / LPR, sg = ln % LPR;
                 const lds_half8* const srd = reinterpret_cast<const lds_half8*>(ost + sr * KP + 8 * sg);
+                // argmax (first maximum of the rounded values) is only needed
+                // with an argmax output or an activation that is not monotone
+                const bool fast = decltype(act)::monotone && !ab;
+                const int olane = hh * K + lr;
+                int nwl = nw - hh;   // window 8u + 2g + hh is valid iff 8u + 2g < nwl
+                asm volatile("" : "+v"(nwl));   // (opaque: compared against constants, not folded back)
 #pragma unroll
                 for (int p = 0; p < 4; ++p) {
+                    const int u = p >> 1;
 #pragma unroll
-                    for (int gg = 0; gg < 2; ++gg)
+                    for (int gg = 0; gg < 2; ++gg) {
+                        const int g = 2 * (p & 1) + gg;
 #pragma unroll
-                        for (int t = 0; t < NTK; ++t)
-                            ost[(2 * gg + hh) * KP + 32 * t + lr] = pv[t][p >> 1][2 * (p & 1) + gg];
+                        for (int t = 0; t < NTK; ++t) {
+                            const float bk = bsl[32 * t];
+                            const float sk = ssl[32 * t];
+                            const floatx16& c = acc[u][t];
+                            half_t best;
+                            if (fast) {
+                                // v = fp16(act(fma(acc, s, b))): the fused multiply-add
+                                // (one rounding), a non-decreasing activation and the
+                                // fp16 rounding are monotone in acc -- non-decreasing
+                                // for s >= 0, non-increasing for s < 0 -- so the max
+                                // of the four rounded values is v of the largest
+                                // (s >= 0) or smallest (s < 0) accumulator: pool
+                                // first, then one scale/bias/act/convert per window.
+                                // (No scale: s = 1, and fma(acc, 1, b) = acc + b.)
+                                const float hi = __builtin_fmaxf(__builtin_fmaxf(c[4 * g], c[4 * g + 1]),
+                                                                 __builtin_fmaxf(c[4 * g + 2], c[4 * g + 3]));
+                                const float lo = __builtin_fminf(__builtin_fminf(c[4 * g], c[4 * g + 1]),
+                                                                 __builtin_fminf(c[4 * g + 2], c[4 * g + 3]));
+                                best = (half_t)act.f(__builtin_fmaf(sk >= 0.0f ? hi : lo, sk, bk));
+                            } else {
+                                // decided on the rounded fp16 intermediate, first
+                                // maximum in window order (0,0),(0,1),(1,0),(1,1)
+                                best = (half_t)act.f(__builtin_fmaf(c[4 * g], sk, bk));
+                                int bi = 0;
+#pragma unroll
+                                for (int e = 1; e < 4; ++e) {
+                                    const half_t v = (half_t)act.f(__builtin_fmaf(c[4 * g + e], sk, bk));
+                                    const bool gt = v > best;
+                                    best = gt ? v : best;
+                                    bi = gt ? e : bi;
+                                }
+                                const int w0 = 8 * u + 2 * g;
+                                if (ab && lr < K - 32 * t && w0 < nwl) ab[olane + w0 * K + 32 * t] = (uint8_t)bi;
+                            }
+                            ost[(2 * gg + hh) * KP + 32 * t + lr] = best;
+                        }
+                    }
                     wave_lds_sync();
                     if (sr < 4) {
                         const half8 v = *srd;

@@ -491,6 +491,18 @@ __device__ __forceinline__ void store_tile(const lds_half* T, int ldt, int rows,
 // Orders this wave's LDS accesses around a hand-off through LDS between its
 // own lanes (LDS instructions of one wave execute in order; this also keeps
 // the compiler from moving accesses across it).
+// The lane id, computed where it is used (v_mbcnt over a full mask): the asm
+// block has no inputs and is volatile, so the compiler can neither hoist it
+// out of a loop nor keep an earlier copy alive across the loop (a per-lane
+// value held across a register-bound main loop gets spilled, and its reload
+// waits for every load in flight).
+__device__ __forceinline__ int lane_id_here()
+{
+    int l;
+    asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+    return l;
+}
+
 __device__ __forceinline__ void wave_lds_sync()
 {
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
