@@ -255,7 +255,7 @@ void k_conv_w(ConvWArgs a)
     // of row tiles u = 0, 1 (tile rows 32u + lane%32), the same layout the
     // runtime-chunk path loads directly.  POOL: tile row 4i + j is element
     // j = 2dy + dx of the tile's window i; STORE: pixel tile*64 + 4i + j.
-    const int qi = lane >> 2, qm = lane & 3;
+    const int qm = lane & 3;
     // A lane's four tile rows: the pixel of row j is base + off(j) with
     // off(j) = (dy W + dx) C (POOL, the window's 2x2 pixels) or j C (STORE,
     // consecutive pixels are C apart); bits 6j..6j+5 hold the tap masks of
@@ -548,11 +548,17 @@ void k_conv_w(ConvWArgs a)
                                 __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read
                             }
                         } else {
+                            // the fragment of column tile t + 1 is read while tile
+                            // t's two MFMAs run (two fragment registers, not one:
+                            // with one, every read waits out the LDS latency)
+                            half8 wv = frag_tr_at(wlane[0] + 16 * st * Wn.ld, 4 * Wn.ld);
 #pragma unroll
                             for (int t = 0; t < NTK; ++t) {
-                                const half8 wv = frag_tr_at(wlane[t] + (64 * c + 16 * q) * Wn.ld, 4 * Wn.ld);
+                                half8 wn = wv;
+                                if (t + 1 < NTK) wn = frag_tr_at(wlane[t + 1] + 16 * st * Wn.ld, 4 * Wn.ld);
                                 acc[0][t] = mfma32x32x16(x0, wv, acc[0][t]);
                                 acc[1][t] = mfma32x32x16(x1, wv, acc[1][t]);
+                                wv = wn;
                             }
                         }
                     }
