@@ -212,3 +212,22 @@ def test_chain_conv_bn_pool_validation(L):
     assert bn(pool=2) == E_ARG
     assert bn(pool=0, am=P) == E_ARG           # argmax needs a pool
     assert bn(shape=fc.ConvShape(1, 8, 8, 64, 136, 3, 3, 1, 1)) == E_UNSUP
+
+
+def test_empty_inputs_launch_nothing(L):
+    # an empty batch or a pooled output of zero size is a no-op: FC_OK with
+    # NULL data pointers, decided before any HIP call (so it runs without a GPU)
+    import ctypes as C
+    empty = fc.ConvShape(0, 8, 8, 64, 64, 3, 3, 1, 1)
+    one_row = fc.ConvShape(1, 1, 8, 64, 64, 3, 3, 1, 1)    # 1x8 image: the 2x2 pool has no output
+    assert L.chain_conv_pool(NUL, P, NUL, 1, 1, NUL, C.byref(empty), NUL, None) == OK
+    assert L.chain_conv_pool(P, P, NUL, 1, 1, NUL, C.byref(one_row), NUL, None) == OK
+    assert L.chain_conv_bn_pool(NUL, P, P, NUL, 1, 1, NUL, C.byref(empty), NUL, None) == OK
+    assert L.chain_conv_bn_pool(P, P, P, NUL, 1, 1, NUL, C.byref(one_row), NUL, None) == OK
+    kp = (C.c_int32 * 3)(64, 64, 128)
+    wp = (C.c_void_p * 3)(P, P, P)
+    ap = (C.c_int * 3)(1, 1, 0)
+    assert L.chain_convN(NUL, C.byref(empty), 3, wp, None, ap, kp, NUL, None) == OK
+    assert L.chain_gemm2_variant(NUL, P, NUL, 1, P, NUL, NUL, 0, 64, 64, 64, 3, None) == OK
+    wd = (C.c_int32 * 4)(64, 64, 64, 64)
+    assert L.chain_gemmN(NUL, 3, wp, None, ap, wd, NUL, 0, None) == OK

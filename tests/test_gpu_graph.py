@@ -46,7 +46,7 @@ def check_replays(step, inp, fresh, out, eager):
         assert torch.equal(out, ref), "replay %d differs from the eager launch" % r
 
 
-@pytest.mark.parametrize("variant", ["rf", "lds"])
+@pytest.mark.parametrize("variant", ["rf", "lds", "stream"])
 def test_chain_gemm2_graph(fc, variant):
     print("case graph chain_gemm2", variant, flush=True)
     N0 = 64 if variant == "rf" else 256
@@ -78,4 +78,43 @@ def test_chain_conv2_graph(fc):
     step = lambda: fc.chain_conv2(x, w0, b0, w1, b1, act="relu", out=out)
     fresh = lambda r: dev(inputs.conv2_inputs(2, 10, 14, 64, 64, 256, seed=300 + r)["x"])
     eager = lambda src: fc.chain_conv2(src, w0, b0, w1, b1, act="relu")
+    check_replays(step, x, fresh, out, eager)
+
+
+def test_chain_gemmN_graph(fc):
+    print("case graph chain_gemmN", flush=True)
+    wd = [256, 64, 64, 128]
+    acts = ["relu", "relu", "none"]
+    d = inputs.gemmN_inputs(1000, wd, "uniform", seed=14)
+    A = dev(d["A"])
+    Ws, bs = [dev(w) for w in d["Ws"]], [dev(b) for b in d["bs"]]
+    out = torch.empty((1000, 128), dtype=torch.float16, device="cuda")
+    step = lambda: fc.chain_gemmN(A, Ws, bs, acts, out=out)
+    fresh = lambda r: dev(inputs.gemmN_inputs(1000, wd, "uniform", seed=400 + r)["A"])
+    eager = lambda src: fc.chain_gemmN(src, Ws, bs, acts)
+    check_replays(step, A, fresh, out, eager)
+
+
+def test_chain_convN_graph(fc):
+    print("case graph chain_convN", flush=True)
+    ks = [64, 64, 256]
+    acts = ["relu", "relu", "none"]
+    d = inputs.convN_inputs(2, 10, 14, 64, ks, seed=15)
+    x = dev(d["x"])
+    ws, bs = [dev(w) for w in d["ws"]], [dev(b) for b in d["bs"]]
+    out = torch.empty((2, 10, 14, 256), dtype=torch.float16, device="cuda")
+    step = lambda: fc.chain_convN(x, ws, bs, acts, out=out)
+    fresh = lambda r: dev(inputs.convN_inputs(2, 10, 14, 64, ks, seed=500 + r)["x"])
+    eager = lambda src: fc.chain_convN(src, ws, bs, acts)
+    check_replays(step, x, fresh, out, eager)
+
+
+def test_chain_conv_bn_pool_graph(fc):
+    print("case graph chain_conv_bn_pool", flush=True)
+    d = inputs.conv_bn_pool_inputs(2, 18, 22, 64, 128, seed=16)
+    x, w, sc, sh = dev(d["x"]), dev(d["w"]), dev(d["scale"]), dev(d["shift"])
+    out = torch.empty((2, 9, 11, 128), dtype=torch.float16, device="cuda")
+    step = lambda: fc.chain_conv_bn_pool(x, w, sc, sh, act="relu", pool="max2x2", out=out)
+    fresh = lambda r: dev(inputs.conv_bn_pool_inputs(2, 18, 22, 64, 128, seed=600 + r)["x"])
+    eager = lambda src: fc.chain_conv_bn_pool(src, w, sc, sh, act="relu", pool="max2x2")
     check_replays(step, x, fresh, out, eager)
