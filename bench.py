@@ -309,7 +309,8 @@ def cpu_baseline(prob, seconds):
                 passes += 1
         sample = "first %d of %d rows" % (rows, M) if rows < M else "all %d rows x %d passes" % (M, passes)
         return {"value": per_row * rows * passes / t / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
-                "sample": sample + " (fp64, unfused, same seeded inputs)", "seconds": round(t, 3)}
+                "sample": sample + " (fp64, unfused, same seeded inputs)", "seconds": round(t, 3),
+                "cpu_model": cpu_model()}
     n = s["n"]
     per_img = prob.flops / n
 
@@ -330,7 +331,43 @@ def cpu_baseline(prob, seconds):
     t = run(imgs) if imgs != 1 else tp
     return {"value": per_img * imgs / t / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
             "sample": "first %d of %d images (fp64, unfused, same seeded inputs)" % (imgs, n),
-            "seconds": round(t, 3)}
+            "seconds": round(t, 3), "cpu_model": cpu_model()}
+
+
+def mfma_probe(torch, fc, waves_per_simd=2, iters=2048):
+    """The matrix-core rate the GPU sustains on register operands (fc_probe_mfma:
+    8 independent 32x32x16 fp16 MFMAs per round, every CU), event-timed on the
+    current stream after one warm-up launch, and the shader clock derived from
+    the kernel's own counters (s_memtime ticks over 100 MHz s_memrealtime ticks)."""
+    n = torch.cuda.get_device_properties(0).multi_processor_count
+    stamps = torch.zeros(4 * n, dtype=torch.int64, device="cuda")
+    sink = torch.zeros(n, dtype=torch.float32, device="cuda")
+    fc.probe_mfma(stamps, sink, waves_per_simd, iters)
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    blocks = fc.probe_mfma(stamps, sink, waves_per_simd, iters)
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1)
+    flops = blocks * 4 * waves_per_simd * iters * 8 * 32768
+    st = stamps.view(-1, 4)[:blocks].cpu().tolist()
+    clk = sorted((b[1] - b[0]) / ((b[3] - b[2]) / 100e6) / 1e9 for b in st if b[3] > b[2])
+    return {"tflops": round(flops / (ms * 1e-3) / 1e12, 1), "ms": round(ms, 4), "waves_per_simd": waves_per_simd,
+            "pct_of_nominal": round(100 * flops / (ms * 1e-3) / 1e12 / PEAK_F16_TFLOPS, 1),
+            "sclk_ghz_median": round(clk[len(clk) // 2], 3) if clk else None}
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 def measured_traffic(name, kernel_hash):
@@ -364,6 +401,7 @@ def main():
                     help="GEMM-chain workloads: profile the residence variants on the GPU first "
                          "(chain_gemm2_tune) and time the fastest")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-probe", action="store_true", help="skip the matrix-core rate / clock probe")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run one 256 MiB device copy (known bytes, for PMC counter calibration)")
     args = ap.parse_args()
@@ -442,6 +480,12 @@ def main():
                  "algorithmic_bytes": prob.bytes_fused, "algorithmic_flops": prob.flops,
                  "executed_flops": prob.flops_exec})
 
+    probe = None
+    if not args.no_probe:
+        probe = mfma_probe(torch, fc)
+        log("mfma probe: %.1f TFLOP/s (%.1f%% of nominal), shader clock %s GHz"
+            % (probe["tflops"], probe["pct_of_nominal"], probe["sclk_ghz_median"]))
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(prob, args.cpu_seconds)
@@ -453,6 +497,8 @@ def main():
         "vs_baseline": None, "dtype": "f16", "accumulate": "f32", "data": "synthetic",
         "config": dict(prob.config, cache="cold (rotating %d buffer sets)" % prob.nsets if prob.nsets > 1 else "warm"),
         "pct_fp16_mfma_peak": round(100 * tflops / PEAK_F16_TFLOPS, 2),
+        "pct_of_measured_mfma_peak": round(100 * tflops / probe["tflops"], 2) if probe else None,
+        "mfma_probe": probe,
         "roofline": roof, "unfused": unfused, "cpu_baseline": cpu, "kernel_src": h,
     }
     print(json.dumps(out), flush=True)

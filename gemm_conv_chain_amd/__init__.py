@@ -78,9 +78,10 @@ def lib():
                                   ctypes.POINTER(ctypes.c_int), ctypes.POINTER(_i32), _vp, _vp]
         L.chain_conv_bn_pool.argtypes = [_vp, _vp, _vp, _vp, ctypes.c_int, ctypes.c_int, _vp,
                                          ctypes.POINTER(ConvShape), _vp, _vp]
+        L.fc_probe_mfma.argtypes = [_i32, _i32, _vp, _vp, _i32, ctypes.POINTER(_i32), _vp]
         L.fc_tune_clear.restype = None
         L.fc_tune_clear.argtypes = []
-        for name in ("chain_conv_bn_pool", "chain_convN", "chain_gemm2_tune", "chain_gemm2_auto_variant", "chain_gemm2", "chain_gemm2_variant", "chain_gemmN", "chain_conv_pool", "chain_conv2", "gemm_bias_act",
+        for name in ("fc_probe_mfma", "chain_conv_bn_pool", "chain_convN", "chain_gemm2_tune", "chain_gemm2_auto_variant", "chain_gemm2", "chain_gemm2_variant", "chain_gemmN", "chain_conv_pool", "chain_conv2", "gemm_bias_act",
                      "conv_bias_act", "maxpool2x2", "pad_channels"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
@@ -192,6 +193,21 @@ def auto_variant(M, K0, N0, N1, act="relu"):
     _check("chain_gemm2_auto_variant", lib().chain_gemm2_auto_variant(int(M), int(K0), int(N0), int(N1), _act(act),
                                                                       ctypes.byref(v)))
     return _VARIANT_NAME[v.value]
+
+
+def probe_mfma(stamps, sink, waves_per_simd=2, iters=2048):
+    """Enqueue the matrix-core rate probe (fc_probe_mfma) on the current
+    stream; stamps: int64 [4 * n], sink: float32 [n] with n >= the CU count
+    (checked by the library before launching).  Returns the grid
+    size (blocks); FLOPs per launch = blocks * 4 * waves_per_simd * iters * 8 * 32768."""
+    torch = _torch()
+    if stamps.dtype != torch.int64 or sink.dtype != torch.float32 or not stamps.is_cuda or not sink.is_cuda:
+        raise TypeError("stamps must be a CUDA int64 tensor and sink a CUDA float32 tensor")
+    blocks = _i32(0)
+    capacity = min(stamps.numel() // 4, sink.numel())
+    _check("fc_probe_mfma", lib().fc_probe_mfma(int(waves_per_simd), int(iters), _ptr(stamps), _ptr(sink),
+                                                int(capacity), ctypes.byref(blocks), _stream(stamps)))
+    return blocks.value
 
 
 def tune_clear():

@@ -257,6 +257,26 @@ fc_status maxpool2x2(const fc_half *x, fc_half *y, uint8_t *argmax, int32_t n, i
 fc_status pad_channels(const fc_half *src, fc_half *dst, int64_t outer, int32_t c_in, int32_t c_out,
                        int32_t inner, void *stream);
 
+/*
+ * fc_probe_mfma -- measurement aid, not part of any chain: one block per CU,
+ * waves_per_simd (1 or 2) waves per SIMD, each issuing iters x 8 independent
+ * fp16 MFMAs (32x32x16, fp32 accumulate) on register operands (no memory
+ * traffic), so that (launch time, FLOPs = blocks * 4 * waves_per_simd * iters
+ * * 8 * 32768) gives the matrix-core rate the GPU sustains.  The first wave of
+ * each block writes 4 counters to stamps[4 * block ...]: shader clock
+ * (s_memtime) before and after its loop, then the 100 MHz real-time counter
+ * before and after, from which the host derives the shader clock under full
+ * MFMA load.  sink[block] receives one accumulator sum (keeps the work live).
+ *   stamps: device, uint64 [4 * capacity], 8-byte aligned; sink: device,
+ *   float [capacity]; capacity: blocks the buffers hold -- FC_E_SHAPE (and no
+ *   launch) if the grid (the device's CU count) is larger; blocks (host, out):
+ *   the grid size.  iters in 1 .. 2^20.
+ * Enqueued on stream, asynchronous.  Returns the status only (fc_last_error
+ * is not set by this call).
+ */
+fc_status fc_probe_mfma(int32_t waves_per_simd, int32_t iters, uint64_t *stamps, float *sink,
+                        int32_t capacity, int32_t *blocks, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -25,7 +25,7 @@ def test_exports_every_declared_symbol(L):
     names = fc.exported_names()
     for n in ("chain_gemm2", "chain_gemm2_variant", "chain_gemmN", "chain_conv_pool", "chain_conv2", "gemm_bias_act",
               "conv_bias_act", "maxpool2x2", "pad_channels", "fc_abi_version", "fc_status_str", "fc_last_error",
-              "chain_gemm2_tune", "chain_gemm2_auto_variant", "fc_tune_clear", "chain_convN", "chain_conv_bn_pool"):
+              "chain_gemm2_tune", "chain_gemm2_auto_variant", "fc_tune_clear", "chain_convN", "chain_conv_bn_pool", "fc_probe_mfma"):
         assert n in names
     for n in names:
         assert hasattr(L, n), n
@@ -231,3 +231,12 @@ def test_empty_inputs_launch_nothing(L):
     assert L.chain_gemm2_variant(NUL, P, NUL, 1, P, NUL, NUL, 0, 64, 64, 64, 3, None) == OK
     wd = (C.c_int32 * 4)(64, 64, 64, 64)
     assert L.chain_gemmN(NUL, 3, wp, None, ap, wd, NUL, 0, None) == OK
+
+
+def test_probe_validation(L):
+    import ctypes as C
+    b = C.c_int32(0)
+    assert L.fc_probe_mfma(2, 16, NUL, P, 256, C.byref(b), None) == E_NULL
+    assert L.fc_probe_mfma(3, 16, P, P2, 256, C.byref(b), None) == E_SHAPE     # 1 or 2 waves per SIMD
+    assert L.fc_probe_mfma(2, 0, P, P2, 256, C.byref(b), None) == E_SHAPE
+    assert L.fc_probe_mfma(2, 16, C.c_void_p(0x10004), P2, 256, C.byref(b), None) == E_ALIGN
