@@ -16,7 +16,7 @@ busy fraction of the 1024 SIMDs is BUSY / (GRBM_GUI_ACTIVE / 8 * 1024).
 each kernel) from two ``--pmc`` runs (DIR/fetch, DIR/write) of
 ``bench.py --calib-copy``; WORKLOAD is the bench workload, or WORKLOAD@VARIANT
 for a run with ``--variant`` other than the workload's own.  Each counter is scaled by what it reads for the
-256 MiB device-to-device copy that ``--calib-copy`` issues last (known bytes):
+256 MiB device-to-device copy that ``--calib-copy`` issues (known bytes; the largest copy dispatch):
 scale = 262144 KiB / counter value of that dispatch.  With --json the scaled
 HBM bytes of the fused kernel (and the sum over the unfused kernels) are
 recorded for bench.py, keyed by the hash of the kernel sources they were taken
@@ -60,11 +60,13 @@ def _pmc(d, counter):
     copies = [r for r in rows if "copyBuffer" in r["Kernel_Name"]]
     if not copies:
         raise SystemExit("no calibration copy dispatch in %s" % d)
-    calib = max(copies, key=lambda r: int(r["Dispatch_Id"]))
+    # the 256 MiB calibration copy is by far the largest copy dispatch of the run
+    calib = max(copies, key=lambda r: float(r["Counter_Value"]))
     scale = 262144.0 / float(calib["Counter_Value"])
     per = {}
     for r in rows:
-        if _ours(r["Kernel_Name"]) and "k_pad_mid" not in r["Kernel_Name"]:   # padding is input preparation
+        # padding is input preparation and the matrix-core probe is not part of any chain
+        if _ours(r["Kernel_Name"]) and "k_pad_mid" not in r["Kernel_Name"] and "k_mfma_probe" not in r["Kernel_Name"]:
             per.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
     return scale, float(calib["Counter_Value"]), {k: sum(v) / len(v) for k, v in per.items()}
 
