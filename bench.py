@@ -407,7 +407,7 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print("bench.py: this build measures one GPU only (the fused chain needs no collectives; "
+        print("bench.py: measures one GPU only (the fused chain needs no collectives; "
               "--gpus %d is not supported)" % args.gpus, file=sys.stderr)
         sys.exit(2)
 
