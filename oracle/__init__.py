@@ -184,6 +184,19 @@ def maxpool2x2(v):
     return y.view(np.float16), am
 
 
+def avgpool2x2(v) -> np.ndarray:
+    """fp16 [n, P//2, Q//2, K]: 2x2 stride-2 average pool of fp16 v [n,P,Q,K]
+    (floor for odd sizes) -- each window's four values summed and halved twice,
+    exact in fp64, then rounded once to fp16.  A partial reduction of the
+    epilogue (BOLT notes, "Prerequisite: Epilogue fusion")."""
+    v = np.asarray(v, dtype=np.float16)
+    n, P, Q, K = v.shape
+    P2, Q2 = P // 2, Q // 2
+    w = v[:, :2 * P2, :2 * Q2, :].astype(np.float64).reshape(n, P2, 2, Q2, 2, K)
+    s = w[:, :, 0, :, 0] + w[:, :, 0, :, 1] + w[:, :, 1, :, 0] + w[:, :, 1, :, 1]
+    return f64_to_f16(s / 4.0)
+
+
 def chain_gemm2(A, W0, b0, act_kind: int, W1, b1):
     """(ref fp64 [M,N1], H fp16 [M,N0]) for D1 = act(A W0 + b0) W1 + b1."""
     M, K0 = A.shape
@@ -276,6 +289,16 @@ def chain_conv_bn_pool(x, w, scale, shift, act_kind: int = ACT_RELU, want_conv64
     v = f64_to_f16(c64)
     y, am = maxpool2x2(v)
     return y, am, v, (c64 if want_conv64 else None)
+
+
+def chain_conv_avgpool(x, w, b, act_kind: int = ACT_RELU, scale=None):
+    """(y fp16, v fp16) of avgpool2x2(fp16(act(conv(x, w) [* scale] + b))):
+    the Conv+act+pool chain with an average instead of a maximum; with a scale
+    the conv output is batch-normalised as in conv_bn_act.  Built from
+    conv_bias_act / conv_bn_act, the fp16 codec and avgpool2x2."""
+    c = conv_bn_act(x, w, scale, b, act_kind) if scale is not None else conv_bias_act(x, w, b, act_kind)
+    v = f64_to_f16(c)
+    return avgpool2x2(v), v
 
 
 def chain_conv_pool(x, w, b, act_kind: int = ACT_RELU, stride: int = 1, pad: int = 1, want_conv64=False):

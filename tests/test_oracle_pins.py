@@ -450,3 +450,43 @@ def test_conv_bn_unit_scale_is_conv_bias(orc):
     y0, a0, v0, _ = orc.chain_conv_pool(d["x"], d["w"], d["b"], orc.ACT_RELU)
     assert np.array_equal(v1.view(np.uint16), v0.view(np.uint16))
     assert np.array_equal(y1.view(np.uint16), y0.view(np.uint16)) and np.array_equal(a1, a0)
+
+
+# ----------------------------------------------------------- average pool
+def test_avgpool_golden(orc):
+    g = read_fields("avgpool_4x4.txt")
+    v = f16(g["v"])[None, :, :, None]
+    y = orc.avgpool2x2(v)
+    assert np.array_equal(y[0, :, :, 0].astype(np.float64), g["y"])
+
+
+def test_avgpool_rounds_the_mean_once(orc):
+    # the mean is formed exactly and rounded once: {1, 1, 1, 1 + 2^-10} has mean
+    # 1 + 2^-12 (a quarter ulp above 1 -> 1.0); three values of 1 + 2^-10 give
+    # 1 + 0.75 * 2^-10 (-> 1 + 2^-10); rounding each partial sum would differ
+    a, b = 1.0, 1.0 + 2.0 ** -10
+    v = f16([[a, a], [a, b]])[None, :, :, None]
+    assert float(orc.avgpool2x2(v)[0, 0, 0, 0]) == 1.0
+    v = f16([[a, b], [b, b]])[None, :, :, None]
+    assert float(orc.avgpool2x2(v)[0, 0, 0, 0]) == b
+
+
+def test_avgpool_bounds_and_constant(orc):
+    v = f16(RNG.standard_normal((2, 7, 9, 5)))
+    y = orc.avgpool2x2(v).astype(np.float64)
+    ymax, _ = orc.maxpool2x2(v)
+    assert y.shape == (2, 3, 4, 5)                          # floor for odd sizes
+    assert np.all(y <= ymax.astype(np.float64))
+    ymin = -orc.maxpool2x2(f16(-v.astype(np.float64)))[0].astype(np.float64)
+    assert np.all(y >= ymin)
+    c = np.full((1, 4, 6, 3), 0.3, dtype=np.float16)
+    assert np.array_equal(orc.avgpool2x2(c).view(np.uint16), np.full((1, 2, 3, 3), 0.3, np.float16).view(np.uint16))
+
+
+def test_chain_conv_avgpool_composition(orc):
+    # the chain pools the rounded fp16 conv output (the same v as the max chain)
+    d = inputs.conv_pool_inputs(1, 6, 8, 8, 16, seed=32)
+    y, v = orc.chain_conv_avgpool(d["x"], d["w"], d["b"], orc.ACT_RELU)
+    _, _, vmax, _ = orc.chain_conv_pool(d["x"], d["w"], d["b"], orc.ACT_RELU)
+    assert np.array_equal(v.view(np.uint16), vmax.view(np.uint16))
+    assert np.array_equal(y.view(np.uint16), orc.avgpool2x2(v).view(np.uint16))
