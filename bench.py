@@ -154,6 +154,7 @@ class Problem:
             self.flops_exec = 2 * npix * k * 9 * cp         # executed: padded to 64
             npool = n * (h // 2) * (w // 2)
             self.bn = bool(s.get("bn"))
+            self.pool = s.get("pool", "max2x2")
             self.bytes_fused = 2 * (npix * cp + 9 * cp * k + k + npool * k) + (2 * k if self.bn else 0)
             self.bytes_interm = 2 * npix * k
             xp = fc.pad_channels(t(d["x"]), cp)             # input preparation, outside the timed chain
@@ -166,7 +167,7 @@ class Problem:
             self.H = torch.empty((n, h, w, k), dtype=torch.float16, device=dev)
             self.config = {"workload": name, "x": [n, h, w, c], "channels_padded_to": cp,
                            "conv": "3x3 s1 p1 %d->%d %s ReLU" % (c, k, "x scale + shift" if self.bn else "+b"),
-                           "pool": "max 2x2 s2"}
+                           "pool": ("avg" if self.pool == "avg2x2" else "max") + " 2x2 s2"}
             self.kernel = "k_conv_w"
         torch.cuda.synchronize()
 
@@ -189,7 +190,7 @@ class Problem:
             fc.chain_conv_bn_pool(self.X[j], w, sc, sh, act="relu", pool="max2x2", out=self.Y[j])
         else:
             w, b = self.W
-            fc.chain_conv_pool(self.X[j], w, b, act="relu", pool="max2x2", out=self.Y[j])
+            fc.chain_conv_pool(self.X[j], w, b, act="relu", pool=self.pool, out=self.Y[j])
 
     def step_unfused(self, i):
         """The two-kernel baseline: the intermediate goes to HBM and back."""
@@ -225,7 +226,10 @@ class Problem:
         else:
             w, b = self.W
             fc.conv_bias_act(self.X[j], w, b, act="relu", out=self.H)
-            fc.maxpool2x2(self.H, out=self.Y[j])
+            if self.pool == "avg2x2":
+                fc.avgpool2x2(self.H, out=self.Y[j])
+            else:
+                fc.maxpool2x2(self.H, out=self.Y[j])
 
 
 def time_steps(torch, fn, steps, warmup):
@@ -322,6 +326,8 @@ def cpu_baseline(prob, seconds):
             oracle.chain_convN(d["x"][:imgs], d["ws"], d["bs"], [actk[a] for a in s["acts"]])
         elif s.get("bn"):
             oracle.chain_conv_bn_pool(d["x"][:imgs], d["w"], d["scale"], d["shift"], oracle.ACT_RELU)
+        elif s.get("pool") == "avg2x2":
+            oracle.chain_conv_avgpool(d["x"][:imgs], d["w"], d["b"], oracle.ACT_RELU)
         else:
             oracle.chain_conv_pool(d["x"][:imgs], d["w"], d["b"], oracle.ACT_RELU)
         return time.perf_counter() - t
@@ -391,7 +397,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="b2b_gemm_rf",
                     choices=["b2b_gemm_tiny", "b2b_gemm_rf", "b2b_gemm_lds", "gemm3_rf", "conv3x3_conv1x1", "conv3x3_conv1x1x2",
-                             "conv3x3_relu_maxpool", "conv3x3_bn_relu_maxpool"])
+                             "conv3x3_relu_maxpool", "conv3x3_bn_relu_maxpool", "conv3x3_relu_avgpool"])
     ap.add_argument("--variant", choices=["rf", "lds", "stream"], default=None,
                     help="GEMM-chain kernel variant (default: rf, or lds for b2b_gemm_lds)")
     ap.add_argument("--warm", action="store_true", help="reuse one buffer set (cache-warm timing)")

@@ -20,7 +20,7 @@ import os
 import re
 
 __all__ = ["lib", "FusedChainError", "chain_gemm2", "tune_chain_gemm2", "auto_variant", "tune_clear", "chain_gemmN", "chain_conv_pool", "chain_conv_bn_pool", "chain_conv2", "chain_convN",
-           "gemm_bias_act", "conv_bias_act", "maxpool2x2", "pad_channels", "pad_weight_channels", "abi_version", "ACT", "VARIANT",
+           "gemm_bias_act", "conv_bias_act", "maxpool2x2", "avgpool2x2", "pad_channels", "pad_weight_channels", "abi_version", "ACT", "VARIANT",
            "LIB_PATH", "HEADER_PATH", "exported_names"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -28,7 +28,7 @@ LIB_PATH = os.path.join(_HERE, "libfusedchain.so")
 HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "fusedchain.h")
 
 ACT = {"none": 0, "relu": 1, "gelu_tanh": 2, "hardswish": 3}
-POOL = {"none": 0, "max2x2": 1}
+POOL = {"none": 0, "max2x2": 1, "avg2x2": 2}
 VARIANT = {"auto": 0, "rf": 1, "lds": 2, "stream": 3}
 
 
@@ -70,6 +70,7 @@ def lib():
         L.gemm_bias_act.argtypes = [_vp, _vp, _vp, ctypes.c_int, _vp, _i64, _i32, _i32, _vp]
         L.conv_bias_act.argtypes = [_vp, _vp, _vp, ctypes.c_int, _vp, ctypes.POINTER(ConvShape), _vp]
         L.maxpool2x2.argtypes = [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _vp]
+        L.avgpool2x2.argtypes = [_vp, _vp, _i32, _i32, _i32, _i32, _vp]
         L.pad_channels.argtypes = [_vp, _vp, _i64, _i32, _i32, _i32, _vp]
         L.chain_gemm2_tune.argtypes = [_vp, _vp, _vp, ctypes.c_int, _vp, _vp, _vp, _i64, _i32, _i32, _i32, _i32,
                                        ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_float), _vp]
@@ -81,7 +82,7 @@ def lib():
         L.fc_probe_mfma.argtypes = [_i32, _i32, _vp, _vp, _i32, ctypes.POINTER(_i32), _vp]
         L.fc_tune_clear.restype = None
         L.fc_tune_clear.argtypes = []
-        for name in ("fc_probe_mfma", "chain_conv_bn_pool", "chain_convN", "chain_gemm2_tune", "chain_gemm2_auto_variant", "chain_gemm2", "chain_gemm2_variant", "chain_gemmN", "chain_conv_pool", "chain_conv2", "gemm_bias_act",
+        for name in ("avgpool2x2", "fc_probe_mfma", "chain_conv_bn_pool", "chain_convN", "chain_gemm2_tune", "chain_gemm2_auto_variant", "chain_gemm2", "chain_gemm2_variant", "chain_gemmN", "chain_conv_pool", "chain_conv2", "gemm_bias_act",
                      "conv_bias_act", "maxpool2x2", "pad_channels"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
@@ -360,6 +361,17 @@ def chain_convN(x, ws, bs, acts, out=None):
     ap = (ctypes.c_int * n)(*[_act(a) for a in acts])
     kp = (_i32 * n)(*ks)
     _check("chain_convN", lib().chain_convN(_ptr(x), ctypes.byref(sh), n, wp, bp, ap, kp, _ptr(out), _stream(x)))
+    return out
+
+
+def avgpool2x2(x, out=None):
+    """y [n, h/2, w/2, c] = 2x2/2 average pool of NHWC x (fp16 mean of each window)."""
+    _need(x, "x", 4)
+    n, h, w, c = x.shape
+    if out is None:
+        out = _torch().empty((n, h // 2, w // 2, c), dtype=x.dtype, device=x.device)
+    _need(out, "out", 4)
+    _check("avgpool2x2", lib().avgpool2x2(_ptr(x), _ptr(out), n, h, w, c, _stream(x)))
     return out
 
 

@@ -15,7 +15,7 @@ namespace fc {
 hipError_t run_conv_bias_act3x3(const half_t* x, const half_t* w, const half_t* scale, const half_t* b, int act,
                                 half_t* y, int NB, int H, int W, int C, int K, hipStream_t st);
 hipError_t run_conv_pool3x3(const half_t* x, const half_t* w, const half_t* scale, const half_t* b, int act,
-                            half_t* y, uint8_t* argmax, int NB, int H, int W, int C, int K, hipStream_t st);
+                            bool avg, half_t* y, uint8_t* argmax, int NB, int H, int W, int C, int K, hipStream_t st);
 hipError_t run_chain_conv2_3x3(const half_t* x, const half_t* w0, const half_t* b0, int act, const half_t* w1,
                                const half_t* b1, half_t* y, int NB, int H, int W, int C, int K0, int K1,
                                hipStream_t st);
@@ -23,7 +23,8 @@ hipError_t run_chain_convN_3x3(const half_t* x, int nst, const half_t* const* w,
                                const int* act, const int* widths, half_t* y, int NB, int H, int W, int C,
                                hipStream_t st);
 bool gemmn_fits(int nst, const int* widths);
-hipError_t run_maxpool2x2(const half_t* v, half_t* y, uint8_t* am, int NB, int P, int Q, int K, hipStream_t st);
+hipError_t run_pool2x2(bool avg, const half_t* v, half_t* y, uint8_t* am, int NB, int P, int Q, int K,
+                       hipStream_t st);
 hipError_t run_pad_mid(const half_t* src, half_t* dst, long outer, int c_in, int c_out, int inner, hipStream_t st);
 bool convw_fits(int C, int K);
 }  // namespace fc
@@ -316,8 +317,8 @@ static fc_status conv_pool_impl(const char* name, const fc_half* x, const fc_hal
 {
     fc_status s = check_act(act);
     if (s != FC_OK) return s;
-    if ((int)pool < 0 || (int)pool > 1) return fail(FC_E_ARG, "pool %d out of range", (int)pool);
-    if (pool == FC_POOL_NONE && argmax) return fail(FC_E_ARG, "argmax needs a pool");
+    if ((int)pool < 0 || (int)pool > 2) return fail(FC_E_ARG, "pool %d out of range", (int)pool);
+    if (pool != FC_POOL_MAX_2X2_S2 && argmax) return fail(FC_E_ARG, "argmax needs the max pool");
     s = check_conv(shape, 128);
     if (s != FC_OK) return s;
     const long npix = (long)shape->n * shape->h * shape->w;
@@ -332,8 +333,8 @@ static fc_status conv_pool_impl(const char* name, const fc_half* x, const fc_hal
         return hip_status(fc::run_conv_bias_act3x3(H(x), H(w), H(scale), H(b), act, Hm(y), shape->n, shape->h,
                                                     shape->w, shape->c, shape->k, st),
                           name);
-    return hip_status(fc::run_conv_pool3x3(H(x), H(w), H(scale), H(b), act, Hm(y), argmax, shape->n, shape->h,
-                                           shape->w, shape->c, shape->k, st),
+    return hip_status(fc::run_conv_pool3x3(H(x), H(w), H(scale), H(b), act, pool == FC_POOL_AVG_2X2_S2, Hm(y),
+                                           argmax, shape->n, shape->h, shape->w, shape->c, shape->k, st),
                       name);
 }
 
@@ -425,7 +426,17 @@ fc_status maxpool2x2(const fc_half* x, fc_half* y, uint8_t* argmax, int32_t n, i
     if (nout == 0) return ok();
     if (!aligned16(x) || !aligned16(y) || ((uintptr_t)argmax & 7u))
         return fail(FC_E_ALIGN, "x, y 16-byte and argmax 8-byte aligned");
-    return hip_status(fc::run_maxpool2x2(H(x), Hm(y), argmax, n, h, w, c, (hipStream_t)stream), "maxpool2x2");
+    return hip_status(fc::run_pool2x2(false, H(x), Hm(y), argmax, n, h, w, c, (hipStream_t)stream), "maxpool2x2");
+}
+
+fc_status avgpool2x2(const fc_half* x, fc_half* y, int32_t n, int32_t h, int32_t w, int32_t c, void* stream)
+{
+    if (n < 0 || h < 0 || w < 0 || c <= 0 || c % 8) return fail(FC_E_SHAPE, "bad pool shape");
+    const long nout = (long)n * (h / 2) * (w / 2);
+    if (nout > 0 && (!x || !y)) return fail(FC_E_NULL, "x and y are required");
+    if (nout == 0) return ok();
+    if (!aligned16(x) || !aligned16(y)) return fail(FC_E_ALIGN, "x and y must be 16-byte aligned");
+    return hip_status(fc::run_pool2x2(true, H(x), Hm(y), nullptr, n, h, w, c, (hipStream_t)stream), "avgpool2x2");
 }
 
 fc_status pad_channels(const fc_half* src, fc_half* dst, int64_t outer, int32_t c_in, int32_t c_out, int32_t inner,

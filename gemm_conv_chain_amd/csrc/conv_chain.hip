@@ -6,8 +6,9 @@
 //   conv3x3 -> bias -> ReLU -> 2x2/2 max pool (Welder's Conv+ReLU+MaxPool
 //   tile graph):  k_conv_w<NTK, EPI_POOL>; the conv output tile never leaves
 //   the VGPRs: the pool is a partial reduction of 4 accumulator registers.
+//   the same with a 2x2/2 average instead of the maximum: k_conv_w<NTK, EPI_AVG>.
 //   conv3x3 -> bias -> act, stored (unfused baseline): k_conv_w<NTK, EPI_STORE>.
-//   2x2/2 max pool of a stored tensor (unfused baseline): k_maxpool2x2.
+//   2x2/2 max or average pool of a stored tensor (unfused baselines): k_pool2x2.
 //   channel zero-padding (input preparation): k_pad_mid.
 //
 // Implicit GEMM (interview page, "Conv optimisation" item 2): the GEMM view is
@@ -123,7 +124,9 @@ struct Conv3x3Rows {
 };
 
 // ------------------------------------------- weights-resident conv kernel
-enum { EPI_STORE = 0, EPI_POOL = 1 };
+enum { EPI_STORE = 0, EPI_POOL = 1, EPI_AVG = 2 };
+// the pooling epilogues enumerate GEMM rows window-major
+__host__ __device__ constexpr bool epi_pools(int e) { return e != EPI_STORE; }
 
 // With the chunk count known at compile time: CONVW_WPS waves per SIMD
 // (4 * CONVW_WPS per block, 512 / CONVW_WPS registers each) and a register
@@ -206,7 +209,7 @@ void k_conv_w(ConvWArgs a)
     const long t_begin = (long)xcd_block(blockIdx.x, gridDim.x) * a.tiles_per_block;
     const long t_end = min(t_begin + a.tiles_per_block, a.ntiles);
     const int nch = KCH ? KCH : a.Kp >> 6;
-    const long nrows = EPI == EPI_POOL ? (long)a.NB * (a.H >> 1) * (a.W >> 1) * 4 : (long)a.NB * a.H * a.W;
+    const long nrows = epi_pools(EPI) ? (long)a.NB * (a.H >> 1) * (a.W >> 1) * 4 : (long)a.NB * a.H * a.W;
 
     Conv3x3Rows ld;
     ld.x = a.x; ld.H = a.H; ld.W = a.W; ld.C = a.C; ld.M = (long)a.NB * a.H * a.W;
@@ -217,7 +220,7 @@ void k_conv_w(ConvWArgs a)
         const bool ok = gr < nrows;
         const unsigned g = ok ? (unsigned)gr : 0u;
         unsigned n, p, q;
-        if (EPI == EPI_POOL) {
+        if (epi_pools(EPI)) {
             const unsigned win = g >> 2, e = g & 3u;
             n = a.fa.div(win);
             const unsigned rem = win - n * a.fa.d;
@@ -274,7 +277,7 @@ void k_conv_w(ConvWArgs a)
         QRows r;
         r.bits = 0;
         const int qi = lane_id_here() >> 2;   // recomputed per tile, not held across the main loop
-        if (EPI == EPI_POOL) {
+        if (epi_pools(EPI)) {
             const long wi = tl * 16 + qi;
             const bool ok = wi < (nrows >> 2);
             const unsigned g = ok ? (unsigned)wi : 0u;
@@ -312,7 +315,7 @@ void k_conv_w(ConvWArgs a)
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj) {
             const bool ok = (r.bits >> (6 * jj + rr)) & (r.bits >> (6 * jj + 3 + ss)) & 1u;
-            const int off = EPI == EPI_POOL ? ((jj >> 1) * w + (jj & 1)) * 64 : jj * 64;
+            const int off = epi_pools(EPI) ? ((jj >> 1) * w + (jj & 1)) * 64 : jj * 64;
             const half_t* p = r.base + (delta + off);
 #pragma unroll
             for (int h = 0; h < 2; ++h) A[h][jj] = ld16_if(p + 32 * h, ok);
@@ -376,7 +379,7 @@ void k_conv_w(ConvWArgs a)
         const lds_float* const ssl = ss + lr;
         const lds_half8* const orb = reinterpret_cast<const lds_half8*>(ost + rr * 32 + 8 * grp);
         act_dispatch(a.act, [&](auto act) {
-            if (EPI == EPI_POOL) {
+            if (epi_pools(EPI)) {
                 // windows are enumerated like y's pixels
                 const long win0 = row0 >> 2;
                 half_t* yb = a.y + win0 * K;
@@ -396,7 +399,7 @@ void k_conv_w(ConvWArgs a)
                 const lds_half8* const srd = reinterpret_cast<const lds_half8*>(ost + sr * KP + 8 * sg);
                 // argmax (first maximum of the rounded values) is only needed
                 // with an argmax output or an activation that is not monotone
-                const bool fast = decltype(act)::monotone && !ab;
+                const bool fast = EPI == EPI_POOL && decltype(act)::monotone && !ab;
                 const int olane = hh * K + lr;
                 int nwl = nw - hh;   // window 8u + 2g + hh is valid iff 8u + 2g < nwl
                 asm volatile("" : "+v"(nwl));   // (opaque: compared against constants, not folded back)
@@ -426,6 +429,14 @@ void k_conv_w(ConvWArgs a)
                                 const float lo = __builtin_fminf(__builtin_fminf(c[4 * g], c[4 * g + 1]),
                                                                  __builtin_fminf(c[4 * g + 2], c[4 * g + 3]));
                                 best = (half_t)act.f(__builtin_fmaf(sk >= 0.0f ? hi : lo, sk, bk));
+                            } else if (EPI == EPI_AVG) {
+                                // mean of the four rounded fp16 values (fp32 sum,
+                                // an exact quarter), rounded once to fp16
+                                float sum = 0.0f;
+#pragma unroll
+                                for (int e = 0; e < 4; ++e)
+                                    sum += (float)(half_t)act.f(__builtin_fmaf(c[4 * g + e], sk, bk));
+                                best = (half_t)(sum * 0.25f);
                             } else {
                                 // decided on the rounded fp16 intermediate, first
                                 // maximum in window order (0,0),(0,1),(1,0),(1,1)
@@ -685,7 +696,7 @@ hipError_t run_conv_bias_act3x3(const half_t* x, const half_t* w, const half_t* 
 }
 
 hipError_t run_conv_pool3x3(const half_t* x, const half_t* w, const half_t* scale, const half_t* b, int act,
-                            half_t* y, uint8_t* argmax, int NB, int H, int W, int C, int K, hipStream_t st)
+                            bool avg, half_t* y, uint8_t* argmax, int NB, int H, int W, int C, int K, hipStream_t st)
 {
     ConvWArgs a;
     a.x = x; a.w = w; a.s = scale; a.b = b; a.y = y; a.argmax = argmax;
@@ -697,7 +708,7 @@ hipError_t run_conv_pool3x3(const half_t* x, const half_t* w, const half_t* scal
     a.fa = FastDiv::make((unsigned)(H / 2) * (unsigned)(W / 2));
     a.fb = FastDiv::make((unsigned)(W / 2));
     a.fc16 = FastDiv::make((unsigned)C / 16);
-    return launch_convw<EPI_POOL>(a, st);
+    return avg ? launch_convw<EPI_AVG>(a, st) : launch_convw<EPI_POOL>(a, st);
 }
 
 hipError_t run_chain_conv2_3x3(const half_t* x, const half_t* w0, const half_t* b0, int act, const half_t* w1,
@@ -753,8 +764,9 @@ hipError_t run_chain_convN_3x3(const half_t* x, int nst, const half_t* const* w,
 
 // ------------------------------------------------------------ max pool 2x2/2
 // One thread: one output pixel x 8 channels (16-byte loads of the 4 inputs).
-__global__ __launch_bounds__(256) void k_maxpool2x2(const half_t* __restrict__ v, half_t* __restrict__ y,
-                                                    uint8_t* __restrict__ am, int NB, int P, int Q, int K)
+template <bool AVG>
+__global__ __launch_bounds__(256) void k_pool2x2(const half_t* __restrict__ v, half_t* __restrict__ y,
+                                                 uint8_t* __restrict__ am, int NB, int P, int Q, int K)
 {
     const int PO = P >> 1, QO = Q >> 1, KB = K >> 3;
     const long total = (long)NB * PO * QO * KB;
@@ -772,6 +784,14 @@ __global__ __launch_bounds__(256) void k_maxpool2x2(const half_t* __restrict__ v
             in[e] = ld16(v + (((long)n * P + p) * Q + q) * K + 8 * kb);
         }
         half8 o;
+        if (AVG) {
+            // mean of the four fp16 values (fp32 sum, exact quarter), one rounding
+#pragma unroll
+            for (int c = 0; c < 8; ++c)
+                o[c] = (half_t)((((float)in[0][c] + (float)in[1][c]) + (float)in[2][c] + (float)in[3][c]) * 0.25f);
+            *reinterpret_cast<half8*>(y + pix * K + 8 * kb) = o;
+            continue;
+        }
         uint8_t ai[8];
 #pragma unroll
         for (int c = 0; c < 8; ++c) {
@@ -795,13 +815,17 @@ __global__ __launch_bounds__(256) void k_maxpool2x2(const half_t* __restrict__ v
     }
 }
 
-hipError_t run_maxpool2x2(const half_t* v, half_t* y, uint8_t* am, int NB, int P, int Q, int K, hipStream_t st)
+hipError_t run_pool2x2(bool avg, const half_t* v, half_t* y, uint8_t* am, int NB, int P, int Q, int K,
+                       hipStream_t st)
 {
     const long total = (long)NB * (P / 2) * (Q / 2) * (K / 8);
     if (total == 0) return hipSuccess;
     long blocks = (total + 255) / 256;
     if (blocks > 65536) blocks = 65536;
-    hipLaunchKernelGGL(k_maxpool2x2, dim3((unsigned)blocks), dim3(256), 0, st, v, y, am, NB, P, Q, K);
+    if (avg)
+        hipLaunchKernelGGL(k_pool2x2<true>, dim3((unsigned)blocks), dim3(256), 0, st, v, y, nullptr, NB, P, Q, K);
+    else
+        hipLaunchKernelGGL(k_pool2x2<false>, dim3((unsigned)blocks), dim3(256), 0, st, v, y, am, NB, P, Q, K);
     return hipGetLastError();
 }
 

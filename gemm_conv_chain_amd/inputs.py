@@ -145,6 +145,8 @@ WORKLOADS = {
     "conv3x3_bn_relu_maxpool": dict(kind="conv_pool", bn=True, n=32, h=112, w=112, c=60, cpad=64, k=128, act="relu",
                                     desc="NHWC x[32,112,112,60->64] conv3x3 60->128 x scale + shift (batch norm) "
                                          "+ReLU -> maxpool2x2"),
+    "conv3x3_relu_avgpool": dict(kind="conv_pool", pool="avg2x2", n=32, h=112, w=112, c=60, cpad=64, k=128,
+                                 act="relu", desc="NHWC x[32,112,112,60->64] conv3x3 60->128 +b+ReLU -> avgpool2x2"),
     "conv3x3_relu_maxpool": dict(kind="conv_pool", n=32, h=112, w=112, c=60, cpad=64, k=128, act="relu",
                                  desc="NHWC x[32,112,112,60->64] conv3x3 60->128 +b+ReLU -> maxpool2x2"),
 }

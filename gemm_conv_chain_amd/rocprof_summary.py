@@ -114,7 +114,7 @@ def pmc(d, workload, json_path=None):
         fused = {"b2b_gemm_tiny": "k_chain_rf", "b2b_gemm_rf": "k_chain_rf", "b2b_gemm_lds": "k_gemm_lds<4, true",
                  "b2b_gemm_lds@stream": "k_chain_stream", "gemm3_rf": "k_chain_rf",
                  "conv3x3_conv1x1": "k_chain_rf", "conv3x3_conv1x1x2": "k_chain_rf", "conv3x3_relu_maxpool": "k_conv_w<4, 1",
-                 "conv3x3_bn_relu_maxpool": "k_conv_w<4, 1"}[workload]
+                 "conv3x3_bn_relu_maxpool": "k_conv_w<4, 1", "conv3x3_relu_avgpool": "k_conv_w<4, 2"}[workload]
         fk = [k for k in fetch if fused in k]
         if len(fk) != 1:
             raise SystemExit("cannot identify the fused kernel among %s" % list(fetch))

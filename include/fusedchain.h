@@ -69,7 +69,11 @@ typedef enum {
  * x * min(max(x + 3, 0), 6) / 6 (BOLT notes, "Enabling deeper operator
  * fusion": Conv2D + BiasAdd + Hardswish in one kernel). */
 typedef enum { FC_ACT_NONE = 0, FC_ACT_RELU = 1, FC_ACT_GELU_TANH = 2, FC_ACT_HARDSWISH = 3 } fc_act;
-typedef enum { FC_POOL_NONE = 0, FC_POOL_MAX_2X2_S2 = 1 } fc_pool;
+/* 2x2 stride-2 pooling of the conv output in registers: the maximum (Welder
+ * notes, Conv+ReLU+MaxPool), or the average -- another partial reduction in
+ * the epilogue (BOLT notes, "Prerequisite: Epilogue fusion"): the mean of the
+ * window's four fp16-rounded values, rounded once to fp16. */
+typedef enum { FC_POOL_NONE = 0, FC_POOL_MAX_2X2_S2 = 1, FC_POOL_AVG_2X2_S2 = 2 } fc_pool;
 typedef enum { FC_VARIANT_AUTO = 0, FC_VARIANT_RF = 1, FC_VARIANT_LDS = 2, FC_VARIANT_STREAM = 3 } fc_variant;
 
 /* x NHWC [n,h,w,c]; w HWIO [r,s,c,k]; output spatial size
@@ -173,6 +177,8 @@ fc_status chain_gemmN(const fc_half *A, int32_t nstages, const fc_half *const *W
  *   pool == FC_POOL_MAX_2X2_S2: y [n, P/2, Q/2, k] (floor), argmax (nullable,
  *   uint8 [n, P/2, Q/2, k]) = 2*dy + dx of the first maximum in the order
  *   (0,0),(0,1),(1,0),(1,1), decided on the fp16-rounded values;
+ *   pool == FC_POOL_AVG_2X2_S2: y [n, P/2, Q/2, k] = fp16 of the mean of each
+ *   window's four fp16 values (argmax must be NULL);
  *   pool == FC_POOL_NONE: y [n, P, Q, k] = act(conv + b) (argmax must be NULL).
  * Implemented shapes: r = s = 3, stride 1, pad 1, c % 32 == 0 (pad channels
  * with pad_channels first), k % 8 == 0 and k <= 128 (all output channels in
@@ -248,6 +254,12 @@ fc_status conv_bias_act(const fc_half *x, const fc_half *w, const fc_half *b, fc
  * argmax nullable (8-byte aligned), encoded as in chain_conv_pool. */
 fc_status maxpool2x2(const fc_half *x, fc_half *y, uint8_t *argmax, int32_t n, int32_t h, int32_t w, int32_t c,
                      void *stream);
+
+/* y [n, h/2, w/2, c] = 2x2 stride-2 average pool of x NHWC [n,h,w,c] (floor):
+ * the mean of each window's four fp16 values, rounded once to fp16 -- the
+ * unfused baseline of FC_POOL_AVG_2X2_S2 (BOLT notes, "Prerequisite: Epilogue
+ * fusion").  c % 8 == 0; x and y 16-byte aligned. */
+fc_status avgpool2x2(const fc_half *x, fc_half *y, int32_t n, int32_t h, int32_t w, int32_t c, void *stream);
 
 /* ---- input preparation (BOLT notes, "Templated code generation": tensors
  *      whose channel count is not a multiple of 8 are zero-padded) ----

@@ -103,7 +103,7 @@ def test_conv_validation(L):
     assert L.chain_conv_pool(P, P, NUL, 1, 1, P2, ctypes.byref(shape(k=136)), NUL, None) == E_UNSUP
     assert L.chain_conv_pool(P, P, NUL, 1, 1, P2, ctypes.byref(shape(r=5, s=5)), NUL, None) == E_UNSUP
     assert L.chain_conv_pool(P, P, NUL, 1, 1, P2, ctypes.byref(shape(stride=2)), NUL, None) == E_UNSUP
-    assert L.chain_conv_pool(P, P, NUL, 1, 2, P2, ctypes.byref(sh), NUL, None) == E_ARG
+    assert L.chain_conv_pool(P, P, NUL, 1, 3, P2, ctypes.byref(sh), NUL, None) == E_ARG   # pool kinds are 0..2
     assert L.chain_conv_pool(P, P, NUL, 1, 0, P2, ctypes.byref(sh), P, None) == E_ARG  # argmax needs a pool
     assert L.chain_conv_pool(BAD, P, NUL, 1, 1, P2, ctypes.byref(sh), NUL, None) == E_ALIGN
     assert L.conv_bias_act(P, P, NUL, 1, P2, ctypes.byref(shape(h=-1)), None) == E_SHAPE
@@ -209,7 +209,7 @@ def test_chain_conv_bn_pool_validation(L):
     assert bn(shift=BAD) == E_ALIGN
     assert bn(w=NUL) == E_NULL
     assert bn(act=5) == E_ARG
-    assert bn(pool=2) == E_ARG
+    assert bn(pool=3) == E_ARG
     assert bn(pool=0, am=P) == E_ARG           # argmax needs a pool
     assert bn(shape=fc.ConvShape(1, 8, 8, 64, 136, 3, 3, 1, 1)) == E_UNSUP
 
@@ -240,3 +240,11 @@ def test_probe_validation(L):
     assert L.fc_probe_mfma(3, 16, P, P2, 256, C.byref(b), None) == E_SHAPE     # 1 or 2 waves per SIMD
     assert L.fc_probe_mfma(2, 0, P, P2, 256, C.byref(b), None) == E_SHAPE
     assert L.fc_probe_mfma(2, 16, C.c_void_p(0x10004), P2, 256, C.byref(b), None) == E_ALIGN
+
+
+def test_avg_pool_validation(L):
+    import ctypes as C
+    sh = fc.ConvShape(1, 8, 8, 64, 64, 3, 3, 1, 1)
+    assert L.chain_conv_pool(P, P, NUL, 1, 2, P2, C.byref(sh), P, None) == E_ARG    # argmax only with the max pool
+    assert L.chain_conv_pool(P, P, NUL, 1, 3, P2, C.byref(sh), NUL, None) == E_ARG
+    assert L.chain_conv_bn_pool(P, P, P, NUL, 1, 2, P2, C.byref(sh), P, None) == E_ARG

@@ -314,3 +314,48 @@ def test_conv_bn_pool_full_size_sampled(fc):
     for img in (0, 31):
         di = dict(d, x=d["x"][img:img + 1])
         check_bn_pool(y[img:img + 1], am[img:img + 1], di, "relu", "full bn img %d" % img)
+
+
+@pytest.mark.parametrize("n,h,w,c,k,act", [(2, 8, 10, 64, 128, "relu"), (1, 9, 7, 32, 64, "gelu_tanh"),
+                                           (3, 30, 34, 64, 128, "none")])
+def test_conv_avgpool(fc, n, h, w, c, k, act):
+    # the 2x2 average of the rounded conv output (many tiles and a ragged last
+    # tile in the third case, the runtime-chunk path in the second)
+    d = inputs.conv_pool_inputs(n, h, w, c, k, seed=7 * n + h)
+    print("case conv_avgpool", n, h, w, c, k, act, flush=True)
+    y = to_np(fc.chain_conv_pool(dev(d["x"]), dev(d["w"]), dev(d["b"]), act=act, pool="avg2x2"))
+    yo, _ = oracle.chain_conv_avgpool(d["x"], d["w"], d["b"], ACTS[act])
+    assert_close(y, yo.astype(np.float64), "conv_avgpool")
+
+
+def test_conv_bn_avgpool(fc):
+    d = inputs.conv_bn_pool_inputs(2, 12, 14, 64, 96, seed=9)
+    print("case conv_bn_avgpool", flush=True)
+    y = to_np(fc.chain_conv_bn_pool(dev(d["x"]), dev(d["w"]), dev(d["scale"]), dev(d["shift"]), act="relu",
+                                    pool="avg2x2"))
+    yo, _ = oracle.chain_conv_avgpool(d["x"], d["w"], d["shift"], oracle.ACT_RELU, scale=d["scale"])
+    assert_close(y, yo.astype(np.float64), "conv_bn_avgpool")
+
+
+@pytest.mark.slow
+def test_conv_avgpool_full_size_sampled(fc):
+    spec, d = inputs.workload("conv3x3_relu_avgpool")
+    print("case full conv3x3_relu_avgpool", flush=True)
+    x = fc.pad_channels(dev(d["x"]), 64)
+    w = fc.pad_weight_channels(dev(d["w"]), 64)
+    y = to_np(fc.chain_conv_pool(x, w, dev(d["b"]), act="relu", pool="avg2x2"))   # the launch the bench times
+    assert np.all(np.isfinite(y.astype(np.float64)))
+    for img in (0, 31):
+        yo, _ = oracle.chain_conv_avgpool(d["x"][img:img + 1], d["w"], d["b"], oracle.ACT_RELU)
+        assert_close(y[img:img + 1], yo.astype(np.float64), "full avg img %d" % img)
+
+
+def test_avgpool2x2(fc):
+    # the unfused baseline's pool kernel (odd sizes floor)
+    rng = np.random.default_rng(1)
+    v = rng.standard_normal((2, 7, 9, 24)).astype(np.float16)
+    print("case avgpool2x2", flush=True)
+    y = to_np(fc.avgpool2x2(dev(v)))
+    yo = oracle.avgpool2x2(v)
+    assert y.shape == yo.shape
+    assert_close(y, yo.astype(np.float64), "avgpool2x2")
