@@ -248,3 +248,16 @@ def test_avg_pool_validation(L):
     assert L.chain_conv_pool(P, P, NUL, 1, 2, P2, C.byref(sh), P, None) == E_ARG    # argmax only with the max pool
     assert L.chain_conv_pool(P, P, NUL, 1, 3, P2, C.byref(sh), NUL, None) == E_ARG
     assert L.chain_conv_bn_pool(P, P, P, NUL, 1, 2, P2, C.byref(sh), P, None) == E_ARG
+
+
+def test_residence_limits(L):
+    # the register-resident chain holds W0 and W1 in LDS: K0 = 320 fits with
+    # N0 = N1 = 128, K0 = 384 does not (auto then streams the weights); the conv
+    # holds all 3x3 weights: c = 128 fits with k = 64, not with k = 72
+    fc.tune_clear()
+    assert fc.auto_variant(300, 320, 128, 128) == "rf"
+    assert fc.auto_variant(300, 384, 128, 128) == "stream"
+    assert g2(L, M=300, K0=384, N0=128, N1=128, variant=1) == E_UNSUP
+    import ctypes as C
+    assert L.chain_conv_pool(P, P, NUL, 1, 1, P2, C.byref(fc.ConvShape(1, 6, 10, 128, 72, 3, 3, 1, 1)), NUL,
+                             None) == E_UNSUP

@@ -62,7 +62,8 @@ def pool_both(fc, x, w, b, act="relu"):
 
 
 @pytest.mark.parametrize("n,h,w,c,k", [(2, 8, 10, 64, 128), (1, 5, 7, 32, 64), (2, 9, 6, 64, 72), (1, 4, 6, 96, 64),
-                                       (1, 12, 12, 64, 8), (3, 3, 17, 32, 32)])
+                                       (1, 12, 12, 64, 8), (3, 3, 17, 32, 32),
+                                       (1, 6, 10, 128, 64)])   # c = 128: the largest weights that fit in LDS with k = 64
 def test_conv_pool_small(fc, n, h, w, c, k):
     d = inputs.conv_pool_inputs(n, h, w, c, k, seed=h * w)
     print("case conv_pool", n, h, w, c, k, flush=True)

@@ -75,6 +75,8 @@ def test_lds_shape_ragged(fc):
     (64, 32, 200, 16, "gelu_tanh", "stream"), (300, 576, 256, 256, "gelu_tanh", "stream"),
     (130, 72, 96, 264, "hardswish", "rf"), (130, 72, 96, 264, "hardswish", "lds"),
     (300, 576, 256, 256, "hardswish", "stream"),
+    # the register-resident limit: K0 = 320 is the largest k with W0, W1 (N0 = N1 = 128) in LDS together
+    (300, 320, 128, 128, "relu", "rf"), (300, 320, 128, 128, "gelu_tanh", "auto"),
 ])
 def test_edge_shapes(fc, M, K0, N0, N1, act, variant):
     d = inputs.gemm2_inputs(M, K0, N0, N1, "normal", seed=M + K0)
