@@ -5,8 +5,13 @@
 
 A step is one pass of the fused chain over one batch of synthetic input (one
 kernel launch: GEMM0 + epilogue + on-chip hand-off + GEMM1 + epilogue, or
-conv + bias + ReLU + pool).  Inputs are resident in HBM before the timed
-region; the step rotates over enough copies of the activations and outputs
+conv + bias + ReLU + pool).  The headline workload (default: conv3x3 + ReLU +
+2x2 max pool on x[32,112,112,60->64], the largest configuration) gives
+`value`; the other configurations -- the tiny and register-resident two-GEMM
+chains, the LDS-resident two-GEMM shape under the LDS-resident kernel, the
+streamed variant and the profiler's choice, and the conv3x3 -> conv1x1 chain --
+are measured in the same run and reported under `configs`.  Inputs are
+resident in HBM before the timed region; the step rotates over enough copies of the activations and outputs
 (> 2x the 256 MiB Infinity Cache) that every step reads its inputs from HBM.
 Timing: HIP events on the stream the kernels run on (torch's current stream).
 
@@ -377,8 +382,10 @@ def cpu_model():
 
 
 def measured_traffic(name, kernel_hash):
-    """HBM bytes per launch from the committed rocprofv3 PMC summary, if it
-    was taken on the current kernel sources; else None."""
+    """HBM bytes per launch from the committed rocprofv3 PMC summary
+    (profiles/traffic.json), if it was taken on the current kernel sources;
+    else None.  These counters come from separate profiling runs, not from
+    this process: the JSON marks them with traffic_source."""
     p = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(p):
         return None
@@ -390,19 +397,102 @@ def measured_traffic(name, kernel_hash):
     return e
 
 
+def roofline(prob, ms_kernel, tr):
+    """Roofline position of one launch of the fused kernel: algorithmic bytes
+    (HBM side of the ridge) or FLOPs (MFMA side) over the event-timed mean
+    launch duration, against MI355X's published peaks."""
+    ai = prob.flops / prob.bytes_fused
+    ksec = ms_kernel * 1e-3
+    traffic = None
+    if tr is not None:
+        traffic = int(tr["fetch_kib"] * tr["fetch_scale"] * 1024 + tr["write_kib"] * tr["write_scale"] * 1024)
+    if ai < RIDGE:
+        achieved = prob.bytes_fused / ksec / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic}
+    else:
+        achieved = prob.flops / ksec / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": round(PEAK_F16_TFLOPS, 1),
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK_F16_TFLOPS, 4), "traffic": traffic}
+    if tr is not None:
+        roof["traffic_source"] = "profiles/traffic.json[%s] (rocprofv3 FETCH_SIZE/WRITE_SIZE, src %s)" % (
+            prob.traffic_key, tr.get("src_hash"))
+        roof["traffic_over_algorithmic"] = round(traffic / prob.bytes_fused, 4)
+        if "mfma_busy_frac" in tr:
+            # rocprofv3 counters of the same kernel (profiled dispatches, which run a little slower)
+            roof["mfma_busy_frac_pmc"] = tr["mfma_busy_frac"]
+    roof.update({"kernel": prob.kernel, "kernel_ms": round(ms_kernel, 5), "flop_per_byte": round(ai, 1),
+                 "algorithmic_bytes": prob.bytes_fused, "algorithmic_flops": prob.flops,
+                 "executed_flops": prob.flops_exec})
+    return roof
+
+
+def measure(torch, fc, prob, steps, warmup, unfused=True, warm=True):
+    """Time the fused step (and the unfused two-kernel baseline); returns the
+    record of one workload."""
+    ms_step, ms_kernel, ms_wall, method = time_steps(torch, prob.step, steps, warmup)
+    log("%s fused:   %.4f ms/step (%s, events), kernel %.4f ms, wall %.4f ms"
+        % (prob.name, ms_step, method, ms_kernel, ms_wall))
+    h = kernel_src_hash()
+    tr = measured_traffic(prob.traffic_key, h)
+    roof = roofline(prob, ms_kernel, tr)
+    roof["timing"] = method
+    if warm and prob.nsets > 1:
+        # secondary: the same launch on one buffer set (inputs warm in the 256 MiB Infinity Cache / L2)
+        warm_ms, _, _, _ = time_steps(torch, lambda i: prob.step(0), steps, 2)
+        roof["warm_cache_kernel_ms"] = round(warm_ms, 5)
+        log("%s fused, warm cache: %.4f ms/step" % (prob.name, warm_ms))
+    un = None
+    if unfused:
+        u_step, _, _, _ = time_steps(torch, prob.step_unfused, max(5, steps // 2), 2)
+        ub = prob.bytes_fused + 2 * prob.bytes_interm
+        un = {"ms_per_step": round(u_step, 5), "algorithmic_bytes": ub,
+              "fused_over_unfused_bytes": round(prob.bytes_fused / ub, 4),
+              "speedup_fused": round(u_step / ms_step, 3)}
+        if tr is not None and "unfused_bytes" in tr and roof["traffic"] is not None:
+            un["profiled_bytes"] = tr["unfused_bytes"]
+            un["profiled_fused_over_unfused"] = round(roof["traffic"] / tr["unfused_bytes"], 4)
+        log("%s unfused: %.4f ms/step -> fused speedup %.2fx" % (prob.name, u_step, u_step / ms_step))
+    tflops = prob.flops / (ms_step * 1e-3) / 1e12
+    return {"ms_per_step": round(ms_step, 5), "tflops": round(tflops, 3),
+            "pct_fp16_mfma_peak": round(100 * tflops / PEAK_F16_TFLOPS, 2), "roofline": roof, "unfused": un,
+            "config": dict(prob.config, cache="cold (rotating %d buffer sets)" % prob.nsets
+                           if prob.nsets > 1 else "warm")}
+
+
+# The other configurations, measured in the same run beside the headline one
+# (one record each; the two-GEMM LDS-resident shape under each kernel variant
+# and under the profiler's choice).
+SIDE_CONFIGS = [("b2b_gemm_tiny", None), ("b2b_gemm_rf", None), ("b2b_gemm_lds", None), ("b2b_gemm_lds", "stream"),
+                ("b2b_gemm_lds", "tuned"), ("conv3x3_conv1x1", None)]
+WORKLOADS = ["b2b_gemm_tiny", "b2b_gemm_rf", "b2b_gemm_lds", "gemm3_rf", "conv3x3_conv1x1", "conv3x3_conv1x1x2",
+             "conv3x3_relu_maxpool", "conv3x3_bn_relu_maxpool", "conv3x3_relu_avgpool"]
+
+
+def tune(fc, prob, name):
+    W0, b0, W1, b1 = prob.W
+    best, times, _ = fc.tune_chain_gemm2(prob.X[0], W0, b0, W1, b1, act=prob.act, out=prob.Y[0], reps=10)
+    log("%s tuned: %s (%s)" % (name, best, ", ".join("%s %.2f us" % kv for kv in sorted(times.items()))))
+    prob.config.update(variant=best, tuned_us={k: round(v, 2) for k, v in times.items()})
+    prob.kernel = {"rf": "k_chain_rf", "lds": "k_gemm_lds", "stream": "k_chain_stream"}[best]
+    prob.traffic_key = name if best == ("lds" if name == "b2b_gemm_lds" else "rf") else name + "@" + best
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="b2b_gemm_rf",
-                    choices=["b2b_gemm_tiny", "b2b_gemm_rf", "b2b_gemm_lds", "gemm3_rf", "conv3x3_conv1x1", "conv3x3_conv1x1x2",
-                             "conv3x3_relu_maxpool", "conv3x3_bn_relu_maxpool", "conv3x3_relu_avgpool"])
+    ap.add_argument("--workload", default="conv3x3_relu_maxpool", choices=WORKLOADS,
+                    help="the headline workload (default: the conv3x3 + ReLU + 2x2 max-pool chain on "
+                         "x[32,112,112,60->64], the largest configuration)")
     ap.add_argument("--variant", choices=["rf", "lds", "stream"], default=None,
                     help="GEMM-chain kernel variant (default: rf, or lds for b2b_gemm_lds)")
     ap.add_argument("--warm", action="store_true", help="reuse one buffer set (cache-warm timing)")
     ap.add_argument("--no-unfused", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="measure only the headline workload (no per-configuration sub-records)")
     ap.add_argument("--tune", action="store_true",
                     help="GEMM-chain workloads: profile the residence variants on the GPU first "
                          "(chain_gemm2_tune) and time the fastest")
@@ -431,30 +521,9 @@ def main():
         if prob.spec["kind"] != "gemm2":
             print("bench.py: --tune applies to the two-GEMM chain workloads", file=sys.stderr)
             sys.exit(2)
-        W0, b0, W1, b1 = prob.W
-        best, times, _ = fc.tune_chain_gemm2(prob.X[0], W0, b0, W1, b1, act=prob.act, out=prob.Y[0], reps=10)
-        log("tuned: %s (%s)" % (best, ", ".join("%s %.2f us" % kv for kv in sorted(times.items()))))
-        prob.config.update(variant=best, tuned_us={k: round(v, 2) for k, v in times.items()})
-        prob.kernel = {"rf": "k_chain_rf", "lds": "k_gemm_lds", "stream": "k_chain_stream"}[best]
-        prob.traffic_key = args.workload if best == ("lds" if args.workload == "b2b_gemm_lds" else "rf") \
-            else args.workload + "@" + best
+        tune(fc, prob, args.workload)
 
-    ms_step, ms_kernel, ms_wall, method = time_steps(torch, prob.step, args.steps, args.warmup)
-    log("fused:   %.4f ms/step (%s, events), kernel %.4f ms, wall %.4f ms" % (ms_step, method, ms_kernel, ms_wall))
-    warm_ms = None
-    if prob.nsets > 1:
-        # secondary: the same launch on one buffer set (inputs warm in the 256 MiB Infinity Cache / L2)
-        warm_ms, _, _, _ = time_steps(torch, lambda i: prob.step(0), args.steps, 2)
-        log("fused, warm cache: %.4f ms/step" % warm_ms)
-
-    unfused = None
-    if not args.no_unfused:
-        u_step, u_kernel, _, _ = time_steps(torch, prob.step_unfused, max(5, args.steps // 2), 2)
-        ub = prob.bytes_fused + 2 * prob.bytes_interm
-        unfused = {"ms_per_step": round(u_step, 5), "algorithmic_bytes": ub,
-                   "fused_over_unfused_bytes": round(prob.bytes_fused / ub, 4),
-                   "speedup_fused": round(u_step / ms_step, 3)}
-        log("unfused: %.4f ms/step -> fused speedup %.2fx" % (u_step, u_step / ms_step))
+    head = measure(torch, fc, prob, args.steps, args.warmup, unfused=not args.no_unfused)
 
     if args.calib_copy:
         src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
@@ -463,35 +532,6 @@ def main():
         torch.cuda.synchronize()
         dst.copy_(src)
         torch.cuda.synchronize()
-
-    tflops = prob.flops / (ms_step * 1e-3) / 1e12
-    ai = prob.flops / prob.bytes_fused
-    ksec = ms_kernel * 1e-3
-    h = kernel_src_hash()
-    tr = measured_traffic(prob.traffic_key, h)
-    traffic = None
-    if tr is not None:
-        traffic = int(tr["fetch_kib"] * tr["fetch_scale"] * 1024 + tr["write_kib"] * tr["write_scale"] * 1024)
-        if unfused is not None and "unfused_bytes" in tr:
-            unfused["measured_bytes"] = tr["unfused_bytes"]
-            unfused["measured_fused_over_unfused"] = round(traffic / tr["unfused_bytes"], 4)
-    if ai < RIDGE:
-        achieved = prob.bytes_fused / ksec / 1e9
-        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic}
-    else:
-        achieved = prob.flops / ksec / 1e12
-        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": round(PEAK_F16_TFLOPS, 1),
-                "unit": "TFLOP/s", "frac": round(achieved / PEAK_F16_TFLOPS, 4), "traffic": traffic}
-    if tr is not None and "mfma_busy_frac" in tr:
-        # rocprofv3 counters of the same kernel (profiled dispatches, which run a little slower)
-        roof["mfma_busy_frac_pmc"] = tr["mfma_busy_frac"]
-    if warm_ms is not None:
-        roof["warm_cache_kernel_ms"] = round(warm_ms, 5)
-    roof.update({"kernel": prob.kernel, "kernel_ms": round(ms_kernel, 5), "timing": method,
-                 "flop_per_byte": round(ai, 1),
-                 "algorithmic_bytes": prob.bytes_fused, "algorithmic_flops": prob.flops,
-                 "executed_flops": prob.flops_exec})
 
     probe = None
     if not args.no_probe:
@@ -503,17 +543,42 @@ def main():
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(prob, args.cpu_seconds)
         log("oracle:  %.5f TFLOP/s on %d threads (%s)" % (cpu["value"], cpu["cores"], cpu["sample"]))
+    host = prob.host
 
+    side = None
+    if not args.no_configs:
+        del prob
+        torch.cuda.empty_cache()
+        side = {}
+        for name, variant in SIDE_CONFIGS:
+            if name == args.workload and variant in (None, args.variant) and not args.tune:
+                continue
+            key = name if variant is None else name + "@" + variant
+            p = Problem(name, cold=not args.warm, variant=None if variant == "tuned" else variant)
+            if variant == "tuned":
+                tune(fc, p, name)
+            rec = measure(torch, fc, p, args.steps, args.warmup, unfused=not args.no_unfused, warm=False)
+            if probe:
+                rec["pct_of_measured_mfma_peak"] = round(100 * rec["tflops"] / probe["tflops"], 2)
+            side[key] = rec
+            del p
+            torch.cuda.empty_cache()
+            if variant == "tuned":
+                fc.tune_clear()
+
+    tflops = head["tflops"]
     out = {
-        "metric": METRIC, "value": round(tflops, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": round(ms_step, 5), "higher_is_better": True, "scaling": "weak",
+        "metric": METRIC, "value": tflops, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": head["ms_per_step"], "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "f16", "accumulate": "f32", "data": "synthetic",
-        "config": dict(prob.config, cache="cold (rotating %d buffer sets)" % prob.nsets if prob.nsets > 1 else "warm"),
-        "pct_fp16_mfma_peak": round(100 * tflops / PEAK_F16_TFLOPS, 2),
+        "config": head["config"],
+        "pct_fp16_mfma_peak": head["pct_fp16_mfma_peak"],
         "pct_of_measured_mfma_peak": round(100 * tflops / probe["tflops"], 2) if probe else None,
         "mfma_probe": probe,
-        "roofline": roof, "unfused": unfused, "cpu_baseline": cpu, "kernel_src": h,
+        "roofline": head["roofline"], "unfused": head["unfused"], "cpu_baseline": cpu,
+        "configs": side, "kernel_src": kernel_src_hash(),
     }
+    del host
     print(json.dumps(out), flush=True)
 
 

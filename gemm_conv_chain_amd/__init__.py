@@ -113,6 +113,10 @@ def _check(fn, status):
 
 
 # ------------------------------------------------------------ tensor helpers
+# The C ABI sees pointers only, so every size the kernels rely on is checked
+# here, against the sizes the inputs imply, before the library is called:
+# shapes, dtypes and contiguity first (ValueError / TypeError, testable with
+# host tensors), then that every tensor is a device tensor on one device.
 def _torch():
     import torch
     return torch
@@ -122,18 +126,45 @@ def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
-def _need(t, name, ndim=None):
+def _ndim(t, name, ndim):
+    """t (may be None) is a tensor with ndim dimensions; returns its shape."""
     torch = _torch()
     if t is None:
-        return
-    if t.dtype != torch.float16:
-        raise TypeError("%s must be float16, got %s" % (name, t.dtype))
-    if not t.is_cuda:
-        raise TypeError("%s must be a device tensor" % name)
-    if not t.is_contiguous():
-        raise ValueError("%s must be contiguous" % name)
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch tensor, got %s" % (name, type(t).__name__))
     if ndim is not None and t.dim() != ndim:
-        raise ValueError("%s must have %d dims, got %s" % (name, ndim, tuple(t.shape)))
+        raise ValueError("%s must have %d dims, got shape %s" % (name, ndim, tuple(t.shape)))
+    return tuple(t.shape)
+
+
+def _validate(items):
+    """items: (tensor or None, name, shape, dtype) with shape a tuple of ints
+    or None (any shape) and dtype None for float16.  Checks every shape,
+    dtype and contiguity, then that all tensors sit on one CUDA device."""
+    torch = _torch()
+    live = []
+    for t, name, shape, dtype in items:
+        if t is None:
+            continue
+        if not isinstance(t, torch.Tensor):
+            raise TypeError("%s must be a torch tensor, got %s" % (name, type(t).__name__))
+        want = torch.float16 if dtype is None else dtype
+        if t.dtype != want:
+            raise TypeError("%s must be %s, got %s" % (name, want, t.dtype))
+        if shape is not None and tuple(t.shape) != tuple(shape):
+            raise ValueError("%s must have shape %s, got %s" % (name, tuple(shape), tuple(t.shape)))
+        if not t.is_contiguous():
+            raise ValueError("%s must be contiguous" % name)
+        live.append((t, name))
+    dev = None
+    for t, name in live:
+        if not t.is_cuda:
+            raise TypeError("%s must be a device tensor" % name)
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError("%s is on %s, the other tensors on %s" % (name, t.device, dev))
 
 
 def _stream(t):
@@ -145,18 +176,30 @@ def _act(a):
     return ACT[a] if isinstance(a, str) else int(a)
 
 
+def _empty(shape, like, dtype=None):
+    torch = _torch()
+    return torch.empty(shape, dtype=like.dtype if dtype is None else dtype, device=like.device)
+
+
+def _gemm2_shapes(A, W0, b0, W1, b1, out):
+    M, K0 = _ndim(A, "A", 2)
+    K0w, N0 = _ndim(W0, "W0", 2)
+    N0w, N1 = _ndim(W1, "W1", 2)
+    if K0w != K0 or N0w != N0:
+        raise ValueError("shape mismatch A%s W0%s W1%s" % (tuple(A.shape), tuple(W0.shape), tuple(W1.shape)))
+    if out is None:
+        _validate([(A, "A", None, None), (W0, "W0", None, None), (b0, "b0", (N0,), None), (W1, "W1", None, None),
+                   (b1, "b1", (N1,), None)])
+        out = _empty((M, N1), A)
+    _validate([(A, "A", None, None), (W0, "W0", None, None), (b0, "b0", (N0,), None), (W1, "W1", None, None),
+               (b1, "b1", (N1,), None), (out, "out", (M, N1), None)])
+    return M, K0, N0, N1, out
+
+
 # ------------------------------------------------------------ entry points
 def chain_gemm2(A, W0, b0, W1, b1, act="relu", out=None, variant="auto"):
     """D1 [M, N1] = act(A [M,K0] @ W0 [K0,N0] + b0) @ W1 [N0,N1] + b1 (fp16)."""
-    for t, n, d in ((A, "A", 2), (W0, "W0", 2), (W1, "W1", 2), (b0, "b0", 1), (b1, "b1", 1)):
-        _need(t, n, d)
-    M, K0 = A.shape
-    N0, N1 = W0.shape[1], W1.shape[1]
-    if W0.shape[0] != K0 or W1.shape[0] != N0:
-        raise ValueError("shape mismatch A%s W0%s W1%s" % (tuple(A.shape), tuple(W0.shape), tuple(W1.shape)))
-    if out is None:
-        out = _torch().empty((M, N1), dtype=A.dtype, device=A.device)
-    _need(out, "out", 2)
+    M, K0, N0, N1, out = _gemm2_shapes(A, W0, b0, W1, b1, out)
     v = VARIANT[variant] if isinstance(variant, str) else int(variant)
     _check("chain_gemm2", lib().chain_gemm2_variant(_ptr(A), _ptr(W0), _ptr(b0), _act(act), _ptr(W1), _ptr(b1),
                                                     _ptr(out), M, K0, N0, N1, v, _stream(A)))
@@ -170,15 +213,7 @@ def tune_chain_gemm2(A, W0, b0, W1, b1, act="relu", out=None, reps=20):
     """Time every applicable variant of chain_gemm2 on these tensors (blocking),
     cache the fastest for this shape (later variant='auto' calls use it).
     Returns (best variant name, {variant name: us per launch}, out)."""
-    for t, n, d in ((A, "A", 2), (W0, "W0", 2), (W1, "W1", 2), (b0, "b0", 1), (b1, "b1", 1)):
-        _need(t, n, d)
-    M, K0 = A.shape
-    N0, N1 = W0.shape[1], W1.shape[1]
-    if W0.shape[0] != K0 or W1.shape[0] != N0:
-        raise ValueError("shape mismatch A%s W0%s W1%s" % (tuple(A.shape), tuple(W0.shape), tuple(W1.shape)))
-    if out is None:
-        out = _torch().empty((M, N1), dtype=A.dtype, device=A.device)
-    _need(out, "out", 2)
+    M, K0, N0, N1, out = _gemm2_shapes(A, W0, b0, W1, b1, out)
     best = ctypes.c_int(-1)
     us = (ctypes.c_float * 4)()
     _check("chain_gemm2_tune", lib().chain_gemm2_tune(_ptr(A), _ptr(W0), _ptr(b0), _act(act), _ptr(W1), _ptr(b1),
@@ -202,8 +237,7 @@ def probe_mfma(stamps, sink, waves_per_simd=2, iters=2048):
     (checked by the library before launching).  Returns the grid
     size (blocks); FLOPs per launch = blocks * 4 * waves_per_simd * iters * 8 * 32768."""
     torch = _torch()
-    if stamps.dtype != torch.int64 or sink.dtype != torch.float32 or not stamps.is_cuda or not sink.is_cuda:
-        raise TypeError("stamps must be a CUDA int64 tensor and sink a CUDA float32 tensor")
+    _validate([(stamps, "stamps", None, torch.int64), (sink, "sink", None, torch.float32)])
     blocks = _i32(0)
     capacity = min(stamps.numel() // 4, sink.numel())
     _check("fc_probe_mfma", lib().fc_probe_mfma(int(waves_per_simd), int(iters), _ptr(stamps), _ptr(sink),
@@ -222,18 +256,20 @@ def chain_gemmN(A, Ws, bs, acts, out=None):
     n = len(Ws)
     if len(bs) != n or len(acts) != n:
         raise ValueError("Ws, bs and acts must have the same length")
-    _need(A, "A", 2)
-    for i in range(n):
-        _need(Ws[i], "W%d" % i, 2)
-        _need(bs[i], "b%d" % i, 1)
-    M = A.shape[0]
-    widths = [A.shape[1]] + [W.shape[1] for W in Ws]
+    M, K = _ndim(A, "A", 2)
+    widths = [K]
     for i, W in enumerate(Ws):
-        if W.shape[0] != widths[i]:
-            raise ValueError("W%d has %d rows, the previous width is %d" % (i, W.shape[0], widths[i]))
+        r, c = _ndim(W, "W%d" % i, 2)
+        if r != widths[i]:
+            raise ValueError("W%d has %d rows, the previous width is %d" % (i, r, widths[i]))
+        widths.append(c)
+    items = [(A, "A", None, None)]
+    for i in range(n):
+        items += [(Ws[i], "W%d" % i, None, None), (bs[i], "b%d" % i, (widths[i + 1],), None)]
     if out is None:
-        out = _torch().empty((M, widths[-1]), dtype=A.dtype, device=A.device)
-    _need(out, "out", 2)
+        _validate(items)
+        out = _empty((M, widths[-1]), A)
+    _validate(items + [(out, "out", (M, widths[-1]), None)])
     Wp = (_vp * n)(*[W.data_ptr() for W in Ws])
     bp = (_vp * n)(*[None if b is None else b.data_ptr() for b in bs])
     ap = (ctypes.c_int * n)(*[_act(a) for a in acts])
@@ -244,24 +280,41 @@ def chain_gemmN(A, Ws, bs, acts, out=None):
 
 def gemm_bias_act(A, W, b, act="none", out=None):
     """C [M, N] = act(A [M,K] @ W [K,N] + b) (fp16)."""
-    for t, n, d in ((A, "A", 2), (W, "W", 2), (b, "b", 1)):
-        _need(t, n, d)
-    M, K = A.shape
-    N = W.shape[1]
+    M, K = _ndim(A, "A", 2)
+    Kw, N = _ndim(W, "W", 2)
+    if Kw != K:
+        raise ValueError("shape mismatch A%s W%s" % (tuple(A.shape), tuple(W.shape)))
+    items = [(A, "A", None, None), (W, "W", None, None), (b, "b", (N,), None)]
     if out is None:
-        out = _torch().empty((M, N), dtype=A.dtype, device=A.device)
-    _need(out, "out", 2)
+        _validate(items)
+        out = _empty((M, N), A)
+    _validate(items + [(out, "out", (M, N), None)])
     _check("gemm_bias_act", lib().gemm_bias_act(_ptr(A), _ptr(W), _ptr(b), _act(act), _ptr(out), M, K, N,
                                                 _stream(A)))
     return out
 
 
 def _conv_shape(x, w, stride=1, pad=1):
-    n, h, wd, c = x.shape
-    r, s, c2, k = w.shape
+    n, h, wd, c = _ndim(x, "x", 4)
+    r, s, c2, k = _ndim(w, "w", 4)
     if c2 != c:
         raise ValueError("x has %d channels, w expects %d" % (c, c2))
     return ConvShape(n, h, wd, c, k, r, s, stride, pad)
+
+
+def _conv_out_hw(sh):
+    P = (sh.h + 2 * sh.pad - sh.r) // sh.stride + 1
+    Q = (sh.w + 2 * sh.pad - sh.s) // sh.stride + 1
+    return max(P, 0), max(Q, 0)
+
+
+def _argmax_tensor(argmax, oshape, like):
+    """None/False: no argmax; True: allocate one; else the caller's uint8 tensor."""
+    if argmax is True:
+        return _empty(oshape, like, _torch().uint8)
+    if argmax is None or argmax is False:
+        return None
+    return argmax
 
 
 def chain_conv_pool(x, w, b, act="relu", pool="max2x2", out=None, argmax=None):
@@ -273,28 +326,25 @@ def chain_conv_pool(x, w, b, act="relu", pool="max2x2", out=None, argmax=None):
 def chain_conv_bn_pool(x, w, scale, shift, act="relu", pool="max2x2", out=None, argmax=None):
     """y = maxpool2x2(act(conv3x3(x, w) * scale + shift)) per output channel (batch
     norm at inference as a scale and a shift); pool='none' stores act(...)."""
-    _need(scale, "scale", 1)
     if scale is None:
         raise ValueError("scale is required")
     return _conv_pool("chain_conv_bn_pool", x, w, scale, shift, act, pool, out, argmax)
 
 
 def _conv_pool(fn, x, w, scale, b, act, pool, out, argmax):
-    torch = _torch()
-    for t, n, d in ((x, "x", 4), (w, "w", 4), (b, "b", 1)):
-        _need(t, n, d)
     sh = _conv_shape(x, w)
-    P, Q = sh.h, sh.w   # 3x3, stride 1, pad 1
+    P, Q = _conv_out_hw(sh)
     p = POOL[pool] if isinstance(pool, str) else int(pool)
     oshape = (sh.n, P // 2, Q // 2, sh.k) if p else (sh.n, P, Q, sh.k)
+    am = _argmax_tensor(argmax, oshape, x) if argmax is not True else None   # the caller's, checked below
+    items = [(x, "x", None, None), (w, "w", None, None), (b, "b" if scale is None else "shift", (sh.k,), None),
+             (scale, "scale", (sh.k,), None), (am, "argmax", oshape, _torch().uint8)]
     if out is None:
-        out = torch.empty(oshape, dtype=x.dtype, device=x.device)
-    _need(out, "out", 4)
-    am = None
+        _validate(items)
+        out = _empty(oshape, x)
+    _validate(items + [(out, "out", oshape, None)])
     if argmax is True:
-        am = torch.empty(oshape, dtype=torch.uint8, device=x.device)
-    elif argmax is not None and argmax is not False:
-        am = argmax
+        am = _argmax_tensor(True, oshape, x)
     L = lib()
     if scale is None:
         st = L.chain_conv_pool(_ptr(x), _ptr(w), _ptr(b), _act(act), p, _ptr(out), ctypes.byref(sh), _ptr(am),
@@ -308,29 +358,39 @@ def _conv_pool(fn, x, w, scale, b, act, pool, out, argmax):
 
 def conv_bias_act(x, w, b, act="relu", out=None):
     """y NHWC = act(conv3x3(x, w) + b)."""
-    for t, n, d in ((x, "x", 4), (w, "w", 4), (b, "b", 1)):
-        _need(t, n, d)
     sh = _conv_shape(x, w)
+    P, Q = _conv_out_hw(sh)
+    items = [(x, "x", None, None), (w, "w", None, None), (b, "b", (sh.k,), None)]
     if out is None:
-        out = _torch().empty((sh.n, sh.h, sh.w, sh.k), dtype=x.dtype, device=x.device)
-    _need(out, "out", 4)
+        _validate(items)
+        out = _empty((sh.n, P, Q, sh.k), x)
+    _validate(items + [(out, "out", (sh.n, P, Q, sh.k), None)])
     _check("conv_bias_act", lib().conv_bias_act(_ptr(x), _ptr(w), _ptr(b), _act(act), _ptr(out), ctypes.byref(sh),
                                                 _stream(x)))
     return out
 
 
+def _w1x1(t, name, kin):
+    """A 1x1 conv weight: [kin, kout] or [1, 1, kin, kout]; returns kout."""
+    shp = _ndim(t, name, None)
+    if len(shp) == 2 and shp[0] == kin:
+        return shp[1]
+    if len(shp) == 4 and shp[:3] == (1, 1, kin):
+        return shp[3]
+    raise ValueError("%s must be [%d, k] or [1, 1, %d, k], got %s" % (name, kin, kin, shp))
+
+
 def chain_conv2(x, w0, b0, w1, b1, act="relu", out=None):
     """y = conv1x1(act(conv3x3(x, w0) + b0), w1) + b1; w1 is [k0, k1] or [1,1,k0,k1]."""
-    for t, n, d in ((x, "x", 4), (w0, "w0", 4), (b0, "b0", 1), (b1, "b1", 1)):
-        _need(t, n, d)
-    _need(w1, "w1")
     sh = _conv_shape(x, w0)
-    k1 = w1.shape[-1]
-    if w1.numel() != sh.k * k1:
-        raise ValueError("w1 must hold k0 x k1 = %d x %d values" % (sh.k, k1))
+    P, Q = _conv_out_hw(sh)
+    k1 = _w1x1(w1, "w1", sh.k)
+    items = [(x, "x", None, None), (w0, "w0", None, None), (b0, "b0", (sh.k,), None), (w1, "w1", None, None),
+             (b1, "b1", (k1,), None)]
     if out is None:
-        out = _torch().empty((sh.n, sh.h, sh.w, k1), dtype=x.dtype, device=x.device)
-    _need(out, "out", 4)
+        _validate(items)
+        out = _empty((sh.n, P, Q, k1), x)
+    _validate(items + [(out, "out", (sh.n, P, Q, k1), None)])
     _check("chain_conv2", lib().chain_conv2(_ptr(x), _ptr(w0), _ptr(b0), _act(act), _ptr(w1), _ptr(b1), k1,
                                             _ptr(out), ctypes.byref(sh), _stream(x)))
     return out
@@ -343,19 +403,18 @@ def chain_convN(x, ws, bs, acts, out=None):
     n = len(ws)
     if len(bs) != n or len(acts) != n:
         raise ValueError("ws, bs and acts must have the same length")
-    _need(x, "x", 4)
-    _need(ws[0], "w0", 4)
-    for i in range(n):
-        _need(ws[i], "w%d" % i)
-        _need(bs[i], "b%d" % i, 1)
     sh = _conv_shape(x, ws[0])
-    ks = [sh.k] + [int(w.shape[-1]) for w in ws[1:]]
+    P, Q = _conv_out_hw(sh)
+    ks = [sh.k]
     for i in range(1, n):
-        if ws[i].numel() != ks[i - 1] * ks[i]:
-            raise ValueError("w%d must hold %d x %d values" % (i, ks[i - 1], ks[i]))
+        ks.append(_w1x1(ws[i], "w%d" % i, ks[-1]))
+    items = [(x, "x", None, None)]
+    for i in range(n):
+        items += [(ws[i], "w%d" % i, None, None), (bs[i], "b%d" % i, (ks[i],), None)]
     if out is None:
-        out = _torch().empty((sh.n, sh.h, sh.w, ks[-1]), dtype=x.dtype, device=x.device)
-    _need(out, "out", 4)
+        _validate(items)
+        out = _empty((sh.n, P, Q, ks[-1]), x)
+    _validate(items + [(out, "out", (sh.n, P, Q, ks[-1]), None)])
     wp = (_vp * n)(*[w.data_ptr() for w in ws])
     bp = (_vp * n)(*[None if b is None else b.data_ptr() for b in bs])
     ap = (ctypes.c_int * n)(*[_act(a) for a in acts])
@@ -366,33 +425,36 @@ def chain_convN(x, ws, bs, acts, out=None):
 
 def avgpool2x2(x, out=None):
     """y [n, h/2, w/2, c] = 2x2/2 average pool of NHWC x (fp16 mean of each window)."""
-    _need(x, "x", 4)
-    n, h, w, c = x.shape
+    n, h, w, c = _ndim(x, "x", 4)
+    oshape = (n, h // 2, w // 2, c)
     if out is None:
-        out = _torch().empty((n, h // 2, w // 2, c), dtype=x.dtype, device=x.device)
-    _need(out, "out", 4)
+        _validate([(x, "x", None, None)])
+        out = _empty(oshape, x)
+    _validate([(x, "x", None, None), (out, "out", oshape, None)])
     _check("avgpool2x2", lib().avgpool2x2(_ptr(x), _ptr(out), n, h, w, c, _stream(x)))
     return out
 
 
 def maxpool2x2(x, out=None, argmax=None):
     """y [n, h/2, w/2, c] = 2x2/2 max pool of NHWC x (+ optional argmax)."""
-    torch = _torch()
-    _need(x, "x", 4)
-    n, h, w, c = x.shape
+    n, h, w, c = _ndim(x, "x", 4)
     oshape = (n, h // 2, w // 2, c)
+    am = _argmax_tensor(argmax, oshape, x) if argmax is not True else None   # the caller's, checked below
+    items = [(x, "x", None, None), (am, "argmax", oshape, _torch().uint8)]
     if out is None:
-        out = torch.empty(oshape, dtype=x.dtype, device=x.device)
-    _need(out, "out", 4)
-    am = torch.empty(oshape, dtype=torch.uint8, device=x.device) if argmax is True else (
-        argmax if argmax is not None and argmax is not False else None)
+        _validate(items)
+        out = _empty(oshape, x)
+    _validate(items + [(out, "out", oshape, None)])
+    if argmax is True:
+        am = _argmax_tensor(True, oshape, x)
     _check("maxpool2x2", lib().maxpool2x2(_ptr(x), _ptr(out), _ptr(am), n, h, w, c, _stream(x)))
     return (out, am) if am is not None else out
 
 
 def pad_channels(x, c_out):
     """Zero-pad the channels (last dim) of NHWC x to c_out."""
-    _need(x, "x")
+    _ndim(x, "x", None)
+    _validate([(x, "x", None, None)])
     c_in = x.shape[-1]
     out = _torch().empty(tuple(x.shape[:-1]) + (c_out,), dtype=x.dtype, device=x.device)
     _check("pad_channels", lib().pad_channels(_ptr(x), _ptr(out), x.numel() // max(c_in, 1), c_in, c_out, 1,
@@ -402,7 +464,8 @@ def pad_channels(x, c_out):
 
 def pad_weight_channels(w, c_out):
     """Zero-pad the input channels of HWIO w [r,s,c,k] to c_out."""
-    _need(w, "w", 4)
+    _ndim(w, "w", 4)
+    _validate([(w, "w", None, None)])
     r, s, c_in, k = w.shape
     out = _torch().empty((r, s, c_out, k), dtype=w.dtype, device=w.device)
     _check("pad_channels", lib().pad_channels(_ptr(w), _ptr(out), r * s, c_in, c_out, k, _stream(w)))

@@ -81,6 +81,10 @@ fc_status check_conv(const fc_conv_shape* s, int kmax)
     if (s->k > kmax) return fail(FC_E_UNSUPPORTED, "k=%d exceeds the %d output channels one block keeps", s->k, kmax);
     if ((long)s->n * s->h * s->w > 0x7fffffffL)
         return fail(FC_E_UNSUPPORTED, "n*h*w exceeds 2^31 - 1 pixels (pixel indices are 32-bit)");
+    // tap offsets from a pixel (or a pool window's first pixel) to its 3x3
+    // neighbours span less than 2 (w + 2) c elements and are 32-bit
+    if (((long)s->w + 2) * s->c >= (1L << 30))
+        return fail(FC_E_UNSUPPORTED, "(w+2)*c=%ld: 3x3 tap offsets would exceed 32 bits", ((long)s->w + 2) * s->c);
     return FC_OK;
 }
 

@@ -1,10 +1,18 @@
 """Comparison helpers for GPU-vs-oracle parity (test infrastructure)."""
+import json
+import os
+
 import numpy as np
 
 # Tolerance of the fused chains against the fp64 oracle:
 #   max |gpu - ref| <= REL * max |ref| + ABS   over the whole compared tensor.
 REL = 1e-2
 ABS = 1e-3
+
+# Diagnostics of every whole-tensor comparison made in this process (what,
+# elements, max|err|, tolerance, fraction bit-equal to fp16(ref), max fp16-ulp
+# distance); written as JSON lines to $FC_PARITY_DIAG when that is set.
+DIAG = []
 
 
 def to_np(t):
@@ -22,6 +30,50 @@ def assert_close(gpu, ref, what=""):
     tol = REL * float(np.max(np.abs(r))) + ABS
     assert err <= tol, "%s: max|err| %.3e > tol %.3e (max|ref| %.3e)" % (what, err, tol, np.max(np.abs(r)))
     return err
+
+
+def ordered16(h):
+    """fp16 bit patterns -> integers in the order of the values (+0 and -0 both
+    0), so that |ordered16(a) - ordered16(b)| counts the fp16 values between a
+    and b: their distance in units in the last place."""
+    u = np.asarray(h, dtype=np.float16).view(np.uint16).astype(np.int64)
+    mag = u & 0x7FFF
+    return np.where(u & 0x8000, -mag, mag)
+
+
+def diagnostics(gpu16, ref64, ref16=None):
+    """Fraction of GPU outputs bit-equal to the oracle's fp16 rounding of its
+    fp64 result, and the largest distance between the two in fp16 ulps.
+    ref16 (the oracle's own rounding) is computed with the oracle's codec when
+    not given."""
+    g = np.asarray(gpu16, dtype=np.float16)
+    if ref16 is None:
+        import oracle
+        ref16 = oracle.f64_to_f16(np.asarray(ref64, dtype=np.float64))
+    r = np.asarray(ref16, dtype=np.float16)
+    if g.size == 0:
+        return {"elements": 0, "bit_equal_frac": 1.0, "max_ulp": 0}
+    d = np.abs(ordered16(g) - ordered16(r))
+    return {"elements": int(g.size), "bit_equal_frac": float(np.mean(d == 0)), "max_ulp": int(d.max()),
+            "frac_within_1ulp": float(np.mean(d <= 1))}
+
+
+def check_full(gpu16, ref64, what, ref16=None):
+    """Whole-tensor comparison: the tolerance over every element (max|ref|
+    over the whole tensor), plus the bit-equality / ulp diagnostics, printed
+    and recorded."""
+    err = assert_close(gpu16, ref64, what)
+    r = np.asarray(ref64, dtype=np.float64)
+    rec = {"what": what, "max_err": err, "tol": REL * float(np.max(np.abs(r))) + ABS if r.size else ABS}
+    rec.update(diagnostics(gpu16, ref64, ref16))
+    DIAG.append(rec)
+    print("parity %-40s n=%d max|err| %.3e tol %.3e bit-equal %.4f max %d ulp" % (
+        what, rec["elements"], err, rec["tol"], rec["bit_equal_frac"], rec["max_ulp"]), flush=True)
+    path = os.environ.get("FC_PARITY_DIAG")
+    if path:
+        with open(path, "a") as f:
+            f.write(json.dumps(rec) + "\n")
+    return rec
 
 
 def ulp16(x):

@@ -119,6 +119,13 @@ def test_conv_validation(L):
     assert L.chain_conv2(P, P, NUL, 1, P, NUL, 64, P2, ctypes.byref(shape(n=32768, h=256, w=256, k=64)),
                          None) == E_UNSUP
     assert b"2^31" in L.fc_last_error()
+    # 3x3 tap offsets are 32-bit: (w + 2) * c must stay below 2^30 (a very wide row)
+    wide = shape(n=1, h=1, w=(1 << 24), c=64)
+    assert L.chain_conv_pool(P, P, NUL, 1, 1, P2, ctypes.byref(wide), NUL, None) == E_UNSUP
+    assert b"32 bits" in L.fc_last_error()
+    assert L.conv_bias_act(P, P, NUL, 1, P2, ctypes.byref(wide), None) == E_UNSUP
+    assert L.chain_conv2(P, P, NUL, 1, P, NUL, 64, P2, ctypes.byref(shape(n=1, h=1, w=(1 << 24), k=64)), None) == E_UNSUP
+    assert L.chain_conv_pool(P, P, NUL, 1, 1, P2, ctypes.byref(shape(n=1, h=1, w=(1 << 24) - 3)), NUL, None) == OK
 
 
 def test_empty_tensors_may_be_null(L):

@@ -5,7 +5,7 @@ import pytest
 
 import oracle
 from gemm_conv_chain_amd import inputs
-from parity import assert_close, pool_tie_mask, to_np
+from parity import assert_close, check_full, pool_tie_mask, to_np
 
 pytestmark = pytest.mark.gpu
 torch = pytest.importorskip("torch")
@@ -28,10 +28,14 @@ ACTS = {"none": oracle.ACT_NONE, "relu": oracle.ACT_RELU, "gelu_tanh": oracle.AC
         "hardswish": oracle.ACT_HARDSWISH}
 
 
-def check_pool(y, am, x_np, w_np, b_np, what, act="relu"):
-    """y, am from the GPU; oracle on the (unpadded) inputs."""
+def check_pool(y, am, x_np, w_np, b_np, what, act="relu", full=False):
+    """y, am from the GPU; oracle on the (unpadded) inputs.  full: record the
+    whole-tensor diagnostics (y against the oracle's pooled fp16 values)."""
     yo, amo, v, c64 = oracle.chain_conv_pool(x_np, w_np, b_np, ACTS[act], want_conv64=True)
-    assert_close(y, yo.astype(np.float64), what)
+    if full:
+        check_full(y, yo.astype(np.float64), what, ref16=yo)
+    else:
+        assert_close(y, yo.astype(np.float64), what)
     if am is not None:
         ties = pool_tie_mask(c64, c64.shape[1], c64.shape[2])
         free = ~ties
@@ -189,25 +193,28 @@ def test_maxpool2x2(fc):
 
 
 @pytest.mark.slow
-def test_conv_pool_full_size_sampled(fc):
+def test_conv_pool_full_size(fc):
+    """Conv+ReLU+MaxPool at full size, in the launch the bench times (no
+    argmax, pool taken on the accumulators) and with argmax (bit-identical
+    y): every pooled output against the oracle, argmax on every tie-free
+    window."""
     spec, d = inputs.workload("conv3x3_relu_maxpool")
     print("case full conv3x3_relu_maxpool", flush=True)
     x = fc.pad_channels(dev(d["x"]), 64)
     w = fc.pad_weight_channels(dev(d["w"]), 64)
-    y, am = pool_both(fc, x, w, dev(d["b"]))   # without argmax: the launch the bench times
-    assert np.all(np.isfinite(y.astype(np.float64)))
-    for img in (0, 31):
-        check_pool(y[img:img + 1], am[img:img + 1], d["x"][img:img + 1], d["w"], d["b"], "full img %d" % img)
+    y, am = pool_both(fc, x, w, dev(d["b"]))
+    free, ties = check_pool(y, am, d["x"], d["w"], d["b"], "full conv3x3_relu_maxpool", full=True)
+    print("argmax: %d tie-free windows equal, %d tie windows (y only)" % (free, ties), flush=True)
+    assert free > 0.5 * am.size
 
 
 @pytest.mark.slow
-def test_conv2_full_size_sampled(fc):
+def test_conv2_full_size(fc):
     spec, d = inputs.workload("conv3x3_conv1x1")
     print("case full conv3x3_conv1x1", flush=True)
     y = to_np(fc.chain_conv2(*(dev(d[k]) for k in ("x", "w0", "b0", "w1", "b1"))))
-    for img in (0, 17, 31):
-        ref, _ = oracle.chain_conv2(d["x"][img:img + 1], d["w0"], d["b0"], oracle.ACT_RELU, d["w1"], d["b1"])
-        assert_close(y[img:img + 1], ref, "full conv2 img %d" % img)
+    ref, _ = oracle.chain_conv2(d["x"], d["w0"], d["b0"], oracle.ACT_RELU, d["w1"], d["b1"])
+    check_full(y, ref, "full conv3x3_conv1x1")
 
 
 @pytest.mark.parametrize("n,h,w,c,ks,acts", [
@@ -238,19 +245,20 @@ def test_chain_convN_unscaled_zero_bias(fc):
 
 
 @pytest.mark.slow
-def test_convN_full_size_sampled(fc):
+def test_convN_full_size(fc):
     spec, d = inputs.workload("conv3x3_conv1x1x2")
     print("case full conv3x3_conv1x1x2", flush=True)
     y = to_np(fc.chain_convN(dev(d["x"]), [dev(x) for x in d["ws"]], [dev(b) for b in d["bs"]], spec["acts"]))
-    assert np.all(np.isfinite(y.astype(np.float64)))
-    for img in (0, 31):
-        ref = oracle.chain_convN(d["x"][img:img + 1], d["ws"], d["bs"], [ACTS[a] for a in spec["acts"]])
-        assert_close(y[img:img + 1], ref, "full convN img %d" % img)
+    ref = oracle.chain_convN(d["x"], d["ws"], d["bs"], [ACTS[a] for a in spec["acts"]])
+    check_full(y, ref, "full conv3x3_conv1x1x2")
 
 
-def check_bn_pool(y, am, d, act, what):
+def check_bn_pool(y, am, d, act, what, full=False):
     yo, amo, _, c64 = oracle.chain_conv_bn_pool(d["x"], d["w"], d["scale"], d["shift"], ACTS[act], want_conv64=True)
-    assert_close(y, yo.astype(np.float64), what)
+    if full:
+        check_full(y, yo.astype(np.float64), what, ref16=yo)
+    else:
+        assert_close(y, yo.astype(np.float64), what)
     ties = pool_tie_mask(c64, c64.shape[1], c64.shape[2])
     free = ~ties
     assert np.array_equal(am[free], amo[free]), "%s: argmax differs on %d tie-free windows" % (
@@ -301,7 +309,7 @@ def test_conv_bn_unit_scale_equals_bias_path(fc):
 
 
 @pytest.mark.slow
-def test_conv_bn_pool_full_size_sampled(fc):
+def test_conv_bn_pool_full_size(fc):
     spec, d = inputs.workload("conv3x3_bn_relu_maxpool")
     print("case full conv3x3_bn_relu_maxpool", flush=True)
     x = fc.pad_channels(dev(d["x"]), 64)
@@ -311,10 +319,8 @@ def test_conv_bn_pool_full_size_sampled(fc):
     y2, am = fc.chain_conv_bn_pool(x, w, sc, sh, argmax=True)
     torch.cuda.synchronize()
     assert np.array_equal(y.view(np.uint16), to_np(y2).view(np.uint16))
-    am = to_np(am)
-    for img in (0, 31):
-        di = dict(d, x=d["x"][img:img + 1])
-        check_bn_pool(y[img:img + 1], am[img:img + 1], di, "relu", "full bn img %d" % img)
+    free = check_bn_pool(y, to_np(am), d, "relu", "full conv3x3_bn_relu_maxpool", full=True)
+    assert free > 0.5 * y.size
 
 
 @pytest.mark.parametrize("n,h,w,c,k,act", [(2, 8, 10, 64, 128, "relu"), (1, 9, 7, 32, 64, "gelu_tanh"),
@@ -339,16 +345,14 @@ def test_conv_bn_avgpool(fc):
 
 
 @pytest.mark.slow
-def test_conv_avgpool_full_size_sampled(fc):
+def test_conv_avgpool_full_size(fc):
     spec, d = inputs.workload("conv3x3_relu_avgpool")
     print("case full conv3x3_relu_avgpool", flush=True)
     x = fc.pad_channels(dev(d["x"]), 64)
     w = fc.pad_weight_channels(dev(d["w"]), 64)
     y = to_np(fc.chain_conv_pool(x, w, dev(d["b"]), act="relu", pool="avg2x2"))   # the launch the bench times
-    assert np.all(np.isfinite(y.astype(np.float64)))
-    for img in (0, 31):
-        yo, _ = oracle.chain_conv_avgpool(d["x"][img:img + 1], d["w"], d["b"], oracle.ACT_RELU)
-        assert_close(y[img:img + 1], yo.astype(np.float64), "full avg img %d" % img)
+    yo, _ = oracle.chain_conv_avgpool(d["x"], d["w"], d["b"], oracle.ACT_RELU)
+    check_full(y, yo.astype(np.float64), "full conv3x3_relu_avgpool", ref16=yo)
 
 
 def test_avgpool2x2(fc):
