@@ -170,10 +170,13 @@ class Problem:
             self.X = [xp] + [xp.clone() for _ in range(self.nsets - 1)]
             self.Y = [torch.empty((n, h // 2, w // 2, k), dtype=torch.float16, device=dev) for _ in range(self.nsets)]
             self.H = torch.empty((n, h, w, k), dtype=torch.float16, device=dev)
-            self.config = {"workload": name, "x": [n, h, w, c], "channels_padded_to": cp,
+            self.conv_variant = variant or "auto"
+            if variant:
+                self.traffic_key = name + "@" + variant
+            self.config = {"workload": name, "x": [n, h, w, c], "channels_padded_to": cp, "variant": self.conv_variant,
                            "conv": "3x3 s1 p1 %d->%d %s ReLU" % (c, k, "x scale + shift" if self.bn else "+b"),
                            "pool": ("avg" if self.pool == "avg2x2" else "max") + " 2x2 s2"}
-            self.kernel = "k_conv_w"
+            self.kernel = "k_conv_w" if variant == "lds_weights" else "k_conv_pool_wr"
         torch.cuda.synchronize()
 
     def step(self, i):
@@ -192,10 +195,11 @@ class Problem:
             fc.chain_convN(self.X[j], self.W[:n], self.W[n:], self.acts, out=self.Y[j])
         elif self.bn:
             w, sc, sh = self.W
-            fc.chain_conv_bn_pool(self.X[j], w, sc, sh, act="relu", pool="max2x2", out=self.Y[j])
+            fc.chain_conv_bn_pool(self.X[j], w, sc, sh, act="relu", pool="max2x2", out=self.Y[j],
+                                  variant=self.conv_variant)
         else:
             w, b = self.W
-            fc.chain_conv_pool(self.X[j], w, b, act="relu", pool=self.pool, out=self.Y[j])
+            fc.chain_conv_pool(self.X[j], w, b, act="relu", pool=self.pool, out=self.Y[j], variant=self.conv_variant)
 
     def step_unfused(self, i):
         """The two-kernel baseline: the intermediate goes to HBM and back."""
@@ -486,8 +490,9 @@ def main():
     ap.add_argument("--workload", default="conv3x3_relu_maxpool", choices=WORKLOADS,
                     help="the headline workload (default: the conv3x3 + ReLU + 2x2 max-pool chain on "
                          "x[32,112,112,60->64], the largest configuration)")
-    ap.add_argument("--variant", choices=["rf", "lds", "stream"], default=None,
-                    help="GEMM-chain kernel variant (default: rf, or lds for b2b_gemm_lds)")
+    ap.add_argument("--variant", choices=["rf", "lds", "stream", "lds_weights", "reg_weights"], default=None,
+                    help="kernel form: GEMM chains rf / lds / stream (default rf, or lds for b2b_gemm_lds); "
+                         "conv + pool chains lds_weights / reg_weights (default: the library's choice)")
     ap.add_argument("--warm", action="store_true", help="reuse one buffer set (cache-warm timing)")
     ap.add_argument("--no-unfused", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")

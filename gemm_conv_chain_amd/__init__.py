@@ -19,7 +19,7 @@ import ctypes
 import os
 import re
 
-__all__ = ["lib", "FusedChainError", "chain_gemm2", "tune_chain_gemm2", "auto_variant", "tune_clear", "chain_gemmN", "chain_conv_pool", "chain_conv_bn_pool", "chain_conv2", "chain_convN",
+__all__ = ["CONV_VARIANT", "lib", "FusedChainError", "chain_gemm2", "tune_chain_gemm2", "auto_variant", "tune_clear", "chain_gemmN", "chain_conv_pool", "chain_conv_bn_pool", "chain_conv2", "chain_convN",
            "gemm_bias_act", "conv_bias_act", "maxpool2x2", "avgpool2x2", "pad_channels", "pad_weight_channels", "abi_version", "ACT", "VARIANT",
            "LIB_PATH", "HEADER_PATH", "exported_names"]
 
@@ -30,6 +30,7 @@ HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "fusedchain.h")
 ACT = {"none": 0, "relu": 1, "gelu_tanh": 2, "hardswish": 3}
 POOL = {"none": 0, "max2x2": 1, "avg2x2": 2}
 VARIANT = {"auto": 0, "rf": 1, "lds": 2, "stream": 3}
+CONV_VARIANT = {"auto": 0, "lds_weights": 1, "reg_weights": 2}
 
 
 class FusedChainError(RuntimeError):
@@ -79,10 +80,12 @@ def lib():
                                   ctypes.POINTER(ctypes.c_int), ctypes.POINTER(_i32), _vp, _vp]
         L.chain_conv_bn_pool.argtypes = [_vp, _vp, _vp, _vp, ctypes.c_int, ctypes.c_int, _vp,
                                          ctypes.POINTER(ConvShape), _vp, _vp]
+        L.chain_conv_pool_ex.argtypes = [_vp, _vp, _vp, _vp, ctypes.c_int, ctypes.c_int, _vp,
+                                         ctypes.POINTER(ConvShape), _vp, ctypes.c_int, _vp]
         L.fc_probe_mfma.argtypes = [_i32, _i32, _vp, _vp, _i32, ctypes.POINTER(_i32), _vp]
         L.fc_tune_clear.restype = None
         L.fc_tune_clear.argtypes = []
-        for name in ("avgpool2x2", "fc_probe_mfma", "chain_conv_bn_pool", "chain_convN", "chain_gemm2_tune", "chain_gemm2_auto_variant", "chain_gemm2", "chain_gemm2_variant", "chain_gemmN", "chain_conv_pool", "chain_conv2", "gemm_bias_act",
+        for name in ("chain_conv_pool_ex", "avgpool2x2", "fc_probe_mfma", "chain_conv_bn_pool", "chain_convN", "chain_gemm2_tune", "chain_gemm2_auto_variant", "chain_gemm2", "chain_gemm2_variant", "chain_gemmN", "chain_conv_pool", "chain_conv2", "gemm_bias_act",
                      "conv_bias_act", "maxpool2x2", "pad_channels"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
@@ -317,24 +320,26 @@ def _argmax_tensor(argmax, oshape, like):
     return argmax
 
 
-def chain_conv_pool(x, w, b, act="relu", pool="max2x2", out=None, argmax=None):
+def chain_conv_pool(x, w, b, act="relu", pool="max2x2", out=None, argmax=None, variant="auto"):
     """y = maxpool2x2(act(conv3x3(x, w) + b)) (or act(conv+b) with pool='none').
-    ``argmax``: None, True (allocate) or a uint8 tensor; returns y or (y, argmax)."""
-    return _conv_pool("chain_conv_pool", x, w, None, b, act, pool, out, argmax)
+    ``argmax``: None, True (allocate) or a uint8 tensor; returns y or (y, argmax).
+    ``variant``: kernel form ("auto", "lds_weights", "reg_weights")."""
+    return _conv_pool("chain_conv_pool", x, w, None, b, act, pool, out, argmax, variant)
 
 
-def chain_conv_bn_pool(x, w, scale, shift, act="relu", pool="max2x2", out=None, argmax=None):
+def chain_conv_bn_pool(x, w, scale, shift, act="relu", pool="max2x2", out=None, argmax=None, variant="auto"):
     """y = maxpool2x2(act(conv3x3(x, w) * scale + shift)) per output channel (batch
     norm at inference as a scale and a shift); pool='none' stores act(...)."""
     if scale is None:
         raise ValueError("scale is required")
-    return _conv_pool("chain_conv_bn_pool", x, w, scale, shift, act, pool, out, argmax)
+    return _conv_pool("chain_conv_bn_pool", x, w, scale, shift, act, pool, out, argmax, variant)
 
 
-def _conv_pool(fn, x, w, scale, b, act, pool, out, argmax):
+def _conv_pool(fn, x, w, scale, b, act, pool, out, argmax, variant="auto"):
     sh = _conv_shape(x, w)
     P, Q = _conv_out_hw(sh)
     p = POOL[pool] if isinstance(pool, str) else int(pool)
+    v = CONV_VARIANT[variant] if isinstance(variant, str) else int(variant)
     oshape = (sh.n, P // 2, Q // 2, sh.k) if p else (sh.n, P, Q, sh.k)
     am = _argmax_tensor(argmax, oshape, x) if argmax is not True else None   # the caller's, checked below
     items = [(x, "x", None, None), (w, "w", None, None), (b, "b" if scale is None else "shift", (sh.k,), None),
@@ -345,13 +350,8 @@ def _conv_pool(fn, x, w, scale, b, act, pool, out, argmax):
     _validate(items + [(out, "out", oshape, None)])
     if argmax is True:
         am = _argmax_tensor(True, oshape, x)
-    L = lib()
-    if scale is None:
-        st = L.chain_conv_pool(_ptr(x), _ptr(w), _ptr(b), _act(act), p, _ptr(out), ctypes.byref(sh), _ptr(am),
-                               _stream(x))
-    else:
-        st = L.chain_conv_bn_pool(_ptr(x), _ptr(w), _ptr(scale), _ptr(b), _act(act), p, _ptr(out), ctypes.byref(sh),
-                                  _ptr(am), _stream(x))
+    st = lib().chain_conv_pool_ex(_ptr(x), _ptr(w), _ptr(scale), _ptr(b), _act(act), p, _ptr(out), ctypes.byref(sh),
+                                  _ptr(am), v, _stream(x))
     _check(fn, st)
     return (out, am) if am is not None else out
 

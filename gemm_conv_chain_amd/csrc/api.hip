@@ -15,7 +15,9 @@ namespace fc {
 hipError_t run_conv_bias_act3x3(const half_t* x, const half_t* w, const half_t* scale, const half_t* b, int act,
                                 half_t* y, int NB, int H, int W, int C, int K, hipStream_t st);
 hipError_t run_conv_pool3x3(const half_t* x, const half_t* w, const half_t* scale, const half_t* b, int act,
-                            bool avg, half_t* y, uint8_t* argmax, int NB, int H, int W, int C, int K, hipStream_t st);
+                            bool avg, half_t* y, uint8_t* argmax, int NB, int H, int W, int C, int K, bool regw,
+                            hipStream_t st);
+bool conv_pool_wr_fits(int W, int C, int K);
 hipError_t run_chain_conv2_3x3(const half_t* x, const half_t* w0, const half_t* b0, int act, const half_t* w1,
                                const half_t* b1, half_t* y, int NB, int H, int W, int C, int K0, int K1,
                                hipStream_t st);
@@ -314,15 +316,17 @@ fc_status gemm_bias_act(const fc_half* A, const fc_half* W, const fc_half* b, fc
                       "gemm_bias_act");
 }
 
-// conv3x3 -> (x scale) + b -> act -> optional 2x2 max pool (scale may be NULL).
+// conv3x3 -> (x scale) + b -> act -> optional 2x2 pool (scale may be NULL),
+// in the kernel form `variant` (fc_conv_variant).
 static fc_status conv_pool_impl(const char* name, const fc_half* x, const fc_half* w, const fc_half* scale,
                                 const fc_half* b, fc_act act, fc_pool pool, fc_half* y, const fc_conv_shape* shape,
-                                uint8_t* argmax, void* stream)
+                                uint8_t* argmax, int variant, void* stream)
 {
     fc_status s = check_act(act);
     if (s != FC_OK) return s;
     if ((int)pool < 0 || (int)pool > 2) return fail(FC_E_ARG, "pool %d out of range", (int)pool);
     if (pool != FC_POOL_MAX_2X2_S2 && argmax) return fail(FC_E_ARG, "argmax needs the max pool");
+    if (variant < 0 || variant > 2) return fail(FC_E_ARG, "conv variant %d out of range", variant);
     s = check_conv(shape, 128);
     if (s != FC_OK) return s;
     const long npix = (long)shape->n * shape->h * shape->w;
@@ -330,15 +334,21 @@ static fc_status conv_pool_impl(const char* name, const fc_half* x, const fc_hal
     if (!w || (npix > 0 && !x) || (nout > 0 && !y)) return fail(FC_E_NULL, "x, w and y are required");
     if (!aligned16(x) || !aligned16(w) || !aligned16(y) || !aligned16(b) || !aligned16(scale))
         return fail(FC_E_ALIGN, "tensor pointers must be 16-byte aligned");
+    const bool lds_ok = fc::convw_fits(shape->c, shape->k);
+    const bool reg_ok = pool != FC_POOL_NONE && fc::conv_pool_wr_fits(shape->w, shape->c, shape->k);
+    if (variant == FC_CONV_REG_WEIGHTS && !reg_ok)
+        return fail(FC_E_UNSUPPORTED, "register-weights conv needs c == 64, 64 < k <= 128, w*c < 2^27 and a pool");
+    if (variant == FC_CONV_LDS_WEIGHTS && !lds_ok) return fail(FC_E_UNSUPPORTED, "weights exceed LDS");
+    if (variant == FC_CONV_AUTO && !lds_ok && !reg_ok) return fail(FC_E_UNSUPPORTED, "weights exceed LDS");
     if (nout == 0) return ok();
-    if (!fc::convw_fits(shape->c, shape->k)) return fail(FC_E_UNSUPPORTED, "weights exceed LDS");
+    const bool regw = variant == FC_CONV_REG_WEIGHTS || (variant == FC_CONV_AUTO && reg_ok);
     hipStream_t st = (hipStream_t)stream;
     if (pool == FC_POOL_NONE)
         return hip_status(fc::run_conv_bias_act3x3(H(x), H(w), H(scale), H(b), act, Hm(y), shape->n, shape->h,
                                                     shape->w, shape->c, shape->k, st),
                           name);
     return hip_status(fc::run_conv_pool3x3(H(x), H(w), H(scale), H(b), act, pool == FC_POOL_AVG_2X2_S2, Hm(y),
-                                           argmax, shape->n, shape->h, shape->w, shape->c, shape->k, st),
+                                           argmax, shape->n, shape->h, shape->w, shape->c, shape->k, regw, st),
                       name);
 }
 
@@ -346,7 +356,7 @@ fc_status chain_conv_pool(const fc_half* x, const fc_half* w, const fc_half* b, 
                           fc_half* y, const fc_conv_shape* shape, uint8_t* argmax, void* stream)
 {
     return conv_pool_impl(pool == FC_POOL_NONE ? "conv_bias_act" : "chain_conv_pool", x, w, nullptr, b, act, pool, y,
-                          shape, argmax, stream);
+                          shape, argmax, FC_CONV_AUTO, stream);
 }
 
 fc_status chain_conv_bn_pool(const fc_half* x, const fc_half* w, const fc_half* scale, const fc_half* shift,
@@ -354,7 +364,16 @@ fc_status chain_conv_bn_pool(const fc_half* x, const fc_half* w, const fc_half* 
                              void* stream)
 {
     if (!scale) return fail(FC_E_NULL, "scale is required (use chain_conv_pool for a plain bias)");
-    return conv_pool_impl("chain_conv_bn_pool", x, w, scale, shift, act, pool, y, shape, argmax, stream);
+    return conv_pool_impl("chain_conv_bn_pool", x, w, scale, shift, act, pool, y, shape, argmax, FC_CONV_AUTO,
+                          stream);
+}
+
+fc_status chain_conv_pool_ex(const fc_half* x, const fc_half* w, const fc_half* scale, const fc_half* shift,
+                             fc_act act, fc_pool pool, fc_half* y, const fc_conv_shape* shape, uint8_t* argmax,
+                             fc_conv_variant variant, void* stream)
+{
+    return conv_pool_impl("chain_conv_pool_ex", x, w, scale, shift, act, pool, y, shape, argmax, (int)variant,
+                          stream);
 }
 
 fc_status conv_bias_act(const fc_half* x, const fc_half* w, const fc_half* b, fc_act act, fc_half* y,

@@ -27,26 +27,6 @@ namespace fc {
 // 3x3, stride 1, pad 1 NHWC conv pixels as GEMM rows (P = H, Q = W).  A lane
 // half h reads, for chunk c, the 32 consecutive k = 64c + 32h + [0, 32): a
 // single (r, s) position and 32 consecutive channels (C % 32 == 0).
-// Unsigned division by a runtime constant d >= 1 without a divide sequence:
-// magic = floor(2^32 / d) (2^32 - 1 for d = 1) gives q0 = mulhi(x, magic) in
-// {x/d - 1, x/d}, and one comparison fixes it (exact for every 32-bit x).
-struct FastDiv {
-    unsigned d, magic;
-    static FastDiv make(unsigned dd)
-    {
-        FastDiv f;
-        f.d = dd;
-        f.magic = dd > 1 ? (unsigned)(0x100000000ull / dd) : 0xffffffffu;
-        return f;
-    }
-    __device__ __forceinline__ unsigned div(unsigned x) const
-    {
-        unsigned q = __umulhi(x, magic);
-        if (x - q * d >= d) ++q;
-        return q;
-    }
-};
-
 struct Conv3x3Rows {
     static constexpr bool kRaw = false;   // loads land in operand layout
     const half_t* x;
@@ -695,9 +675,14 @@ hipError_t run_conv_bias_act3x3(const half_t* x, const half_t* w, const half_t* 
     return launch_convw<EPI_STORE>(a, st);
 }
 
+hipError_t run_conv_pool_wr(const half_t* x, const half_t* w, const half_t* scale, const half_t* b, int act, bool avg,
+                            half_t* y, uint8_t* argmax, int NB, int H, int W, int K, hipStream_t st);
+
 hipError_t run_conv_pool3x3(const half_t* x, const half_t* w, const half_t* scale, const half_t* b, int act,
-                            bool avg, half_t* y, uint8_t* argmax, int NB, int H, int W, int C, int K, hipStream_t st)
+                            bool avg, half_t* y, uint8_t* argmax, int NB, int H, int W, int C, int K, bool regw,
+                            hipStream_t st)
 {
+    if (regw) return run_conv_pool_wr(x, w, scale, b, act, avg, y, argmax, NB, H, W, K, st);
     ConvWArgs a;
     a.x = x; a.w = w; a.s = scale; a.b = b; a.y = y; a.argmax = argmax;
     a.NB = NB; a.H = H; a.W = W; a.C = C; a.K = K;

@@ -132,6 +132,26 @@ template <> struct Act<ACT_HARDSWISH> {
     }
 };
 
+// Unsigned division by a runtime constant d >= 1 without a divide sequence:
+// magic = floor(2^32 / d) (2^32 - 1 for d = 1) gives q0 = mulhi(x, magic) in
+// {x/d - 1, x/d}, and one comparison fixes it (exact for every 32-bit x).
+struct FastDiv {
+    unsigned d, magic;
+    static FastDiv make(unsigned dd)
+    {
+        FastDiv f;
+        f.d = dd;
+        f.magic = dd > 1 ? (unsigned)(0x100000000ull / dd) : 0xffffffffu;
+        return f;
+    }
+    __device__ __forceinline__ unsigned div(unsigned x) const
+    {
+        unsigned q = __umulhi(x, magic);
+        if (x - q * d >= d) ++q;
+        return q;
+    }
+};
+
 template <int V> struct IntC {
     static constexpr int value = V;
 };

@@ -76,6 +76,19 @@ typedef enum { FC_ACT_NONE = 0, FC_ACT_RELU = 1, FC_ACT_GELU_TANH = 2, FC_ACT_HA
 typedef enum { FC_POOL_NONE = 0, FC_POOL_MAX_2X2_S2 = 1, FC_POOL_AVG_2X2_S2 = 2 } fc_pool;
 typedef enum { FC_VARIANT_AUTO = 0, FC_VARIANT_RF = 1, FC_VARIANT_LDS = 2, FC_VARIANT_STREAM = 3 } fc_variant;
 
+/* Kernel forms of the conv + activation + 2x2 pool chain (chain_conv_pool_ex).
+ * Both keep the conv output in registers and compute the same values up to
+ * fp32 summation order:
+ *   FC_CONV_LDS_WEIGHTS  the HWIO weights resident in LDS, rows of pixels
+ *                        streamed from global memory into registers (every
+ *                        shape chain_conv_pool accepts);
+ *   FC_CONV_REG_WEIGHTS  the weights resident in registers as matrix-core
+ *                        operands, the input halo of each tile streamed into
+ *                        LDS (c == 64, 64 < k <= 128, a max or average pool);
+ *   FC_CONV_AUTO         the choice chain_conv_pool_tune cached for the shape,
+ *                        else REG_WEIGHTS where it applies, else LDS_WEIGHTS. */
+typedef enum { FC_CONV_AUTO = 0, FC_CONV_LDS_WEIGHTS = 1, FC_CONV_REG_WEIGHTS = 2 } fc_conv_variant;
+
 /* x NHWC [n,h,w,c]; w HWIO [r,s,c,k]; output spatial size
  * P = (h + 2*pad - r)/stride + 1, Q = (w + 2*pad - s)/stride + 1. */
 typedef struct {
@@ -204,6 +217,18 @@ fc_status chain_conv_pool(const fc_half *x, const fc_half *w, const fc_half *b, 
 fc_status chain_conv_bn_pool(const fc_half *x, const fc_half *w, const fc_half *scale, const fc_half *shift,
                              fc_act act, fc_pool pool, fc_half *y, const fc_conv_shape *shape,
                              uint8_t *argmax, void *stream);
+
+/*
+ * chain_conv_pool_ex -- chain_conv_pool (scale == NULL: shift is the bias) or
+ * chain_conv_bn_pool (scale != NULL) with an explicit kernel form
+ * (fc_conv_variant).  FC_E_UNSUPPORTED if the requested form does not take
+ * the shape or the pool (FC_CONV_REG_WEIGHTS needs c == 64, 64 < k <= 128,
+ * w * c < 2^27 and pool != FC_POOL_NONE); FC_E_ARG for an unknown form.
+ * Everything else as chain_conv_pool.
+ */
+fc_status chain_conv_pool_ex(const fc_half *x, const fc_half *w, const fc_half *scale, const fc_half *shift,
+                             fc_act act, fc_pool pool, fc_half *y, const fc_conv_shape *shape, uint8_t *argmax,
+                             fc_conv_variant variant, void *stream);
 
 /*
  * chain_conv2 -- y = conv1x1(act(conv(x, w0) + b0), w1) + b1, the first conv's

@@ -25,7 +25,7 @@ def test_exports_every_declared_symbol(L):
     names = fc.exported_names()
     for n in ("chain_gemm2", "chain_gemm2_variant", "chain_gemmN", "chain_conv_pool", "chain_conv2", "gemm_bias_act",
               "conv_bias_act", "maxpool2x2", "pad_channels", "fc_abi_version", "fc_status_str", "fc_last_error",
-              "chain_gemm2_tune", "chain_gemm2_auto_variant", "fc_tune_clear", "chain_convN", "chain_conv_bn_pool", "fc_probe_mfma"):
+              "chain_gemm2_tune", "chain_gemm2_auto_variant", "fc_tune_clear", "chain_convN", "chain_conv_bn_pool", "fc_probe_mfma", "chain_conv_pool_ex"):
         assert n in names
     for n in names:
         assert hasattr(L, n), n
@@ -126,6 +126,21 @@ def test_conv_validation(L):
     assert L.conv_bias_act(P, P, NUL, 1, P2, ctypes.byref(wide), None) == E_UNSUP
     assert L.chain_conv2(P, P, NUL, 1, P, NUL, 64, P2, ctypes.byref(shape(n=1, h=1, w=(1 << 24), k=64)), None) == E_UNSUP
     assert L.chain_conv_pool(P, P, NUL, 1, 1, P2, ctypes.byref(shape(n=1, h=1, w=(1 << 24) - 3)), NUL, None) == OK
+
+
+def test_conv_variant_validation(L):
+    sh = shape(c=64, k=128)
+    ex = L.chain_conv_pool_ex
+    ex.argtypes = [ctypes.c_void_p] * 4 + [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.POINTER(fc.ConvShape),
+                                           ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
+    assert ex(P, P, NUL, NUL, 1, 1, P2, ctypes.byref(sh), NUL, 3, None) == E_ARG
+    assert ex(P, P, NUL, NUL, 1, 1, P2, ctypes.byref(sh), NUL, -1, None) == E_ARG
+    # register-weights form: c == 64, 64 < k <= 128 and a pool
+    assert ex(P, P, NUL, NUL, 1, 1, P2, ctypes.byref(shape(c=32, k=128)), NUL, 2, None) == E_UNSUP
+    assert ex(P, P, NUL, NUL, 1, 1, P2, ctypes.byref(shape(c=64, k=64)), NUL, 2, None) == E_UNSUP
+    assert ex(P, P, NUL, NUL, 1, 0, P2, ctypes.byref(sh), NUL, 2, None) == E_UNSUP
+    assert ex(P, P, NUL, NUL, 1, 1, P2, ctypes.byref(shape(c=128, k=128)), NUL, 1, None) == E_UNSUP   # LDS form: weights exceed LDS
+    assert ex(P, P, NUL, NUL, 1, 2, P2, ctypes.byref(shape(h=1)), NUL, 2, None) == OK                 # empty pooled output
 
 
 def test_empty_tensors_may_be_null(L):

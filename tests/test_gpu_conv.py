@@ -170,13 +170,16 @@ def test_conv2_fused_equals_unfused(fc):
 def test_conv_pool_fused_equals_unfused(fc):
     d = inputs.conv_pool_inputs(2, 16, 16, 64, 128, seed=3)
     x, w, b = dev(d["x"]), dev(d["w"]), dev(d["b"])
-    yf, af = fc.chain_conv_pool(x, w, b, argmax=True)
+    yf, af = fc.chain_conv_pool(x, w, b, argmax=True, variant="lds_weights")
     v = fc.conv_bias_act(x, w, b, act="relu")
     yu, au = fc.maxpool2x2(v, argmax=True)
     torch.cuda.synchronize()
-    # same accumulation order in both paths: bit-identical
+    # the LDS-weights form and the unfused conv share the accumulation order: bit-identical
     assert np.array_equal(to_np(yf).view(np.uint16), to_np(yu).view(np.uint16))
     assert np.array_equal(to_np(af), to_np(au))
+    # the register-weights form sums the two channel halves last: within the tolerance
+    yr = fc.chain_conv_pool(x, w, b, variant="reg_weights")
+    assert_close(to_np(yr), to_np(yu).astype(np.float64), "reg-weights fused vs unfused")
 
 
 def test_maxpool2x2(fc):
