@@ -474,12 +474,35 @@ WORKLOADS = ["b2b_gemm_tiny", "b2b_gemm_rf", "b2b_gemm_lds", "gemm3_rf", "conv3x
 
 
 def tune(fc, prob, name):
-    W0, b0, W1, b1 = prob.W
-    best, times, _ = fc.tune_chain_gemm2(prob.X[0], W0, b0, W1, b1, act=prob.act, out=prob.Y[0], reps=10)
-    log("%s tuned: %s (%s)" % (name, best, ", ".join("%s %.2f us" % kv for kv in sorted(times.items()))))
-    prob.config.update(variant=best, tuned_us={k: round(v, 2) for k, v in times.items()})
-    prob.kernel = {"rf": "k_chain_rf", "lds": "k_gemm_lds", "stream": "k_chain_stream"}[best]
-    prob.traffic_key = name if best == ("lds" if name == "b2b_gemm_lds" else "rf") else name + "@" + best
+    """Profile every configuration of the workload's chain on its first buffer
+    set (the library caches the fastest for the shape; the timed steps then run
+    it under the 'auto' form)."""
+    kind = prob.spec["kind"]
+    if kind == "gemm2":
+        W0, b0, W1, b1 = prob.W
+        best, table, _ = fc.tune_chain_gemm2_table(prob.X[0], W0, b0, W1, b1, act=prob.act, out=prob.Y[0], reps=10)
+        prob.config["variant"] = "auto"
+        prob.kernel = {"rf": "k_chain_rf", "lds": "k_gemm_lds", "stream": "k_chain_stream"}[best["variant"]]
+        default = "lds" if name == "b2b_gemm_lds" else "rf"
+        prob.traffic_key = name if best["variant"] == default else name + "@" + best["variant"]
+    elif kind == "conv_pool":
+        if prob.bn:
+            w, sc, sh = prob.W
+            best, table, _ = fc.tune_conv_pool(prob.X[0], w, sh, scale=sc, pool="max2x2", out=prob.Y[0], reps=10)
+        else:
+            w, b = prob.W
+            best, table, _ = fc.tune_conv_pool(prob.X[0], w, b, pool=prob.pool, out=prob.Y[0], reps=10)
+        prob.conv_variant = "auto"
+        prob.config["variant"] = "auto"
+        prob.kernel = "k_conv_w" if best["variant"] == "lds_weights" else "k_conv_pool_wr"
+        prob.traffic_key = name + "@" + best["variant"]
+    else:
+        raise ValueError("--tune applies to the two-GEMM and the pooled conv workloads")
+    log("%s tuned: %s waves %d (%s)" % (name, best["variant"], best["waves"], ", ".join(
+        "%s/%d %.2f us" % (r["variant"], r["waves"], r["us"]) for r in table)))
+    prob.config.update(tuned={"best": {"variant": best["variant"], "waves": best["waves"]},
+                              "table": [{"variant": r["variant"], "waves": r["waves"], "us": round(r["us"], 2)}
+                                        for r in table]})
 
 
 def main():
@@ -499,8 +522,8 @@ def main():
     ap.add_argument("--no-configs", action="store_true",
                     help="measure only the headline workload (no per-configuration sub-records)")
     ap.add_argument("--tune", action="store_true",
-                    help="GEMM-chain workloads: profile the residence variants on the GPU first "
-                         "(chain_gemm2_tune) and time the fastest")
+                    help="two-GEMM and pooled conv workloads: profile every kernel configuration on the GPU "
+                         "first (chain_gemm2_tune_ex / chain_conv_pool_tune) and time the fastest")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-probe", action="store_true", help="skip the matrix-core rate / clock probe")
     ap.add_argument("--calib-copy", action="store_true",
@@ -523,8 +546,8 @@ def main():
     log("workload %s: %d buffer set(s), %.1f MB fused algorithmic bytes, %.3f GFLOP"
         % (args.workload, prob.nsets, prob.bytes_fused / 1e6, prob.flops / 1e9))
     if args.tune:
-        if prob.spec["kind"] != "gemm2":
-            print("bench.py: --tune applies to the two-GEMM chain workloads", file=sys.stderr)
+        if prob.spec["kind"] not in ("gemm2", "conv_pool"):
+            print("bench.py: --tune applies to the two-GEMM and the pooled conv workloads", file=sys.stderr)
             sys.exit(2)
         tune(fc, prob, args.workload)
 

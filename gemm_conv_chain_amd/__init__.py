@@ -19,7 +19,7 @@ import ctypes
 import os
 import re
 
-__all__ = ["CONV_VARIANT", "lib", "FusedChainError", "chain_gemm2", "tune_chain_gemm2", "auto_variant", "tune_clear", "chain_gemmN", "chain_conv_pool", "chain_conv_bn_pool", "chain_conv2", "chain_convN",
+__all__ = ["TuneEntry", "tune_chain_gemm2_table", "auto_config", "tune_conv_pool", "conv_auto_config", "CONV_VARIANT", "lib", "FusedChainError", "chain_gemm2", "tune_chain_gemm2", "auto_variant", "tune_clear", "chain_gemmN", "chain_conv_pool", "chain_conv_bn_pool", "chain_conv2", "chain_convN",
            "gemm_bias_act", "conv_bias_act", "maxpool2x2", "avgpool2x2", "pad_channels", "pad_weight_channels", "abi_version", "ACT", "VARIANT",
            "LIB_PATH", "HEADER_PATH", "exported_names"]
 
@@ -41,6 +41,12 @@ class FusedChainError(RuntimeError):
 
 class ConvShape(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in ("n", "h", "w", "c", "k", "r", "s", "stride", "pad")]
+
+
+class TuneEntry(ctypes.Structure):
+    """One configuration timed by the profiler: kernel form, tile-owning waves
+    per block (0 = the form's own block shape), microseconds per launch."""
+    _fields_ = [("variant", ctypes.c_int32), ("waves", ctypes.c_int32), ("us", ctypes.c_float)]
 
 
 _lib = None
@@ -81,11 +87,23 @@ def lib():
         L.chain_conv_bn_pool.argtypes = [_vp, _vp, _vp, _vp, ctypes.c_int, ctypes.c_int, _vp,
                                          ctypes.POINTER(ConvShape), _vp, _vp]
         L.chain_conv_pool_ex.argtypes = [_vp, _vp, _vp, _vp, ctypes.c_int, ctypes.c_int, _vp,
-                                         ctypes.POINTER(ConvShape), _vp, ctypes.c_int, _vp]
+                                         ctypes.POINTER(ConvShape), _vp, ctypes.c_int, _i32, _vp]
+        L.chain_gemm2_ex.argtypes = [_vp, _vp, _vp, ctypes.c_int, _vp, _vp, _vp, _i64, _i32, _i32, _i32,
+                                     ctypes.c_int, _i32, _vp]
         L.fc_probe_mfma.argtypes = [_i32, _i32, _vp, _vp, _i32, ctypes.POINTER(_i32), _vp]
+        L.chain_gemm2_tune_ex.argtypes = [_vp, _vp, _vp, ctypes.c_int, _vp, _vp, _vp, _i64, _i32, _i32, _i32, _i32,
+                                          ctypes.POINTER(TuneEntry), _i32, ctypes.POINTER(_i32),
+                                          ctypes.POINTER(TuneEntry), _vp]
+        L.chain_gemm2_auto_config.argtypes = [_i64, _i32, _i32, _i32, ctypes.c_int, ctypes.POINTER(TuneEntry)]
+        L.chain_conv_pool_tune.argtypes = [_vp, _vp, _vp, _vp, ctypes.c_int, ctypes.c_int, _vp,
+                                           ctypes.POINTER(ConvShape), _vp, _i32, ctypes.POINTER(TuneEntry), _i32,
+                                           ctypes.POINTER(_i32), ctypes.POINTER(TuneEntry), _vp]
+        L.chain_conv_pool_auto_config.argtypes = [ctypes.POINTER(ConvShape), ctypes.c_int, ctypes.c_int, _i32,
+                                                  ctypes.POINTER(TuneEntry)]
         L.fc_tune_clear.restype = None
         L.fc_tune_clear.argtypes = []
-        for name in ("chain_conv_pool_ex", "avgpool2x2", "fc_probe_mfma", "chain_conv_bn_pool", "chain_convN", "chain_gemm2_tune", "chain_gemm2_auto_variant", "chain_gemm2", "chain_gemm2_variant", "chain_gemmN", "chain_conv_pool", "chain_conv2", "gemm_bias_act",
+        for name in ("chain_gemm2_ex", "chain_gemm2_tune_ex", "chain_gemm2_auto_config", "chain_conv_pool_tune",
+                     "chain_conv_pool_auto_config", "chain_conv_pool_ex", "avgpool2x2", "fc_probe_mfma", "chain_conv_bn_pool", "chain_convN", "chain_gemm2_tune", "chain_gemm2_auto_variant", "chain_gemm2", "chain_gemm2_variant", "chain_gemmN", "chain_conv_pool", "chain_conv2", "gemm_bias_act",
                      "conv_bias_act", "maxpool2x2", "pad_channels"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
@@ -200,12 +218,18 @@ def _gemm2_shapes(A, W0, b0, W1, b1, out):
 
 
 # ------------------------------------------------------------ entry points
-def chain_gemm2(A, W0, b0, W1, b1, act="relu", out=None, variant="auto"):
-    """D1 [M, N1] = act(A [M,K0] @ W0 [K0,N0] + b0) @ W1 [N0,N1] + b1 (fp16)."""
+def chain_gemm2(A, W0, b0, W1, b1, act="relu", out=None, variant="auto", waves=None):
+    """D1 [M, N1] = act(A [M,K0] @ W0 [K0,N0] + b0) @ W1 [N0,N1] + b1 (fp16).
+    ``waves`` (explicit variant only): tile-owning waves per block of the
+    register-resident form (chain_gemm2_ex)."""
     M, K0, N0, N1, out = _gemm2_shapes(A, W0, b0, W1, b1, out)
     v = VARIANT[variant] if isinstance(variant, str) else int(variant)
-    _check("chain_gemm2", lib().chain_gemm2_variant(_ptr(A), _ptr(W0), _ptr(b0), _act(act), _ptr(W1), _ptr(b1),
-                                                    _ptr(out), M, K0, N0, N1, v, _stream(A)))
+    if waves is None:
+        _check("chain_gemm2", lib().chain_gemm2_variant(_ptr(A), _ptr(W0), _ptr(b0), _act(act), _ptr(W1), _ptr(b1),
+                                                        _ptr(out), M, K0, N0, N1, v, _stream(A)))
+    else:
+        _check("chain_gemm2_ex", lib().chain_gemm2_ex(_ptr(A), _ptr(W0), _ptr(b0), _act(act), _ptr(W1), _ptr(b1),
+                                                      _ptr(out), M, K0, N0, N1, v, int(waves), _stream(A)))
     return out
 
 
@@ -224,6 +248,77 @@ def tune_chain_gemm2(A, W0, b0, W1, b1, act="relu", out=None, reps=20):
                                                       _stream(A)))
     times = {_VARIANT_NAME[v]: float(us[v]) for v in (1, 2, 3) if us[v] >= 0}
     return _VARIANT_NAME[best.value], times, out
+
+
+def tune_chain_gemm2_table(A, W0, b0, W1, b1, act="relu", out=None, reps=20):
+    """Time every configuration of chain_gemm2 for these tensors (blocking) and
+    cache the fastest.  Returns (best, table, out) where best and the table rows
+    are dicts {variant, waves, us}."""
+    M, K0, N0, N1, out = _gemm2_shapes(A, W0, b0, W1, b1, out)
+    table = (TuneEntry * 16)()
+    best = TuneEntry()
+    n = _i32(0)
+    _check("chain_gemm2_tune_ex", lib().chain_gemm2_tune_ex(_ptr(A), _ptr(W0), _ptr(b0), _act(act), _ptr(W1), _ptr(b1),
+                                                            _ptr(out), M, K0, N0, N1, int(reps), table, 16,
+                                                            ctypes.byref(n), ctypes.byref(best), _stream(A)))
+    return _entry(best, _VARIANT_NAME), [_entry(table[i], _VARIANT_NAME) for i in range(min(n.value, 16))], out
+
+
+def _entry(e, names):
+    return {"variant": names[e.variant], "waves": int(e.waves), "us": float(e.us)}
+
+
+def auto_config(M, K0, N0, N1, act="relu"):
+    """{variant, waves} that chain_gemm2(variant='auto') runs for this shape."""
+    e = TuneEntry()
+    _check("chain_gemm2_auto_config", lib().chain_gemm2_auto_config(int(M), int(K0), int(N0), int(N1), _act(act),
+                                                                    ctypes.byref(e)))
+    d = _entry(e, _VARIANT_NAME)
+    d.pop("us")
+    return d
+
+
+_CONV_VARIANT_NAME = {v: k for k, v in CONV_VARIANT.items()}
+
+
+def tune_conv_pool(x, w, b, act="relu", pool="max2x2", scale=None, out=None, argmax=None, reps=20):
+    """Time every configuration of the pooled conv chain for these tensors
+    (blocking) and cache the fastest (chain_conv_pool_tune).  b is the bias,
+    or the shift when scale is given.  Returns (best, table, out) with
+    dict rows {variant, waves, us}."""
+    sh = _conv_shape(x, w)
+    P, Q = _conv_out_hw(sh)
+    p = POOL[pool] if isinstance(pool, str) else int(pool)
+    oshape = (sh.n, P // 2, Q // 2, sh.k)
+    am = _argmax_tensor(argmax, oshape, x) if argmax is not True else None
+    items = [(x, "x", None, None), (w, "w", None, None), (b, "b" if scale is None else "shift", (sh.k,), None),
+             (scale, "scale", (sh.k,), None), (am, "argmax", oshape, _torch().uint8)]
+    if out is None:
+        _validate(items)
+        out = _empty(oshape, x)
+    _validate(items + [(out, "out", oshape, None)])
+    if argmax is True:
+        am = _argmax_tensor(True, oshape, x)
+    table = (TuneEntry * 16)()
+    best = TuneEntry()
+    n = _i32(0)
+    _check("chain_conv_pool_tune", lib().chain_conv_pool_tune(_ptr(x), _ptr(w), _ptr(scale), _ptr(b), _act(act), p,
+                                                              _ptr(out), ctypes.byref(sh), _ptr(am), int(reps), table,
+                                                              16, ctypes.byref(n), ctypes.byref(best), _stream(x)))
+    return (_entry(best, _CONV_VARIANT_NAME), [_entry(table[i], _CONV_VARIANT_NAME) for i in range(min(n.value, 16))],
+            out)
+
+
+def conv_auto_config(n, h, w, c, k, act="relu", pool="max2x2", argmax=False):
+    """{variant, waves} that the pooled conv chain runs under variant='auto'."""
+    e = TuneEntry()
+    sh = ConvShape(n, h, w, c, k, 3, 3, 1, 1)
+    p = POOL[pool] if isinstance(pool, str) else int(pool)
+    _check("chain_conv_pool_auto_config", lib().chain_conv_pool_auto_config(ctypes.byref(sh), _act(act), p,
+                                                                            1 if argmax else 0, ctypes.byref(e)))
+    d = _entry(e, _CONV_VARIANT_NAME)
+    d.pop("us")
+    return d
 
 
 def auto_variant(M, K0, N0, N1, act="relu"):
@@ -320,22 +415,24 @@ def _argmax_tensor(argmax, oshape, like):
     return argmax
 
 
-def chain_conv_pool(x, w, b, act="relu", pool="max2x2", out=None, argmax=None, variant="auto"):
+def chain_conv_pool(x, w, b, act="relu", pool="max2x2", out=None, argmax=None, variant="auto", waves=0):
     """y = maxpool2x2(act(conv3x3(x, w) + b)) (or act(conv+b) with pool='none').
     ``argmax``: None, True (allocate) or a uint8 tensor; returns y or (y, argmax).
-    ``variant``: kernel form ("auto", "lds_weights", "reg_weights")."""
-    return _conv_pool("chain_conv_pool", x, w, None, b, act, pool, out, argmax, variant)
+    ``variant``: kernel form ("auto", "lds_weights", "reg_weights"); ``waves``:
+    tile-owning waves per block of the pooled "lds_weights" form (0 = 8)."""
+    return _conv_pool("chain_conv_pool", x, w, None, b, act, pool, out, argmax, variant, waves)
 
 
-def chain_conv_bn_pool(x, w, scale, shift, act="relu", pool="max2x2", out=None, argmax=None, variant="auto"):
+def chain_conv_bn_pool(x, w, scale, shift, act="relu", pool="max2x2", out=None, argmax=None, variant="auto",
+                       waves=0):
     """y = maxpool2x2(act(conv3x3(x, w) * scale + shift)) per output channel (batch
     norm at inference as a scale and a shift); pool='none' stores act(...)."""
     if scale is None:
         raise ValueError("scale is required")
-    return _conv_pool("chain_conv_bn_pool", x, w, scale, shift, act, pool, out, argmax, variant)
+    return _conv_pool("chain_conv_bn_pool", x, w, scale, shift, act, pool, out, argmax, variant, waves)
 
 
-def _conv_pool(fn, x, w, scale, b, act, pool, out, argmax, variant="auto"):
+def _conv_pool(fn, x, w, scale, b, act, pool, out, argmax, variant="auto", waves=0):
     sh = _conv_shape(x, w)
     P, Q = _conv_out_hw(sh)
     p = POOL[pool] if isinstance(pool, str) else int(pool)
@@ -351,7 +448,7 @@ def _conv_pool(fn, x, w, scale, b, act, pool, out, argmax, variant="auto"):
     if argmax is True:
         am = _argmax_tensor(True, oshape, x)
     st = lib().chain_conv_pool_ex(_ptr(x), _ptr(w), _ptr(scale), _ptr(b), _act(act), p, _ptr(out), ctypes.byref(sh),
-                                  _ptr(am), v, _stream(x))
+                                  _ptr(am), v, int(waves), _stream(x))
     _check(fn, st)
     return (out, am) if am is not None else out
 

@@ -6,7 +6,7 @@
 
 #include <map>
 #include <mutex>
-#include <tuple>
+#include <vector>
 
 #include "../../include/fusedchain.h"
 #include "fc_launch.h"
@@ -16,7 +16,7 @@ hipError_t run_conv_bias_act3x3(const half_t* x, const half_t* w, const half_t* 
                                 half_t* y, int NB, int H, int W, int C, int K, hipStream_t st);
 hipError_t run_conv_pool3x3(const half_t* x, const half_t* w, const half_t* scale, const half_t* b, int act,
                             bool avg, half_t* y, uint8_t* argmax, int NB, int H, int W, int C, int K, bool regw,
-                            hipStream_t st);
+                            int waves, hipStream_t st);
 bool conv_pool_wr_fits(int W, int C, int K);
 hipError_t run_chain_conv2_3x3(const half_t* x, const half_t* w0, const half_t* b0, int act, const half_t* w1,
                                const half_t* b1, half_t* y, int NB, int H, int W, int C, int K0, int K1,
@@ -114,32 +114,149 @@ fc_status check_g2_ptrs(const fc_half* A, const fc_half* W0, const fc_half* b0, 
     return FC_OK;
 }
 
-// Tuned variant choices (chain_gemm2_tune), per device and shape.
-typedef std::tuple<int, int64_t, int32_t, int32_t, int32_t, int> TuneKey;   // device, M, K0, N0, N1, act
+// ---- profiled configurations (chain_gemm2_tune_ex, chain_conv_pool_tune):
+// kernel form and tile-owning waves per block, cached per device and shape.
+struct Config {
+    int variant;
+    int waves;   // 0: the kernel's own block shape
+};
+typedef std::vector<int64_t> TuneKey;   // kind, device, shape ...
 std::mutex g_tune_mu;
-std::map<TuneKey, int> g_tune;
+std::map<TuneKey, Config> g_tune;
+enum { TK_GEMM2 = 0, TK_CONV_POOL = 1 };
 
-int rule_variant(bool rf_ok, bool stream_ok)
+// The cached configuration for key (device appended here), if any.  The
+// device is only queried when something has been tuned.
+bool tuned_config(TuneKey key, Config* out)
 {
-    return rf_ok ? fc::VARIANT_RF : (stream_ok ? fc::VARIANT_STREAM : fc::VARIANT_LDS);
+    std::lock_guard<std::mutex> g(g_tune_mu);
+    if (g_tune.empty()) return false;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return false;
+    key.insert(key.begin() + 1, dev);
+    auto it = g_tune.find(key);
+    if (it == g_tune.end()) return false;
+    *out = it->second;
+    return true;
 }
 
-// The variant FC_VARIANT_AUTO runs: the tuned one for this device and shape if
-// any, else the static rule.  The device is only queried when something has
-// been tuned.
-int auto_variant(int64_t M, int32_t K0, int32_t N0, int32_t N1, int act, bool rf_ok, bool stream_ok)
+void store_config(TuneKey key, int dev, Config c)
 {
-    {
-        std::lock_guard<std::mutex> g(g_tune_mu);
-        if (!g_tune.empty()) {
-            int dev = 0;
-            if (hipGetDevice(&dev) == hipSuccess) {
-                auto it = g_tune.find(TuneKey(dev, M, K0, N0, N1, act));
-                if (it != g_tune.end()) return it->second;
-            }
+    key.insert(key.begin() + 1, dev);
+    std::lock_guard<std::mutex> g(g_tune_mu);
+    g_tune[key] = c;
+}
+
+TuneKey gemm2_key(int64_t M, int32_t K0, int32_t N0, int32_t N1, int act) { return {TK_GEMM2, M, K0, N0, N1, act}; }
+
+TuneKey conv_key(const fc_conv_shape* s, int act, int pool, bool argmax)
+{
+    return {TK_CONV_POOL, s->n, s->h, s->w, s->c, s->k, act, pool, argmax ? 1 : 0};
+}
+
+// Candidates of the two-GEMM chain: the register-resident form with 8, 4, 2
+// or 1 tile-owning waves per block (a block covers 32 * waves rows per
+// round), then the streamed-weight and the LDS-resident forms (fixed block
+// shapes).  The first applicable one is the untuned rule.
+int gemm2_candidates(bool rf_ok, bool stream_ok, Config* out)
+{
+    int n = 0;
+    if (rf_ok)
+        for (int w : {8, 4, 2, 1}) out[n++] = Config{fc::VARIANT_RF, w};
+    if (stream_ok) out[n++] = Config{fc::VARIANT_STREAM, 0};
+    out[n++] = Config{fc::VARIANT_LDS, 0};
+    return n;
+}
+
+// Untuned: the first candidate; for the register-resident form, blocks of
+// the smallest power-of-two number of tile-owning waves that covers the
+// 32-row tiles with one block per CU (small problems then spread over many
+// CUs in small blocks instead of filling a few blocks).
+Config gemm2_config(int64_t M, int32_t K0, int32_t N0, int32_t N1, int act, bool rf_ok, bool stream_ok)
+{
+    Config c;
+    if (tuned_config(gemm2_key(M, K0, N0, N1, act), &c)) return c;
+    Config cand[8];
+    gemm2_candidates(rf_ok, stream_ok, cand);
+    c = cand[0];
+    if (c.variant == fc::VARIANT_RF) {
+        const int64_t tiles = (M + 31) / 32, cus = fc::device_cu_count();
+        c.waves = 1;
+        while (c.waves < 8 && (int64_t)c.waves * cus < tiles) c.waves *= 2;
+    }
+    return c;
+}
+
+// Candidates of the conv + pool chain: the register-weights form (when it
+// takes the shape), then the LDS-weights form with 8 or 4 tile-owning waves
+// per block (two or one per SIMD).
+int conv_candidates(bool lds_ok, bool reg_ok, Config* out)
+{
+    int n = 0;
+    if (reg_ok) out[n++] = Config{FC_CONV_REG_WEIGHTS, 0};
+    if (lds_ok)
+        for (int w : {8, 4}) out[n++] = Config{FC_CONV_LDS_WEIGHTS, w};
+    return n;
+}
+
+Config conv_config(const fc_conv_shape* s, int act, int pool, bool argmax, bool lds_ok, bool reg_ok)
+{
+    Config c;
+    if (tuned_config(conv_key(s, act, pool, argmax), &c)) return c;
+    Config cand[8];
+    conv_candidates(lds_ok, reg_ok, cand);
+    return cand[0];
+}
+
+// Times `reps` launches of f (after one untimed launch) between two events
+// on st; *us = mean microseconds per launch.
+template <class F>
+hipError_t time_launches(F&& f, int reps, hipStream_t st, hipEvent_t t0, hipEvent_t t1, float* us)
+{
+    hipError_t e = f();   // untimed: first-use set-up (LDS limits, code upload)
+    if (e == hipSuccess) e = hipEventRecord(t0, st);
+    for (int r = 0; r < reps && e == hipSuccess; ++r) e = f();
+    if (e == hipSuccess) e = hipEventRecord(t1, st);
+    if (e == hipSuccess) e = hipEventSynchronize(t1);
+    float ms = 0.0f;
+    if (e == hipSuccess) e = hipEventElapsedTime(&ms, t0, t1);
+    if (e == hipSuccess) *us = 1000.0f * ms / (float)reps;
+    return e;
+}
+
+// Times every candidate config[0 .. n), fills table (up to capacity rows)
+// and *best, and caches the fastest under key.
+template <class F>
+fc_status profile(const char* name, F&& launch, const Config* cand, int n, int reps, const TuneKey& key,
+                  fc_tune_entry* table, int32_t capacity, int32_t* count, fc_tune_entry* best, hipStream_t st)
+{
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_status(e, name);
+    hipEvent_t t0 = nullptr, t1 = nullptr;
+    e = hipEventCreate(&t0);
+    if (e == hipSuccess) e = hipEventCreate(&t1);
+    int ib = -1;
+    float tb = 0.0f;
+    for (int i = 0; i < n && e == hipSuccess; ++i) {
+        float us = -1.0f;
+        e = time_launches([&]() { return launch(cand[i]); }, reps, st, t0, t1, &us);
+        if (e != hipSuccess) break;
+        if (table && i < capacity) table[i] = fc_tune_entry{cand[i].variant, cand[i].waves, us};
+        if (ib < 0 || us < tb) {
+            ib = i;
+            tb = us;
         }
     }
-    return rule_variant(rf_ok, stream_ok);
+    if (t0) (void)hipEventDestroy(t0);
+    if (t1) (void)hipEventDestroy(t1);
+    if (e != hipSuccess) return hip_status(e, name);
+    store_config(key, dev, cand[ib]);
+    if (count) *count = n;
+    if (best) *best = fc_tune_entry{cand[ib].variant, cand[ib].waves, tb};
+    // the last launch is not the winner's: run the winner once more, so the
+    // output holds what the cached configuration computes
+    return hip_status(launch(cand[ib]), name);
 }
 
 }  // namespace
@@ -175,21 +292,45 @@ fc_status chain_gemm2_variant(const fc_half* A, const fc_half* W0, const fc_half
     s = check_g2_shape(M, K0, N0, N1, act, &rf_ok, &stream_ok);
     if (s != FC_OK) return s;
     if ((int)variant < 0 || (int)variant > 3) return fail(FC_E_ARG, "variant %d out of range", (int)variant);
-    int v = variant;
-    if (v == FC_VARIANT_RF && !rf_ok)
+    Config c{(int)variant, 0};
+    if (c.variant == FC_VARIANT_RF && !rf_ok)
         return fail(FC_E_UNSUPPORTED, "register-resident variant needs N0<=128 and W0,W1 within LDS");
-    if (v == FC_VARIANT_STREAM && !stream_ok)
+    if (c.variant == FC_VARIANT_STREAM && !stream_ok)
         return fail(FC_E_UNSUPPORTED, "streamed variant needs N1<=16128 (biases beside the weight buffers)");
     if (M == 0) return ok();
-    if (v == FC_VARIANT_AUTO) v = auto_variant(M, K0, N0, N1, (int)act, rf_ok, stream_ok);
-    return hip_status(fc::run_chain_gemm2(H(A), H(W0), H(b0), act, H(W1), H(b1), Hm(D1), M, K0, N0, N1, v,
-                                          (hipStream_t)stream),
+    if (c.variant == FC_VARIANT_AUTO) c = gemm2_config(M, K0, N0, N1, (int)act, rf_ok, stream_ok);
+    return hip_status(fc::run_chain_gemm2(H(A), H(W0), H(b0), act, H(W1), H(b1), Hm(D1), M, K0, N0, N1, c.variant,
+                                          c.waves, (hipStream_t)stream),
                       "chain_gemm2");
 }
 
-fc_status chain_gemm2_tune(const fc_half* A, const fc_half* W0, const fc_half* b0, fc_act act, const fc_half* W1,
-                           const fc_half* b1, fc_half* D1, int64_t M, int32_t K0, int32_t N0, int32_t N1,
-                           int32_t reps, fc_variant* best, float* us, void* stream)
+fc_status chain_gemm2_ex(const fc_half* A, const fc_half* W0, const fc_half* b0, fc_act act, const fc_half* W1,
+                         const fc_half* b1, fc_half* D1, int64_t M, int32_t K0, int32_t N0, int32_t N1,
+                         fc_variant variant, int32_t waves, void* stream)
+{
+    bool rf_ok = false, stream_ok = false;
+    if (M < 0 || K0 <= 0 || N0 <= 0 || N1 <= 0) return fail(FC_E_SHAPE, "M>=0 and K0, N0, N1 > 0 required");
+    fc_status s = check_g2_ptrs(A, W0, b0, W1, b1, D1, M);
+    if (s != FC_OK) return s;
+    s = check_g2_shape(M, K0, N0, N1, act, &rf_ok, &stream_ok);
+    if (s != FC_OK) return s;
+    if ((int)variant < 1 || (int)variant > 3) return fail(FC_E_ARG, "variant %d: RF, LDS or STREAM", (int)variant);
+    if (variant == FC_VARIANT_RF ? (waves < 0 || waves > 8) : waves != 0)
+        return fail(FC_E_ARG, "waves=%d: 0..8 for the register-resident form, 0 otherwise", (int)waves);
+    if (variant == FC_VARIANT_RF && !rf_ok)
+        return fail(FC_E_UNSUPPORTED, "register-resident variant needs N0<=128 and W0,W1 within LDS");
+    if (variant == FC_VARIANT_STREAM && !stream_ok)
+        return fail(FC_E_UNSUPPORTED, "streamed variant needs N1<=16128 (biases beside the weight buffers)");
+    if (M == 0) return ok();
+    return hip_status(fc::run_chain_gemm2(H(A), H(W0), H(b0), act, H(W1), H(b1), Hm(D1), M, K0, N0, N1, (int)variant,
+                                          waves, (hipStream_t)stream),
+                      "chain_gemm2_ex");
+}
+
+fc_status chain_gemm2_tune_ex(const fc_half* A, const fc_half* W0, const fc_half* b0, fc_act act, const fc_half* W1,
+                              const fc_half* b1, fc_half* D1, int64_t M, int32_t K0, int32_t N0, int32_t N1,
+                              int32_t reps, fc_tune_entry* table, int32_t capacity, int32_t* count,
+                              fc_tune_entry* best, void* stream)
 {
     bool rf_ok = false, stream_ok = false;
     if (M < 0 || K0 <= 0 || N0 <= 0 || N1 <= 0) return fail(FC_E_SHAPE, "M>=0 and K0, N0, N1 > 0 required");
@@ -199,54 +340,57 @@ fc_status chain_gemm2_tune(const fc_half* A, const fc_half* W0, const fc_half* b
     if (s != FC_OK) return s;
     if (M == 0) return fail(FC_E_SHAPE, "M == 0: nothing to time");
     if (reps < 1 || reps > 1000) return fail(FC_E_SHAPE, "reps=%d outside 1..1000", (int)reps);
+    if (capacity < 0 || (capacity > 0 && !table)) return fail(FC_E_NULL, "table is required for capacity > 0");
+    Config cand[8];
+    const int n = gemm2_candidates(rf_ok, stream_ok, cand);
     hipStream_t st = (hipStream_t)stream;
-    int dev = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e != hipSuccess) return hip_status(e, "chain_gemm2_tune: hipGetDevice");
-    hipEvent_t t0 = nullptr, t1 = nullptr;
-    e = hipEventCreate(&t0);
-    if (e == hipSuccess) e = hipEventCreate(&t1);
-    float tv[4] = {-1.0f, -1.0f, -1.0f, -1.0f};
-    int vbest = -1;
-    const int cand[3] = {fc::VARIANT_RF, fc::VARIANT_STREAM, fc::VARIANT_LDS};
-    for (int i = 0; i < 3 && e == hipSuccess; ++i) {
-        const int v = cand[i];
-        if ((v == fc::VARIANT_RF && !rf_ok) || (v == fc::VARIANT_STREAM && !stream_ok)) continue;
-        auto launch = [&]() {
-            return fc::run_chain_gemm2(H(A), H(W0), H(b0), act, H(W1), H(b1), Hm(D1), M, K0, N0, N1, v, st);
-        };
-        e = launch();   // untimed: first-use set-up (LDS limits, code upload)
-        if (e == hipSuccess) e = hipEventRecord(t0, st);
-        for (int r = 0; r < reps && e == hipSuccess; ++r) e = launch();
-        if (e == hipSuccess) e = hipEventRecord(t1, st);
-        if (e == hipSuccess) e = hipEventSynchronize(t1);
-        float ms = 0.0f;
-        if (e == hipSuccess) e = hipEventElapsedTime(&ms, t0, t1);
-        if (e != hipSuccess) break;
-        tv[v] = 1000.0f * ms / (float)reps;
-        if (vbest < 0 || tv[v] < tv[vbest]) vbest = v;
+    auto launch = [&](const Config& c) {
+        return fc::run_chain_gemm2(H(A), H(W0), H(b0), act, H(W1), H(b1), Hm(D1), M, K0, N0, N1, c.variant, c.waves,
+                                   st);
+    };
+    return profile("chain_gemm2_tune", launch, cand, n, reps, gemm2_key(M, K0, N0, N1, (int)act), table, capacity,
+                   count, best, st);
+}
+
+fc_status chain_gemm2_tune(const fc_half* A, const fc_half* W0, const fc_half* b0, fc_act act, const fc_half* W1,
+                           const fc_half* b1, fc_half* D1, int64_t M, int32_t K0, int32_t N0, int32_t N1,
+                           int32_t reps, fc_variant* best, float* us, void* stream)
+{
+    fc_tune_entry table[8], b{};
+    int32_t n = 0;
+    fc_status s = chain_gemm2_tune_ex(A, W0, b0, act, W1, b1, D1, M, K0, N0, N1, reps, table, 8, &n, &b, stream);
+    if (s != FC_OK) return s;
+    if (best) *best = (fc_variant)b.variant;
+    if (us) {
+        for (int i = 0; i < 4; ++i) us[i] = -1.0f;
+        for (int i = 0; i < n; ++i) {
+            float& u = us[table[i].variant];
+            if (u < 0.0f || table[i].us < u) u = table[i].us;
+        }
+        us[FC_VARIANT_AUTO] = b.us;
     }
-    if (t0) (void)hipEventDestroy(t0);
-    if (t1) (void)hipEventDestroy(t1);
-    if (e != hipSuccess) return hip_status(e, "chain_gemm2_tune");
-    tv[FC_VARIANT_AUTO] = tv[vbest];
-    {
-        std::lock_guard<std::mutex> g(g_tune_mu);
-        g_tune[TuneKey(dev, M, K0, N0, N1, (int)act)] = vbest;
-    }
-    if (best) *best = (fc_variant)vbest;
-    if (us)
-        for (int i = 0; i < 4; ++i) us[i] = tv[i];
     return ok();
 }
 
 fc_status chain_gemm2_auto_variant(int64_t M, int32_t K0, int32_t N0, int32_t N1, fc_act act, fc_variant* out)
 {
+    if (!out) return fail(FC_E_NULL, "out is required");
+    fc_tune_entry e;
+    fc_status s = chain_gemm2_auto_config(M, K0, N0, N1, act, &e);
+    if (s == FC_OK) *out = (fc_variant)e.variant;
+    return s;
+}
+
+fc_status chain_gemm2_auto_config(int64_t M, int32_t K0, int32_t N0, int32_t N1, fc_act act, fc_tune_entry* out)
+{
     bool rf_ok = false, stream_ok = false;
     if (!out) return fail(FC_E_NULL, "out is required");
     fc_status s = check_g2_shape(M, K0, N0, N1, act, &rf_ok, &stream_ok);
     if (s != FC_OK) return s;
-    *out = (fc_variant)auto_variant(M, K0, N0, N1, (int)act, rf_ok, stream_ok);
+    Config c;
+    const bool t = tuned_config(gemm2_key(M, K0, N0, N1, (int)act), &c);
+    if (!t) c = gemm2_config(M, K0, N0, N1, (int)act, rf_ok, stream_ok);
+    *out = fc_tune_entry{c.variant, c.waves, -1.0f};
     return ok();
 }
 
@@ -316,11 +460,10 @@ fc_status gemm_bias_act(const fc_half* A, const fc_half* W, const fc_half* b, fc
                       "gemm_bias_act");
 }
 
-// conv3x3 -> (x scale) + b -> act -> optional 2x2 pool (scale may be NULL),
-// in the kernel form `variant` (fc_conv_variant).
-static fc_status conv_pool_impl(const char* name, const fc_half* x, const fc_half* w, const fc_half* scale,
-                                const fc_half* b, fc_act act, fc_pool pool, fc_half* y, const fc_conv_shape* shape,
-                                uint8_t* argmax, int variant, void* stream)
+// Validation of the conv (+ pool) chain: shapes, pointers, the kernel form.
+static fc_status check_conv_pool(const fc_half* x, const fc_half* w, const fc_half* scale, const fc_half* b,
+                                 fc_act act, fc_pool pool, const fc_half* y, const fc_conv_shape* shape,
+                                 const uint8_t* argmax, int variant, bool* lds_ok, bool* reg_ok)
 {
     fc_status s = check_act(act);
     if (s != FC_OK) return s;
@@ -334,29 +477,89 @@ static fc_status conv_pool_impl(const char* name, const fc_half* x, const fc_hal
     if (!w || (npix > 0 && !x) || (nout > 0 && !y)) return fail(FC_E_NULL, "x, w and y are required");
     if (!aligned16(x) || !aligned16(w) || !aligned16(y) || !aligned16(b) || !aligned16(scale))
         return fail(FC_E_ALIGN, "tensor pointers must be 16-byte aligned");
-    const bool lds_ok = fc::convw_fits(shape->c, shape->k);
-    const bool reg_ok = pool != FC_POOL_NONE && fc::conv_pool_wr_fits(shape->w, shape->c, shape->k);
-    if (variant == FC_CONV_REG_WEIGHTS && !reg_ok)
+    *lds_ok = fc::convw_fits(shape->c, shape->k);
+    *reg_ok = pool != FC_POOL_NONE && fc::conv_pool_wr_fits(shape->w, shape->c, shape->k);
+    if (variant == FC_CONV_REG_WEIGHTS && !*reg_ok)
         return fail(FC_E_UNSUPPORTED, "register-weights conv needs c == 64, 64 < k <= 128, w*c < 2^27 and a pool");
-    if (variant == FC_CONV_LDS_WEIGHTS && !lds_ok) return fail(FC_E_UNSUPPORTED, "weights exceed LDS");
-    if (variant == FC_CONV_AUTO && !lds_ok && !reg_ok) return fail(FC_E_UNSUPPORTED, "weights exceed LDS");
+    if (variant == FC_CONV_LDS_WEIGHTS && !*lds_ok) return fail(FC_E_UNSUPPORTED, "weights exceed LDS");
+    if (variant == FC_CONV_AUTO && !*lds_ok && !*reg_ok) return fail(FC_E_UNSUPPORTED, "weights exceed LDS");
+    return FC_OK;
+}
+
+static hipError_t launch_conv_pool(const fc_half* x, const fc_half* w, const fc_half* scale, const fc_half* b,
+                                   fc_act act, fc_pool pool, fc_half* y, const fc_conv_shape* shape, uint8_t* argmax,
+                                   Config c, hipStream_t st)
+{
+    return fc::run_conv_pool3x3(H(x), H(w), H(scale), H(b), act, pool == FC_POOL_AVG_2X2_S2, Hm(y), argmax, shape->n,
+                                shape->h, shape->w, shape->c, shape->k, c.variant == FC_CONV_REG_WEIGHTS, c.waves, st);
+}
+
+// conv3x3 -> (x scale) + b -> act -> optional 2x2 pool (scale may be NULL),
+// in the kernel form `variant` (fc_conv_variant).
+static fc_status conv_pool_impl(const char* name, const fc_half* x, const fc_half* w, const fc_half* scale,
+                                const fc_half* b, fc_act act, fc_pool pool, fc_half* y, const fc_conv_shape* shape,
+                                uint8_t* argmax, int variant, int waves, void* stream)
+{
+    bool lds_ok = false, reg_ok = false;
+    fc_status s = check_conv_pool(x, w, scale, b, act, pool, y, shape, argmax, variant, &lds_ok, &reg_ok);
+    if (s != FC_OK) return s;
+    if (variant == FC_CONV_LDS_WEIGHTS && pool != FC_POOL_NONE ? (waves < 0 || waves > 8) : waves != 0)
+        return fail(FC_E_ARG, "waves=%d: 0..8 for the pooled LDS-weights form, 0 otherwise", (int)waves);
+    const long nout = pool == FC_POOL_NONE ? (long)shape->n * shape->h * shape->w
+                                           : (long)shape->n * (shape->h / 2) * (shape->w / 2);
     if (nout == 0) return ok();
-    const bool regw = variant == FC_CONV_REG_WEIGHTS || (variant == FC_CONV_AUTO && reg_ok);
     hipStream_t st = (hipStream_t)stream;
     if (pool == FC_POOL_NONE)
         return hip_status(fc::run_conv_bias_act3x3(H(x), H(w), H(scale), H(b), act, Hm(y), shape->n, shape->h,
                                                     shape->w, shape->c, shape->k, st),
                           name);
-    return hip_status(fc::run_conv_pool3x3(H(x), H(w), H(scale), H(b), act, pool == FC_POOL_AVG_2X2_S2, Hm(y),
-                                           argmax, shape->n, shape->h, shape->w, shape->c, shape->k, regw, st),
-                      name);
+    Config c{variant, waves};
+    if (variant == FC_CONV_AUTO) c = conv_config(shape, (int)act, (int)pool, argmax != nullptr, lds_ok, reg_ok);
+    return hip_status(launch_conv_pool(x, w, scale, b, act, pool, y, shape, argmax, c, st), name);
+}
+
+fc_status chain_conv_pool_tune(const fc_half* x, const fc_half* w, const fc_half* scale, const fc_half* shift,
+                               fc_act act, fc_pool pool, fc_half* y, const fc_conv_shape* shape, uint8_t* argmax,
+                               int32_t reps, fc_tune_entry* table, int32_t capacity, int32_t* count,
+                               fc_tune_entry* best, void* stream)
+{
+    bool lds_ok = false, reg_ok = false;
+    fc_status s = check_conv_pool(x, w, scale, shift, act, pool, y, shape, argmax, FC_CONV_AUTO, &lds_ok, &reg_ok);
+    if (s != FC_OK) return s;
+    if (pool == FC_POOL_NONE) return fail(FC_E_ARG, "the profiler times the pooled chains (pool != FC_POOL_NONE)");
+    if ((long)shape->n * (shape->h / 2) * (shape->w / 2) == 0) return fail(FC_E_SHAPE, "empty output: nothing to time");
+    if (reps < 1 || reps > 1000) return fail(FC_E_SHAPE, "reps=%d outside 1..1000", (int)reps);
+    if (capacity < 0 || (capacity > 0 && !table)) return fail(FC_E_NULL, "table is required for capacity > 0");
+    Config cand[8];
+    const int n = conv_candidates(lds_ok, reg_ok, cand);
+    hipStream_t st = (hipStream_t)stream;
+    auto launch = [&](const Config& c) { return launch_conv_pool(x, w, scale, shift, act, pool, y, shape, argmax, c, st); };
+    return profile("chain_conv_pool_tune", launch, cand, n, reps, conv_key(shape, (int)act, (int)pool, argmax != nullptr),
+                   table, capacity, count, best, st);
+}
+
+fc_status chain_conv_pool_auto_config(const fc_conv_shape* shape, fc_act act, fc_pool pool, int32_t with_argmax,
+                                      fc_tune_entry* out)
+{
+    if (!out) return fail(FC_E_NULL, "out is required");
+    fc_status s = check_act(act);
+    if (s != FC_OK) return s;
+    if ((int)pool < 1 || (int)pool > 2) return fail(FC_E_ARG, "pool %d: a pooled chain is required", (int)pool);
+    s = check_conv(shape, 128);
+    if (s != FC_OK) return s;
+    const bool lds_ok = fc::convw_fits(shape->c, shape->k);
+    const bool reg_ok = fc::conv_pool_wr_fits(shape->w, shape->c, shape->k);
+    if (!lds_ok && !reg_ok) return fail(FC_E_UNSUPPORTED, "weights exceed LDS");
+    const Config c = conv_config(shape, (int)act, (int)pool, with_argmax != 0, lds_ok, reg_ok);
+    *out = fc_tune_entry{c.variant, c.waves, -1.0f};
+    return ok();
 }
 
 fc_status chain_conv_pool(const fc_half* x, const fc_half* w, const fc_half* b, fc_act act, fc_pool pool,
                           fc_half* y, const fc_conv_shape* shape, uint8_t* argmax, void* stream)
 {
     return conv_pool_impl(pool == FC_POOL_NONE ? "conv_bias_act" : "chain_conv_pool", x, w, nullptr, b, act, pool, y,
-                          shape, argmax, FC_CONV_AUTO, stream);
+                          shape, argmax, FC_CONV_AUTO, 0, stream);
 }
 
 fc_status chain_conv_bn_pool(const fc_half* x, const fc_half* w, const fc_half* scale, const fc_half* shift,
@@ -364,15 +567,15 @@ fc_status chain_conv_bn_pool(const fc_half* x, const fc_half* w, const fc_half* 
                              void* stream)
 {
     if (!scale) return fail(FC_E_NULL, "scale is required (use chain_conv_pool for a plain bias)");
-    return conv_pool_impl("chain_conv_bn_pool", x, w, scale, shift, act, pool, y, shape, argmax, FC_CONV_AUTO,
+    return conv_pool_impl("chain_conv_bn_pool", x, w, scale, shift, act, pool, y, shape, argmax, FC_CONV_AUTO, 0,
                           stream);
 }
 
 fc_status chain_conv_pool_ex(const fc_half* x, const fc_half* w, const fc_half* scale, const fc_half* shift,
                              fc_act act, fc_pool pool, fc_half* y, const fc_conv_shape* shape, uint8_t* argmax,
-                             fc_conv_variant variant, void* stream)
+                             fc_conv_variant variant, int32_t waves, void* stream)
 {
-    return conv_pool_impl("chain_conv_pool_ex", x, w, scale, shift, act, pool, y, shape, argmax, (int)variant,
+    return conv_pool_impl("chain_conv_pool_ex", x, w, scale, shift, act, pool, y, shape, argmax, (int)variant, waves,
                           stream);
 }
 

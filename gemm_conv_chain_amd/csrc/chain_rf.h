@@ -49,6 +49,8 @@ struct RfArgs {
     int act;
     long ntiles;        // ceil(M / 32)
     long tiles_per_block;
+    int wpb;            // waves per block that own row tiles (1..RF_WAVES; 0 = all): the block
+                        // covers 32 * wpb rows per round, the other waves only stage the weights
     // N-stage chains only (kernel template NMID > 0): NMID middle GEMMs run
     // between the first and the last, each on the previous one's fp16 output
     // kept in the lane.  Middle i maps width Nin_i (N0, then Nm[0]) to Nm[i].
@@ -149,7 +151,8 @@ void k_chain_rf(Loader ld, RfArgs a)
     // ring.
     constexpr int R = KCH >= 4 ? 4 : (KCH > 0 ? KCH : 2);
     constexpr int PD = R - 1;
-    long tile = t_begin + wave;
+    const int wpb = a.wpb > 0 ? a.wpb : RF_WAVES;
+    long tile = wave < wpb ? t_begin + wave : t_end;
     half8 xr[R][4];
     typename Loader::Row row;
     // Prologue.  Every wave first issues its share of the weight (and bias)
@@ -215,7 +218,7 @@ void k_chain_rf(Loader ld, RfArgs a)
 #pragma unroll
     for (int t1 = 0; t1 < 2; ++t1) w1lane[t1] = W1n.p + frag_lane_off(W1n, 32 * t1, lane) + 4 * hh * W1n.ld;
 
-    for (; tile < t_end; tile += RF_WAVES) {
+    for (; tile < t_end; tile += wpb) {
         floatx16 acc0[NT0];
 #pragma unroll
         for (int t = 0; t < NT0; ++t) acc0[t] = zero16();
@@ -270,7 +273,7 @@ void k_chain_rf(Loader ld, RfArgs a)
         // branch leave the ring registers to be merged after it, and that copy
         // waits for every load in flight -- the prefetch's full latency before
         // GEMM1.
-        const long ntile = tile + RF_WAVES;
+        const long ntile = tile + wpb;
         const typename Loader::Row nrow = ld.row((ntile < t_end ? ntile : a.ntiles) * 32 + lr);
 #pragma unroll
         for (int p = 0; p < PD; ++p)
@@ -480,7 +483,7 @@ static hipError_t launch_rf_k(const Loader& ld, RfArgs a, hipStream_t st)
     static std::atomic<unsigned long long> lds_set{0};
     hipError_t e = allow_full_lds((const void*)k_chain_rf<NT0, KCH, Loader, NMID>, &lds_set);
     if (e != hipSuccess) return e;
-    const long per_block_min = RF_WAVES;  // at least one tile per wave
+    const long per_block_min = a.wpb > 0 ? a.wpb : RF_WAVES;  // at least one tile per tile-owning wave
     long grid = device_cu_count();
     if (grid * per_block_min > a.ntiles) grid = (a.ntiles + per_block_min - 1) / per_block_min;
     if (grid < 1) grid = 1;
@@ -513,5 +516,9 @@ inline hipError_t launch_rf(const Loader& ld, const RfArgs& a, int nt0, hipStrea
     }
     return hipErrorInvalidValue;
 }
+
+// Dense-row instantiations (gemm_rf.hip): the two-GEMM chain (nmid = 0) and
+// the N-stage chains (nmid = 1, 2 middle GEMMs).
+hipError_t run_rf_dense(const half_t* A, const RfArgs& a, int nmid, hipStream_t st);
 
 }  // namespace fc

@@ -446,6 +446,9 @@ inline bool stream_fits_lds(int N0, int N1)
     return N0 <= 256 && (long)cs_lds_bytes(N0P, 0) + 4 * N1p <= (long)RF_LDS_LIMIT;
 }
 
+// Instantiated in gemm_stream.hip.
+hipError_t run_stream(const StreamArgs& a, int act, hipStream_t st);
+
 inline hipError_t launch_stream(const StreamArgs& a, int act, hipStream_t st)
 {
     if (a.N0 <= 64) return launch_stream_n<2>(a, act, st);

@@ -138,6 +138,7 @@ struct ConvWArgs {
     int act;
     long ntiles;       // 64-row tiles
     long tiles_per_block;
+    int wpb;           // waves per block that own tiles (1..NWAVES; 0 = all); the others only stage weights
     // row decoding: STORE: pixel = (n, p, q) with fa = P*Q, fb = Q;
     // POOL: window = (n, i, j) with fa = (P/2)*(Q/2), fb = Q/2; fc16 = C/16
     FastDiv fa, fb, fc16;
@@ -302,7 +303,8 @@ void k_conv_w(ConvWArgs a)
         }
     };
 
-    long tile = t_begin + wave;
+    const int wpb = a.wpb > 0 ? a.wpb : NWAVES;
+    long tile = wave < wpb ? t_begin + wave : t_end;
     Conv3x3Rows::Row rows[2];
     QRows qrows;
     if (tile < t_end) {
@@ -324,7 +326,7 @@ void k_conv_w(ConvWArgs a)
         bs[i] = (a.b && i < a.K) ? (float)a.b[i] : 0.0f;
         ss[i] = (a.s && i < a.K) ? (float)a.s[i] : 1.0f;
     }
-    if (tid == 0) *next_tile = (int)(t_begin + NWAVES);
+    if (tid == 0) *next_tile = (int)(t_begin + wpb);
     __syncthreads();
 
     // Per-lane parts of the W fragment addresses: column k_out = 32t + lane%32,
@@ -624,7 +626,7 @@ static hipError_t launch_convw_k(ConvWArgs a, hipStream_t st)
     static std::atomic<unsigned long long> lds_set{0};
     hipError_t e = allow_full_lds((const void*)k_conv_w<NTK, EPI, KCH>, &lds_set);
     if (e != hipSuccess) return e;
-    constexpr int nwaves = convw_threads(KCH) / 64;
+    const int nwaves = a.wpb > 0 ? a.wpb : convw_threads(KCH) / 64;
     long grid = device_cu_count();
     if (grid * nwaves > a.ntiles) grid = (a.ntiles + nwaves - 1) / nwaves;
     if (grid < 1) grid = 1;
@@ -666,6 +668,7 @@ hipError_t run_conv_bias_act3x3(const half_t* x, const half_t* w, const half_t* 
     a.x = x; a.w = w; a.s = scale; a.b = b; a.y = y; a.argmax = nullptr;
     a.NB = NB; a.H = H; a.W = W; a.C = C; a.K = K;
     a.Kr = 9 * C; a.Kp = (9 * C + 63) / 64 * 64; a.act = act;
+    a.wpb = 0;
     const long rows = (long)NB * H * W;
     if (rows == 0) return hipSuccess;
     a.ntiles = (rows + 63) / 64;
@@ -680,13 +683,14 @@ hipError_t run_conv_pool_wr(const half_t* x, const half_t* w, const half_t* scal
 
 hipError_t run_conv_pool3x3(const half_t* x, const half_t* w, const half_t* scale, const half_t* b, int act,
                             bool avg, half_t* y, uint8_t* argmax, int NB, int H, int W, int C, int K, bool regw,
-                            hipStream_t st)
+                            int waves, hipStream_t st)
 {
     if (regw) return run_conv_pool_wr(x, w, scale, b, act, avg, y, argmax, NB, H, W, K, st);
     ConvWArgs a;
     a.x = x; a.w = w; a.s = scale; a.b = b; a.y = y; a.argmax = argmax;
     a.NB = NB; a.H = H; a.W = W; a.C = C; a.K = K;
     a.Kr = 9 * C; a.Kp = (9 * C + 63) / 64 * 64; a.act = act;
+    a.wpb = waves;
     const long rows = (long)NB * (H / 2) * (W / 2) * 4;
     if (rows == 0) return hipSuccess;
     a.ntiles = (rows + 63) / 64;

@@ -1,7 +1,8 @@
 // gemm_chain.hip -- fused back-to-back GEMM kernels and the single-GEMM
 // (unfused baseline) kernel.
 //
-//   register-resident chain   : chain_rf.h  (N0 <= 128, weights fit in LDS)
+//   register-resident chain   : chain_rf.h, instantiated in gemm_rf.hip (N0 <= 128, weights fit in LDS)
+//   streamed-weight chain     : chain_stream.h, instantiated in gemm_stream.hip
 //   LDS-resident chain        : k_gemm_lds<NT0W, true>   (N0 <= 256)
 //   gemm + bias + act         : k_gemm_lds<NT0W, false>  (any N, 256-wide column blocks)
 //
@@ -393,7 +394,7 @@ static hipError_t launch_lds_t(const LdsArgs& a, hipStream_t st)
 // ---------------------------------------------------------------- entry points
 
 hipError_t run_chain_gemm2(const half_t* A, const half_t* W0, const half_t* b0, int act, const half_t* W1,
-                           const half_t* b1, half_t* D1, long M, int K0, int N0, int N1, int variant,
+                           const half_t* b1, half_t* D1, long M, int K0, int N0, int N1, int variant, int waves,
                            hipStream_t st)
 {
     if (M == 0) return hipSuccess;
@@ -406,14 +407,8 @@ hipError_t run_chain_gemm2(const half_t* A, const half_t* W0, const half_t* b0, 
         a.act = act;
         a.ntiles = (M + 31) / 32;
         a.tiles_per_block = 0;
-        if (K0 == 64 || K0 == 256 || K0 == 576) {   // compile-time chunk counts: quad-coalesced rows
-            DenseRowsQ ld;
-            ld.A = A; ld.M = M; ld.K = K0;
-            return launch_rf(ld, a, (N0 + 31) / 32, st);
-        }
-        DenseRows ld;
-        ld.A = A; ld.M = M; ld.K = K0;
-        return launch_rf(ld, a, (N0 + 31) / 32, st);
+        a.wpb = waves;
+        return run_rf_dense(A, a, 0, st);
     }
     if (variant == VARIANT_STREAM) {
         StreamArgs a;
@@ -421,7 +416,7 @@ hipError_t run_chain_gemm2(const half_t* A, const half_t* W0, const half_t* b0, 
         a.M = M; a.K0 = K0; a.N0 = N0; a.N1 = N1;
         a.N1p = (N1 + CS_N1C - 1) / CS_N1C * CS_N1C;
         a.ntiles = (M + CS_MT - 1) / CS_MT;
-        return launch_stream(a, act, st);
+        return run_stream(a, act, st);
     }
     LdsArgs a;
     a.A = A; a.W0 = W0; a.b0 = b0; a.W1 = W1; a.b1 = b1; a.out = D1;
@@ -491,15 +486,7 @@ hipError_t run_chain_gemmN(const half_t* A, int nst, const half_t* const* W, con
     if (M == 0) return hipSuccess;
     RfArgs a{};
     gemmn_args(nst, W, b, act, widths, D, M, a);
-    const int nt0 = (a.N0 + 31) / 32;
-    if (a.K0 == 64 || a.K0 == 256 || a.K0 == 576) {
-        DenseRowsQ ld;
-        ld.A = A; ld.M = M; ld.K = a.K0;
-        return nst == 3 ? launch_rf<DenseRowsQ, 1>(ld, a, nt0, st) : launch_rf<DenseRowsQ, 2>(ld, a, nt0, st);
-    }
-    DenseRows ld;
-    ld.A = A; ld.M = M; ld.K = a.K0;
-    return nst == 3 ? launch_rf<DenseRows, 1>(ld, a, nt0, st) : launch_rf<DenseRows, 2>(ld, a, nt0, st);
+    return run_rf_dense(A, a, nst - 2, st);
 }
 
 bool stream_fits(int N0, int N1)

@@ -130,6 +130,13 @@ fc_status chain_gemm2_variant(const fc_half *A, const fc_half *W0, const fc_half
                               const fc_half *W1, const fc_half *b1, fc_half *D1,
                               int64_t M, int32_t K0, int32_t N0, int32_t N1,
                               fc_variant variant, void *stream);
+/* chain_gemm2_ex -- one explicit configuration, as the profiler times it:
+ * variant (not AUTO) and, for FC_VARIANT_RF, waves = tile-owning waves per
+ * block, 1..8 (0 = 8); other variants take waves == 0.  FC_E_ARG otherwise. */
+fc_status chain_gemm2_ex(const fc_half *A, const fc_half *W0, const fc_half *b0, fc_act act,
+                         const fc_half *W1, const fc_half *b1, fc_half *D1,
+                         int64_t M, int32_t K0, int32_t N0, int32_t N1,
+                         fc_variant variant, int32_t waves, void *stream);
 
 /*
  * chain_gemm2_tune -- hardware profiling of the fused-chain variants for one
@@ -157,13 +164,48 @@ fc_status chain_gemm2_tune(const fc_half *A, const fc_half *W0, const fc_half *b
                            int64_t M, int32_t K0, int32_t N0, int32_t N1,
                            int32_t reps, fc_variant *best, float *us, void *stream);
 
+/* One timed configuration of the profiler: the kernel form (fc_variant for
+ * the GEMM chains, fc_conv_variant for the conv chains), the number of waves
+ * per block that own row tiles (0: the form's own block shape; the
+ * register-resident GEMM chain takes 8, 4, 2 or 1 -- a block then covers
+ * 32 * waves rows per round -- and the LDS-weights conv 8 or 4), and the
+ * mean microseconds per launch (-1 where nothing was timed). */
+typedef struct {
+    int32_t variant;
+    int32_t waves;
+    float us;
+} fc_tune_entry;
+
+/*
+ * chain_gemm2_tune_ex -- as chain_gemm2_tune, over every configuration the
+ * library can run for the shape (each residence form; the register-resident
+ * one with 8, 4, 2 and 1 tile-owning waves per block).  table (host, may be
+ * NULL when capacity == 0) receives min(count, capacity) rows in the order
+ * timed; count (host, may be NULL) the number of configurations timed; best
+ * (host, may be NULL) the fastest, which is cached for the shape and runs
+ * under FC_VARIANT_AUTO.  D1 holds the chain's result on return.  BLOCKING,
+ * like chain_gemm2_tune.  FC_E_NULL if capacity > 0 and table is NULL.
+ */
+fc_status chain_gemm2_tune_ex(const fc_half *A, const fc_half *W0, const fc_half *b0, fc_act act,
+                              const fc_half *W1, const fc_half *b1, fc_half *D1,
+                              int64_t M, int32_t K0, int32_t N0, int32_t N1, int32_t reps,
+                              fc_tune_entry *table, int32_t capacity, int32_t *count, fc_tune_entry *best,
+                              void *stream);
+
+/* The configuration FC_VARIANT_AUTO runs for this shape on the current
+ * device (us = -1): the tuned one, else the static rule -- register-resident
+ * when it applies, with the smallest power-of-two number of tile-owning waves
+ * (1..8) that covers ceil(M / 32) row tiles with one block per CU; else
+ * STREAM; else LDS.  Host only. */
+fc_status chain_gemm2_auto_config(int64_t M, int32_t K0, int32_t N0, int32_t N1, fc_act act, fc_tune_entry *out);
+
 /* The variant FC_VARIANT_AUTO runs for this shape on the current device:
  * the tuned choice if chain_gemm2_tune cached one, else the static rule (RF
  * when it applies, else STREAM, else LDS).  Host only, launches nothing.
  * Returns FC_E_SHAPE / FC_E_ARG / FC_E_UNSUPPORTED as chain_gemm2 would. */
 fc_status chain_gemm2_auto_variant(int64_t M, int32_t K0, int32_t N0, int32_t N1, fc_act act, fc_variant *out);
 
-/* Forget every tuned choice (all devices). */
+/* Forget every tuned choice (all devices, GEMM and conv chains). */
 void fc_tune_clear(void);
 
 /*
@@ -221,14 +263,42 @@ fc_status chain_conv_bn_pool(const fc_half *x, const fc_half *w, const fc_half *
 /*
  * chain_conv_pool_ex -- chain_conv_pool (scale == NULL: shift is the bias) or
  * chain_conv_bn_pool (scale != NULL) with an explicit kernel form
- * (fc_conv_variant).  FC_E_UNSUPPORTED if the requested form does not take
- * the shape or the pool (FC_CONV_REG_WEIGHTS needs c == 64, 64 < k <= 128,
- * w * c < 2^27 and pool != FC_POOL_NONE); FC_E_ARG for an unknown form.
+ * (fc_conv_variant) and, for FC_CONV_LDS_WEIGHTS with a pool, the number of
+ * tile-owning waves per block (1..8; 0 = 8); other forms take waves == 0.
+ * FC_E_UNSUPPORTED if the requested form does not take the shape or the pool
+ * (FC_CONV_REG_WEIGHTS needs c == 64, 64 < k <= 128, w * c < 2^27 and
+ * pool != FC_POOL_NONE); FC_E_ARG for an unknown form or a bad waves value.
  * Everything else as chain_conv_pool.
  */
 fc_status chain_conv_pool_ex(const fc_half *x, const fc_half *w, const fc_half *scale, const fc_half *shift,
                              fc_act act, fc_pool pool, fc_half *y, const fc_conv_shape *shape, uint8_t *argmax,
-                             fc_conv_variant variant, void *stream);
+                             fc_conv_variant variant, int32_t waves, void *stream);
+
+/*
+ * chain_conv_pool_tune -- hardware profiling of the pooled conv chain for one
+ * shape (BOLT notes, "Light-weight performance profiler"; Welder notes,
+ * "Tile-graph Scheduling": candidate configurations measured on the GPU, the
+ * fastest kept): times the register-weights form (where it takes the shape)
+ * and the LDS-weights form with 8 and 4 tile-owning waves per block, reps
+ * launches each after one untimed launch, on the caller's buffers, and
+ * caches the fastest for (device, n, h, w, c, k, act, pool, argmax != NULL):
+ * chain_conv_pool / chain_conv_bn_pool / FC_CONV_AUTO then run it.
+ * Arguments as chain_conv_pool_ex (scale may be NULL), pool must be a 2x2
+ * pool, plus reps (1..1000), table / capacity / count / best as
+ * chain_gemm2_tune_ex.  y (and argmax) hold the chain's result on return.
+ * BLOCKING (waits for its own events; not during stream capture).
+ */
+fc_status chain_conv_pool_tune(const fc_half *x, const fc_half *w, const fc_half *scale, const fc_half *shift,
+                               fc_act act, fc_pool pool, fc_half *y, const fc_conv_shape *shape, uint8_t *argmax,
+                               int32_t reps, fc_tune_entry *table, int32_t capacity, int32_t *count,
+                               fc_tune_entry *best, void *stream);
+
+/* The configuration FC_CONV_AUTO runs for this pooled shape on the current
+ * device (us = -1): the tuned one, else the register-weights form where it
+ * applies, else the LDS-weights form with 8 waves.  with_argmax: whether the
+ * call passes an argmax output (a different kernel).  Host only. */
+fc_status chain_conv_pool_auto_config(const fc_conv_shape *shape, fc_act act, fc_pool pool, int32_t with_argmax,
+                                      fc_tune_entry *out);
 
 /*
  * chain_conv2 -- y = conv1x1(act(conv(x, w0) + b0), w1) + b1, the first conv's

@@ -25,7 +25,8 @@ def test_exports_every_declared_symbol(L):
     names = fc.exported_names()
     for n in ("chain_gemm2", "chain_gemm2_variant", "chain_gemmN", "chain_conv_pool", "chain_conv2", "gemm_bias_act",
               "conv_bias_act", "maxpool2x2", "pad_channels", "fc_abi_version", "fc_status_str", "fc_last_error",
-              "chain_gemm2_tune", "chain_gemm2_auto_variant", "fc_tune_clear", "chain_convN", "chain_conv_bn_pool", "fc_probe_mfma", "chain_conv_pool_ex"):
+              "chain_gemm2_tune", "chain_gemm2_auto_variant", "fc_tune_clear", "chain_convN", "chain_conv_bn_pool", "fc_probe_mfma", "chain_conv_pool_ex", "chain_gemm2_ex",
+              "chain_gemm2_tune_ex", "chain_gemm2_auto_config", "chain_conv_pool_tune", "chain_conv_pool_auto_config"):
         assert n in names
     for n in names:
         assert hasattr(L, n), n
@@ -131,16 +132,52 @@ def test_conv_validation(L):
 def test_conv_variant_validation(L):
     sh = shape(c=64, k=128)
     ex = L.chain_conv_pool_ex
-    ex.argtypes = [ctypes.c_void_p] * 4 + [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.POINTER(fc.ConvShape),
-                                           ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
-    assert ex(P, P, NUL, NUL, 1, 1, P2, ctypes.byref(sh), NUL, 3, None) == E_ARG
-    assert ex(P, P, NUL, NUL, 1, 1, P2, ctypes.byref(sh), NUL, -1, None) == E_ARG
+    assert ex(P, P, NUL, NUL, 1, 1, P2, ctypes.byref(sh), NUL, 3, 0, None) == E_ARG
+    assert ex(P, P, NUL, NUL, 1, 1, P2, ctypes.byref(sh), NUL, -1, 0, None) == E_ARG
     # register-weights form: c == 64, 64 < k <= 128 and a pool
-    assert ex(P, P, NUL, NUL, 1, 1, P2, ctypes.byref(shape(c=32, k=128)), NUL, 2, None) == E_UNSUP
-    assert ex(P, P, NUL, NUL, 1, 1, P2, ctypes.byref(shape(c=64, k=64)), NUL, 2, None) == E_UNSUP
-    assert ex(P, P, NUL, NUL, 1, 0, P2, ctypes.byref(sh), NUL, 2, None) == E_UNSUP
-    assert ex(P, P, NUL, NUL, 1, 1, P2, ctypes.byref(shape(c=128, k=128)), NUL, 1, None) == E_UNSUP   # LDS form: weights exceed LDS
-    assert ex(P, P, NUL, NUL, 1, 2, P2, ctypes.byref(shape(h=1)), NUL, 2, None) == OK                 # empty pooled output
+    assert ex(P, P, NUL, NUL, 1, 1, P2, ctypes.byref(shape(c=32, k=128)), NUL, 2, 0, None) == E_UNSUP
+    assert ex(P, P, NUL, NUL, 1, 1, P2, ctypes.byref(shape(c=64, k=64)), NUL, 2, 0, None) == E_UNSUP
+    assert ex(P, P, NUL, NUL, 1, 0, P2, ctypes.byref(sh), NUL, 2, 0, None) == E_UNSUP
+    assert ex(P, P, NUL, NUL, 1, 1, P2, ctypes.byref(shape(c=128, k=128)), NUL, 1, 0, None) == E_UNSUP   # LDS form: weights exceed LDS
+    assert ex(P, P, NUL, NUL, 1, 2, P2, ctypes.byref(shape(h=1)), NUL, 2, 0, None) == OK                 # empty pooled output
+    # tile-owning waves: 0..8 for the pooled LDS-weights form only
+    assert ex(P, P, NUL, NUL, 1, 1, P2, ctypes.byref(sh), NUL, 1, 9, None) == E_ARG
+    assert ex(P, P, NUL, NUL, 1, 1, P2, ctypes.byref(sh), NUL, 2, 4, None) == E_ARG
+    assert ex(P, P, NUL, NUL, 1, 0, P2, ctypes.byref(sh), NUL, 1, 4, None) == E_ARG
+    assert ex(P, P, NUL, NUL, 1, 1, P2, ctypes.byref(shape(h=1)), NUL, 1, 4, None) == OK
+
+
+def test_tuner_validation(L):
+    E = fc.TuneEntry
+    t = (E * 4)()
+    n = ctypes.c_int32(0)
+    b = E()
+    tx = L.chain_gemm2_tune_ex
+    assert tx(P, P, NUL, 1, P, NUL, P2, 512, 64, 64, 64, 0, t, 4, ctypes.byref(n), ctypes.byref(b), None) == E_SHAPE
+    assert tx(P, P, NUL, 1, P, NUL, P2, 512, 64, 64, 64, 1001, t, 4, ctypes.byref(n), ctypes.byref(b), None) == E_SHAPE
+    assert tx(P, P, NUL, 1, P, NUL, P2, 0, 64, 64, 64, 5, t, 4, ctypes.byref(n), ctypes.byref(b), None) == E_SHAPE
+    assert tx(P, P, NUL, 1, P, NUL, P2, 512, 64, 64, 64, 5, None, 4, ctypes.byref(n), ctypes.byref(b), None) == E_NULL
+    assert tx(P, P, NUL, 1, P, NUL, P2, 512, 64, 64, 60, 5, t, 4, ctypes.byref(n), ctypes.byref(b), None) == E_SHAPE
+    ct = L.chain_conv_pool_tune
+    sh = shape(c=64, k=128)
+    assert ct(P, P, NUL, NUL, 1, 0, P2, ctypes.byref(sh), NUL, 5, t, 4, ctypes.byref(n), ctypes.byref(b), None) == E_ARG
+    assert ct(P, P, NUL, NUL, 1, 1, P2, ctypes.byref(sh), NUL, 0, t, 4, ctypes.byref(n), ctypes.byref(b), None) == E_SHAPE
+    assert ct(P, P, NUL, NUL, 1, 1, P2, ctypes.byref(shape(h=1)), NUL, 5, t, 4, ctypes.byref(n), ctypes.byref(b), None) == E_SHAPE
+    assert ct(P, P, NUL, NUL, 1, 1, P2, ctypes.byref(sh), NUL, 5, None, 4, ctypes.byref(n), ctypes.byref(b), None) == E_NULL
+    # explicit configurations
+    gx = L.chain_gemm2_ex
+    assert gx(P, P, NUL, 1, P, NUL, P2, 512, 64, 64, 64, 1, 9, None) == E_ARG
+    assert gx(P, P, NUL, 1, P, NUL, P2, 512, 64, 64, 64, 0, 0, None) == E_ARG   # AUTO is not a configuration
+    assert gx(P, P, NUL, 1, P, NUL, P2, 512, 64, 64, 64, 2, 4, None) == E_ARG   # LDS form takes waves == 0
+    assert gx(P, P, NUL, 1, P, NUL, P2, 0, 64, 64, 64, 1, 2, None) == OK
+    # the untuned rule, queried without a GPU
+    fc.tune_clear()
+    assert fc.auto_config(65536, 256, 64, 128) == {"variant": "rf", "waves": 8}
+    assert fc.auto_config(512, 64, 64, 64) == {"variant": "rf", "waves": 1}       # 16 row tiles: 16 one-wave blocks
+    assert fc.auto_config(20000, 256, 64, 128) == {"variant": "rf", "waves": 4}
+    assert fc.auto_config(65536, 576, 256, 256, "gelu_tanh") == {"variant": "stream", "waves": 0}
+    assert fc.conv_auto_config(32, 112, 112, 64, 128) == {"variant": "reg_weights", "waves": 0}
+    assert fc.conv_auto_config(2, 8, 8, 32, 64) == {"variant": "lds_weights", "waves": 8}
 
 
 def test_empty_tensors_may_be_null(L):

@@ -1,0 +1,115 @@
+"""The configuration profiler (BOLT notes, "Light-weight performance
+profiler"; Welder notes, "Tile-graph Scheduling": candidate configurations
+are measured on the GPU and the fastest is kept): every configuration it can
+choose computes the chain correctly, every candidate is timed, the fastest is
+cached per shape and then runs under 'auto'."""
+import numpy as np
+import pytest
+
+import oracle
+from gemm_conv_chain_amd import inputs
+from parity import assert_close, to_np
+from test_gpu_conv import check_pool, dev
+
+pytestmark = pytest.mark.gpu
+torch = pytest.importorskip("torch")
+ACTS = {"none": oracle.ACT_NONE, "relu": oracle.ACT_RELU, "gelu_tanh": oracle.ACT_GELU_TANH}
+
+
+@pytest.fixture(scope="module")
+def fc():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import gemm_conv_chain_amd as m
+    m.lib()
+    return m
+
+
+def gemm_ref(d, act):
+    ref, _ = oracle.chain_gemm2(d["A"], d["W0"], d["b0"], ACTS[act], d["W1"], d["b1"])
+    return ref
+
+
+@pytest.mark.parametrize("waves", [1, 2, 4, 8])
+@pytest.mark.parametrize("M,K0,N0,N1", [(512, 64, 64, 64), (1000, 256, 64, 128), (70001, 256, 64, 128),
+                                        (333, 200, 96, 136)])
+def test_gemm2_rf_waves(fc, M, K0, N0, N1, waves):
+    # the register-resident form with 1..8 tile-owning waves per block (a block
+    # covers 32 * waves rows per round); ragged last tiles, a runtime chunk count
+    d = inputs.gemm2_inputs(M, K0, N0, N1, "uniform", seed=M + waves)
+    A, W0, b0, W1, b1 = (dev(d[k]) for k in ("A", "W0", "b0", "W1", "b1"))
+    print("case rf waves", M, K0, N0, N1, waves, flush=True)
+    out = to_np(fc.chain_gemm2(A, W0, b0, W1, b1, act="relu", variant="rf", waves=waves))
+    assert_close(out, gemm_ref(d, "relu"), "rf waves=%d" % waves)
+
+
+@pytest.mark.parametrize("waves", [1, 3, 4, 8])
+@pytest.mark.parametrize("n,h,w,c,k", [(3, 30, 34, 64, 128), (2, 9, 6, 32, 64)])
+def test_conv_lds_weights_waves(fc, n, h, w, c, k, waves):
+    d = inputs.conv_pool_inputs(n, h, w, c, k, seed=n * h + waves)
+    print("case conv lds waves", n, h, w, c, k, waves, flush=True)
+    y, am = fc.chain_conv_pool(dev(d["x"]), dev(d["w"]), dev(d["b"]), argmax=True, variant="lds_weights", waves=waves)
+    y2 = fc.chain_conv_pool(dev(d["x"]), dev(d["w"]), dev(d["b"]), variant="lds_weights", waves=waves)
+    torch.cuda.synchronize()
+    y, am, y2 = to_np(y), to_np(am), to_np(y2)
+    assert np.array_equal(y.view(np.uint16), y2.view(np.uint16))
+    check_pool(y, am, d["x"], d["w"], d["b"], "conv lds waves=%d" % waves)
+
+
+@pytest.mark.parametrize("M,K0,N0,N1,act", [(512, 64, 64, 64, "relu"), (20000, 256, 64, 128, "relu"),
+                                            (4000, 576, 256, 256, "gelu_tanh")])
+def test_tune_gemm2_table(fc, M, K0, N0, N1, act):
+    d = inputs.gemm2_inputs(M, K0, N0, N1, "uniform", seed=17)
+    A, W0, b0, W1, b1 = (dev(d[k]) for k in ("A", "W0", "b0", "W1", "b1"))
+    print("case tune table", M, K0, N0, N1, act, flush=True)
+    fc.tune_clear()
+    best, table, out = fc.tune_chain_gemm2_table(A, W0, b0, W1, b1, act=act, reps=3)
+    torch.cuda.synchronize()
+    print(best, table, flush=True)
+    ref = gemm_ref(d, act)
+    assert_close(to_np(out), ref, "tuned output")
+    cfgs = {(r["variant"], r["waves"]) for r in table}
+    assert all(r["us"] > 0 for r in table)
+    if N0 <= 128:
+        # M_t / waves per block: four values of the register-resident form
+        assert {("rf", w) for w in (1, 2, 4, 8)} <= cfgs
+    assert ("lds", 0) in cfgs and ("stream", 0) in cfgs     # the residence forms
+    fastest = min(table, key=lambda r: r["us"])
+    assert (best["variant"], best["waves"]) == (fastest["variant"], fastest["waves"])
+    assert fc.auto_config(M, K0, N0, N1, act) == {"variant": best["variant"], "waves": best["waves"]}
+    assert_close(to_np(fc.chain_gemm2(A, W0, b0, W1, b1, act=act)), ref, "auto after tuning")
+    fc.tune_clear()
+    assert fc.auto_config(M, K0, N0, N1, act)["variant"] == ("rf" if N0 <= 128 else "stream")
+    if N0 <= 128:   # untuned: the smallest power-of-two wave count covering the row tiles, one block per CU
+        cus = torch.cuda.get_device_properties(0).multi_processor_count
+        w = 1
+        while w < 8 and w * cus < (M + 31) // 32:
+            w *= 2
+        assert fc.auto_config(M, K0, N0, N1, act)["waves"] == w
+
+
+@pytest.mark.parametrize("pool", ["max2x2", "avg2x2"])
+def test_tune_conv_pool(fc, pool):
+    d = inputs.conv_pool_inputs(3, 30, 34, 64, 128, seed=23)
+    x, w, b = dev(d["x"]), dev(d["w"]), dev(d["b"])
+    print("case tune conv", pool, flush=True)
+    fc.tune_clear()
+    best, table, out = fc.tune_conv_pool(x, w, b, pool=pool, reps=3)
+    torch.cuda.synchronize()
+    print(best, table, flush=True)
+    cfgs = {(r["variant"], r["waves"]) for r in table}
+    assert cfgs == {("reg_weights", 0), ("lds_weights", 8), ("lds_weights", 4)}
+    assert all(r["us"] > 0 for r in table)
+    fastest = min(table, key=lambda r: r["us"])
+    assert (best["variant"], best["waves"]) == (fastest["variant"], fastest["waves"])
+    assert fc.conv_auto_config(3, 30, 34, 64, 128, pool=pool) == {"variant": best["variant"], "waves": best["waves"]}
+    if pool == "max2x2":
+        yo, _, _, _ = oracle.chain_conv_pool(d["x"], d["w"], d["b"], oracle.ACT_RELU)
+    else:
+        yo, _ = oracle.chain_conv_avgpool(d["x"], d["w"], d["b"], oracle.ACT_RELU)
+    assert_close(to_np(out), yo.astype(np.float64), "tuned conv output")
+    assert_close(to_np(fc.chain_conv_pool(x, w, b, pool=pool)), yo.astype(np.float64), "auto after tuning")
+    # an argmax output selects another kernel: untuned, it keeps the rule
+    assert fc.conv_auto_config(3, 30, 34, 64, 128, pool=pool, argmax=True)["variant"] == "reg_weights"
+    fc.tune_clear()
+    assert fc.conv_auto_config(3, 30, 34, 64, 128, pool=pool) == {"variant": "reg_weights", "waves": 0}
