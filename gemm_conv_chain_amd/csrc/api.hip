@@ -69,7 +69,7 @@ fc_status check_act(fc_act act)
     return FC_OK;
 }
 
-// Shapes the conv kernels implement: 3x3, stride 1, pad 1, c % 32, k % 8.
+// Shapes the conv kernels implement: 3x3, stride 1, pad 1, c % 8, k % 8.
 fc_status check_conv(const fc_conv_shape* s, int kmax)
 {
     if (!s) return fail(FC_E_NULL, "shape is NULL");
@@ -79,7 +79,6 @@ fc_status check_conv(const fc_conv_shape* s, int kmax)
     if (s->c % 8 || s->k % 8) return fail(FC_E_SHAPE, "c=%d and k=%d must be multiples of 8", s->c, s->k);
     if (s->r != 3 || s->s != 3 || s->stride != 1 || s->pad != 1)
         return fail(FC_E_UNSUPPORTED, "only 3x3 stride-1 pad-1 convolutions are implemented");
-    if (s->c % 32) return fail(FC_E_UNSUPPORTED, "c=%d: pad channels to a multiple of 32", s->c);
     if (s->k > kmax) return fail(FC_E_UNSUPPORTED, "k=%d exceeds the %d output channels one block keeps", s->k, kmax);
     if ((long)s->n * s->h * s->w > 0x7fffffffL)
         return fail(FC_E_UNSUPPORTED, "n*h*w exceeds 2^31 - 1 pixels (pixel indices are 32-bit)");

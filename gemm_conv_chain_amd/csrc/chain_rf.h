@@ -136,7 +136,9 @@ void k_chain_rf(Loader ld, RfArgs a)
     lds_float* bms = b1s + a.N1p;   // middle biases (NMID > 0), Nmp[0] then Nmp[1]
     lds_half* Ost = (lds_half*)(bms + (NMID > 0 ? a.Nmp[0] : 0) + (NMID > 1 ? a.Nmp[1] : 0)) + wave * 32 * RF_OLD;
 
-    const long t_begin = (long)blockIdx.x * a.tiles_per_block;
+    // Block ranges renumbered so that each XCD works on one contiguous stretch
+    // of rows (the conv loader's 3x3 halo rows are then shared within one L2).
+    const long t_begin = (long)xcd_block(blockIdx.x, gridDim.x) * a.tiles_per_block;
     const long t_end = min(t_begin + a.tiles_per_block, a.ntiles);
     const int nch = KCH ? KCH : a.K0p >> 6;
 

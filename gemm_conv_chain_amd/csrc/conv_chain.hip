@@ -25,14 +25,15 @@ namespace fc {
 
 // ------------------------------------------------------------- row loader
 // 3x3, stride 1, pad 1 NHWC conv pixels as GEMM rows (P = H, Q = W).  A lane
-// half h reads, for chunk c, the 32 consecutive k = 64c + 32h + [0, 32): a
-// single (r, s) position and 32 consecutive channels (C % 32 == 0).
+// reads 8 consecutive k at a time (one MFMA k-group): 8 consecutive channels
+// of one (r, s) position, since C % 8 == 0 (the pages' alignment of 8 fp16 =
+// 128 bits).
 struct Conv3x3Rows {
     static constexpr bool kRaw = false;   // loads land in operand layout
     const half_t* x;
     int H, W, C;
     long M;   // N*H*W (< 2^31)
-    FastDiv fhw, fw, fc16;   // by H*W, by W, by C/16
+    FastDiv fhw, fw, fc8;    // by H*W, by W, by C/8
     // A GEMM row = one output pixel: its centre in x and a 9-bit mask whose
     // bit 3r+s says that tap (r, s) lies inside the image (0 for a row past M).
     struct Row {
@@ -43,7 +44,7 @@ struct Conv3x3Rows {
     {
         fhw = FastDiv::make((unsigned)H * (unsigned)W);
         fw = FastDiv::make((unsigned)W);
-        fc16 = FastDiv::make((unsigned)C / 16);
+        fc8 = FastDiv::make((unsigned)C / 8);
     }
     __device__ __forceinline__ Row make(int n, int p, int q, bool ok) const
     {
@@ -67,11 +68,12 @@ struct Conv3x3Rows {
     }
     // Chunk c, lane half hh, vector q: k = 64c + 16q + 8hh + [0, 8), the
     // MFMA's own k order, so that the two lanes holding one pixel's k-step
-    // read 32 contiguous bytes (one cache access per pixel and load
-    // instruction).  k lies in tap rs = k / C at channel k % C; a 16-aligned
-    // run of k never crosses a tap (C % 32 == 0).  KCH = 9 chunks (9C rounded
-    // up to 64) means C = 64, known at compile time: then rs = c and the
-    // channel is 16q + 8hh.
+    // read contiguous bytes when their k-groups share a tap.  k-group
+    // kg = k / 8 lies in tap rs = kg / (C/8) at channel 8 (kg % (C/8)); taps
+    // past the ninth (k in the zero padding of the last chunk) read zero (bit
+    // rs of the 9-bit tap mask is 0).  KCH = 9 chunks (9C rounded up to 64)
+    // means C = 64, known at compile time: then rs = c and the channel is
+    // 16q + 8hh.
     template <int KCH>
     __device__ __forceinline__ void load(const Row& r, int c, int hh, half8 out[4]) const
     {
@@ -89,9 +91,9 @@ struct Conv3x3Rows {
                 coff = 16 * q + 8 * hh;
                 cc = 64;
             } else {
-                const unsigned kq = 4u * c + q;          // k / 16
-                rs = fc16.div(kq);
-                coff = (int)(kq - rs * fc16.d) * 16 + 8 * hh;
+                const unsigned kg = 8u * c + 2u * q + (unsigned)hh;   // k / 8
+                rs = fc8.div(kg);
+                coff = (int)(kg - rs * fc8.d) * 8;
                 cc = C;
             }
             const int rr = (int)((rs * 11u) >> 5);       // rs / 3 for rs < 32
@@ -140,8 +142,8 @@ struct ConvWArgs {
     long tiles_per_block;
     int wpb;           // waves per block that own tiles (1..NWAVES; 0 = all); the others only stage weights
     // row decoding: STORE: pixel = (n, p, q) with fa = P*Q, fb = Q;
-    // POOL: window = (n, i, j) with fa = (P/2)*(Q/2), fb = Q/2; fc16 = C/16
-    FastDiv fa, fb, fc16;
+    // POOL: window = (n, i, j) with fa = (P/2)*(Q/2), fb = Q/2; fc8 = C/8
+    FastDiv fa, fb, fc8;
 };
 
 // LDS: weights [Kp][KP] (natural, swizzled or padded), biases, scales, the
@@ -194,7 +196,7 @@ void k_conv_w(ConvWArgs a)
 
     Conv3x3Rows ld;
     ld.x = a.x; ld.H = a.H; ld.W = a.W; ld.C = a.C; ld.M = (long)a.NB * a.H * a.W;
-    ld.fc16 = a.fc16;
+    ld.fc8 = a.fc8;
 
     // GEMM row -> conv output pixel
     auto make_row = [&](long gr) -> Conv3x3Rows::Row {
@@ -674,7 +676,7 @@ hipError_t run_conv_bias_act3x3(const half_t* x, const half_t* w, const half_t* 
     a.ntiles = (rows + 63) / 64;
     a.fa = FastDiv::make((unsigned)H * (unsigned)W);
     a.fb = FastDiv::make((unsigned)W);
-    a.fc16 = FastDiv::make((unsigned)C / 16);
+    a.fc8 = FastDiv::make((unsigned)C / 8);
     return launch_convw<EPI_STORE>(a, st);
 }
 
@@ -696,7 +698,7 @@ hipError_t run_conv_pool3x3(const half_t* x, const half_t* w, const half_t* scal
     a.ntiles = (rows + 63) / 64;
     a.fa = FastDiv::make((unsigned)(H / 2) * (unsigned)(W / 2));
     a.fb = FastDiv::make((unsigned)(W / 2));
-    a.fc16 = FastDiv::make((unsigned)C / 16);
+    a.fc8 = FastDiv::make((unsigned)C / 8);
     return avg ? launch_convw<EPI_AVG>(a, st) : launch_convw<EPI_POOL>(a, st);
 }
 

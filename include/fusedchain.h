@@ -235,8 +235,8 @@ fc_status chain_gemmN(const fc_half *A, int32_t nstages, const fc_half *const *W
  *   pool == FC_POOL_AVG_2X2_S2: y [n, P/2, Q/2, k] = fp16 of the mean of each
  *   window's four fp16 values (argmax must be NULL);
  *   pool == FC_POOL_NONE: y [n, P, Q, k] = act(conv + b) (argmax must be NULL).
- * Implemented shapes: r = s = 3, stride 1, pad 1, c % 32 == 0 (pad channels
- * with pad_channels first), k % 8 == 0 and k <= 128 (all output channels in
+ * Implemented shapes: r = s = 3, stride 1, pad 1, c % 8 == 0 (pad other channel
+ * counts with pad_channels first), k % 8 == 0 and k <= 128 (all output channels in
  * one block), n*h*w < 2^31, and the weights, held in LDS for the whole
  * kernel, within 160 KiB: roundup(k,32) * (roundup(9c,64) + 8) * 2 bytes
  * (c = 64: k <= 128; c = 128: k <= 64).  Others: FC_E_UNSUPPORTED.
@@ -306,7 +306,7 @@ fc_status chain_conv_pool_auto_config(const fc_conv_shape *shape, fc_act act, fc
  * interview page, conv item 5).
  *   x NHWC [n,h,w,c], w0 HWIO [3,3,c,k0] (k0 = shape0->k), b0 [k0],
  *   w1 [k0 x k1] (= HWIO [1,1,k0,k1]), b1 [k1], y NHWC [n,P,Q,k1].
- * Implemented: r = s = 3, stride 1, pad 1, c % 32 == 0, k0 % 8 == 0 and
+ * Implemented: r = s = 3, stride 1, pad 1, c % 8 == 0, k0 % 8 == 0 and
  * k0 <= 128, k1 % 8 == 0, n*h*w < 2^31, and both weights fit in LDS together.
  */
 fc_status chain_conv2(const fc_half *x, const fc_half *w0, const fc_half *b0, fc_act act,
@@ -325,7 +325,7 @@ fc_status chain_conv2(const fc_half *x, const fc_half *w0, const fc_half *b0, fc
  * for i = 1 .. nstages-1; each X_i with i < nstages rounded once to fp16.
  * k (host array, nstages entries): output channels of every stage, k[0] ==
  * shape0->k.  nstages is 3 or 4 (two stages: chain_conv2).  shape0 follows
- * chain_conv_pool's rules (3x3, stride 1, pad 1, c % 32 == 0, k[0] <= 128);
+ * chain_conv_pool's rules (3x3, stride 1, pad 1, c % 8 == 0, k[0] <= 128);
  * k[1 .. nstages-2] <= 128 and all weights must fit in LDS together, else
  * FC_E_UNSUPPORTED.  b or b[i] may be NULL.  w, b, act and k are host
  * arrays read during the call; the tensors are device pointers owned by the

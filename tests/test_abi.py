@@ -100,7 +100,11 @@ def test_conv_validation(L):
     assert L.chain_conv_pool(P, P, NUL, 1, 1, P2, None, NUL, None) == E_NULL
     assert L.chain_conv_pool(NUL, P, NUL, 1, 1, P2, ctypes.byref(sh), NUL, None) == E_NULL
     assert L.chain_conv_pool(P, P, NUL, 1, 1, P2, ctypes.byref(shape(c=60)), NUL, None) == E_SHAPE
-    assert L.chain_conv_pool(P, P, NUL, 1, 1, P2, ctypes.byref(shape(c=40)), NUL, None) == E_UNSUP
+    # any c % 8 == 0 is implemented (n = 0: validated, nothing to launch)
+    for c in (8, 24, 40, 56):
+        assert L.chain_conv_pool(P, P, NUL, 1, 1, P2, ctypes.byref(shape(n=0, c=c)), NUL, None) == OK
+        assert L.conv_bias_act(P, P, NUL, 1, P2, ctypes.byref(shape(n=0, c=c)), None) == OK
+        assert L.chain_conv2(P, P, NUL, 1, P, NUL, 64, P2, ctypes.byref(shape(n=0, c=c, k=64)), None) == OK
     assert L.chain_conv_pool(P, P, NUL, 1, 1, P2, ctypes.byref(shape(k=136)), NUL, None) == E_UNSUP
     assert L.chain_conv_pool(P, P, NUL, 1, 1, P2, ctypes.byref(shape(r=5, s=5)), NUL, None) == E_UNSUP
     assert L.chain_conv_pool(P, P, NUL, 1, 1, P2, ctypes.byref(shape(stride=2)), NUL, None) == E_UNSUP
@@ -254,7 +258,8 @@ def test_chain_convN_validation(L):
     assert cn(y=BAD) == E_ALIGN
     assert cn(acts=(1, 9, 0, 0)) == E_ARG
     assert cn(k=(64, 136, 128)) == E_UNSUP    # intermediate wider than 128: not register-resident
-    assert cn(shape=fc.ConvShape(1, 8, 8, 48, 64, 3, 3, 1, 1)) == E_UNSUP   # c % 32
+    assert cn(shape=fc.ConvShape(0, 8, 8, 48, 64, 3, 3, 1, 1)) == OK        # c % 8 == 0 is enough
+    assert cn(shape=fc.ConvShape(0, 8, 8, 44, 64, 3, 3, 1, 1)) == E_SHAPE
 
 
 def test_chain_conv_bn_pool_validation(L):

@@ -367,3 +367,64 @@ def test_avgpool2x2(fc):
     yo = oracle.avgpool2x2(v)
     assert y.shape == yo.shape
     assert_close(y, yo.astype(np.float64), "avgpool2x2")
+
+
+# ---- channel counts that are multiples of 8 but not of 32: each 8-channel
+# group of a tap is one MFMA k-group, so taps straddle the 64-wide k chunks
+# (c = 8: eight taps per chunk; c = 24, 40: a tap split across two chunks)
+NARROW_C = [8, 24, 40]
+
+
+@pytest.mark.parametrize("c", NARROW_C)
+def test_conv_pool_narrow_channels(fc, c):
+    d = inputs.conv_pool_inputs(2, 10, 18, c, 96, seed=c)
+    print("case conv_pool narrow c", c, flush=True)
+    y, am = pool_both(fc, dev(d["x"]), dev(d["w"]), dev(d["b"]))
+    free, _ = check_pool(y, am, d["x"], d["w"], d["b"], "conv_pool c=%d" % c, full=True)
+    assert free > 0
+
+
+@pytest.mark.parametrize("c", NARROW_C)
+def test_conv_bias_act_narrow_channels(fc, c):
+    d = inputs.conv_pool_inputs(2, 11, 13, c, 64, seed=c + 1)
+    print("case conv_bias_act narrow c", c, flush=True)
+    y = to_np(fc.conv_bias_act(dev(d["x"]), dev(d["w"]), dev(d["b"]), act="gelu_tanh"))
+    check_full(y, oracle.conv_bias_act(d["x"], d["w"], d["b"], oracle.ACT_GELU_TANH), "conv_bias_act c=%d" % c)
+
+
+@pytest.mark.parametrize("c", NARROW_C)
+def test_conv2_narrow_channels(fc, c):
+    d = inputs.conv2_inputs(1, 9, 14, c, 64, 40, seed=c + 2)
+    print("case conv2 narrow c", c, flush=True)
+    y = to_np(fc.chain_conv2(dev(d["x"]), dev(d["w0"]), dev(d["b0"]), dev(d["w1"]), dev(d["b1"]), act="relu"))
+    ref, _ = oracle.chain_conv2(d["x"], d["w0"], d["b0"], oracle.ACT_RELU, d["w1"], d["b1"])
+    check_full(y, ref, "conv2 c=%d" % c)
+
+
+@pytest.mark.parametrize("c", NARROW_C)
+def test_chain_convN_narrow_channels(fc, c):
+    ks, acts = [64, 48, 32], ["relu", "relu", "none"]
+    d = inputs.convN_inputs(2, 7, 12, c, ks, seed=c + 3)
+    print("case convN narrow c", c, flush=True)
+    y = to_np(fc.chain_convN(dev(d["x"]), [dev(x) for x in d["ws"]], [dev(b) for b in d["bs"]], acts))
+    ref = oracle.chain_convN(d["x"], d["ws"], d["bs"], [ACTS[a] for a in acts])
+    check_full(y, ref, "convN c=%d" % c)
+
+
+@pytest.mark.parametrize("c", NARROW_C)
+def test_conv_bn_pool_narrow_channels(fc, c):
+    d = inputs.conv_bn_pool_inputs(2, 8, 14, c, 128, seed=c + 4)
+    x, wt, sc, sh = dev(d["x"]), dev(d["w"]), dev(d["scale"]), dev(d["shift"])
+    print("case conv_bn_pool narrow c", c, flush=True)
+    y, am = fc.chain_conv_bn_pool(x, wt, sc, sh, act="relu", argmax=True)
+    torch.cuda.synchronize()
+    assert check_bn_pool(to_np(y), to_np(am), d, "relu", "conv_bn_pool c=%d" % c, full=True) > 0
+
+
+@pytest.mark.parametrize("c", NARROW_C)
+def test_conv_avgpool_narrow_channels(fc, c):
+    d = inputs.conv_pool_inputs(1, 12, 10, c, 32, seed=c + 5)
+    print("case conv_avgpool narrow c", c, flush=True)
+    y = to_np(fc.chain_conv_pool(dev(d["x"]), dev(d["w"]), dev(d["b"]), act="relu", pool="avg2x2"))
+    yo, _ = oracle.chain_conv_avgpool(d["x"], d["w"], d["b"], oracle.ACT_RELU)
+    check_full(y, yo.astype(np.float64), "conv_avgpool c=%d" % c, ref16=yo)
