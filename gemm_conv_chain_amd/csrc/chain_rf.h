@@ -216,9 +216,6 @@ void k_chain_rf(Loader ld, RfArgs a)
     const lds_half* w0lane[NT0];
 #pragma unroll
     for (int t = 0; t < NT0; ++t) w0lane[t] = W0n.p + frag_lane_off(W0n, 32 * t, lane) + 8 * hh * W0n.ld;
-    const lds_half* w1lane[2];
-#pragma unroll
-    for (int t1 = 0; t1 < 2; ++t1) w1lane[t1] = W1n.p + frag_lane_off(W1n, 32 * t1, lane) + 4 * hh * W1n.ld;
 
     for (; tile < t_end; tile += wpb) {
         floatx16 acc0[NT0];
@@ -306,15 +303,15 @@ void k_chain_rf(Loader ld, RfArgs a)
             for (int i = 0; i < NMID; ++i) {
                 int lm = lane;
                 asm volatile("" : "+v"(lm));
-                const lds_half* wml[2];
-#pragma unroll
-                for (int t1 = 0; t1 < 2; ++t1)
-                    wml[t1] = Wmn[i].p + frag_lane_off(Wmn[i], 32 * t1, lm) + 4 * (lm >> 5) * Wmn[i].ld;
                 const lds_float* bmi = bms + (i == 0 ? 0 : a.Nmp[0]);
                 half8 hn[8];
 #pragma unroll
                 for (int p = 0; p < 2; ++p) {
                     if (64 * p < a.Nmp[i]) {
+                        const lds_half* wml[2];
+#pragma unroll
+                        for (int t1 = 0; t1 < 2; ++t1)
+                            wml[t1] = Wmn[i].p + frag_lane_off(Wmn[i], 64 * p + 32 * t1, lm) + 4 * (lm >> 5) * Wmn[i].ld;
                         floatx16 am[2];
                         am[0] = zero16();
                         am[1] = zero16();
@@ -323,7 +320,7 @@ void k_chain_rf(Loader ld, RfArgs a)
                             if (s2 < ks) {
 #pragma unroll
                                 for (int t1 = 0; t1 < 2; ++t1) {
-                                    const half8 w = frag_tr_at(wml[t1] + 64 * p + 16 * s2 * Wmn[i].ld, 8 * Wmn[i].ld);
+                                    const half8 w = frag_tr_at(wml[t1] + 16 * s2 * Wmn[i].ld, 8 * Wmn[i].ld);
                                     am[t1] = mfma32x32x16(w, hf[s2], am[t1]);
                                 }
                             }
@@ -348,6 +345,17 @@ void k_chain_rf(Loader ld, RfArgs a)
 
         // GEMM1 over N1 in chunks of 64 columns (two 32x32 tiles).
         for (int n1c = 0; n1c < a.N1p; n1c += 64) {
+            // W1^T fragment bases of this 64-column chunk (the swizzle does
+            // not commute with adding 64 columns); from an opaque lane index
+            // so they are not hoisted out of the loop and held.
+            const lds_half* w1lane[2];
+            {
+                int l1 = lane;
+                asm volatile("" : "+v"(l1));
+#pragma unroll
+                for (int t1 = 0; t1 < 2; ++t1)
+                    w1lane[t1] = W1n.p + frag_lane_off(W1n, n1c + 32 * t1, l1) + 4 * (l1 >> 5) * W1n.ld;
+            }
             floatx16 acc1[2];
             acc1[0] = zero16();
             acc1[1] = zero16();
@@ -358,7 +366,7 @@ void k_chain_rf(Loader ld, RfArgs a)
                 if (NMID == 0 || s < ks) {
 #pragma unroll
                     for (int t1 = 0; t1 < 2; ++t1) {
-                        const half8 w = frag_tr_at(w1lane[t1] + n1c + 16 * s * W1n.ld, 8 * W1n.ld);
+                        const half8 w = frag_tr_at(w1lane[t1] + 16 * s * W1n.ld, 8 * W1n.ld);
                         acc1[t1] = mfma32x32x16(w, hf[s], acc1[t1]);
                     }
                 }

@@ -101,7 +101,10 @@ __device__ __forceinline__ void cs_dma_chunk(const half_t* __restrict__ G, int r
     constexpr int RPI = 64 / VPR;                  // rows per instruction
     constexpr int RSTEP = RPI * CS_WAVES;          // rows between a wave's instructions
     const int rloc = RPI * wave + lane / VPR;      // row (within the instruction's group) of this lane
-    const int col = ((lane % VPR) * 8) ^ ((rloc & 3) << 4);   // rloc & 3 is the same in every instruction
+    // the WTile swizzle of a width that is a multiple of 128 (rloc & 3 is the
+    // same in every instruction)
+    static_assert(WC % 128 == 0, "chunk rows are swizzled as 128-column multiples");
+    const int col = ((lane % VPR) * 8) ^ ((rloc & 3) << 5);
     const unsigned voff = c0 + col < cols ? (unsigned)(rloc * ld + col) * 2u : CS_OUTSIDE;
     // The resources depend only on kernel arguments; computed from an opaque
     // r0 they stay here instead of being hoisted (and spilled) for every step.
@@ -224,7 +227,7 @@ void k_chain_stream(StreamArgs a)
         {
             WTile t0;
             t0.ld = CS_WC0;
-            t0.swz = true;
+            t0.swz = wtile_swz(CS_WC0);
 #pragma unroll
             for (int t = 0; t < NT0; ++t) ow0[t] = frag_lane_off(t0, 32 * t, lo) + 8 * hho * CS_WC0;
         }
@@ -311,7 +314,7 @@ void k_chain_stream(StreamArgs a)
             {
                 WTile t1;
                 t1.ld = CS_N1C;
-                t1.swz = true;
+                t1.swz = wtile_swz(CS_N1C);
 #pragma unroll
                 for (int t = 0; t < 4; ++t) ow1[t] = frag_lane_off(t1, 32 * t, l1) + 4 * (l1 >> 5) * CS_N1C;
             }

@@ -448,30 +448,44 @@ void k_conv_w(ConvWArgs a)
                     wave_lds_sync();   // the next pass overwrites the staging area
                 }
             } else {
+                // Whole output rows here too: for each (u, g) and register pair
+                // e = 2eh, 2eh + 1, the two lane halves hold tile rows
+                // 32u + 8g + 4hh + e of every channel 32t + lr, i.e. four
+                // complete rows.  They are staged as [4][KP] fp16 (row
+                // 2(e % 2) + hh) and stored by KP/8 lanes per row, 16 bytes
+                // each, so every store instruction writes whole rows of y (no
+                // cache line of y is written in several partial pieces).
                 half_t* yb = a.y + row0 * K;
                 const int nr = (int)min(64L, nrows - row0);
+                const int vpr = KP / 8;               // 16-byte vectors per staged row
+                const int sr = ln / vpr, sg = ln - sr * vpr;
+                const lds_half8* const orw = reinterpret_cast<const lds_half8*>(ost + sr * KP + 8 * sg);
+                lds_half* const owr = ost + hh * KP + lr;
+                float bk[NTK], sk[NTK];
 #pragma unroll
                 for (int t = 0; t < NTK; ++t) {
-                    const float bk = bsl[32 * t];
-                    const float sk = ssl[32 * t];
+                    bk[t] = bsl[32 * t];
+                    sk[t] = ssl[32 * t];
+                }
 #pragma unroll
-                    for (int u = 0; u < 2; ++u) {
+                for (int u = 0; u < 2; ++u) {
+#pragma unroll
+                    for (int g = 0; g < 4; ++g) {
 #pragma unroll
                         for (int eh = 0; eh < 2; ++eh) {
-                            // staged row (e % 2) * 8 + 2g + hh for e = 2eh, 2eh + 1
 #pragma unroll
-                            for (int g = 0; g < 4; ++g)
+                            for (int ei = 0; ei < 2; ++ei)
 #pragma unroll
-                                for (int e = 2 * eh; e < 2 * eh + 2; ++e)
-                                    ow[((e & 1) * 8 + 2 * g) * 32] =
-                                        (half_t)act.f(__builtin_fmaf(acc[u][t][4 * g + e], sk, bk));
+                                for (int t = 0; t < NTK; ++t)
+                                    owr[2 * ei * KP + 32 * t] =
+                                        (half_t)act.f(__builtin_fmaf(acc[u][t][4 * g + 2 * eh + ei], sk[t], bk[t]));
                             wave_lds_sync();
-                            // staged row rr -> tile row
-                            const int e = 2 * eh + (rr >> 3), g = (rr & 7) >> 1, h1 = rr & 1;
-                            const int row = 32 * u + 8 * g + 4 * h1 + e;
-                            const half8 v = *orb;
-                            if (row < nr && 8 * grp < K - 32 * t)
-                                st_out(reinterpret_cast<half8*>(yb + row * K + 32 * t + 8 * grp), v);
+                            // staged row sr = 2 ei + h1 -> tile row 32u + 8g + 4 h1 + 2 eh + ei
+                            const int row = 32 * u + 8 * g + 4 * (sr & 1) + 2 * eh + (sr >> 1);
+                            if (sr < 4) {
+                                const half8 v = *orw;
+                                if (row < nr && 8 * sg < K) st_out(reinterpret_cast<half8*>(yb + row * K + 8 * sg), v);
+                            }
                             wave_lds_sync();
                         }
                     }

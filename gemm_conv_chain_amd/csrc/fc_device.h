@@ -313,8 +313,8 @@ __device__ __forceinline__ void stage_transposed(const half_t* __restrict__ G, i
 // receives element (i % 4) of the 8-byte chunks addressed by lanes
 // 4e + i/4, e = 0..3.  So lane j of a group addresses row k0 + 8h + j/4 (+4 for
 // the second read), columns nb + 16*(group & 1) + 4*(j % 4) .. +3.
-// Conflict-free when the row stride is 32 bytes modulo 128 (the four rows a
-// group reads then fill all 32 banks).
+// Conflict-free when the row stride is 64 bytes (times an odd number) modulo
+// 256: the four rows each 32-lane half reads then fill all 64 banks.
 typedef __fp16 fp16x4_t __attribute__((__vector_size__(4 * sizeof(__fp16))));
 typedef FC_LDS fp16x4_t lds_fp16x4_t;
 
@@ -334,28 +334,42 @@ __device__ __forceinline__ half8 frag_tr(const lds_half* T, int ldt, int k0, int
 }
 
 // A natural (row-major, rows = k) weight tile in LDS, optionally XOR-swizzled.
+//
+// Bank geometry (measured on gfx950 with the LDS bank-conflict counter): a
+// transposing 8-byte read of 64 lanes is served at 256 bytes per clock, i.e.
+// 64 four-byte banks, when the 32 lanes of each half touch 256 distinct bank
+// bytes.  Such a half reads 4 rows x 32 columns (64 bytes per row) of the
+// tile, so the four rows' 64-byte pieces must sit at four different offsets
+// modulo 256 bytes.
+//   N % 64 == 32: the row stride (64 * odd bytes) already separates them.
+//   N % 128 == 64: rows 2q and 2q+1 differ by 128 bytes; rows 2,3 (mod 4)
+//                  flip the 64-byte piece (XOR 32 halves).
+//   N % 128 == 0:  every row starts at the same bank; row r (mod 4) takes
+//                  piece r (XOR 32 (r % 4) halves).
+// Both XORs keep 8-half (16-byte) vectors whole and commute with adding a
+// multiple of 128 columns (not 64).
 struct WTile {
     lds_half* p;
     int ld;      // row stride in halves
-    bool swz;    // XOR the 16-half segment index with (row & 3)
+    int swz;     // 0: none; 1: XOR columns with 32 (row % 4); 2: XOR with 32 ((row / 2) % 2)
     __device__ __forceinline__ int off(int r, int c) const
     {
-        return r * ld + (swz ? (c ^ ((r & 3) << 4)) : c);
+        const int m = swz == 1 ? (r & 3) << 5 : swz == 2 ? ((r >> 1) & 1) << 5 : 0;
+        return r * ld + (c ^ m);
     }
 };
 
-// Row stride / swizzle for a natural [rows x N] fp16 tile (N % 32 == 0): N a
-// multiple of 64 uses the XOR swizzle and no padding; otherwise 16 halves of
-// padding (row stride 96 bytes mod 128).  Either way the four rows one
-// 16-lane group reads fall into four different 32-byte bank groups.
-__host__ __device__ constexpr int wtile_ld(int N) { return (N % 64 == 0) ? N : N + 16; }
-__host__ __device__ constexpr bool wtile_swz(int N) { return N % 64 == 0; }
+// Row stride / swizzle for a natural [rows x N] fp16 tile (N % 32 == 0): no
+// padding, the swizzle chosen from N as above.
+__host__ __device__ constexpr int wtile_ld(int N) { return N; }
+__host__ __device__ constexpr int wtile_swz(int N) { return N % 128 == 0 ? 1 : N % 64 == 0 ? 2 : 0; }
 
 // Lane part of a transposing fragment read from a WTile: the offset (in
 // halves) of this lane's 8-byte chunk for rows starting at 0 and the column
-// block nb (nb % 64 == 0 or 32: the XOR only touches the two low segment
-// bits, so for nb % 64 == 0 it commutes with adding nb).  Add row * ld for
-// the row base; the second read of a fragment is 4 rows further down.
+// block nb (nb % 32 == 0; pass the full column: the swizzle does not commute
+// with adding 64 columns).  Add row * ld for the row base with a row offset
+// that is a multiple of 4 (the swizzle depends on row % 4); the second read
+// of a fragment is 4 (or 8) rows further down.
 __device__ __forceinline__ int frag_lane_off(const WTile& T, int nb, int lane)
 {
     const int g = lane >> 4, i = lane & 15;

@@ -36,8 +36,8 @@ struct LdsArgs {
 };
 
 // Weight chunks are staged in their natural row-major layout (rows = k) with
-// a row stride of (columns + 16) halves: 32 bytes modulo 128, which keeps the
-// transposing fragment reads conflict-free.
+// a row stride of (columns + 32) halves: 64 bytes times an odd number modulo
+// 256, which keeps the transposing fragment reads conflict-free.
 __host__ __device__ constexpr int lds_wcols(int N0P, bool chain)
 {
     return chain ? (N0P > LDS_N1C ? N0P : LDS_N1C) : N0P;
@@ -45,7 +45,7 @@ __host__ __device__ constexpr int lds_wcols(int N0P, bool chain)
 
 inline size_t lds_lds_bytes(int N0P, bool chain)
 {
-    size_t b = (size_t)2 * LDS_KC * (lds_wcols(N0P, chain) + 16) * 2;
+    size_t b = (size_t)2 * LDS_KC * (lds_wcols(N0P, chain) + 32) * 2;
     if (chain) b += (size_t)LDS_MT * (N0P + 8) * 2;
     b += (size_t)(N0P + (chain ? LDS_N1C : 0)) * 4;   // biases (fp32)
     return b;
@@ -104,7 +104,7 @@ void k_gemm_lds(LdsArgs a)
 {
     constexpr int N0P = 64 * NT0W;
     constexpr int WC = lds_wcols(N0P, CHAIN);
-    constexpr int LDW = WC + 16;
+    constexpr int LDW = WC + 32;
     constexpr int WBUF = LDS_KC * LDW;   // halves per weight buffer
     constexpr int LDH = N0P + 8;
     constexpr int NV0 = (LDS_KC * N0P / 8 + LDS_THREADS - 1) / LDS_THREADS;   // W0 vectors per thread

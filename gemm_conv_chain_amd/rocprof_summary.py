@@ -4,6 +4,9 @@
     python -m gemm_conv_chain_amd.rocprof_summary pmc    DIR WORKLOAD [--json profiles/traffic.json]
     python -m gemm_conv_chain_amd.rocprof_summary mfma   DIR [WORKLOAD --json profiles/traffic.json]
         (DIR from --pmc SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_VALU_MFMA_MOPS_F16 GRBM_GUI_ACTIVE; run after pmc)
+    python -m gemm_conv_chain_amd.rocprof_summary lds    DIR
+        (DIR from --pmc SQ_LDS_IDX_ACTIVE SQ_LDS_BANK_CONFLICT SQ_LDS_ADDR_CONFLICT SQ_INSTS_LDS
+         SQ_ACTIVE_INST_LDS GRBM_GUI_ACTIVE)
 
 ``trace``: the kernel_stats.csv rows (calls, average/min/max duration).
 ``mfma``: matrix-core activity per dispatch of this library's kernels.  On
@@ -113,8 +116,14 @@ def pmc(d, workload, json_path=None):
         import bench
         fused = {"b2b_gemm_tiny": "k_chain_rf", "b2b_gemm_rf": "k_chain_rf", "b2b_gemm_lds": "k_gemm_lds<4, true",
                  "b2b_gemm_lds@stream": "k_chain_stream", "gemm3_rf": "k_chain_rf",
-                 "conv3x3_conv1x1": "k_chain_rf", "conv3x3_conv1x1x2": "k_chain_rf", "conv3x3_relu_maxpool": "k_conv_w<4, 1",
-                 "conv3x3_bn_relu_maxpool": "k_conv_w<4, 1", "conv3x3_relu_avgpool": "k_conv_w<4, 2"}[workload]
+                 "conv3x3_conv1x1": "k_chain_rf", "conv3x3_conv1x1x2": "k_chain_rf",
+                 # pooled convs: the register-weights kernel is the automatic choice at these shapes
+                 "conv3x3_relu_maxpool": "k_conv_pool_wr", "conv3x3_bn_relu_maxpool": "k_conv_pool_wr",
+                 "conv3x3_relu_avgpool": "k_conv_pool_wr",
+                 "conv3x3_relu_maxpool@reg_weights": "k_conv_pool_wr",
+                 "conv3x3_relu_maxpool@lds_weights": "k_conv_w<4, 1",
+                 "conv3x3_bn_relu_maxpool@lds_weights": "k_conv_w<4, 1",
+                 "conv3x3_relu_avgpool@lds_weights": "k_conv_w<4, 2"}[workload]
         fk = [k for k in fetch if fused in k]
         if len(fk) != 1:
             raise SystemExit("cannot identify the fused kernel among %s" % list(fetch))
@@ -131,9 +140,39 @@ def pmc(d, workload, json_path=None):
             json.dump(db, f, indent=1, sort_keys=True)
 
 
+LDS_COUNTERS = ("SQ_LDS_IDX_ACTIVE", "SQ_LDS_BANK_CONFLICT", "SQ_LDS_ADDR_CONFLICT", "SQ_INSTS_LDS",
+                "SQ_ACTIVE_INST_LDS", "GRBM_GUI_ACTIVE")
+
+
+def lds(d):
+    """LDS activity per dispatch of this library's kernels (DIR from --pmc of
+    LDS_COUNTERS).  bank-conflict ratio = SQ_LDS_BANK_CONFLICT /
+    (SQ_LDS_IDX_ACTIVE - SQ_LDS_BANK_CONFLICT): stalled cycles per useful LDS
+    cycle; LDS busy = SQ_LDS_IDX_ACTIVE over the 256 CUs' active clocks
+    (GRBM_GUI_ACTIVE is summed over the 8 XCDs)."""
+    rows = _rows(os.path.join(d, "**", "*counter_collection.csv"))
+    per = {}
+    for r in rows:
+        if _ours(r["Kernel_Name"]) and "k_mfma_probe" not in r["Kernel_Name"]:
+            per.setdefault(r["Kernel_Name"], {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    print("| kernel | LDS instructions | LDS active (clk) | bank-conflict stall (clk) | address-conflict stall (clk) "
+          "| conflicts / useful cycle | LDS busy fraction |")
+    print("|---|---|---|---|---|---|---|")
+    for k in sorted(per):
+        v = {c: sum(x) / len(x) for c, x in per[k].items()}
+        idx, bank, addr, insts, act = (v.get(c, 0.0) for c in ("SQ_LDS_IDX_ACTIVE", "SQ_LDS_BANK_CONFLICT",
+                                                                "SQ_LDS_ADDR_CONFLICT", "SQ_INSTS_LDS",
+                                                                "GRBM_GUI_ACTIVE"))
+        ratio = bank / (idx - bank) if idx > bank else 0.0
+        busy = idx / (act / 8 * 256) if act else 0.0
+        print("| `%s` | %.0f | %.0f | %.0f | %.0f | %.4f | %.3f |" % (k[:90], insts, idx, bank, addr, ratio, busy))
+
+
 if __name__ == "__main__":
     if sys.argv[1] == "trace":
         trace(sys.argv[2])
+    elif sys.argv[1] == "lds":
+        lds(sys.argv[2])
     elif sys.argv[1] == "mfma":
         jp = sys.argv[sys.argv.index("--json") + 1] if "--json" in sys.argv else None
         mfma(sys.argv[2], sys.argv[3] if len(sys.argv) > 3 and sys.argv[3] != "--json" else None, jp)
