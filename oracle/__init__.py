@@ -26,6 +26,9 @@ the chain rounds.  Semantics, with the passages they follow:
   interview page item 5) + bias.
 * ``chain_conv_pool``-- conv + bias + ReLU -> fp16 -> maxpool, the Welder
   Conv -> ReLU -> MaxPool tile graph (Figure 5 in the Welder notes).
+* ``winograd``       -- (submodule, numpy fp64) the same conv by Winograd
+  F(2x2, 3x3) (interview page, "Conv optimisation", item 3), exactly and under
+  the fp16 rounding model of a half-precision implementation.
 
 Parity status: every function is pinned by ``tests/test_oracle_pins.py``
 (hand-worked examples under ``tests/golden/``, brute force on tiny inputs,

@@ -490,3 +490,114 @@ def test_chain_conv_avgpool_composition(orc):
     _, _, vmax, _ = orc.chain_conv_pool(d["x"], d["w"], d["b"], orc.ACT_RELU)
     assert np.array_equal(v.view(np.uint16), vmax.view(np.uint16))
     assert np.array_equal(y.view(np.uint16), orc.avgpool2x2(v).view(np.uint16))
+
+
+# ------------------------------------------------------- Winograd F(2x2, 3x3)
+def _brute_conv(x, w):
+    """Direct 3x3 / stride 1 / pad 1 cross-correlation by explicit loops over
+    (r, s, c) with Fractions (exact), x [n,H,W,C], w [3,3,C,K] (small ints)."""
+    n, H, W, C = x.shape
+    K = w.shape[-1]
+    y = np.zeros((n, H, W, K), dtype=object)
+    for im in range(n):
+        for p in range(H):
+            for q in range(W):
+                for k in range(K):
+                    s = Fraction(0)
+                    for r in range(3):
+                        for t in range(3):
+                            pp, qq = p + r - 1, q + t - 1
+                            if 0 <= pp < H and 0 <= qq < W:
+                                for c in range(C):
+                                    s += Fraction(float(x[im, pp, qq, c])) * Fraction(float(w[r, t, c, k]))
+                    y[im, p, q, k] = s
+    return y
+
+
+def test_winograd_1d_identity():
+    """F(2,3): A^T [(G g) (.) (B^T d)] equals the two correlation outputs
+    d0 g0 + d1 g1 + d2 g2 and d1 g0 + d2 g1 + d3 g2 (exact on integers)."""
+    from oracle import winograd as W
+    BT, G, AT = W.matrices()
+    for _ in range(50):
+        d = RNG.integers(-9, 10, 4).astype(np.float64)
+        g = RNG.integers(-9, 10, 3).astype(np.float64)
+        y = AT @ ((G @ g) * (BT @ d))
+        assert np.array_equal(y, [d[0] * g[0] + d[1] * g[1] + d[2] * g[2], d[1] * g[0] + d[2] * g[1] + d[3] * g[2]])
+
+
+def test_winograd_exact_on_small_integers():
+    """Every step is exact on small integers, so the fp64 F(2x2,3x3) conv of
+    whole tiles equals brute-force direct convolution exactly (odd H and W:
+    the last row / column is outside every whole tile)."""
+    from oracle import winograd as W
+    x = f16(RNG.integers(-4, 5, (2, 7, 9, 3)))
+    w = f16(RNG.integers(-3, 4, (3, 3, 3, 5)))
+    b = f16(RNG.integers(-2, 3, 5))
+    got = W.conv_tiles(x, w, b, "exact")
+    ref = _brute_conv(x, w)[:, :6, :8, :] + np.array([Fraction(float(v)) for v in b], dtype=object)
+    assert got.shape == ref.shape
+    assert all(Fraction(float(g)) == r for g, r in zip(got.ravel(), ref.ravel()))
+
+
+def test_winograd_sobel_golden():
+    """The hand-worked Sobel fixture (3x3 image -> one whole 2x2 tile)."""
+    from oracle import winograd as W
+    g = read_fields("conv_sobel_3x3.txt")
+    y = W.conv_tiles(f16(g["x"])[None, :, :, None], f16(g["w"])[:, :, None, None], None, "exact")
+    assert np.array_equal(y[0, :, :, 0], g["y"][:2, :2])
+
+
+def test_winograd_multiplication_count():
+    """The interview page's count: (m + r - 1)^2 = 16 products instead of
+    m^2 r^2 = 36 for a 2x2 tile of a 3x3 filter, 4/9 of the direct work."""
+    from oracle import winograd as W
+    wino, direct = W.multiplications_per_tile()
+    assert (wino, direct) == (16, 36)
+    assert Fraction(wino, direct) == Fraction(4, 9)
+
+
+def test_winograd_input_rounding_golden():
+    """fp16 model of the input transform: rows first, one rounding per stage
+    (hand-worked patch; the exact transform keeps 2^-10 that it loses)."""
+    from oracle import winograd as W
+    g = read_fields("winograd_input_rounding.txt")
+    d = g["d"][None, :, :, None]
+    assert np.array_equal(W.input_transform(d, "exact")[0, :, :, 0], g["v_exact"])
+    assert np.array_equal(W.input_transform(d, "fp16")[0, :, :, 0], g["v_fp16"])
+
+
+def test_winograd_weight_transform_closed_form():
+    """U = G g G^T entry by entry from its closed form (corners are the
+    filter's corners, the centre is the sum of the nine taps over 4, ...)."""
+    from oracle import winograd as W
+    w = f16(RNG.standard_normal((3, 3, 2, 3)))
+    U = W.weight_transform(w, "exact")
+    g = w.astype(np.float64)
+    assert np.array_equal(U[0, 0], g[0, 0])
+    assert np.array_equal(U[3, 3], g[2, 2])
+    assert np.array_equal(U[0, 3], g[0, 2])
+    assert np.allclose(U[1, 1], g.sum(axis=(0, 1)) / 4, rtol=0, atol=1e-15)
+    assert np.allclose(U[0, 1], (g[0, 0] + g[0, 1] + g[0, 2]) / 2, rtol=0, atol=1e-15)
+    assert np.allclose(U[2, 1], ((g[0] - g[1] + g[2]).sum(axis=0)) / 4, rtol=0, atol=1e-15)
+    U16 = W.weight_transform(w, "fp16")
+    assert np.array_equal(U16, U.astype(np.float16).astype(np.float64))
+
+
+def test_winograd_fp16_model_error_bound(orc):
+    """The fp16 model stays within its rounding bound of the exact transform,
+    and the direct convolution equals the exact model up to fp64 rounding.
+    With m = max |d| over a patch channel, |t| <= 2m and |V| <= 4m; each
+    rounding errs by at most 2^-11 of its result, so |V16 - V| <= 2 (2^-11 2m)
+    + 2^-11 4m = 2^-8 m (relative to V itself the error is unbounded: the sums
+    cancel)."""
+    from oracle import winograd as W
+    x = f16(RNG.uniform(-1, 1, (2, 6, 10, 8)))
+    w = f16(RNG.standard_normal((3, 3, 8, 16)) / 8)
+    d = W.patches(x, 3, 5)
+    V, V16 = W.input_transform(d, "exact"), W.input_transform(d, "fp16")
+    m = np.abs(d).max(axis=(-3, -2), keepdims=True)
+    assert np.all(np.abs(V16 - V) <= 2.0 ** -8 * m)
+    assert np.any(V16 != V)   # the model does round
+    direct = orc.conv_bias_act(x, w, None, orc.ACT_NONE)
+    assert np.allclose(W.conv_tiles(x, w, None, "exact"), direct[:, :6, :10], rtol=0, atol=1e-12)
