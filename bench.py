@@ -173,10 +173,20 @@ class Problem:
             self.conv_variant = variant or "auto"
             if variant:
                 self.traffic_key = name + "@" + variant
+            if variant == "winograd":
+                if self.bn:
+                    raise ValueError("the Winograd chain takes a bias, not a batch-norm scale")
+                # weight transform once per weight tensor, outside the timed step (like the padding)
+                self.U = fc.winograd_weights(wp)
+                tiles = n * (h // 2) * (w // 2)
+                self.flops_exec = 2 * tiles * 16 * cp * k   # 16 products per tile, channel and output channel
+                self.flops_note = ("value and roofline count the direct convolution's %.2f GFLOP per launch; the "
+                                   "Winograd kernel executes %.2f GFLOP on the matrix cores"
+                                   % (self.flops / 1e9, self.flops_exec / 1e9))
             self.config = {"workload": name, "x": [n, h, w, c], "channels_padded_to": cp, "variant": self.conv_variant,
                            "conv": "3x3 s1 p1 %d->%d %s ReLU" % (c, k, "x scale + shift" if self.bn else "+b"),
                            "pool": ("avg" if self.pool == "avg2x2" else "max") + " 2x2 s2"}
-            self.kernel = "k_conv_w" if variant == "lds_weights" else "k_conv_pool_wr"
+            self.kernel = {"lds_weights": "k_conv_w", "winograd": "k_conv_pool_wino"}.get(variant, "k_conv_pool_wr")
         torch.cuda.synchronize()
 
     def step(self, i):
@@ -197,6 +207,8 @@ class Problem:
             w, sc, sh = self.W
             fc.chain_conv_bn_pool(self.X[j], w, sc, sh, act="relu", pool="max2x2", out=self.Y[j],
                                   variant=self.conv_variant)
+        elif self.conv_variant == "winograd":
+            fc.chain_conv_pool_winograd(self.X[j], self.U, self.W[1], act="relu", pool=self.pool, out=self.Y[j])
         else:
             w, b = self.W
             fc.chain_conv_pool(self.X[j], w, b, act="relu", pool=self.pool, out=self.Y[j], variant=self.conv_variant)
@@ -428,6 +440,9 @@ def roofline(prob, ms_kernel, tr):
     roof.update({"kernel": prob.kernel, "kernel_ms": round(ms_kernel, 5), "flop_per_byte": round(ai, 1),
                  "algorithmic_bytes": prob.bytes_fused, "algorithmic_flops": prob.flops,
                  "executed_flops": prob.flops_exec})
+    if getattr(prob, "flops_note", None):
+        roof["flops_note"] = prob.flops_note
+        roof["executed_frac"] = round(prob.flops_exec / ksec / 1e12 / PEAK_F16_TFLOPS, 4)
     return roof
 
 
@@ -468,7 +483,7 @@ def measure(torch, fc, prob, steps, warmup, unfused=True, warm=True):
 # (one record each; the two-GEMM LDS-resident shape under each kernel variant
 # and under the profiler's choice).
 SIDE_CONFIGS = [("b2b_gemm_tiny", None), ("b2b_gemm_rf", None), ("b2b_gemm_lds", None), ("b2b_gemm_lds", "stream"),
-                ("b2b_gemm_lds", "tuned"), ("conv3x3_conv1x1", None)]
+                ("b2b_gemm_lds", "tuned"), ("conv3x3_conv1x1", None), ("conv3x3_relu_maxpool", "winograd")]
 WORKLOADS = ["b2b_gemm_tiny", "b2b_gemm_rf", "b2b_gemm_lds", "gemm3_rf", "conv3x3_conv1x1", "conv3x3_conv1x1x2",
              "conv3x3_relu_maxpool", "conv3x3_bn_relu_maxpool", "conv3x3_relu_avgpool"]
 
@@ -513,9 +528,10 @@ def main():
     ap.add_argument("--workload", default="conv3x3_relu_maxpool", choices=WORKLOADS,
                     help="the headline workload (default: the conv3x3 + ReLU + 2x2 max-pool chain on "
                          "x[32,112,112,60->64], the largest configuration)")
-    ap.add_argument("--variant", choices=["rf", "lds", "stream", "lds_weights", "reg_weights"], default=None,
+    ap.add_argument("--variant", choices=["rf", "lds", "stream", "lds_weights", "reg_weights", "winograd"], default=None,
                     help="kernel form: GEMM chains rf / lds / stream (default rf, or lds for b2b_gemm_lds); "
-                         "conv + pool chains lds_weights / reg_weights (default: the library's choice)")
+                         "conv + pool chains lds_weights / reg_weights (default: the library's choice) or "
+                         "winograd (F(2x2,3x3), its own numerics)")
     ap.add_argument("--warm", action="store_true", help="reuse one buffer set (cache-warm timing)")
     ap.add_argument("--no-unfused", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")

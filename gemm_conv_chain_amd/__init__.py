@@ -100,9 +100,12 @@ def lib():
                                            ctypes.POINTER(_i32), ctypes.POINTER(TuneEntry), _vp]
         L.chain_conv_pool_auto_config.argtypes = [ctypes.POINTER(ConvShape), ctypes.c_int, ctypes.c_int, _i32,
                                                   ctypes.POINTER(TuneEntry)]
+        L.winograd_weights.argtypes = [_vp, _vp, _i32, _i32, _vp]
+        L.chain_conv_pool_winograd.argtypes = [_vp, _vp, _vp, ctypes.c_int, ctypes.c_int, _vp,
+                                               ctypes.POINTER(ConvShape), _vp, _vp]
         L.fc_tune_clear.restype = None
         L.fc_tune_clear.argtypes = []
-        for name in ("chain_gemm2_ex", "chain_gemm2_tune_ex", "chain_gemm2_auto_config", "chain_conv_pool_tune",
+        for name in ("winograd_weights", "chain_conv_pool_winograd", "chain_gemm2_ex", "chain_gemm2_tune_ex", "chain_gemm2_auto_config", "chain_conv_pool_tune",
                      "chain_conv_pool_auto_config", "chain_conv_pool_ex", "avgpool2x2", "fc_probe_mfma", "chain_conv_bn_pool", "chain_convN", "chain_gemm2_tune", "chain_gemm2_auto_variant", "chain_gemm2", "chain_gemm2_variant", "chain_gemmN", "chain_conv_pool", "chain_conv2", "gemm_bias_act",
                      "conv_bias_act", "maxpool2x2", "pad_channels"):
             getattr(L, name).restype = ctypes.c_int
@@ -450,6 +453,50 @@ def _conv_pool(fn, x, w, scale, b, act, pool, out, argmax, variant="auto", waves
     st = lib().chain_conv_pool_ex(_ptr(x), _ptr(w), _ptr(scale), _ptr(b), _act(act), p, _ptr(out), ctypes.byref(sh),
                                   _ptr(am), v, int(waves), _stream(x))
     _check(fn, st)
+    return (out, am) if am is not None else out
+
+
+def winograd_weights(w, out=None):
+    """U = G g G^T of a 3x3 HWIO weight w [3, 3, c, k] for chain_conv_pool_winograd,
+    in the library's operand layout, returned as a [16, c/8, k, 8] fp16 tensor."""
+    r, s, c, k = _ndim(w, "w", 4)
+    if (r, s) != (3, 3):
+        raise ValueError("w must be [3, 3, c, k], got %s" % ((r, s, c, k),))
+    if c % 8 or k % 8:
+        raise ValueError("c=%d and k=%d must be multiples of 8" % (c, k))
+    oshape = (16, c // 8, k, 8)
+    if out is None:
+        _validate([(w, "w", None, None)])
+        out = _empty(oshape, w)
+    _validate([(w, "w", None, None), (out, "out", oshape, None)])
+    _check("winograd_weights", lib().winograd_weights(_ptr(w), _ptr(out), c, k, _stream(w)))
+    return out
+
+
+def chain_conv_pool_winograd(x, U, b, act="relu", pool="max2x2", out=None, argmax=None):
+    """y = pool2x2(act(conv3x3(x, w) + b)) with the conv by Winograd F(2x2, 3x3)
+    from U = winograd_weights(w).  ``argmax`` as for chain_conv_pool (max pool)."""
+    n, h, wd, c = _ndim(x, "x", 4)
+    ushape = _ndim(U, "U", 4)
+    if ushape[0] != 16 or ushape[1] != c // 8 or ushape[3] != 8 or c % 8:
+        raise ValueError("U must be [16, %d, k, 8] (winograd_weights of a [3, 3, %d, k] weight), got %s"
+                         % (c // 8, c, ushape))
+    k = ushape[2]
+    sh = ConvShape(n, h, wd, c, k, 3, 3, 1, 1)
+    p = POOL[pool] if isinstance(pool, str) else int(pool)
+    oshape = (n, h // 2, wd // 2, k)
+    am = _argmax_tensor(argmax, oshape, x) if argmax is not True else None
+    items = [(x, "x", None, None), (U, "U", None, None), (b, "b", (k,), None),
+             (am, "argmax", oshape, _torch().uint8)]
+    if out is None:
+        _validate(items)
+        out = _empty(oshape, x)
+    _validate(items + [(out, "out", oshape, None)])
+    if argmax is True:
+        am = _argmax_tensor(True, oshape, x)
+    st = lib().chain_conv_pool_winograd(_ptr(x), _ptr(U), _ptr(b), _act(act), p, _ptr(out), ctypes.byref(sh),
+                                        _ptr(am), _stream(x))
+    _check("chain_conv_pool_winograd", st)
     return (out, am) if am is not None else out
 
 

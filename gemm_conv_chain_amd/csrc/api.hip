@@ -29,6 +29,10 @@ hipError_t run_pool2x2(bool avg, const half_t* v, half_t* y, uint8_t* am, int NB
                        hipStream_t st);
 hipError_t run_pad_mid(const half_t* src, half_t* dst, long outer, int c_in, int c_out, int inner, hipStream_t st);
 bool convw_fits(int C, int K);
+bool wino_fits(int C, int K);
+hipError_t run_wino_weights(const half_t* w, half_t* U, int C, int K, hipStream_t st);
+hipError_t run_conv_pool_wino(const half_t* x, const half_t* U, const half_t* b, int act, bool avg, half_t* y,
+                              uint8_t* argmax, int NB, int H, int W, int C, int K, hipStream_t st);
 }  // namespace fc
 
 using fc::half_t;
@@ -662,6 +666,42 @@ fc_status avgpool2x2(const fc_half* x, fc_half* y, int32_t n, int32_t h, int32_t
     if (nout == 0) return ok();
     if (!aligned16(x) || !aligned16(y)) return fail(FC_E_ALIGN, "x and y must be 16-byte aligned");
     return hip_status(fc::run_pool2x2(true, H(x), Hm(y), nullptr, n, h, w, c, (hipStream_t)stream), "avgpool2x2");
+}
+
+fc_status winograd_weights(const fc_half* w, fc_half* U, int32_t c, int32_t k, void* stream)
+{
+    if (c <= 0 || k <= 0 || c % 8 || k % 8) return fail(FC_E_SHAPE, "c=%d and k=%d must be positive multiples of 8", c, k);
+    if ((long)c * k * 16 >= (1L << 31)) return fail(FC_E_UNSUPPORTED, "16*c*k exceeds 2^31 - 1 elements");
+    if (!w || !U) return fail(FC_E_NULL, "w and U are required");
+    if (!aligned16(w) || !aligned16(U)) return fail(FC_E_ALIGN, "w and U must be 16-byte aligned");
+    return hip_status(fc::run_wino_weights(H(w), Hm(U), c, k, (hipStream_t)stream), "winograd_weights");
+}
+
+fc_status chain_conv_pool_winograd(const fc_half* x, const fc_half* U, const fc_half* b, fc_act act, fc_pool pool,
+                                   fc_half* y, const fc_conv_shape* shape, uint8_t* argmax, void* stream)
+{
+    fc_status s = check_act(act);
+    if (s != FC_OK) return s;
+    if ((int)pool < 0 || (int)pool > 2) return fail(FC_E_ARG, "pool %d out of range", (int)pool);
+    if (pool != FC_POOL_MAX_2X2_S2 && argmax) return fail(FC_E_ARG, "argmax needs the max pool");
+    s = check_conv(shape, 128);
+    if (s != FC_OK) return s;
+    if (pool == FC_POOL_NONE)
+        return fail(FC_E_UNSUPPORTED, "the Winograd chain pools each 2x2 output tile (pool must be max or avg)");
+    if (!fc::wino_fits(shape->c, shape->k))
+        return fail(FC_E_UNSUPPORTED, "Winograd kernel: c must be 32 or 64 and k a multiple of 16 up to 128");
+    // input halos are addressed from the image's base with 31-bit byte offsets
+    if ((long)shape->h * shape->w * shape->c * 2 >= (1L << 31))
+        return fail(FC_E_UNSUPPORTED, "an image of %ld bytes: images must stay below 2^31 bytes",
+                    (long)shape->h * shape->w * shape->c * 2);
+    const long nout = (long)shape->n * (shape->h / 2) * (shape->w / 2);
+    if (!U || (nout > 0 && (!x || !y))) return fail(FC_E_NULL, "x, U and y are required");
+    if (!aligned16(x) || !aligned16(U) || !aligned16(y) || !aligned16(b) || !aligned16(argmax))
+        return fail(FC_E_ALIGN, "tensor pointers (argmax included) must be 16-byte aligned");
+    if (nout == 0) return ok();
+    return hip_status(fc::run_conv_pool_wino(H(x), H(U), H(b), (int)act, pool == FC_POOL_AVG_2X2_S2, Hm(y), argmax,
+                                             shape->n, shape->h, shape->w, shape->c, shape->k, (hipStream_t)stream),
+                      "chain_conv_pool_winograd");
 }
 
 fc_status pad_channels(const fc_half* src, fc_half* dst, int64_t outer, int32_t c_in, int32_t c_out, int32_t inner,

@@ -356,6 +356,43 @@ fc_status maxpool2x2(const fc_half *x, fc_half *y, uint8_t *argmax, int32_t n, i
  * fusion").  c % 8 == 0; x and y 16-byte aligned. */
 fc_status avgpool2x2(const fc_half *x, fc_half *y, int32_t n, int32_t h, int32_t w, int32_t c, void *stream);
 
+/* ---- Winograd F(2x2, 3x3) conv + pool (interview page, "Conv optimisation",
+ *      item 3: (m + r - 1)^2 = 16 products per 2x2 output tile of a 3x3
+ *      filter instead of m^2 r^2 = 36, paid for with transforms and a small
+ *      loss of precision; the transforms are Lavin and Gray's minimal
+ *      filtering algorithm: U = G g G^T, V = B^T d B, Y = A^T [sum_c U.V] A) ----
+ *
+ * winograd_weights -- the transformed weights U = G g G^T of every (c, k),
+ * computed exactly (fp64) and rounded once to fp16.
+ *   w: HWIO [3, 3, c, k] (device); U: 16*c*k fp16 (device, caller-owned),
+ *   written in the library's operand layout [16][c/8][k][8]: U[xi][nu][c][k]
+ *   at (((4 xi + nu) * (c/8) + c/8) * k + k) * 8 + c % 8.  Compute once per
+ *   weight tensor and pass to chain_conv_pool_winograd.
+ *   c, k > 0 and multiples of 8 (else FC_E_SHAPE); 16*c*k < 2^31
+ *   (FC_E_UNSUPPORTED); NULL -> FC_E_NULL; pointers 16-byte aligned. */
+fc_status winograd_weights(const fc_half *w, fc_half *U, int32_t c, int32_t k, void *stream);
+
+/* chain_conv_pool_winograd -- y = pool2x2(act(conv(x, w) + b)) with the 3x3
+ * conv evaluated by F(2x2, 3x3) from U = winograd_weights(w): each 2x2
+ * Winograd output tile is one pool window (Welder notes, Conv + ReLU +
+ * MaxPool tile graph, Figure 5), so the conv output stays in registers.
+ * Numerics: V = B^T d B in fp16 arithmetic (rows first, one rounding per
+ * stage), the 16 channel contractions on the matrix cores with fp32
+ * accumulation, A^T M A + bias + act in fp32, one rounding to fp16; the pool
+ * and argmax as for chain_conv_pool (argmax on the fp16 values, first maximum
+ * in the order (0,0),(0,1),(1,0),(1,1)).  The result differs from the direct
+ * conv by the rounding of U and V (the precision loss the page names).
+ *   x NHWC [n,h,w,c]; U as written by winograd_weights for (c, k); b [k] or
+ *   NULL; y [n, h/2, w/2, k] (floor); argmax (max pool only, nullable) uint8
+ *   [n, h/2, w/2, k].  pool: FC_POOL_MAX_2X2_S2 or FC_POOL_AVG_2X2_S2
+ *   (FC_POOL_NONE -> FC_E_UNSUPPORTED).
+ * Implemented: r = s = 3, stride 1, pad 1, c in {32, 64} (pad other channel
+ * counts with pad_channels), k % 16 == 0 and k <= 128, n*h*w < 2^31 and
+ * h*w*c*2 < 2^31 bytes (one image); others FC_E_UNSUPPORTED (FC_E_SHAPE for c or k not
+ * multiples of 8).  All pointers, argmax included, 16-byte aligned. */
+fc_status chain_conv_pool_winograd(const fc_half *x, const fc_half *U, const fc_half *b, fc_act act, fc_pool pool,
+                                   fc_half *y, const fc_conv_shape *shape, uint8_t *argmax, void *stream);
+
 /* ---- input preparation (BOLT notes, "Templated code generation": tensors
  *      whose channel count is not a multiple of 8 are zero-padded) ----
  * dst[o][j][i] = j < c_in ? src[o][j][i] : 0 for a tensor viewed as

@@ -325,3 +325,40 @@ def test_residence_limits(L):
     import ctypes as C
     assert L.chain_conv_pool(P, P, NUL, 1, 1, P2, C.byref(fc.ConvShape(1, 6, 10, 128, 72, 3, 3, 1, 1)), NUL,
                              None) == E_UNSUP
+
+
+def test_winograd_validation(L):
+    import ctypes as C
+    ww = L.winograd_weights
+    assert ww(P, P2, 12, 128, None) == E_SHAPE
+    assert ww(P, P2, 64, 0, None) == E_SHAPE
+    assert ww(NUL, P2, 64, 128, None) == E_NULL
+    assert ww(P, BAD, 64, 128, None) == E_ALIGN
+    assert ww(P, P2, 65536, 4096, None) == E_UNSUP   # 16 c k >= 2^31
+
+    cw = L.chain_conv_pool_winograd
+
+    def call(sh, pool=1, act=1, am=NUL, x=P, U=P, y=P2, b=NUL):
+        return cw(x, U, b, act, pool, y, C.byref(sh), am, None)
+    empty = shape(n=0)
+    assert call(empty) == OK                            # validated, nothing to launch
+    assert call(shape(n=0, c=32, k=64)) == OK
+    assert call(shape(n=0, k=48)) == OK
+    assert call(shape(n=0, c=8, k=64)) == E_UNSUP       # c must be 32 or 64
+    assert call(shape(n=0, c=96, k=64)) == E_UNSUP
+    assert call(shape(n=0, k=40)) == E_UNSUP            # k % 16
+    assert call(shape(n=0, k=136)) == E_UNSUP
+    assert call(shape(n=0, c=60)) == E_SHAPE
+    assert call(shape(n=0, r=5, s=5)) == E_UNSUP
+    assert call(empty, pool=0) == E_UNSUP               # the chain pools every output tile
+    assert call(empty, pool=3) == E_ARG
+    assert call(empty, pool=2, am=P) == E_ARG           # argmax needs the max pool
+    assert call(empty, act=7) == E_ARG
+    assert call(empty, U=NUL) == E_NULL
+    assert call(shape(n=1), x=NUL) == E_NULL
+    assert call(empty, am=BAD) == E_ALIGN
+    assert call(empty, b=BAD) == E_ALIGN
+    assert call(shape(n=1, h=1, w=8)) == OK             # pooled output empty (floor)
+    big = shape(n=1, h=8192, w=2048, c=64, k=64)        # one image of 2 GiB: offsets exceed 31 bits
+    assert call(big) == E_UNSUP
+    assert b"2^31" in L.fc_last_error()
