@@ -483,7 +483,8 @@ def measure(torch, fc, prob, steps, warmup, unfused=True, warm=True):
 # (one record each; the two-GEMM LDS-resident shape under each kernel variant
 # and under the profiler's choice).
 SIDE_CONFIGS = [("b2b_gemm_tiny", None), ("b2b_gemm_rf", None), ("b2b_gemm_lds", None), ("b2b_gemm_lds", "stream"),
-                ("b2b_gemm_lds", "tuned"), ("conv3x3_conv1x1", None), ("conv3x3_relu_maxpool", "winograd")]
+                ("b2b_gemm_lds", "tuned"), ("conv3x3_conv1x1", None), ("conv3x3_conv1x1", "tuned"),
+                ("conv3x3_relu_maxpool", "winograd")]
 WORKLOADS = ["b2b_gemm_tiny", "b2b_gemm_rf", "b2b_gemm_lds", "gemm3_rf", "conv3x3_conv1x1", "conv3x3_conv1x1x2",
              "conv3x3_relu_maxpool", "conv3x3_bn_relu_maxpool", "conv3x3_relu_avgpool"]
 
@@ -511,8 +512,12 @@ def tune(fc, prob, name):
         prob.config["variant"] = "auto"
         prob.kernel = "k_conv_w" if best["variant"] == "lds_weights" else "k_conv_pool_wr"
         prob.traffic_key = name + "@" + best["variant"]
+    elif kind == "conv2":
+        w0, b0, w1, b1 = prob.W
+        best, table, _ = fc.tune_chain_conv2(prob.X[0], w0, b0, w1, b1, act="relu", out=prob.Y[0], reps=10)
+        prob.config["variant"] = "auto"
     else:
-        raise ValueError("--tune applies to the two-GEMM and the pooled conv workloads")
+        raise ValueError("--tune applies to the two-GEMM, the conv3x3 -> conv1x1 and the pooled conv workloads")
     log("%s tuned: %s waves %d (%s)" % (name, best["variant"], best["waves"], ", ".join(
         "%s/%d %.2f us" % (r["variant"], r["waves"], r["us"]) for r in table)))
     prob.config.update(tuned={"best": {"variant": best["variant"], "waves": best["waves"]},
@@ -562,8 +567,9 @@ def main():
     log("workload %s: %d buffer set(s), %.1f MB fused algorithmic bytes, %.3f GFLOP"
         % (args.workload, prob.nsets, prob.bytes_fused / 1e6, prob.flops / 1e9))
     if args.tune:
-        if prob.spec["kind"] not in ("gemm2", "conv_pool"):
-            print("bench.py: --tune applies to the two-GEMM and the pooled conv workloads", file=sys.stderr)
+        if prob.spec["kind"] not in ("gemm2", "conv2", "conv_pool") or args.variant == "winograd":
+            print("bench.py: --tune applies to the two-GEMM, the conv3x3 -> conv1x1 and the pooled direct-conv "
+                  "workloads", file=sys.stderr)
             sys.exit(2)
         tune(fc, prob, args.workload)
 

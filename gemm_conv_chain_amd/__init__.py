@@ -100,12 +100,18 @@ def lib():
                                            ctypes.POINTER(_i32), ctypes.POINTER(TuneEntry), _vp]
         L.chain_conv_pool_auto_config.argtypes = [ctypes.POINTER(ConvShape), ctypes.c_int, ctypes.c_int, _i32,
                                                   ctypes.POINTER(TuneEntry)]
+        L.chain_conv2_ex.argtypes = [_vp, _vp, _vp, ctypes.c_int, _vp, _vp, _i32, _vp, ctypes.POINTER(ConvShape),
+                                     _i32, _vp]
+        L.chain_conv2_tune.argtypes = [_vp, _vp, _vp, ctypes.c_int, _vp, _vp, _i32, _vp, ctypes.POINTER(ConvShape),
+                                       _i32, ctypes.POINTER(TuneEntry), _i32, ctypes.POINTER(_i32),
+                                       ctypes.POINTER(TuneEntry), _vp]
+        L.chain_conv2_auto_config.argtypes = [ctypes.POINTER(ConvShape), _i32, ctypes.c_int, ctypes.POINTER(TuneEntry)]
         L.winograd_weights.argtypes = [_vp, _vp, _i32, _i32, _vp]
         L.chain_conv_pool_winograd.argtypes = [_vp, _vp, _vp, ctypes.c_int, ctypes.c_int, _vp,
                                                ctypes.POINTER(ConvShape), _vp, _vp]
         L.fc_tune_clear.restype = None
         L.fc_tune_clear.argtypes = []
-        for name in ("winograd_weights", "chain_conv_pool_winograd", "chain_gemm2_ex", "chain_gemm2_tune_ex", "chain_gemm2_auto_config", "chain_conv_pool_tune",
+        for name in ("chain_conv2_auto_config", "chain_conv2_ex", "chain_conv2_tune", "winograd_weights", "chain_conv_pool_winograd", "chain_gemm2_ex", "chain_gemm2_tune_ex", "chain_gemm2_auto_config", "chain_conv_pool_tune",
                      "chain_conv_pool_auto_config", "chain_conv_pool_ex", "avgpool2x2", "fc_probe_mfma", "chain_conv_bn_pool", "chain_convN", "chain_gemm2_tune", "chain_gemm2_auto_variant", "chain_gemm2", "chain_gemm2_variant", "chain_gemmN", "chain_conv_pool", "chain_conv2", "gemm_bias_act",
                      "conv_bias_act", "maxpool2x2", "pad_channels"):
             getattr(L, name).restype = ctypes.c_int
@@ -524,8 +530,7 @@ def _w1x1(t, name, kin):
     raise ValueError("%s must be [%d, k] or [1, 1, %d, k], got %s" % (name, kin, kin, shp))
 
 
-def chain_conv2(x, w0, b0, w1, b1, act="relu", out=None):
-    """y = conv1x1(act(conv3x3(x, w0) + b0), w1) + b1; w1 is [k0, k1] or [1,1,k0,k1]."""
+def _conv2_prep(x, w0, b0, w1, b1, out):
     sh = _conv_shape(x, w0)
     P, Q = _conv_out_hw(sh)
     k1 = _w1x1(w1, "w1", sh.k)
@@ -535,9 +540,41 @@ def chain_conv2(x, w0, b0, w1, b1, act="relu", out=None):
         _validate(items)
         out = _empty((sh.n, P, Q, k1), x)
     _validate(items + [(out, "out", (sh.n, P, Q, k1), None)])
-    _check("chain_conv2", lib().chain_conv2(_ptr(x), _ptr(w0), _ptr(b0), _act(act), _ptr(w1), _ptr(b1), k1,
-                                            _ptr(out), ctypes.byref(sh), _stream(x)))
+    return sh, k1, out
+
+
+def chain_conv2(x, w0, b0, w1, b1, act="relu", out=None, waves=0):
+    """y = conv1x1(act(conv3x3(x, w0) + b0), w1) + b1; w1 is [k0, k1] or [1,1,k0,k1].
+    ``waves``: tile-owning waves per block (1..8), 0 = the library's choice."""
+    sh, k1, out = _conv2_prep(x, w0, b0, w1, b1, out)
+    _check("chain_conv2", lib().chain_conv2_ex(_ptr(x), _ptr(w0), _ptr(b0), _act(act), _ptr(w1), _ptr(b1), k1,
+                                               _ptr(out), ctypes.byref(sh), int(waves), _stream(x)))
     return out
+
+
+def tune_chain_conv2(x, w0, b0, w1, b1, act="relu", out=None, reps=20):
+    """Time every block shape of the conv3x3 -> conv1x1 chain for these tensors
+    (blocking) and cache the fastest (chain_conv2_tune).  Returns (best, table,
+    out) with dict rows {variant, waves, us}."""
+    sh, k1, out = _conv2_prep(x, w0, b0, w1, b1, out)
+    table = (TuneEntry * 16)()
+    best = TuneEntry()
+    n = _i32(0)
+    _check("chain_conv2_tune", lib().chain_conv2_tune(_ptr(x), _ptr(w0), _ptr(b0), _act(act), _ptr(w1), _ptr(b1), k1,
+                                                      _ptr(out), ctypes.byref(sh), int(reps), table, 16,
+                                                      ctypes.byref(n), ctypes.byref(best), _stream(x)))
+    return _entry(best, _VARIANT_NAME), [_entry(table[i], _VARIANT_NAME) for i in range(min(n.value, 16))], out
+
+
+def conv2_auto_config(n, h, w, c, k0, k1, act="relu"):
+    """{variant, waves} that chain_conv2 runs for this shape (waves=0)."""
+    e = TuneEntry()
+    sh = ConvShape(n, h, w, c, k0, 3, 3, 1, 1)
+    _check("chain_conv2_auto_config", lib().chain_conv2_auto_config(ctypes.byref(sh), int(k1), _act(act),
+                                                                    ctypes.byref(e)))
+    d = _entry(e, _VARIANT_NAME)
+    d.pop("us")
+    return d
 
 
 def chain_convN(x, ws, bs, acts, out=None):

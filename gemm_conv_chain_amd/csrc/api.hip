@@ -19,7 +19,7 @@ hipError_t run_conv_pool3x3(const half_t* x, const half_t* w, const half_t* scal
                             int waves, hipStream_t st);
 bool conv_pool_wr_fits(int W, int C, int K);
 hipError_t run_chain_conv2_3x3(const half_t* x, const half_t* w0, const half_t* b0, int act, const half_t* w1,
-                               const half_t* b1, half_t* y, int NB, int H, int W, int C, int K0, int K1,
+                               const half_t* b1, half_t* y, int NB, int H, int W, int C, int K0, int K1, int waves,
                                hipStream_t st);
 hipError_t run_chain_convN_3x3(const half_t* x, int nst, const half_t* const* w, const half_t* const* b,
                                const int* act, const int* widths, half_t* y, int NB, int H, int W, int C,
@@ -126,7 +126,7 @@ struct Config {
 typedef std::vector<int64_t> TuneKey;   // kind, device, shape ...
 std::mutex g_tune_mu;
 std::map<TuneKey, Config> g_tune;
-enum { TK_GEMM2 = 0, TK_CONV_POOL = 1 };
+enum { TK_GEMM2 = 0, TK_CONV_POOL = 1, TK_CONV2 = 2 };
 
 // The cached configuration for key (device appended here), if any.  The
 // device is only queried when something has been tuned.
@@ -187,6 +187,32 @@ Config gemm2_config(int64_t M, int32_t K0, int32_t N0, int32_t N1, int act, bool
         c.waves = 1;
         while (c.waves < 8 && (int64_t)c.waves * cus < tiles) c.waves *= 2;
     }
+    return c;
+}
+
+TuneKey conv2_key(const fc_conv_shape* s, int k1, int act)
+{
+    return {TK_CONV2, s->n, s->h, s->w, s->c, s->k, k1, act};
+}
+
+// Candidates of the conv3x3 -> conv1x1 chain (register-resident form): 8, 4,
+// 2 or 1 tile-owning waves per block.
+int conv2_candidates(Config* out)
+{
+    int n = 0;
+    for (int w : {8, 4, 2, 1}) out[n++] = Config{fc::VARIANT_RF, w};
+    return n;
+}
+
+// Untuned: as for the two-GEMM chain, the smallest power-of-two number of
+// tile-owning waves whose blocks, one per CU, cover the 32-pixel tiles.
+Config conv2_config(const fc_conv_shape* s, int k1, int act)
+{
+    Config c;
+    if (tuned_config(conv2_key(s, k1, act), &c)) return c;
+    const int64_t tiles = ((int64_t)s->n * s->h * s->w + 31) / 32, cus = fc::device_cu_count();
+    c = Config{fc::VARIANT_RF, 1};
+    while (c.waves < 8 && (int64_t)c.waves * cus < tiles) c.waves *= 2;
     return c;
 }
 
@@ -588,8 +614,8 @@ fc_status conv_bias_act(const fc_half* x, const fc_half* w, const fc_half* b, fc
     return chain_conv_pool(x, w, b, act, FC_POOL_NONE, y, shape, nullptr, stream);
 }
 
-fc_status chain_conv2(const fc_half* x, const fc_half* w0, const fc_half* b0, fc_act act, const fc_half* w1,
-                      const fc_half* b1, int32_t k1, fc_half* y, const fc_conv_shape* shape0, void* stream)
+static fc_status check_conv2(const fc_half* x, const fc_half* w0, const fc_half* b0, fc_act act, const fc_half* w1,
+                             const fc_half* b1, int32_t k1, const fc_half* y, const fc_conv_shape* shape0)
 {
     fc_status s = check_act(act);
     if (s != FC_OK) return s;
@@ -600,12 +626,62 @@ fc_status chain_conv2(const fc_half* x, const fc_half* w0, const fc_half* b0, fc
     if (!w0 || !w1 || (npix > 0 && (!x || !y))) return fail(FC_E_NULL, "x, w0, w1 and y are required");
     if (!aligned16(x) || !aligned16(w0) || !aligned16(w1) || !aligned16(y) || !aligned16(b0) || !aligned16(b1))
         return fail(FC_E_ALIGN, "tensor pointers must be 16-byte aligned");
-    if (npix == 0) return ok();
     if (!fc::rf_fits(9 * shape0->c, shape0->k, k1))
         return fail(FC_E_UNSUPPORTED, "w0 and w1 do not fit in LDS together");
+    return FC_OK;
+}
+
+fc_status chain_conv2_ex(const fc_half* x, const fc_half* w0, const fc_half* b0, fc_act act, const fc_half* w1,
+                         const fc_half* b1, int32_t k1, fc_half* y, const fc_conv_shape* shape0, int32_t waves,
+                         void* stream)
+{
+    if (waves < 0 || waves > 8) return fail(FC_E_ARG, "waves=%d: 1..8, or 0 for the library's choice", (int)waves);
+    fc_status s = check_conv2(x, w0, b0, act, w1, b1, k1, y, shape0);
+    if (s != FC_OK) return s;
+    if ((long)shape0->n * shape0->h * shape0->w == 0) return ok();
+    const int wv = waves > 0 ? waves : conv2_config(shape0, k1, (int)act).waves;
     return hip_status(fc::run_chain_conv2_3x3(H(x), H(w0), H(b0), act, H(w1), H(b1), Hm(y), shape0->n, shape0->h,
-                                              shape0->w, shape0->c, shape0->k, k1, (hipStream_t)stream),
+                                              shape0->w, shape0->c, shape0->k, k1, wv, (hipStream_t)stream),
                       "chain_conv2");
+}
+
+fc_status chain_conv2(const fc_half* x, const fc_half* w0, const fc_half* b0, fc_act act, const fc_half* w1,
+                      const fc_half* b1, int32_t k1, fc_half* y, const fc_conv_shape* shape0, void* stream)
+{
+    return chain_conv2_ex(x, w0, b0, act, w1, b1, k1, y, shape0, 0, stream);
+}
+
+fc_status chain_conv2_auto_config(const fc_conv_shape* shape0, int32_t k1, fc_act act, fc_tune_entry* out)
+{
+    if (!shape0 || !out) return fail(FC_E_NULL, "shape0 and out are required");
+    fc_status s = check_act(act);
+    if (s != FC_OK) return s;
+    if (k1 <= 0 || k1 % 8) return fail(FC_E_SHAPE, "k1=%d must be a positive multiple of 8", k1);
+    s = check_conv(shape0, 128);
+    if (s != FC_OK) return s;
+    const Config c = conv2_config(shape0, k1, (int)act);
+    *out = fc_tune_entry{c.variant, c.waves, -1.0f};
+    return ok();
+}
+
+fc_status chain_conv2_tune(const fc_half* x, const fc_half* w0, const fc_half* b0, fc_act act, const fc_half* w1,
+                           const fc_half* b1, int32_t k1, fc_half* y, const fc_conv_shape* shape0, int32_t reps,
+                           fc_tune_entry* table, int32_t capacity, int32_t* count, fc_tune_entry* best, void* stream)
+{
+    fc_status s = check_conv2(x, w0, b0, act, w1, b1, k1, y, shape0);
+    if (s != FC_OK) return s;
+    if ((long)shape0->n * shape0->h * shape0->w == 0) return fail(FC_E_SHAPE, "empty output: nothing to time");
+    if (reps < 1 || reps > 1000) return fail(FC_E_SHAPE, "reps=%d outside 1..1000", (int)reps);
+    if (capacity < 0 || (capacity > 0 && !table)) return fail(FC_E_NULL, "table is required for capacity > 0");
+    Config cand[8];
+    const int n = conv2_candidates(cand);
+    hipStream_t st = (hipStream_t)stream;
+    auto launch = [&](const Config& c) {
+        return fc::run_chain_conv2_3x3(H(x), H(w0), H(b0), act, H(w1), H(b1), Hm(y), shape0->n, shape0->h, shape0->w,
+                                       shape0->c, shape0->k, k1, c.waves, st);
+    };
+    return profile("chain_conv2_tune", launch, cand, n, reps, conv2_key(shape0, k1, (int)act), table, capacity, count,
+                   best, st);
 }
 
 fc_status chain_convN(const fc_half* x, const fc_conv_shape* shape0, int32_t nstages, const fc_half* const* w,

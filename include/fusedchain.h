@@ -313,6 +313,34 @@ fc_status chain_conv2(const fc_half *x, const fc_half *w0, const fc_half *b0, fc
                       const fc_half *w1, const fc_half *b1, int32_t k1, fc_half *y,
                       const fc_conv_shape *shape0, void *stream);
 
+/* chain_conv2_ex -- chain_conv2 with the block shape chosen by the caller:
+ * waves = tile-owning waves per block (1..8; a block's round covers 32 * waves
+ * pixels) or 0 for the library's choice (the profiled one if
+ * chain_conv2_tune ran for this shape, else the smallest power of two whose
+ * blocks, one per CU, cover the 32-pixel tiles).  Other waves -> FC_E_ARG. */
+fc_status chain_conv2_ex(const fc_half *x, const fc_half *w0, const fc_half *b0, fc_act act, const fc_half *w1,
+                         const fc_half *b1, int32_t k1, fc_half *y, const fc_conv_shape *shape0, int32_t waves,
+                         void *stream);
+
+/* The configuration chain_conv2 runs for this shape on the current device
+ * (variant FC_VARIANT_RF, waves; us = -1): the tuned one, else the rule of
+ * chain_conv2_ex(waves = 0).  Host only. */
+fc_status chain_conv2_auto_config(const fc_conv_shape *shape0, int32_t k1, fc_act act, fc_tune_entry *out);
+
+/* chain_conv2_tune -- the profiler of chain_conv2 (BOLT notes, "Light-weight
+ * performance profiler"): times reps launches (1..1000, after one untimed
+ * launch) of each block shape (8, 4, 2, 1 tile-owning waves; variant
+ * FC_VARIANT_RF) on this input, writes up to capacity rows of table
+ * (us = mean microseconds per launch), *count = candidates timed, *best = the
+ * fastest, and caches it for (device, shape, k1, act): chain_conv2 and
+ * chain_conv2_ex(waves = 0) then run it.  y is written (by the winner last).
+ * Synchronises the stream.  Errors as chain_conv2; an empty output ->
+ * FC_E_SHAPE. */
+fc_status chain_conv2_tune(const fc_half *x, const fc_half *w0, const fc_half *b0, fc_act act, const fc_half *w1,
+                           const fc_half *b1, int32_t k1, fc_half *y, const fc_conv_shape *shape0, int32_t reps,
+                           fc_tune_entry *table, int32_t capacity, int32_t *count, fc_tune_entry *best,
+                           void *stream);
+
 /*
  * chain_convN -- a 3x3 convolution followed by 1x1 convolutions in one
  * kernel, every intermediate kept in registers (BOLT notes, "Persistent

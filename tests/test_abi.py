@@ -362,3 +362,25 @@ def test_winograd_validation(L):
     big = shape(n=1, h=8192, w=2048, c=64, k=64)        # one image of 2 GiB: offsets exceed 31 bits
     assert call(big) == E_UNSUP
     assert b"2^31" in L.fc_last_error()
+
+
+def test_conv2_waves_and_tuner_validation(L):
+    import ctypes as C
+    sh0 = shape(k=64)
+    ex = L.chain_conv2_ex
+    assert ex(P, P, NUL, 1, P, NUL, 64, P2, C.byref(shape(n=0, k=64)), 0, None) == OK
+    assert ex(P, P, NUL, 1, P, NUL, 64, P2, C.byref(shape(n=0, k=64)), 4, None) == OK
+    assert ex(P, P, NUL, 1, P, NUL, 64, P2, C.byref(sh0), 9, None) == E_ARG
+    assert ex(P, P, NUL, 1, P, NUL, 64, P2, C.byref(sh0), -1, None) == E_ARG
+    assert ex(P, P, NUL, 1, P, NUL, 60, P2, C.byref(sh0), 0, None) == E_SHAPE
+    tab = (fc.TuneEntry * 4)()
+    n = C.c_int32(0)
+    best = fc.TuneEntry()
+    tn = L.chain_conv2_tune
+    assert tn(P, P, NUL, 1, P, NUL, 64, P2, C.byref(sh0), 0, tab, 4, C.byref(n), C.byref(best), None) == E_SHAPE
+    assert tn(P, P, NUL, 1, P, NUL, 64, P2, C.byref(sh0), 1001, tab, 4, C.byref(n), C.byref(best), None) == E_SHAPE
+    assert tn(P, P, NUL, 1, P, NUL, 64, P2, C.byref(shape(n=0, k=64)), 5, tab, 4, C.byref(n), C.byref(best),
+              None) == E_SHAPE
+    assert tn(P, P, NUL, 1, P, NUL, 64, P2, C.byref(sh0), 5, None, 4, C.byref(n), C.byref(best), None) == E_NULL
+    assert tn(P, P, NUL, 1, P, NUL, 64, P2, C.byref(shape(c=64, k=128)), 5, tab, 4, C.byref(n), C.byref(best),
+              None) == E_UNSUP

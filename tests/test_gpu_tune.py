@@ -113,3 +113,38 @@ def test_tune_conv_pool(fc, pool):
     assert fc.conv_auto_config(3, 30, 34, 64, 128, pool=pool, argmax=True)["variant"] == "reg_weights"
     fc.tune_clear()
     assert fc.conv_auto_config(3, 30, 34, 64, 128, pool=pool) == {"variant": "reg_weights", "waves": 0}
+
+
+@pytest.mark.parametrize("waves", [1, 2, 4, 8])
+@pytest.mark.parametrize("n,h,w,c,k0,k1", [(2, 33, 35, 64, 64, 256), (1, 7, 9, 32, 96, 40)])
+def test_conv2_waves(fc, n, h, w, c, k0, k1, waves):
+    # every block shape the profiler may choose computes the chain (several
+    # rounds per block and a ragged last tile in the first shape)
+    d = inputs.conv2_inputs(n, h, w, c, k0, k1, seed=h + waves)
+    print("case conv2 waves", waves, n, h, w, c, k0, k1, flush=True)
+    y = to_np(fc.chain_conv2(dev(d["x"]), dev(d["w0"]), dev(d["b0"]), dev(d["w1"]), dev(d["b1"]), act="relu",
+                             waves=waves))
+    ref, _ = oracle.chain_conv2(d["x"], d["w0"], d["b0"], oracle.ACT_RELU, d["w1"], d["b1"])
+    assert_close(y, ref, "conv2 waves=%d" % waves)
+
+
+def test_tune_conv2(fc):
+    d = inputs.conv2_inputs(4, 28, 28, 64, 64, 256, seed=5)
+    args = [dev(d[k]) for k in ("x", "w0", "b0", "w1", "b1")]
+    print("case tune conv2", flush=True)
+    fc.tune_clear()
+    rule = fc.conv2_auto_config(4, 28, 28, 64, 64, 256)
+    assert rule["variant"] == "rf" and rule["waves"] in (1, 2, 4, 8)
+    best, table, out = fc.tune_chain_conv2(*args, reps=3)
+    torch.cuda.synchronize()
+    print(best, table, flush=True)
+    assert sorted(r["waves"] for r in table) == [1, 2, 4, 8]
+    assert all(r["variant"] == "rf" and r["us"] > 0 for r in table)
+    fastest = min(table, key=lambda r: r["us"])
+    assert best["waves"] == fastest["waves"]
+    assert fc.conv2_auto_config(4, 28, 28, 64, 64, 256) == {"variant": "rf", "waves": best["waves"]}
+    ref, _ = oracle.chain_conv2(d["x"], d["w0"], d["b0"], oracle.ACT_RELU, d["w1"], d["b1"])
+    assert_close(to_np(out), ref, "tuned conv2 output")
+    assert_close(to_np(fc.chain_conv2(*args)), ref, "conv2 auto after tuning")
+    fc.tune_clear()
+    assert fc.conv2_auto_config(4, 28, 28, 64, 64, 256) == rule
