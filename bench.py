@@ -386,6 +386,41 @@ def mfma_probe(torch, fc, waves_per_simd=2, iters=2048):
             "sclk_ghz_median": round(clk[len(clk) // 2], 3) if clk else None}
 
 
+def read_probe(torch, fc, nbytes, copies=5):
+    """The rate at which the GPU streams nbytes from memory once (fc_probe_read,
+    event-timed), on buffers evicted from the 256 MiB Infinity Cache by the
+    other copies (copies x nbytes > 256 MiB): mean of one pass over the
+    copies after a first, untimed pass."""
+    n16 = nbytes // 16
+    bufs = [torch.empty(n16 * 4, dtype=torch.int32, device="cuda").fill_(i + 1) for i in range(copies)]
+    sink = torch.zeros(4 * torch.cuda.get_device_properties(0).multi_processor_count, dtype=torch.int32,
+                       device="cuda")
+    for b in bufs:
+        fc.probe_read(b, sink)
+    torch.cuda.synchronize()
+    ms = []
+    for b in bufs:
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0.record()
+        fc.probe_read(b, sink)
+        t1.record()
+        torch.cuda.synchronize()
+        ms.append(t0.elapsed_time(t1))
+    m = sum(ms) / len(ms)
+    del bufs
+    return {"bytes": nbytes, "us": round(m * 1e3, 2), "tb_per_s": round(nbytes / (m * 1e-3) / 1e12, 3)}
+
+
+def launch_floor(torch, fc, steps=50):
+    """Per-launch time of an almost empty kernel (one block reading 16 bytes)
+    replayed back to back from a captured HIP graph, like the chains' steps:
+    the floor under the small-problem rows."""
+    buf = torch.zeros(4, dtype=torch.int32, device="cuda")
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+    ms, _, _, _ = time_steps(torch, lambda i: fc.probe_read(buf, sink), steps, 3)
+    return round(ms, 5)
+
+
 def cpu_model():
     try:
         with open("/proc/cpuinfo") as f:
@@ -588,6 +623,12 @@ def main():
         probe = mfma_probe(torch, fc)
         log("mfma probe: %.1f TFLOP/s (%.1f%% of nominal), shader clock %s GHz"
             % (probe["tflops"], probe["pct_of_nominal"], probe["sclk_ghz_median"]))
+        # the read rate of a stream the size of the 65536 x 576 fp16 row matrix
+        # of the two-GEMM LDS-resident workload, and the graph launch floor
+        probe["hbm_read"] = read_probe(torch, fc, 65536 * 576 * 2)
+        probe["launch_floor_ms"] = launch_floor(torch, fc)
+        log("read probe: %.2f TB/s streaming %.1f MB once; graph launch floor %.4f ms"
+            % (probe["hbm_read"]["tb_per_s"], probe["hbm_read"]["bytes"] / 1e6, probe["launch_floor_ms"]))
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -610,6 +651,10 @@ def main():
             rec = measure(torch, fc, p, args.steps, args.warmup, unfused=not args.no_unfused, warm=False)
             if probe:
                 rec["pct_of_measured_mfma_peak"] = round(100 * rec["tflops"] / probe["tflops"], 2)
+                if p.spec["kind"] == "gemm2" and p.spec["M"] <= 4096:
+                    # launch-bound: the step against an almost empty graph-replayed launch
+                    rec["launch_floor_ms"] = probe["launch_floor_ms"]
+                    rec["over_launch_floor"] = round(rec["ms_per_step"] / probe["launch_floor_ms"], 2)
             side[key] = rec
             del p
             torch.cuda.empty_cache()

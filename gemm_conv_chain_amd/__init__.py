@@ -91,6 +91,7 @@ def lib():
         L.chain_gemm2_ex.argtypes = [_vp, _vp, _vp, ctypes.c_int, _vp, _vp, _vp, _i64, _i32, _i32, _i32,
                                      ctypes.c_int, _i32, _vp]
         L.fc_probe_mfma.argtypes = [_i32, _i32, _vp, _vp, _i32, ctypes.POINTER(_i32), _vp]
+        L.fc_probe_read.argtypes = [_vp, _i64, _vp, _i32, ctypes.POINTER(_i32), _vp]
         L.chain_gemm2_tune_ex.argtypes = [_vp, _vp, _vp, ctypes.c_int, _vp, _vp, _vp, _i64, _i32, _i32, _i32, _i32,
                                           ctypes.POINTER(TuneEntry), _i32, ctypes.POINTER(_i32),
                                           ctypes.POINTER(TuneEntry), _vp]
@@ -112,7 +113,7 @@ def lib():
         L.fc_tune_clear.restype = None
         L.fc_tune_clear.argtypes = []
         for name in ("chain_conv2_auto_config", "chain_conv2_ex", "chain_conv2_tune", "winograd_weights", "chain_conv_pool_winograd", "chain_gemm2_ex", "chain_gemm2_tune_ex", "chain_gemm2_auto_config", "chain_conv_pool_tune",
-                     "chain_conv_pool_auto_config", "chain_conv_pool_ex", "avgpool2x2", "fc_probe_mfma", "chain_conv_bn_pool", "chain_convN", "chain_gemm2_tune", "chain_gemm2_auto_variant", "chain_gemm2", "chain_gemm2_variant", "chain_gemmN", "chain_conv_pool", "chain_conv2", "gemm_bias_act",
+                     "chain_conv_pool_auto_config", "chain_conv_pool_ex", "avgpool2x2", "fc_probe_mfma", "fc_probe_read", "chain_conv_bn_pool", "chain_convN", "chain_gemm2_tune", "chain_gemm2_auto_variant", "chain_gemm2", "chain_gemm2_variant", "chain_gemmN", "chain_conv_pool", "chain_conv2", "gemm_bias_act",
                      "conv_bias_act", "maxpool2x2", "pad_channels"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
@@ -349,6 +350,18 @@ def probe_mfma(stamps, sink, waves_per_simd=2, iters=2048):
     capacity = min(stamps.numel() // 4, sink.numel())
     _check("fc_probe_mfma", lib().fc_probe_mfma(int(waves_per_simd), int(iters), _ptr(stamps), _ptr(sink),
                                                 int(capacity), ctypes.byref(blocks), _stream(stamps)))
+    return blocks.value
+
+
+def probe_read(buf, sink):
+    """Enqueue the memory read-rate probe (fc_probe_read) over the bytes of the
+    contiguous device tensor buf on the current stream; sink: int32 [n] with n
+    >= the grid (4 x the CU count for large buffers).  Returns the grid size."""
+    torch = _torch()
+    _validate([(buf, "buf", None, getattr(buf, "dtype", None)), (sink, "sink", None, torch.int32)])
+    blocks = _i32(0)
+    _check("fc_probe_read", lib().fc_probe_read(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink),
+                                                int(sink.numel()), ctypes.byref(blocks), _stream(buf)))
     return blocks.value
 
 

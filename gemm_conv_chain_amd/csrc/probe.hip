@@ -1,6 +1,7 @@
-// probe.hip -- measurement aid, not part of any chain: the matrix-core rate
-// and the shader clock this GPU sustains, for reading the chains' fractions
-// of peak against what the hardware actually delivers.
+// probe.hip -- measurement aids, not part of any chain: the matrix-core rate
+// and the shader clock this GPU sustains, and the rate at which it streams a
+// buffer from memory, for reading the chains' fractions of peak against what
+// the hardware actually delivers.
 //
 // Every wave issues `iters` rounds of eight independent fp16 MFMAs
 // (32x32x16, fp32 accumulate) on operands held in registers -- no memory
@@ -49,7 +50,51 @@ void k_mfma_probe(int iters, unsigned long long* __restrict__ stamps, float* __r
     }
 }
 
+// Streams n16 16-byte vectors of p once: consecutive threads read consecutive
+// vectors (whole cache lines per wave), four independent loads in flight per
+// thread per round, grid-stride; the XOR of everything read goes to
+// sink[block] so that no load is dead.
+__global__ __launch_bounds__(256) void k_read_probe(const u32x4* __restrict__ p, long n16, unsigned* __restrict__ sink)
+{
+    u32x4 acc = {0u, 0u, 0u, 0u};
+    const long stride = (long)gridDim.x * 256;
+    long i = (long)blockIdx.x * 256 + threadIdx.x;
+    for (; i + 3 * stride < n16; i += 4 * stride) {
+        const u32x4 a = __builtin_nontemporal_load(p + i);
+        const u32x4 b = __builtin_nontemporal_load(p + i + stride);
+        const u32x4 c = __builtin_nontemporal_load(p + i + 2 * stride);
+        const u32x4 d = __builtin_nontemporal_load(p + i + 3 * stride);
+        acc ^= a ^ b ^ c ^ d;
+    }
+    for (; i < n16; i += stride) acc ^= __builtin_nontemporal_load(p + i);
+    unsigned v = acc[0] ^ acc[1] ^ acc[2] ^ acc[3];
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v ^= (unsigned)__shfl_xor((int)v, o);
+    __shared__ unsigned part[4];
+    if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = v;
+    __syncthreads();
+    if (threadIdx.x == 0) sink[blockIdx.x] = part[0] ^ part[1] ^ part[2] ^ part[3];
+}
+
 }  // namespace fc
+
+extern "C" fc_status fc_probe_read(const void* buf, int64_t nbytes, uint32_t* sink, int32_t capacity,
+                                   int32_t* blocks, void* stream)
+{
+    if (!buf || !sink || !blocks) return FC_E_NULL;
+    if (nbytes < 16 || nbytes % 16) return FC_E_SHAPE;
+    if (((uintptr_t)buf & 15u) || ((uintptr_t)sink & 3u)) return FC_E_ALIGN;
+    const long n16 = (long)(nbytes / 16);
+    long grid = 4L * fc::device_cu_count();   // four blocks per CU, or fewer for small buffers
+    if (grid > (n16 + 255) / 256) grid = (n16 + 255) / 256;
+    if (grid < 1) return FC_E_HIP;
+    if (grid > capacity) return FC_E_SHAPE;
+    hipLaunchKernelGGL(fc::k_read_probe, dim3((unsigned)grid), dim3(256), 0, (hipStream_t)stream,
+                       reinterpret_cast<const fc::u32x4*>(buf), n16, reinterpret_cast<unsigned*>(sink));
+    if (hipGetLastError() != hipSuccess) return FC_E_HIP;
+    *blocks = (int32_t)grid;
+    return FC_OK;
+}
 
 extern "C" fc_status fc_probe_mfma(int32_t waves_per_simd, int32_t iters, uint64_t* stamps, float* sink,
                                    int32_t capacity, int32_t* blocks, void* stream)

@@ -449,6 +449,21 @@ fc_status pad_channels(const fc_half *src, fc_half *dst, int64_t outer, int32_t 
 fc_status fc_probe_mfma(int32_t waves_per_simd, int32_t iters, uint64_t *stamps, float *sink,
                         int32_t capacity, int32_t *blocks, void *stream);
 
+/*
+ * fc_probe_read -- measurement aid, not part of any chain: streams the nbytes
+ * (a multiple of 16, >= 16) at buf once with 16-byte non-temporal loads,
+ * consecutive threads on consecutive vectors, four independent loads in
+ * flight per thread, four 256-thread blocks per CU (fewer for small buffers).
+ * Timed by the caller around the launch, it gives the memory read rate the
+ * GPU sustains for a stream of that size (cold: after other data evicted it).
+ *   buf: device, 16-byte aligned; sink: device, uint32 [capacity] (one XOR of
+ *   the data per block, keeps the loads live); blocks (host, out): the grid.
+ *   FC_E_SHAPE (no launch) if the grid exceeds capacity.  Enqueued on stream,
+ *   asynchronous.  Returns the status only.
+ */
+fc_status fc_probe_read(const void *buf, int64_t nbytes, uint32_t *sink, int32_t capacity, int32_t *blocks,
+                        void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -384,3 +384,12 @@ def test_conv2_waves_and_tuner_validation(L):
     assert tn(P, P, NUL, 1, P, NUL, 64, P2, C.byref(sh0), 5, None, 4, C.byref(n), C.byref(best), None) == E_NULL
     assert tn(P, P, NUL, 1, P, NUL, 64, P2, C.byref(shape(c=64, k=128)), 5, tab, 4, C.byref(n), C.byref(best),
               None) == E_UNSUP
+
+
+def test_probe_read_validation(L):
+    import ctypes as C
+    blocks = C.c_int32(0)
+    assert L.fc_probe_read(NUL, 64, P2, 8, C.byref(blocks), None) == E_NULL
+    assert L.fc_probe_read(P, 8, P2, 8, C.byref(blocks), None) == E_SHAPE
+    assert L.fc_probe_read(P, 72, P2, 8, C.byref(blocks), None) == E_SHAPE    # not a multiple of 16
+    assert L.fc_probe_read(BAD, 64, P2, 8, C.byref(blocks), None) == E_ALIGN

@@ -33,3 +33,26 @@ def test_probe_refuses_small_buffers(fc):
         fc.probe_mfma(stamps, sink, 2, 16)
     torch.cuda.synchronize()
     assert int(stamps.abs().sum()) == 0        # nothing was launched
+
+
+def test_probe_read_reads_everything(fc):
+    # the per-block XORs combine to the XOR of every 32-bit word of the buffer
+    # (a ragged size: not a multiple of the grid's stride)
+    import numpy as np
+    n = 4 * 100003
+    host = np.random.default_rng(3).integers(0, 2**31 - 1, n, dtype=np.int64).astype(np.int32)
+    buf = torch.from_numpy(host).cuda()
+    sink = torch.zeros(4 * 1024, dtype=torch.int32, device="cuda")
+    print("case read probe", flush=True)
+    blocks = fc.probe_read(buf, sink)
+    torch.cuda.synchronize()
+    got = np.bitwise_xor.reduce(sink[:blocks].cpu().numpy().view(np.uint32))
+    assert got == np.bitwise_xor.reduce(host.view(np.uint32))
+
+
+def test_probe_read_rate_plausible(fc):
+    import bench
+    r = bench.read_probe(torch, fc, 64 << 20, copies=5)
+    print(r, flush=True)
+    assert 0.3 < r["tb_per_s"] < 1.2 * bench.PEAK_HBM_GBS / 1000.0
+    assert 0 < bench.launch_floor(torch, fc, steps=10) < 0.1
