@@ -393,7 +393,7 @@ def read_probe(torch, fc, nbytes, copies=5):
     copies after a first, untimed pass."""
     n16 = nbytes // 16
     bufs = [torch.empty(n16 * 4, dtype=torch.int32, device="cuda").fill_(i + 1) for i in range(copies)]
-    sink = torch.zeros(4 * torch.cuda.get_device_properties(0).multi_processor_count, dtype=torch.int32,
+    sink = torch.zeros(2 * torch.cuda.get_device_properties(0).multi_processor_count, dtype=torch.int32,
                        device="cuda")
     for b in bufs:
         fc.probe_read(b, sink)

@@ -356,7 +356,7 @@ def probe_mfma(stamps, sink, waves_per_simd=2, iters=2048):
 def probe_read(buf, sink):
     """Enqueue the memory read-rate probe (fc_probe_read) over the bytes of the
     contiguous device tensor buf on the current stream; sink: int32 [n] with n
-    >= the grid (4 x the CU count for large buffers).  Returns the grid size."""
+    >= the grid (2 x the CU count for large buffers).  Returns the grid size."""
     torch = _torch()
     _validate([(buf, "buf", None, getattr(buf, "dtype", None)), (sink, "sink", None, torch.int32)])
     blocks = _i32(0)

@@ -453,7 +453,7 @@ fc_status fc_probe_mfma(int32_t waves_per_simd, int32_t iters, uint64_t *stamps,
  * fc_probe_read -- measurement aid, not part of any chain: streams the nbytes
  * (a multiple of 16, >= 16) at buf once with 16-byte non-temporal loads,
  * consecutive threads on consecutive vectors, four independent loads in
- * flight per thread, four 256-thread blocks per CU (fewer for small buffers).
+ * flight per thread, two 256-thread blocks per CU (fewer for small buffers).
  * Timed by the caller around the launch, it gives the memory read rate the
  * GPU sustains for a stream of that size (cold: after other data evicted it).
  *   buf: device, 16-byte aligned; sink: device, uint32 [capacity] (one XOR of

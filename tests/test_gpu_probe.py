@@ -42,7 +42,7 @@ def test_probe_read_reads_everything(fc):
     n = 4 * 100003
     host = np.random.default_rng(3).integers(0, 2**31 - 1, n, dtype=np.int64).astype(np.int32)
     buf = torch.from_numpy(host).cuda()
-    sink = torch.zeros(4 * 1024, dtype=torch.int32, device="cuda")
+    sink = torch.zeros(2 * 1024, dtype=torch.int32, device="cuda")
     print("case read probe", flush=True)
     blocks = fc.probe_read(buf, sink)
     torch.cuda.synchronize()
