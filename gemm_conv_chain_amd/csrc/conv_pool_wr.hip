@@ -31,12 +31,16 @@
 //     Pixels outside the image, and the two padding columns, read zero from
 //     outside the buffer resource -- the conv's zero padding needs no branch.
 //   * Operand A is read from the halo with ds_read_b128 in MFMA layout.  A
-//     pixel's 32 channels of one half are four 16-byte slots, slot s of pixel
-//     p stored at s ^ ((p >> 1) & 3); with the 20-pixel row stride the eight
-//     lanes of each LDS access phase hit eight different 16-byte bank groups
-//     for every tap.  The DMA picks, for every LDS slot, the global 16 bytes
-//     that belong there (quads of lanes still read one 64-byte segment: the
-//     fast address path).
+//     pixel's 32 channels of one half are four 16-byte slots; slot s of the
+//     pixel in halo row hr, column hc is stored at s ^ wr_swz(hr, hc) with
+//     wr_swz = (hr & 1) | ((hc >> 2) & 1) << 1.  The LDS (64 banks) serves 16
+//     lanes of a 16-byte read per clock: such a group reads pixels of two
+//     halo rows and four columns spaced 2 apart, i.e. four pixels with each
+//     value of hc % 4 (the 64-byte piece, with the 20-pixel row stride); the
+//     swizzle gives those four distinct slots, so the 16 lanes touch 16
+//     different 16-byte bank groups for every tap.  The DMA picks, for every
+//     LDS slot, the global 16 bytes that belong there (quads of lanes still
+//     read one 64-byte segment: the fast address path).
 //   * Per k-step a wave issues NRT ds_read_b128 and 2 NRT MFMAs (32x32x16
 //     f16, fp32 accumulate); the next k-step's operands are read while the
 //     current MFMAs run.
@@ -76,6 +80,9 @@ static_assert(WR_SLOTS % 64 == 0, "whole DMA instructions per part");
 static_assert(2 * WR_LDS <= 160 * 1024, "two blocks per CU");
 
 enum { WR_MAX = 0, WR_AVG = 1 };
+
+// slot swizzle of halo pixel (hr, hc) (see the header comment)
+__device__ __forceinline__ int wr_swz(int hr, int hc) { return (hr & 1) | (((hc >> 2) & 1) << 1); }
 
 struct WrArgs {
     const half_t* x;   // [NB, H, W, 64]
@@ -203,7 +210,7 @@ void k_conv_pool_wr(WrArgs a)
                 const int slot = 64 * j + ln;
                 const int p = slot >> 2, part = slot & 3;
                 const int hr = p / WR_HROW, hcl = p - hr * WR_HROW;
-                const int g = part ^ ((p >> 1) & 3);
+                const int g = part ^ wr_swz(hr, hcl);
                 const unsigned off =
                     hcl < 18 ? (unsigned)(hr * W + hcl) * (unsigned)(2 * C) + (unsigned)(64 * wc + 16 * g) : CS_OUTSIDE;
                 dma16(rs, off, (const lds_half*)(dst + j * 1024));
@@ -216,7 +223,7 @@ void k_conv_pool_wr(WrArgs a)
                 const int hr = p / WR_HROW, hcl = p - hr * WR_HROW;
                 const int ih = ih0 + hr, iw = iw0 + hcl;
                 const bool ok = hcl < 18 && ih >= 0 && ih < a.H && iw >= 0 && iw < W;
-                const int g = part ^ ((p >> 1) & 3);
+                const int g = part ^ wr_swz(hr, hcl);
                 const unsigned off =
                     ok ? (unsigned)((ih - ib) * W + iw) * (unsigned)(2 * C) + (unsigned)(64 * wc + 16 * g) : CS_OUTSIDE;
                 dma16(rs, off, (const lds_half*)(dst + j * 1024));
@@ -226,14 +233,14 @@ void k_conv_pool_wr(WrArgs a)
 
     // ---- A-operand offset in a part: lane l reads, for MFMA row m = l % 32
     // (window w = m / 4, dy = (m / 2) % 2, dx = m % 2) and k-group l / 32, tap
-    // (r, s), k-step half q, slot 2q + l / 32 of halo pixel
-    // p = (dy + r) * 20 + 2w + dx + s.
+    // (r, s), k-step half q, slot 2q + l / 32 of halo pixel (row dy + r,
+    // column 2w + dx + s).
     auto a_off = [&](int tap, int q) -> int {
         const int ln = lane_id_here();   // recomputed per k-step, not held across the loop
         const int m = ln & 31;
         const int r = tap / 3, s = tap % 3;
-        const int p = ((m >> 1) & 1) * WR_HROW + 2 * (m >> 2) + (m & 1) + r * WR_HROW + s;
-        return p * 64 + (((2 * q + (ln >> 5)) ^ ((p >> 1) & 3)) << 4);
+        const int hr = ((m >> 1) & 1) + r, hc = 2 * (m >> 2) + (m & 1) + s;
+        return (hr * WR_HROW + hc) * 64 + (((2 * q + (ln >> 5)) ^ wr_swz(hr, hc)) << 4);
     };
 
     floatx16 acc[WR_NRT][2];

@@ -123,7 +123,8 @@ def pmc(d, workload, json_path=None):
                  "conv3x3_relu_maxpool@reg_weights": "k_conv_pool_wr",
                  "conv3x3_relu_maxpool@lds_weights": "k_conv_w<4, 1",
                  "conv3x3_bn_relu_maxpool@lds_weights": "k_conv_w<4, 1",
-                 "conv3x3_relu_avgpool@lds_weights": "k_conv_w<4, 2"}[workload]
+                 "conv3x3_relu_avgpool@lds_weights": "k_conv_w<4, 2",
+                 "conv3x3_relu_maxpool@winograd": "k_conv_pool_wino"}[workload]
         fk = [k for k in fetch if fused in k]
         if len(fk) != 1:
             raise SystemExit("cannot identify the fused kernel among %s" % list(fetch))
