@@ -22,8 +22,8 @@
 //     from global memory straight into LDS by the LDS-DMA load
 //     (buffer_load_dwordx4 ... lds: no registers, no LDS stores) into three
 //     rotating buffers, two steps ahead of the MFMAs that read them; each step
-//     ends with one block barrier.  Chunks are XOR-swizzled (16-half segment
-//     ^= row & 3) so the transposing fragment reads are conflict-free without
+//     ends with one block barrier.  Chunks are XOR-swizzled (64-byte piece
+//     ^= row & 3, the WTile layout) so the transposing fragment reads are conflict-free without
 //     padding, which the DMA's contiguous 1 KiB per instruction excludes.
 //   * Rows of A arrive quad-coalesced (each quad of lanes reads one 64-byte
 //     segment) two steps ahead, into a ring of three register sets, and are
@@ -86,7 +86,7 @@ inline size_t cs_lds_bytes(int N0P, int N1p)
 
 // Rows [r0, r0 + RC) x columns [c0, c0 + WC) of the row-major G (valid rows
 // x cols, leading dimension ld; zero outside) into the XOR-swizzled LDS tile
-// T (row stride WC halves; element (r, c) at r * WC + (c ^ ((r & 3) << 4))):
+// T (row stride WC halves; element (r, c) at r * WC + (c ^ ((r & 3) << 5))):
 // CS_DMA_PER_WAVE requests per wave.  A DMA instruction writes 1 KiB of
 // consecutive LDS, lane i at bytes [16i, 16i + 16), so lane i fetches the
 // global vector whose swizzled slot that is.  Each instruction addresses its
