@@ -15,16 +15,18 @@ The functions mirror the C entry points:
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 import re
 
 __all__ = ["TuneEntry", "tune_chain_gemm2_table", "auto_config", "tune_conv_pool", "conv_auto_config", "CONV_VARIANT", "lib", "FusedChainError", "chain_gemm2", "tune_chain_gemm2", "auto_variant", "tune_clear", "chain_gemmN", "chain_conv_pool", "chain_conv_bn_pool", "chain_conv2", "chain_convN",
            "gemm_bias_act", "conv_bias_act", "maxpool2x2", "avgpool2x2", "pad_channels", "pad_weight_channels", "abi_version", "ACT", "VARIANT",
-           "LIB_PATH", "HEADER_PATH", "exported_names"]
+           "LIB_PATH", "POISON_LIB_PATH", "poison_build", "HEADER_PATH", "exported_names"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libfusedchain.so")
+POISON_LIB_PATH = os.path.join(_HERE, "libfusedchain_poison.so")
 HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "fusedchain.h")
 
 ACT = {"none": 0, "relu": 1, "gelu_tanh": 2, "hardswish": 3}
@@ -50,74 +52,101 @@ class TuneEntry(ctypes.Structure):
 
 
 _lib = None
+_poison_lib = None
+_override = None
 _vp = ctypes.c_void_p
 _i32 = ctypes.c_int32
 _i64 = ctypes.c_int64
 
 
 def lib():
-    """Load libfusedchain.so (built by ``gemm_conv_chain_amd.build``)."""
+    """The library every call goes through: libfusedchain.so (built by
+    ``gemm_conv_chain_amd.build``), or the poison debug build inside a
+    ``poison_build()`` block."""
     global _lib
+    if _override is not None:
+        return _override
     if _lib is None:
-        if not os.path.exists(LIB_PATH):
-            raise FusedChainError("load", -1, "libfusedchain.so not built: run python -m gemm_conv_chain_amd.build")
-        L = ctypes.CDLL(LIB_PATH)
-        L.fc_abi_version.restype = _i32
-        L.fc_status_str.restype = ctypes.c_char_p
-        L.fc_status_str.argtypes = [ctypes.c_int]
-        L.fc_last_error.restype = ctypes.c_char_p
-        L.chain_gemm2.argtypes = [_vp, _vp, _vp, ctypes.c_int, _vp, _vp, _vp, _i64, _i32, _i32, _i32, _vp]
-        L.chain_gemm2_variant.argtypes = [_vp, _vp, _vp, ctypes.c_int, _vp, _vp, _vp, _i64, _i32, _i32, _i32,
-                                          ctypes.c_int, _vp]
-        L.chain_gemmN.argtypes = [_vp, _i32, ctypes.POINTER(_vp), ctypes.POINTER(_vp), ctypes.POINTER(ctypes.c_int),
-                                  ctypes.POINTER(_i32), _vp, _i64, _vp]
-        L.chain_conv_pool.argtypes = [_vp, _vp, _vp, ctypes.c_int, ctypes.c_int, _vp, ctypes.POINTER(ConvShape),
-                                      _vp, _vp]
-        L.chain_conv2.argtypes = [_vp, _vp, _vp, ctypes.c_int, _vp, _vp, _i32, _vp, ctypes.POINTER(ConvShape), _vp]
-        L.gemm_bias_act.argtypes = [_vp, _vp, _vp, ctypes.c_int, _vp, _i64, _i32, _i32, _vp]
-        L.conv_bias_act.argtypes = [_vp, _vp, _vp, ctypes.c_int, _vp, ctypes.POINTER(ConvShape), _vp]
-        L.maxpool2x2.argtypes = [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _vp]
-        L.avgpool2x2.argtypes = [_vp, _vp, _i32, _i32, _i32, _i32, _vp]
-        L.pad_channels.argtypes = [_vp, _vp, _i64, _i32, _i32, _i32, _vp]
-        L.chain_gemm2_tune.argtypes = [_vp, _vp, _vp, ctypes.c_int, _vp, _vp, _vp, _i64, _i32, _i32, _i32, _i32,
-                                       ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_float), _vp]
-        L.chain_gemm2_auto_variant.argtypes = [_i64, _i32, _i32, _i32, ctypes.c_int, ctypes.POINTER(ctypes.c_int)]
-        L.chain_convN.argtypes = [_vp, ctypes.POINTER(ConvShape), _i32, ctypes.POINTER(_vp), ctypes.POINTER(_vp),
-                                  ctypes.POINTER(ctypes.c_int), ctypes.POINTER(_i32), _vp, _vp]
-        L.chain_conv_bn_pool.argtypes = [_vp, _vp, _vp, _vp, ctypes.c_int, ctypes.c_int, _vp,
-                                         ctypes.POINTER(ConvShape), _vp, _vp]
-        L.chain_conv_pool_ex.argtypes = [_vp, _vp, _vp, _vp, ctypes.c_int, ctypes.c_int, _vp,
-                                         ctypes.POINTER(ConvShape), _vp, ctypes.c_int, _i32, _vp]
-        L.chain_gemm2_ex.argtypes = [_vp, _vp, _vp, ctypes.c_int, _vp, _vp, _vp, _i64, _i32, _i32, _i32,
-                                     ctypes.c_int, _i32, _vp]
-        L.fc_probe_mfma.argtypes = [_i32, _i32, _vp, _vp, _i32, ctypes.POINTER(_i32), _vp]
-        L.fc_probe_read.argtypes = [_vp, _i64, _vp, _i32, ctypes.POINTER(_i32), _vp]
-        L.chain_gemm2_tune_ex.argtypes = [_vp, _vp, _vp, ctypes.c_int, _vp, _vp, _vp, _i64, _i32, _i32, _i32, _i32,
-                                          ctypes.POINTER(TuneEntry), _i32, ctypes.POINTER(_i32),
-                                          ctypes.POINTER(TuneEntry), _vp]
-        L.chain_gemm2_auto_config.argtypes = [_i64, _i32, _i32, _i32, ctypes.c_int, ctypes.POINTER(TuneEntry)]
-        L.chain_conv_pool_tune.argtypes = [_vp, _vp, _vp, _vp, ctypes.c_int, ctypes.c_int, _vp,
-                                           ctypes.POINTER(ConvShape), _vp, _i32, ctypes.POINTER(TuneEntry), _i32,
-                                           ctypes.POINTER(_i32), ctypes.POINTER(TuneEntry), _vp]
-        L.chain_conv_pool_auto_config.argtypes = [ctypes.POINTER(ConvShape), ctypes.c_int, ctypes.c_int, _i32,
-                                                  ctypes.POINTER(TuneEntry)]
-        L.chain_conv2_ex.argtypes = [_vp, _vp, _vp, ctypes.c_int, _vp, _vp, _i32, _vp, ctypes.POINTER(ConvShape),
-                                     _i32, _vp]
-        L.chain_conv2_tune.argtypes = [_vp, _vp, _vp, ctypes.c_int, _vp, _vp, _i32, _vp, ctypes.POINTER(ConvShape),
-                                       _i32, ctypes.POINTER(TuneEntry), _i32, ctypes.POINTER(_i32),
-                                       ctypes.POINTER(TuneEntry), _vp]
-        L.chain_conv2_auto_config.argtypes = [ctypes.POINTER(ConvShape), _i32, ctypes.c_int, ctypes.POINTER(TuneEntry)]
-        L.winograd_weights.argtypes = [_vp, _vp, _i32, _i32, _vp]
-        L.chain_conv_pool_winograd.argtypes = [_vp, _vp, _vp, ctypes.c_int, ctypes.c_int, _vp,
-                                               ctypes.POINTER(ConvShape), _vp, _vp]
-        L.fc_tune_clear.restype = None
-        L.fc_tune_clear.argtypes = []
-        for name in ("chain_conv2_auto_config", "chain_conv2_ex", "chain_conv2_tune", "winograd_weights", "chain_conv_pool_winograd", "chain_gemm2_ex", "chain_gemm2_tune_ex", "chain_gemm2_auto_config", "chain_conv_pool_tune",
-                     "chain_conv_pool_auto_config", "chain_conv_pool_ex", "avgpool2x2", "fc_probe_mfma", "fc_probe_read", "chain_conv_bn_pool", "chain_convN", "chain_gemm2_tune", "chain_gemm2_auto_variant", "chain_gemm2", "chain_gemm2_variant", "chain_gemmN", "chain_conv_pool", "chain_conv2", "gemm_bias_act",
-                     "conv_bias_act", "maxpool2x2", "pad_channels"):
-            getattr(L, name).restype = ctypes.c_int
-        _lib = L
+        _lib = _load(LIB_PATH)
     return _lib
+
+
+@contextlib.contextmanager
+def poison_build():
+    """Route every call inside the with-block through libfusedchain_poison.so,
+    the -DFC_DEBUG_POISON build: its kernels overwrite each LDS buffer with a
+    poison pattern (fp16 65504) when the barrier that releases it has passed,
+    so a read that races its producer changes the results.  Test use only."""
+    global _override, _poison_lib
+    if _poison_lib is None:
+        _poison_lib = _load(POISON_LIB_PATH)
+    prev, _override = _override, _poison_lib
+    try:
+        yield _poison_lib
+    finally:
+        _override = prev
+
+
+def _load(path):
+    if not os.path.exists(path):
+        raise FusedChainError("load", -1, "%s not built: run python -m gemm_conv_chain_amd.build"
+                              % os.path.basename(path))
+    L = ctypes.CDLL(path)
+    L.fc_abi_version.restype = _i32
+    L.fc_status_str.restype = ctypes.c_char_p
+    L.fc_status_str.argtypes = [ctypes.c_int]
+    L.fc_last_error.restype = ctypes.c_char_p
+    L.chain_gemm2.argtypes = [_vp, _vp, _vp, ctypes.c_int, _vp, _vp, _vp, _i64, _i32, _i32, _i32, _vp]
+    L.chain_gemm2_variant.argtypes = [_vp, _vp, _vp, ctypes.c_int, _vp, _vp, _vp, _i64, _i32, _i32, _i32,
+                                      ctypes.c_int, _vp]
+    L.chain_gemmN.argtypes = [_vp, _i32, ctypes.POINTER(_vp), ctypes.POINTER(_vp), ctypes.POINTER(ctypes.c_int),
+                              ctypes.POINTER(_i32), _vp, _i64, _vp]
+    L.chain_conv_pool.argtypes = [_vp, _vp, _vp, ctypes.c_int, ctypes.c_int, _vp, ctypes.POINTER(ConvShape),
+                                  _vp, _vp]
+    L.chain_conv2.argtypes = [_vp, _vp, _vp, ctypes.c_int, _vp, _vp, _i32, _vp, ctypes.POINTER(ConvShape), _vp]
+    L.gemm_bias_act.argtypes = [_vp, _vp, _vp, ctypes.c_int, _vp, _i64, _i32, _i32, _vp]
+    L.conv_bias_act.argtypes = [_vp, _vp, _vp, ctypes.c_int, _vp, ctypes.POINTER(ConvShape), _vp]
+    L.maxpool2x2.argtypes = [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _vp]
+    L.avgpool2x2.argtypes = [_vp, _vp, _i32, _i32, _i32, _i32, _vp]
+    L.pad_channels.argtypes = [_vp, _vp, _i64, _i32, _i32, _i32, _vp]
+    L.chain_gemm2_tune.argtypes = [_vp, _vp, _vp, ctypes.c_int, _vp, _vp, _vp, _i64, _i32, _i32, _i32, _i32,
+                                   ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_float), _vp]
+    L.chain_gemm2_auto_variant.argtypes = [_i64, _i32, _i32, _i32, ctypes.c_int, ctypes.POINTER(ctypes.c_int)]
+    L.chain_convN.argtypes = [_vp, ctypes.POINTER(ConvShape), _i32, ctypes.POINTER(_vp), ctypes.POINTER(_vp),
+                              ctypes.POINTER(ctypes.c_int), ctypes.POINTER(_i32), _vp, _vp]
+    L.chain_conv_bn_pool.argtypes = [_vp, _vp, _vp, _vp, ctypes.c_int, ctypes.c_int, _vp,
+                                     ctypes.POINTER(ConvShape), _vp, _vp]
+    L.chain_conv_pool_ex.argtypes = [_vp, _vp, _vp, _vp, ctypes.c_int, ctypes.c_int, _vp,
+                                     ctypes.POINTER(ConvShape), _vp, ctypes.c_int, _i32, _vp]
+    L.chain_gemm2_ex.argtypes = [_vp, _vp, _vp, ctypes.c_int, _vp, _vp, _vp, _i64, _i32, _i32, _i32,
+                                 ctypes.c_int, _i32, _vp]
+    L.fc_probe_mfma.argtypes = [_i32, _i32, _vp, _vp, _i32, ctypes.POINTER(_i32), _vp]
+    L.fc_probe_read.argtypes = [_vp, _i64, _vp, _i32, ctypes.POINTER(_i32), _vp]
+    L.chain_gemm2_tune_ex.argtypes = [_vp, _vp, _vp, ctypes.c_int, _vp, _vp, _vp, _i64, _i32, _i32, _i32, _i32,
+                                      ctypes.POINTER(TuneEntry), _i32, ctypes.POINTER(_i32),
+                                      ctypes.POINTER(TuneEntry), _vp]
+    L.chain_gemm2_auto_config.argtypes = [_i64, _i32, _i32, _i32, ctypes.c_int, ctypes.POINTER(TuneEntry)]
+    L.chain_conv_pool_tune.argtypes = [_vp, _vp, _vp, _vp, ctypes.c_int, ctypes.c_int, _vp,
+                                       ctypes.POINTER(ConvShape), _vp, _i32, ctypes.POINTER(TuneEntry), _i32,
+                                       ctypes.POINTER(_i32), ctypes.POINTER(TuneEntry), _vp]
+    L.chain_conv_pool_auto_config.argtypes = [ctypes.POINTER(ConvShape), ctypes.c_int, ctypes.c_int, _i32,
+                                              ctypes.POINTER(TuneEntry)]
+    L.chain_conv2_ex.argtypes = [_vp, _vp, _vp, ctypes.c_int, _vp, _vp, _i32, _vp, ctypes.POINTER(ConvShape),
+                                 _i32, _vp]
+    L.chain_conv2_tune.argtypes = [_vp, _vp, _vp, ctypes.c_int, _vp, _vp, _i32, _vp, ctypes.POINTER(ConvShape),
+                                   _i32, ctypes.POINTER(TuneEntry), _i32, ctypes.POINTER(_i32),
+                                   ctypes.POINTER(TuneEntry), _vp]
+    L.chain_conv2_auto_config.argtypes = [ctypes.POINTER(ConvShape), _i32, ctypes.c_int, ctypes.POINTER(TuneEntry)]
+    L.winograd_weights.argtypes = [_vp, _vp, _i32, _i32, _vp]
+    L.chain_conv_pool_winograd.argtypes = [_vp, _vp, _vp, ctypes.c_int, ctypes.c_int, _vp,
+                                           ctypes.POINTER(ConvShape), _vp, _vp]
+    L.fc_tune_clear.restype = None
+    L.fc_tune_clear.argtypes = []
+    for name in ("chain_conv2_auto_config", "chain_conv2_ex", "chain_conv2_tune", "winograd_weights", "chain_conv_pool_winograd", "chain_gemm2_ex", "chain_gemm2_tune_ex", "chain_gemm2_auto_config", "chain_conv_pool_tune",
+                 "chain_conv_pool_auto_config", "chain_conv_pool_ex", "avgpool2x2", "fc_probe_mfma", "fc_probe_read", "chain_conv_bn_pool", "chain_convN", "chain_gemm2_tune", "chain_gemm2_auto_variant", "chain_gemm2", "chain_gemm2_variant", "chain_gemmN", "chain_conv_pool", "chain_conv2", "gemm_bias_act",
+                 "conv_bias_act", "maxpool2x2", "pad_channels"):
+        getattr(L, name).restype = ctypes.c_int
+    return L
 
 
 def _lib_status_str(s):

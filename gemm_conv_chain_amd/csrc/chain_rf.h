@@ -74,7 +74,7 @@ constexpr size_t RF_OSTAGE_BYTES = (size_t)RF_WAVES * 32 * RF_OLD * 2;
 
 // LDS bytes used by the RF kernel for a given padded problem: W0 and W1 in
 // their natural layout (rows = k), the biases, the per-wave output tiles.
-inline size_t rf_lds_bytes(int N0P, int K0p, int N1p)
+__host__ __device__ inline size_t rf_lds_bytes(int N0P, int K0p, int N1p)
 {
     return (size_t)K0p * wtile_ld(N0P) * 2 + (size_t)N0P * wtile_ld(N1p) * 2 + (size_t)(N0P + N1p) * 4 +
            RF_OSTAGE_BYTES;
@@ -82,7 +82,7 @@ inline size_t rf_lds_bytes(int N0P, int K0p, int N1p)
 
 // ... and with nmid middle GEMMs (padded widths Nmp[0..nmid-1]): their weight
 // tiles sit between W0 and the last GEMM's, their biases after b1.
-inline size_t rf_lds_bytes_n(int N0P, int K0p, int N1p, int nmid, const int* Nmp)
+__host__ __device__ inline size_t rf_lds_bytes_n(int N0P, int K0p, int N1p, int nmid, const int* Nmp)
 {
     size_t b = (size_t)K0p * wtile_ld(N0P) * 2;
     int nin = N0P;
@@ -164,6 +164,11 @@ void k_chain_rf(Loader ld, RfArgs a)
     // weight requests, which hit L2, are not queued behind the row stream.
     // Weights beyond one batch of RF_WB vectors per thread are staged after
     // the barrier-free first batch (their loads then wait behind the rows).
+    if constexpr (kPoison) {
+        lds_poison(smem, (int)(NMID ? rf_lds_bytes_n(N0P, a.K0p, a.N1p, NMID, a.Nmp) : rf_lds_bytes(N0P, a.K0p, a.N1p)),
+                   tid, RF_THREADS);
+        __syncthreads();
+    }
     WStage2<RF_WB> ws;
     ws.G0 = a.W0; ws.rows0 = a.K0; ws.cols0 = a.N0; ws.ldg0 = a.N0; ws.nr0 = a.K0p; ws.ncp0 = N0P; ws.T0 = W0n;
     ws.G1 = a.W1; ws.rows1 = NMID ? a.Nin1 : a.N0; ws.cols1 = a.N1; ws.ldg1 = a.N1; ws.nr1 = nin1p; ws.ncp1 = a.N1p;

@@ -79,7 +79,7 @@ struct StreamArgs {
 };
 
 // LDS bytes: three weight buffers, then the biases in fp32 (N0P + N1p).
-inline size_t cs_lds_bytes(int N0P, int N1p)
+__host__ __device__ inline size_t cs_lds_bytes(int N0P, int N1p)
 {
     return (size_t)CS_NBUF * CS_BUFH * 2 + (size_t)(N0P + N1p) * 4;
 }
@@ -138,6 +138,10 @@ void k_chain_stream(StreamArgs a)
     const int nch = KCH ? KCH : (a.K0 + CS_KC0 - 1) / CS_KC0;
     const int np = a.N1p / CS_N1C;
     const int S = nch + np * NJ;                                     // stream steps per tile
+    if constexpr (kPoison) {
+        lds_poison(smem, (int)cs_lds_bytes(N0P, a.N1p), tid, CS_THREADS);
+        __syncthreads();
+    }
 
     // Biases in fp32 (zero past N0 / N1), once per block, before any request
     // of the stream is in flight.
@@ -240,6 +244,10 @@ void k_chain_stream(StreamArgs a)
         // bufs[0]; issues the group of step c + 2.
         auto step0 = [&](int c, auto SC) {
             constexpr int sc = decltype(SC)::value;
+            if constexpr (kPoison) {   // bufs[2] was released by the last step's barrier
+                lds_poison(bufs[2], CS_BUFH * 2, tid, CS_THREADS);
+                __syncthreads();
+            }
             dma_step(c + 2 < S ? c + 2 : c + 2 - S, bufs[2]);
             const bool pa = c + 2 < nch;
             if (pa) load_a(rsA, c + 2, ring[(sc + 2) % 3]);
@@ -324,6 +332,10 @@ void k_chain_stream(StreamArgs a)
 #pragma unroll
             for (int j = 0; j < NJ; ++j) {
                 const int tau = nch + p * NJ + j;
+                if constexpr (kPoison) {
+                    lds_poison(bufs[2], CS_BUFH * 2, tid, CS_THREADS);
+                    __syncthreads();
+                }
                 dma_step(tau + 2 < S ? tau + 2 : tau + 2 - S, bufs[2]);
                 if (p == 0 && j == 0) {
                     // the next tile's first chunks (rows past M read zero)

@@ -149,7 +149,7 @@ struct ConvWArgs {
 // LDS: weights [Kp][KP] (natural, swizzled or padded), biases, scales, the
 // tile counter, then a 1 KiB output staging area per wave.
 constexpr int CW_OSTAGE = 1024;
-inline size_t convw_lds_bytes(int KP, int Kp)
+__host__ __device__ inline size_t convw_lds_bytes(int KP, int Kp)
 {
     return (size_t)Kp * wtile_ld(KP) * 2 + (size_t)KP * 8 + 16 + (size_t)8 * CW_OSTAGE;
 }
@@ -323,6 +323,10 @@ void k_conv_w(ConvWArgs a)
         }
     }
 
+    if constexpr (kPoison) {
+        lds_poison(smem, (int)convw_lds_bytes(KP, a.Kp), tid, NTHR);
+        __syncthreads();
+    }
     stage_natural<8>(a.w, a.Kr, a.K, a.K, a.Kp, KP, Wn, tid, NTHR);
     for (int i = tid; i < KP; i += NTHR) {
         bs[i] = (a.b && i < a.K) ? (float)a.b[i] : 0.0f;

@@ -140,6 +140,10 @@ void k_conv_pool_wr(WrArgs a)
         for (int pc = 0; pc < (9 * C + WR_WPIECE - 1) / WR_WPIECE; ++pc) {
             const int r0 = pc * WR_WPIECE;
             if (pc > 0) __syncthreads();   // the previous piece's fragments are read
+            if constexpr (kPoison) {
+                lds_poison(smem, WR_WPIECE * Wn.ld * 2, tid, WR_THREADS);
+                __syncthreads();
+            }
             stage_natural<8>(a.w + (long)r0 * a.K, 9 * C - r0, a.K, a.K, WR_WPIECE, KPB, Wn, tid, WR_THREADS);
             __syncthreads();
 #pragma unroll
@@ -155,6 +159,10 @@ void k_conv_pool_wr(WrArgs a)
             }
         }
         __syncthreads();   // LDS is reused for the halos
+    }
+    if constexpr (kPoison) {
+        lds_poison(smem, WR_LDS, tid, WR_THREADS);
+        __syncthreads();
     }
     lds_char* const lds = (lds_char*)smem;
     lds_half* const ost = (lds_half*)(lds + WR_STAGE_OFF + wave * WR_STAGE);
@@ -379,6 +387,10 @@ void k_conv_pool_wr(WrArgs a)
     __syncthreads();
     while (rt + WR_NRT <= rt_end) {
         const long rtn = rt + WR_NRT;
+        if constexpr (kPoison) {   // the previous tile's halo buffer, released by its barriers
+            lds_poison(lds + (sb ^ 1) * WR_BUF_BYTES, WR_BUF_BYTES, tid, WR_THREADS);
+            __syncthreads();
+        }
         if (rtn < rt_end) dma_tile(rtn, (int)min((long)WR_NRT, rt_end - rtn), lds + (sb ^ 1) * WR_BUF_BYTES);
         compute(IntC<WR_NRT>{}, lds + sb * WR_BUF_BYTES);
         finish(rt, WR_NRT);

@@ -111,6 +111,11 @@ __global__ __launch_bounds__(WI_THREADS) void k_conv_pool_wino(WinoArgs a)
     const long b_begin = lb * a.nbatch / gridDim.x;
     const long b_end = (lb + 1) * a.nbatch / gridDim.x;
 
+    if constexpr (kPoison) {
+        lds_poison(smem, (int)wino_lds_bytes<C>(a.K), tid, WI_THREADS);
+        __syncthreads();
+    }
+
     // ---- transformed weights of this wave's 16 channels -> registers:
     // operand B of (xn, s): rows c = 32 s + 8 (lane / 16) + [0, 8), column
     // 16 wave + lane % 16.
@@ -246,6 +251,16 @@ __global__ __launch_bounds__(WI_THREADS) void k_conv_pool_wino(WinoArgs a)
 
     for (long bt = b_begin; bt < b_end; ++bt) {
         const int par = (int)((bt - b_begin) & 1);
+        if constexpr (kPoison) {
+            // released by the last barrier: the halo buffer batch bt + 2 refills,
+            // the V buffer batch bt + 1's transform writes, the staging areas
+            // batch bt's epilogue writes
+            lds_poison(hbuf + par * HBUF, HBUF * 2, tid, WI_THREADS);
+            lds_poison(vbuf + (par ^ 1) * (16 * WI_TILES * C), 16 * WI_TILES * C * 2, tid, WI_THREADS);
+            lds_poison(ost + par * (WI_TILES * a.K), WI_TILES * a.K * 2, tid, WI_THREADS);
+            lds_poison(ast + par * (WI_TILES * a.K), WI_TILES * a.K, tid, WI_THREADS);
+            __syncthreads();
+        }
         if (bt > b_begin) store_batch(bt - 1, par ^ 1);
         // batch bt + 2's halo into the buffer batch bt's transform has released
         if (bt + 2 < b_end) issue_halo(bt + 2, hbuf + par * HBUF);

@@ -542,4 +542,35 @@ __device__ __forceinline__ void wave_lds_sync()
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 }
 
+// ------------------------------------------------------------------ LDS poison
+// Debug build (-DFC_DEBUG_POISON: libfusedchain_poison.so).  A kernel fills
+// its LDS with a poison pattern when it starts, and the kernels that reuse LDS
+// buffers (DMA rings, double buffers) poison each buffer again after the
+// barrier that releases it and before its next producer writes it.  A read
+// that is not ordered after its producer -- a missing barrier, a memory-counter
+// wait that retires too few requests -- then returns poison instead of stale
+// but plausible data.  The pattern is the fp16 pair (65504, 65504): finite, so
+// a read whose products are multiplied by zero stays harmless, and large enough
+// that a poisoned operand sends the outputs out of tolerance or to infinity;
+// as bytes (0xFF, 0x7B) it is no valid pool index.  In the product build
+// kPoison is false and every poison step compiles to nothing.
+#ifdef FC_DEBUG_POISON
+constexpr bool kPoison = true;
+#else
+constexpr bool kPoison = false;
+#endif
+constexpr unsigned kPoisonWord = 0x7BFF7BFFu;
+
+// Fill `bytes` (a multiple of 16) of LDS at p (an LDS pointer, or the
+// kernel's dynamic LDS array) with the poison; the threads tid = 0 ..
+// nthreads - 1 of the caller take 16-byte pieces in turn.
+template <class P>
+__device__ __forceinline__ void lds_poison(P p, int bytes, int tid, int nthreads)
+{
+    typedef FC_LDS u32x4 lds_u32x4;
+    const u32x4 v = {kPoisonWord, kPoisonWord, kPoisonWord, kPoisonWord};
+    lds_u32x4* q = (lds_u32x4*)p;
+    for (int i = tid; i < bytes / 16; i += nthreads) q[i] = v;
+}
+
 }  // namespace fc

@@ -43,7 +43,7 @@ __host__ __device__ constexpr int lds_wcols(int N0P, bool chain)
     return chain ? (N0P > LDS_N1C ? N0P : LDS_N1C) : N0P;
 }
 
-inline size_t lds_lds_bytes(int N0P, bool chain)
+__host__ __device__ inline size_t lds_lds_bytes(int N0P, bool chain)
 {
     size_t b = (size_t)2 * LDS_KC * (lds_wcols(N0P, chain) + 32) * 2;
     if (chain) b += (size_t)LDS_MT * (N0P + 8) * 2;
@@ -172,6 +172,10 @@ void k_gemm_lds(LdsArgs a)
     half8 af0[2][4], af1[2][4], af2[2][4];
     WChunk<NV0> w0r;
 
+    if constexpr (kPoison) {
+        lds_poison(smem, (int)lds_lds_bytes(N0P, CHAIN), tid, LDS_THREADS);
+        __syncthreads();
+    }
     // Prologue: W0 chunk 0 into LDS, A chunks 0 and 1 in flight.
     load_a(0, af0);
     if (1 < nch0) load_a(1, af1);
@@ -191,6 +195,10 @@ void k_gemm_lds(LdsArgs a)
     // ---------------- GEMM0 (transposed: C0^T = W0^T A^T) ----------------
     auto step0 = [&](int c, half8 (&raw)[2][4], half8 (&ld2)[2][4]) {
         const bool more = c + 1 < nch0;
+        if constexpr (kPoison) {   // the buffer this step refills was released by the last barrier
+            if (more) lds_poison(Wb + ((c + 1) & 1) * WBUF, WBUF * 2, tid, LDS_THREADS);
+            __syncthreads();
+        }
         if (more) wchunk_load<NV0>(W0b, a.K0, ncols0, a.N0, LDS_KC * (c + 1), N0P, tid, w0r);
         if (c + 2 < nch0) load_a(c + 2, ld2);
         __builtin_amdgcn_sched_barrier(0);   // keep the prefetches issued here
@@ -282,6 +290,11 @@ void k_gemm_lds(LdsArgs a)
     for (int n1c = 0; n1c < a.N1; n1c += LDS_N1C) {
         const half_t* W1b = a.W1 + n1c;
         const int ncols1 = a.N1 - n1c;
+        if constexpr (kPoison) {   // both weight buffers (the last output tile) and b1s are free
+            lds_poison(Wb, 2 * WBUF * 2, tid, LDS_THREADS);
+            lds_poison(b1s, LDS_N1C * 4, tid, LDS_THREADS);
+            __syncthreads();
+        }
         if (n1c > 0) wchunk_load<NV1>(W1b, a.N0, ncols1, a.N1, 0, LDS_N1C, tid, w1r);
         for (int i = tid; i < LDS_N1C; i += LDS_THREADS) b1s[i] = (a.b1 && i < ncols1) ? (float)a.b1[n1c + i] : 0.0f;
         wchunk_store<NV1>(Wb + buf * WBUF, LDW, LDS_N1C, tid, w1r);
@@ -294,6 +307,10 @@ void k_gemm_lds(LdsArgs a)
         }
         for (int c = 0; c < nch1; ++c) {
             const bool more = c + 1 < nch1;
+            if constexpr (kPoison) {
+                if (more) lds_poison(Wb + (buf ^ 1) * WBUF, WBUF * 2, tid, LDS_THREADS);
+                __syncthreads();
+            }
             if (more) wchunk_load<NV1>(W1b, a.N0, ncols1, a.N1, LDS_KC * (c + 1), LDS_N1C, tid, w1r);
             __builtin_amdgcn_sched_barrier(0);
             const lds_half* wb = Wb + buf * WBUF;

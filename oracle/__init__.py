@@ -73,12 +73,16 @@ def build(force: bool = True) -> str:
 
 
 def lib():
+    """liboracle.so, or the build named by $FC_ORACLE_LIB (the address- and
+    undefined-behaviour-sanitizer build the host sanitizer test runs the pins
+    against)."""
     global _lib
     with _lock:
         if _lib is None:
-            if not os.path.exists(_LIB):
+            path = os.environ.get("FC_ORACLE_LIB") or _LIB
+            if path == _LIB and not os.path.exists(_LIB):
                 build(force=True)
-            L = ctypes.CDLL(_LIB)
+            L = ctypes.CDLL(path)
             L.orc_f16_to_f64.restype = ctypes.c_double
             L.orc_f16_to_f64.argtypes = [ctypes.c_uint16]
             L.orc_f64_to_f16.restype = ctypes.c_uint16

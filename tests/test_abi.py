@@ -32,6 +32,18 @@ def test_exports_every_declared_symbol(L):
         assert hasattr(L, n), n
 
 
+def test_poison_build_exports_the_same_abi(L):
+    # the LDS-poison debug build is the same library with extra LDS writes
+    with fc.poison_build() as D:
+        assert fc.lib() is D and D is not L
+        for n in fc.exported_names():
+            assert hasattr(D, n), n
+        assert D.fc_abi_version() == L.fc_abi_version()
+        # validation is unchanged: a null operand is refused before any HIP call
+        assert D.chain_gemm2(NUL, P, P, 1, P, P, P, 64, 64, 64, 64, NUL) == E_NULL
+    assert fc.lib() is L
+
+
 def test_version_and_status_strings(L):
     assert fc.abi_version() == 2
     for code, name in enumerate(["FC_OK", "FC_E_NULL", "FC_E_SHAPE", "FC_E_ALIGN", "FC_E_UNSUPPORTED", "FC_E_HIP",
