@@ -481,6 +481,31 @@ def roofline(prob, ms_kernel, tr):
     return roof
 
 
+_MODEL_VARIANT = {"k_chain_rf": "rf", "k_gemm_lds": "lds", "k_chain_stream": "stream", "k_conv_w": "lds_weights",
+                  "k_conv_pool_wino": "winograd", "k_conv_pool_wr": "reg_weights"}
+
+
+def traffic_model(prob, tr):
+    """Predicted bytes of the kernel's tile schedule beside the measured FETCH
+    (gemm_conv_chain_amd.traffic_model: algorithmic reads, Welder's per-tile
+    MemTraffic, and an LRU model of each XCD's L2 = the predicted FETCH_SIZE),
+    in MB per launch; None for workloads without a model."""
+    from gemm_conv_chain_amd import traffic_model as tm
+    m = tm.for_workload(prob.spec, _MODEL_VARIANT.get(prob.kernel))
+    if m is None:
+        return None
+    mb = lambda v: round(v / 1e6, 3)
+    rec = {"unit": "MB", "kernel": m["kernel"], "blocks": m["blocks"],
+           "read_algorithmic": mb(m["read_algorithmic"]), "read_per_tile": mb(m["read_per_tile"]),
+           "read_l2_model": mb(m["read_l2_model"]), "write": mb(m["write"]),
+           "lds_bytes_per_block": m["lds_bytes_per_block"], "lds_fits": m["lds_fits"]}
+    if tr is not None:
+        fetch = tr["fetch_kib"] * tr["fetch_scale"] * 1024
+        rec["measured_read"] = mb(fetch)
+        rec["measured_read_over_l2_model"] = round(fetch / m["read_l2_model"], 4)
+    return rec
+
+
 def measure(torch, fc, prob, steps, warmup, unfused=True, warm=True):
     """Time the fused step (and the unfused two-kernel baseline); returns the
     record of one workload."""
@@ -491,6 +516,9 @@ def measure(torch, fc, prob, steps, warmup, unfused=True, warm=True):
     tr = measured_traffic(prob.traffic_key, h)
     roof = roofline(prob, ms_kernel, tr)
     roof["timing"] = method
+    model = traffic_model(prob, tr)
+    if model is not None:
+        roof["traffic_model"] = model
     if warm and prob.nsets > 1:
         # secondary: the same launch on one buffer set (inputs warm in the 256 MiB Infinity Cache / L2)
         warm_ms, _, _, _ = time_steps(torch, lambda i: prob.step(0), steps, 2)
