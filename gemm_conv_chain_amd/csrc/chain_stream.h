@@ -40,8 +40,10 @@
 // instruction issued through inline assembly, and the kernel waits itself,
 // with exact counts: the group of requests issued at the start of step s
 // (weights and rows for step s + 2) must be complete at the end of step s + 1,
-// when only the next group (and the 8 stores of a pass that ended in
-// between) may still be in flight.  The waits name the row registers as
+// when only the next group may still be in flight.  Loads retire from the
+// counter in issue order but stores need not (a store can complete before an
+// older load), so the count never includes stores: the 8 stores of a pass
+// that ended in between are waited for as well.  The waits name the row registers as
 // outputs, so nothing that reads them is scheduled before the wait.  Buffer
 // instructions also give the masking: offsets past a resource's size read
 // zero and drop stores, so rows past M, k past K0 and columns past N0 / N1
@@ -113,6 +115,8 @@ __device__ __forceinline__ void cs_dma_chunk(const half_t* __restrict__ G, int r
     for (int i = 0; i < CS_DMA_PER_WAVE; ++i) {
         const int rb = r0 + RSTEP * i;             // first row of this instruction's group
         const i32x4 rs = buf_rsrc(G + (long)rb * ld + c0, ((long)(rows - rb) * ld - c0) * 2);
+        if constexpr (kPoison)   // poison first: a read the real DMA has not reached yet sees it
+            dma16(buf_rsrc(&fc_poison_line, sizeof(PoisonLine)), 16u * (unsigned)lane, T + (wave + CS_WAVES * i) * 512);
         dma16(rs, voff, T + (wave + CS_WAVES * i) * 512);
     }
 }
@@ -124,7 +128,7 @@ void k_chain_stream(StreamArgs a)
     constexpr int N0P = 32 * NT0;
     constexpr int KS1 = 2 * NT0;                                     // GEMM1 k-steps
     constexpr int NJ = (N0P + CS_KC1 - 1) / CS_KC1;                  // W1 chunks per pass
-    constexpr int NDMA = CS_DMA_PER_WAVE;
+    constexpr int NDMA = CS_DMA_PER_WAVE * kDmaFactor;   // DMA requests per wave per chunk
     extern __shared__ __align__(16) char smem[];
     typedef FC_LDS float lds_float;
     lds_half* bufs[CS_NBUF];
@@ -244,10 +248,6 @@ void k_chain_stream(StreamArgs a)
         // bufs[0]; issues the group of step c + 2.
         auto step0 = [&](int c, auto SC) {
             constexpr int sc = decltype(SC)::value;
-            if constexpr (kPoison) {   // bufs[2] was released by the last step's barrier
-                lds_poison(bufs[2], CS_BUFH * 2, tid, CS_THREADS);
-                __syncthreads();
-            }
             dma_step(c + 2 < S ? c + 2 : c + 2 - S, bufs[2]);
             const bool pa = c + 2 < nch;
             if (pa) load_a(rsA, c + 2, ring[(sc + 2) % 3]);
@@ -268,10 +268,20 @@ void k_chain_stream(StreamArgs a)
                 acc0[i % NT0] = mfma32x32x16(wf[i % 3], op[i / NT0], acc0[i % NT0]);
             }
             // the group of step c - 1 is complete once at most this step's
-            // group (and, at c == 0, the previous tile's last stores) remain
+            // group remains (at c == 0 of a later tile the previous tile's
+            // last stores are waited for too: a store may complete before an
+            // older load, so only loads issued after the needed ones may stay
+            // in flight.  The first of the two waits there is implied by the
+            // second; without it this branch is scheduled differently and
+            // the NT0 = 8 kernels spill registers.)
             if (c == 0 && !first) {
-                if (pa) vm_wait<NDMA + 4 + 8>();
-                else vm_wait<NDMA + 8>();
+                if (pa) {
+                    vm_wait<NDMA + 4 + 8>();
+                    vm_wait<NDMA + 4>();
+                } else {
+                    vm_wait<NDMA + 8>();
+                    vm_wait<NDMA>();
+                }
             } else {
                 if (pa) vm_wait<NDMA + 4>();
                 else vm_wait<NDMA>();
@@ -332,10 +342,6 @@ void k_chain_stream(StreamArgs a)
 #pragma unroll
             for (int j = 0; j < NJ; ++j) {
                 const int tau = nch + p * NJ + j;
-                if constexpr (kPoison) {
-                    lds_poison(bufs[2], CS_BUFH * 2, tid, CS_THREADS);
-                    __syncthreads();
-                }
                 dma_step(tau + 2 < S ? tau + 2 : tau + 2 - S, bufs[2]);
                 if (p == 0 && j == 0) {
                     // the next tile's first chunks (rows past M read zero)
@@ -357,16 +363,17 @@ void k_chain_stream(StreamArgs a)
                     if (i + 2 < NM) wf[(i + 2) % 3] = wfrag(i + 2);
                     acc1[i % 4] = mfma32x32x16(wf[i % 3], hf[8 * j + i / 4], acc1[i % 4]);
                 }
-                // in flight may remain: this step's group, and the prefetch
-                // (first step) or the previous pass's 8 stores (later passes)
+                // in flight may remain: this step's group and, at the first
+                // step, the next tile's prefetched rows (loads issued after
+                // the group of the previous step; the previous pass's stores
+                // are not counted -- a store may complete before an older
+                // load -- so they are waited for)
                 if (j == 0 && p == 0) {
                     // (with a single GEMM1 step the prefetch is needed at the
                     // very next step: wait for it here)
                     if (S == nch + 1) vm_wait<0>();
                     else if (nch > 1) vm_wait<NDMA + 8>();
                     else vm_wait<NDMA + 4>();
-                } else if (j == 0) {
-                    vm_wait<NDMA + 8>();
                 } else {
                     vm_wait<NDMA>();
                 }
@@ -417,41 +424,6 @@ void k_chain_stream(StreamArgs a)
     vm_wait<0>();
 }
 
-// ----------------------------------------------------------------- launch
-
-template <int NT0, int KCH, int ACT>
-static hipError_t launch_stream_k(const StreamArgs& a, hipStream_t st)
-{
-    const size_t lds = cs_lds_bytes(32 * NT0, a.N1p);
-    static std::atomic<unsigned long long> lds_set{0};
-    hipError_t e = allow_full_lds((const void*)k_chain_stream<NT0, KCH, ACT>, &lds_set);
-    if (e != hipSuccess) return e;
-    long grid = device_cu_count();
-    if (grid > a.ntiles) grid = a.ntiles;
-    hipLaunchKernelGGL((k_chain_stream<NT0, KCH, ACT>), dim3((unsigned)grid), dim3(CS_THREADS), lds, st, a);
-    return hipGetLastError();
-}
-
-template <int NT0, int ACT>
-static hipError_t launch_stream_a(const StreamArgs& a, hipStream_t st)
-{
-    switch ((a.K0 + CS_KC0 - 1) / CS_KC0) {
-    case 1: return launch_stream_k<NT0, 1, ACT>(a, st);
-    case 4: return launch_stream_k<NT0, 4, ACT>(a, st);
-    case 9: return launch_stream_k<NT0, 9, ACT>(a, st);
-    }
-    return launch_stream_k<NT0, 0, ACT>(a, st);
-}
-
-template <int NT0>
-static hipError_t launch_stream_n(const StreamArgs& a, int act, hipStream_t st)
-{
-    if (act == ACT_GELU_TANH) return launch_stream_a<NT0, ACT_GELU_TANH>(a, st);
-    if (act == ACT_HARDSWISH) return launch_stream_a<NT0, ACT_HARDSWISH>(a, st);
-    if (act == ACT_RELU) return launch_stream_a<NT0, ACT_RELU>(a, st);
-    return launch_stream_a<NT0, ACT_NONE>(a, st);
-}
-
 // N0 is padded to 64, 128 or 256 columns (zero weights, zero bias).  The
 // biases must fit in LDS beside the three weight buffers.
 inline bool stream_fits_lds(int N0, int N1)
@@ -463,13 +435,5 @@ inline bool stream_fits_lds(int N0, int N1)
 
 // Instantiated in gemm_stream.hip.
 hipError_t run_stream(const StreamArgs& a, int act, hipStream_t st);
-
-inline hipError_t launch_stream(const StreamArgs& a, int act, hipStream_t st)
-{
-    if (a.N0 <= 64) return launch_stream_n<2>(a, act, st);
-    if (a.N0 <= 128) return launch_stream_n<4>(a, act, st);
-    if (a.N0 <= 256) return launch_stream_n<8>(a, act, st);
-    return hipErrorInvalidValue;
-}
 
 }  // namespace fc

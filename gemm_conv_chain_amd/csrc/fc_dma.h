@@ -38,6 +38,24 @@ __device__ __forceinline__ void dma16(i32x4 rsrc, unsigned voff, const lds_half*
                  : "memory", "m0");
 }
 
+// Poison (debug builds): 1 KiB of the poison pattern in global memory, the
+// source of the poison LDS-DMA requests of the streamed kernels (a DMA fills
+// LDS without the registers an LDS store loop would take).
+struct PoisonLine {
+    unsigned w[256];
+};
+__host__ __device__ constexpr PoisonLine make_poison_line()
+{
+    PoisonLine p{};
+    for (int i = 0; i < 256; ++i) p.w[i] = kPoisonWord;
+    return p;
+}
+static __device__ __align__(16) PoisonLine fc_poison_line = make_poison_line();
+
+// DMA requests per real one: 2 in the poison build (each 1 KiB DMA is
+// preceded by one that writes the poison to the same LDS bytes).
+constexpr int kDmaFactor = kPoison ? 2 : 1;
+
 // 16-byte load into registers (the kernel waits for it with vm_wait).
 // Non-temporal: each row line is read once, by one instruction (quad layout).
 __device__ __forceinline__ void bload16(half8& dst, i32x4 rsrc, unsigned voff)
