@@ -581,11 +581,11 @@ def tune(fc, prob, name):
         prob.config["variant"] = "auto"
     else:
         raise ValueError("--tune applies to the two-GEMM, the conv3x3 -> conv1x1 and the pooled conv workloads")
-    log("%s tuned: %s waves %d (%s)" % (name, best["variant"], best["waves"], ", ".join(
-        "%s/%d %.2f us" % (r["variant"], r["waves"], r["us"]) for r in table)))
-    prob.config.update(tuned={"best": {"variant": best["variant"], "waves": best["waves"]},
-                              "table": [{"variant": r["variant"], "waves": r["waves"], "us": round(r["us"], 2)}
-                                        for r in table]})
+    log("%s tuned: %s waves %d stages %d (%s)" % (name, best["variant"], best["waves"], best["stages"], ", ".join(
+        "%s/%d/%d %.2f us" % (r["variant"], r["waves"], r["stages"], r["us"]) for r in table)))
+    prob.config.update(tuned={"best": {"variant": best["variant"], "waves": best["waves"], "stages": best["stages"]},
+                              "table": [{"variant": r["variant"], "waves": r["waves"], "stages": r["stages"],
+                                         "us": round(r["us"], 2)} for r in table]})
 
 
 def main():

@@ -47,8 +47,11 @@ class ConvShape(ctypes.Structure):
 
 class TuneEntry(ctypes.Structure):
     """One configuration timed by the profiler: kernel form, tile-owning waves
-    per block (0 = the form's own block shape), microseconds per launch."""
-    _fields_ = [("variant", ctypes.c_int32), ("waves", ctypes.c_int32), ("us", ctypes.c_float)]
+    per block (0 = the form's own block shape), pipeline stages of the
+    register-resident row stream (0 = the default 4, or 2), microseconds per
+    launch."""
+    _fields_ = [("variant", ctypes.c_int32), ("waves", ctypes.c_int32), ("stages", ctypes.c_int32),
+                ("us", ctypes.c_float)]
 
 
 _lib = None
@@ -119,7 +122,7 @@ def _load(path):
     L.chain_conv_pool_ex.argtypes = [_vp, _vp, _vp, _vp, ctypes.c_int, ctypes.c_int, _vp,
                                      ctypes.POINTER(ConvShape), _vp, ctypes.c_int, _i32, _vp]
     L.chain_gemm2_ex.argtypes = [_vp, _vp, _vp, ctypes.c_int, _vp, _vp, _vp, _i64, _i32, _i32, _i32,
-                                 ctypes.c_int, _i32, _vp]
+                                 ctypes.c_int, _i32, _i32, _vp]
     L.fc_probe_mfma.argtypes = [_i32, _i32, _vp, _vp, _i32, ctypes.POINTER(_i32), _vp]
     L.fc_probe_read.argtypes = [_vp, _i64, _vp, _i32, ctypes.POINTER(_i32), _vp]
     L.chain_gemm2_tune_ex.argtypes = [_vp, _vp, _vp, ctypes.c_int, _vp, _vp, _vp, _i64, _i32, _i32, _i32, _i32,
@@ -132,7 +135,7 @@ def _load(path):
     L.chain_conv_pool_auto_config.argtypes = [ctypes.POINTER(ConvShape), ctypes.c_int, ctypes.c_int, _i32,
                                               ctypes.POINTER(TuneEntry)]
     L.chain_conv2_ex.argtypes = [_vp, _vp, _vp, ctypes.c_int, _vp, _vp, _i32, _vp, ctypes.POINTER(ConvShape),
-                                 _i32, _vp]
+                                 _i32, _i32, _vp]
     L.chain_conv2_tune.argtypes = [_vp, _vp, _vp, ctypes.c_int, _vp, _vp, _i32, _vp, ctypes.POINTER(ConvShape),
                                    _i32, ctypes.POINTER(TuneEntry), _i32, ctypes.POINTER(_i32),
                                    ctypes.POINTER(TuneEntry), _vp]
@@ -257,18 +260,20 @@ def _gemm2_shapes(A, W0, b0, W1, b1, out):
 
 
 # ------------------------------------------------------------ entry points
-def chain_gemm2(A, W0, b0, W1, b1, act="relu", out=None, variant="auto", waves=None):
+def chain_gemm2(A, W0, b0, W1, b1, act="relu", out=None, variant="auto", waves=None, stages=0):
     """D1 [M, N1] = act(A [M,K0] @ W0 [K0,N0] + b0) @ W1 [N0,N1] + b1 (fp16).
-    ``waves`` (explicit variant only): tile-owning waves per block of the
-    register-resident form (chain_gemm2_ex)."""
+    ``waves`` / ``stages`` (explicit variant only, chain_gemm2_ex): tile-owning
+    waves per block and row-stream pipeline stages (4 or 2; 0 = 4) of the
+    register-resident form."""
     M, K0, N0, N1, out = _gemm2_shapes(A, W0, b0, W1, b1, out)
     v = VARIANT[variant] if isinstance(variant, str) else int(variant)
-    if waves is None:
+    if waves is None and not stages:
         _check("chain_gemm2", lib().chain_gemm2_variant(_ptr(A), _ptr(W0), _ptr(b0), _act(act), _ptr(W1), _ptr(b1),
                                                         _ptr(out), M, K0, N0, N1, v, _stream(A)))
     else:
         _check("chain_gemm2_ex", lib().chain_gemm2_ex(_ptr(A), _ptr(W0), _ptr(b0), _act(act), _ptr(W1), _ptr(b1),
-                                                      _ptr(out), M, K0, N0, N1, v, int(waves), _stream(A)))
+                                                      _ptr(out), M, K0, N0, N1, v, int(waves or 0), int(stages),
+                                                      _stream(A)))
     return out
 
 
@@ -304,11 +309,11 @@ def tune_chain_gemm2_table(A, W0, b0, W1, b1, act="relu", out=None, reps=20):
 
 
 def _entry(e, names):
-    return {"variant": names[e.variant], "waves": int(e.waves), "us": float(e.us)}
+    return {"variant": names[e.variant], "waves": int(e.waves), "stages": int(e.stages), "us": float(e.us)}
 
 
 def auto_config(M, K0, N0, N1, act="relu"):
-    """{variant, waves} that chain_gemm2(variant='auto') runs for this shape."""
+    """{variant, waves, stages} that chain_gemm2(variant='auto') runs for this shape."""
     e = TuneEntry()
     _check("chain_gemm2_auto_config", lib().chain_gemm2_auto_config(int(M), int(K0), int(N0), int(N1), _act(act),
                                                                     ctypes.byref(e)))
@@ -349,7 +354,7 @@ def tune_conv_pool(x, w, b, act="relu", pool="max2x2", scale=None, out=None, arg
 
 
 def conv_auto_config(n, h, w, c, k, act="relu", pool="max2x2", argmax=False):
-    """{variant, waves} that the pooled conv chain runs under variant='auto'."""
+    """{variant, waves, stages} that the pooled conv chain runs under variant='auto' (stages 0)."""
     e = TuneEntry()
     sh = ConvShape(n, h, w, c, k, 3, 3, 1, 1)
     p = POOL[pool] if isinstance(pool, str) else int(pool)
@@ -585,12 +590,13 @@ def _conv2_prep(x, w0, b0, w1, b1, out):
     return sh, k1, out
 
 
-def chain_conv2(x, w0, b0, w1, b1, act="relu", out=None, waves=0):
+def chain_conv2(x, w0, b0, w1, b1, act="relu", out=None, waves=0, stages=0):
     """y = conv1x1(act(conv3x3(x, w0) + b0), w1) + b1; w1 is [k0, k1] or [1,1,k0,k1].
-    ``waves``: tile-owning waves per block (1..8), 0 = the library's choice."""
+    ``waves``: tile-owning waves per block (1..8) and ``stages``: row-stream
+    pipeline stages (4 or 2; 0 = 4), or both 0 for the library's choice."""
     sh, k1, out = _conv2_prep(x, w0, b0, w1, b1, out)
     _check("chain_conv2", lib().chain_conv2_ex(_ptr(x), _ptr(w0), _ptr(b0), _act(act), _ptr(w1), _ptr(b1), k1,
-                                               _ptr(out), ctypes.byref(sh), int(waves), _stream(x)))
+                                               _ptr(out), ctypes.byref(sh), int(waves), int(stages), _stream(x)))
     return out
 
 
@@ -609,7 +615,7 @@ def tune_chain_conv2(x, w0, b0, w1, b1, act="relu", out=None, reps=20):
 
 
 def conv2_auto_config(n, h, w, c, k0, k1, act="relu"):
-    """{variant, waves} that chain_conv2 runs for this shape (waves=0)."""
+    """{variant, waves, stages} that chain_conv2 runs for this shape (waves=0)."""
     e = TuneEntry()
     sh = ConvShape(n, h, w, c, k0, 3, 3, 1, 1)
     _check("chain_conv2_auto_config", lib().chain_conv2_auto_config(ctypes.byref(sh), int(k1), _act(act),

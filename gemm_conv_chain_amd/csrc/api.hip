@@ -20,7 +20,7 @@ hipError_t run_conv_pool3x3(const half_t* x, const half_t* w, const half_t* scal
 bool conv_pool_wr_fits(int W, int C, int K);
 hipError_t run_chain_conv2_3x3(const half_t* x, const half_t* w0, const half_t* b0, int act, const half_t* w1,
                                const half_t* b1, half_t* y, int NB, int H, int W, int C, int K0, int K1, int waves,
-                               hipStream_t st);
+                               int stages, hipStream_t st);
 hipError_t run_chain_convN_3x3(const half_t* x, int nst, const half_t* const* w, const half_t* const* b,
                                const int* act, const int* widths, half_t* y, int NB, int H, int W, int C,
                                hipStream_t st);
@@ -121,8 +121,17 @@ fc_status check_g2_ptrs(const fc_half* A, const fc_half* W0, const fc_half* b0, 
 // kernel form and tile-owning waves per block, cached per device and shape.
 struct Config {
     int variant;
-    int waves;   // 0: the kernel's own block shape
+    int waves;    // 0: the kernel's own block shape
+    int stages;   // register-resident chains: row-chunk ring depth (0: the default 4; 2)
 };
+
+// The register-resident kernels come with a two-stage row ring for 4 or 9
+// chunks of 64 (k = 193..256 or 513..576).
+bool two_stage_ok(int K0)
+{
+    const int c = (K0 + 63) / 64;
+    return c == 4 || c == 9;
+}
 typedef std::vector<int64_t> TuneKey;   // kind, device, shape ...
 std::mutex g_tune_mu;
 std::map<TuneKey, Config> g_tune;
@@ -159,33 +168,41 @@ TuneKey conv_key(const fc_conv_shape* s, int act, int pool, bool argmax)
 
 // Candidates of the two-GEMM chain: the register-resident form with 8, 4, 2
 // or 1 tile-owning waves per block (a block covers 32 * waves rows per
-// round), then the streamed-weight and the LDS-resident forms (fixed block
-// shapes).  The first applicable one is the untuned rule.
-int gemm2_candidates(bool rf_ok, bool stream_ok, Config* out)
+// round), each with the default four-stage row ring and, where the kernels
+// exist (two_stage_ok), a two-stage one; then the streamed-weight and the
+// LDS-resident forms (fixed block shapes).  The first applicable one is the
+// untuned rule.  At most 10.
+int gemm2_candidates(bool rf_ok, bool stream_ok, int K0, Config* out)
 {
     int n = 0;
-    if (rf_ok)
-        for (int w : {8, 4, 2, 1}) out[n++] = Config{fc::VARIANT_RF, w};
-    if (stream_ok) out[n++] = Config{fc::VARIANT_STREAM, 0};
-    out[n++] = Config{fc::VARIANT_LDS, 0};
+    if (rf_ok) {
+        for (int w : {8, 4, 2, 1}) out[n++] = Config{fc::VARIANT_RF, w, 0};
+        if (two_stage_ok(K0))
+            for (int w : {8, 4, 2, 1}) out[n++] = Config{fc::VARIANT_RF, w, 2};
+    }
+    if (stream_ok) out[n++] = Config{fc::VARIANT_STREAM, 0, 0};
+    out[n++] = Config{fc::VARIANT_LDS, 0, 0};
     return n;
 }
 
 // Untuned: the first candidate; for the register-resident form, blocks of
 // the smallest power-of-two number of tile-owning waves that covers the
 // 32-row tiles with one block per CU (small problems then spread over many
-// CUs in small blocks instead of filling a few blocks).
+// CUs in small blocks instead of filling a few blocks), and with 8 waves the
+// two-stage row ring where it is built (measured: 4-9% faster than four
+// stages at 8 waves; fewer waves per block need the deeper ring).
 Config gemm2_config(int64_t M, int32_t K0, int32_t N0, int32_t N1, int act, bool rf_ok, bool stream_ok)
 {
     Config c;
     if (tuned_config(gemm2_key(M, K0, N0, N1, act), &c)) return c;
-    Config cand[8];
-    gemm2_candidates(rf_ok, stream_ok, cand);
+    Config cand[16];
+    gemm2_candidates(rf_ok, stream_ok, K0, cand);
     c = cand[0];
     if (c.variant == fc::VARIANT_RF) {
         const int64_t tiles = (M + 31) / 32, cus = fc::device_cu_count();
         c.waves = 1;
         while (c.waves < 8 && (int64_t)c.waves * cus < tiles) c.waves *= 2;
+        c.stages = c.waves == 8 && two_stage_ok(K0) ? 2 : 0;
     }
     return c;
 }
@@ -196,23 +213,28 @@ TuneKey conv2_key(const fc_conv_shape* s, int k1, int act)
 }
 
 // Candidates of the conv3x3 -> conv1x1 chain (register-resident form): 8, 4,
-// 2 or 1 tile-owning waves per block.
-int conv2_candidates(Config* out)
+// 2 or 1 tile-owning waves per block, each with the four-stage and (where it
+// exists) the two-stage row ring.
+int conv2_candidates(const fc_conv_shape* s, Config* out)
 {
     int n = 0;
-    for (int w : {8, 4, 2, 1}) out[n++] = Config{fc::VARIANT_RF, w};
+    for (int w : {8, 4, 2, 1}) out[n++] = Config{fc::VARIANT_RF, w, 0};
+    if (two_stage_ok(9 * s->c))
+        for (int w : {8, 4, 2, 1}) out[n++] = Config{fc::VARIANT_RF, w, 2};
     return n;
 }
 
 // Untuned: as for the two-GEMM chain, the smallest power-of-two number of
-// tile-owning waves whose blocks, one per CU, cover the 32-pixel tiles.
+// tile-owning waves whose blocks, one per CU, cover the 32-pixel tiles (with
+// 8 waves, the two-stage row ring where it is built).
 Config conv2_config(const fc_conv_shape* s, int k1, int act)
 {
     Config c;
     if (tuned_config(conv2_key(s, k1, act), &c)) return c;
     const int64_t tiles = ((int64_t)s->n * s->h * s->w + 31) / 32, cus = fc::device_cu_count();
-    c = Config{fc::VARIANT_RF, 1};
+    c = Config{fc::VARIANT_RF, 1, 0};
     while (c.waves < 8 && (int64_t)c.waves * cus < tiles) c.waves *= 2;
+    c.stages = c.waves == 8 && two_stage_ok(9 * s->c) ? 2 : 0;
     return c;
 }
 
@@ -224,7 +246,7 @@ int conv_candidates(bool lds_ok, bool reg_ok, Config* out)
     int n = 0;
     if (reg_ok) out[n++] = Config{FC_CONV_REG_WEIGHTS, 0};
     if (lds_ok)
-        for (int w : {8, 4}) out[n++] = Config{FC_CONV_LDS_WEIGHTS, w};
+        for (int w : {8, 4}) out[n++] = Config{FC_CONV_LDS_WEIGHTS, w, 0};
     return n;
 }
 
@@ -271,7 +293,7 @@ fc_status profile(const char* name, F&& launch, const Config* cand, int n, int r
         float us = -1.0f;
         e = time_launches([&]() { return launch(cand[i]); }, reps, st, t0, t1, &us);
         if (e != hipSuccess) break;
-        if (table && i < capacity) table[i] = fc_tune_entry{cand[i].variant, cand[i].waves, us};
+        if (table && i < capacity) table[i] = fc_tune_entry{cand[i].variant, cand[i].waves, cand[i].stages, us};
         if (ib < 0 || us < tb) {
             ib = i;
             tb = us;
@@ -282,7 +304,7 @@ fc_status profile(const char* name, F&& launch, const Config* cand, int n, int r
     if (e != hipSuccess) return hip_status(e, name);
     store_config(key, dev, cand[ib]);
     if (count) *count = n;
-    if (best) *best = fc_tune_entry{cand[ib].variant, cand[ib].waves, tb};
+    if (best) *best = fc_tune_entry{cand[ib].variant, cand[ib].waves, cand[ib].stages, tb};
     // the last launch is not the winner's: run the winner once more, so the
     // output holds what the cached configuration computes
     return hip_status(launch(cand[ib]), name);
@@ -321,7 +343,7 @@ fc_status chain_gemm2_variant(const fc_half* A, const fc_half* W0, const fc_half
     s = check_g2_shape(M, K0, N0, N1, act, &rf_ok, &stream_ok);
     if (s != FC_OK) return s;
     if ((int)variant < 0 || (int)variant > 3) return fail(FC_E_ARG, "variant %d out of range", (int)variant);
-    Config c{(int)variant, 0};
+    Config c{(int)variant, 0, 0};
     if (c.variant == FC_VARIANT_RF && !rf_ok)
         return fail(FC_E_UNSUPPORTED, "register-resident variant needs N0<=128 and W0,W1 within LDS");
     if (c.variant == FC_VARIANT_STREAM && !stream_ok)
@@ -329,13 +351,13 @@ fc_status chain_gemm2_variant(const fc_half* A, const fc_half* W0, const fc_half
     if (M == 0) return ok();
     if (c.variant == FC_VARIANT_AUTO) c = gemm2_config(M, K0, N0, N1, (int)act, rf_ok, stream_ok);
     return hip_status(fc::run_chain_gemm2(H(A), H(W0), H(b0), act, H(W1), H(b1), Hm(D1), M, K0, N0, N1, c.variant,
-                                          c.waves, (hipStream_t)stream),
+                                          c.waves, c.stages, (hipStream_t)stream),
                       "chain_gemm2");
 }
 
 fc_status chain_gemm2_ex(const fc_half* A, const fc_half* W0, const fc_half* b0, fc_act act, const fc_half* W1,
                          const fc_half* b1, fc_half* D1, int64_t M, int32_t K0, int32_t N0, int32_t N1,
-                         fc_variant variant, int32_t waves, void* stream)
+                         fc_variant variant, int32_t waves, int32_t stages, void* stream)
 {
     bool rf_ok = false, stream_ok = false;
     if (M < 0 || K0 <= 0 || N0 <= 0 || N1 <= 0) return fail(FC_E_SHAPE, "M>=0 and K0, N0, N1 > 0 required");
@@ -346,13 +368,17 @@ fc_status chain_gemm2_ex(const fc_half* A, const fc_half* W0, const fc_half* b0,
     if ((int)variant < 1 || (int)variant > 3) return fail(FC_E_ARG, "variant %d: RF, LDS or STREAM", (int)variant);
     if (variant == FC_VARIANT_RF ? (waves < 0 || waves > 8) : waves != 0)
         return fail(FC_E_ARG, "waves=%d: 0..8 for the register-resident form, 0 otherwise", (int)waves);
+    if (variant == FC_VARIANT_RF ? (stages != 0 && stages != 2 && stages != 4) : stages != 0)
+        return fail(FC_E_ARG, "stages=%d: 0 (= 4), 4 or 2 for the register-resident form, 0 otherwise", (int)stages);
+    if (stages == 2 && !two_stage_ok(K0))
+        return fail(FC_E_UNSUPPORTED, "the two-stage row ring is built for K0 in 193..256 or 513..576");
     if (variant == FC_VARIANT_RF && !rf_ok)
         return fail(FC_E_UNSUPPORTED, "register-resident variant needs N0<=128 and W0,W1 within LDS");
     if (variant == FC_VARIANT_STREAM && !stream_ok)
         return fail(FC_E_UNSUPPORTED, "streamed variant needs N1<=16128 (biases beside the weight buffers)");
     if (M == 0) return ok();
     return hip_status(fc::run_chain_gemm2(H(A), H(W0), H(b0), act, H(W1), H(b1), Hm(D1), M, K0, N0, N1, (int)variant,
-                                          waves, (hipStream_t)stream),
+                                          waves, stages == 4 ? 0 : stages, (hipStream_t)stream),
                       "chain_gemm2_ex");
 }
 
@@ -370,12 +396,12 @@ fc_status chain_gemm2_tune_ex(const fc_half* A, const fc_half* W0, const fc_half
     if (M == 0) return fail(FC_E_SHAPE, "M == 0: nothing to time");
     if (reps < 1 || reps > 1000) return fail(FC_E_SHAPE, "reps=%d outside 1..1000", (int)reps);
     if (capacity < 0 || (capacity > 0 && !table)) return fail(FC_E_NULL, "table is required for capacity > 0");
-    Config cand[8];
-    const int n = gemm2_candidates(rf_ok, stream_ok, cand);
+    Config cand[16];
+    const int n = gemm2_candidates(rf_ok, stream_ok, K0, cand);
     hipStream_t st = (hipStream_t)stream;
     auto launch = [&](const Config& c) {
         return fc::run_chain_gemm2(H(A), H(W0), H(b0), act, H(W1), H(b1), Hm(D1), M, K0, N0, N1, c.variant, c.waves,
-                                   st);
+                                   c.stages, st);
     };
     return profile("chain_gemm2_tune", launch, cand, n, reps, gemm2_key(M, K0, N0, N1, (int)act), table, capacity,
                    count, best, st);
@@ -385,9 +411,9 @@ fc_status chain_gemm2_tune(const fc_half* A, const fc_half* W0, const fc_half* b
                            const fc_half* b1, fc_half* D1, int64_t M, int32_t K0, int32_t N0, int32_t N1,
                            int32_t reps, fc_variant* best, float* us, void* stream)
 {
-    fc_tune_entry table[8], b{};
+    fc_tune_entry table[16], b{};
     int32_t n = 0;
-    fc_status s = chain_gemm2_tune_ex(A, W0, b0, act, W1, b1, D1, M, K0, N0, N1, reps, table, 8, &n, &b, stream);
+    fc_status s = chain_gemm2_tune_ex(A, W0, b0, act, W1, b1, D1, M, K0, N0, N1, reps, table, 16, &n, &b, stream);
     if (s != FC_OK) return s;
     if (best) *best = (fc_variant)b.variant;
     if (us) {
@@ -419,7 +445,7 @@ fc_status chain_gemm2_auto_config(int64_t M, int32_t K0, int32_t N0, int32_t N1,
     Config c;
     const bool t = tuned_config(gemm2_key(M, K0, N0, N1, (int)act), &c);
     if (!t) c = gemm2_config(M, K0, N0, N1, (int)act, rf_ok, stream_ok);
-    *out = fc_tune_entry{c.variant, c.waves, -1.0f};
+    *out = fc_tune_entry{c.variant, c.waves, c.stages, -1.0f};
     return ok();
 }
 
@@ -580,7 +606,7 @@ fc_status chain_conv_pool_auto_config(const fc_conv_shape* shape, fc_act act, fc
     const bool reg_ok = fc::conv_pool_wr_fits(shape->w, shape->c, shape->k);
     if (!lds_ok && !reg_ok) return fail(FC_E_UNSUPPORTED, "weights exceed LDS");
     const Config c = conv_config(shape, (int)act, (int)pool, with_argmax != 0, lds_ok, reg_ok);
-    *out = fc_tune_entry{c.variant, c.waves, -1.0f};
+    *out = fc_tune_entry{c.variant, c.waves, c.stages, -1.0f};
     return ok();
 }
 
@@ -633,22 +659,29 @@ static fc_status check_conv2(const fc_half* x, const fc_half* w0, const fc_half*
 
 fc_status chain_conv2_ex(const fc_half* x, const fc_half* w0, const fc_half* b0, fc_act act, const fc_half* w1,
                          const fc_half* b1, int32_t k1, fc_half* y, const fc_conv_shape* shape0, int32_t waves,
-                         void* stream)
+                         int32_t stages, void* stream)
 {
     if (waves < 0 || waves > 8) return fail(FC_E_ARG, "waves=%d: 1..8, or 0 for the library's choice", (int)waves);
+    if (stages != 0 && stages != 2 && stages != 4)
+        return fail(FC_E_ARG, "stages=%d: 4 or 2, or 0 for the library's choice", (int)stages);
+    if (waves == 0 && stages != 0) return fail(FC_E_ARG, "stages needs an explicit waves");
     fc_status s = check_conv2(x, w0, b0, act, w1, b1, k1, y, shape0);
     if (s != FC_OK) return s;
+    if (stages == 2 && !two_stage_ok(9 * shape0->c))
+        return fail(FC_E_UNSUPPORTED, "the two-stage row ring is built for 9c in 193..256 or 513..576");
     if ((long)shape0->n * shape0->h * shape0->w == 0) return ok();
-    const int wv = waves > 0 ? waves : conv2_config(shape0, k1, (int)act).waves;
+    const Config c = waves > 0 ? Config{fc::VARIANT_RF, waves, stages == 4 ? 0 : stages}
+                               : conv2_config(shape0, k1, (int)act);
     return hip_status(fc::run_chain_conv2_3x3(H(x), H(w0), H(b0), act, H(w1), H(b1), Hm(y), shape0->n, shape0->h,
-                                              shape0->w, shape0->c, shape0->k, k1, wv, (hipStream_t)stream),
+                                              shape0->w, shape0->c, shape0->k, k1, c.waves, c.stages,
+                                              (hipStream_t)stream),
                       "chain_conv2");
 }
 
 fc_status chain_conv2(const fc_half* x, const fc_half* w0, const fc_half* b0, fc_act act, const fc_half* w1,
                       const fc_half* b1, int32_t k1, fc_half* y, const fc_conv_shape* shape0, void* stream)
 {
-    return chain_conv2_ex(x, w0, b0, act, w1, b1, k1, y, shape0, 0, stream);
+    return chain_conv2_ex(x, w0, b0, act, w1, b1, k1, y, shape0, 0, 0, stream);
 }
 
 fc_status chain_conv2_auto_config(const fc_conv_shape* shape0, int32_t k1, fc_act act, fc_tune_entry* out)
@@ -660,7 +693,7 @@ fc_status chain_conv2_auto_config(const fc_conv_shape* shape0, int32_t k1, fc_ac
     s = check_conv(shape0, 128);
     if (s != FC_OK) return s;
     const Config c = conv2_config(shape0, k1, (int)act);
-    *out = fc_tune_entry{c.variant, c.waves, -1.0f};
+    *out = fc_tune_entry{c.variant, c.waves, c.stages, -1.0f};
     return ok();
 }
 
@@ -673,12 +706,12 @@ fc_status chain_conv2_tune(const fc_half* x, const fc_half* w0, const fc_half* b
     if ((long)shape0->n * shape0->h * shape0->w == 0) return fail(FC_E_SHAPE, "empty output: nothing to time");
     if (reps < 1 || reps > 1000) return fail(FC_E_SHAPE, "reps=%d outside 1..1000", (int)reps);
     if (capacity < 0 || (capacity > 0 && !table)) return fail(FC_E_NULL, "table is required for capacity > 0");
-    Config cand[8];
-    const int n = conv2_candidates(cand);
+    Config cand[16];
+    const int n = conv2_candidates(shape0, cand);
     hipStream_t st = (hipStream_t)stream;
     auto launch = [&](const Config& c) {
         return fc::run_chain_conv2_3x3(H(x), H(w0), H(b0), act, H(w1), H(b1), Hm(y), shape0->n, shape0->h, shape0->w,
-                                       shape0->c, shape0->k, k1, c.waves, st);
+                                       shape0->c, shape0->k, k1, c.waves, c.stages, st);
     };
     return profile("chain_conv2_tune", launch, cand, n, reps, conv2_key(shape0, k1, (int)act), table, capacity, count,
                    best, st);

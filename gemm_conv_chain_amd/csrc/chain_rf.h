@@ -49,6 +49,7 @@ struct RfArgs {
     int act;
     long ntiles;        // ceil(M / 32)
     long tiles_per_block;
+    int stages;         // row chunks in flight + 1 (ring depth): 0 = the default (4), or 2
     int wpb;            // waves per block that own row tiles (1..RF_WAVES; 0 = all): the block
                         // covers 32 * wpb rows per round, the other waves only stage the weights
     // N-stage chains only (kernel template NMID > 0): NMID middle GEMMs run
@@ -99,8 +100,9 @@ __host__ __device__ inline size_t rf_lds_bytes_n(int N0P, int K0p, int N1p, int 
 // One block per CU (its LDS holds both weight matrices), 8 waves: 2 waves per
 // SIMD.  Saying so lets the scheduler spend registers on loads in flight
 // instead of shrinking them for an occupancy the LDS use rules out.
-// NMID: middle GEMMs of an N-stage chain (0 for two GEMMs).
-template <int NT0, int KCH, class Loader, int NMID = 0>
+// NMID: middle GEMMs of an N-stage chain (0 for two GEMMs).  RD: ring depth
+// (pipeline stages) of the row chunks, 0 = the default.
+template <int NT0, int KCH, class Loader, int NMID = 0, int RD = 0>
 __global__ __launch_bounds__(RF_THREADS) __attribute__((amdgpu_waves_per_eu(1, 2)))
 void k_chain_rf(Loader ld, RfArgs a)
 {
@@ -151,7 +153,7 @@ void k_chain_rf(Loader ld, RfArgs a)
     // the prologue is slower: the extra requests delay the weight loads every
     // wave waits for.)  KCH == 0 (runtime chunk count) falls back to a two-set
     // ring.
-    constexpr int R = KCH >= 4 ? 4 : (KCH > 0 ? KCH : 2);
+    constexpr int R = (KCH > 0 && RD > 0) ? (RD < KCH ? RD : KCH) : (KCH >= 4 ? 4 : (KCH > 0 ? KCH : 2));
     constexpr int PD = R - 1;
     const int wpb = a.wpb > 0 ? a.wpb : RF_WAVES;
     long tile = wave < wpb ? t_begin + wave : t_end;
@@ -491,12 +493,12 @@ struct DenseRowsQ {
 
 // ----------------------------------------------------------------- launch
 
-template <int NT0, int KCH, class Loader, int NMID = 0>
+template <int NT0, int KCH, class Loader, int NMID = 0, int RD = 0>
 static hipError_t launch_rf_k(const Loader& ld, RfArgs a, hipStream_t st)
 {
     const size_t lds = NMID ? rf_lds_bytes_n(32 * NT0, a.K0p, a.N1p, NMID, a.Nmp) : rf_lds_bytes(32 * NT0, a.K0p, a.N1p);
     static std::atomic<unsigned long long> lds_set{0};
-    hipError_t e = allow_full_lds((const void*)k_chain_rf<NT0, KCH, Loader, NMID>, &lds_set);
+    hipError_t e = allow_full_lds((const void*)k_chain_rf<NT0, KCH, Loader, NMID, RD>, &lds_set);
     if (e != hipSuccess) return e;
     const long per_block_min = a.wpb > 0 ? a.wpb : RF_WAVES;  // at least one tile per tile-owning wave
     long grid = device_cu_count();
@@ -504,14 +506,23 @@ static hipError_t launch_rf_k(const Loader& ld, RfArgs a, hipStream_t st)
     if (grid < 1) grid = 1;
     a.tiles_per_block = (a.ntiles + grid - 1) / grid;
     grid = (a.ntiles + a.tiles_per_block - 1) / a.tiles_per_block;
-    hipLaunchKernelGGL((k_chain_rf<NT0, KCH, Loader, NMID>), dim3((unsigned)grid), dim3(RF_THREADS), lds, st, ld, a);
+    hipLaunchKernelGGL((k_chain_rf<NT0, KCH, Loader, NMID, RD>), dim3((unsigned)grid), dim3(RF_THREADS), lds, st, ld,
+                       a);
     return hipGetLastError();
 }
 
-// Compile-time chunk counts for the k lengths in use (64, 256, 576).
+// Compile-time chunk counts for the k lengths in use (64, 256, 576); the
+// two-GEMM chains with 4 or 9 chunks also come with a two-stage row ring
+// (a.stages == 2: one chunk in flight instead of three).
 template <int NT0, class Loader, int NMID = 0>
 static hipError_t launch_rf_t(const Loader& ld, const RfArgs& a, hipStream_t st)
 {
+    if constexpr (NMID == 0) {
+        if (a.stages == 2) {
+            if ((a.K0p >> 6) == 4) return launch_rf_k<NT0, 4, Loader, 0, 2>(ld, a, st);
+            if ((a.K0p >> 6) == 9) return launch_rf_k<NT0, 9, Loader, 0, 2>(ld, a, st);
+        }
+    }
     switch (a.K0p >> 6) {
     case 1: return launch_rf_k<NT0, 1, Loader, NMID>(ld, a, st);
     case 4: return launch_rf_k<NT0, 4, Loader, NMID>(ld, a, st);

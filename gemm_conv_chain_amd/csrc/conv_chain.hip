@@ -722,7 +722,7 @@ hipError_t run_conv_pool3x3(const half_t* x, const half_t* w, const half_t* scal
 
 hipError_t run_chain_conv2_3x3(const half_t* x, const half_t* w0, const half_t* b0, int act, const half_t* w1,
                                const half_t* b1, half_t* y, int NB, int H, int W, int C, int K0, int K1, int waves,
-                               hipStream_t st)
+                               int stages, hipStream_t st)
 {
     const long M = (long)NB * H * W;
     if (M == 0) return hipSuccess;
@@ -735,6 +735,7 @@ hipError_t run_chain_conv2_3x3(const half_t* x, const half_t* w0, const half_t* 
     a.ntiles = (M + 31) / 32;
     a.tiles_per_block = 0;
     a.wpb = waves;
+    a.stages = stages;
     Conv3x3Rows ld;
     ld.x = x; ld.H = H; ld.W = W; ld.C = C; ld.M = M;
     ld.set_divisors();

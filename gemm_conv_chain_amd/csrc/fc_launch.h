@@ -35,10 +35,11 @@ bool gemmn_fits(int nst, const int* widths);
 hipError_t run_chain_gemmN(const half_t* A, int nst, const half_t* const* W, const half_t* const* b, const int* act,
                            const int* widths, half_t* D, long M, hipStream_t st);
 
-// waves: tile-owning waves per block of the register-resident variant (0 = all)
+// waves: tile-owning waves per block of the register-resident variant (0 = all);
+// stages: its row-chunk ring depth (0 = the default 4, or 2)
 hipError_t run_chain_gemm2(const half_t* A, const half_t* W0, const half_t* b0, int act, const half_t* W1,
                            const half_t* b1, half_t* D1, long M, int K0, int N0, int N1, int variant, int waves,
-                           hipStream_t st);
+                           int stages, hipStream_t st);
 hipError_t run_gemm_bias_act(const half_t* A, const half_t* W, const half_t* b, int act, half_t* C, long M,
                              int K, int N, hipStream_t st);
 

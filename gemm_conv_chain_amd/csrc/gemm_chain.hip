@@ -412,7 +412,7 @@ static hipError_t launch_lds_t(const LdsArgs& a, hipStream_t st)
 
 hipError_t run_chain_gemm2(const half_t* A, const half_t* W0, const half_t* b0, int act, const half_t* W1,
                            const half_t* b1, half_t* D1, long M, int K0, int N0, int N1, int variant, int waves,
-                           hipStream_t st)
+                           int stages, hipStream_t st)
 {
     if (M == 0) return hipSuccess;
     if (variant == VARIANT_RF) {
@@ -425,6 +425,7 @@ hipError_t run_chain_gemm2(const half_t* A, const half_t* W0, const half_t* b0, 
         a.ntiles = (M + 31) / 32;
         a.tiles_per_block = 0;
         a.wpb = waves;
+        a.stages = stages;
         return run_rf_dense(A, a, 0, st);
     }
     if (variant == VARIANT_STREAM) {

@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define FC_ABI_VERSION 2
+#define FC_ABI_VERSION 3
 
 typedef uint16_t fc_half;
 
@@ -132,11 +132,13 @@ fc_status chain_gemm2_variant(const fc_half *A, const fc_half *W0, const fc_half
                               fc_variant variant, void *stream);
 /* chain_gemm2_ex -- one explicit configuration, as the profiler times it:
  * variant (not AUTO) and, for FC_VARIANT_RF, waves = tile-owning waves per
- * block, 1..8 (0 = 8); other variants take waves == 0.  FC_E_ARG otherwise. */
+ * block, 1..8 (0 = 8), and stages = row-chunk ring depth, 4 (or 0) or 2 (2
+ * is built for K0 in 193..256 and 513..576, else FC_E_UNSUPPORTED); other
+ * variants take waves == 0 and stages == 0.  FC_E_ARG otherwise. */
 fc_status chain_gemm2_ex(const fc_half *A, const fc_half *W0, const fc_half *b0, fc_act act,
                          const fc_half *W1, const fc_half *b1, fc_half *D1,
                          int64_t M, int32_t K0, int32_t N0, int32_t N1,
-                         fc_variant variant, int32_t waves, void *stream);
+                         fc_variant variant, int32_t waves, int32_t stages, void *stream);
 
 /*
  * chain_gemm2_tune -- hardware profiling of the fused-chain variants for one
@@ -168,18 +170,23 @@ fc_status chain_gemm2_tune(const fc_half *A, const fc_half *W0, const fc_half *b
  * the GEMM chains, fc_conv_variant for the conv chains), the number of waves
  * per block that own row tiles (0: the form's own block shape; the
  * register-resident GEMM chain takes 8, 4, 2 or 1 -- a block then covers
- * 32 * waves rows per round -- and the LDS-weights conv 8 or 4), and the
- * mean microseconds per launch (-1 where nothing was timed). */
+ * 32 * waves rows per round -- and the LDS-weights conv 8 or 4), the
+ * pipeline stages of the register-resident chains' row stream (0: the
+ * default ring of 4 chunks, three in flight; 2: two chunks, one in flight;
+ * the BOLT profiler's "stages" parameter), and the mean microseconds per
+ * launch (-1 where nothing was timed). */
 typedef struct {
     int32_t variant;
     int32_t waves;
+    int32_t stages;
     float us;
 } fc_tune_entry;
 
 /*
  * chain_gemm2_tune_ex -- as chain_gemm2_tune, over every configuration the
  * library can run for the shape (each residence form; the register-resident
- * one with 8, 4, 2 and 1 tile-owning waves per block).  table (host, may be
+ * one with 8, 4, 2 and 1 tile-owning waves per block, each with 4 and, where
+ * built, 2 pipeline stages: at most 10 configurations).  table (host, may be
  * NULL when capacity == 0) receives min(count, capacity) rows in the order
  * timed; count (host, may be NULL) the number of configurations timed; best
  * (host, may be NULL) the fastest, which is cached for the shape and runs
@@ -195,8 +202,8 @@ fc_status chain_gemm2_tune_ex(const fc_half *A, const fc_half *W0, const fc_half
 /* The configuration FC_VARIANT_AUTO runs for this shape on the current
  * device (us = -1): the tuned one, else the static rule -- register-resident
  * when it applies, with the smallest power-of-two number of tile-owning waves
- * (1..8) that covers ceil(M / 32) row tiles with one block per CU; else
- * STREAM; else LDS.  Host only. */
+ * (1..8) that covers ceil(M / 32) row tiles with one block per CU (with 8
+ * waves, 2 pipeline stages where built); else STREAM; else LDS.  Host only. */
 fc_status chain_gemm2_auto_config(int64_t M, int32_t K0, int32_t N0, int32_t N1, fc_act act, fc_tune_entry *out);
 
 /* The variant FC_VARIANT_AUTO runs for this shape on the current device:
@@ -315,12 +322,14 @@ fc_status chain_conv2(const fc_half *x, const fc_half *w0, const fc_half *b0, fc
 
 /* chain_conv2_ex -- chain_conv2 with the block shape chosen by the caller:
  * waves = tile-owning waves per block (1..8; a block's round covers 32 * waves
- * pixels) or 0 for the library's choice (the profiled one if
- * chain_conv2_tune ran for this shape, else the smallest power of two whose
- * blocks, one per CU, cover the 32-pixel tiles).  Other waves -> FC_E_ARG. */
+ * pixels) and stages = row-chunk ring depth (4, or 2 where built: 9c in
+ * 193..256 or 513..576, else FC_E_UNSUPPORTED; 0 = 4), or waves = stages = 0
+ * for the library's choice (the profiled one if chain_conv2_tune ran for this
+ * shape, else the smallest power of two whose blocks, one per CU, cover the
+ * 32-pixel tiles, with 4 stages).  Other values -> FC_E_ARG. */
 fc_status chain_conv2_ex(const fc_half *x, const fc_half *w0, const fc_half *b0, fc_act act, const fc_half *w1,
                          const fc_half *b1, int32_t k1, fc_half *y, const fc_conv_shape *shape0, int32_t waves,
-                         void *stream);
+                         int32_t stages, void *stream);
 
 /* The configuration chain_conv2 runs for this shape on the current device
  * (variant FC_VARIANT_RF, waves; us = -1): the tuned one, else the rule of
@@ -330,7 +339,7 @@ fc_status chain_conv2_auto_config(const fc_conv_shape *shape0, int32_t k1, fc_ac
 /* chain_conv2_tune -- the profiler of chain_conv2 (BOLT notes, "Light-weight
  * performance profiler"): times reps launches (1..1000, after one untimed
  * launch) of each block shape (8, 4, 2, 1 tile-owning waves; variant
- * FC_VARIANT_RF) on this input, writes up to capacity rows of table
+ * FC_VARIANT_RF) with 4 and, where built, 2 pipeline stages on this input, writes up to capacity rows of table
  * (us = mean microseconds per launch), *count = candidates timed, *best = the
  * fastest, and caches it for (device, shape, k1, act): chain_conv2 and
  * chain_conv2_ex(waves = 0) then run it.  y is written (by the winner last).

@@ -45,7 +45,7 @@ def test_poison_build_exports_the_same_abi(L):
 
 
 def test_version_and_status_strings(L):
-    assert fc.abi_version() == 2
+    assert fc.abi_version() == 3
     for code, name in enumerate(["FC_OK", "FC_E_NULL", "FC_E_SHAPE", "FC_E_ALIGN", "FC_E_UNSUPPORTED", "FC_E_HIP",
                                  "FC_E_ARG"]):
         assert L.fc_status_str(code).decode() == name
@@ -182,18 +182,24 @@ def test_tuner_validation(L):
     assert ct(P, P, NUL, NUL, 1, 1, P2, ctypes.byref(sh), NUL, 5, None, 4, ctypes.byref(n), ctypes.byref(b), None) == E_NULL
     # explicit configurations
     gx = L.chain_gemm2_ex
-    assert gx(P, P, NUL, 1, P, NUL, P2, 512, 64, 64, 64, 1, 9, None) == E_ARG
-    assert gx(P, P, NUL, 1, P, NUL, P2, 512, 64, 64, 64, 0, 0, None) == E_ARG   # AUTO is not a configuration
-    assert gx(P, P, NUL, 1, P, NUL, P2, 512, 64, 64, 64, 2, 4, None) == E_ARG   # LDS form takes waves == 0
-    assert gx(P, P, NUL, 1, P, NUL, P2, 0, 64, 64, 64, 1, 2, None) == OK
+    assert gx(P, P, NUL, 1, P, NUL, P2, 512, 64, 64, 64, 1, 9, 0, None) == E_ARG
+    assert gx(P, P, NUL, 1, P, NUL, P2, 512, 64, 64, 64, 0, 0, 0, None) == E_ARG   # AUTO is not a configuration
+    assert gx(P, P, NUL, 1, P, NUL, P2, 512, 64, 64, 64, 2, 4, 0, None) == E_ARG   # LDS form takes waves == 0
+    assert gx(P, P, NUL, 1, P, NUL, P2, 0, 64, 64, 64, 1, 2, 0, None) == OK
+    # pipeline stages of the register-resident form: 4 (= 0) or 2, 2 built for 4 or 9 chunks of K0
+    assert gx(P, P, NUL, 1, P, NUL, P2, 0, 256, 64, 64, 1, 2, 2, None) == OK
+    assert gx(P, P, NUL, 1, P, NUL, P2, 0, 576, 64, 64, 1, 2, 4, None) == OK
+    assert gx(P, P, NUL, 1, P, NUL, P2, 512, 64, 64, 64, 1, 2, 2, None) == E_UNSUP
+    assert gx(P, P, NUL, 1, P, NUL, P2, 512, 256, 64, 64, 1, 2, 3, None) == E_ARG
+    assert gx(P, P, NUL, 1, P, NUL, P2, 512, 256, 64, 64, 2, 0, 2, None) == E_ARG   # LDS form takes stages == 0
     # the untuned rule, queried without a GPU
     fc.tune_clear()
-    assert fc.auto_config(65536, 256, 64, 128) == {"variant": "rf", "waves": 8}
-    assert fc.auto_config(512, 64, 64, 64) == {"variant": "rf", "waves": 1}       # 16 row tiles: 16 one-wave blocks
-    assert fc.auto_config(20000, 256, 64, 128) == {"variant": "rf", "waves": 4}
-    assert fc.auto_config(65536, 576, 256, 256, "gelu_tanh") == {"variant": "stream", "waves": 0}
-    assert fc.conv_auto_config(32, 112, 112, 64, 128) == {"variant": "reg_weights", "waves": 0}
-    assert fc.conv_auto_config(2, 8, 8, 32, 64) == {"variant": "lds_weights", "waves": 8}
+    assert fc.auto_config(65536, 256, 64, 128) == {"variant": "rf", "waves": 8, "stages": 2}   # two-stage ring at 8 waves
+    assert fc.auto_config(512, 64, 64, 64) == {"variant": "rf", "waves": 1, "stages": 0}   # 16 one-wave blocks
+    assert fc.auto_config(20000, 256, 64, 128) == {"variant": "rf", "waves": 4, "stages": 0}
+    assert fc.auto_config(65536, 576, 256, 256, "gelu_tanh") == {"variant": "stream", "waves": 0, "stages": 0}
+    assert fc.conv_auto_config(32, 112, 112, 64, 128) == {"variant": "reg_weights", "waves": 0, "stages": 0}
+    assert fc.conv_auto_config(2, 8, 8, 32, 64) == {"variant": "lds_weights", "waves": 8, "stages": 0}
 
 
 def test_empty_tensors_may_be_null(L):
@@ -380,11 +386,15 @@ def test_conv2_waves_and_tuner_validation(L):
     import ctypes as C
     sh0 = shape(k=64)
     ex = L.chain_conv2_ex
-    assert ex(P, P, NUL, 1, P, NUL, 64, P2, C.byref(shape(n=0, k=64)), 0, None) == OK
-    assert ex(P, P, NUL, 1, P, NUL, 64, P2, C.byref(shape(n=0, k=64)), 4, None) == OK
-    assert ex(P, P, NUL, 1, P, NUL, 64, P2, C.byref(sh0), 9, None) == E_ARG
-    assert ex(P, P, NUL, 1, P, NUL, 64, P2, C.byref(sh0), -1, None) == E_ARG
-    assert ex(P, P, NUL, 1, P, NUL, 60, P2, C.byref(sh0), 0, None) == E_SHAPE
+    assert ex(P, P, NUL, 1, P, NUL, 64, P2, C.byref(shape(n=0, k=64)), 0, 0, None) == OK
+    assert ex(P, P, NUL, 1, P, NUL, 64, P2, C.byref(shape(n=0, k=64)), 4, 0, None) == OK
+    assert ex(P, P, NUL, 1, P, NUL, 64, P2, C.byref(shape(n=0, k=64)), 4, 2, None) == OK      # 9 chunks of 64
+    assert ex(P, P, NUL, 1, P, NUL, 64, P2, C.byref(sh0), 9, 0, None) == E_ARG
+    assert ex(P, P, NUL, 1, P, NUL, 64, P2, C.byref(sh0), -1, 0, None) == E_ARG
+    assert ex(P, P, NUL, 1, P, NUL, 64, P2, C.byref(sh0), 4, 3, None) == E_ARG
+    assert ex(P, P, NUL, 1, P, NUL, 64, P2, C.byref(sh0), 0, 2, None) == E_ARG               # stages need waves
+    assert ex(P, P, NUL, 1, P, NUL, 64, P2, C.byref(shape(c=32, k=64)), 4, 2, None) == E_UNSUP  # 9c = 288
+    assert ex(P, P, NUL, 1, P, NUL, 60, P2, C.byref(sh0), 0, 0, None) == E_SHAPE
     tab = (fc.TuneEntry * 4)()
     n = C.c_int32(0)
     best = fc.TuneEntry()

@@ -68,15 +68,20 @@ def test_tune_gemm2_table(fc, M, K0, N0, N1, act):
     print(best, table, flush=True)
     ref = gemm_ref(d, act)
     assert_close(to_np(out), ref, "tuned output")
-    cfgs = {(r["variant"], r["waves"]) for r in table}
+    cfgs = {(r["variant"], r["waves"], r["stages"]) for r in table}
     assert all(r["us"] > 0 for r in table)
     if N0 <= 128:
-        # M_t / waves per block: four values of the register-resident form
-        assert {("rf", w) for w in (1, 2, 4, 8)} <= cfgs
-    assert ("lds", 0) in cfgs and ("stream", 0) in cfgs     # the residence forms
+        # M_t / waves per block: four values of the register-resident form,
+        # and for 4 or 9 chunks of K0 two pipeline depths of each
+        assert {("rf", w, 0) for w in (1, 2, 4, 8)} <= cfgs
+        if (K0 + 63) // 64 in (4, 9):
+            assert {("rf", w, 2) for w in (1, 2, 4, 8)} <= cfgs
+    assert ("lds", 0, 0) in cfgs and ("stream", 0, 0) in cfgs     # the residence forms
     fastest = min(table, key=lambda r: r["us"])
-    assert (best["variant"], best["waves"]) == (fastest["variant"], fastest["waves"])
-    assert fc.auto_config(M, K0, N0, N1, act) == {"variant": best["variant"], "waves": best["waves"]}
+    key = lambda r: (r["variant"], r["waves"], r["stages"])
+    assert key(best) == key(fastest)
+    assert fc.auto_config(M, K0, N0, N1, act) == {"variant": best["variant"], "waves": best["waves"],
+                                                  "stages": best["stages"]}
     assert_close(to_np(fc.chain_gemm2(A, W0, b0, W1, b1, act=act)), ref, "auto after tuning")
     fc.tune_clear()
     assert fc.auto_config(M, K0, N0, N1, act)["variant"] == ("rf" if N0 <= 128 else "stream")
@@ -102,7 +107,8 @@ def test_tune_conv_pool(fc, pool):
     assert all(r["us"] > 0 for r in table)
     fastest = min(table, key=lambda r: r["us"])
     assert (best["variant"], best["waves"]) == (fastest["variant"], fastest["waves"])
-    assert fc.conv_auto_config(3, 30, 34, 64, 128, pool=pool) == {"variant": best["variant"], "waves": best["waves"]}
+    assert fc.conv_auto_config(3, 30, 34, 64, 128, pool=pool) == {"variant": best["variant"], "waves": best["waves"],
+                                                                  "stages": 0}
     if pool == "max2x2":
         yo, _, _, _ = oracle.chain_conv_pool(d["x"], d["w"], d["b"], oracle.ACT_RELU)
     else:
@@ -112,20 +118,35 @@ def test_tune_conv_pool(fc, pool):
     # an argmax output selects another kernel: untuned, it keeps the rule
     assert fc.conv_auto_config(3, 30, 34, 64, 128, pool=pool, argmax=True)["variant"] == "reg_weights"
     fc.tune_clear()
-    assert fc.conv_auto_config(3, 30, 34, 64, 128, pool=pool) == {"variant": "reg_weights", "waves": 0}
+    assert fc.conv_auto_config(3, 30, 34, 64, 128, pool=pool) == {"variant": "reg_weights", "waves": 0, "stages": 0}
 
 
 @pytest.mark.parametrize("waves", [1, 2, 4, 8])
 @pytest.mark.parametrize("n,h,w,c,k0,k1", [(2, 33, 35, 64, 64, 256), (1, 7, 9, 32, 96, 40)])
 def test_conv2_waves(fc, n, h, w, c, k0, k1, waves):
-    # every block shape the profiler may choose computes the chain (several
-    # rounds per block and a ragged last tile in the first shape)
+    # every block shape and pipeline depth the profiler may choose computes the
+    # chain (several rounds per block and a ragged last tile in the first shape)
     d = inputs.conv2_inputs(n, h, w, c, k0, k1, seed=h + waves)
-    print("case conv2 waves", waves, n, h, w, c, k0, k1, flush=True)
-    y = to_np(fc.chain_conv2(dev(d["x"]), dev(d["w0"]), dev(d["b0"]), dev(d["w1"]), dev(d["b1"]), act="relu",
-                             waves=waves))
     ref, _ = oracle.chain_conv2(d["x"], d["w0"], d["b0"], oracle.ACT_RELU, d["w1"], d["b1"])
-    assert_close(y, ref, "conv2 waves=%d" % waves)
+    for stages in ((4, 2) if c == 64 else (4,)):
+        print("case conv2 waves", waves, "stages", stages, n, h, w, c, k0, k1, flush=True)
+        y = to_np(fc.chain_conv2(dev(d["x"]), dev(d["w0"]), dev(d["b0"]), dev(d["w1"]), dev(d["b1"]), act="relu",
+                                 waves=waves, stages=stages))
+        assert_close(y, ref, "conv2 waves=%d stages=%d" % (waves, stages))
+
+
+@pytest.mark.parametrize("waves", [1, 8])
+@pytest.mark.parametrize("M,K0,N0,N1", [(1000, 256, 64, 128), (70001, 256, 64, 128), (3000, 576, 64, 64)])
+def test_gemm2_rf_two_stages(fc, M, K0, N0, N1, waves):
+    # the two-stage row ring (one chunk in flight) of the register-resident form;
+    # the same k order as the four-stage ring, so the two agree bit for bit
+    d = inputs.gemm2_inputs(M, K0, N0, N1, "uniform", seed=M + 3 * waves)
+    A, W0, b0, W1, b1 = (dev(d[k]) for k in ("A", "W0", "b0", "W1", "b1"))
+    print("case rf two stages", M, K0, N0, N1, waves, flush=True)
+    y2 = to_np(fc.chain_gemm2(A, W0, b0, W1, b1, act="relu", variant="rf", waves=waves, stages=2))
+    y4 = to_np(fc.chain_gemm2(A, W0, b0, W1, b1, act="relu", variant="rf", waves=waves, stages=4))
+    assert np.array_equal(y2.view(np.uint16), y4.view(np.uint16))
+    assert_close(y2, gemm_ref(d, "relu"), "rf stages=2 waves=%d" % waves)
 
 
 def test_tune_conv2(fc):
@@ -138,11 +159,13 @@ def test_tune_conv2(fc):
     best, table, out = fc.tune_chain_conv2(*args, reps=3)
     torch.cuda.synchronize()
     print(best, table, flush=True)
-    assert sorted(r["waves"] for r in table) == [1, 2, 4, 8]
+    # block shapes (8, 4, 2, 1 waves) x pipeline stages (4, 2)
+    assert sorted((r["waves"], r["stages"]) for r in table) == [(w, s) for w in (1, 2, 4, 8) for s in (0, 2)]
     assert all(r["variant"] == "rf" and r["us"] > 0 for r in table)
     fastest = min(table, key=lambda r: r["us"])
-    assert best["waves"] == fastest["waves"]
-    assert fc.conv2_auto_config(4, 28, 28, 64, 64, 256) == {"variant": "rf", "waves": best["waves"]}
+    assert (best["waves"], best["stages"]) == (fastest["waves"], fastest["stages"])
+    assert fc.conv2_auto_config(4, 28, 28, 64, 64, 256) == {"variant": "rf", "waves": best["waves"],
+                                                             "stages": best["stages"]}
     ref, _ = oracle.chain_conv2(d["x"], d["w0"], d["b0"], oracle.ACT_RELU, d["w1"], d["b1"])
     assert_close(to_np(out), ref, "tuned conv2 output")
     assert_close(to_np(fc.chain_conv2(*args)), ref, "conv2 auto after tuning")
