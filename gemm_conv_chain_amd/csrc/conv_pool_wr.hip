@@ -11,27 +11,34 @@
 //
 // Mapping to CDNA4 (gfx950), for C = 64 input channels and 65..128 output
 // channels (the x[32,112,112,60->64] -> 128 workload):
-//   * Block = 4 waves (256 threads), one block per CU, one wave per SIMD.
-//     Wave (kh, wc) computes output columns [64 wc, 64 wc + 64) over input
-//     channels [32 kh, 32 kh + 32) of every tap: the reduction is split in two
-//     (split-K), so that each wave holds its share of the HWIO weights ONCE,
-//     as ready MFMA operand-B fragments, in 144 registers (9 taps x 2 k-steps
-//     x 2 column tiles x 4); the main loop reads no weights.  The weights
-//     arrive through LDS in 128-row pieces (natural layout, read with the
-//     transposing LDS load).
+//   * Block = 8 waves (512 threads), one block per CU: two groups of four
+//     waves, one wave of each group per SIMD.  Wave q of a group computes
+//     output columns [32 q, 32 q + 32) over the whole reduction (9 taps x 64
+//     channels): it holds its 576 x 32 slice of the HWIO weights ONCE, as
+//     ready MFMA operand-B fragments, in 144 registers (36 k-steps x 4); the
+//     main loop reads no weights and the waves never exchange partial sums.
+//     The weights arrive through LDS in 128-row pieces (natural layout, read
+//     with the transposing LDS load).
 //   * GEMM rows are ordered window-major: a 32-row MFMA tile ("row tile") is
 //     8 consecutive 2x2 pool windows of one pooled row (window 2g + h of the
 //     tile lands in lane half h, accumulator registers 4g..4g+3), so the pool
 //     is three max (or a sum) per output in registers.  A row tile needs a
 //     4-row x 18-column input halo (stored with a row stride of 20 pixels).
-//   * A block tile is up to 4 consecutive row tiles (128 pixels).  Its input
-//     halo goes straight from global memory into LDS by the LDS-DMA load
-//     (buffer_load_dwordx4 ... lds), into two buffers: the next tile's halo is
-//     requested while the current tile's 18 k-steps run on the matrix cores.
-//     Pixels outside the image, and the two padding columns, read zero from
-//     outside the buffer resource -- the conv's zero padding needs no branch.
+//   * A tile is 2 consecutive row tiles (64 pixels); the block's tiles
+//     alternate between the two groups.  The groups run in ping-pong: in each
+//     phase one group runs a tile's 72 MFMAs per wave and nothing else, while
+//     the other group (the second wave of every SIMD) stores, runs its
+//     previous tile's epilogue and requests a later tile's halo; one barrier
+//     per phase.  Each SIMD's matrix pipe is then fed by one wave at a time
+//     while the other wave's non-matrix work hides under it (two waves that
+//     both run all phases tend to reach their non-matrix phases together).
+//   * A tile's input halo goes straight from global memory into LDS by the
+//     LDS-DMA load (buffer_load_dwordx4 ... lds), into a ring of four
+//     buffers, three phases ahead of its MFMAs.  Pixels outside the image,
+//     and the two padding columns, read zero from outside the buffer resource
+//     -- the conv's zero padding needs no branch.
 //   * Operand A is read from the halo with ds_read_b128 in MFMA layout.  A
-//     pixel's 32 channels of one half are four 16-byte slots; slot s of the
+//     pixel's channel half (32 channels) is four 16-byte slots; slot s of the
 //     pixel in halo row hr, column hc is stored at s ^ wr_swz(hr, hc) with
 //     wr_swz = (hr & 1) | ((hc >> 2) & 1) << 1.  The LDS (64 banks) serves 16
 //     lanes of a 16-byte read per clock: such a group reads pixels of two
@@ -41,19 +48,18 @@
 //     different 16-byte bank groups for every tap.  The DMA picks, for every
 //     LDS slot, the global 16 bytes that belong there (quads of lanes still
 //     read one 64-byte segment: the fast address path).
-//   * Per k-step a wave issues NRT ds_read_b128 and 2 NRT MFMAs (32x32x16
-//     f16, fp32 accumulate); the next k-step's operands are read while the
-//     current MFMAs run.
-//   * After a tile, the two waves of a column half exchange partial sums
-//     through LDS: wave kh finishes row tiles 2kh and 2kh + 1 (adds the
-//     partner's partial of those rows) and hands the other two over.
+//   * Per k-step a wave issues 2 ds_read_b128 and 2 MFMAs (32x32x16 f16,
+//     fp32 accumulate), with no address arithmetic; the operands are read two
+//     k-steps ahead.
 //   * Work split: the row tiles of the whole problem are divided into equal
 //     contiguous ranges, one per block (49 row tiles each at the workload
-//     above), processed four at a time; a range's last tile may hold 1..3
-//     row tiles (those MFMAs are skipped, not masked).
-//   * Epilogue per row tile: pool (or average), scale/bias, activation, fp16;
-//     the pooled values go through a 1 KiB per-wave LDS staging area and leave
-//     as 16-byte stores of whole 128-byte channel runs.
+//     above); a range's last tile may hold 1 row tile (those MFMAs are
+//     skipped, not masked).
+//   * Epilogue per row tile: pool (or average), scale/bias, activation, fp16,
+//     into the group's LDS staging area [2 row tiles][8 windows][128
+//     columns] (two per group, alternate tiles); two phases later every
+//     thread of the group stores one 16-byte piece, so every pooled pixel
+//     leaves as whole 128-byte lines.
 #include "fc_dma.h"
 #include "fc_launch.h"
 
@@ -61,23 +67,25 @@ namespace fc {
 
 namespace {
 
-constexpr int WR_THREADS = 256;
-constexpr int WR_NRT = 2;                           // row tiles per block tile
+constexpr int WR_THREADS = 512;                     // two groups of 4 waves
+constexpr int WR_NRT = 2;                           // row tiles per tile
+constexpr int WR_NBUF = 4;                          // halo ring depth (tiles)
 constexpr int WR_HROW = 20;                         // halo row stride (pixels): 18 used + 2 padding
 constexpr int WR_HPIX = 4 * WR_HROW;                // pixels per row-tile halo
 constexpr int WR_SLOTS = 4 * WR_HPIX;               // 16-byte slots per row-tile halo (32 channels)
 constexpr int WR_PART_BYTES = 16 * WR_SLOTS;        // 5 KiB: one row tile, one channel half
-constexpr int WR_DMA_PER_PART = WR_SLOTS / 64;      // 1 KiB DMA instructions per part
+constexpr int WR_DMA_PER_PART = WR_SLOTS / 64;      // 1 KiB DMA instructions per part (one part per wave)
 constexpr int WR_BUF_BYTES = 2 * WR_NRT * WR_PART_BYTES;   // one tile's halo (2 row tiles x 2 halves)
-constexpr int WR_RED_BYTES = 8192;                  // per-wave partial sums handed over (1 row tile x 2 column tiles)
-constexpr int WR_STAGE = 1024;                      // per-wave output staging
-constexpr int WR_RED_OFF = 2 * WR_BUF_BYTES;
-constexpr int WR_STAGE_OFF = WR_RED_OFF + 4 * WR_RED_BYTES;
-constexpr int WR_BIAS_OFF = WR_STAGE_OFF + 4 * WR_STAGE;
-constexpr int WR_LDS = WR_BIAS_OFF + 2 * 128 * 4;    // 77 KiB: two blocks per CU
+constexpr int WR_STAGE_BYTES = WR_NRT * 8 * 128 * 2;       // one tile's pooled outputs [row tile][window][128]
+constexpr int WR_STAGE_OFF = WR_NBUF * WR_BUF_BYTES;
+constexpr int WR_BIAS_OFF = WR_STAGE_OFF + 4 * WR_STAGE_BYTES;   // two staging areas per group
+constexpr int WR_LDS = WR_BIAS_OFF + 2 * 128 * 4;    // 97 KiB: one block per CU
 constexpr int WR_WPIECE = 128;                      // weight rows staged through LDS at a time
+constexpr int WR_APD = 2;                           // A-operand prefetch distance (k-steps)
 static_assert(WR_SLOTS % 64 == 0, "whole DMA instructions per part");
-static_assert(2 * WR_LDS <= 160 * 1024, "two blocks per CU");
+static_assert(4 * WR_NRT == WR_THREADS / 64, "one halo part per wave of a group");
+static_assert(2 * WR_STAGE_BYTES == 16 * WR_THREADS, "one 16-byte output piece per thread of a group");
+static_assert(WR_LDS <= 160 * 1024, "one block per CU");
 
 enum { WR_MAX = 0, WR_AVG = 1 };
 
@@ -108,16 +116,16 @@ void k_conv_pool_wr(WrArgs a)
 {
     constexpr int C = 64;
     constexpr int KPB = 128;                 // block columns (padded)
+    constexpr int NST = 9 * C / 16;          // k-steps of 16
     extern __shared__ __align__(16) char smem[];
     typedef FC_LDS char lds_char;
     typedef FC_LDS half8 lds_half8;
-    typedef FC_LDS floatx4 lds_floatx4;
     typedef Act<ACT> act;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wc = wave & 1, kh = wave >> 1;
     const int lr = lane & 31, hh = lane >> 5;
+    const int wq = wave & 3, wg = wave >> 2;   // column quarter, group (owner of the tiles j with j % 2 == wg)
 
     // ---- this block's row tiles (block indices renumbered so that each XCD
     // works on one contiguous stretch: neighbouring ranges share halo rows,
@@ -127,15 +135,15 @@ void k_conv_pool_wr(WrArgs a)
     const long rt_end = (lb + 1) * a.nrt / a.nblocks;
 
     // ---- weights -> operand-B fragments in registers, through LDS in pieces.
-    // wf[st][ct], st = 2 tap + q: HWIO rows k = 64 tap + 32 kh + 16 q + 8 hh +
-    // [0, 8), column 64 wc + 32 ct + lr.
-    half8 wf[18][2];
+    // wf[st]: HWIO rows k = 16 st + 8 hh + [0, 8), column 32 wave + lr.
+    half8 wf[NST];
     {
         WTile Wn;
         Wn.p = (lds_half*)smem;
         Wn.ld = wtile_ld(KPB);
         Wn.swz = wtile_swz(KPB);
         static_assert(WR_WPIECE * KPB * 2 <= WR_LDS, "a weight piece fits the LDS of the block");
+        static_assert(WR_WPIECE % 16 == 0, "whole k-steps per piece");
 #pragma unroll
         for (int pc = 0; pc < (9 * C + WR_WPIECE - 1) / WR_WPIECE; ++pc) {
             const int r0 = pc * WR_WPIECE;
@@ -147,16 +155,9 @@ void k_conv_pool_wr(WrArgs a)
             stage_natural<8>(a.w + (long)r0 * a.K, 9 * C - r0, a.K, a.K, WR_WPIECE, KPB, Wn, tid, WR_THREADS);
             __syncthreads();
 #pragma unroll
-            for (int st = 0; st < 18; ++st) {
-                const int krow0 = 64 * (st >> 1) + 16 * (st & 1);   // + 32 kh (runtime, wave-uniform)
-                if (krow0 + 32 < r0 || krow0 >= r0 + WR_WPIECE) continue;
-                const int kr = krow0 + 32 * kh - r0;
-                if (kr < 0 || kr >= WR_WPIECE) continue;
-#pragma unroll
-                for (int ct = 0; ct < 2; ++ct)
-                    wf[st][ct] = frag_tr_at(Wn.p + frag_lane_off(Wn, 64 * wc + 32 * ct, lane) + (kr + 8 * hh) * Wn.ld,
-                                            4 * Wn.ld);
-            }
+            for (int st = r0 / 16; st < NST && st < (r0 + WR_WPIECE) / 16; ++st)
+                wf[st] = frag_tr_at(Wn.p + frag_lane_off(Wn, 32 * wq, lane) + (16 * st - r0 + 8 * hh) * Wn.ld,
+                                    4 * Wn.ld);
         }
         __syncthreads();   // LDS is reused for the halos
     }
@@ -165,7 +166,7 @@ void k_conv_pool_wr(WrArgs a)
         __syncthreads();
     }
     lds_char* const lds = (lds_char*)smem;
-    lds_half* const ost = (lds_half*)(lds + WR_STAGE_OFF + wave * WR_STAGE);
+    lds_half* const stage = (lds_half*)(lds + WR_STAGE_OFF);
     // bias and scale per column (fp32) in LDS, read by the epilogue (held in
     // registers they would push the main loop past 256 registers)
     typedef FC_LDS float lds_float;
@@ -174,7 +175,6 @@ void k_conv_pool_wr(WrArgs a)
         bsl[i] = (a.b && i < a.K) ? (float)a.b[i] : 0.0f;
         bsl[KPB + i] = (a.s && i < a.K) ? (float)a.s[i] : 1.0f;
     }
-    __syncthreads();
 
     // ---- row tile -> (n, pooled row i, column block jb)
     struct RT {
@@ -189,143 +189,157 @@ void k_conv_pool_wr(WrArgs a)
         r.n = (int)n;
         return r;
     };
+    // tiles of this block: tile j covers row tiles [rt_begin + WR_NRT j, + tile_nrt(j))
+    const int ntiles = (int)((rt_end - rt_begin + WR_NRT - 1) / WR_NRT);
+    auto tile_nrt = [&](int j) -> int { return (int)min((long)WR_NRT, rt_end - rt_begin - (long)WR_NRT * j); };
 
     // ---- halo DMA.  Wave w fetches part w of a tile: row tile u = w / 2,
     // channel half c = w % 2 (5 instructions).  Lane L of instruction j fills
     // slot 64 j + L of the part: pixel p = slot / 4 of the halo (row p / 20,
-    // column p % 20), global 16-byte chunk (slot % 4) ^ ((p >> 1) & 3) of
-    // channels [32 c, 32 c + 32).  Halos inside the image use the precomputed
-    // per-lane offsets rel[j] (OUTSIDE for the two padding columns); halos
-    // that cross the border take per-lane checks.
+    // column p % 20), global 16-byte chunk (slot % 4) ^ wr_swz of channels
+    // [32 c, 32 c + 32).  The offsets from the halo origin are the same for
+    // every tile; pixels outside the image (the conv's zero padding) are
+    // masked to an offset outside the buffer resource, which reads zero.
+    // Returns whether this wave issued the requests (a tile of one row tile
+    // has no part for waves 2 and 3).
     const int W = a.W;
-    auto dma_tile = [&](long rt, int nrt, lds_char* buf) {
-        const int u = kh;   // row tile of this wave's part; channel half wc
-        if (u >= nrt) return;
-        const RT t = decode(rt + u);
-        const int ih0 = 2 * t.i - 1, iw0 = 16 * t.jb - 1;   // halo origin in the image
-        const bool inside = ih0 >= 0 && ih0 + 4 <= a.H && iw0 >= 0 && iw0 + 18 <= W;
-        const int ib = inside ? ih0 : (ih0 < 0 ? 0 : ih0);
-        const long base_pix = ((long)t.n * a.H + ib) * W + (inside ? iw0 : 0);
-        const long total_pix = (long)a.NB * a.H * W;
-        const i32x4 rs = buf_rsrc(a.x + base_pix * C, (total_pix - base_pix) * (long)(2 * C));
-        lds_char* const dst = buf + wave * WR_PART_BYTES;
-        // lane-derived values come from a lane id computed here: derived from
-        // `lane` they are hoisted out of the tile loop and held across it
-        const int ln = lane_id_here();
-        if (inside) {
+    // per-lane offsets from the halo origin (OUTSIDE for the two padding
+    // columns), formed once: lane L of instruction i fills slot 64 i + L
+    unsigned dma_off[WR_DMA_PER_PART];
 #pragma unroll
-            for (int j = 0; j < WR_DMA_PER_PART; ++j) {
-                const int slot = 64 * j + ln;
-                const int p = slot >> 2, part = slot & 3;
-                const int hr = p / WR_HROW, hcl = p - hr * WR_HROW;
-                const int g = part ^ wr_swz(hr, hcl);
-                const unsigned off =
-                    hcl < 18 ? (unsigned)(hr * W + hcl) * (unsigned)(2 * C) + (unsigned)(64 * wc + 16 * g) : CS_OUTSIDE;
-                dma16(rs, off, (const lds_half*)(dst + j * 1024));
-            }
-        } else {
-#pragma unroll
-            for (int j = 0; j < WR_DMA_PER_PART; ++j) {
-                const int slot = 64 * j + ln;
-                const int p = slot >> 2, part = slot & 3;
-                const int hr = p / WR_HROW, hcl = p - hr * WR_HROW;
-                const int ih = ih0 + hr, iw = iw0 + hcl;
-                const bool ok = hcl < 18 && ih >= 0 && ih < a.H && iw >= 0 && iw < W;
-                const int g = part ^ wr_swz(hr, hcl);
-                const unsigned off =
-                    ok ? (unsigned)((ih - ib) * W + iw) * (unsigned)(2 * C) + (unsigned)(64 * wc + 16 * g) : CS_OUTSIDE;
-                dma16(rs, off, (const lds_half*)(dst + j * 1024));
-            }
+    for (int i = 0; i < WR_DMA_PER_PART; ++i) {
+        const int slot = 64 * i + lane;
+        const int p = slot >> 2, part = slot & 3;
+        const int hr = p / WR_HROW, hcl = p - hr * WR_HROW;
+        const int g = part ^ wr_swz(hr, hcl);
+        dma_off[i] = hcl < 18 ? (unsigned)(hr * W + hcl) * (unsigned)(2 * C) + (unsigned)(64 * (wq & 1) + 16 * g)
+                              : CS_OUTSIDE;
+    }
+    const long total_pix = (long)a.NB * a.H * W;
+    auto dma_tile = [&](int j) -> bool {
+        const int u = wq >> 1;
+        if (j >= ntiles || u >= tile_nrt(j)) return false;
+        lds_char* const dst = lds + (j % WR_NBUF) * WR_BUF_BYTES + wq * WR_PART_BYTES;
+        if constexpr (kPoison) {   // released by the barrier of the tile before
+            lds_poison(dst, WR_PART_BYTES, lane, 64);
+            wave_lds_sync();
         }
+        const RT t = decode(rt_begin + (long)WR_NRT * j + u);
+        const int ih0 = 2 * t.i - 1, iw0 = 16 * t.jb - 1;   // halo origin in the image
+        // the origin's pixel index (one row / column before the image at its
+        // top / left border: those pixels are masked below and never read)
+        const long base_pix = ((long)t.n * a.H + ih0) * W + iw0;
+        const i32x4 rs = buf_rsrc((const void*)((long)a.x + base_pix * (2 * C)), (total_pix - base_pix) * (long)(2 * C));
+        // pixels of the halo inside the image, as a bit mask over the 80
+        // halo pixels (bit 20 hr + hc; scalar work): rows [rlo, rhi), columns
+        // [clo, chi)
+        const int rlo = ih0 < 0 ? -ih0 : 0, rhi = min(4, a.H - ih0);
+        const int clo = iw0 < 0 ? -iw0 : 0, chi = min(18, W - iw0);
+        const unsigned long long cm = ((1ull << chi) - 1) & ~((1ull << clo) - 1);
+        unsigned long long m_lo = 0;   // pixels 0..63
+        unsigned m_hi = 0;             // pixels 64..79
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            if (r >= rlo && r < rhi) {
+                m_lo |= cm << (20 * r);
+                if (r == 3) m_hi = (unsigned)(cm >> 4);
+            }
+        const int quad = lane_id_here() >> 2;   // pixel of the lane within the instruction's 16
+#pragma unroll
+        for (int i = 0; i < WR_DMA_PER_PART; ++i) {
+            const unsigned win = i < 4 ? (unsigned)(m_lo >> (16 * i)) & 0xffffu : m_hi;   // pixels 16 i .. 16 i + 15
+            const unsigned off = (win >> quad) & 1u ? dma_off[i] : CS_OUTSIDE;
+            dma16(rs, off, (const lds_half*)(dst + i * 1024));
+        }
+        return true;
     };
 
-    // ---- A-operand offset in a part: lane l reads, for MFMA row m = l % 32
-    // (window w = m / 4, dy = (m / 2) % 2, dx = m % 2) and k-group l / 32, tap
-    // (r, s), k-step half q, slot 2q + l / 32 of halo pixel (row dy + r,
-    // column 2w + dx + s).
-    auto a_off = [&](int tap, int q) -> int {
-        const int ln = lane_id_here();   // recomputed per k-step, not held across the loop
-        const int m = ln & 31;
-        const int r = tap / 3, s = tap % 3;
-        const int hr = ((m >> 1) & 1) + r, hc = 2 * (m >> 2) + (m & 1) + s;
-        return (hr * WR_HROW + hc) * 64 + (((2 * q + (ln >> 5)) ^ wr_swz(hr, hc)) << 4);
-    };
+    floatx16 acc[2];
 
-    floatx16 acc[WR_NRT][2];
-#pragma unroll
-    for (int u = 0; u < WR_NRT; ++u)
-#pragma unroll
-        for (int ct = 0; ct < 2; ++ct) acc[u][ct] = zero16();
-
-    // One tile: 9 taps x 2 k-steps over this wave's channel half, NRT row
-    // tiles; the operands of k-step st + 1 are read before the MFMAs of st.
+    // One tile: 36 k-steps over all 576 k, NRT row tiles (the first k-step
+    // starts the accumulators from zero); the operands of k-step st + WR_APD
+    // are read before the MFMAs of st.  Operand A: lane l
+    // reads, for MFMA row m = l % 32 (window w = m / 4, dy = (m / 2) % 2,
+    // dx = m % 2) and k-group l / 32, tap (r, s), k-step q of the tap
+    // (channels 16 q + 8 (l / 32) + [0, 8)), slot 2 (q % 2) + l / 32 of halo
+    // pixel (row dy + r, column 2w + dx + s) in the part of channel half
+    // q / 2.  The lane's address depends on the tap only through r % 2 and s
+    // (the swizzle) plus a constant, so the 12 lane addresses are formed once
+    // per tile and each read takes its constant as the instruction's offset.
     auto compute = [&](auto nrt_c, const lds_char* buf) {
         constexpr int NRT = decltype(nrt_c)::value;
-        const lds_char* hb = buf + kh * WR_PART_BYTES;
-        half8 af[2][NRT];
+        constexpr int R = WR_APD + 1;
+        const int ln = lane_id_here();
+        const int m = ln & 31, hi = ln >> 5;
+        const int dy = (m >> 1) & 1, dx = m & 1, w4 = m >> 2;
+        const lds_char* const lb = buf + (dy * WR_HROW + 2 * w4 + dx) * 64;
+        const lds_char* ap[2][3][2];
+#pragma unroll
+        for (int rp = 0; rp < 2; ++rp)
+#pragma unroll
+            for (int sc = 0; sc < 3; ++sc)
+#pragma unroll
+                for (int qo = 0; qo < 2; ++qo)
+                    ap[rp][sc][qo] = lb + (((hi | 2 * qo) ^ wr_swz(dy + rp, 2 * w4 + dx + sc)) << 4);
+        half8 af[R][NRT];
         auto load_a = [&](int st, half8 (&dst)[NRT]) {
-            const int off = a_off(st >> 1, st & 1);
+            const int tap = st >> 2, q = st & 3, r = tap / 3, sc = tap % 3;
+            const lds_char* const p = ap[r & 1][sc][q & 1] + (q >> 1) * WR_PART_BYTES + (r * WR_HROW + sc) * 64;
 #pragma unroll
-            for (int u = 0; u < NRT; ++u)
-                dst[u] = *reinterpret_cast<const lds_half8*>(hb + 2 * u * WR_PART_BYTES + off);
+            for (int u = 0; u < NRT; ++u) dst[u] = *reinterpret_cast<const lds_half8*>(p + 2 * u * WR_PART_BYTES);
         };
-        load_a(0, af[0]);
 #pragma unroll
-        for (int st = 0; st < 18; ++st) {   // st = 2 tap + q
-            if (st + 1 < 18) load_a(st + 1, af[(st + 1) & 1]);
+        for (int st = 0; st < WR_APD; ++st) load_a(st, af[st]);
 #pragma unroll
-            for (int u = 0; u < NRT; ++u)
+        for (int st = 0; st < NST; ++st) {
+            if (st + WR_APD < NST) load_a(st + WR_APD, af[(st + WR_APD) % R]);
+            __builtin_amdgcn_sched_barrier(0);   // keep the prefetch issued here
 #pragma unroll
-                for (int ct = 0; ct < 2; ++ct) acc[u][ct] = mfma32x32x16(af[st & 1][u], wf[st][ct], acc[u][ct]);
+            for (int u = 0; u < NRT; ++u) acc[u] = mfma32x32x16(af[st % R][u], wf[st], st == 0 ? zero16() : acc[u]);
         }
     };
 
-    // ---- partial sums: wave (kh, wc) hands row tile 1 - kh to wave
-    // (1 - kh, wc) through its area [ct][r / 4][lane] (float4).  (Row tiles
-    // are named at compile time: a runtime index would move the accumulator
-    // array to scratch memory.)
-    lds_floatx4* const red_out = (lds_floatx4*)(lds + WR_RED_OFF + wave * WR_RED_BYTES);
-    const lds_floatx4* const red_in = (const lds_floatx4*)(lds + WR_RED_OFF + (wave ^ 2) * WR_RED_BYTES);
-    auto hand_over = [&](const floatx16 (&ac)[2]) {
+    // ---- epilogue of tile j, window by window: registers 4g..4g+3 of row
+    // tile u hold window 2g + hh of column 32 wave + lr; pool, scale/bias,
+    // act, fp16 into the staging area [u][window][128] of this tile's parity
+    auto epilogue_sc = [&](auto scaled_c, int j, int nloc) {
+        constexpr bool scaled = decltype(scaled_c)::value;   // false: every scale is 1
+        const int col = 32 * wq + lr;
+        const float bk = bsl[col], sk = bsl[KPB + col];
+        lds_half* const sg = stage + (2 * wg + ((j >> 1) & 1)) * (WR_STAGE_BYTES / 2);
+        if constexpr (kPoison) {   // this wave's columns of the area, released two barriers ago
 #pragma unroll
-        for (int ct = 0; ct < 2; ++ct)
-#pragma unroll
-            for (int r4 = 0; r4 < 4; ++r4) {
-                floatx4 v;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) v[e] = ac[ct][4 * r4 + e];
-                red_out[(ct * 4 + r4) * 64 + lane] = v;
-            }
-    };
-
-    // ---- epilogue of one row tile, window by window: registers 4g..4g+3 of
-    // column tile ct hold window 2g + hh; the partner's four values of that
-    // window are added just before the window is pooled; then scale/bias,
-    // act, fp16, staged and stored
-    auto epilogue = [&](long rt, const floatx16 (&ac)[2]) {
-        const RT t = decode(rt);
-        const int K = a.K;
-        const long win0 = ((long)t.n * a.P2 + t.i) * a.Q2 + 8 * t.jb;   // y index of the tile's first window
-        const int nw = min(8, a.Q2 - 8 * t.jb);                          // valid windows
+            for (int i = 0; i < WR_NRT * 8; ++i) sg[i * 128 + col] = (half_t)65504.0f;
+        }
         // with a non-decreasing activation and no argmax, pool the accumulators first
         constexpr bool fast = EPI == WR_MAX && act::monotone && !AM;
 #pragma unroll
-        for (int ct = 0; ct < 2; ++ct) {
-            const int col = 64 * wc + 32 * ct + lr;
-            const float bk = bsl[col], sk = bsl[KPB + col];
+        for (int u = 0; u < 2; ++u) {
+            if (u >= nloc) break;
+            const int ut = u;
+            long win0 = 0;
+            int nw = 0;
+            if constexpr (AM) {
+                const RT t = decode(rt_begin + (long)WR_NRT * j + ut);
+                win0 = ((long)t.n * a.P2 + t.i) * a.Q2 + 8 * t.jb;
+                nw = min(8, a.Q2 - 8 * t.jb);
+            }
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
-                floatx4 c = red_in[(ct * 4 + g) * 64 + lane];
+                floatx4 c;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) c[e] += ac[ct][4 * g + e];
+                for (int e = 0; e < 4; ++e) c[e] = acc[u][4 * g + e];
                 half_t best;
                 if (fast) {
                     // fp16(act(fma(acc, s, b))) is monotone in acc (non-decreasing
                     // for s >= 0, non-increasing for s < 0): pool the accumulators
                     // first, then one scale/bias/act/convert per window
-                    const float hi = __builtin_fmaxf(__builtin_fmaxf(c[0], c[1]), __builtin_fmaxf(c[2], c[3]));
-                    const float lo = __builtin_fminf(__builtin_fminf(c[0], c[1]), __builtin_fminf(c[2], c[3]));
-                    best = (half_t)act::f(__builtin_fmaf(sk >= 0.0f ? hi : lo, sk, bk));
+                    float pick = __builtin_fmaxf(__builtin_fmaxf(c[0], c[1]), __builtin_fmaxf(c[2], c[3]));
+                    if (scaled) {
+                        const float lo = __builtin_fminf(__builtin_fminf(c[0], c[1]), __builtin_fminf(c[2], c[3]));
+                        pick = sk >= 0.0f ? pick : lo;
+                    }
+                    best = (half_t)act::f(__builtin_fmaf(pick, sk, bk));
                 } else if (EPI == WR_AVG) {
                     // mean of the four rounded values (fp32 sum, exact quarter), one rounding
                     float sum = 0.0f;
@@ -344,62 +358,68 @@ void k_conv_pool_wr(WrArgs a)
                         bi = gt ? e : bi;
                     }
                     const int wi = 2 * g + hh;
-                    if (AM && wi < nw && col < K) a.argmax[(win0 + wi) * K + col] = (uint8_t)bi;
+                    if (AM && wi < nw && col < a.K) a.argmax[(win0 + wi) * a.K + col] = (uint8_t)bi;
                 }
-                // staged as [8 windows][64 columns]
-                ost[(2 * g + hh) * 64 + 32 * ct + lr] = best;
+                sg[(8 * ut + 2 * g + hh) * 128 + col] = best;
             }
         }
-        wave_lds_sync();
-        // 16 bytes per lane: window lane / 8, columns 64 wc + 8 (lane % 8) + [0, 8)
-        const int sw = lane >> 3, sc = lane & 7;
-        const half8 v = *reinterpret_cast<const lds_half8*>(ost + sw * 64 + 8 * sc);
-        const int col = 64 * wc + 8 * sc;
-        if (sw < nw && col < K) st_out(reinterpret_cast<half8*>(a.y + (win0 + sw) * K + col), v);
-        wave_lds_sync();   // the next row tile overwrites the staging area
     };
-    // the partial-sum exchange and the epilogue of one tile (wave kh finishes
-    // row tile kh)
-    auto finish = [&](long rt, int nrt) {
-        __syncthreads();   // every wave has read the previous tile's partial sums
-        if (kh == 0) {
-            if (nrt > 1) hand_over(acc[1]);
-        } else {
-            hand_over(acc[0]);
-        }
-        vm_wait<0>();      // the next tile's halo has landed (and this wave's stores are done)
-        __syncthreads();   // ... for all waves; the partial sums are visible
-        if (kh == 0) epilogue(rt, acc[0]);
-        else if (nrt > 1) epilogue(rt + 1, acc[1]);
-#pragma unroll
-        for (int u = 0; u < WR_NRT; ++u)
-#pragma unroll
-            for (int ct = 0; ct < 2; ++ct) acc[u][ct] = zero16();
+    auto epilogue = [&](int j, int nloc) {
+        if (a.s) epilogue_sc(IntC<1>{}, j, nloc);
+        else epilogue_sc(IntC<0>{}, j, nloc);
+    };
+    // ---- stores of tile j's staged outputs: thread t takes 16 bytes
+    // (columns 8 (t % 16) + [0, 8)) of pooled pixel t / 16 of the tile: row
+    // tile u = wave / 2 (wave-uniform: its decode is scalar work), window
+    // 4 (wave % 2) + lane / 16.  The lane's part of the address is formed once.
+    const int st_wi = 4 * (wq & 1) + (lane >> 4), st_c8 = 8 * (lane & 15);
+    const int st_off = st_wi * a.K + st_c8;
+    auto store_tile = [&](int j) {
+        const int u = wq >> 1;
+        if (u >= tile_nrt(j)) return;
+        const RT t = decode(rt_begin + (long)WR_NRT * j + u);
+        const half_t* const yrow = a.y + (((long)t.n * a.P2 + t.i) * a.Q2 + 8 * t.jb) * a.K;
+        const lds_half* const sg = stage + (2 * wg + ((j >> 1) & 1)) * (WR_STAGE_BYTES / 2);
+        const half8 v = *reinterpret_cast<const lds_half8*>(sg + (4 * wq + (lane >> 4)) * 128 + st_c8);
+        if (st_c8 < a.K && st_wi < a.Q2 - 8 * t.jb) st_out(reinterpret_cast<half8*>(const_cast<half_t*>(yrow) + st_off), v);
     };
 
-    // ---- main loop over this block's full tiles (2 row tiles); the halo
-    // buffers alternate between tiles, and each tile requests the next
-    // tile's halo before its MFMAs.  A last tile of 1 row tile follows.
-    long rt = rt_begin;
-    int sb = 0;   // buffer of the current tile
-    if (rt < rt_end) dma_tile(rt, (int)min((long)WR_NRT, rt_end - rt), lds);
-    vm_wait<0>();
-    __syncthreads();
-    while (rt + WR_NRT <= rt_end) {
-        const long rtn = rt + WR_NRT;
-        if constexpr (kPoison) {   // the previous tile's halo buffer, released by its barriers
-            lds_poison(lds + (sb ^ 1) * WR_BUF_BYTES, WR_BUF_BYTES, tid, WR_THREADS);
-            __syncthreads();
-        }
-        if (rtn < rt_end) dma_tile(rtn, (int)min((long)WR_NRT, rt_end - rtn), lds + (sb ^ 1) * WR_BUF_BYTES);
-        compute(IntC<WR_NRT>{}, lds + sb * WR_BUF_BYTES);
-        finish(rt, WR_NRT);
-        sb ^= 1;
-        rt = rtn;
+    // ---- phase loop (ping-pong).  Tile j belongs to group j % 2.  In phase
+    // k, group k % 2 runs tile k's MFMAs and nothing else, while the other
+    // group, one wave per SIMD beside it, stores its tile k - 3 (staged two
+    // phases ago), runs the epilogue of its tile k - 1, requests the halo of
+    // its tile k + 3 and waits for the halo of its tile k + 1; one barrier
+    // ends every phase.  So the matrix cores of a SIMD always have one wave
+    // feeding them, and each wave's non-matrix work hides under the other's
+    // MFMAs.  The ring holds four halos: tile k + 3 reuses tile k - 1's
+    // buffer, freed by the barrier that ended phase k - 1; each group stages
+    // its outputs in two areas used by alternate tiles.  Memory-counter waits
+    // count this wave's halo requests only: the vector-memory counter retires
+    // loads in issue order, but a store can complete before an older load, so
+    // a wait that counted stores could pass with the halo still in flight;
+    // stores issued after the awaited requests only make the wait stricter.
+    if (wg == 0) {
+        dma_tile(0);
+        if (dma_tile(2)) vm_wait<WR_DMA_PER_PART>();   // tile 0's part has landed
+        else vm_wait<0>();
+    } else {
+        dma_tile(1);
     }
-    if (rt < rt_end) {
-        compute(IntC<1>{}, lds + sb * WR_BUF_BYTES);
-        finish(rt, 1);
+    __syncthreads();   // tile 0's halo visible
+    for (int k = 0; k <= ntiles + 2; ++k) {
+        if (wg == (k & 1)) {
+            const lds_char* const buf = lds + (k % WR_NBUF) * WR_BUF_BYTES;
+            if (k < ntiles) {
+                if (tile_nrt(k) == WR_NRT) compute(IntC<WR_NRT>{}, buf);
+                else compute(IntC<1>{}, buf);
+            }
+        } else {
+            if (k >= 3) store_tile(k - 3);
+            if (k >= 1 && k - 1 < ntiles) epilogue(k - 1, tile_nrt(k - 1));
+            if (dma_tile(k + 3)) vm_wait<WR_DMA_PER_PART>();   // tile k + 1's part has landed
+            else vm_wait<0>();
+        }
+        __syncthreads();
     }
 }
 
@@ -409,7 +429,7 @@ static hipError_t launch_wr(WrArgs a, hipStream_t st)
     static std::atomic<unsigned long long> lds_set{0};
     hipError_t e = allow_full_lds((const void*)k_conv_pool_wr<EPI, ACT, AM>, &lds_set);
     if (e != hipSuccess) return e;
-    long nb = 2L * device_cu_count();   // two blocks per CU
+    long nb = device_cu_count();   // one block per CU
     if (nb > a.nrt) nb = a.nrt;
     a.nblocks = (int)nb;
     hipLaunchKernelGGL((k_conv_pool_wr<EPI, ACT, AM>), dim3((unsigned)nb), dim3(WR_THREADS), (size_t)WR_LDS, st, a);

@@ -128,12 +128,14 @@ def _ranges(ntiles, nblocks):
 
 def conv_pool_wr(n, h, w, c, k, cus=256, argmax=False):
     """Register-weights conv + 2x2 pool (k_conv_pool_wr): row tile = one pooled
-    row of 8 windows (halo 4 x 18 pixels), blocks of 2 row tiles per step, two
-    blocks per CU, weights read once per block."""
+    row of 8 windows (halo 4 x 18 pixels), tiles of 2 row tiles taken in order
+    (alternately by the block's two wave groups), one block per CU, weights
+    read once per block; LDS: a ring of four 20 KiB halo buffers, four 4 KiB
+    output staging areas and the bias/scale."""
     P2, Q2 = h // 2, w // 2
     JB = -(-Q2 // 8)
     nrt = n * P2 * JB
-    nb = min(2 * cus, nrt)
+    nb = min(cus, nrt)
     bt = []
     for a, b in _ranges(nrt, nb):
         bt.append([list(range(s, min(s + 2, b))) for s in range(a, b, 2)])
@@ -143,7 +145,7 @@ def conv_pool_wr(n, h, w, c, k, cus=256, argmax=False):
         img, i = divmod(q, P2)
         return _halo_pixels(img, 2 * i - 1, 16 * jb - 1, 4, 18, h, w)
     out = 2 * n * P2 * Q2 * k + (n * P2 * Q2 * k if argmax else 0)
-    r = _run(bt, nb, 2 * 9 * c * k, c, pix, out, 77 * 1024 + 512)
+    r = _run(bt, nb, 2 * 9 * c * k, c, pix, out, 4 * 20480 + 4 * 4096 + 1024)
     r.update(read_algorithmic=2 * (n * h * w * c + 9 * c * k), kernel="k_conv_pool_wr", tiles=nrt, blocks=nb)
     return r
 

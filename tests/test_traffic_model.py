@@ -93,10 +93,13 @@ def test_l2_model_predicts_fetch(key, variant):
     """The model's L2 misses against the calibrated FETCH_SIZE of the same
     kernel at full size (profiles/traffic.json): within 10%, and closer than
     either bound (algorithmic or per-tile) wherever those differ from it."""
+    import bench
     db = _measured()
     if key not in db:
         pytest.skip("no counters for " + key)
     e = db[key]
+    if e.get("src_hash") != bench.kernel_src_hash():
+        pytest.skip("the committed counters of %s were taken on other kernel sources" % key)
     fetch = e["fetch_kib"] * e["fetch_scale"] * 1024
     spec, _ = inputs.workload(key.split("@")[0])
     r = tm.for_workload(spec, variant)
