@@ -135,7 +135,7 @@ void k_conv_pool_wr(WrArgs a)
     const long rt_end = (lb + 1) * a.nrt / a.nblocks;
 
     // ---- weights -> operand-B fragments in registers, through LDS in pieces.
-    // wf[st]: HWIO rows k = 16 st + 8 hh + [0, 8), column 32 wave + lr.
+    // wf[st]: HWIO rows k = 16 st + 8 hh + [0, 8), column 32 wq + lr.
     half8 wf[NST];
     {
         WTile Wn;
@@ -189,9 +189,20 @@ void k_conv_pool_wr(WrArgs a)
         r.n = (int)n;
         return r;
     };
-    // tiles of this block: tile j covers row tiles [rt_begin + WR_NRT j, + tile_nrt(j))
+    // tiles of this block: tile j covers row tiles [tile_first(j), + tile_nrt(j)).
+    // Even blocks walk their range forward, odd blocks backward: neighbouring
+    // ranges (which meet in the same XCD's L2) then reach the two input rows
+    // their halos share at the same time -- both at the start or both at the
+    // end -- and the second fetch of those rows hits in L2.
     const int ntiles = (int)((rt_end - rt_begin + WR_NRT - 1) / WR_NRT);
-    auto tile_nrt = [&](int j) -> int { return (int)min((long)WR_NRT, rt_end - rt_begin - (long)WR_NRT * j); };
+    const bool backward = lb & 1;
+    auto tile_first = [&](int j) -> long {
+        return backward ? max(rt_begin, rt_end - (long)WR_NRT * (j + 1)) : rt_begin + (long)WR_NRT * j;
+    };
+    auto tile_nrt = [&](int j) -> int {
+        return (int)(backward ? rt_end - (long)WR_NRT * j - tile_first(j)
+                              : min((long)WR_NRT, rt_end - rt_begin - (long)WR_NRT * j));
+    };
 
     // ---- halo DMA.  Wave w fetches part w of a tile: row tile u = w / 2,
     // channel half c = w % 2 (5 instructions).  Lane L of instruction j fills
@@ -224,7 +235,7 @@ void k_conv_pool_wr(WrArgs a)
             lds_poison(dst, WR_PART_BYTES, lane, 64);
             wave_lds_sync();
         }
-        const RT t = decode(rt_begin + (long)WR_NRT * j + u);
+        const RT t = decode(tile_first(j) + u);
         const int ih0 = 2 * t.i - 1, iw0 = 16 * t.jb - 1;   // halo origin in the image
         // the origin's pixel index (one row / column before the image at its
         // top / left border: those pixels are masked below and never read)
@@ -320,7 +331,7 @@ void k_conv_pool_wr(WrArgs a)
             long win0 = 0;
             int nw = 0;
             if constexpr (AM) {
-                const RT t = decode(rt_begin + (long)WR_NRT * j + ut);
+                const RT t = decode(tile_first(j) + ut);
                 win0 = ((long)t.n * a.P2 + t.i) * a.Q2 + 8 * t.jb;
                 nw = min(8, a.Q2 - 8 * t.jb);
             }
@@ -377,7 +388,7 @@ void k_conv_pool_wr(WrArgs a)
     auto store_tile = [&](int j) {
         const int u = wq >> 1;
         if (u >= tile_nrt(j)) return;
-        const RT t = decode(rt_begin + (long)WR_NRT * j + u);
+        const RT t = decode(tile_first(j) + u);
         const half_t* const yrow = a.y + (((long)t.n * a.P2 + t.i) * a.Q2 + 8 * t.jb) * a.K;
         const lds_half* const sg = stage + (2 * wg + ((j >> 1) & 1)) * (WR_STAGE_BYTES / 2);
         const half8 v = *reinterpret_cast<const lds_half8*>(sg + (4 * wq + (lane >> 4)) * 128 + st_c8);

@@ -110,6 +110,10 @@ __global__ __launch_bounds__(WI_THREADS) void k_conv_pool_wino(WinoArgs a)
     const long lb = xcd_block(blockIdx.x, gridDim.x);
     const long b_begin = lb * a.nbatch / gridDim.x;
     const long b_end = (lb + 1) * a.nbatch / gridDim.x;
+    // odd blocks walk their range backward (batch index bt -> row position
+    // b_begin + b_end - 1 - bt): neighbouring ranges then reach the input rows
+    // their halos share at the same time and the second fetch hits in L2
+    const bool backward = lb & 1;
 
     if constexpr (kPoison) {
         lds_poison(smem, (int)wino_lds_bytes<C>(a.K), tid, WI_THREADS);
@@ -148,7 +152,7 @@ __global__ __launch_bounds__(WI_THREADS) void k_conv_pool_wino(WinoArgs a)
     auto issue_halo = [&](long bt, lds_half* hb) {
         unsigned n;
         int ib, jb;
-        batch_pos(bt, n, ib, jb);
+        batch_pos(backward ? b_begin + b_end - 1 - bt : bt, n, ib, jb);
         const long img = (long)a.H * a.W * C;
         const i32x4 rs = buf_rsrc(a.x + (long)n * img, img * 2);
         const int ln = lane_id_here();
@@ -213,7 +217,7 @@ __global__ __launch_bounds__(WI_THREADS) void k_conv_pool_wino(WinoArgs a)
     auto store_batch = [&](long bt, int pr) {
         unsigned n;
         int ib, jb;
-        batch_pos(bt, n, ib, jb);
+        batch_pos(backward ? b_begin + b_end - 1 - bt : bt, n, ib, jb);
         const int kv8 = a.K / 8;
         if (tid < WI_TILES * kv8) {
             const int tb = tid / kv8, kv = tid - tb * kv8;

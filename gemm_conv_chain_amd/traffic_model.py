@@ -129,7 +129,8 @@ def _ranges(ntiles, nblocks):
 def conv_pool_wr(n, h, w, c, k, cus=256, argmax=False):
     """Register-weights conv + 2x2 pool (k_conv_pool_wr): row tile = one pooled
     row of 8 windows (halo 4 x 18 pixels), tiles of 2 row tiles taken in order
-    (alternately by the block's two wave groups), one block per CU, weights
+    (alternately by the block's two wave groups; odd blocks walk their range
+    backward), one block per CU, weights
     read once per block; LDS: a ring of four 20 KiB halo buffers, four 4 KiB
     output staging areas and the bias/scale."""
     P2, Q2 = h // 2, w // 2
@@ -137,8 +138,11 @@ def conv_pool_wr(n, h, w, c, k, cus=256, argmax=False):
     nrt = n * P2 * JB
     nb = min(cus, nrt)
     bt = []
-    for a, b in _ranges(nrt, nb):
-        bt.append([list(range(s, min(s + 2, b))) for s in range(a, b, 2)])
+    for lb, (a, b) in enumerate(_ranges(nrt, nb)):
+        if lb % 2 == 0:
+            bt.append([list(range(s, min(s + 2, b))) for s in range(a, b, 2)])
+        else:   # odd blocks walk their range backward
+            bt.append([list(range(max(a, e - 2), e)) for e in range(b, a, -2)])
 
     def pix(rt):
         q, jb = divmod(rt, JB)
@@ -158,7 +162,8 @@ def conv_pool_wino(n, h, w, c, k, cus=256, argmax=False):
     bh, bw = -(-TH // 2), -(-TW // 8)
     nbatch = n * bh * bw
     nb = min(nbatch, cus)
-    bt = [[[t] for t in range(a, b)] for a, b in _ranges(nbatch, nb)]
+    bt = [[[t] for t in (range(a, b) if lb % 2 == 0 else range(b - 1, a - 1, -1))]
+          for lb, (a, b) in enumerate(_ranges(nbatch, nb))]   # odd blocks walk backward
 
     def pix(bi):
         img, r = divmod(bi, bh * bw)
