@@ -131,7 +131,9 @@ class Problem:
             self.H = torch.empty((n, h, w, k0), dtype=torch.float16, device=dev)
             self.config = {"workload": name, "x": [n, h, w, c], "conv0": "3x3 s1 p1 %d->%d +b ReLU" % (c, k0),
                            "conv1": "1x1 %d->%d +b" % (k0, k1)}
-            self.kernel = "k_chain_rf"
+            cfg = self.fc.conv2_auto_config(n, h, w, c, k0, k1)
+            self.config["variant"] = cfg["variant"]
+            self.kernel = "k_conv2_pipe" if cfg["variant"] == "pipe" else "k_chain_rf"
         elif s["kind"] == "convN":
             n, h, w, c, ks = s["n"], s["h"], s["w"], s["c"], s["ks"]
             self.acts = s["acts"]
@@ -495,7 +497,7 @@ def roofline(prob, ms_kernel, tr):
 
 
 _MODEL_VARIANT = {"k_chain_rf": "rf", "k_gemm_lds": "lds", "k_chain_stream": "stream", "k_conv_w": "lds_weights",
-                  "k_conv_pool_wino": "winograd", "k_conv_pool_wr": "reg_weights"}
+                  "k_conv_pool_wino": "winograd", "k_conv_pool_wr": "reg_weights", "k_conv2_pipe": "pipe"}
 
 
 def traffic_model(prob, tr):
@@ -590,8 +592,12 @@ def tune(fc, prob, name):
         prob.traffic_key = name + "@" + best["variant"]
     elif kind == "conv2":
         w0, b0, w1, b1 = prob.W
+        s = prob.spec
+        default = fc.conv2_auto_config(s["n"], s["h"], s["w"], s["c"], s["k0"], s["k1"])["variant"]   # untuned rule
         best, table, _ = fc.tune_chain_conv2(prob.X[0], w0, b0, w1, b1, act="relu", out=prob.Y[0], reps=10)
         prob.config["variant"] = "auto"
+        prob.kernel = "k_conv2_pipe" if best["variant"] == "pipe" else "k_chain_rf"
+        prob.traffic_key = name if best["variant"] == default else name + "@" + best["variant"]
     else:
         raise ValueError("--tune applies to the two-GEMM, the conv3x3 -> conv1x1 and the pooled conv workloads")
     log("%s tuned: %s waves %d stages %d (%s)" % (name, best["variant"], best["waves"], best["stages"], ", ".join(

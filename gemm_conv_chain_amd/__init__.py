@@ -31,7 +31,7 @@ HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "fusedchain.h")
 
 ACT = {"none": 0, "relu": 1, "gelu_tanh": 2, "hardswish": 3}
 POOL = {"none": 0, "max2x2": 1, "avg2x2": 2}
-VARIANT = {"auto": 0, "rf": 1, "lds": 2, "stream": 3}
+VARIANT = {"auto": 0, "rf": 1, "lds": 2, "stream": 3, "pipe": 4}
 CONV_VARIANT = {"auto": 0, "lds_weights": 1, "reg_weights": 2}
 
 
@@ -136,6 +136,8 @@ def _load(path):
                                               ctypes.POINTER(TuneEntry)]
     L.chain_conv2_ex.argtypes = [_vp, _vp, _vp, ctypes.c_int, _vp, _vp, _i32, _vp, ctypes.POINTER(ConvShape),
                                  _i32, _i32, _vp]
+    L.chain_conv2_variant.argtypes = [_vp, _vp, _vp, ctypes.c_int, _vp, _vp, _i32, _vp, ctypes.POINTER(ConvShape),
+                                      ctypes.c_int, _i32, _i32, _vp]
     L.chain_conv2_tune.argtypes = [_vp, _vp, _vp, ctypes.c_int, _vp, _vp, _i32, _vp, ctypes.POINTER(ConvShape),
                                    _i32, ctypes.POINTER(TuneEntry), _i32, ctypes.POINTER(_i32),
                                    ctypes.POINTER(TuneEntry), _vp]
@@ -145,7 +147,7 @@ def _load(path):
                                            ctypes.POINTER(ConvShape), _vp, _vp]
     L.fc_tune_clear.restype = None
     L.fc_tune_clear.argtypes = []
-    for name in ("chain_conv2_auto_config", "chain_conv2_ex", "chain_conv2_tune", "winograd_weights", "chain_conv_pool_winograd", "chain_gemm2_ex", "chain_gemm2_tune_ex", "chain_gemm2_auto_config", "chain_conv_pool_tune",
+    for name in ("chain_conv2_auto_config", "chain_conv2_ex", "chain_conv2_variant", "chain_conv2_tune", "winograd_weights", "chain_conv_pool_winograd", "chain_gemm2_ex", "chain_gemm2_tune_ex", "chain_gemm2_auto_config", "chain_conv_pool_tune",
                  "chain_conv_pool_auto_config", "chain_conv_pool_ex", "avgpool2x2", "fc_probe_mfma", "fc_probe_read", "chain_conv_bn_pool", "chain_convN", "chain_gemm2_tune", "chain_gemm2_auto_variant", "chain_gemm2", "chain_gemm2_variant", "chain_gemmN", "chain_conv_pool", "chain_conv2", "gemm_bias_act",
                  "conv_bias_act", "maxpool2x2", "pad_channels"):
         getattr(L, name).restype = ctypes.c_int
@@ -590,13 +592,18 @@ def _conv2_prep(x, w0, b0, w1, b1, out):
     return sh, k1, out
 
 
-def chain_conv2(x, w0, b0, w1, b1, act="relu", out=None, waves=0, stages=0):
+def chain_conv2(x, w0, b0, w1, b1, act="relu", out=None, waves=0, stages=0, variant="auto"):
     """y = conv1x1(act(conv3x3(x, w0) + b0), w1) + b1; w1 is [k0, k1] or [1,1,k0,k1].
-    ``waves``: tile-owning waves per block (1..8) and ``stages``: row-stream
-    pipeline stages (4 or 2; 0 = 4), or both 0 for the library's choice."""
+    ``variant``: kernel form ("auto", "rf" or "pipe"); for "rf", ``waves``:
+    tile-owning waves per block (1..8) and ``stages``: row-stream pipeline
+    stages (4 or 2; 0 = 4).  waves > 0 with variant "auto" means "rf"."""
     sh, k1, out = _conv2_prep(x, w0, b0, w1, b1, out)
-    _check("chain_conv2", lib().chain_conv2_ex(_ptr(x), _ptr(w0), _ptr(b0), _act(act), _ptr(w1), _ptr(b1), k1,
-                                               _ptr(out), ctypes.byref(sh), int(waves), int(stages), _stream(x)))
+    v = VARIANT[variant] if isinstance(variant, str) else int(variant)
+    if v == 0 and waves:
+        v = VARIANT["rf"]
+    _check("chain_conv2", lib().chain_conv2_variant(_ptr(x), _ptr(w0), _ptr(b0), _act(act), _ptr(w1), _ptr(b1), k1,
+                                                    _ptr(out), ctypes.byref(sh), v, int(waves), int(stages),
+                                                    _stream(x)))
     return out
 
 

@@ -21,6 +21,9 @@ bool conv_pool_wr_fits(int W, int C, int K);
 hipError_t run_chain_conv2_3x3(const half_t* x, const half_t* w0, const half_t* b0, int act, const half_t* w1,
                                const half_t* b1, half_t* y, int NB, int H, int W, int C, int K0, int K1, int waves,
                                int stages, hipStream_t st);
+bool conv2_pipe_fits(int W, int C, int K0, int K1);
+hipError_t run_chain_conv2_pipe(const half_t* x, const half_t* w0, const half_t* b0, int act, const half_t* w1,
+                                const half_t* b1, half_t* y, int NB, int H, int W, int K1, hipStream_t st);
 hipError_t run_chain_convN_3x3(const half_t* x, int nst, const half_t* const* w, const half_t* const* b,
                                const int* act, const int* widths, half_t* y, int NB, int H, int W, int C,
                                hipStream_t st);
@@ -212,25 +215,32 @@ TuneKey conv2_key(const fc_conv_shape* s, int k1, int act)
     return {TK_CONV2, s->n, s->h, s->w, s->c, s->k, k1, act};
 }
 
-// Candidates of the conv3x3 -> conv1x1 chain (register-resident form): 8, 4,
-// 2 or 1 tile-owning waves per block, each with the four-stage and (where it
+bool conv2_pipe_ok(const fc_conv_shape* s, int k1) { return fc::conv2_pipe_fits(s->w, s->c, s->k, k1); }
+
+// Candidates of the conv3x3 -> conv1x1 chain: the pipelined two-group form
+// (where it takes the shape), then the register-resident form with 8, 4, 2 or
+// 1 tile-owning waves per block, each with the four-stage and (where it
 // exists) the two-stage row ring.
-int conv2_candidates(const fc_conv_shape* s, Config* out)
+int conv2_candidates(const fc_conv_shape* s, int k1, Config* out)
 {
     int n = 0;
+    if (conv2_pipe_ok(s, k1)) out[n++] = Config{fc::VARIANT_PIPE, 0, 0};
     for (int w : {8, 4, 2, 1}) out[n++] = Config{fc::VARIANT_RF, w, 0};
     if (two_stage_ok(9 * s->c))
         for (int w : {8, 4, 2, 1}) out[n++] = Config{fc::VARIANT_RF, w, 2};
     return n;
 }
 
-// Untuned: as for the two-GEMM chain, the smallest power-of-two number of
-// tile-owning waves whose blocks, one per CU, cover the 32-pixel tiles (with
-// 8 waves, the two-stage row ring where it is built).
+// Untuned: the pipelined two-group form where it takes the shape (measured
+// faster at the 32 x 56 x 56 x 64 -> 64 -> 256 workload); else, as for the
+// two-GEMM chain, the smallest power-of-two number of tile-owning waves whose
+// blocks, one per CU, cover the 32-pixel tiles (with 8 waves, the two-stage
+// row ring where it is built).
 Config conv2_config(const fc_conv_shape* s, int k1, int act)
 {
     Config c;
     if (tuned_config(conv2_key(s, k1, act), &c)) return c;
+    if (conv2_pipe_ok(s, k1)) return Config{fc::VARIANT_PIPE, 0, 0};
     const int64_t tiles = ((int64_t)s->n * s->h * s->w + 31) / 32, cus = fc::device_cu_count();
     c = Config{fc::VARIANT_RF, 1, 0};
     while (c.waves < 8 && (int64_t)c.waves * cus < tiles) c.waves *= 2;
@@ -657,6 +667,39 @@ static fc_status check_conv2(const fc_half* x, const fc_half* w0, const fc_half*
     return FC_OK;
 }
 
+static hipError_t run_conv2(const Config& c, const fc_half* x, const fc_half* w0, const fc_half* b0, fc_act act,
+                            const fc_half* w1, const fc_half* b1, int32_t k1, fc_half* y, const fc_conv_shape* s,
+                            hipStream_t st)
+{
+    if (c.variant == fc::VARIANT_PIPE)
+        return fc::run_chain_conv2_pipe(H(x), H(w0), H(b0), act, H(w1), H(b1), Hm(y), s->n, s->h, s->w, k1, st);
+    return fc::run_chain_conv2_3x3(H(x), H(w0), H(b0), act, H(w1), H(b1), Hm(y), s->n, s->h, s->w, s->c, s->k, k1,
+                                   c.waves, c.stages, st);
+}
+
+fc_status chain_conv2_variant(const fc_half* x, const fc_half* w0, const fc_half* b0, fc_act act, const fc_half* w1,
+                              const fc_half* b1, int32_t k1, fc_half* y, const fc_conv_shape* shape0,
+                              fc_variant variant, int32_t waves, int32_t stages, void* stream)
+{
+    if (variant != FC_VARIANT_AUTO && variant != FC_VARIANT_RF && variant != FC_VARIANT_PIPE)
+        return fail(FC_E_ARG, "variant=%d: the conv chain runs FC_VARIANT_AUTO, _RF or _PIPE", (int)variant);
+    if (variant == FC_VARIANT_RF ? (waves < 1 || waves > 8) : waves != 0)
+        return fail(FC_E_ARG, "waves=%d: 1..8 for FC_VARIANT_RF, else 0", (int)waves);
+    if (variant == FC_VARIANT_RF ? (stages != 0 && stages != 2 && stages != 4) : stages != 0)
+        return fail(FC_E_ARG, "stages=%d: 4 or 2 (0 = 4) for FC_VARIANT_RF, else 0", (int)stages);
+    fc_status s = check_conv2(x, w0, b0, act, w1, b1, k1, y, shape0);
+    if (s != FC_OK) return s;
+    if (stages == 2 && !two_stage_ok(9 * shape0->c))
+        return fail(FC_E_UNSUPPORTED, "the two-stage row ring is built for 9c in 193..256 or 513..576");
+    if (variant == FC_VARIANT_PIPE && !conv2_pipe_ok(shape0, k1))
+        return fail(FC_E_UNSUPPORTED, "the pipelined form takes c = 64, k0 = 64, k1 <= 256 (c=%d k0=%d k1=%d)",
+                    shape0->c, shape0->k, (int)k1);
+    if ((long)shape0->n * shape0->h * shape0->w == 0) return ok();
+    const Config c = variant == FC_VARIANT_AUTO ? conv2_config(shape0, k1, (int)act)
+                                                : Config{(int)variant, waves, stages == 4 ? 0 : stages};
+    return hip_status(run_conv2(c, x, w0, b0, act, w1, b1, k1, y, shape0, (hipStream_t)stream), "chain_conv2");
+}
+
 fc_status chain_conv2_ex(const fc_half* x, const fc_half* w0, const fc_half* b0, fc_act act, const fc_half* w1,
                          const fc_half* b1, int32_t k1, fc_half* y, const fc_conv_shape* shape0, int32_t waves,
                          int32_t stages, void* stream)
@@ -665,17 +708,8 @@ fc_status chain_conv2_ex(const fc_half* x, const fc_half* w0, const fc_half* b0,
     if (stages != 0 && stages != 2 && stages != 4)
         return fail(FC_E_ARG, "stages=%d: 4 or 2, or 0 for the library's choice", (int)stages);
     if (waves == 0 && stages != 0) return fail(FC_E_ARG, "stages needs an explicit waves");
-    fc_status s = check_conv2(x, w0, b0, act, w1, b1, k1, y, shape0);
-    if (s != FC_OK) return s;
-    if (stages == 2 && !two_stage_ok(9 * shape0->c))
-        return fail(FC_E_UNSUPPORTED, "the two-stage row ring is built for 9c in 193..256 or 513..576");
-    if ((long)shape0->n * shape0->h * shape0->w == 0) return ok();
-    const Config c = waves > 0 ? Config{fc::VARIANT_RF, waves, stages == 4 ? 0 : stages}
-                               : conv2_config(shape0, k1, (int)act);
-    return hip_status(fc::run_chain_conv2_3x3(H(x), H(w0), H(b0), act, H(w1), H(b1), Hm(y), shape0->n, shape0->h,
-                                              shape0->w, shape0->c, shape0->k, k1, c.waves, c.stages,
-                                              (hipStream_t)stream),
-                      "chain_conv2");
+    return chain_conv2_variant(x, w0, b0, act, w1, b1, k1, y, shape0, waves > 0 ? FC_VARIANT_RF : FC_VARIANT_AUTO,
+                               waves, stages, stream);
 }
 
 fc_status chain_conv2(const fc_half* x, const fc_half* w0, const fc_half* b0, fc_act act, const fc_half* w1,
@@ -707,12 +741,9 @@ fc_status chain_conv2_tune(const fc_half* x, const fc_half* w0, const fc_half* b
     if (reps < 1 || reps > 1000) return fail(FC_E_SHAPE, "reps=%d outside 1..1000", (int)reps);
     if (capacity < 0 || (capacity > 0 && !table)) return fail(FC_E_NULL, "table is required for capacity > 0");
     Config cand[16];
-    const int n = conv2_candidates(shape0, cand);
+    const int n = conv2_candidates(shape0, k1, cand);
     hipStream_t st = (hipStream_t)stream;
-    auto launch = [&](const Config& c) {
-        return fc::run_chain_conv2_3x3(H(x), H(w0), H(b0), act, H(w1), H(b1), Hm(y), shape0->n, shape0->h, shape0->w,
-                                       shape0->c, shape0->k, k1, c.waves, c.stages, st);
-    };
+    auto launch = [&](const Config& c) { return run_conv2(c, x, w0, b0, act, w1, b1, k1, y, shape0, st); };
     return profile("chain_conv2_tune", launch, cand, n, reps, conv2_key(shape0, k1, (int)act), table, capacity, count,
                    best, st);
 }

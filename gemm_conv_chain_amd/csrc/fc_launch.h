@@ -7,7 +7,7 @@ namespace fc {
 
 typedef _Float16 half_t;
 
-enum { VARIANT_AUTO = 0, VARIANT_RF = 1, VARIANT_LDS = 2, VARIANT_STREAM = 3 };
+enum { VARIANT_AUTO = 0, VARIANT_RF = 1, VARIANT_LDS = 2, VARIANT_STREAM = 3, VARIANT_PIPE = 4 };
 
 // LDS a block may use (gfx950: 160 KiB per CU; one block of the persistent
 // kernels per CU).

@@ -247,6 +247,34 @@ def conv2_rf(n, h, w, c, k0, k1, cus=256, k_more=()):
     return r
 
 
+def conv2_pipe(n, h, w, c, k0, k1, cus=256):
+    """conv3x3 -> conv1x1 in two pipelined wave groups (k_conv2_pipe): row
+    tile = 2 image rows x 16 columns (halo 4 x 18 pixels), tiles of 2 row
+    tiles taken in order (odd blocks walk their range backward), one block per
+    CU, both weight matrices read once per block; LDS: three 20 KiB halo
+    buffers, two 8 KiB intermediate tiles, four 8 KiB output staging tiles and
+    the biases."""
+    P2, JB = -(-h // 2), -(-w // 16)
+    nrt = n * P2 * JB
+    nb = min(cus, nrt)
+    bt = []
+    for lb, (a, b) in enumerate(_ranges(nrt, nb)):
+        if lb % 2 == 0:
+            bt.append([list(range(s, min(s + 2, b))) for s in range(a, b, 2)])
+        else:
+            bt.append([list(range(max(a, e - 2), e)) for e in range(b, a, -2)])
+
+    def pix(rt):
+        q, jb = divmod(rt, JB)
+        img, i = divmod(q, P2)
+        return _halo_pixels(img, 2 * i - 1, 16 * jb - 1, 4, 18, h, w)
+    wb = 2 * (9 * c * k0 + k0 * k1)
+    out = 2 * n * h * w * k1
+    r = _run(bt, nb, wb, c, pix, out, 3 * 20480 + 2 * 8192 + 4 * 8192 + 4 * (64 + 256))
+    r.update(read_algorithmic=2 * n * h * w * c + wb, kernel="k_conv2_pipe", tiles=nrt, blocks=nb)
+    return r
+
+
 def gemm_chain(M, K0, N0, N1, variant, cus=256):
     """Two-GEMM chain: the rows of A are read once by the tile that owns them
     (no halo), each block reads the weights once; the weights of all blocks
@@ -291,6 +319,8 @@ def for_workload(spec: dict, variant: str | None = None, cus: int = 256, argmax:
     if kind == "gemmN":
         return gemm_chain_n(spec["M"], spec["widths"], cus)
     if kind == "conv2":
+        if variant != "rf" and spec["c"] == 64 and spec["k0"] == 64 and spec["k1"] <= 256:
+            return conv2_pipe(spec["n"], spec["h"], spec["w"], spec["c"], spec["k0"], spec["k1"], cus)
         return conv2_rf(spec["n"], spec["h"], spec["w"], spec["c"], spec["k0"], spec["k1"], cus)
     if kind == "convN":
         ks = spec["ks"]

@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define FC_ABI_VERSION 3
+#define FC_ABI_VERSION 4
 
 typedef uint16_t fc_half;
 
@@ -74,7 +74,13 @@ typedef enum { FC_ACT_NONE = 0, FC_ACT_RELU = 1, FC_ACT_GELU_TANH = 2, FC_ACT_HA
  * the epilogue (BOLT notes, "Prerequisite: Epilogue fusion"): the mean of the
  * window's four fp16-rounded values, rounded once to fp16. */
 typedef enum { FC_POOL_NONE = 0, FC_POOL_MAX_2X2_S2 = 1, FC_POOL_AVG_2X2_S2 = 2 } fc_pool;
-typedef enum { FC_VARIANT_AUTO = 0, FC_VARIANT_RF = 1, FC_VARIANT_LDS = 2, FC_VARIANT_STREAM = 3 } fc_variant;
+typedef enum {
+    FC_VARIANT_AUTO = 0,
+    FC_VARIANT_RF = 1,
+    FC_VARIANT_LDS = 2,
+    FC_VARIANT_STREAM = 3,
+    FC_VARIANT_PIPE = 4   /* conv3x3 -> conv1x1 only (chain_conv2_variant) */
+} fc_variant;
 
 /* Kernel forms of the conv + activation + 2x2 pool chain (chain_conv_pool_ex).
  * Both keep the conv output in registers and compute the same values up to
@@ -309,37 +315,58 @@ fc_status chain_conv_pool_auto_config(const fc_conv_shape *shape, fc_act act, fc
 
 /*
  * chain_conv2 -- y = conv1x1(act(conv(x, w0) + b0), w1) + b1, the first conv's
- * output kept in VGPRs (BOLT persistent conv fusion; a 1x1 conv is a GEMM,
- * interview page, conv item 5).
+ * output kept on chip (BOLT persistent conv fusion; a 1x1 conv is a GEMM,
+ * interview page, conv item 5), rounded once to fp16.
  *   x NHWC [n,h,w,c], w0 HWIO [3,3,c,k0] (k0 = shape0->k), b0 [k0],
  *   w1 [k0 x k1] (= HWIO [1,1,k0,k1]), b1 [k1], y NHWC [n,P,Q,k1].
  * Implemented: r = s = 3, stride 1, pad 1, c % 8 == 0, k0 % 8 == 0 and
  * k0 <= 128, k1 % 8 == 0, n*h*w < 2^31, and both weights fit in LDS together.
+ * Two kernel forms (chain_conv2_variant): FC_VARIANT_RF keeps the first conv's
+ * output in the VGPRs of the wave that computed it (any shape above);
+ * FC_VARIANT_PIPE runs the two convs in two pipelined wave groups of one block
+ * per CU -- the 3x3 conv's weights in registers, its input halo streamed into
+ * LDS by LDS-DMA, the intermediate tile in LDS for the 1x1 conv of the other
+ * group -- for c = 64, k0 = 64, k1 <= 256 and w * c < 2^27.  The library
+ * runs the profiled form if chain_conv2_tune ran for the shape, else
+ * FC_VARIANT_PIPE where it applies, else FC_VARIANT_RF.  Both compute the same
+ * values up to the fp32 summation order.
  */
 fc_status chain_conv2(const fc_half *x, const fc_half *w0, const fc_half *b0, fc_act act,
                       const fc_half *w1, const fc_half *b1, int32_t k1, fc_half *y,
                       const fc_conv_shape *shape0, void *stream);
 
-/* chain_conv2_ex -- chain_conv2 with the block shape chosen by the caller:
- * waves = tile-owning waves per block (1..8; a block's round covers 32 * waves
- * pixels) and stages = row-chunk ring depth (4, or 2 where built: 9c in
- * 193..256 or 513..576, else FC_E_UNSUPPORTED; 0 = 4), or waves = stages = 0
- * for the library's choice (the profiled one if chain_conv2_tune ran for this
- * shape, else the smallest power of two whose blocks, one per CU, cover the
- * 32-pixel tiles, with 4 stages).  Other values -> FC_E_ARG. */
+/* chain_conv2_ex -- chain_conv2 with the FC_VARIANT_RF block shape chosen by
+ * the caller: waves = tile-owning waves per block (1..8; a block's round covers
+ * 32 * waves pixels) and stages = row-chunk ring depth (4, or 2 where built:
+ * 9c in 193..256 or 513..576, else FC_E_UNSUPPORTED; 0 = 4), or waves =
+ * stages = 0 for the library's choice (as chain_conv2; the untuned rule of
+ * FC_VARIANT_RF is the smallest power of two whose blocks, one per CU, cover
+ * the 32-pixel tiles, with 2 stages at 8 waves where built).  Other values ->
+ * FC_E_ARG. */
 fc_status chain_conv2_ex(const fc_half *x, const fc_half *w0, const fc_half *b0, fc_act act, const fc_half *w1,
                          const fc_half *b1, int32_t k1, fc_half *y, const fc_conv_shape *shape0, int32_t waves,
                          int32_t stages, void *stream);
 
+/* chain_conv2_variant -- chain_conv2 with the kernel form chosen by the
+ * caller: FC_VARIANT_AUTO (waves = stages = 0: the library's choice),
+ * FC_VARIANT_RF (waves, stages as chain_conv2_ex, waves >= 1) or
+ * FC_VARIANT_PIPE (waves = stages = 0; FC_E_UNSUPPORTED outside its shapes).
+ * Other variants or values -> FC_E_ARG; errors otherwise as chain_conv2. */
+fc_status chain_conv2_variant(const fc_half *x, const fc_half *w0, const fc_half *b0, fc_act act,
+                              const fc_half *w1, const fc_half *b1, int32_t k1, fc_half *y,
+                              const fc_conv_shape *shape0, fc_variant variant, int32_t waves, int32_t stages,
+                              void *stream);
+
 /* The configuration chain_conv2 runs for this shape on the current device
- * (variant FC_VARIANT_RF, waves; us = -1): the tuned one, else the rule of
- * chain_conv2_ex(waves = 0).  Host only. */
+ * (variant FC_VARIANT_PIPE or FC_VARIANT_RF with waves and stages; us = -1):
+ * the tuned one, else the untuned rule of chain_conv2.  Host only. */
 fc_status chain_conv2_auto_config(const fc_conv_shape *shape0, int32_t k1, fc_act act, fc_tune_entry *out);
 
 /* chain_conv2_tune -- the profiler of chain_conv2 (BOLT notes, "Light-weight
  * performance profiler"): times reps launches (1..1000, after one untimed
- * launch) of each block shape (8, 4, 2, 1 tile-owning waves; variant
- * FC_VARIANT_RF) with 4 and, where built, 2 pipeline stages on this input, writes up to capacity rows of table
+ * launch) of each candidate -- FC_VARIANT_PIPE where it applies, and each
+ * FC_VARIANT_RF block shape (8, 4, 2, 1 tile-owning waves) with 4 and, where
+ * built, 2 pipeline stages -- on this input, writes up to capacity rows of table
  * (us = mean microseconds per launch), *count = candidates timed, *best = the
  * fastest, and caches it for (device, shape, k1, act): chain_conv2 and
  * chain_conv2_ex(waves = 0) then run it.  y is written (by the winner last).

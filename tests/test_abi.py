@@ -26,7 +26,8 @@ def test_exports_every_declared_symbol(L):
     for n in ("chain_gemm2", "chain_gemm2_variant", "chain_gemmN", "chain_conv_pool", "chain_conv2", "gemm_bias_act",
               "conv_bias_act", "maxpool2x2", "pad_channels", "fc_abi_version", "fc_status_str", "fc_last_error",
               "chain_gemm2_tune", "chain_gemm2_auto_variant", "fc_tune_clear", "chain_convN", "chain_conv_bn_pool", "fc_probe_mfma", "chain_conv_pool_ex", "chain_gemm2_ex",
-              "chain_gemm2_tune_ex", "chain_gemm2_auto_config", "chain_conv_pool_tune", "chain_conv_pool_auto_config"):
+              "chain_gemm2_tune_ex", "chain_gemm2_auto_config", "chain_conv_pool_tune", "chain_conv_pool_auto_config",
+              "chain_conv2_variant", "chain_conv2_ex", "chain_conv2_tune", "chain_conv2_auto_config"):
         assert n in names
     for n in names:
         assert hasattr(L, n), n
@@ -45,7 +46,7 @@ def test_poison_build_exports_the_same_abi(L):
 
 
 def test_version_and_status_strings(L):
-    assert fc.abi_version() == 3
+    assert fc.abi_version() == 4
     for code, name in enumerate(["FC_OK", "FC_E_NULL", "FC_E_SHAPE", "FC_E_ALIGN", "FC_E_UNSUPPORTED", "FC_E_HIP",
                                  "FC_E_ARG"]):
         assert L.fc_status_str(code).decode() == name
@@ -200,6 +201,12 @@ def test_tuner_validation(L):
     assert fc.auto_config(65536, 576, 256, 256, "gelu_tanh") == {"variant": "stream", "waves": 0, "stages": 0}
     assert fc.conv_auto_config(32, 112, 112, 64, 128) == {"variant": "reg_weights", "waves": 0, "stages": 0}
     assert fc.conv_auto_config(2, 8, 8, 32, 64) == {"variant": "lds_weights", "waves": 8, "stages": 0}
+    # conv3x3 -> conv1x1: the pipelined two-group form where it applies, else the register-resident one
+    assert fc.conv2_auto_config(32, 56, 56, 64, 64, 256) == {"variant": "pipe", "waves": 0, "stages": 0}
+    assert fc.conv2_auto_config(1, 7, 9, 64, 64, 40) == {"variant": "pipe", "waves": 0, "stages": 0}
+    assert fc.conv2_auto_config(32, 56, 56, 64, 64, 264)["variant"] == "rf"    # k1 > 256
+    assert fc.conv2_auto_config(32, 56, 56, 32, 64, 256)["variant"] == "rf"    # c != 64
+    assert fc.conv2_auto_config(32, 56, 56, 64, 96, 256)["variant"] == "rf"    # k0 != 64
 
 
 def test_empty_tensors_may_be_null(L):
@@ -395,6 +402,23 @@ def test_conv2_waves_and_tuner_validation(L):
     assert ex(P, P, NUL, 1, P, NUL, 64, P2, C.byref(sh0), 0, 2, None) == E_ARG               # stages need waves
     assert ex(P, P, NUL, 1, P, NUL, 64, P2, C.byref(shape(c=32, k=64)), 4, 2, None) == E_UNSUP  # 9c = 288
     assert ex(P, P, NUL, 1, P, NUL, 60, P2, C.byref(sh0), 0, 0, None) == E_SHAPE
+    va = L.chain_conv2_variant
+    RF, PIPE = fc.VARIANT["rf"], fc.VARIANT["pipe"]
+    e0 = C.byref(shape(n=0, k=64))
+    assert va(P, P, NUL, 1, P, NUL, 256, P2, e0, 0, 0, 0, None) == OK
+    assert va(P, P, NUL, 1, P, NUL, 256, P2, e0, PIPE, 0, 0, None) == OK
+    assert va(P, P, NUL, 1, P, NUL, 256, P2, e0, RF, 8, 2, None) == OK
+    assert va(P, P, NUL, 1, P, NUL, 256, P2, e0, RF, 0, 0, None) == E_ARG       # RF needs waves
+    assert va(P, P, NUL, 1, P, NUL, 256, P2, e0, PIPE, 8, 0, None) == E_ARG     # PIPE takes no waves
+    assert va(P, P, NUL, 1, P, NUL, 256, P2, e0, PIPE, 0, 2, None) == E_ARG
+    assert va(P, P, NUL, 1, P, NUL, 256, P2, e0, 0, 4, 0, None) == E_ARG        # AUTO takes no waves
+    for v in (fc.VARIANT["lds"], fc.VARIANT["stream"], 5, -1):
+        assert va(P, P, NUL, 1, P, NUL, 256, P2, e0, v, 0, 0, None) == E_ARG
+    assert va(P, P, NUL, 1, P, NUL, 256, P2, C.byref(shape(n=0, c=32, k=64)), PIPE, 0, 0, None) == E_UNSUP
+    assert va(P, P, NUL, 1, P, NUL, 256, P2, C.byref(shape(n=0, c=64, k=96)), PIPE, 0, 0, None) == E_UNSUP
+    assert va(P, P, NUL, 1, P, NUL, 264, P2, e0, PIPE, 0, 0, None) == E_UNSUP
+    assert va(NUL, P, NUL, 1, P, NUL, 256, P2, C.byref(shape(c=64, k=64)), PIPE, 0, 0, None) == E_NULL
+    assert va(P, P, NUL, 1, P, NUL, 60, P2, e0, PIPE, 0, 0, None) == E_SHAPE
     tab = (fc.TuneEntry * 4)()
     n = C.c_int32(0)
     best = fc.TuneEntry()

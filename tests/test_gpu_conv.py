@@ -212,12 +212,45 @@ def test_conv_pool_full_size(fc):
 
 
 @pytest.mark.slow
-def test_conv2_full_size(fc):
+@pytest.mark.parametrize("variant", ["auto", "rf"])
+def test_conv2_full_size(fc, variant):
+    # "auto" is the pipelined two-group form at this shape (the bench's launch)
     spec, d = inputs.workload("conv3x3_conv1x1")
-    print("case full conv3x3_conv1x1", flush=True)
-    y = to_np(fc.chain_conv2(*(dev(d[k]) for k in ("x", "w0", "b0", "w1", "b1"))))
+    print("case full conv3x3_conv1x1", variant, flush=True)
+    args = [dev(d[k]) for k in ("x", "w0", "b0", "w1", "b1")]
+    y = to_np(fc.chain_conv2(*args, variant=variant, waves=8 if variant == "rf" else 0))
     ref, _ = oracle.chain_conv2(d["x"], d["w0"], d["b0"], oracle.ACT_RELU, d["w1"], d["b1"])
-    check_full(y, ref, "full conv3x3_conv1x1")
+    check_full(y, ref, "full conv3x3_conv1x1 " + variant)
+
+
+@pytest.mark.parametrize("n,h,w,k1", [
+    (1, 1, 1, 8),          # one pixel: one row tile, 31 of its 32 rows outside the image
+    (1, 2, 17, 256),       # odd width: a second column block with one valid column
+    (3, 5, 7, 40),         # odd height: the last row pair has one valid row
+    (2, 33, 35, 256),      # several tiles per block, ragged in both directions
+    (1, 16, 16, 200),      # k1 not a multiple of 64
+    (4, 28, 28, 64),
+    (40, 9, 10, 128),      # more row tiles than blocks: odd block ranges walk backward
+])
+def test_conv2_pipe(fc, n, h, w, k1):
+    d = inputs.conv2_inputs(n, h, w, 64, 64, k1, seed=n + h + w + k1)
+    print("case conv2 pipe", n, h, w, k1, flush=True)
+    args = [dev(d[k]) for k in ("x", "w0", "b0", "w1", "b1")]
+    y = to_np(fc.chain_conv2(*args, act="relu", variant="pipe"))
+    ref, _ = oracle.chain_conv2(d["x"], d["w0"], d["b0"], oracle.ACT_RELU, d["w1"], d["b1"])
+    check_full(y, ref, "conv2 pipe %s" % ((n, h, w, k1),))
+    rf = to_np(fc.chain_conv2(*args, act="relu", variant="rf", waves=8))
+    # the same fp16 intermediate; the two forms differ only in fp32 summation order
+    assert np.abs(y.astype(np.float64) - rf).max() <= 2 * np.abs(ref).max() * 2.0 ** -10 + 1e-3
+
+
+@pytest.mark.parametrize("act", ["none", "gelu_tanh", "hardswish"])
+def test_conv2_pipe_acts(fc, act):
+    d = inputs.conv2_inputs(2, 9, 20, 64, 64, 96, seed=41)
+    print("case conv2 pipe", act, flush=True)
+    y = to_np(fc.chain_conv2(*(dev(d[k]) for k in ("x", "w0", "b0", "w1", "b1")), act=act, variant="pipe"))
+    ref, _ = oracle.chain_conv2(d["x"], d["w0"], d["b0"], ACTS[act], d["w1"], d["b1"])
+    check_full(y, ref, "conv2 pipe " + act)
 
 
 @pytest.mark.parametrize("n,h,w,c,ks,acts", [

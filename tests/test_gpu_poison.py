@@ -144,7 +144,8 @@ def test_poison_conv_bias_act_and_conv2(fc):
     prod, pois = both(fc, lambda: fc.conv_bias_act(x, w0, b0, act="none"))
     same_bits(prod, pois, "conv_bias_act")
     assert_close(pois[0], oracle.conv_bias_act(d["x"], d["w0"], d["b0"], oracle.ACT_NONE), "poison conv_bias_act")
-    prod, pois = both(fc, lambda: fc.chain_conv2(x, w0, b0, w1, b1, act="none"))
-    same_bits(prod, pois, "chain_conv2")
     ref, _ = oracle.chain_conv2(d["x"], d["w0"], d["b0"], oracle.ACT_NONE, d["w1"], d["b1"])
-    assert_close(pois[0], ref, "poison chain_conv2")
+    for variant, waves in (("pipe", 0), ("rf", 8)):
+        prod, pois = both(fc, lambda: fc.chain_conv2(x, w0, b0, w1, b1, act="none", variant=variant, waves=waves))
+        same_bits(prod, pois, "chain_conv2 " + variant)
+        assert_close(pois[0], ref, "poison chain_conv2 " + variant)
