@@ -131,9 +131,12 @@ class Problem:
             self.H = torch.empty((n, h, w, k0), dtype=torch.float16, device=dev)
             self.config = {"workload": name, "x": [n, h, w, c], "conv0": "3x3 s1 p1 %d->%d +b ReLU" % (c, k0),
                            "conv1": "1x1 %d->%d +b" % (k0, k1)}
-            cfg = self.fc.conv2_auto_config(n, h, w, c, k0, k1)
-            self.config["variant"] = cfg["variant"]
-            self.kernel = "k_conv2_pipe" if cfg["variant"] == "pipe" else "k_chain_rf"
+            default = self.fc.conv2_auto_config(n, h, w, c, k0, k1)["variant"]
+            self.conv_variant = variant or default
+            if self.conv_variant != default:
+                self.traffic_key = name + "@" + self.conv_variant
+            self.config["variant"] = self.conv_variant
+            self.kernel = "k_conv2_pipe" if self.conv_variant == "pipe" else "k_chain_rf"
         elif s["kind"] == "convN":
             n, h, w, c, ks = s["n"], s["h"], s["w"], s["c"], s["ks"]
             self.acts = s["acts"]
@@ -153,7 +156,12 @@ class Problem:
             self.Hs = [torch.empty((n, h, w, k), dtype=torch.float16, device=dev) for k in ks[:-1]]
             self.config = {"workload": name, "x": [n, h, w, c], "conv0": "3x3 s1 p1 %d->%d +b %s" % (c, ks[0], self.acts[0]),
                            "conv1x1": ["%d->%d +b %s" % (ks[i - 1], ks[i], self.acts[i]) for i in range(1, len(ks))]}
-            self.kernel = "k_chain_rf"
+            default = self.fc.convN_auto_variant(n, h, w, c, ks)
+            self.conv_variant = variant or default
+            if self.conv_variant != default:
+                self.traffic_key = name + "@" + self.conv_variant
+            self.config["variant"] = self.conv_variant
+            self.kernel = "k_conv2_pipe" if self.conv_variant == "pipe" else "k_chain_rf"
         else:
             n, h, w, c, cp, k = s["n"], s["h"], s["w"], s["c"], s["cpad"], s["k"]
             npix = n * h * w
@@ -201,10 +209,12 @@ class Problem:
             fc.chain_gemmN(self.X[j], self.W[:n], self.W[n:], self.acts, out=self.Y[j])
         elif s["kind"] == "conv2":
             w0, b0, w1, b1 = self.W
-            fc.chain_conv2(self.X[j], w0, b0, w1, b1, act="relu", out=self.Y[j])
+            rf = self.conv_variant == "rf"   # the register form at the full workload's rule: 8 waves, 2 stages
+            fc.chain_conv2(self.X[j], w0, b0, w1, b1, act="relu", out=self.Y[j], variant=self.conv_variant,
+                           waves=8 if rf else 0, stages=2 if rf else 0)
         elif s["kind"] == "convN":
             n = len(self.acts)
-            fc.chain_convN(self.X[j], self.W[:n], self.W[n:], self.acts, out=self.Y[j])
+            fc.chain_convN(self.X[j], self.W[:n], self.W[n:], self.acts, out=self.Y[j], variant=self.conv_variant)
         elif self.bn:
             w, sc, sh = self.W
             fc.chain_conv_bn_pool(self.X[j], w, sc, sh, act="relu", pool="max2x2", out=self.Y[j],
@@ -595,6 +605,7 @@ def tune(fc, prob, name):
         s = prob.spec
         default = fc.conv2_auto_config(s["n"], s["h"], s["w"], s["c"], s["k0"], s["k1"])["variant"]   # untuned rule
         best, table, _ = fc.tune_chain_conv2(prob.X[0], w0, b0, w1, b1, act="relu", out=prob.Y[0], reps=10)
+        prob.conv_variant = "auto"
         prob.config["variant"] = "auto"
         prob.kernel = "k_conv2_pipe" if best["variant"] == "pipe" else "k_chain_rf"
         prob.traffic_key = name if best["variant"] == default else name + "@" + best["variant"]
@@ -618,8 +629,10 @@ def main():
     ap.add_argument("--workload", default="conv3x3_relu_maxpool", choices=WORKLOADS,
                     help="the headline workload (default: the conv3x3 + ReLU + 2x2 max-pool chain on "
                          "x[32,112,112,60->64], the largest configuration)")
-    ap.add_argument("--variant", choices=["rf", "lds", "stream", "lds_weights", "reg_weights", "winograd"], default=None,
+    ap.add_argument("--variant", choices=["rf", "lds", "stream", "pipe", "lds_weights", "reg_weights", "winograd"],
+                    default=None,
                     help="kernel form: GEMM chains rf / lds / stream (default rf, or lds for b2b_gemm_lds); "
+                         "conv3x3 -> conv1x1 chains pipe / rf (default: the library's choice); "
                          "conv + pool chains lds_weights / reg_weights (default: the library's choice) or "
                          "winograd (F(2x2,3x3), its own numerics)")
     ap.add_argument("--warm", action="store_true", help="reuse one buffer set (cache-warm timing)")

@@ -20,7 +20,7 @@ import ctypes
 import os
 import re
 
-__all__ = ["TuneEntry", "tune_chain_gemm2_table", "auto_config", "tune_conv_pool", "conv_auto_config", "CONV_VARIANT", "lib", "FusedChainError", "chain_gemm2", "tune_chain_gemm2", "auto_variant", "tune_clear", "chain_gemmN", "chain_conv_pool", "chain_conv_bn_pool", "chain_conv2", "chain_convN",
+__all__ = ["TuneEntry", "tune_chain_gemm2_table", "auto_config", "tune_conv_pool", "conv_auto_config", "CONV_VARIANT", "lib", "FusedChainError", "chain_gemm2", "tune_chain_gemm2", "auto_variant", "tune_clear", "chain_gemmN", "chain_conv_pool", "chain_conv_bn_pool", "chain_conv2", "chain_convN", "convN_auto_variant",
            "gemm_bias_act", "conv_bias_act", "maxpool2x2", "avgpool2x2", "pad_channels", "pad_weight_channels", "abi_version", "ACT", "VARIANT",
            "LIB_PATH", "POISON_LIB_PATH", "poison_build", "HEADER_PATH", "exported_names"]
 
@@ -117,6 +117,10 @@ def _load(path):
     L.chain_gemm2_auto_variant.argtypes = [_i64, _i32, _i32, _i32, ctypes.c_int, ctypes.POINTER(ctypes.c_int)]
     L.chain_convN.argtypes = [_vp, ctypes.POINTER(ConvShape), _i32, ctypes.POINTER(_vp), ctypes.POINTER(_vp),
                               ctypes.POINTER(ctypes.c_int), ctypes.POINTER(_i32), _vp, _vp]
+    L.chain_convN_variant.argtypes = [_vp, ctypes.POINTER(ConvShape), _i32, ctypes.POINTER(_vp), ctypes.POINTER(_vp),
+                                      ctypes.POINTER(ctypes.c_int), ctypes.POINTER(_i32), _vp, ctypes.c_int, _vp]
+    L.chain_convN_auto_variant.argtypes = [ctypes.POINTER(ConvShape), _i32, ctypes.POINTER(_i32),
+                                           ctypes.POINTER(ctypes.c_int)]
     L.chain_conv_bn_pool.argtypes = [_vp, _vp, _vp, _vp, ctypes.c_int, ctypes.c_int, _vp,
                                      ctypes.POINTER(ConvShape), _vp, _vp]
     L.chain_conv_pool_ex.argtypes = [_vp, _vp, _vp, _vp, ctypes.c_int, ctypes.c_int, _vp,
@@ -148,7 +152,7 @@ def _load(path):
     L.fc_tune_clear.restype = None
     L.fc_tune_clear.argtypes = []
     for name in ("chain_conv2_auto_config", "chain_conv2_ex", "chain_conv2_variant", "chain_conv2_tune", "winograd_weights", "chain_conv_pool_winograd", "chain_gemm2_ex", "chain_gemm2_tune_ex", "chain_gemm2_auto_config", "chain_conv_pool_tune",
-                 "chain_conv_pool_auto_config", "chain_conv_pool_ex", "avgpool2x2", "fc_probe_mfma", "fc_probe_read", "chain_conv_bn_pool", "chain_convN", "chain_gemm2_tune", "chain_gemm2_auto_variant", "chain_gemm2", "chain_gemm2_variant", "chain_gemmN", "chain_conv_pool", "chain_conv2", "gemm_bias_act",
+                 "chain_conv_pool_auto_config", "chain_conv_pool_ex", "avgpool2x2", "fc_probe_mfma", "fc_probe_read", "chain_conv_bn_pool", "chain_convN", "chain_convN_variant", "chain_convN_auto_variant", "chain_gemm2_tune", "chain_gemm2_auto_variant", "chain_gemm2", "chain_gemm2_variant", "chain_gemmN", "chain_conv_pool", "chain_conv2", "gemm_bias_act",
                  "conv_bias_act", "maxpool2x2", "pad_channels"):
         getattr(L, name).restype = ctypes.c_int
     return L
@@ -632,10 +636,21 @@ def conv2_auto_config(n, h, w, c, k0, k1, act="relu"):
     return d
 
 
-def chain_convN(x, ws, bs, acts, out=None):
+def convN_auto_variant(n, h, w, c, ks):
+    """The kernel form ("pipe" or "rf") chain_convN runs for x [n,h,w,c] and
+    stage widths ks (host only)."""
+    sh = ConvShape(n, h, w, c, ks[0], 3, 3, 1, 1)
+    kp = (_i32 * len(ks))(*ks)
+    v = ctypes.c_int(-1)
+    _check("chain_convN_auto_variant", lib().chain_convN_auto_variant(ctypes.byref(sh), len(ks), kp, ctypes.byref(v)))
+    return _VARIANT_NAME[v.value]
+
+
+def chain_convN(x, ws, bs, acts, out=None, variant="auto"):
     """y = stage_{n-1}(... stage_0(x)): stage 0 = act[0](conv3x3(x, ws[0]) + bs[0]),
     stage i > 0 = act[i](1x1 conv with ws[i] [k_{i-1}, k_i] (or [1,1,k_{i-1},k_i]) + bs[i]);
-    n = 3 or 4, every intermediate rounded once to fp16 and kept on chip."""
+    n = 3 or 4, every intermediate rounded once to fp16 and kept on chip.
+    ``variant``: kernel form ("auto", "rf" or "pipe")."""
     n = len(ws)
     if len(bs) != n or len(acts) != n:
         raise ValueError("ws, bs and acts must have the same length")
@@ -655,7 +670,9 @@ def chain_convN(x, ws, bs, acts, out=None):
     bp = (_vp * n)(*[None if b is None else b.data_ptr() for b in bs])
     ap = (ctypes.c_int * n)(*[_act(a) for a in acts])
     kp = (_i32 * n)(*ks)
-    _check("chain_convN", lib().chain_convN(_ptr(x), ctypes.byref(sh), n, wp, bp, ap, kp, _ptr(out), _stream(x)))
+    v = VARIANT[variant] if isinstance(variant, str) else int(variant)
+    _check("chain_convN", lib().chain_convN_variant(_ptr(x), ctypes.byref(sh), n, wp, bp, ap, kp, _ptr(out), v,
+                                                    _stream(x)))
     return out
 
 

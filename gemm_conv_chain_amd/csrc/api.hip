@@ -22,6 +22,8 @@ hipError_t run_chain_conv2_3x3(const half_t* x, const half_t* w0, const half_t* 
                                const half_t* b1, half_t* y, int NB, int H, int W, int C, int K0, int K1, int waves,
                                int stages, hipStream_t st);
 bool conv2_pipe_fits(int W, int C, int K0, int K1);
+hipError_t run_chain_conv3_pipe(const half_t* x, const half_t* const* w, const half_t* const* b, const int* act,
+                                half_t* y, int NB, int H, int W, int K2, hipStream_t st);
 hipError_t run_chain_conv2_pipe(const half_t* x, const half_t* w0, const half_t* b0, int act, const half_t* w1,
                                 const half_t* b1, half_t* y, int NB, int H, int W, int K1, hipStream_t st);
 hipError_t run_chain_convN_3x3(const half_t* x, int nst, const half_t* const* w, const half_t* const* b,
@@ -748,10 +750,11 @@ fc_status chain_conv2_tune(const fc_half* x, const fc_half* w0, const fc_half* b
                    best, st);
 }
 
-fc_status chain_convN(const fc_half* x, const fc_conv_shape* shape0, int32_t nstages, const fc_half* const* w,
-                      const fc_half* const* b, const fc_act* act, const int32_t* k, fc_half* y, void* stream)
+// shape rules of chain_convN: widths[0..nstages] filled, *pipe_ok = the
+// pipelined form applies
+static fc_status check_convN_shape(const fc_conv_shape* shape0, int32_t nstages, const int32_t* k, int* widths,
+                                   bool* pipe_ok)
 {
-    if (!w || !act || !k) return fail(FC_E_NULL, "w, act and k are required");
     if (nstages < 3 || nstages > 4)
         return fail(FC_E_UNSUPPORTED, "nstages=%d: chain_convN runs 3 or 4 stages (chain_conv2 runs 2)", (int)nstages);
     fc_status s = check_conv(shape0, 128);
@@ -759,6 +762,23 @@ fc_status chain_convN(const fc_half* x, const fc_conv_shape* shape0, int32_t nst
     if (k[0] != shape0->k) return fail(FC_E_SHAPE, "k[0]=%d must equal shape0->k=%d", (int)k[0], (int)shape0->k);
     for (int i = 1; i < nstages; ++i)
         if (k[i] <= 0 || k[i] % 8) return fail(FC_E_SHAPE, "k[%d]=%d must be a positive multiple of 8", i, (int)k[i]);
+    widths[0] = 9 * shape0->c;
+    for (int i = 0; i < nstages; ++i) widths[i + 1] = k[i];
+    *pipe_ok = nstages == 3 && k[1] == 64 && fc::conv2_pipe_fits(shape0->w, shape0->c, shape0->k, k[2]);
+    return FC_OK;
+}
+
+fc_status chain_convN_variant(const fc_half* x, const fc_conv_shape* shape0, int32_t nstages, const fc_half* const* w,
+                              const fc_half* const* b, const fc_act* act, const int32_t* k, fc_half* y,
+                              fc_variant variant, void* stream)
+{
+    if (variant != FC_VARIANT_AUTO && variant != FC_VARIANT_RF && variant != FC_VARIANT_PIPE)
+        return fail(FC_E_ARG, "variant=%d: the conv chain runs FC_VARIANT_AUTO, _RF or _PIPE", (int)variant);
+    if (!w || !act || !k) return fail(FC_E_NULL, "w, act and k are required");
+    int widths[5];
+    bool pipe_ok = false;
+    fc_status s = check_convN_shape(shape0, nstages, k, widths, &pipe_ok);
+    if (s != FC_OK) return s;
     const long npix = (long)shape0->n * shape0->h * shape0->w;
     if (npix > 0 && (!x || !y)) return fail(FC_E_NULL, "x and y are required");
     if (!aligned16(x) || !aligned16(y)) return fail(FC_E_ALIGN, "tensor pointers must be 16-byte aligned");
@@ -775,15 +795,42 @@ fc_status chain_convN(const fc_half* x, const fc_conv_shape* shape0, int32_t nst
         bh[i] = H(bi);
         acts[i] = (int)act[i];
     }
-    int widths[5];
-    widths[0] = 9 * shape0->c;
-    for (int i = 0; i < nstages; ++i) widths[i + 1] = k[i];
-    if (!fc::gemmn_fits(nstages, widths))
+    if (variant == FC_VARIANT_PIPE && !pipe_ok)
+        return fail(FC_E_UNSUPPORTED, "the pipelined form takes 3 stages with c = 64, k = 64, 64, <= 256");
+    const bool use_pipe = variant == FC_VARIANT_PIPE || (variant == FC_VARIANT_AUTO && pipe_ok);
+    if (!use_pipe && !fc::gemmn_fits(nstages, widths))
         return fail(FC_E_UNSUPPORTED, "register residence: every intermediate width <= 128 and all weights within LDS");
     if (npix == 0) return ok();
+    if (use_pipe)
+        return hip_status(fc::run_chain_conv3_pipe(H(x), wh, bh, acts, Hm(y), shape0->n, shape0->h, shape0->w, k[2],
+                                                   (hipStream_t)stream),
+                          "chain_convN");
     return hip_status(fc::run_chain_convN_3x3(H(x), nstages, wh, bh, acts, widths, Hm(y), shape0->n, shape0->h,
                                               shape0->w, shape0->c, (hipStream_t)stream),
                       "chain_convN");
+}
+
+fc_status chain_convN_auto_variant(const fc_conv_shape* shape0, int32_t nstages, const int32_t* k, fc_variant* out)
+{
+    if (!k || !out) return fail(FC_E_NULL, "k and out are required");
+    int widths[5];
+    bool pipe_ok = false;
+    fc_status s = check_convN_shape(shape0, nstages, k, widths, &pipe_ok);
+    if (s != FC_OK) return s;
+    if (pipe_ok) {
+        *out = FC_VARIANT_PIPE;
+        return ok();
+    }
+    if (!fc::gemmn_fits(nstages, widths))
+        return fail(FC_E_UNSUPPORTED, "register residence: every intermediate width <= 128 and all weights within LDS");
+    *out = FC_VARIANT_RF;
+    return ok();
+}
+
+fc_status chain_convN(const fc_half* x, const fc_conv_shape* shape0, int32_t nstages, const fc_half* const* w,
+                      const fc_half* const* b, const fc_act* act, const int32_t* k, fc_half* y, void* stream)
+{
+    return chain_convN_variant(x, shape0, nstages, w, b, act, k, y, FC_VARIANT_AUTO, stream);
 }
 
 fc_status maxpool2x2(const fc_half* x, fc_half* y, uint8_t* argmax, int32_t n, int32_t h, int32_t w, int32_t c,

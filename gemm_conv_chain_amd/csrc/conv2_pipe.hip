@@ -55,15 +55,20 @@ constexpr int CP_DMA_PER_PART = CP_SLOTS / 64;      // 1 KiB DMA instructions pe
 constexpr int CP_BUF_BYTES = 4 * CP_PART_BYTES;     // one tile's halo (2 row tiles x 2 halves)
 constexpr int CP_H_BYTES = 64 * CP_K0 * 2;          // one tile's intermediate [64][64] fp16
 constexpr int CP_OST_BYTES = 64 * 64 * 2;           // per group-1 wave output staging [64][64] fp16
+// LDS: the halo ring, H (and H2, the middle 1x1 conv's output, with MID)
+// double-buffered, the output staging, the biases b0 | bm | b1
 constexpr int CP_H_OFF = CP_NBUF * CP_BUF_BYTES;
-constexpr int CP_OST_OFF = CP_H_OFF + 2 * CP_H_BYTES;
-constexpr int CP_BIAS_OFF = CP_OST_OFF + 4 * CP_OST_BYTES;
-constexpr int CP_LDS = CP_BIAS_OFF + (CP_K0 + CP_K1P) * 4;   // 109 KiB
+constexpr int cp_ost_off(int mid) { return CP_H_OFF + 2 * CP_H_BYTES * (1 + mid); }
+constexpr int cp_bias_off(int mid) { return cp_ost_off(mid) + 4 * CP_OST_BYTES; }
+constexpr int cp_lds(int mid) { return cp_bias_off(mid) + (2 * CP_K0 + CP_K1P) * 4; }   // 110 / 126 KiB
 constexpr int CP_W0_BYTES = 9 * CP_C * CP_K0 * 2;            // 72 KiB, staged once at the start
 constexpr int CP_W1_BYTES = CP_K0 * CP_K1P * 2;              // 32 KiB
+constexpr int CP_WM_BYTES = CP_K0 * CP_K0 * 2;               // 8 KiB (MID)
 constexpr int CP_APD = 2;                                    // A-operand prefetch distance (k-steps)
 static_assert(CP_SLOTS % 64 == 0, "whole DMA instructions per part");
-static_assert(CP_LDS <= 160 * 1024 && CP_W0_BYTES + CP_W1_BYTES <= CP_LDS, "LDS budget");
+static_assert(cp_lds(1) <= 160 * 1024 && CP_W0_BYTES + CP_W1_BYTES <= cp_bias_off(0) &&
+                  CP_W0_BYTES + CP_W1_BYTES + CP_WM_BYTES <= cp_bias_off(1),
+              "LDS budget");
 
 // slot swizzle of halo pixel (hr, hc): 16 lanes of a 16-byte read land on 16
 // different bank groups (rows r and r + 1 and columns with each hc % 4)
@@ -77,6 +82,9 @@ struct PipeArgs {
     const half_t* b0;   // [64] or null
     const half_t* w1;   // [64, K1]
     const half_t* b1;   // [K1] or null
+    const half_t* wm;   // middle 1x1 conv [64, 64] (MID)
+    const half_t* bm;   // [64] or null (MID)
+    int act1, act2;     // activations after the middle (MID) and the last 1x1 conv
     half_t* y;          // [NB, H, W, K1]
     int NB, H, W, K1;
     int P2, JB;         // row pairs ceil(H / 2), column blocks ceil(W / 16)
@@ -87,10 +95,14 @@ struct PipeArgs {
 
 }  // namespace
 
-template <int ACT>
+// MID = 1: a middle 1x1 conv 64 -> 64 between the two, run by group 0 one
+// phase after its 3x3 conv of the same tile (H -> H2 in LDS); group 1 then
+// reads H2, one phase later still.
+template <int ACT, int MID>
 __global__ __launch_bounds__(CP_THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void k_conv2_pipe(PipeArgs a)
 {
+    constexpr int CP_OST_OFF = cp_ost_off(MID), CP_BIAS_OFF = cp_bias_off(MID), CP_LDS = cp_lds(MID);
     constexpr int NST = 9 * CP_C / 16;   // k-steps of the 3x3 conv
     extern __shared__ __align__(16) char smem[];
     typedef FC_LDS char lds_char;
@@ -143,14 +155,21 @@ void k_conv2_pipe(PipeArgs a)
     }
     stage_natural<8>(a.w0, 9 * CP_C, CP_K0, CP_K0, 9 * CP_C, CP_K0, W0n, tid, CP_THREADS);
     stage_natural<8>(a.w1, CP_K0, a.K1, a.K1, CP_K0, CP_K1P, W1n, tid, CP_THREADS);
+    WTile Wmn;
+    Wmn.p = (lds_half*)(lds + CP_W0_BYTES + CP_W1_BYTES);
+    Wmn.ld = wtile_ld(CP_K0);
+    Wmn.swz = wtile_swz(CP_K0);
+    if constexpr (MID > 0) stage_natural<8>(a.wm, CP_K0, CP_K0, CP_K0, CP_K0, CP_K0, Wmn, tid, CP_THREADS);
     __syncthreads();
-    lds_float* const bsl = (lds_float*)(lds + CP_BIAS_OFF);   // b0 [64] then b1 [K1P] (past the weights)
-    for (int i = tid; i < CP_K0 + CP_K1P; i += CP_THREADS) {
+    lds_float* const bsl = (lds_float*)(lds + CP_BIAS_OFF);   // b0 [64], bm [64], b1 [K1P] (past the weights)
+    for (int i = tid; i < 2 * CP_K0 + CP_K1P; i += CP_THREADS) {
         float v = 0.0f;
         if (i < CP_K0) {
             if (a.b0) v = (float)a.b0[i];
-        } else if (a.b1 && i - CP_K0 < a.K1) {
-            v = (float)a.b1[i - CP_K0];
+        } else if (i < 2 * CP_K0) {
+            if (MID > 0 && a.bm) v = (float)a.bm[i - CP_K0];
+        } else if (a.b1 && i - 2 * CP_K0 < a.K1) {
+            v = (float)a.b1[i - 2 * CP_K0];
         }
         bsl[i] = v;
     }
@@ -166,8 +185,11 @@ void k_conv2_pipe(PipeArgs a)
     };
     auto buf_of = [&](int j) -> lds_char* { return lds + (j % CP_NBUF) * CP_BUF_BYTES; };
     auto h_of = [&](int j) -> lds_half* { return (lds_half*)(lds + CP_H_OFF + (j & 1) * CP_H_BYTES); };
+    auto h2_of = [&](int j) -> lds_half* { return (lds_half*)(lds + CP_H_OFF + (2 + (j & 1)) * CP_H_BYTES); };
 
-    const int nph = ntiles + 1;   // phase k: group 0 on tile k, group 1 on tile k - 1
+    // phase k: group 0 on tile k (and, MID, on tile k - 1's middle conv),
+    // group 1 on tile k - 1 - MID
+    const int nph = ntiles + 1 + MID;
     if (wg == 0) {
         // ---- group 0: halo DMA, the 3x3 conv, H to LDS
         half8 wf[NST];   // W0 rows 16 st + 8 hh + [0, 8), column 32 (wq % 2) + lr
@@ -175,6 +197,13 @@ void k_conv2_pipe(PipeArgs a)
         for (int st = 0; st < NST; ++st)
             wf[st] = frag_tr_at(W0n.p + frag_lane_off(W0n, 32 * (wq & 1), lane) + (16 * st + 8 * hh) * W0n.ld,
                                 4 * W0n.ld);
+        half8 wmf[MID > 0 ? 4 : 1];   // Wm rows 16 s + 8 hh + [0, 8), column 32 (wq % 2) + lr
+        if constexpr (MID > 0) {
+#pragma unroll
+            for (int s2 = 0; s2 < 4; ++s2)
+                wmf[s2] = frag_tr_at(Wmn.p + frag_lane_off(Wmn, 32 * (wq & 1), lane) + (16 * s2 + 8 * hh) * Wmn.ld,
+                                     4 * Wmn.ld);
+        }
         release_weights();
         const int W = a.W;
         unsigned dma_off[CP_DMA_PER_PART];   // per-lane offsets from the halo origin
@@ -275,6 +304,33 @@ void k_conv2_pipe(PipeArgs a)
                     *reinterpret_cast<lds_half4*>(hs + cp_hoff(r, c0 >> 3) + (c0 & 7)) = o;
                 }
             }
+            if constexpr (MID > 0) {
+                // the middle 1x1 conv of tile k - 1 (its H published by the last
+                // barrier): channels 32 ct.. of row tile u, + bm, act1, fp16 -> H2
+                if (k >= 1 && k - 1 < ntiles && u < tile_nrt(k - 1)) {
+                    const lds_half* const hs = h_of(k - 1);
+                    floatx16 am = zero16();
+#pragma unroll
+                    for (int s2 = 0; s2 < 4; ++s2) {
+                        const half8 hp = *reinterpret_cast<const lds_half8*>(hs + cp_hoff(32 * u + lr, 2 * s2 + hh));
+                        am = mfma32x32x16(wmf[s2], hp, am);
+                    }
+                    lds_half* const h2 = h2_of(k - 1);
+                    typedef FC_LDS half4 lds_half4;
+                    typedef FC_LDS floatx4 lds_floatx4;
+                    act_dispatch(a.act1, [&](auto act1) {
+#pragma unroll
+                        for (int g = 0; g < 4; ++g) {
+                            const int c0 = 32 * ct + 8 * g + 4 * hh;
+                            const floatx4 bk = *reinterpret_cast<const lds_floatx4*>(bsl + CP_K0 + c0);
+                            half4 o;
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) o[e] = (half_t)act1.f(am[4 * g + e] + bk[e]);
+                            *reinterpret_cast<lds_half4*>(h2 + cp_hoff(32 * u + lr, c0 >> 3) + (c0 & 7)) = o;
+                        }
+                    });
+                }
+            }
             if (dma_tile(k + 2)) vm_wait<CP_DMA_PER_PART>();   // tile k + 1's part has landed
             else vm_wait<0>();
             __syncthreads();
@@ -293,10 +349,10 @@ void k_conv2_pipe(PipeArgs a)
         const int K1 = a.K1;
         __syncthreads();   // (group 0's first barrier: tile 0's halo visible)
         for (int k = 0; k < nph; ++k) {
-            const int j = k - 1;
+            const int j = k - 1 - MID;
             if (j >= 0) {
                 const int nrt = tile_nrt(j);
-                const lds_half* const hs = h_of(j);
+                const lds_half* const hs = MID > 0 ? h2_of(j) : h_of(j);
                 floatx16 acc[2][2];
 #pragma unroll
                 for (int s = 0; s < 4; ++s) {
@@ -314,20 +370,22 @@ void k_conv2_pipe(PipeArgs a)
                 // 8 g + 4 hh + [0, 4): + b1, fp16, 8 bytes to staging [pixel][64 channels]
                 typedef FC_LDS half4 lds_half4;
                 typedef FC_LDS floatx4 lds_floatx4;
+                act_dispatch(a.act2, [&](auto act2) {
 #pragma unroll
-                for (int t = 0; t < 2; ++t)
+                    for (int t = 0; t < 2; ++t)
 #pragma unroll
-                    for (int g = 0; g < 4; ++g) {
-                        const int cl = 32 * t + 8 * g + 4 * hh;
-                        const floatx4 bk = *reinterpret_cast<const lds_floatx4*>(bsl + CP_K0 + 64 * wq + cl);
+                        for (int g = 0; g < 4; ++g) {
+                            const int cl = 32 * t + 8 * g + 4 * hh;
+                            const floatx4 bk = *reinterpret_cast<const lds_floatx4*>(bsl + 2 * CP_K0 + 64 * wq + cl);
 #pragma unroll
-                        for (int uu = 0; uu < 2; ++uu) {
-                            half4 o;
+                            for (int uu = 0; uu < 2; ++uu) {
+                                half4 o;
 #pragma unroll
-                            for (int e = 0; e < 4; ++e) o[e] = (half_t)(acc[uu][t][4 * g + e] + bk[e]);
-                            *reinterpret_cast<lds_half4*>(ost + cp_hoff(32 * uu + lr, cl >> 3) + (cl & 7)) = o;
+                                for (int e = 0; e < 4; ++e) o[e] = (half_t)act2.f(acc[uu][t][4 * g + e] + bk[e]);
+                                *reinterpret_cast<lds_half4*>(ost + cp_hoff(32 * uu + lr, cl >> 3) + (cl & 7)) = o;
+                            }
                         }
-                    }
+                });
                 wave_lds_sync();
                 // stores: lane L takes 16 bytes (channels 64 wq + 8 (L % 8) + [0, 8))
                 // of rows L / 8 + 8 i; row r -> pixel of row tile r / 32
@@ -353,17 +411,28 @@ void k_conv2_pipe(PipeArgs a)
     }
 }
 
-template <int ACT>
+template <int ACT, int MID>
 static hipError_t launch_pipe(PipeArgs a, hipStream_t st)
 {
     static std::atomic<unsigned long long> lds_set{0};
-    hipError_t e = allow_full_lds((const void*)k_conv2_pipe<ACT>, &lds_set);
+    hipError_t e = allow_full_lds((const void*)k_conv2_pipe<ACT, MID>, &lds_set);
     if (e != hipSuccess) return e;
     long nb = device_cu_count();   // one block per CU
     if (nb > a.nrt) nb = a.nrt;
     a.nblocks = (int)nb;
-    hipLaunchKernelGGL((k_conv2_pipe<ACT>), dim3((unsigned)nb), dim3(CP_THREADS), (size_t)CP_LDS, st, a);
+    hipLaunchKernelGGL((k_conv2_pipe<ACT, MID>), dim3((unsigned)nb), dim3(CP_THREADS), (size_t)cp_lds(MID), st, a);
     return hipGetLastError();
+}
+
+template <int MID>
+static hipError_t launch_pipe_act(int act, const PipeArgs& a, hipStream_t st)
+{
+    switch (act) {
+    case ACT_RELU: return launch_pipe<ACT_RELU, MID>(a, st);
+    case ACT_GELU_TANH: return launch_pipe<ACT_GELU_TANH, MID>(a, st);
+    case ACT_HARDSWISH: return launch_pipe<ACT_HARDSWISH, MID>(a, st);
+    default: return launch_pipe<ACT_NONE, MID>(a, st);
+    }
 }
 
 // The conv3x3 -> conv1x1 shapes this kernel takes (3x3/s1/p1 checked by the
@@ -374,25 +443,41 @@ bool conv2_pipe_fits(int W, int C, int K0, int K1)
     return C == CP_C && K0 == CP_K0 && K1 > 0 && K1 <= CP_K1P && K1 % 8 == 0 && (long)W * C < (1L << 27);
 }
 
-hipError_t run_chain_conv2_pipe(const half_t* x, const half_t* w0, const half_t* b0, int act, const half_t* w1,
-                                const half_t* b1, half_t* y, int NB, int H, int W, int K1, hipStream_t st)
+static PipeArgs pipe_args(const half_t* x, const half_t* w0, const half_t* b0, const half_t* w1, const half_t* b1,
+                          half_t* y, int NB, int H, int W, int K1)
 {
-    PipeArgs a;
+    PipeArgs a{};
     a.x = x; a.w0 = w0; a.b0 = b0; a.w1 = w1; a.b1 = b1; a.y = y;
     a.NB = NB; a.H = H; a.W = W; a.K1 = K1;
+    a.act1 = ACT_NONE; a.act2 = ACT_NONE;
     a.P2 = (H + 1) / 2;
     a.JB = (W + 15) / 16;
     a.nrt = (long)NB * a.P2 * a.JB;
-    if (a.nrt == 0) return hipSuccess;
     a.nblocks = 1;
-    a.fjb = FastDiv::make((unsigned)a.JB);
-    a.fp2 = FastDiv::make((unsigned)a.P2);
-    switch (act) {
-    case ACT_RELU: return launch_pipe<ACT_RELU>(a, st);
-    case ACT_GELU_TANH: return launch_pipe<ACT_GELU_TANH>(a, st);
-    case ACT_HARDSWISH: return launch_pipe<ACT_HARDSWISH>(a, st);
-    default: return launch_pipe<ACT_NONE>(a, st);
+    if (a.nrt > 0) {
+        a.fjb = FastDiv::make((unsigned)a.JB);
+        a.fp2 = FastDiv::make((unsigned)a.P2);
     }
+    return a;
+}
+
+hipError_t run_chain_conv2_pipe(const half_t* x, const half_t* w0, const half_t* b0, int act, const half_t* w1,
+                                const half_t* b1, half_t* y, int NB, int H, int W, int K1, hipStream_t st)
+{
+    const PipeArgs a = pipe_args(x, w0, b0, w1, b1, y, NB, H, W, K1);
+    if (a.nrt == 0) return hipSuccess;
+    return launch_pipe_act<0>(act, a, st);
+}
+
+// conv3x3 (64 -> 64, act0) -> conv1x1 (64 -> 64, act1) -> conv1x1 (64 -> K2, act2)
+hipError_t run_chain_conv3_pipe(const half_t* x, const half_t* const* w, const half_t* const* b, const int* act,
+                                half_t* y, int NB, int H, int W, int K2, hipStream_t st)
+{
+    PipeArgs a = pipe_args(x, w[0], b[0], w[2], b[2], y, NB, H, W, K2);
+    if (a.nrt == 0) return hipSuccess;
+    a.wm = w[1]; a.bm = b[1];
+    a.act1 = act[1]; a.act2 = act[2];
+    return launch_pipe_act<1>(act[0], a, st);
 }
 
 }  // namespace fc

@@ -116,8 +116,8 @@ def pmc(d, workload, json_path=None):
         import bench
         fused = {"b2b_gemm_tiny": "k_chain_rf", "b2b_gemm_rf": "k_chain_rf", "b2b_gemm_lds": "k_gemm_lds<4, true",
                  "b2b_gemm_lds@stream": "k_chain_stream", "gemm3_rf": "k_chain_rf",
-                 "conv3x3_conv1x1": "k_conv2_pipe", "conv3x3_conv1x1@rf": "k_chain_rf",
-                 "conv3x3_conv1x1x2": "k_chain_rf",
+                 "conv3x3_conv1x1": "k_conv2_pipe<1, 0>", "conv3x3_conv1x1@rf": "k_chain_rf",
+                 "conv3x3_conv1x1x2": "k_conv2_pipe<1, 1>", "conv3x3_conv1x1x2@rf": "k_chain_rf",
                  # pooled convs: the register-weights kernel is the automatic choice at these shapes
                  "conv3x3_relu_maxpool": "k_conv_pool_wr", "conv3x3_bn_relu_maxpool": "k_conv_pool_wr",
                  "conv3x3_relu_avgpool": "k_conv_pool_wr",

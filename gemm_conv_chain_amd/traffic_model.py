@@ -247,13 +247,14 @@ def conv2_rf(n, h, w, c, k0, k1, cus=256, k_more=()):
     return r
 
 
-def conv2_pipe(n, h, w, c, k0, k1, cus=256):
+def conv2_pipe(n, h, w, c, k0, k1, cus=256, mid=0):
     """conv3x3 -> conv1x1 in two pipelined wave groups (k_conv2_pipe): row
     tile = 2 image rows x 16 columns (halo 4 x 18 pixels), tiles of 2 row
     tiles taken in order (odd blocks walk their range backward), one block per
     CU, both weight matrices read once per block; LDS: three 20 KiB halo
     buffers, two 8 KiB intermediate tiles, four 8 KiB output staging tiles and
-    the biases."""
+    the biases.  mid > 0: a middle 1x1 conv k0 -> mid (its weights resident
+    too, two more 8 KiB intermediate tiles)."""
     P2, JB = -(-h // 2), -(-w // 16)
     nrt = n * P2 * JB
     nb = min(cus, nrt)
@@ -268,9 +269,9 @@ def conv2_pipe(n, h, w, c, k0, k1, cus=256):
         q, jb = divmod(rt, JB)
         img, i = divmod(q, P2)
         return _halo_pixels(img, 2 * i - 1, 16 * jb - 1, 4, 18, h, w)
-    wb = 2 * (9 * c * k0 + k0 * k1)
+    wb = 2 * (9 * c * k0 + (k0 * mid + mid * k1 if mid else k0 * k1))
     out = 2 * n * h * w * k1
-    r = _run(bt, nb, wb, c, pix, out, 3 * 20480 + 2 * 8192 + 4 * 8192 + 4 * (64 + 256))
+    r = _run(bt, nb, wb, c, pix, out, 3 * 20480 + (4 if mid else 2) * 8192 + 4 * 8192 + 4 * (128 + 256))
     r.update(read_algorithmic=2 * n * h * w * c + wb, kernel="k_conv2_pipe", tiles=nrt, blocks=nb)
     return r
 
@@ -324,6 +325,10 @@ def for_workload(spec: dict, variant: str | None = None, cus: int = 256, argmax:
         return conv2_rf(spec["n"], spec["h"], spec["w"], spec["c"], spec["k0"], spec["k1"], cus)
     if kind == "convN":
         ks = spec["ks"]
+        if (variant != "rf" and len(ks) == 3 and spec["c"] == 64 and ks[0] == 64 and ks[1] == 64
+                and ks[2] <= 256):
+            r = conv2_pipe(spec["n"], spec["h"], spec["w"], spec["c"], ks[0], ks[2], cus, mid=ks[1])
+            return r
         return conv2_rf(spec["n"], spec["h"], spec["w"], spec["c"], ks[0], ks[1], cus, ks[2:])
     if kind == "conv_pool":
         n, h, w, c, k = spec["n"], spec["h"], spec["w"], spec["cpad"], spec["k"]

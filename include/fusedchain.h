@@ -79,7 +79,7 @@ typedef enum {
     FC_VARIANT_RF = 1,
     FC_VARIANT_LDS = 2,
     FC_VARIANT_STREAM = 3,
-    FC_VARIANT_PIPE = 4   /* conv3x3 -> conv1x1 only (chain_conv2_variant) */
+    FC_VARIANT_PIPE = 4   /* conv3x3 -> conv1x1 (-> conv1x1) only: chain_conv2_variant, chain_convN_variant */
 } fc_variant;
 
 /* Kernel forms of the conv + activation + 2x2 pool chain (chain_conv_pool_ex).
@@ -391,13 +391,33 @@ fc_status chain_conv2_tune(const fc_half *x, const fc_half *w0, const fc_half *b
  * shape0->k.  nstages is 3 or 4 (two stages: chain_conv2).  shape0 follows
  * chain_conv_pool's rules (3x3, stride 1, pad 1, c % 8 == 0, k[0] <= 128);
  * k[1 .. nstages-2] <= 128 and all weights must fit in LDS together, else
- * FC_E_UNSUPPORTED.  b or b[i] may be NULL.  w, b, act and k are host
+ * FC_E_UNSUPPORTED -- except three stages with c = 64 and k = {64, 64, <= 256},
+ * which run the pipelined form (chain_convN_variant, FC_VARIANT_PIPE) and may
+ * exceed that LDS rule.  b or b[i] may be NULL.  w, b, act and k are host
  * arrays read during the call; the tensors are device pointers owned by the
  * caller.  An empty batch is a no-op.
  */
 fc_status chain_convN(const fc_half *x, const fc_conv_shape *shape0, int32_t nstages,
                       const fc_half *const *w, const fc_half *const *b, const fc_act *act,
                       const int32_t *k, fc_half *y, void *stream);
+
+/* chain_convN_variant -- chain_convN with the kernel form chosen by the caller:
+ * FC_VARIANT_AUTO (the pipelined form where it applies, else the register-
+ * resident one), FC_VARIANT_RF (the register-resident chain, k_chain_rf with
+ * the conv loader: every shape chain_convN takes) or FC_VARIANT_PIPE (three
+ * stages only, c = 64, k = {64, 64, <= 256}, w * c < 2^27: the two pipelined
+ * wave groups of chain_conv2's FC_VARIANT_PIPE, the middle 1x1 conv run by the
+ * 3x3 conv's group one tile behind; FC_E_UNSUPPORTED outside those shapes).
+ * Other variants -> FC_E_ARG; errors otherwise as chain_convN. */
+fc_status chain_convN_variant(const fc_half *x, const fc_conv_shape *shape0, int32_t nstages,
+                              const fc_half *const *w, const fc_half *const *b, const fc_act *act,
+                              const int32_t *k, fc_half *y, fc_variant variant, void *stream);
+
+/* The variant chain_convN runs for this shape: FC_VARIANT_PIPE where the
+ * pipelined form applies, else FC_VARIANT_RF.  Host only, launches nothing;
+ * shape errors as chain_convN (FC_E_NULL for a NULL k or out). */
+fc_status chain_convN_auto_variant(const fc_conv_shape *shape0, int32_t nstages, const int32_t *k,
+                                   fc_variant *out);
 
 /* ---- unfused single-operator kernels (the two-kernel baselines) ---- */
 

@@ -27,7 +27,7 @@ def test_exports_every_declared_symbol(L):
               "conv_bias_act", "maxpool2x2", "pad_channels", "fc_abi_version", "fc_status_str", "fc_last_error",
               "chain_gemm2_tune", "chain_gemm2_auto_variant", "fc_tune_clear", "chain_convN", "chain_conv_bn_pool", "fc_probe_mfma", "chain_conv_pool_ex", "chain_gemm2_ex",
               "chain_gemm2_tune_ex", "chain_gemm2_auto_config", "chain_conv_pool_tune", "chain_conv_pool_auto_config",
-              "chain_conv2_variant", "chain_conv2_ex", "chain_conv2_tune", "chain_conv2_auto_config"):
+              "chain_conv2_variant", "chain_convN_variant", "chain_conv2_ex", "chain_conv2_tune", "chain_conv2_auto_config"):
         assert n in names
     for n in names:
         assert hasattr(L, n), n
@@ -285,6 +285,28 @@ def test_chain_convN_validation(L):
     assert cn(k=(64, 136, 128)) == E_UNSUP    # intermediate wider than 128: not register-resident
     assert cn(shape=fc.ConvShape(0, 8, 8, 48, 64, 3, 3, 1, 1)) == OK        # c % 8 == 0 is enough
     assert cn(shape=fc.ConvShape(0, 8, 8, 44, 64, 3, 3, 1, 1)) == E_SHAPE
+    # three stages at c = 64, k = {64, 64, <= 256} run the pipelined form,
+    # which is not bound by the register-residence LDS rule
+    assert cn(k=(64, 64, 256), shape=fc.ConvShape(0, 8, 8, 64, 64, 3, 3, 1, 1)) == OK
+
+    def cv(v, n=3, k=(64, 64, 128), shape=fc.ConvShape(0, 8, 8, 64, 64, 3, 3, 1, 1)):
+        kp = (C.c_int32 * 4)(*(list(k) + [0] * (4 - len(k))))
+        wp = (C.c_void_p * 4)(P, P, P, P)
+        ap = (C.c_int * 4)(1, 1, 0, 0)
+        return L.chain_convN_variant(P, C.byref(shape), n, wp, None, ap, kp, P2, v, None)
+    AUTO, RF, PIPE = 0, fc.VARIANT["rf"], fc.VARIANT["pipe"]
+    assert cv(AUTO) == OK and cv(RF) == OK and cv(PIPE) == OK
+    for v in (fc.VARIANT["lds"], fc.VARIANT["stream"], 5, -1):
+        assert cv(v) == E_ARG
+    assert cv(PIPE, k=(64, 64, 264)) == E_UNSUP                 # k[2] > 256
+    assert cv(PIPE, k=(64, 64, 256)) == OK
+    assert cv(RF, k=(64, 64, 256)) == OK
+    assert cv(RF, k=(64, 136, 128)) == E_UNSUP                  # intermediate wider than 128
+    assert cv(PIPE, k=(64, 32, 128)) == E_UNSUP                 # the middle stage must be 64 wide
+    assert cv(PIPE, n=4, k=(64, 64, 64, 64)) == E_UNSUP
+    assert cv(RF, n=4, k=(64, 64, 64, 64)) == OK
+    assert cv(PIPE, k=(96, 64, 128), shape=fc.ConvShape(0, 8, 8, 64, 96, 3, 3, 1, 1)) == E_UNSUP
+    assert cv(PIPE, shape=fc.ConvShape(0, 8, 8, 32, 64, 3, 3, 1, 1)) == E_UNSUP
 
 
 def test_chain_conv_bn_pool_validation(L):

@@ -280,6 +280,48 @@ def test_chain_convN_unscaled_zero_bias(fc):
     assert_close(y, ref, "convN unscaled")
 
 
+@pytest.mark.parametrize("n,h,w,k2", [(1, 1, 1, 8), (1, 2, 17, 256), (3, 5, 7, 40), (2, 33, 35, 256),
+                                       (1, 16, 16, 200), (4, 28, 28, 64), (40, 9, 10, 128)])
+def test_convN_pipe(fc, n, h, w, k2):
+    # three stages in the pipelined form: 1x1 images, ragged tile tails,
+    # block counts above and below the CU count, odd and wide last stages
+    d = inputs.convN_inputs(n, h, w, 64, [64, 64, k2], seed=h * w + k2)
+    acts = ["relu", "relu", "none"]
+    print("case convN pipe", (n, h, w, k2), flush=True)
+    args = (dev(d["x"]), [dev(x) for x in d["ws"]], [dev(b) for b in d["bs"]], acts)
+    y = to_np(fc.chain_convN(*args, variant="pipe"))
+    ref = oracle.chain_convN(d["x"], d["ws"], d["bs"], [ACTS[a] for a in acts])
+    check_full(y, ref, "convN pipe %s" % ((n, h, w, k2),))
+    if k2 <= 128:
+        rf = to_np(fc.chain_convN(*args, variant="rf"))
+        # the same fp16 intermediates; the two forms differ only in fp32 summation order
+        assert np.abs(y.astype(np.float64) - rf).max() <= 4 * np.abs(ref).max() * 2.0 ** -10 + 1e-3
+
+
+@pytest.mark.parametrize("acts", [["gelu_tanh", "hardswish", "none"], ["none", "none", "relu"],
+                                  ["hardswish", "gelu_tanh", "gelu_tanh"]])
+def test_convN_pipe_acts(fc, acts):
+    d = inputs.convN_inputs(2, 9, 20, 64, [64, 64, 96], seed=43)
+    print("case convN pipe", acts, flush=True)
+    y = to_np(fc.chain_convN(dev(d["x"]), [dev(x) for x in d["ws"]], [dev(b) for b in d["bs"]], acts,
+                             variant="pipe"))
+    ref = oracle.chain_convN(d["x"], d["ws"], d["bs"], [ACTS[a] for a in acts])
+    check_full(y, ref, "convN pipe %s" % (acts,))
+
+
+def test_convN_pipe_unscaled_zero_bias(fc):
+    # unit-variance weights and zero biases: a dropped k chunk or a swapped
+    # middle stage does not hide under the bias
+    d = inputs.convN_inputs(2, 20, 22, 64, [64, 64, 96], seed=47)
+    ws = [(x.astype(np.float32) * 4).astype(np.float16) for x in d["ws"]]
+    bs = [np.zeros_like(b) for b in d["bs"]]
+    acts = ["relu", "relu", "none"]
+    print("case convN pipe unscaled", flush=True)
+    y = to_np(fc.chain_convN(dev(d["x"]), [dev(x) for x in ws], [dev(b) for b in bs], acts, variant="pipe"))
+    ref = oracle.chain_convN(d["x"], ws, bs, [ACTS[a] for a in acts])
+    assert_close(y, ref, "convN pipe unscaled")
+
+
 @pytest.mark.slow
 def test_convN_full_size(fc):
     spec, d = inputs.workload("conv3x3_conv1x1x2")
