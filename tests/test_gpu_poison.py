@@ -149,3 +149,18 @@ def test_poison_conv_bias_act_and_conv2(fc):
         prod, pois = both(fc, lambda: fc.chain_conv2(x, w0, b0, w1, b1, act="none", variant=variant, waves=waves))
         same_bits(prod, pois, "chain_conv2 " + variant)
         assert_close(pois[0], ref, "poison chain_conv2 " + variant)
+
+
+def test_poison_convN_pipe(fc):
+    # the three-stage pipelined form: H and H2 double-buffered, the halo ring
+    # reused every three tiles
+    ks = [64, 64, 192]
+    d = inputs.convN_inputs(2, 30, 34, 64, ks, seed=19)
+    x, ws, bs = dev(d["x"]), [dev(w) for w in d["ws"]], [dev(b) for b in d["bs"]]
+    acts = ["relu", "gelu_tanh", "none"]
+    print("case poison chain_convN", flush=True)
+    ref = oracle.chain_convN(d["x"], d["ws"], d["bs"], [ACTS[a] for a in acts])
+    for variant in ("pipe", "rf"):
+        prod, pois = both(fc, lambda: fc.chain_convN(x, ws, bs, acts, variant=variant))
+        same_bits(prod, pois, "chain_convN " + variant)
+        assert_close(pois[0], ref, "poison chain_convN " + variant)
