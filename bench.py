@@ -569,10 +569,10 @@ def measure(torch, fc, prob, steps, warmup, unfused=True, warm=True):
 
 # The other configurations, measured in the same run beside the headline one
 # (one record each; the two-GEMM LDS-resident shape under each kernel variant
-# and under the profiler's choice).
+# and under the profiler's choice, the three-stage GEMM and conv chains).
 SIDE_CONFIGS = [("b2b_gemm_tiny", None), ("b2b_gemm_rf", None), ("b2b_gemm_lds", None), ("b2b_gemm_lds", "stream"),
-                ("b2b_gemm_lds", "tuned"), ("conv3x3_conv1x1", None), ("conv3x3_conv1x1", "tuned"),
-                ("conv3x3_relu_maxpool", "winograd")]
+                ("b2b_gemm_lds", "tuned"), ("gemm3_rf", None), ("conv3x3_conv1x1", None), ("conv3x3_conv1x1", "tuned"),
+                ("conv3x3_conv1x1x2", None), ("conv3x3_relu_maxpool", "winograd")]
 WORKLOADS = ["b2b_gemm_tiny", "b2b_gemm_rf", "b2b_gemm_lds", "gemm3_rf", "conv3x3_conv1x1", "conv3x3_conv1x1x2",
              "conv3x3_relu_maxpool", "conv3x3_bn_relu_maxpool", "conv3x3_relu_avgpool"]
 
