@@ -27,7 +27,7 @@ def test_exports_every_declared_symbol(L):
               "conv_bias_act", "maxpool2x2", "pad_channels", "fc_abi_version", "fc_status_str", "fc_last_error",
               "chain_gemm2_tune", "chain_gemm2_auto_variant", "fc_tune_clear", "chain_convN", "chain_conv_bn_pool", "fc_probe_mfma", "chain_conv_pool_ex", "chain_gemm2_ex",
               "chain_gemm2_tune_ex", "chain_gemm2_auto_config", "chain_conv_pool_tune", "chain_conv_pool_auto_config",
-              "chain_conv2_variant", "chain_convN_variant", "chain_conv2_ex", "chain_conv2_tune", "chain_conv2_auto_config"):
+              "chain_conv2_variant", "chain_convN_variant", "chain_convN_auto_variant", "chain_conv2_ex", "chain_conv2_tune", "chain_conv2_auto_config"):
         assert n in names
     for n in names:
         assert hasattr(L, n), n
@@ -307,6 +307,35 @@ def test_chain_convN_validation(L):
     assert cv(RF, n=4, k=(64, 64, 64, 64)) == OK
     assert cv(PIPE, k=(96, 64, 128), shape=fc.ConvShape(0, 8, 8, 64, 96, 3, 3, 1, 1)) == E_UNSUP
     assert cv(PIPE, shape=fc.ConvShape(0, 8, 8, 32, 64, 3, 3, 1, 1)) == E_UNSUP
+
+
+def test_chain_convN_auto_variant(L):
+    import ctypes as C
+    RF, PIPE = fc.VARIANT["rf"], fc.VARIANT["pipe"]
+
+    def av(shape, ks):
+        kp = (C.c_int32 * len(ks))(*ks)
+        v = C.c_int(-1)
+        r = L.chain_convN_auto_variant(C.byref(shape), len(ks), kp, C.byref(v))
+        return r, v.value
+    sh = lambda c, k: fc.ConvShape(2, 8, 8, c, k, 3, 3, 1, 1)
+    assert av(sh(64, 64), [64, 64, 256]) == (OK, PIPE)
+    assert av(sh(64, 64), [64, 64, 8]) == (OK, PIPE)
+    assert av(sh(64, 64), [64, 32, 128]) == (OK, RF)        # middle stage not 64 wide
+    assert av(sh(64, 64), [64, 64, 64, 64]) == (OK, RF)     # four stages
+    assert av(sh(32, 64), [64, 64, 128]) == (OK, RF)        # c != 64
+    assert av(sh(64, 32), [32, 64, 128]) == (OK, RF)        # k[0] != 64
+    assert av(sh(64, 64), [64, 136, 128])[0] == E_UNSUP     # neither form takes it
+    assert av(sh(64, 64), [72, 64, 128])[0] == E_SHAPE      # k[0] != shape.k
+    assert av(sh(64, 64), [64, 64])[0] == E_UNSUP           # two stages: chain_conv2
+    kp = (C.c_int32 * 3)(64, 64, 64)
+    v = C.c_int(0)
+    assert L.chain_convN_auto_variant(None, 3, kp, C.byref(v)) == E_NULL
+    assert L.chain_convN_auto_variant(C.byref(sh(64, 64)), 3, None, C.byref(v)) == E_NULL
+    assert L.chain_convN_auto_variant(C.byref(sh(64, 64)), 3, kp, None) == E_NULL
+    # the binding's helper
+    assert fc.convN_auto_variant(32, 56, 56, 64, [64, 64, 256]) == "pipe"
+    assert fc.convN_auto_variant(32, 56, 56, 64, [64, 48, 96]) == "rf"
 
 
 def test_chain_conv_bn_pool_validation(L):
