@@ -1,6 +1,7 @@
 // conv2_pipe.hip -- conv3x3 (64 -> 64) + bias + activation -> conv1x1
 // (64 -> k1 <= 256) + bias, in two pipelined wave groups with the input halo
-// streamed into LDS.
+// streamed into LDS; optionally (MID) with a middle conv1x1 (64 -> 64) + bias
+// + activation between them.
 //
 // BOLT's persistent kernel fusion for a 3x3 -> 1x1 conv pair (BOLT notes,
 // "Persistent kernel (GEMM/Conv) fusion": the 1x1 conv is a GEMM over the
@@ -31,8 +32,11 @@
 //     chunks XOR-swizzled by row so the reads are conflict-free).  Bias,
 //     fp16, a per-wave LDS staging tile, and 16-byte stores of whole 128-byte
 //     runs of the output rows.
+//   * MID: group 0 also runs the middle conv1x1 of the tile it convolved one
+//     phase earlier (H -> H2, its 64 x 32 slice of the middle weights in 16
+//     more registers), and group 1 reads H2 one phase later still.
 //   * One barrier per phase: in phase k group 0 computes tile k (and requests
-//     the halo of tile k + 2), group 1 tile k - 1.  Each SIMD holds one wave of
+//     the halo of tile k + 2), group 1 tile k - 1 (k - 2 with MID).  Each SIMD holds one wave of
 //     each group, so the 3x3 conv's matrix work overlaps the 1x1 conv and the
 //     output stores (51 MB at the 32 x 56 x 56 x 256 workload: the stores set
 //     this chain's floor).
