@@ -322,6 +322,19 @@ def test_convN_pipe_unscaled_zero_bias(fc):
     assert_close(y, ref, "convN pipe unscaled")
 
 
+def test_convN_pipe_identity_middle_is_conv2(fc):
+    # an identity middle 1x1 stage (zero bias, no activation) passes the fp16
+    # intermediate through exactly (one nonzero product per output), so the
+    # three-stage pipelined kernel must equal the two-stage one bit for bit
+    d = inputs.conv2_inputs(2, 17, 35, 64, 64, 192, seed=53)
+    x, w0, b0, w1, b1 = (dev(d[k]) for k in ("x", "w0", "b0", "w1", "b1"))
+    eye, zero = dev(np.eye(64, dtype=np.float16)), dev(np.zeros(64, dtype=np.float16))
+    print("case convN pipe identity middle", flush=True)
+    y2 = to_np(fc.chain_conv2(x, w0, b0, w1, b1, act="relu", variant="pipe"))
+    y3 = to_np(fc.chain_convN(x, [w0, eye, w1], [b0, zero, b1], ["relu", "none", "none"], variant="pipe"))
+    assert np.array_equal(y2.view(np.uint16), y3.view(np.uint16))
+
+
 @pytest.mark.slow
 def test_convN_full_size(fc):
     spec, d = inputs.workload("conv3x3_conv1x1x2")

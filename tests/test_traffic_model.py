@@ -68,7 +68,8 @@ def test_one_block_reads_each_line_once():
 
 
 @pytest.mark.parametrize("name,variant", [("conv3x3_conv1x1", None), ("b2b_gemm_lds", "lds"),
-                                          ("b2b_gemm_rf", None), ("gemm3_rf", None)])
+                                          ("b2b_gemm_rf", None), ("gemm3_rf", None), ("conv3x3_conv1x1x2", None),
+                                          ("conv3x3_conv1x1x2", "rf")])
 def test_reads_ordered(name, variant):
     spec, _ = inputs.workload(name)
     r = tm.for_workload(spec, variant)
@@ -88,7 +89,8 @@ def _measured():
                                          ("conv3x3_relu_maxpool@lds_weights", "lds_weights"),
                                          ("conv3x3_relu_maxpool@winograd", "winograd"),
                                          ("conv3x3_conv1x1", None), ("b2b_gemm_lds", "lds"),
-                                         ("b2b_gemm_lds@stream", "stream"), ("b2b_gemm_rf", "rf")])
+                                         ("b2b_gemm_lds@stream", "stream"), ("b2b_gemm_rf", "rf"),
+                                         ("conv3x3_conv1x1x2", None), ("conv3x3_conv1x1x2@rf", "rf")])
 def test_l2_model_predicts_fetch(key, variant):
     """The model's L2 misses against the calibrated FETCH_SIZE of the same
     kernel at full size (profiles/traffic.json): within 10%, and closer than
