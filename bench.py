@@ -609,8 +609,18 @@ def tune(fc, prob, name):
         prob.config["variant"] = "auto"
         prob.kernel = "k_conv2_pipe" if best["variant"] == "pipe" else "k_chain_rf"
         prob.traffic_key = name if best["variant"] == default else name + "@" + best["variant"]
+    elif kind == "convN":
+        n = len(prob.acts)
+        default = prob.fc.convN_auto_variant(prob.spec["n"], prob.spec["h"], prob.spec["w"], prob.spec["c"],
+                                             prob.spec["ks"])   # untuned rule
+        best, table, _ = fc.tune_chain_convN(prob.X[0], prob.W[:n], prob.W[n:], prob.acts, out=prob.Y[0], reps=10)
+        prob.conv_variant = "auto"
+        prob.config["variant"] = "auto"
+        prob.kernel = "k_conv2_pipe" if best["variant"] == "pipe" else "k_chain_rf"
+        prob.traffic_key = name if best["variant"] == default else name + "@" + best["variant"]
     else:
-        raise ValueError("--tune applies to the two-GEMM, the conv3x3 -> conv1x1 and the pooled conv workloads")
+        raise ValueError("--tune applies to the two-GEMM, the conv3x3 -> conv1x1 (-> conv1x1) and the pooled conv "
+                         "workloads")
     log("%s tuned: %s waves %d stages %d (%s)" % (name, best["variant"], best["waves"], best["stages"], ", ".join(
         "%s/%d/%d %.2f us" % (r["variant"], r["waves"], r["stages"], r["us"]) for r in table)))
     prob.config.update(tuned={"best": {"variant": best["variant"], "waves": best["waves"], "stages": best["stages"]},
@@ -641,8 +651,9 @@ def main():
     ap.add_argument("--no-configs", action="store_true",
                     help="measure only the headline workload (no per-configuration sub-records)")
     ap.add_argument("--tune", action="store_true",
-                    help="two-GEMM and pooled conv workloads: profile every kernel configuration on the GPU "
-                         "first (chain_gemm2_tune_ex / chain_conv_pool_tune) and time the fastest")
+                    help="two-GEMM, conv -> 1x1 and pooled conv workloads: profile every kernel configuration on the GPU "
+                         "first (chain_gemm2_tune_ex / chain_conv_pool_tune / chain_conv2_tune / chain_convN_tune) and time "
+                         "the fastest")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-probe", action="store_true", help="skip the matrix-core rate / clock probe")
     ap.add_argument("--calib-copy", action="store_true",
@@ -666,9 +677,9 @@ def main():
     log("workload %s: %d buffer set(s), %.1f MB fused algorithmic bytes, %.3f GFLOP"
         % (args.workload, prob.nsets, prob.bytes_fused / 1e6, prob.flops / 1e9))
     if args.tune:
-        if prob.spec["kind"] not in ("gemm2", "conv2", "conv_pool") or args.variant == "winograd":
-            print("bench.py: --tune applies to the two-GEMM, the conv3x3 -> conv1x1 and the pooled direct-conv "
-                  "workloads", file=sys.stderr)
+        if prob.spec["kind"] not in ("gemm2", "conv2", "convN", "conv_pool") or args.variant == "winograd":
+            print("bench.py: --tune applies to the two-GEMM, the conv3x3 -> conv1x1 (-> conv1x1) and the pooled "
+                  "direct-conv workloads", file=sys.stderr)
             sys.exit(2)
         tune(fc, prob, args.workload)
 

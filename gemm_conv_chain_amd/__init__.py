@@ -20,7 +20,7 @@ import ctypes
 import os
 import re
 
-__all__ = ["TuneEntry", "tune_chain_gemm2_table", "auto_config", "tune_conv_pool", "conv_auto_config", "CONV_VARIANT", "lib", "FusedChainError", "chain_gemm2", "tune_chain_gemm2", "auto_variant", "tune_clear", "chain_gemmN", "chain_conv_pool", "chain_conv_bn_pool", "chain_conv2", "chain_convN", "convN_auto_variant",
+__all__ = ["TuneEntry", "tune_chain_gemm2_table", "auto_config", "tune_conv_pool", "conv_auto_config", "CONV_VARIANT", "lib", "FusedChainError", "chain_gemm2", "tune_chain_gemm2", "auto_variant", "tune_clear", "chain_gemmN", "chain_conv_pool", "chain_conv_bn_pool", "chain_conv2", "chain_convN", "convN_auto_variant", "tune_chain_convN",
            "gemm_bias_act", "conv_bias_act", "maxpool2x2", "avgpool2x2", "pad_channels", "pad_weight_channels", "abi_version", "ACT", "VARIANT",
            "LIB_PATH", "POISON_LIB_PATH", "poison_build", "HEADER_PATH", "exported_names"]
 
@@ -121,6 +121,9 @@ def _load(path):
                                       ctypes.POINTER(ctypes.c_int), ctypes.POINTER(_i32), _vp, ctypes.c_int, _vp]
     L.chain_convN_auto_variant.argtypes = [ctypes.POINTER(ConvShape), _i32, ctypes.POINTER(_i32),
                                            ctypes.POINTER(ctypes.c_int)]
+    L.chain_convN_tune.argtypes = [_vp, ctypes.POINTER(ConvShape), _i32, ctypes.POINTER(_vp), ctypes.POINTER(_vp),
+                                   ctypes.POINTER(ctypes.c_int), ctypes.POINTER(_i32), _vp, _i32,
+                                   ctypes.POINTER(TuneEntry), _i32, ctypes.POINTER(_i32), ctypes.POINTER(TuneEntry), _vp]
     L.chain_conv_bn_pool.argtypes = [_vp, _vp, _vp, _vp, ctypes.c_int, ctypes.c_int, _vp,
                                      ctypes.POINTER(ConvShape), _vp, _vp]
     L.chain_conv_pool_ex.argtypes = [_vp, _vp, _vp, _vp, ctypes.c_int, ctypes.c_int, _vp,
@@ -152,7 +155,7 @@ def _load(path):
     L.fc_tune_clear.restype = None
     L.fc_tune_clear.argtypes = []
     for name in ("chain_conv2_auto_config", "chain_conv2_ex", "chain_conv2_variant", "chain_conv2_tune", "winograd_weights", "chain_conv_pool_winograd", "chain_gemm2_ex", "chain_gemm2_tune_ex", "chain_gemm2_auto_config", "chain_conv_pool_tune",
-                 "chain_conv_pool_auto_config", "chain_conv_pool_ex", "avgpool2x2", "fc_probe_mfma", "fc_probe_read", "chain_conv_bn_pool", "chain_convN", "chain_convN_variant", "chain_convN_auto_variant", "chain_gemm2_tune", "chain_gemm2_auto_variant", "chain_gemm2", "chain_gemm2_variant", "chain_gemmN", "chain_conv_pool", "chain_conv2", "gemm_bias_act",
+                 "chain_conv_pool_auto_config", "chain_conv_pool_ex", "avgpool2x2", "fc_probe_mfma", "fc_probe_read", "chain_conv_bn_pool", "chain_convN", "chain_convN_variant", "chain_convN_auto_variant", "chain_convN_tune", "chain_gemm2_tune", "chain_gemm2_auto_variant", "chain_gemm2", "chain_gemm2_variant", "chain_gemmN", "chain_conv_pool", "chain_conv2", "gemm_bias_act",
                  "conv_bias_act", "maxpool2x2", "pad_channels"):
         getattr(L, name).restype = ctypes.c_int
     return L
@@ -646,11 +649,7 @@ def convN_auto_variant(n, h, w, c, ks):
     return _VARIANT_NAME[v.value]
 
 
-def chain_convN(x, ws, bs, acts, out=None, variant="auto"):
-    """y = stage_{n-1}(... stage_0(x)): stage 0 = act[0](conv3x3(x, ws[0]) + bs[0]),
-    stage i > 0 = act[i](1x1 conv with ws[i] [k_{i-1}, k_i] (or [1,1,k_{i-1},k_i]) + bs[i]);
-    n = 3 or 4, every intermediate rounded once to fp16 and kept on chip.
-    ``variant``: kernel form ("auto", "rf" or "pipe")."""
+def _convN_prep(x, ws, bs, acts, out):
     n = len(ws)
     if len(bs) != n or len(acts) != n:
         raise ValueError("ws, bs and acts must have the same length")
@@ -670,10 +669,33 @@ def chain_convN(x, ws, bs, acts, out=None, variant="auto"):
     bp = (_vp * n)(*[None if b is None else b.data_ptr() for b in bs])
     ap = (ctypes.c_int * n)(*[_act(a) for a in acts])
     kp = (_i32 * n)(*ks)
+    return sh, n, wp, bp, ap, kp, out
+
+
+def chain_convN(x, ws, bs, acts, out=None, variant="auto"):
+    """y = stage_{n-1}(... stage_0(x)): stage 0 = act[0](conv3x3(x, ws[0]) + bs[0]),
+    stage i > 0 = act[i](1x1 conv with ws[i] [k_{i-1}, k_i] (or [1,1,k_{i-1},k_i]) + bs[i]);
+    n = 3 or 4, every intermediate rounded once to fp16 and kept on chip.
+    ``variant``: kernel form ("auto", "rf" or "pipe")."""
+    sh, n, wp, bp, ap, kp, out = _convN_prep(x, ws, bs, acts, out)
     v = VARIANT[variant] if isinstance(variant, str) else int(variant)
     _check("chain_convN", lib().chain_convN_variant(_ptr(x), ctypes.byref(sh), n, wp, bp, ap, kp, _ptr(out), v,
                                                     _stream(x)))
     return out
+
+
+def tune_chain_convN(x, ws, bs, acts, out=None, reps=20):
+    """Time each kernel form of the N-stage conv chain for these tensors
+    (blocking) and cache the fastest (chain_convN_tune).  Returns (best,
+    table, out) with dict rows {variant, waves, stages, us}."""
+    sh, n, wp, bp, ap, kp, out = _convN_prep(x, ws, bs, acts, out)
+    table = (TuneEntry * 4)()
+    best = TuneEntry()
+    cnt = _i32(0)
+    _check("chain_convN_tune", lib().chain_convN_tune(_ptr(x), ctypes.byref(sh), n, wp, bp, ap, kp, _ptr(out),
+                                                      int(reps), table, 4, ctypes.byref(cnt), ctypes.byref(best),
+                                                      _stream(x)))
+    return _entry(best, _VARIANT_NAME), [_entry(table[i], _VARIANT_NAME) for i in range(min(cnt.value, 4))], out
 
 
 def avgpool2x2(x, out=None):

@@ -140,7 +140,7 @@ bool two_stage_ok(int K0)
 typedef std::vector<int64_t> TuneKey;   // kind, device, shape ...
 std::mutex g_tune_mu;
 std::map<TuneKey, Config> g_tune;
-enum { TK_GEMM2 = 0, TK_CONV_POOL = 1, TK_CONV2 = 2 };
+enum { TK_GEMM2 = 0, TK_CONV_POOL = 1, TK_CONV2 = 2, TK_CONVN = 3 };
 
 // The cached configuration for key (device appended here), if any.  The
 // device is only queried when something has been tuned.
@@ -218,6 +218,13 @@ TuneKey conv2_key(const fc_conv_shape* s, int k1, int act)
 }
 
 bool conv2_pipe_ok(const fc_conv_shape* s, int k1) { return fc::conv2_pipe_fits(s->w, s->c, s->k, k1); }
+
+TuneKey convN_key(const fc_conv_shape* s, int nst, const int32_t* k)
+{
+    TuneKey key{TK_CONVN, s->n, s->h, s->w, s->c, nst};
+    for (int i = 0; i < 4; ++i) key.push_back(i < nst ? k[i] : 0);
+    return key;
+}
 
 // Candidates of the conv3x3 -> conv1x1 chain: the pipelined two-group form
 // (where it takes the shape), then the register-resident form with 8, 4, 2 or
@@ -797,7 +804,10 @@ fc_status chain_convN_variant(const fc_half* x, const fc_conv_shape* shape0, int
     }
     if (variant == FC_VARIANT_PIPE && !pipe_ok)
         return fail(FC_E_UNSUPPORTED, "the pipelined form takes 3 stages with c = 64, k = 64, 64, <= 256");
-    const bool use_pipe = variant == FC_VARIANT_PIPE || (variant == FC_VARIANT_AUTO && pipe_ok);
+    bool use_pipe = variant == FC_VARIANT_PIPE || (variant == FC_VARIANT_AUTO && pipe_ok);
+    Config tuned;
+    if (variant == FC_VARIANT_AUTO && tuned_config(convN_key(shape0, nstages, k), &tuned))
+        use_pipe = tuned.variant == fc::VARIANT_PIPE;   // the profiled form (only applicable ones are cached)
     if (!use_pipe && !fc::gemmn_fits(nstages, widths))
         return fail(FC_E_UNSUPPORTED, "register residence: every intermediate width <= 128 and all weights within LDS");
     if (npix == 0) return ok();
@@ -817,6 +827,11 @@ fc_status chain_convN_auto_variant(const fc_conv_shape* shape0, int32_t nstages,
     bool pipe_ok = false;
     fc_status s = check_convN_shape(shape0, nstages, k, widths, &pipe_ok);
     if (s != FC_OK) return s;
+    Config tuned;
+    if (tuned_config(convN_key(shape0, nstages, k), &tuned)) {
+        *out = (fc_variant)tuned.variant;
+        return ok();
+    }
     if (pipe_ok) {
         *out = FC_VARIANT_PIPE;
         return ok();
@@ -831,6 +846,39 @@ fc_status chain_convN(const fc_half* x, const fc_conv_shape* shape0, int32_t nst
                       const fc_half* const* b, const fc_act* act, const int32_t* k, fc_half* y, void* stream)
 {
     return chain_convN_variant(x, shape0, nstages, w, b, act, k, y, FC_VARIANT_AUTO, stream);
+}
+
+fc_status chain_convN_tune(const fc_half* x, const fc_conv_shape* shape0, int32_t nstages, const fc_half* const* w,
+                           const fc_half* const* b, const fc_act* act, const int32_t* k, fc_half* y, int32_t reps,
+                           fc_tune_entry* table, int32_t capacity, int32_t* count, fc_tune_entry* best, void* stream)
+{
+    if (!w || !act || !k) return fail(FC_E_NULL, "w, act and k are required");
+    int widths[5];
+    bool pipe_ok = false;
+    fc_status s = check_convN_shape(shape0, nstages, k, widths, &pipe_ok);
+    if (s != FC_OK) return s;
+    if ((long)shape0->n * shape0->h * shape0->w == 0) return fail(FC_E_SHAPE, "empty output: nothing to time");
+    if (reps < 1 || reps > 1000) return fail(FC_E_SHAPE, "reps=%d outside 1..1000", (int)reps);
+    if (capacity < 0 || (capacity > 0 && !table)) return fail(FC_E_NULL, "table is required for capacity > 0");
+    Config cand[2];
+    int n = 0;
+    if (pipe_ok) cand[n++] = Config{fc::VARIANT_PIPE, 0, 0};
+    if (fc::gemmn_fits(nstages, widths)) cand[n++] = Config{fc::VARIANT_RF, 0, 0};
+    if (n == 0)
+        return fail(FC_E_UNSUPPORTED, "register residence: every intermediate width <= 128 and all weights within LDS");
+    // one validating call per candidate first: argument errors surface as
+    // their own status, before any timing
+    for (int i = 0; i < n; ++i) {
+        s = chain_convN_variant(x, shape0, nstages, w, b, act, k, y, (fc_variant)cand[i].variant, stream);
+        if (s != FC_OK) return s;
+    }
+    hipStream_t st = (hipStream_t)stream;
+    auto launch = [&](const Config& c) -> hipError_t {
+        const fc_status r = chain_convN_variant(x, shape0, nstages, w, b, act, k, y, (fc_variant)c.variant, stream);
+        return r == FC_OK ? hipSuccess : hipErrorLaunchFailure;
+    };
+    return profile("chain_convN_tune", launch, cand, n, reps, convN_key(shape0, nstages, k), table, capacity, count,
+                   best, st);
 }
 
 fc_status maxpool2x2(const fc_half* x, fc_half* y, uint8_t* argmax, int32_t n, int32_t h, int32_t w, int32_t c,

@@ -393,7 +393,8 @@ fc_status chain_conv2_tune(const fc_half *x, const fc_half *w0, const fc_half *b
  * k[1 .. nstages-2] <= 128 and all weights must fit in LDS together, else
  * FC_E_UNSUPPORTED -- except three stages with c = 64 and k = {64, 64, <= 256},
  * which run the pipelined form (chain_convN_variant, FC_VARIANT_PIPE) and may
- * exceed that LDS rule.  b or b[i] may be NULL.  w, b, act and k are host
+ * exceed that LDS rule; after chain_convN_tune for the shape, the profiled form
+ * runs instead.  b or b[i] may be NULL.  w, b, act and k are host
  * arrays read during the call; the tensors are device pointers owned by the
  * caller.  An empty batch is a no-op.
  */
@@ -413,11 +414,26 @@ fc_status chain_convN_variant(const fc_half *x, const fc_conv_shape *shape0, int
                               const fc_half *const *w, const fc_half *const *b, const fc_act *act,
                               const int32_t *k, fc_half *y, fc_variant variant, void *stream);
 
-/* The variant chain_convN runs for this shape: FC_VARIANT_PIPE where the
- * pipelined form applies, else FC_VARIANT_RF.  Host only, launches nothing;
- * shape errors as chain_convN (FC_E_NULL for a NULL k or out). */
+/* The variant chain_convN runs for this shape on the current device: the
+ * profiled one if chain_convN_tune ran for the shape, else FC_VARIANT_PIPE
+ * where the pipelined form applies, else FC_VARIANT_RF.  Host only, launches
+ * nothing; shape errors as chain_convN (FC_E_NULL for a NULL k or out). */
 fc_status chain_convN_auto_variant(const fc_conv_shape *shape0, int32_t nstages, const int32_t *k,
                                    fc_variant *out);
+
+/* chain_convN_tune -- time each kernel form chain_convN can run for these
+ * tensors (the pipelined form where it applies, the register-resident form
+ * where it fits; reps launches each after one untimed launch, on stream,
+ * blocking), write one row per form to table (up to capacity rows; *count =
+ * forms timed), the fastest to *best, and cache it for the shape (device,
+ * n, h, w, c, k[]): chain_convN with FC_VARIANT_AUTO then runs it.  y holds
+ * the winner's output on return.  BOLT notes, "Light-weight performance
+ * profiler".  Errors as chain_convN; reps outside 1..1000 or an empty batch
+ * -> FC_E_SHAPE; capacity > 0 with a NULL table -> FC_E_NULL. */
+fc_status chain_convN_tune(const fc_half *x, const fc_conv_shape *shape0, int32_t nstages,
+                           const fc_half *const *w, const fc_half *const *b, const fc_act *act,
+                           const int32_t *k, fc_half *y, int32_t reps, fc_tune_entry *table, int32_t capacity,
+                           int32_t *count, fc_tune_entry *best, void *stream);
 
 /* ---- unfused single-operator kernels (the two-kernel baselines) ---- */
 

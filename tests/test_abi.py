@@ -27,7 +27,7 @@ def test_exports_every_declared_symbol(L):
               "conv_bias_act", "maxpool2x2", "pad_channels", "fc_abi_version", "fc_status_str", "fc_last_error",
               "chain_gemm2_tune", "chain_gemm2_auto_variant", "fc_tune_clear", "chain_convN", "chain_conv_bn_pool", "fc_probe_mfma", "chain_conv_pool_ex", "chain_gemm2_ex",
               "chain_gemm2_tune_ex", "chain_gemm2_auto_config", "chain_conv_pool_tune", "chain_conv_pool_auto_config",
-              "chain_conv2_variant", "chain_convN_variant", "chain_convN_auto_variant", "chain_conv2_ex", "chain_conv2_tune", "chain_conv2_auto_config"):
+              "chain_conv2_variant", "chain_convN_variant", "chain_convN_auto_variant", "chain_convN_tune", "chain_conv2_ex", "chain_conv2_tune", "chain_conv2_auto_config"):
         assert n in names
     for n in names:
         assert hasattr(L, n), n
@@ -333,6 +333,22 @@ def test_chain_convN_auto_variant(L):
     assert L.chain_convN_auto_variant(None, 3, kp, C.byref(v)) == E_NULL
     assert L.chain_convN_auto_variant(C.byref(sh(64, 64)), 3, None, C.byref(v)) == E_NULL
     assert L.chain_convN_auto_variant(C.byref(sh(64, 64)), 3, kp, None) == E_NULL
+    # the tuner's argument checks (all decided before any HIP call)
+    tab = (fc.TuneEntry * 4)()
+    cnt, best = C.c_int32(0), fc.TuneEntry()
+    wp = (C.c_void_p * 3)(P, P, P)
+    ap = (C.c_int * 3)(1, 1, 0)
+
+    def tn(shape, ks=(64, 64, 128), reps=5, table=tab, capacity=4, n=3):
+        kp = (C.c_int32 * 3)(*ks)
+        return L.chain_convN_tune(P, C.byref(shape), n, wp, None, ap, kp, P2, reps, table, capacity, C.byref(cnt),
+                                  C.byref(best), None)
+    assert tn(sh(64, 64), reps=0) == E_SHAPE
+    assert tn(sh(64, 64), reps=1001) == E_SHAPE
+    assert tn(fc.ConvShape(0, 8, 8, 64, 64, 3, 3, 1, 1)) == E_SHAPE     # empty: nothing to time
+    assert tn(sh(64, 64), table=None) == E_NULL
+    assert tn(sh(64, 64), ks=(64, 136, 128)) == E_UNSUP
+    assert tn(sh(64, 64), n=2) == E_UNSUP
     # the binding's helper
     assert fc.convN_auto_variant(32, 56, 56, 64, [64, 64, 256]) == "pipe"
     assert fc.convN_auto_variant(32, 56, 56, 64, [64, 48, 96]) == "rf"

@@ -172,3 +172,27 @@ def test_tune_conv2(fc):
     assert_close(to_np(fc.chain_conv2(*args)), ref, "conv2 auto after tuning")
     fc.tune_clear()
     assert fc.conv2_auto_config(4, 28, 28, 64, 64, 256) == rule
+
+
+@pytest.mark.parametrize("ks,forms", [([64, 64, 128], ["pipe", "rf"]), ([64, 48, 96], ["rf"])])
+def test_tune_convN(fc, ks, forms):
+    d = inputs.convN_inputs(3, 20, 24, 64, ks, seed=7)
+    ws, bs = [dev(w) for w in d["ws"]], [dev(b) for b in d["bs"]]
+    x = dev(d["x"])
+    acts = ["relu", "relu", "none"]
+    print("case tune convN", ks, flush=True)
+    fc.tune_clear()
+    rule = fc.convN_auto_variant(3, 20, 24, 64, ks)
+    assert rule == forms[0]
+    best, table, out = fc.tune_chain_convN(x, ws, bs, acts, reps=3)
+    torch.cuda.synchronize()
+    print(best, table, flush=True)
+    assert [r["variant"] for r in table] == forms and all(r["us"] > 0 for r in table)
+    fastest = min(table, key=lambda r: r["us"])
+    assert best["variant"] == fastest["variant"]
+    assert fc.convN_auto_variant(3, 20, 24, 64, ks) == best["variant"]
+    ref = oracle.chain_convN(d["x"], d["ws"], d["bs"], [oracle.ACT_RELU, oracle.ACT_RELU, oracle.ACT_NONE])
+    assert_close(to_np(out), ref, "tuned convN output")
+    assert_close(to_np(fc.chain_convN(x, ws, bs, acts)), ref, "convN auto after tuning")
+    fc.tune_clear()
+    assert fc.convN_auto_variant(3, 20, 24, 64, ks) == rule
