@@ -511,17 +511,15 @@ static hipError_t launch_rf_k(const Loader& ld, RfArgs a, hipStream_t st)
     return hipGetLastError();
 }
 
-// Compile-time chunk counts for the k lengths in use (64, 256, 576); the
-// two-GEMM chains with 4 or 9 chunks also come with a two-stage row ring
-// (a.stages == 2: one chunk in flight instead of three).
+// Compile-time chunk counts for the k lengths in use (64, 256, 576); with 4
+// or 9 chunks the chains also come with a two-stage row ring (a.stages == 2:
+// one chunk in flight instead of three).
 template <int NT0, class Loader, int NMID = 0>
 static hipError_t launch_rf_t(const Loader& ld, const RfArgs& a, hipStream_t st)
 {
-    if constexpr (NMID == 0) {
-        if (a.stages == 2) {
-            if ((a.K0p >> 6) == 4) return launch_rf_k<NT0, 4, Loader, 0, 2>(ld, a, st);
-            if ((a.K0p >> 6) == 9) return launch_rf_k<NT0, 9, Loader, 0, 2>(ld, a, st);
-        }
+    if (a.stages == 2) {
+        if ((a.K0p >> 6) == 4) return launch_rf_k<NT0, 4, Loader, NMID, 2>(ld, a, st);
+        if ((a.K0p >> 6) == 9) return launch_rf_k<NT0, 9, Loader, NMID, 2>(ld, a, st);
     }
     switch (a.K0p >> 6) {
     case 1: return launch_rf_k<NT0, 1, Loader, NMID>(ld, a, st);

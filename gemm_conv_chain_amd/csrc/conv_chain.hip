@@ -749,6 +749,14 @@ template <int NMID>
 static hipError_t launch_convN(const Conv3x3Rows& ld, const RfArgs& a, int nt0, hipStream_t st)
 {
     const bool k9 = (a.K0p >> 6) == 9;
+    if (k9 && a.stages == 2) {   // 8 tile-owning waves: the two-stage row ring
+        switch (nt0) {
+        case 1: return launch_rf_k<1, 9, Conv3x3Rows, NMID, 2>(ld, a, st);
+        case 2: return launch_rf_k<2, 9, Conv3x3Rows, NMID, 2>(ld, a, st);
+        case 3: return launch_rf_k<3, 9, Conv3x3Rows, NMID, 2>(ld, a, st);
+        case 4: return launch_rf_k<4, 9, Conv3x3Rows, NMID, 2>(ld, a, st);
+        }
+    }
     switch (nt0) {
     case 1: return k9 ? launch_rf_k<1, 9, Conv3x3Rows, NMID>(ld, a, st) : launch_rf_k<1, 0, Conv3x3Rows, NMID>(ld, a, st);
     case 2: return k9 ? launch_rf_k<2, 9, Conv3x3Rows, NMID>(ld, a, st) : launch_rf_k<2, 0, Conv3x3Rows, NMID>(ld, a, st);
@@ -766,6 +774,7 @@ hipError_t run_chain_convN_3x3(const half_t* x, int nst, const half_t* const* w,
     if (M == 0) return hipSuccess;
     RfArgs a{};
     gemmn_args(nst, w, b, act, widths, y, M, a);
+    a.stages = (a.K0p >> 6) == 9 ? 2 : 0;
     Conv3x3Rows ld;
     ld.x = x; ld.H = H; ld.W = W; ld.C = C; ld.M = M;
     ld.set_divisors();

@@ -504,6 +504,8 @@ hipError_t run_chain_gemmN(const half_t* A, int nst, const half_t* const* W, con
     if (M == 0) return hipSuccess;
     RfArgs a{};
     gemmn_args(nst, W, b, act, widths, D, M, a);
+    // 8 tile-owning waves per block: the two-stage row ring where it is built
+    a.stages = (a.K0p >> 6) == 4 || (a.K0p >> 6) == 9 ? 2 : 0;
     return run_rf_dense(A, a, nst - 2, st);
 }
 
